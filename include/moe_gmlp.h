@@ -1,0 +1,332 @@
+/*
+ * moe_gmlp.h -- C ABI of the fused grouped-MLP MoE expert block for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Pages cited (by title and section):
+ *   [FK] "Boosting MoE Training Throughput with Advanced Fusion Kernels",
+ *        NVIDIA technical blog (zh-cn translation).
+ *   [TE] "NVIDIA Transformer Engine 优化 MoE 生物基础模型训练", the
+ *        Transformer Engine + BioNeMo Mixtral tutorial.
+ *
+ * The block computes, for T tokens routed to k of E local experts:
+ *   forward   Xp = permute(X);  Z_e = Xp_e W1_e^T;  A = p * GLU(Z);
+ *             Yp_e = A_e W2_e^T;  out = unpermute(Yp)
+ *   backward  dYp = permute(dOut);  dA_e = dYp_e W2_e;  dZ, dp = dGLU(...);
+ *             dXp_e = dZ_e W1_e;  dX = unpermute(dXp);  dprobs = gather(dp)
+ * with one grouped-GEMM launch per GEMM whose per-group row counts are read
+ * from device memory ([FK] § "Eliminating host-device synchronization and
+ * CPU launch overhead"), so no call below ever synchronises with the host.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named as device buffers are device addresses owned by the
+ *     caller; the library never allocates, frees, copies to the host or
+ *     synchronises.  Every call only enqueues kernels on `stream` (a
+ *     hipStream_t passed as void*; NULL = the null stream), so every call is
+ *     legal inside hipStreamBeginCapture in global mode.
+ *   - bf16 means IEEE bfloat16 (1-8-7 bits); tensors are row-major with the
+ *     last index contiguous.
+ *   - Host-checkable problems (NULL pointers, unsupported sizes, small
+ *     workspace) return a negative moe_status before anything is launched.
+ *     Problems only visible on the device (padded rows exceeding M_cap,
+ *     duplicate experts in a token's top-k list) OR a bit into the optional
+ *     device int32 *err_flag (MOE_DEVERR_*); kernels then clamp so that no
+ *     access leaves the caller's buffers.
+ *   - Calls are re-entrant; a per-device attribute cache is filled once.
+ */
+#ifndef MOE_GMLP_H
+#define MOE_GMLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,   /* NULL pointer, bad size or flag          */
+  MOE_ERR_UNSUPPORTED = -2,   /* valid request this build does not serve */
+  MOE_ERR_WORKSPACE = -3,     /* workspace NULL or smaller than required */
+  MOE_ERR_LAUNCH = -4,        /* a kernel launch failed (hipGetLastError) */
+  MOE_ERR_DEVICE = -5         /* no usable gfx950 device                 */
+} moe_status;
+
+/* Bits OR-ed into *err_flag by kernels (never read back by the library). */
+#define MOE_DEVERR_MCAP_OVERFLOW 0x1  /* padded row count > M_cap          */
+#define MOE_DEVERR_DUP_EXPERT 0x2     /* a token lists one expert twice    */
+
+/* Group-start alignment of the padded row layout (rows).  Every group of
+ * the permuted layout starts at a multiple of it, so MXFP8 blocks of 32
+ * rows never straddle two experts. */
+#define MOE_GROUP_ALIGN 128
+/* Gate/up interleave block of the repacked FC1 weight (rows). */
+#define MOE_INTERLEAVE 64
+/* MXFP8 block length ([TE] § "Challenge 2", Fig. 3). */
+#define MOE_MX_BLOCK 32
+
+typedef enum moe_act {
+  MOE_ACT_SWIGLU = 0, /* Swish_beta(g) * u   ([FK] § GLU epilogue, eq. SwiGLU) */
+  MOE_ACT_GEGLU = 1,  /* GELU(g) * u, exact erf form                           */
+  MOE_ACT_SRELU = 2   /* max(z, 0)^2, not gated: FC1 width I, no interleave    */
+} moe_act;
+
+typedef enum moe_prec {
+  MOE_PREC_BF16 = 0,  /* bf16 operands, fp32 accumulation                  */
+  MOE_PREC_MXFP8 = 1  /* E4M3 operands with E8M0 scales per 32 along K     */
+} moe_prec;
+
+/* Activation options: the supported GLU family with clamping and scaling
+ * ([FK] § "Overcoming training bottlenecks in MoE blocks", list of supported
+ * activations; § "Optimizing GLU activations with fused GEMM epilogues").
+ *   gated:  g = clamp(z_gate, gate_lo, gate_hi)
+ *           u = clamp(z_up, lin_lo, lin_hi) + lin_offset
+ *           s = act(g) * u,   act = Swish_beta or GELU
+ *   sReLU:  s = max(clamp(z, gate_lo, gate_hi), 0)^2
+ * Gradients pass through a clamp only where lo <= pre-clamp value <= hi.
+ * Use -INFINITY / +INFINITY for no clamp.  The output of the activation is
+ * multiplied by the row's routing probability (ScaledSwiGLU, [TE] §
+ * "Challenge 3"). */
+typedef struct moe_act_params {
+  int32_t act;        /* moe_act */
+  float beta;         /* Swish_beta slope; 1 = SiLU */
+  float gate_lo, gate_hi;
+  float lin_lo, lin_hi;
+  float lin_offset;
+} moe_act_params;
+
+/* ------------------------------------------------------------------------
+ * moe_weight_repack_interleave
+ *   Row permutation of the FC1 weight so that one output tile holds matching
+ *   halves of gate and up columns ([FK] § "Optimizing GLU activations with
+ *   fused GEMM epilogues", Fig. 2).  Done once, e.g. at checkpoint load.
+ *   w1   bf16 [E][2I][H], rows [0,I) gate, [I,2I) up   (inverse: w1i layout)
+ *   w1i  bf16 [E][2I][H], packed row 2b*floor(j/b) + j%b holds gate row j and
+ *        packed row 2b*floor(j/b) + b + j%b holds up row j (b = block)
+ *   block must be MOE_INTERLEAVE; I % block == 0.  inverse != 0 undoes it.
+ *   w1 and w1i must not overlap.  Bit-exact copy.
+ * ---------------------------------------------------------------------- */
+moe_status moe_weight_repack_interleave(const void* w1, void* w1i, int E,
+                                        int I, int H, int block, int inverse,
+                                        void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_permute -- routing metadata and token gather.
+ *   The per-expert token counts (GroupedLinear's split_sizes, [TE] §
+ *   "Challenge 1") and the expert-major row layout are built on the device
+ *   ([FK] § "Eliminating host-device synchronization").
+ *
+ *   MOE_PERMUTE_BUILD_MAP: from expert_idx[T][k] (global ids; local expert e
+ *     is id first_expert+e, any other id is not local) and probs[T][k]:
+ *       split_sizes[E]       rows of each local expert
+ *       offsets[E+1]         exclusive scan of split_sizes
+ *       padded_offsets[E+1]  exclusive scan of split_sizes rounded up to
+ *                            MOE_GROUP_ALIGN (group starts)
+ *       row_id_map[T][k]     row of (t, slot), -1 if the slot is not local;
+ *                            inside a group rows follow ascending t
+ *       row_src[M_cap]       token of each row, -1 for pad rows
+ *       probs_p[M_cap]       probs[t][slot] of each row, 0 for pad rows
+ *     Needs workspace of moe_permute_workspace_size(T, E) bytes.
+ *   MOE_PERMUTE_GATHER: xp[r] = x[row_src[r]] (bf16 [T][H] -> [M_cap][H]) for
+ *     r < padded_offsets[E]; pad rows are zero; rows past padded_offsets[E]
+ *     are not written.  Reads the map built by this or an earlier call.
+ *     Used for X in the forward and for dOut in the backward.
+ *   MOE_PERMUTE_WRITE_MX: also (or, with xp == NULL, only) write the MXFP8
+ *     encoding of the gathered rows along H: xp_q u8 [M_cap][H] E4M3 codes,
+ *     xp_s u8 [M_cap][H/32] E8M0 scales.
+ *   Requires H % 32 == 0 for GATHER, M_cap >= T*k + E*(MOE_GROUP_ALIGN-1)
+ *   unless the caller knows the padded total fits (else MOE_DEVERR_MCAP_
+ *   OVERFLOW is raised and rows past M_cap are dropped).
+ * ---------------------------------------------------------------------- */
+#define MOE_PERMUTE_BUILD_MAP 0x1
+#define MOE_PERMUTE_GATHER 0x2
+#define MOE_PERMUTE_WRITE_MX 0x4
+
+typedef struct moe_permute_args {
+  int32_t flags;
+  int32_t T, k, E, first_expert, H;
+  int64_t M_cap;
+  const int32_t* expert_idx;   /* [T][k]  device */
+  const float* probs;          /* [T][k]  device */
+  int32_t* split_sizes;        /* [E]     device */
+  int32_t* offsets;            /* [E+1]   device (may be NULL) */
+  int32_t* padded_offsets;     /* [E+1]   device */
+  int32_t* row_id_map;         /* [T][k]  device */
+  int32_t* row_src;            /* [M_cap] device */
+  float* probs_p;              /* [M_cap] device */
+  const void* x;               /* bf16 [T][H]     device (GATHER) */
+  void* xp;                    /* bf16 [M_cap][H] device (GATHER) */
+  uint8_t* xp_q;               /* u8 [M_cap][H]     (WRITE_MX) */
+  uint8_t* xp_s;               /* u8 [M_cap][H/32]  (WRITE_MX) */
+  int32_t* err_flag;           /* optional device int32 */
+  void* workspace;             /* device, BUILD_MAP only */
+  size_t workspace_bytes;
+} moe_permute_args;
+
+size_t moe_permute_workspace_size(int T, int E);
+moe_status moe_permute(const moe_permute_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_unpermute -- combine of the expert outputs (the index-add of [TE] §
+ *   "Challenge 1"), in gather form so that no atomics are needed:
+ *     out[t] = bf16( sum_{s < k, row_id_map[t][s] >= 0} yp[row_id_map[t][s]] )
+ *   summed in fp32 in slot order; a token with no local slot gets zeros.
+ *   The same call combines dXp into dX in the backward.  If dprobs_p and
+ *   dprobs are both non-NULL it also writes
+ *     dprobs[t][s] = row_id_map[t][s] >= 0 ? dprobs_p[row_id_map[t][s]] : 0.
+ *   yp bf16 [M_cap][H]; out bf16 [T][H]; H % 8 == 0.
+ * ---------------------------------------------------------------------- */
+typedef struct moe_unpermute_args {
+  int32_t T, k, H;
+  int64_t M_cap;
+  const int32_t* row_id_map;   /* [T][k]     device */
+  const void* yp;              /* bf16 [M_cap][H] device */
+  void* out;                   /* bf16 [T][H] device */
+  const float* dprobs_p;       /* [M_cap] device, optional */
+  float* dprobs;               /* [T][k]  device, optional */
+} moe_unpermute_args;
+
+moe_status moe_unpermute(const moe_unpermute_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_quantize_mxfp8 -- bf16 -> MXFP8 ([TE] § "Challenge 2", Fig. 3;
+ *   § "Challenge 3": bf16 master weights are quantized before the
+ *   low-precision GEMM).  Per block of 32 values v along the chosen axis:
+ *     scale exponent e = clamp(floor(log2 max|v|) - 8, -127, 127) (-127 for
+ *     an all-zero block), scale code = e + 127,
+ *     code = E4M3 round-to-nearest-even of v / 2^e, saturated to +-448.
+ *   MOE_QUANT_ROW: blocks along cols.  q [b][rows][cols], s [b][rows][cols/32]
+ *   MOE_QUANT_COL: blocks along rows, written transposed so the consumer's K
+ *     is contiguous: q [b][cols][rows], s [b][cols][rows/32]
+ *   x bf16 [b][rows][cols] with x_stride elements between batch entries;
+ *   rows and cols must be multiples of 32.  If amax != NULL, *amax is raised
+ *   to max|x| (the caller zeroes it first).
+ * ---------------------------------------------------------------------- */
+#define MOE_QUANT_ROW 0
+#define MOE_QUANT_COL 1
+
+typedef struct moe_quant_args {
+  int32_t mode;
+  int32_t batch, rows, cols;
+  int64_t x_stride;            /* elements between batch entries of x */
+  const void* x;               /* bf16 device */
+  uint8_t* q;                  /* device */
+  uint8_t* s;                  /* device */
+  float* amax;                 /* optional device float */
+} moe_quant_args;
+
+moe_status moe_quantize_mxfp8(const moe_quant_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_grouped_mlp_fwd -- FC1 grouped GEMM with the fused activation epilogue,
+ *   then the FC2 grouped GEMM: two persistent launches whose tile schedulers
+ *   walk split_sizes / padded_offsets on the device.
+ *   ([FK] § "Overcoming training bottlenecks", kernel families 1 and 2,
+ *   Fig. 1; § "Optimizing GLU activations with fused GEMM epilogues";
+ *   [TE] § "Challenge 3": GroupedLinear -> ScaledSwiGLU -> GroupedLinear.)
+ *
+ *   For every local expert e and row r in [padded_offsets[e],
+ *   padded_offsets[e] + split_sizes[e]):
+ *     z[r]  = xp[r] . W1i_e^T                 (fp32 accumulate, stored bf16)
+ *     a[r]  = bf16( probs_p[r] * act(z[r]) )   (act on the fp32 accumulator)
+ *     yp[r] = bf16( a[r] . W2_e^T )
+ *   Rows outside those ranges are not written.
+ *   Shapes: N1 = 2I (gated) or I (sReLU).
+ *     xp   bf16 [M_cap][H]
+ *     w1i  bf16 [E][N1][H], gated: interleaved by moe_weight_repack_interleave
+ *     w2   bf16 [E][H][I]
+ *     z    bf16 [M_cap][N1] in the same (interleaved) column order as w1i rows;
+ *          may be NULL when no backward follows
+ *     a    bf16 [M_cap][I] logical column order
+ *     yp   bf16 [M_cap][H]
+ *     amax optional device float: raised to max|a| over written rows (the
+ *          call zeroes it first, so it holds this call's value)
+ *   Requires H % 64 == 0, I % 64 == 0, E >= 1.
+ *   prec == MOE_PREC_MXFP8 is reserved (MOE_ERR_UNSUPPORTED in this build).
+ *   timing_events: optional hipEvent_t handles; non-NULL entries are recorded
+ *   on `stream` before FC1, between FC1 and FC2, and after FC2.
+ * ---------------------------------------------------------------------- */
+typedef struct moe_fwd_args {
+  int32_t E, H, I;
+  int64_t M_cap;
+  int32_t prec;                /* moe_prec */
+  moe_act_params act;
+  int32_t cu_margin;           /* CUs to leave free for concurrent kernels */
+  const int32_t* split_sizes;     /* [E]     device */
+  const int32_t* padded_offsets;  /* [E+1]   device */
+  const float* probs_p;           /* [M_cap] device */
+  const void* xp;
+  const void* w1i;
+  const void* w2;
+  int64_t w1_stride;           /* elements between experts of w1i (0: N1*H) */
+  int64_t w2_stride;           /* elements between experts of w2  (0: H*I)  */
+  void* z;
+  void* a;
+  float* amax;
+  void* yp;
+  int32_t* err_flag;
+  void* timing_events[3];
+} moe_fwd_args;
+
+moe_status moe_grouped_mlp_fwd(const moe_fwd_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_grouped_mlp_bwd -- FC2 dgrad grouped GEMM with the fused
+ *   dActivation epilogue, then the FC1 dgrad grouped GEMM
+ *   ([FK] § "Overcoming training bottlenecks", kernel family 3, Fig. 1;
+ *   § "Optimizing GLU activations": the backward epilogue reads the GEMM
+ *   output, applies dSwiGLU and writes the result).
+ *
+ *   For every valid row r of expert e:
+ *     dA[r]       = dyp[r] . W2_e                   (fp32, not stored)
+ *     s[r]        = act(z[r])                       (recomputed from bf16 z)
+ *     dprobs_p[r] = sum_j dA[r][j] * s[r][j]        (fixed-order, deterministic)
+ *     dz[r]       = bf16( dact(z[r], probs_p[r] * dA[r]) )  (layout of z)
+ *     dxp[r]      = bf16( dz[r] . W1i_e )           (contracts over N1)
+ *   Shapes as in moe_grouped_mlp_fwd; dyp bf16 [M_cap][H]; dz bf16
+ *   [M_cap][N1]; dprobs_p float [M_cap]; dxp bf16 [M_cap][H].
+ *   Needs workspace of moe_grouped_mlp_workspace_size(...) bytes (partial
+ *   sums of dprobs_p).  timing_events as in the forward (before FC2 dgrad,
+ *   between, after FC1 dgrad).
+ * ---------------------------------------------------------------------- */
+typedef struct moe_bwd_args {
+  int32_t E, H, I;
+  int64_t M_cap;
+  int32_t prec;
+  moe_act_params act;
+  int32_t cu_margin;
+  const int32_t* split_sizes;
+  const int32_t* padded_offsets;
+  const float* probs_p;
+  const void* dyp;
+  const void* w2;
+  const void* z;
+  const void* w1i;
+  int64_t w1_stride;
+  int64_t w2_stride;
+  void* dz;
+  float* dprobs_p;
+  void* dxp;
+  int32_t* err_flag;
+  void* workspace;
+  size_t workspace_bytes;
+  void* timing_events[3];
+} moe_bwd_args;
+
+moe_status moe_grouped_mlp_bwd(const moe_bwd_args* args, void* stream);
+
+/* Workspace bytes moe_grouped_mlp_bwd needs for these sizes. */
+size_t moe_grouped_mlp_workspace_size(int E, int H, int I, int64_t M_cap,
+                                      int prec, int act);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status status);
+
+/* Library version, e.g. 100 = 0.1.0. */
+int moe_gmlp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_GMLP_H */

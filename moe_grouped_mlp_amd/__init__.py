@@ -1,0 +1,17 @@
+"""Fused grouped-MLP MoE expert block for AMD Instinct MI355X (gfx950).
+
+The compute path is the HIP library libmoe_gmlp.so (C ABI in
+include/moe_gmlp.h); this package only marshals arguments to it.  PyTorch is
+used for device memory and streams.  There is no fallback: if the library is
+missing or fails to load, every call raises.
+"""
+
+from .binding import (  # noqa: F401
+    ACT_GEGLU, ACT_SRELU, ACT_SWIGLU, GROUP_ALIGN, INTERLEAVE, MX_BLOCK,
+    PERMUTE_BUILD_MAP, PERMUTE_GATHER, PERMUTE_WRITE_MX, PREC_BF16,
+    PREC_MXFP8, QUANT_COL, QUANT_ROW, MoeError, act_params, lib, lib_path,
+    moe_grouped_mlp_bwd, moe_grouped_mlp_fwd, moe_grouped_mlp_workspace_size,
+    moe_permute, moe_permute_workspace_size, moe_quantize_mxfp8,
+    moe_unpermute, moe_weight_repack_interleave, EXPORTED_SYMBOLS,
+)
+from .block import ExpertBlock  # noqa: F401

@@ -1,0 +1,247 @@
+"""ctypes binding of libmoe_gmlp.so: one Python function per C entry point,
+with the same name and arguments.  Tensors are passed as device pointers
+(``tensor.data_ptr()``) and the stream defaults to torch's current stream.
+The functions only marshal arguments; all work runs in the HIP kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from ctypes import c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(HERE, "libmoe_gmlp.so")
+
+# ---- constants mirrored from include/moe_gmlp.h ---------------------------
+ACT_SWIGLU, ACT_GEGLU, ACT_SRELU = 0, 1, 2
+PREC_BF16, PREC_MXFP8 = 0, 1
+PERMUTE_BUILD_MAP, PERMUTE_GATHER, PERMUTE_WRITE_MX = 0x1, 0x2, 0x4
+QUANT_ROW, QUANT_COL = 0, 1
+GROUP_ALIGN = 128
+INTERLEAVE = 64
+MX_BLOCK = 32
+DEVERR_MCAP_OVERFLOW, DEVERR_DUP_EXPERT = 0x1, 0x2
+
+EXPORTED_SYMBOLS = (
+    "moe_weight_repack_interleave", "moe_permute_workspace_size",
+    "moe_permute", "moe_unpermute", "moe_quantize_mxfp8",
+    "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd",
+    "moe_grouped_mlp_workspace_size", "moe_status_string", "moe_gmlp_version",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {text} (status {status})")
+        self.status = status
+
+
+# ---- argument structs (layout of include/moe_gmlp.h) ----------------------
+class ActParams(ctypes.Structure):
+    _fields_ = [("act", c_int32), ("beta", c_float), ("gate_lo", c_float),
+                ("gate_hi", c_float), ("lin_lo", c_float), ("lin_hi", c_float),
+                ("lin_offset", c_float)]
+
+
+class PermuteArgs(ctypes.Structure):
+    _fields_ = [("flags", c_int32), ("T", c_int32), ("k", c_int32),
+                ("E", c_int32), ("first_expert", c_int32), ("H", c_int32),
+                ("M_cap", c_int64),
+                ("expert_idx", c_void_p), ("probs", c_void_p),
+                ("split_sizes", c_void_p), ("offsets", c_void_p),
+                ("padded_offsets", c_void_p), ("row_id_map", c_void_p),
+                ("row_src", c_void_p), ("probs_p", c_void_p),
+                ("x", c_void_p), ("xp", c_void_p), ("xp_q", c_void_p),
+                ("xp_s", c_void_p), ("err_flag", c_void_p),
+                ("workspace", c_void_p), ("workspace_bytes", c_size_t)]
+
+
+class UnpermuteArgs(ctypes.Structure):
+    _fields_ = [("T", c_int32), ("k", c_int32), ("H", c_int32),
+                ("M_cap", c_int64), ("row_id_map", c_void_p), ("yp", c_void_p),
+                ("out", c_void_p), ("dprobs_p", c_void_p),
+                ("dprobs", c_void_p)]
+
+
+class QuantArgs(ctypes.Structure):
+    _fields_ = [("mode", c_int32), ("batch", c_int32), ("rows", c_int32),
+                ("cols", c_int32), ("x_stride", c_int64), ("x", c_void_p),
+                ("q", c_void_p), ("s", c_void_p), ("amax", c_void_p)]
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [("E", c_int32), ("H", c_int32), ("I", c_int32),
+                ("M_cap", c_int64), ("prec", c_int32), ("act", ActParams),
+                ("cu_margin", c_int32), ("split_sizes", c_void_p),
+                ("padded_offsets", c_void_p), ("probs_p", c_void_p),
+                ("xp", c_void_p), ("w1i", c_void_p), ("w2", c_void_p),
+                ("w1_stride", c_int64), ("w2_stride", c_int64),
+                ("z", c_void_p), ("a", c_void_p), ("amax", c_void_p),
+                ("yp", c_void_p), ("err_flag", c_void_p),
+                ("timing_events", c_void_p * 3)]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [("E", c_int32), ("H", c_int32), ("I", c_int32),
+                ("M_cap", c_int64), ("prec", c_int32), ("act", ActParams),
+                ("cu_margin", c_int32), ("split_sizes", c_void_p),
+                ("padded_offsets", c_void_p), ("probs_p", c_void_p),
+                ("dyp", c_void_p), ("w2", c_void_p), ("z", c_void_p),
+                ("w1i", c_void_p), ("w1_stride", c_int64),
+                ("w2_stride", c_int64), ("dz", c_void_p),
+                ("dprobs_p", c_void_p), ("dxp", c_void_p),
+                ("err_flag", c_void_p), ("workspace", c_void_p),
+                ("workspace_bytes", c_size_t),
+                ("timing_events", c_void_p * 3)]
+
+
+# ---- library loading ------------------------------------------------------
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library.  Raises if it is not built: there is no
+    other implementation to fall back to."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(lib_path):
+            raise ImportError(
+                f"{lib_path} is missing: build it with "
+                "`python -m moe_grouped_mlp_amd.build`")
+        L = ctypes.CDLL(lib_path)
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [c_int]
+        L.moe_gmlp_version.restype = c_int
+        L.moe_weight_repack_interleave.restype = c_int
+        L.moe_weight_repack_interleave.argtypes = [
+            c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_void_p]
+        L.moe_permute_workspace_size.restype = c_size_t
+        L.moe_permute_workspace_size.argtypes = [c_int, c_int]
+        L.moe_grouped_mlp_workspace_size.restype = c_size_t
+        L.moe_grouped_mlp_workspace_size.argtypes = [
+            c_int, c_int, c_int, c_int64, c_int, c_int]
+        for name, st in (("moe_permute", PermuteArgs),
+                         ("moe_unpermute", UnpermuteArgs),
+                         ("moe_quantize_mxfp8", QuantArgs),
+                         ("moe_grouped_mlp_fwd", FwdArgs),
+                         ("moe_grouped_mlp_bwd", BwdArgs)):
+            f = getattr(L, name)
+            f.restype = c_int
+            f.argtypes = [ctypes.POINTER(st), c_void_p]
+        _LIB = L
+    return _LIB
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MoeError(fn, status, lib().moe_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _events(evs):
+    arr = (c_void_p * 3)()
+    for i, e in enumerate(evs or ()):
+        if e is not None:
+            arr[i] = e if isinstance(e, int) else e.cuda_event
+    return arr
+
+
+def act_params(act: int = ACT_SWIGLU, beta: float = 1.0,
+               clamp: float | None = None, gate_lo: float = -math.inf,
+               gate_hi: float = math.inf, lin_lo: float = -math.inf,
+               lin_hi: float = math.inf, lin_offset: float = 0.0) -> ActParams:
+    if clamp is not None:
+        gate_lo, gate_hi, lin_lo, lin_hi = -clamp, clamp, -clamp, clamp
+    return ActParams(act, beta, gate_lo, gate_hi, lin_lo, lin_hi, lin_offset)
+
+
+# ---- entry points ---------------------------------------------------------
+def moe_weight_repack_interleave(w1, w1i, E, I, H, block=INTERLEAVE,
+                                 inverse=False, stream=None):
+    _check("moe_weight_repack_interleave",
+           lib().moe_weight_repack_interleave(_ptr(w1), _ptr(w1i), E, I, H,
+                                              block, int(bool(inverse)),
+                                              _stream(stream)))
+
+
+def moe_permute_workspace_size(T, E) -> int:
+    return lib().moe_permute_workspace_size(T, E)
+
+
+def moe_permute(*, flags, T, k, E, H, M_cap, split_sizes, padded_offsets,
+                row_id_map, first_expert=0, expert_idx=None, probs=None,
+                offsets=None, row_src=None, probs_p=None, x=None, xp=None,
+                xp_q=None, xp_s=None, err_flag=None, workspace=None,
+                stream=None):
+    a = PermuteArgs(flags, T, k, E, first_expert, H, M_cap, _ptr(expert_idx),
+                    _ptr(probs), _ptr(split_sizes), _ptr(offsets),
+                    _ptr(padded_offsets), _ptr(row_id_map), _ptr(row_src),
+                    _ptr(probs_p), _ptr(x), _ptr(xp), _ptr(xp_q), _ptr(xp_s),
+                    _ptr(err_flag), _ptr(workspace), _nbytes(workspace))
+    _check("moe_permute", lib().moe_permute(ctypes.byref(a), _stream(stream)))
+
+
+def moe_unpermute(*, T, k, H, M_cap, row_id_map, yp, out, dprobs_p=None,
+                  dprobs=None, stream=None):
+    a = UnpermuteArgs(T, k, H, M_cap, _ptr(row_id_map), _ptr(yp), _ptr(out),
+                      _ptr(dprobs_p), _ptr(dprobs))
+    _check("moe_unpermute",
+           lib().moe_unpermute(ctypes.byref(a), _stream(stream)))
+
+
+def moe_quantize_mxfp8(*, mode, batch, rows, cols, x, q, s, x_stride=0,
+                       amax=None, stream=None):
+    a = QuantArgs(mode, batch, rows, cols, x_stride, _ptr(x), _ptr(q), _ptr(s),
+                  _ptr(amax))
+    _check("moe_quantize_mxfp8",
+           lib().moe_quantize_mxfp8(ctypes.byref(a), _stream(stream)))
+
+
+def moe_grouped_mlp_workspace_size(E, H, I, M_cap, prec=PREC_BF16,
+                                   act=ACT_SWIGLU) -> int:
+    return lib().moe_grouped_mlp_workspace_size(E, H, I, M_cap, prec, act)
+
+
+def moe_grouped_mlp_fwd(*, E, H, I, M_cap, split_sizes, padded_offsets,
+                        probs_p, xp, w1i, w2, a, yp, z=None, amax=None,
+                        act=None, prec=PREC_BF16, cu_margin=0, w1_stride=0,
+                        w2_stride=0, err_flag=None, timing_events=None,
+                        stream=None):
+    args = FwdArgs(E, H, I, M_cap, prec, act or act_params(), cu_margin,
+                   _ptr(split_sizes), _ptr(padded_offsets), _ptr(probs_p),
+                   _ptr(xp), _ptr(w1i), _ptr(w2), w1_stride, w2_stride,
+                   _ptr(z), _ptr(a), _ptr(amax), _ptr(yp), _ptr(err_flag),
+                   _events(timing_events))
+    _check("moe_grouped_mlp_fwd",
+           lib().moe_grouped_mlp_fwd(ctypes.byref(args), _stream(stream)))
+
+
+def moe_grouped_mlp_bwd(*, E, H, I, M_cap, split_sizes, padded_offsets,
+                        probs_p, dyp, w2, z, w1i, dz, dprobs_p, dxp,
+                        workspace, act=None, prec=PREC_BF16, cu_margin=0,
+                        w1_stride=0, w2_stride=0, err_flag=None,
+                        timing_events=None, stream=None):
+    args = BwdArgs(E, H, I, M_cap, prec, act or act_params(), cu_margin,
+                   _ptr(split_sizes), _ptr(padded_offsets), _ptr(probs_p),
+                   _ptr(dyp), _ptr(w2), _ptr(z), _ptr(w1i), w1_stride,
+                   w2_stride, _ptr(dz), _ptr(dprobs_p), _ptr(dxp),
+                   _ptr(err_flag), _ptr(workspace), _nbytes(workspace),
+                   _events(timing_events))
+    _check("moe_grouped_mlp_bwd",
+           lib().moe_grouped_mlp_bwd(ctypes.byref(args), _stream(stream)))

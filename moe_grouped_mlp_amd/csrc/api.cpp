@@ -1,0 +1,324 @@
+// C ABI of the fused grouped-MLP expert block: argument validation, launch
+// configuration and launch order.  Nothing here allocates device memory,
+// copies to the host or synchronises; every call only enqueues kernels on
+// the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/moe_gmlp.h"
+#include "kernels.h"
+
+namespace {
+
+using moe::kMaxExperts;
+using moe::kMaxTopK;
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  std::atomic<int> state{0};  // 0 unknown, 1 ok, -1 unusable
+  int cu_count = 0;
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+// Attributes of the current device, looked up once per device.
+moe_status device_info(int* cu_count) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_DEVICE;
+  DeviceInfo& d = g_dev[dev];
+  int st = d.state.load(std::memory_order_acquire);
+  if (st == 0) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    st = d.state.load(std::memory_order_relaxed);
+    if (st == 0) {
+      hipDeviceProp_t prop;
+      st = -1;
+      if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+          std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) {
+        d.cu_count = prop.multiProcessorCount;
+        st = 1;
+      }
+      d.state.store(st, std::memory_order_release);
+    }
+  }
+  if (st != 1) return MOE_ERR_DEVICE;
+  *cu_count = d.cu_count;
+  return MOE_OK;
+}
+
+moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+bool act_ok(const moe_act_params& a) {
+  if (a.act != MOE_ACT_SWIGLU && a.act != MOE_ACT_GEGLU && a.act != MOE_ACT_SRELU) return false;
+  if (std::isnan(a.beta) || std::isnan(a.gate_lo) || std::isnan(a.gate_hi) ||
+      std::isnan(a.lin_lo) || std::isnan(a.lin_hi) || !std::isfinite(a.lin_offset))
+    return false;
+  return a.gate_lo <= a.gate_hi && a.lin_lo <= a.lin_hi;
+}
+
+void record(void* ev, hipStream_t s) {
+  if (ev) (void)hipEventRecord(static_cast<hipEvent_t>(ev), s);
+}
+
+// Persistent grid: all CUs but the margin, a multiple of the XCD count so
+// the tile-id remap applies, no more than the tiles that can exist.
+int gemm_grid(int cu_count, int cu_margin, int64_t M_cap, int E, int N) {
+  int g = cu_count - cu_margin;
+  if (g >= 8) g -= g % 8;
+  const int bm = moe::grouped_gemm_tile_m(), bn = moe::grouped_gemm_tile_n();
+  const int64_t ub = ((M_cap + bm - 1) / bm + E) * ((N + bn - 1) / bn);
+  if (ub < g) g = static_cast<int>(ub);
+  return g < 1 ? 1 : g;
+}
+
+int64_t dgrad_parts(int I) {
+  const int bn = moe::grouped_gemm_tile_n();
+  return (I + bn - 1) / bn;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    case MOE_ERR_DEVICE: return "no usable gfx950 device";
+  }
+  return "unknown status";
+}
+
+int moe_gmlp_version(void) { return 100; }
+
+moe_status moe_weight_repack_interleave(const void* w1, void* w1i, int E, int I, int H,
+                                        int block, int inverse, void* stream) {
+  if (!w1 || !w1i || w1 == w1i || E < 1 || I < 1 || H < 8 || H % 8 != 0 ||
+      block != MOE_INTERLEAVE || I % block != 0)
+    return MOE_ERR_INVALID_ARG;
+  int cu = 0;
+  if (moe_status st = device_info(&cu)) return st;
+  return launched(moe::launch_repack_interleave(w1, w1i, E, I, H, block, inverse,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_permute_workspace_size(int T, int E) {
+  if (T < 0 || E < 1) return 0;
+  const int64_t chunks = (static_cast<int64_t>(T) + moe::kRouteChunk - 1) / moe::kRouteChunk;
+  return static_cast<size_t>(chunks * E * sizeof(int32_t));
+}
+
+moe_status moe_permute(const moe_permute_args* a, void* stream) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  const int known = MOE_PERMUTE_BUILD_MAP | MOE_PERMUTE_GATHER | MOE_PERMUTE_WRITE_MX;
+  if (a->flags == 0 || (a->flags & ~known)) return MOE_ERR_INVALID_ARG;
+  if (a->T < 0 || a->k < 1 || a->k > kMaxTopK || a->E < 1 || a->E > kMaxExperts ||
+      a->M_cap < 0 || a->M_cap > INT32_MAX)
+    return MOE_ERR_INVALID_ARG;
+  if (!a->split_sizes || !a->padded_offsets || !a->row_id_map) return MOE_ERR_INVALID_ARG;
+  const bool build = a->flags & MOE_PERMUTE_BUILD_MAP;
+  const bool gather = a->flags & MOE_PERMUTE_GATHER;
+  if (a->flags & MOE_PERMUTE_WRITE_MX) return MOE_ERR_UNSUPPORTED;
+  if (build) {
+    if (!a->expert_idx || !a->probs || !a->row_src || !a->probs_p) return MOE_ERR_INVALID_ARG;
+    if (!a->workspace || a->workspace_bytes < moe_permute_workspace_size(a->T, a->E))
+      return MOE_ERR_WORKSPACE;
+  }
+  if (gather && (!a->x || !a->xp || a->H < 8 || a->H % 8 != 0)) return MOE_ERR_INVALID_ARG;
+  int cu = 0;
+  if (moe_status st = device_info(&cu)) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (build) {
+    if (moe_status st = launched(moe::launch_route(*a, s))) return st;
+  }
+  if (gather) {
+    if (moe_status st = launched(moe::launch_gather(*a, s))) return st;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_unpermute(const moe_unpermute_args* a, void* stream) {
+  if (!a || a->T < 0 || a->k < 1 || a->k > kMaxTopK || a->H < 8 || a->H % 8 != 0 ||
+      a->M_cap < 0 || !a->row_id_map || !a->yp || !a->out)
+    return MOE_ERR_INVALID_ARG;
+  if ((a->dprobs != nullptr) != (a->dprobs_p != nullptr)) return MOE_ERR_INVALID_ARG;
+  int cu = 0;
+  if (moe_status st = device_info(&cu)) return st;
+  if (a->T == 0) return MOE_OK;
+  return launched(moe::launch_unpermute(*a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_quantize_mxfp8(const moe_quant_args* a, void* stream) {
+  (void)stream;
+  if (!a) return MOE_ERR_INVALID_ARG;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+size_t moe_grouped_mlp_workspace_size(int E, int H, int I, int64_t M_cap, int prec, int act) {
+  (void)E;
+  (void)H;
+  (void)prec;
+  (void)act;
+  if (I < 1 || M_cap < 0) return 0;
+  return static_cast<size_t>(M_cap * dgrad_parts(I) * sizeof(float));
+}
+
+// Host-side checks shared by the forward and the backward (no HIP calls, so
+// they answer without a device).
+static moe_status check_common(int E, int H, int I, int64_t M_cap, int prec,
+                               const moe_act_params& act, int cu_margin,
+                               const int32_t* split, const int32_t* padded,
+                               const float* probs_p) {
+  if (E < 1 || E > kMaxExperts || H < 64 || I < 64 || H % 64 != 0 || I % 64 != 0 ||
+      M_cap < 1 || M_cap > INT32_MAX || !act_ok(act) || cu_margin < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (!split || !padded || !probs_p) return MOE_ERR_INVALID_ARG;
+  if (prec == MOE_PREC_MXFP8) return MOE_ERR_UNSUPPORTED;
+  if (prec != MOE_PREC_BF16) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  if (moe_status st = check_common(a->E, a->H, a->I, a->M_cap, a->prec, a->act, a->cu_margin,
+                                   a->split_sizes, a->padded_offsets, a->probs_p))
+    return st;
+  if (!a->xp || !a->w1i || !a->w2 || !a->a || !a->yp) return MOE_ERR_INVALID_ARG;
+  const bool gated = a->act.act != MOE_ACT_SRELU;
+  const int N1 = gated ? 2 * a->I : a->I;
+  if (a->w1_stride != 0 && a->w1_stride < static_cast<int64_t>(N1) * a->H) return MOE_ERR_INVALID_ARG;
+  if (a->w2_stride != 0 && a->w2_stride < static_cast<int64_t>(a->H) * a->I) return MOE_ERR_INVALID_ARG;
+  int cu = 0;
+  if (moe_status st = device_info(&cu)) return st;
+  if (a->cu_margin >= cu) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (a->amax) {
+    if (moe_status st = launched(moe::launch_fill_f32(a->amax, 0.0f, 1, s))) return st;
+  }
+  moe::GemmArgs g{};
+  g.E = a->E;
+  g.M_cap = a->M_cap;
+  g.split = a->split_sizes;
+  g.padded = a->padded_offsets;
+  g.group_m = 8;
+  g.probs = a->probs_p;
+  g.act = moe::to_actp(a->act);
+
+  // FC1: z = xp . W1i^T with the activation epilogue
+  g.N = N1;
+  g.K = a->H;
+  g.A = static_cast<const uint16_t*>(a->xp);
+  g.B = static_cast<const uint16_t*>(a->w1i);
+  g.b_stride = a->w1_stride ? a->w1_stride : static_cast<int64_t>(N1) * a->H;
+  g.C = static_cast<uint16_t*>(a->z);
+  g.ldc = N1;
+  g.act_out = static_cast<uint16_t*>(a->a);
+  g.ld_act = a->I;
+  g.amax = a->amax;
+  record(a->timing_events[0], s);
+  if (moe_status st = launched(moe::launch_grouped_gemm(
+          g, moe::EPI_GLU, false, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, g.N), s)))
+    return st;
+  record(a->timing_events[1], s);
+
+  // FC2: yp = a . W2^T
+  moe::GemmArgs f = g;
+  f.N = a->H;
+  f.K = a->I;
+  f.A = static_cast<const uint16_t*>(a->a);
+  f.B = static_cast<const uint16_t*>(a->w2);
+  f.b_stride = a->w2_stride ? a->w2_stride : static_cast<int64_t>(a->H) * a->I;
+  f.C = static_cast<uint16_t*>(a->yp);
+  f.ldc = a->H;
+  f.act_out = nullptr;
+  f.amax = nullptr;
+  if (moe_status st = launched(moe::launch_grouped_gemm(
+          f, moe::EPI_STORE, false, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, f.N), s)))
+    return st;
+  record(a->timing_events[2], s);
+  return MOE_OK;
+}
+
+moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  if (moe_status st = check_common(a->E, a->H, a->I, a->M_cap, a->prec, a->act, a->cu_margin,
+                                   a->split_sizes, a->padded_offsets, a->probs_p))
+    return st;
+  if (!a->dyp || !a->w2 || !a->z || !a->w1i || !a->dz || !a->dprobs_p || !a->dxp)
+    return MOE_ERR_INVALID_ARG;
+  const bool gated = a->act.act != MOE_ACT_SRELU;
+  const int N1 = gated ? 2 * a->I : a->I;
+  if (a->w1_stride != 0 && a->w1_stride < static_cast<int64_t>(N1) * a->H) return MOE_ERR_INVALID_ARG;
+  if (a->w2_stride != 0 && a->w2_stride < static_cast<int64_t>(a->H) * a->I) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_grouped_mlp_workspace_size(a->E, a->H, a->I, a->M_cap, a->prec,
+                                                     a->act.act);
+  if (!a->workspace || a->workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  int cu = 0;
+  if (moe_status st = device_info(&cu)) return st;
+  if (a->cu_margin >= cu) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  moe::GemmArgs g{};
+  g.E = a->E;
+  g.M_cap = a->M_cap;
+  g.split = a->split_sizes;
+  g.padded = a->padded_offsets;
+  g.group_m = 8;
+  g.probs = a->probs_p;
+  g.act = moe::to_actp(a->act);
+
+  // FC2 dgrad: dA = dyp . W2 (W2 [H][I] read as [K=H][N=I]) + dActivation
+  const int n_part = static_cast<int>(dgrad_parts(a->I));
+  g.N = a->I;
+  g.K = a->H;
+  g.A = static_cast<const uint16_t*>(a->dyp);
+  g.B = static_cast<const uint16_t*>(a->w2);
+  g.b_stride = a->w2_stride ? a->w2_stride : static_cast<int64_t>(a->H) * a->I;
+  g.C = static_cast<uint16_t*>(a->dz);
+  g.ldc = N1;
+  g.zin = static_cast<const uint16_t*>(a->z);
+  g.ldz = N1;
+  g.dp_part = static_cast<float*>(a->workspace);
+  g.n_part = n_part;
+  record(a->timing_events[0], s);
+  if (moe_status st = launched(moe::launch_grouped_gemm(
+          g, moe::EPI_DGLU, true, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, g.N), s)))
+    return st;
+  if (moe_status st = launched(moe::launch_dprobs_reduce(g.dp_part, n_part, a->split_sizes,
+                                                         a->padded_offsets, a->E, a->M_cap,
+                                                         a->dprobs_p, s)))
+    return st;
+  record(a->timing_events[1], s);
+
+  // FC1 dgrad: dxp = dz . W1i (W1i [N1][H] read as [K=N1][N=H])
+  moe::GemmArgs f{};
+  f.E = a->E;
+  f.M_cap = a->M_cap;
+  f.split = a->split_sizes;
+  f.padded = a->padded_offsets;
+  f.group_m = 8;
+  f.act = g.act;
+  f.N = a->H;
+  f.K = N1;
+  f.A = static_cast<const uint16_t*>(a->dz);
+  f.B = static_cast<const uint16_t*>(a->w1i);
+  f.b_stride = a->w1_stride ? a->w1_stride : static_cast<int64_t>(N1) * a->H;
+  f.C = static_cast<uint16_t*>(a->dxp);
+  f.ldc = a->H;
+  if (moe_status st = launched(moe::launch_grouped_gemm(
+          f, moe::EPI_STORE, true, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, f.N), s)))
+    return st;
+  record(a->timing_events[2], s);
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Internal launcher interface between the C ABI (api.cpp) and the gfx950
+// kernels.  All launchers enqueue on `stream` and return hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_gmlp.h"
+
+namespace moe {
+
+constexpr int kMaxExperts = 1024;  // per-call local experts (LDS tables)
+constexpr int kMaxTopK = 8;
+constexpr int kRouteChunk = 256;   // tokens per routing workgroup
+
+// Activation parameters as the kernels see them.
+struct ActP {
+  int act;
+  float beta, glo, ghi, llo, lhi, loff;
+};
+
+inline ActP to_actp(const moe_act_params& a) {
+  return ActP{a.act, a.beta, a.gate_lo, a.gate_hi, a.lin_lo, a.lin_hi, a.lin_offset};
+}
+
+// ---- routing / data movement --------------------------------------------
+hipError_t launch_route(const moe_permute_args& a, hipStream_t s);
+hipError_t launch_gather(const moe_permute_args& a, hipStream_t s);
+hipError_t launch_unpermute(const moe_unpermute_args& a, hipStream_t s);
+hipError_t launch_repack_interleave(const void* src, void* dst, int E, int I,
+                                    int H, int block, int inverse, hipStream_t s);
+hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
+
+// ---- grouped GEMM --------------------------------------------------------
+enum Epi { EPI_STORE = 0, EPI_GLU = 1, EPI_DGLU = 2 };
+
+struct GemmArgs {
+  int E, N, K;
+  int64_t M_cap;
+  const int32_t* split;
+  const int32_t* padded;
+  const uint16_t* A;     // [M_cap][K] bf16
+  const uint16_t* B;     // per expert: B_NT [N][K], B_NN [K][N]
+  int64_t b_stride;      // elements between experts of B
+  int group_m;           // m-tiles per band of the tile order
+  // epilogue
+  uint16_t* C;           // STORE: out [M_cap][N]; GLU: z (nullable); DGLU: dz
+  int64_t ldc;
+  uint16_t* act_out;     // GLU: a [M_cap][ld_act]
+  int64_t ld_act;
+  const float* probs;    // GLU, DGLU: probs_p [M_cap]
+  float* amax;           // GLU (nullable)
+  const uint16_t* zin;   // DGLU: z [M_cap][ldz]
+  int64_t ldz;
+  float* dp_part;        // DGLU: [M_cap][n_part]
+  int n_part;
+  ActP act;
+};
+
+hipError_t launch_grouped_gemm(const GemmArgs& g, int epi, bool b_nn,
+                               int grid, hipStream_t s);
+int grouped_gemm_tile_n();  // BN of the launched configuration
+int grouped_gemm_tile_m();  // BM
+hipError_t launch_dprobs_reduce(const float* part, int n_part, const int32_t* split,
+                                const int32_t* padded, int E, int64_t M_cap,
+                                float* dprobs_p, hipStream_t s);
+
+}  // namespace moe

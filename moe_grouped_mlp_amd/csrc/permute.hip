@@ -1,0 +1,168 @@
+// Token data movement of the expert block (HBM-bound, no MFMA):
+//   gather     Xp[row_id_map[t][s]] = X[t]: each token row is read once and
+//              written to each of its local slots (push form), in 16-byte
+//              vectors, one wave per row; pad rows of every group are zeroed.
+//   unpermute  out[t] = bf16(sum_s Yp[row_id_map[t][s]]) in fp32, slot order:
+//              the index-add combine of the per-expert loop (TE + BioNeMo
+//              Mixtral tutorial, § "Challenge 1: fragmented expert kernels")
+//              in gather form, so no atomics and a deterministic result.
+//   repack     row permutation of the FC1 weight into gate/up blocks
+//              ("Boosting MoE Training Throughput with Advanced Fusion
+//              Kernels", § "Optimizing GLU activations with fused GEMM
+//              epilogues", Fig. 2).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kRowsPerBlock = kBlock / kWave;
+
+// ------------------------------------------------------------- gather ---
+__global__ __launch_bounds__(kBlock) void gather_kernel(
+    const i32x4* __restrict__ x, int T, int k, int H8, const int32_t* __restrict__ row_id_map,
+    int64_t M_cap, i32x4* __restrict__ xp, int tok_blocks,
+    const int32_t* __restrict__ split, const int32_t* __restrict__ padded, int E) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (static_cast<int>(blockIdx.x) < tok_blocks) {
+    for (int t = blockIdx.x * kRowsPerBlock + wave; t < T; t += tok_blocks * kRowsPerBlock) {
+      int rows[kMaxTopK];
+      for (int s = 0; s < kMaxTopK; ++s)
+        rows[s] = s < k ? row_id_map[static_cast<int64_t>(t) * k + s] : -1;
+      const i32x4* src = x + static_cast<int64_t>(t) * H8;
+      for (int c = lane; c < H8; c += kWave) {
+        const i32x4 v = src[c];
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s)
+          if (rows[s] >= 0 && rows[s] < M_cap) xp[static_cast<int64_t>(rows[s]) * H8 + c] = v;
+      }
+    }
+    return;
+  }
+  // pad rows: [padded[e] + split[e], padded[e+1]) for every expert
+  const int pb = blockIdx.x - tok_blocks;
+  const int n_pb = gridDim.x - tok_blocks;
+  const i32x4 zero = {0, 0, 0, 0};
+  for (int e = pb; e < E; e += n_pb) {
+    const int64_t r0 = static_cast<int64_t>(padded[e]) + split[e];
+    const int64_t r1 = min(static_cast<int64_t>(padded[e + 1]), M_cap);
+    for (int64_t r = r0 + wave; r < r1; r += kRowsPerBlock) {
+      i32x4* dst = xp + r * H8;
+      for (int c = lane; c < H8; c += kWave) dst[c] = zero;
+    }
+  }
+}
+
+// ---------------------------------------------------------- unpermute ---
+__global__ __launch_bounds__(kBlock) void unpermute_kernel(
+    const i32x4* __restrict__ yp, int T, int k, int H8, int64_t M_cap,
+    const int32_t* __restrict__ row_id_map, i32x4* __restrict__ out,
+    const float* __restrict__ dprobs_p, float* __restrict__ dprobs) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int t = blockIdx.x * kRowsPerBlock + wave; t < T; t += gridDim.x * kRowsPerBlock) {
+    int rows[kMaxTopK];
+    for (int s = 0; s < kMaxTopK; ++s) {
+      int r = s < k ? row_id_map[static_cast<int64_t>(t) * k + s] : -1;
+      rows[s] = (r >= 0 && r < M_cap) ? r : -1;
+    }
+    if (dprobs && lane < k) {
+      int r = -1;
+      for (int s = 0; s < kMaxTopK; ++s) if (s == lane) r = rows[s];
+      dprobs[static_cast<int64_t>(t) * k + lane] = r >= 0 ? dprobs_p[r] : 0.0f;
+    }
+    for (int c = lane; c < H8; c += kWave) {
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < kMaxTopK; ++s) {
+        if (rows[s] < 0) continue;
+        const i32x4 v = yp[static_cast<int64_t>(rows[s]) * H8 + c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = static_cast<uint32_t>(v[i]);
+          acc[2 * i] += __uint_as_float(w << 16);
+          acc[2 * i + 1] += __uint_as_float(w & 0xffff0000u);
+        }
+      }
+      i32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = static_cast<int>(pack_bf16x2(acc[2 * i], acc[2 * i + 1]));
+      out[static_cast<int64_t>(t) * H8 + c] = o;
+    }
+  }
+}
+
+// ------------------------------------------------------------- repack ---
+// dst row p of expert e <- src row logical(p) (forward) or the reverse.
+__global__ __launch_bounds__(kBlock) void repack_kernel(
+    const i32x4* __restrict__ src, i32x4* __restrict__ dst, int E, int I, int H8, int blk,
+    int inverse) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t rows = static_cast<int64_t>(E) * 2 * I;
+  for (int64_t gr = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave; gr < rows;
+       gr += static_cast<int64_t>(gridDim.x) * kRowsPerBlock) {
+    const int e = static_cast<int>(gr / (2 * I));
+    const int p = static_cast<int>(gr % (2 * I));  // packed row
+    const int b = p / (2 * blk), w = p % (2 * blk);
+    const int logical = (w < blk) ? b * blk + w : I + b * blk + (w - blk);
+    const int64_t base = static_cast<int64_t>(e) * 2 * I;
+    const int64_t s_row = base + (inverse ? p : logical);
+    const int64_t d_row = base + (inverse ? logical : p);
+    const i32x4* s = src + s_row * H8;
+    i32x4* d = dst + d_row * H8;
+    for (int c = lane; c < H8; c += kWave) d[c] = s[c];
+  }
+}
+
+__global__ void fill_f32_kernel(float* p, float v, int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+int blocks_for(int64_t rows, int cap) {
+  int64_t b = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (b > cap) b = cap;
+  return b < 1 ? 1 : static_cast<int>(b);
+}
+
+}  // namespace
+
+hipError_t launch_gather(const moe_permute_args& a, hipStream_t s) {
+  const int H8 = a.H / 8;
+  const int tok_blocks = blocks_for(a.T, 2048);
+  const int pad_blocks = a.E < 256 ? a.E : 256;
+  gather_kernel<<<tok_blocks + pad_blocks, kBlock, 0, s>>>(
+      static_cast<const i32x4*>(a.x), a.T, a.k, H8, a.row_id_map, a.M_cap,
+      static_cast<i32x4*>(a.xp), tok_blocks, a.split_sizes, a.padded_offsets, a.E);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute(const moe_unpermute_args& a, hipStream_t s) {
+  const int H8 = a.H / 8;
+  unpermute_kernel<<<blocks_for(a.T, 2048), kBlock, 0, s>>>(
+      static_cast<const i32x4*>(a.yp), a.T, a.k, H8, a.M_cap, a.row_id_map,
+      static_cast<i32x4*>(a.out), a.dprobs_p, a.dprobs);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_interleave(const void* src, void* dst, int E, int I, int H, int block,
+                                    int inverse, hipStream_t s) {
+  const int64_t rows = static_cast<int64_t>(E) * 2 * I;
+  repack_kernel<<<blocks_for(rows, 4096), kBlock, 0, s>>>(static_cast<const i32x4*>(src),
+                                                          static_cast<i32x4*>(dst), E, I, H / 8,
+                                                          block, inverse);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s) {
+  int64_t b = (n + 255) / 256;
+  if (b > 1024) b = 1024;
+  if (b < 1) b = 1;
+  fill_f32_kernel<<<static_cast<int>(b), 256, 0, s>>>(p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

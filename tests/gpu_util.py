@@ -1,0 +1,141 @@
+"""Helpers shared by the GPU parity tests: moving seeded inputs to the
+device, running the HIP path through the C ABI, and comparing with the
+oracle at the stated tolerances."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import moe_grouped_mlp_amd as mg
+from oracle import moe as om
+from oracle import numerics as nu
+
+RTOL, ATOL = 2e-2, 1e-2          # bf16 outputs against the fp64 oracle
+REL_ATOL = 1e-2                  # absolute slack relative to the tensor RMS
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.cuda().view(torch.bfloat16)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return nu.bf16_to_f64(host_bits(t))
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def assert_close(gpu, ora, what, rtol=RTOL, atol=ATOL, rel_atol=REL_ATOL):
+    """The stated bar (|d| <= atol + rtol |ref|) and a scale-aware one
+    (|d| <= rel_atol * rms(ref) + rtol |ref|), so small-magnitude tensors
+    are not waved through by the absolute term."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ora = np.asarray(ora, dtype=np.float64)
+    assert gpu.shape == ora.shape, (what, gpu.shape, ora.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU values"
+    d = np.abs(gpu - ora)
+    rms = float(np.sqrt(np.mean(ora * ora))) if ora.size else 0.0
+    ok1 = d <= atol + rtol * np.abs(ora)
+    ok2 = d <= rel_atol * rms + rtol * np.abs(ora)
+    bad = ~(ok1 & ok2)
+    if bad.any():
+        i = np.flatnonzero(bad.reshape(-1))[:5]
+        raise AssertionError(
+            f"{what}: {bad.sum()} of {bad.size} outside tolerance; rms={rms:.3e} "
+            f"max|d|={d.max():.3e}; first gpu={gpu.reshape(-1)[i]} "
+            f"oracle={ora.reshape(-1)[i]}")
+
+
+def act_of(wl, prm_override=None):
+    """(binding ActParams, oracle ActParams) for a workload."""
+    kind = {"swiglu": mg.ACT_SWIGLU, "geglu": mg.ACT_GEGLU,
+            "srelu": mg.ACT_SRELU}[wl.act]
+    c = wl.clamp
+    gp = mg.act_params(kind, beta=wl.beta, clamp=c)
+    op = om.ActParams.clamped(c, beta=wl.beta, act=wl.act)
+    return gp, op
+
+
+def run_gpu_layer(wl, M_cap=None, backward=True, block=None):
+    """Run the HIP path on a workload; returns (block, host results)."""
+    gp, _ = act_of(wl)
+    blk = block or mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, act=gp,
+                                  first_expert=wl.first_expert, M_cap=M_cap)
+    w1 = dev_bf16(wl.w1)
+    w2 = dev_bf16(wl.w2)
+    blk.load_weights(w1, w2)
+    x = dev_bf16(wl.x)
+    idx = torch.from_numpy(wl.expert_idx.astype(np.int32)).cuda()
+    probs = torch.from_numpy(wl.probs.astype(np.float32)).cuda()
+    blk.forward(x, idx, probs)
+    if backward:
+        blk.backward(dev_bf16(wl.dout))
+    torch.cuda.synchronize()
+    return blk
+
+
+def uninterleave_cols(packed: np.ndarray, I: int) -> np.ndarray:
+    """Packed (gate/up interleaved) columns -> logical gate|up columns."""
+    src = om.interleave_rows(I)
+    out = np.empty_like(packed)
+    out[..., src] = packed
+    return out
+
+
+def oracle_layer(wl, M_cap, backward=True):
+    _, op = act_of(wl)
+    fw = om.forward(wl.x, wl.w1, wl.w2, wl.expert_idx, wl.probs, wl.E, op,
+                    first_expert=wl.first_expert, M_cap=M_cap)
+    bw = om.backward(fw, wl.dout, wl.w1, wl.w2, op) if backward else None
+    return fw, bw
+
+
+def compare_routing(blk, rt):
+    np.testing.assert_array_equal(blk.split_sizes.cpu().numpy(), rt.split_sizes)
+    np.testing.assert_array_equal(blk.offsets.cpu().numpy(), rt.offsets)
+    np.testing.assert_array_equal(blk.padded_offsets.cpu().numpy(),
+                                  rt.padded_offsets)
+    np.testing.assert_array_equal(blk.row_id_map.cpu().numpy(), rt.row_id_map)
+    np.testing.assert_array_equal(blk.row_src.cpu().numpy(), rt.row_src)
+    np.testing.assert_array_equal(blk.probs_p.cpu().numpy(), rt.probs_p)
+
+
+def compare_layer(blk, wl, fw, bw):
+    """Element-by-element comparison of every stored tensor of the step."""
+    compare_routing(blk, fw.rt)
+    mp = int(fw.rt.padded_offsets[-1])
+    valid = fw.expert >= 0
+    # permuted input: bit-exact, pad rows zero
+    np.testing.assert_array_equal(host_bits(blk.xp)[:mp],
+                                  nu.f64_to_bf16_bits(fw.xp[:mp]))
+    gated = wl.act != "srelu"
+    z = host_f64(blk.z)[valid]
+    if gated:
+        z = uninterleave_cols(z, wl.I)
+    assert_close(z, fw.z[valid], "z")
+    a_gpu = host_f64(blk.a)[valid]
+    assert_close(a_gpu, fw.a[valid], "a")
+    amax = float(blk.amax.cpu()[0])
+    assert amax == np.abs(a_gpu).max()
+    assert abs(amax - fw.amax) <= 2.0 ** -7 * fw.amax + 1e-30
+    assert_close(host_f64(blk.yp)[valid], fw.y[valid], "yp")
+    assert_close(host_f64(blk.out), fw.out, "out")
+    if bw is None:
+        return
+    np.testing.assert_array_equal(host_bits(blk.dyp)[valid],
+                                  nu.f64_to_bf16_bits(bw.dyp[valid]))
+    dz = host_f64(blk.dz)[valid]
+    if gated:
+        dz = uninterleave_cols(dz, wl.I)
+    assert_close(dz, bw.dz[valid], "dz")
+    dp = blk.dprobs_p.cpu().numpy().astype(np.float64)
+    assert_close(dp[valid], bw.dp[valid], "dprobs_p")
+    assert np.all(dp[:mp][~valid[:mp]] == 0)
+    assert_close(host_f64(blk.dxp)[valid], bw.dxp[valid], "dxp")
+    assert_close(host_f64(blk.dx), bw.dx, "dx")
+    assert_close(blk.dprobs.cpu().numpy(), bw.dprobs, "dprobs")

@@ -1,0 +1,188 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+* the library loads and exports every function include/moe_gmlp.h declares;
+* the ctypes structs of the binding have the header's layout (sizeof and
+  offsetof of every field, read from a C program built with gcc);
+* argument validation rejects bad calls before touching a device, and a
+  valid call without a gfx950 device reports MOE_ERR_DEVICE.
+"""
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import moe_grouped_mlp_amd as m
+from moe_grouped_mlp_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_gmlp.h")
+
+INVALID, UNSUPPORTED, WORKSPACE, DEVICE = -1, -2, -3, -5
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = m.lib()
+    declared = _header_functions()
+    assert set(declared) == set(B.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", m.lib_path],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_[a-z0-9_]+)", out))
+    assert set(declared) <= exported
+
+
+STRUCTS = {
+    "moe_act_params": B.ActParams,
+    "moe_permute_args": B.PermuteArgs,
+    "moe_unpermute_args": B.UnpermuteArgs,
+    "moe_quant_args": B.QuantArgs,
+    "moe_fwd_args": B.FwdArgs,
+    "moe_bwd_args": B.BwdArgs,
+}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc missing")
+def test_ctypes_structs_match_header_layout(tmp_path):
+    lines = ['#include <stdio.h>', '#include <stddef.h>',
+             f'#include "{HEADER}"', "int main(void) {"]
+    for cname, st in STRUCTS.items():
+        lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for fname, _ in st._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", '
+                         f'offsetof({cname}, {fname}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-o", str(exe), str(src)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True,
+                         check=True).stdout.split("\n")
+    got = {}
+    for line in out:
+        if line:
+            s, f, v = line.split()
+            got[(s, f)] = int(v)
+    for cname, st in STRUCTS.items():
+        assert got[(cname, "sizeof")] == ctypes.sizeof(st), cname
+        for fname, _ in st._fields_:
+            assert got[(cname, fname)] == getattr(st, fname).offset, \
+                (cname, fname)
+
+
+def _call(fn, st):
+    return getattr(m.lib(), fn)(ctypes.byref(st), None)
+
+
+def test_repack_validation():
+    L = m.lib()
+    assert L.moe_weight_repack_interleave(None, 8, 1, 64, 64, 64, 0, None) == INVALID
+    assert L.moe_weight_repack_interleave(8, 8, 1, 64, 64, 64, 0, None) == INVALID   # alias
+    assert L.moe_weight_repack_interleave(8, 16, 1, 96, 64, 64, 0, None) == INVALID  # I % 64
+    assert L.moe_weight_repack_interleave(8, 16, 1, 64, 64, 32, 0, None) == INVALID  # block
+    assert L.moe_weight_repack_interleave(8, 16, 1, 64, 60, 64, 0, None) == INVALID  # H % 8
+    assert L.moe_weight_repack_interleave(8, 16, 1, 64, 64, 64, 0, None) == DEVICE
+
+
+def _permute_args(**kw):
+    a = B.PermuteArgs()
+    a.flags, a.T, a.k, a.E, a.first_expert, a.H, a.M_cap = (
+        B.PERMUTE_BUILD_MAP | B.PERMUTE_GATHER, 16, 2, 4, 0, 64, 16 * 2 + 4 * 127)
+    for f in ("expert_idx", "probs", "split_sizes", "offsets", "padded_offsets",
+              "row_id_map", "row_src", "probs_p", "x", "xp", "workspace"):
+        setattr(a, f, 64)
+    a.workspace_bytes = B.moe_permute_workspace_size(16, 4)
+    for key, v in kw.items():
+        setattr(a, key, v)
+    return a
+
+
+def test_permute_validation():
+    assert _call("moe_permute", _permute_args()) == DEVICE
+    assert _call("moe_permute", _permute_args(flags=0)) == INVALID
+    assert _call("moe_permute", _permute_args(flags=0x10)) == INVALID
+    assert _call("moe_permute", _permute_args(k=9)) == INVALID
+    assert _call("moe_permute", _permute_args(E=0)) == INVALID
+    assert _call("moe_permute", _permute_args(E=1025)) == INVALID
+    assert _call("moe_permute", _permute_args(row_src=None)) == INVALID
+    assert _call("moe_permute", _permute_args(workspace=None)) == WORKSPACE
+    assert _call("moe_permute", _permute_args(workspace_bytes=1)) == WORKSPACE
+    assert _call("moe_permute", _permute_args(H=60)) == INVALID
+    # gather only needs no workspace
+    assert _call("moe_permute", _permute_args(flags=B.PERMUTE_GATHER,
+                                              workspace=None)) == DEVICE
+    assert B.moe_permute_workspace_size(257, 8) == 2 * 8 * 4
+
+
+def _fwd_args(**kw):
+    a = B.FwdArgs()
+    a.E, a.H, a.I, a.M_cap, a.prec = 4, 128, 256, 1024, B.PREC_BF16
+    a.act = B.act_params()
+    for f in ("split_sizes", "padded_offsets", "probs_p", "xp", "w1i", "w2",
+              "z", "a", "yp"):
+        setattr(a, f, 64)
+    for key, v in kw.items():
+        setattr(a, key, v)
+    return a
+
+
+def test_fwd_validation():
+    assert _call("moe_grouped_mlp_fwd", _fwd_args()) == DEVICE
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(H=96)) == INVALID
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(I=100)) == INVALID
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(E=0)) == INVALID
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(a=None)) == INVALID
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(split_sizes=None)) == INVALID
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(prec=7)) == INVALID
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(cu_margin=-1)) == INVALID
+    assert _call("moe_grouped_mlp_fwd",
+                 _fwd_args(act=B.act_params(act=9))) == INVALID
+    assert _call("moe_grouped_mlp_fwd",
+                 _fwd_args(act=B.act_params(gate_lo=1.0, gate_hi=-1.0))) == INVALID
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(w1_stride=5)) == INVALID
+    # z may be NULL (no backward follows)
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(z=None)) == DEVICE
+
+
+def test_bwd_validation():
+    a = B.BwdArgs()
+    a.E, a.H, a.I, a.M_cap, a.prec = 4, 128, 256, 1024, B.PREC_BF16
+    a.act = B.act_params()
+    for f in ("split_sizes", "padded_offsets", "probs_p", "dyp", "w2", "z",
+              "w1i", "dz", "dprobs_p", "dxp", "workspace"):
+        setattr(a, f, 64)
+    need = B.moe_grouped_mlp_workspace_size(4, 128, 256, 1024)
+    assert need == 1024 * 1 * 4   # one partial per 256-column tile of I
+    a.workspace_bytes = need
+    assert _call("moe_grouped_mlp_bwd", a) == DEVICE
+    a.workspace_bytes = need - 1
+    assert _call("moe_grouped_mlp_bwd", a) == WORKSPACE
+    a.workspace_bytes = need
+    a.z = None
+    assert _call("moe_grouped_mlp_bwd", a) == INVALID
+
+
+def test_unpermute_validation():
+    a = B.UnpermuteArgs(8, 2, 64, 100, 64, 64, 64, None, None)
+    assert _call("moe_unpermute", a) == DEVICE
+    a.dprobs = 64          # dprobs without dprobs_p
+    assert _call("moe_unpermute", a) == INVALID
+    a.dprobs, a.H = None, 12
+    assert _call("moe_unpermute", a) == INVALID
+
+
+def test_status_strings():
+    L = m.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.moe_status_string(code)
+    assert L.moe_status_string(-99) == b"unknown status"
