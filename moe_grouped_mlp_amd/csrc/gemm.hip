@@ -10,14 +10,21 @@
 //   * Tile 256 x 256 x 64 (BM x BN x BK), 4 waves of 64 lanes in a 2 x 2
 //     layout, each wave owning a 128 x 128 sub-tile as 4 x 4 blocks of the
 //     v_mfma_f32_32x32x16_bf16 instruction (fp32 accumulators, 256 per lane).
-//   * A (activations, [M][K] K-contiguous) and B (weights) are staged through
-//     registers into a double-buffered LDS tile (2 x 64 KB); one barrier per
-//     K step; the global loads of step k+1 are in flight while step k runs.
+//   * K-contiguous operands (activations A, and the weights of the forward
+//     GEMMs) go from HBM straight into a double-buffered LDS tile
+//     (buffer_load_dwordx4 ... lds, 2 x 64 KB): each lane fetches the 16-byte
+//     chunk that belongs at its LDS slot of the swizzled layout, so no VGPR
+//     staging and no ds_write.  One barrier per K step; the loads of step
+//     k+1 are in flight while step k runs.
+//   * MFMA operands are double-buffered in registers across the four 16-deep
+//     sub-steps of a K step; the last sub-step's MFMAs are issued after the
+//     barrier and after the first operand reads of the next stage, so LDS
+//     latency hides behind matrix work.
 //   * B comes either as [N][K] ("NT": forward GEMMs, W1 and W2 as stored) or
 //     as [K][N] ("NN": the dgrad GEMMs read the same weights along their
-//     other axis).  NN tiles are transposed in registers (8 x 8 blocks of
-//     bf16 with v_perm_b32) before the LDS store, so both layouts feed the
-//     MFMA from the same K-contiguous LDS image.
+//     other axis).  NN tiles are loaded to registers and transposed there
+//     (8 x 8 blocks of bf16 with v_perm_b32) before the LDS store, so both
+//     layouts feed the MFMA from the same K-contiguous LDS image.
 //   * LDS rows are 128 B (64 bf16); the 16-byte chunk c of row r is stored
 //     at chunk c ^ ((r ^ r >> 3) & 7), which keeps the MFMA operand reads
 //     (8 consecutive rows, same chunk) and the transposed NN stores (rows
@@ -45,6 +52,8 @@
 //          routing probability), reduced in fixed order by a second kernel
 //          (same section: the backward epilogue applies dSwiGLU to the GEMM
 //          output).
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -53,10 +62,29 @@ namespace {
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 64;
+constexpr int BK = 32;
+constexpr int kStages = 4;
+constexpr int kStageA = BM * BK;  // bf16 elements per A stage (16 KB)
+constexpr int kStageB = BN * BK;
 constexpr int kThreads = 256;
 constexpr int kWaveM = 128;  // rows of a wave's sub-tile
 constexpr int kWaveN = 128;  // cols of a wave's sub-tile
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
+// Compile-time loop: f(integral_constant<int, 0>) ... f(<N-1>), so indices
+// into accumulator arrays stay constants (registers, never scratch).
+template <typename F, int... Is>
+MOE_DEV void sfor_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+MOE_DEV void sfor(F&& f) {
+  sfor_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 MOE_DEV int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -72,13 +100,14 @@ struct GluVal {
   bool g_in, u_in;
 };
 
+template <int ACT>
 MOE_DEV GluVal glu_eval(float g_pre, float u_pre, const ActP& p) {
   GluVal r;
   float g = fminf(fmaxf(g_pre, p.glo), p.ghi);
   r.u = fminf(fmaxf(u_pre, p.llo), p.lhi) + p.loff;
   r.g_in = (g_pre >= p.glo) && (g_pre <= p.ghi);
   r.u_in = (u_pre >= p.llo) && (u_pre <= p.lhi);
-  if (p.act == MOE_ACT_GEGLU) {
+  if constexpr (ACT == MOE_ACT_GEGLU) {
     const float kInvSqrt2 = 0.70710678118654752f;
     const float kInvSqrt2Pi = 0.39894228040143268f;
     float cdf = 0.5f * (1.0f + erff(g * kInvSqrt2));
@@ -97,88 +126,79 @@ MOE_DEV GluVal glu_eval(float g_pre, float u_pre, const ActP& p) {
 // Buffer resource over `bytes` bytes at `base`.  Raw (untyped) loads whose
 // VGPR offset reaches num_records return zero without touching memory; row
 // indices therefore always go into the VGPR offset (the scalar offset only
-// carries the K position, which stays inside a row), so partial tiles need
-// no clamping.
+// carries the K position), so partial tiles need no clamping.
 MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            static_cast<int>(bytes), 0x00020000);
 }
 
-MOE_DEV i32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+constexpr int kOutOfRange = 0x7fffffff;  // VGPR offset past any num_records
+
+MOE_DEV void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds_block, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_block, 16, voff, soff, 0, 0);
 }
 
-// K-contiguous [ROWS][BK] tile -> LDS, 16-byte chunks.  Thread t moves the
-// chunk (row t/8 + 32 i, k-chunk t%8) for i < ROWS/32.
-template <int ROWS>
-struct NTLoader {
-  static constexpr int kIters = ROWS * BK / 8 / kThreads;
+// K-contiguous [256][BK] tile (BK = 32) straight from HBM into one LDS stage.
+// LDS image: row r = 64 bytes, 16-byte chunk c stored at c ^ ((r >> 1) & 3).
+// Wave w fills the 1 KB blocks 4w .. 4w+3; lane l of block b lands on row
+// 16 b + l / 4, stored chunk l % 4, so it fetches logical chunk
+// (l % 4) ^ ((l / 8) % 4).
+struct KLoader {
   __amdgpu_buffer_rsrc_t rsrc;
-  int voff;       // bytes, chunk i = 0
-  int row_step;   // bytes between chunk rows i and i+1 (32 rows)
-  int l0, l1;     // LDS chunk index for even / odd i (swizzle flips bit 2)
-  i32x4 reg[kIters];
+  int voff[4];  // bytes
 
-  MOE_DEV void init(const uint16_t* base, int64_t rows_avail, int ld, int tid) {
-    const int64_t rows = rows_avail < ROWS ? rows_avail : ROWS;
+  MOE_DEV void init(const uint16_t* base, int64_t rows_avail, int ld, int wave, int lane) {
+    const int64_t rows = rows_avail < 256 ? rows_avail : 256;
     rsrc = make_rsrc(base, static_cast<uint32_t>(rows * ld * 2));
-    const int row = tid >> 3, kc = tid & 7;
-    voff = (row * ld + kc * 8) * 2;
-    row_step = 32 * ld * 2;
-    l0 = row * 8 + (kc ^ swz(row));
-    l1 = row * 8 + (kc ^ swz(row) ^ 4);
-  }
-  MOE_DEV void load(int k0) {
 #pragma unroll
-    for (int i = 0; i < kIters; ++i) reg[i] = buf_load16(rsrc, voff + i * row_step, k0 * 2);
-  }
-  MOE_DEV void store(uint16_t* s) {
-#pragma unroll
-    for (int i = 0; i < kIters; ++i)
-      *reinterpret_cast<i32x4*>(s + ((i & 1 ? l1 : l0) + 256 * i) * 8) = reg[i];
-  }
-};
-
-// N-contiguous [BK][BN] tile of a [K][N] matrix -> transposed LDS [BN][BK].
-// Each thread moves one 8 (k) x 8 (n) block: 8 row loads of 16 bytes, an
-// in-register 8x8 transpose of bf16 pairs (v_perm_b32), 8 LDS stores.
-// Column blocks past N are clamped to the last block (their results are
-// discarded by the epilogue), so every address lies inside the matrix.
-struct NNLoader {
-  static_assert(BN / 8 * (BK / 8) == kThreads, "one 8x8 block per thread");
-  __amdgpu_buffer_rsrc_t rsrc;
-  int voff;      // bytes
-  int ld2;       // row pitch in bytes
-  int nb, kb;
-  i32x4 reg[8];
-
-  MOE_DEV void init(const uint16_t* mat, uint32_t mat_bytes, int ld, int col0, int tid) {
-    rsrc = make_rsrc(mat, mat_bytes);
-    kb = tid / (BN / 8);
-    nb = tid % (BN / 8);
-    ld2 = ld * 2;
-    const int n = min(col0 + 8 * nb, ld - 8);
-    voff = (8 * kb * ld + n) * 2;
-  }
-  MOE_DEV void load(int k0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) reg[i] = buf_load16(rsrc, voff + (k0 + i) * ld2, 0);
-  }
-  MOE_DEV void store(uint16_t* s) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-      i32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        o[q] = static_cast<int>(__builtin_amdgcn_perm(
-            static_cast<uint32_t>(reg[2 * q + 1][c >> 1]),
-            static_cast<uint32_t>(reg[2 * q][c >> 1]), sel));
-      const int n = 8 * nb + c;
-      *reinterpret_cast<i32x4*>(s + (n * 8 + (kb ^ swz(n))) * 8) = o;
+    for (int j = 0; j < 4; ++j) {
+      const int row = 64 * wave + 16 * j + (lane >> 2);
+      const int kc = (lane & 3) ^ ((lane >> 3) & 3);
+      voff[j] = (row * ld + kc * 8) * 2;
     }
   }
+  // valid == false: fill the stage with zeros (out-of-range offset)
+  MOE_DEV void issue(uint16_t* stage, int k0, int wave_s, bool valid) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dma16(rsrc, stage + (4 * wave_s + j) * 512, valid ? voff[j] : kOutOfRange, valid ? k0 * 2 : 0);
+  }
 };
+
+// N-contiguous [BK][256] tile of a [K][N] matrix, copied as is into one LDS
+// stage: row k = 512 bytes, 16-byte chunk c stored at c ^ (4 (k % 8)).  The
+// MFMA operand is then read with the LDS transpose load.  Wave w fills the
+// 1 KB blocks 4w .. 4w+3 (two rows each).  Column chunks past N are clamped
+// to the last chunk (their results are discarded), so every address lies
+// inside the matrix.
+struct NLoader {
+  __amdgpu_buffer_rsrc_t rsrc;
+  int voff[4];   // bytes
+  int pitch2;    // N * 2
+
+  MOE_DEV void init(const uint16_t* mat, uint32_t mat_bytes, int N, int col0, int wave, int lane) {
+    rsrc = make_rsrc(mat, mat_bytes);
+    pitch2 = N * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 8 * wave + 2 * j + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (row & 7));
+      const int col = min(col0 + 8 * c, N - 8);
+      voff[j] = (row * N + col) * 2;
+    }
+  }
+  MOE_DEV void issue(uint16_t* stage, int k0, int wave_s, bool valid) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dma16(rsrc, stage + (4 * wave_s + j) * 512, valid ? voff[j] : kOutOfRange,
+            valid ? k0 * pitch2 : 0);
+  }
+};
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most `n` vector
+// memory loads of this wave are outstanding.
+constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 
 // --------------------------------------------------- epilogue helpers ---
 // 4 consecutive accumulator values v[r0 .. r0+3] -> 4 bf16 at p (8 bytes).
@@ -215,6 +235,184 @@ MOE_DEV void load_bf16x4(const uint16_t* p, float* v) {
   v[3] = __uint_as_float(w.y & 0xffff0000u);
 }
 
+// ------------------------------------------------------------ epilogues ---
+// Where a tile's outputs sit in a lane.  The MFMA is issued with B as its
+// first operand, so each 32x32 block holds C^T: lane l owns output row
+// (l % 32) of the block and, in register r, column 8 (r / 4) + 4 (l / 32) +
+// r % 4.  A lane thus writes runs of 4 consecutive columns (8 bytes).
+struct TileCtx {
+  int64_t row0;     // first row of the tile (padded layout)
+  int rows_valid;   // rows of the tile that belong to the expert
+  int col0;         // first output column
+  int cols_valid;   // output columns inside N (multiple of 64)
+  int n_t;          // column-tile index
+  int m_lane;       // row of this lane inside the tile, block mi = 0
+  int n_lane;       // first column of this lane inside the tile, block 0
+};
+
+// EPI_STORE: C = bf16(acc)
+MOE_DEV void epi_store(const f32x16 (&acc)[4][4], uint16_t* __restrict__ C, int64_t ldc,
+                       const TileCtx& t) {
+  sfor<4>([&](auto mi) {
+    const int m = t.m_lane + mi * 32;
+    if (m < t.rows_valid) {
+      uint16_t* crow = C + (t.row0 + m) * ldc + t.col0 + t.n_lane;
+      sfor<4>([&](auto ni) {
+        if (t.n_lane - (t.n_lane & 31) + ni * 32 < t.cols_valid) {
+          sfor<4>([&](auto rg) { store_bf16x4(crow + ni * 32 + 8 * rg, acc[mi][ni], 4 * rg); });
+        }
+      });
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one 32-row block at a time
+  });
+}
+
+// EPI_GLU: z = bf16(acc) (may be null), a = bf16(p * act(gate, up)); returns
+// max |a| over this lane's outputs.  Gated: this wave's 128 packed columns
+// [col0 + 128 wn, +128) are gate block q (blocks ni = 0, 1) then up block q
+// (ni = 2, 3), so both halves of an output are in the same lane.
+template <int ACT>
+MOE_DEV float epi_glu(const f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz,
+                      uint16_t* __restrict__ a, int64_t lda,
+                      const float* __restrict__ probs, const ActP& act, const TileCtx& t,
+                      int wn, int lane) {
+  float amax = 0.0f;
+  if constexpr (ACT == MOE_ACT_SRELU) {
+    sfor<4>([&](auto mi) {
+      const int m = t.m_lane + mi * 32;
+      if (m < t.rows_valid) {
+        const int64_t row = t.row0 + m;
+        const float p = probs[row];
+        sfor<4>([&](auto ni) { sfor<4>([&](auto rg) {
+          const int n = t.n_lane + ni * 32 + 8 * rg;
+          if (n < t.cols_valid) {
+            if (z) store_bf16x4(z + row * ldz + t.col0 + n, acc[mi][ni], 4 * rg);
+            float av[4];
+            sfor<4>([&](auto i) {
+              const float zc = fminf(fmaxf(acc[mi][ni][4 * rg + i], act.glo), act.ghi);
+              const float rl = fmaxf(zc, 0.0f);
+              av[i] = p * rl * rl;
+            });
+            amax = fmaxf(amax, store_bf16x4_amax(a + row * lda + t.col0 + n, av));
+          }
+        }); });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  } else if (wn * kWaveN < t.cols_valid) {
+    const int q = (t.col0 + wn * kWaveN) / (2 * MOE_INTERLEAVE);
+    sfor<4>([&](auto mi) {
+      const int m = t.m_lane + mi * 32;
+      if (m < t.rows_valid) {
+        const int64_t row = t.row0 + m;
+        const float p = probs[row];
+        sfor<2>([&](auto h) { sfor<4>([&](auto rg) {
+          const int c = h * 32 + 8 * rg + 4 * (lane >> 5);  // 0..63 in the block
+          if (z) {
+            uint16_t* zrow = z + row * ldz + t.col0 + wn * kWaveN + c;
+            store_bf16x4(zrow, acc[mi][h], 4 * rg);
+            store_bf16x4(zrow + MOE_INTERLEAVE, acc[mi][h + 2], 4 * rg);
+          }
+          float av[4];
+          sfor<4>([&](auto i) {
+            av[i] = p * glu_eval<ACT>(acc[mi][h][4 * rg + i], acc[mi][h + 2][4 * rg + i], act).s;
+          });
+          amax = fmaxf(amax, store_bf16x4_amax(a + row * lda + q * MOE_INTERLEAVE + c, av));
+        }); });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+  return amax;
+}
+
+// EPI_DGLU: acc = dA over logical columns [col0, col0 + BN).  Reads the
+// saved z (both halves), writes dz in the layout of z and returns, per row
+// block mi, this lane's partial sum of dA * s.  The z loads of a row block
+// are all issued before any arithmetic so their latency overlaps.
+//
+// Addresses: the lane's logical columns are col0 + 128 wn + 4 h + 32 ni +
+// 8 rg + i (h = lane / 32); with the 64-column interleave their gate
+// columns are 2 col0 + 256 wn + 4 h + [128 (ni / 2) + 32 (ni % 2) + 8 rg] + i,
+// a lane base plus a compile-time constant, and the up column is 64 further.
+// Whether a 32-column block lies inside N is uniform across the wave.
+template <int ACT>
+MOE_DEV void epi_dglu(const f32x16 (&acc)[4][4], const uint16_t* __restrict__ zin, int64_t ldz,
+                      uint16_t* __restrict__ dz, int64_t lddz,
+                      const float* __restrict__ probs, const ActP& act, const TileCtx& t,
+                      int wn, int lane, float (&dp_out)[4]) {
+  constexpr bool gated = ACT != MOE_ACT_SRELU;
+  const int h4 = 4 * (lane >> 5);
+  const int lane_col = gated ? 2 * t.col0 + 256 * wn + h4 : t.col0 + 128 * wn + h4;
+  sfor<4>([&](auto mi) {
+    const int m = t.m_lane + mi * 32;
+    const bool row_ok = m < t.rows_valid;
+    float dp = 0.0f;
+    if (row_ok) {
+      const int64_t row = t.row0 + m;
+      const float p = probs[row];
+      const uint16_t* zb = zin + row * ldz + lane_col;
+      uint16_t* db = dz + row * lddz + lane_col;
+      uint2 zg[4][4], zu[4][4];
+      sfor<4>([&](auto ni) {
+        if (wn * kWaveN + ni * 32 < t.cols_valid) {
+          sfor<4>([&](auto rg) {
+            if constexpr (gated) {
+              constexpr int off = 128 * (ni / 2) + 32 * (ni % 2) + 8 * rg;
+              zg[ni][rg] = *reinterpret_cast<const uint2*>(zb + off);
+              zu[ni][rg] = *reinterpret_cast<const uint2*>(zb + off + MOE_INTERLEAVE);
+            } else {
+              constexpr int off = 32 * ni + 8 * rg;
+              zg[ni][rg] = *reinterpret_cast<const uint2*>(zb + off);
+            }
+          });
+        }
+      });
+      sfor<4>([&](auto ni) {
+        if (wn * kWaveN + ni * 32 < t.cols_valid) {
+          sfor<4>([&](auto rg) {
+            const float gz[4] = {__uint_as_float(zg[ni][rg].x << 16),
+                                 __uint_as_float(zg[ni][rg].x & 0xffff0000u),
+                                 __uint_as_float(zg[ni][rg].y << 16),
+                                 __uint_as_float(zg[ni][rg].y & 0xffff0000u)};
+            if constexpr (gated) {
+              constexpr int off = 128 * (ni / 2) + 32 * (ni % 2) + 8 * rg;
+              const float uz[4] = {__uint_as_float(zu[ni][rg].x << 16),
+                                   __uint_as_float(zu[ni][rg].x & 0xffff0000u),
+                                   __uint_as_float(zu[ni][rg].y << 16),
+                                   __uint_as_float(zu[ni][rg].y & 0xffff0000u)};
+              float dg[4], du[4];
+              sfor<4>([&](auto i) {
+                const float da = acc[mi][ni][4 * rg + i];
+                const GluVal v = glu_eval<ACT>(gz[i], uz[i], act);
+                const float ds = p * da;
+                dg[i] = v.g_in ? ds * v.u * v.df : 0.0f;
+                du[i] = v.u_in ? ds * v.f : 0.0f;
+                dp += da * v.s;
+              });
+              store_f32x4_bf16(db + off, dg);
+              store_f32x4_bf16(db + off + MOE_INTERLEAVE, du);
+            } else {
+              constexpr int off = 32 * ni + 8 * rg;
+              float d[4];
+              sfor<4>([&](auto i) {
+                const float da = acc[mi][ni][4 * rg + i];
+                const bool in = (gz[i] >= act.glo) && (gz[i] <= act.ghi);
+                const float rl = fmaxf(fminf(fmaxf(gz[i], act.glo), act.ghi), 0.0f);
+                d[i] = in ? p * da * 2.0f * rl : 0.0f;
+                dp += da * rl * rl;
+              });
+              store_f32x4_bf16(db + off, d);
+            }
+          });
+        }
+      });
+    }
+    dp_out[mi] = dp;
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
 // ------------------------------------------------------- block helpers ---
 // Exclusive scan of one int per thread over the 256-thread block.
 MOE_DEV int block_exclusive_scan(int v, int* s_tmp, int& total) {
@@ -240,19 +438,21 @@ MOE_DEV int block_exclusive_scan(int v, int* s_tmp, int& total) {
 }
 
 // ---------------------------------------------------------------- kernel --
-template <int EPI, bool NN>
+template <int EPI, bool NN, int ACT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[kStageA], sA1[kStageA], sA2[kStageA], sA3[kStageA];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[kStageB], sB1[kStageB], sB2[kStageB], sB3[kStageB];
   __shared__ int s_start[kMaxExperts + 1];
   __shared__ int s_split[kMaxExperts];
   __shared__ int s_pad[kMaxExperts];
   __shared__ int s_tmp[kThreads / 64];
+  __shared__ float s_red[2 * BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave >> 1, wn = wave & 1;
   const int E = g.E;
   const int tiles_n = (g.N + BN - 1) / BN;
@@ -286,6 +486,35 @@ void grouped_gemm_kernel(GemmArgs g) {
   int vid = blockIdx.x;
   if (G % kNumXcd == 0) vid = (blockIdx.x % kNumXcd) * (G / kNumXcd) + blockIdx.x / kNumXcd;
 
+  // per-lane LDS byte offsets of the MFMA operands.  K-contiguous image:
+  // row base + 16-byte chunk (2 ks + lane / 32) ^ ((row >> 1) & 3), the
+  // swizzle term being the same for rows 32 apart.  [K][N] image (B of the
+  // dgrad GEMMs, read with ds_read_b64_tr_b16): in each 16-lane group g,
+  // source lane s = 4 r + q points at 4 consecutive columns
+  // nb + 16 (g % 2) + 4 q of row 16 ks + 8 (g / 2) + 4 h + r, h selecting
+  // the first or second 4 of the lane's 8 K values.
+  const int khalf = lane >> 5;
+  const int arow = wm * kWaveM + (lane & 31);
+  const int brow = wn * kWaveN + (lane & 31);
+  int a_off[2], b_off[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    a_off[ks] = (arow * 4 + ((2 * ks + khalf) ^ ((arow >> 1) & 3))) * 16;
+    b_off[ks] = (brow * 4 + ((2 * ks + khalf) ^ ((brow >> 1) & 3))) * 16;
+  }
+  int btr_off[2][4];
+  {
+    const int gq = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int row = 8 * (gq >> 1) + 4 * h + (sl >> 2);   // + 16 ks
+        const int c = wn * 16 + ni * 4 + 2 * (gq & 1) + ((sl & 3) >> 1);
+        btr_off[h][ni] = row * 512 + (c ^ (4 * (row & 7))) * 16 + 8 * (sl & 1);
+      }
+  }
+
   for (int tile = vid; tile < total; tile += G) {
     // expert owning this tile: last e with s_start[e] <= tile
     int lo = 0, hi = E - 1;
@@ -311,211 +540,157 @@ void grouped_gemm_kernel(GemmArgs g) {
     if (rows_valid <= 0) continue;  // only with inconsistent offsets; stays in bounds
 
     const uint16_t* Bexp = g.B + static_cast<int64_t>(e) * g.b_stride;
-    NTLoader<BM> la;
-    la.init(g.A + row0 * g.K, g.M_cap - row0, g.K, tid);
-    NTLoader<BN> lb_nt;
-    NNLoader lb_nn;
+    KLoader la;
+    la.init(g.A + row0 * g.K, g.M_cap - row0, g.K, wave, lane);
+    KLoader lb_k;
+    NLoader lb_n;
     if constexpr (NN) {
-      lb_nn.init(Bexp, static_cast<uint32_t>(static_cast<int64_t>(g.K) * g.N * 2), g.N, col0, tid);
+      lb_n.init(Bexp, static_cast<uint32_t>(static_cast<int64_t>(g.K) * g.N * 2), g.N, col0,
+                wave, lane);
     } else {
-      lb_nt.init(Bexp + static_cast<int64_t>(col0) * g.K, g.N - col0, g.K, tid);
+      lb_k.init(Bexp + static_cast<int64_t>(col0) * g.K, g.N - col0, g.K, wave, lane);
     }
+    const int nk = g.K / BK;
+    auto issue_stage = [&](uint16_t* a_st, uint16_t* b_st, int kt) {
+      const bool valid = kt < nk;
+      la.issue(a_st, kt * BK, wave_s, valid);
+      if constexpr (NN) lb_n.issue(b_st, kt * BK, wave_s, valid);
+      else lb_k.issue(b_st, kt * BK, wave_s, valid);
+    };
 
     f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    sfor<4>([&](auto mi) { sfor<4>([&](auto ni) { acc[mi][ni] = f32x16{}; }); });
 
-    const int nk = g.K / BK;
-    la.load(0);
-    if constexpr (NN) lb_nn.load(0); else lb_nt.load(0);
-    la.store(sA[0]);
-    if constexpr (NN) lb_nn.store(sB[0]); else lb_nt.store(sB[0]);
-    __syncthreads();
+    bf16x8 fa[2][4], fb[2][4];
+    // operands of the 16-deep sub-step ks of stage s into register set buf
+    auto read_frags = [&](const uint16_t* a_st, const uint16_t* b_st, auto ks, auto buf) {
+      const char* ca = reinterpret_cast<const char*>(a_st);
+      const char* cb = reinterpret_cast<const char*>(b_st);
+      sfor<4>([&](auto i) {
+        fa[buf][i] = *reinterpret_cast<const bf16x8*>(ca + a_off[ks] + i * 32 * 64);
+      });
+      if constexpr (NN) {
+        sfor<4>([&](auto ni) {
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_t*)(cb + btr_off[0][ni] + ks * 16 * 512));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_t*)(cb + btr_off[1][ni] + ks * 16 * 512));
+          const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          fb[buf][ni] = __builtin_bit_cast(bf16x8, both);
+        });
+      } else {
+        sfor<4>([&](auto i) {
+          fb[buf][i] = *reinterpret_cast<const bf16x8*>(cb + b_off[ks] + i * 32 * 64);
+        });
+      }
+    };
+    // C^T blocks: B fragment first, so a lane owns one output row
+    auto mfma_all = [&](auto buf) {
+      sfor<4>([&](auto mi) { sfor<4>([&](auto ni) {
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][ni], fa[buf][mi],
+                                                              acc[mi][ni], 0, 0, 0);
+      }); });
+    };
+    // Issue order inside a phase.  A DMA load blocks the wave until the
+    // address unit accepts it (about 16 cycles per 1 KB wave load, shared by
+    // the four waves), so the loads of the next stage are spread between
+    // MFMAs instead of issued in a burst; the operand reads of the next
+    // 16-deep sub-step go in between as well.
+    constexpr int kReadsPerPhase = NN ? 12 : 8;
+    auto pin_load_phase = [&]() {
+      sfor<8>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (DMA) load
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      });
+      if constexpr (kReadsPerPhase > 8)
+        __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerPhase - 8, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto pin_phase = [&]() {
+      sfor<8>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerPhase / 8 + (NN ? 1 : 0), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    };
 
-    // per-lane LDS chunk coordinates of the MFMA operands
-    const int arow = wm * kWaveM + (lane & 31);
-    const int brow = wn * kWaveN + (lane & 31);
-    const int khalf = lane >> 5;
+    // 4-stage pipeline, loads run 3 K steps ahead.  Every K step issues 8
+    // DMA loads per wave; before the barrier of step kt a wave waits until
+    // only the loads of steps kt+2 and kt+3 are outstanding.  The loop is
+    // unrolled by 4 so every stage is a distinct LDS array named statically
+    // (the compiler then sees that a load in flight never targets the stage
+    // being read); steps past the end of K load zeros.
+    constexpr int kLoadsPerStep = 8;
+    __syncthreads();  // all waves are done with the LDS of the previous tile
+    issue_stage(sA0, sB0, 0);
+    issue_stage(sA1, sB1, 1);
+    issue_stage(sA2, sB2, 2);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerStep));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    read_frags(sA0, sB0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
 
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        la.load((kt + 1) * BK);
-        if constexpr (NN) lb_nn.load((kt + 1) * BK); else lb_nt.load((kt + 1) * BK);
-      }
-      const uint16_t* a_s = sA[cur];
-      const uint16_t* b_s = sB[cur];
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int ch = ks * 2 + khalf;
-        bf16x8 af[4], bfr[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-          const int r = arow + mi * 32;
-          af[mi] = *reinterpret_cast<const bf16x8*>(a_s + (r * 8 + (ch ^ swz(r))) * 8);
-        }
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const int r = brow + ni * 32;
-          bfr[ni] = *reinterpret_cast<const bf16x8*>(b_s + (r * 8 + (ch ^ swz(r))) * 8);
-        }
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
-      }
-      if (more) {
-        la.store(sA[cur ^ 1]);
-        if constexpr (NN) lb_nn.store(sB[cur ^ 1]); else lb_nt.store(sB[cur ^ 1]);
-      }
-      __syncthreads();
+    // one K step on stage cur, next stage nxt, loads for step kt+3 into ld
+    auto kstep = [&](const uint16_t* a_cur, const uint16_t* b_cur, const uint16_t* a_nxt,
+                     const uint16_t* b_nxt, uint16_t* a_ld, uint16_t* b_ld, int kt) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue_stage(a_ld, b_ld, kt + 3);
+      read_frags(a_cur, b_cur, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+      mfma_all(std::integral_constant<int, 0>{});
+      pin_load_phase();
+      // the stage of step kt+1 has landed (only steps kt+2, kt+3 in flight)
+      // and this wave's reads of stage kt are done; then a bare barrier
+      // (no fence: a fence would also wait for the loads still in flight)
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerStep));
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      read_frags(a_nxt, b_nxt, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+      mfma_all(std::integral_constant<int, 1>{});
+      pin_phase();
+    };
+    // whole rounds of 4 steps; steps past K run on zero-filled stages
+    for (int kt = 0; kt < nk; kt += 4) {
+      kstep(sA0, sB0, sA1, sB1, sA3, sB3, kt);
+      kstep(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
+      kstep(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
+      kstep(sA3, sB3, sA0, sB0, sA2, sB2, kt + 3);
     }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // drain the tail reloads
 
     // ------------------------------------------------------ epilogues ---
-    // The MFMA is issued with B as its first operand, so each 32x32 block
-    // holds C^T: lane l owns output row (l % 32) of the block and, in
-    // register r, column 8 * (r / 4) + 4 * (l / 32) + r % 4.  A lane thus
-    // writes runs of 4 consecutive columns (8 bytes of bf16).
-    const int m_lane = wm * kWaveM + (lane & 31);
-    const int n_lane = wn * kWaveN + 4 * (lane >> 5);
-
+    TileCtx t;
+    t.row0 = row0;
+    t.rows_valid = rows_valid;
+    t.col0 = col0;
+    t.cols_valid = cols_valid;
+    t.n_t = n_t;
+    t.m_lane = wm * kWaveM + (lane & 31);
+    t.n_lane = wn * kWaveN + 4 * (lane >> 5);
     if constexpr (EPI == EPI_STORE) {
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int m = m_lane + mi * 32;
-        if (m >= rows_valid) continue;
-        uint16_t* crow = g.C + (row0 + m) * g.ldc + col0;
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-          for (int rg = 0; rg < 4; ++rg) {
-            const int n = n_lane + ni * 32 + 8 * rg;
-            if (n < cols_valid) store_bf16x4(crow + n, acc[mi][ni], 4 * rg);
-          }
-      }
+      epi_store(acc, g.C, g.ldc, t);
     } else if constexpr (EPI == EPI_GLU) {
-      float amax = 0.0f;
-      if (g.act.act == MOE_ACT_SRELU) {
-        // not gated: each output column is independent, FC1 width = I
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-          const int m = m_lane + mi * 32;
-          if (m >= rows_valid) continue;
-          const int64_t row = row0 + m;
-          const float p = g.probs[row];
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-              const int n = n_lane + ni * 32 + 8 * rg;
-              if (n >= cols_valid) continue;
-              if (g.C) store_bf16x4(g.C + row * g.ldc + col0 + n, acc[mi][ni], 4 * rg);
-              float av[4];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float zc = fminf(fmaxf(acc[mi][ni][4 * rg + i], g.act.glo), g.act.ghi);
-                const float rl = fmaxf(zc, 0.0f);
-                av[i] = p * rl * rl;
-              }
-              amax = fmaxf(amax, store_bf16x4_amax(g.act_out + row * g.ld_act + col0 + n, av));
-            }
-        }
-      } else if (wn * kWaveN < cols_valid) {
-        // This wave's packed columns [col0 + 128 wn, +128) are gate block q
-        // (blocks ni = 0, 1) followed by up block q (ni = 2, 3).
-        const int q = (col0 + wn * kWaveN) / (2 * MOE_INTERLEAVE);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-          const int m = m_lane + mi * 32;
-          if (m >= rows_valid) continue;
-          const int64_t row = row0 + m;
-          const float p = g.probs[row];
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-              const int c = h * 32 + 8 * rg + 4 * (lane >> 5);  // 0..63 in the block
-              if (g.C) {
-                uint16_t* zrow = g.C + row * g.ldc + col0 + wn * kWaveN + c;
-                store_bf16x4(zrow, acc[mi][h], 4 * rg);
-                store_bf16x4(zrow + MOE_INTERLEAVE, acc[mi][h + 2], 4 * rg);
-              }
-              float av[4];
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                av[i] = p * glu_eval(acc[mi][h][4 * rg + i], acc[mi][h + 2][4 * rg + i], g.act).s;
-              amax = fmaxf(amax, store_bf16x4_amax(
-                                     g.act_out + row * g.ld_act + q * MOE_INTERLEAVE + c, av));
-            }
-        }
-      }
+      float amax = epi_glu<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, g.probs, g.act, t, wn, lane);
       if (g.amax) {
         amax = wave_max(amax);
         if (lane == 0) atomic_max_nonneg(g.amax, amax);
       }
-    } else {  // EPI_DGLU: acc = dA over logical columns [col0, col0 + BN)
-      const bool gated = g.act.act != MOE_ACT_SRELU;
-      float* red = reinterpret_cast<float*>(&sA[0][0]);  // [2][BM], free after the loop
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int m = m_lane + mi * 32;
-        const bool row_ok = m < rows_valid;
-        const int64_t row = row0 + (row_ok ? m : 0);
-        const float p = row_ok ? g.probs[row] : 0.0f;
-        float dp = 0.0f;
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-          for (int rg = 0; rg < 4; ++rg) {
-            const int n = n_lane + ni * 32 + 8 * rg;
-            if (!row_ok || n >= cols_valid) continue;
-            const int j = col0 + n;  // logical column of dA (4 consecutive)
-            if (gated) {
-              const int pg = (j / MOE_INTERLEAVE) * 2 * MOE_INTERLEAVE + (j % MOE_INTERLEAVE);
-              float gz[4], uz[4], dg[4], du[4];
-              load_bf16x4(g.zin + row * g.ldz + pg, gz);
-              load_bf16x4(g.zin + row * g.ldz + pg + MOE_INTERLEAVE, uz);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float da = acc[mi][ni][4 * rg + i];
-                const GluVal v = glu_eval(gz[i], uz[i], g.act);
-                const float ds = p * da;
-                dg[i] = v.g_in ? ds * v.u * v.df : 0.0f;
-                du[i] = v.u_in ? ds * v.f : 0.0f;
-                dp += da * v.s;
-              }
-              store_f32x4_bf16(g.C + row * g.ldc + pg, dg);
-              store_f32x4_bf16(g.C + row * g.ldc + pg + MOE_INTERLEAVE, du);
-            } else {
-              float zv[4], dz[4];
-              load_bf16x4(g.zin + row * g.ldz + j, zv);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float da = acc[mi][ni][4 * rg + i];
-                const bool in = (zv[i] >= g.act.glo) && (zv[i] <= g.act.ghi);
-                const float rl = fmaxf(fminf(fmaxf(zv[i], g.act.glo), g.act.ghi), 0.0f);
-                dz[i] = in ? p * da * 2.0f * rl : 0.0f;
-                dp += da * rl * rl;
-              }
-              store_f32x4_bf16(g.C + row * g.ldc + j, dz);
-            }
-          }
+    } else {
+      float dp[4];
+      epi_dglu<ACT>(acc, g.zin, g.ldz, g.C, g.ldc, g.probs, g.act, t, wn, lane, dp);
+      sfor<4>([&](auto mi) {
         // lanes l and l ^ 32 hold the same row: fixed-order pair sum
-        dp += __shfl_xor(dp, 32, kWave);
-        if (lane < 32) red[wn * BM + m] = dp;
-      }
+        const float v = dp[mi] + __shfl_xor(dp[mi], 32, kWave);
+        if (lane < 32) s_red[wn * BM + t.m_lane + mi * 32] = v;
+      });
       __syncthreads();
       {
         const int m = tid;  // BM == kThreads
-        if (m < rows_valid) g.dp_part[(row0 + m) * g.n_part + n_t] = red[m] + red[BM + m];
+        if (m < rows_valid) g.dp_part[(row0 + m) * g.n_part + n_t] = s_red[m] + s_red[BM + m];
       }
-      __syncthreads();
     }
   }
 }
@@ -554,18 +729,29 @@ __global__ __launch_bounds__(256) void dprobs_reduce_kernel(
 int grouped_gemm_tile_n() { return BN; }
 int grouped_gemm_tile_m() { return BM; }
 
-hipError_t launch_grouped_gemm(const GemmArgs& g, int epi, bool b_nn, int grid, hipStream_t s) {
+template <int EPI, bool NN>
+hipError_t launch_act(const GemmArgs& g, int grid, hipStream_t s) {
   dim3 blk(kThreads), grd(grid);
-  if (b_nn) {
-    if (epi == EPI_STORE) grouped_gemm_kernel<EPI_STORE, true><<<grd, blk, 0, s>>>(g);
-    else if (epi == EPI_DGLU) grouped_gemm_kernel<EPI_DGLU, true><<<grd, blk, 0, s>>>(g);
-    else return hipErrorInvalidValue;
-  } else {
-    if (epi == EPI_STORE) grouped_gemm_kernel<EPI_STORE, false><<<grd, blk, 0, s>>>(g);
-    else if (epi == EPI_GLU) grouped_gemm_kernel<EPI_GLU, false><<<grd, blk, 0, s>>>(g);
-    else return hipErrorInvalidValue;
+  switch (g.act.act) {
+    case MOE_ACT_SWIGLU: grouped_gemm_kernel<EPI, NN, MOE_ACT_SWIGLU><<<grd, blk, 0, s>>>(g); break;
+    case MOE_ACT_GEGLU: grouped_gemm_kernel<EPI, NN, MOE_ACT_GEGLU><<<grd, blk, 0, s>>>(g); break;
+    case MOE_ACT_SRELU: grouped_gemm_kernel<EPI, NN, MOE_ACT_SRELU><<<grd, blk, 0, s>>>(g); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm(const GemmArgs& g, int epi, bool b_nn, int grid, hipStream_t s) {
+  dim3 blk(kThreads), grd(grid);
+  if (epi == EPI_STORE) {
+    // the plain epilogue does not depend on the activation
+    if (b_nn) grouped_gemm_kernel<EPI_STORE, true, MOE_ACT_SWIGLU><<<grd, blk, 0, s>>>(g);
+    else grouped_gemm_kernel<EPI_STORE, false, MOE_ACT_SWIGLU><<<grd, blk, 0, s>>>(g);
+    return hipGetLastError();
+  }
+  if (epi == EPI_GLU && !b_nn) return launch_act<EPI_GLU, false>(g, grid, s);
+  if (epi == EPI_DGLU && b_nn) return launch_act<EPI_DGLU, true>(g, grid, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_dprobs_reduce(const float* part, int n_part, const int32_t* split,
