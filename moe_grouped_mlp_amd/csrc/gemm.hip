@@ -139,10 +139,12 @@ MOE_DEV void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds_block, int voff, int 
 }
 
 // K-contiguous [256][BK] tile (BK = 32) straight from HBM into one LDS stage.
-// LDS image: row r = 64 bytes, 16-byte chunk c stored at c ^ ((r >> 1) & 3).
-// Wave w fills the 1 KB blocks 4w .. 4w+3; lane l of block b lands on row
-// 16 b + l / 4, stored chunk l % 4, so it fetches logical chunk
-// (l % 4) ^ ((l / 8) % 4).
+// LDS image: row r = 64 bytes, 16-byte chunk c stored at c ^ ((r >> 2) & 3).
+// A 16-byte LDS read serves 16 lanes per cycle over 64 banks (256 bytes);
+// the operand reads touch 16 consecutive rows in one chunk, which this
+// swizzle spreads over all 16 bank groups.  Wave w fills the 1 KB blocks
+// 4w .. 4w+3; lane l of block b lands on row 16 b + l / 4, stored chunk
+// l % 4, so it fetches logical chunk (l % 4) ^ ((l / 16) % 4).
 struct KLoader {
   __amdgpu_buffer_rsrc_t rsrc;
   int voff[4];  // bytes
@@ -153,7 +155,7 @@ struct KLoader {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = 64 * wave + 16 * j + (lane >> 2);
-      const int kc = (lane & 3) ^ ((lane >> 3) & 3);
+      const int kc = (lane & 3) ^ ((lane >> 4) & 3);
       voff[j] = (row * ld + kc * 8) * 2;
     }
   }
@@ -487,7 +489,7 @@ void grouped_gemm_kernel(GemmArgs g) {
   if (G % kNumXcd == 0) vid = (blockIdx.x % kNumXcd) * (G / kNumXcd) + blockIdx.x / kNumXcd;
 
   // per-lane LDS byte offsets of the MFMA operands.  K-contiguous image:
-  // row base + 16-byte chunk (2 ks + lane / 32) ^ ((row >> 1) & 3), the
+  // row base + 16-byte chunk (2 ks + lane / 32) ^ ((row >> 2) & 3), the
   // swizzle term being the same for rows 32 apart.  [K][N] image (B of the
   // dgrad GEMMs, read with ds_read_b64_tr_b16): in each 16-lane group g,
   // source lane s = 4 r + q points at 4 consecutive columns
@@ -499,8 +501,8 @@ void grouped_gemm_kernel(GemmArgs g) {
   int a_off[2], b_off[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    a_off[ks] = (arow * 4 + ((2 * ks + khalf) ^ ((arow >> 1) & 3))) * 16;
-    b_off[ks] = (brow * 4 + ((2 * ks + khalf) ^ ((brow >> 1) & 3))) * 16;
+    a_off[ks] = (arow * 4 + ((2 * ks + khalf) ^ ((arow >> 2) & 3))) * 16;
+    b_off[ks] = (brow * 4 + ((2 * ks + khalf) ^ ((brow >> 2) & 3))) * 16;
   }
   int btr_off[2][4];
   {
@@ -515,159 +517,186 @@ void grouped_gemm_kernel(GemmArgs g) {
       }
   }
 
-  for (int tile = vid; tile < total; tile += G) {
+  // ---- per-tile geometry --------------------------------------------
+  struct TileInfo {
+    int e, n_t, col0, cols_valid, rows_valid;
+    int64_t row0;
+  };
+  auto tile_info = [&](int tile) {
     // expert owning this tile: last e with s_start[e] <= tile
     int lo = 0, hi = E - 1;
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
       if (s_start[mid] <= tile) lo = mid; else hi = mid - 1;
     }
-    const int e = lo;
-    const int local = tile - s_start[e];
-    const int tm_e = (s_split[e] + BM - 1) / BM;
+    TileInfo ti;
+    ti.e = lo;
+    const int local = tile - s_start[ti.e];
+    const int tm_e = (s_split[ti.e] + BM - 1) / BM;
     const int band = local / (g.group_m * tiles_n);
     const int first_m = band * g.group_m;
     const int gm = min(g.group_m, tm_e - first_m);
     const int rem = local - band * g.group_m * tiles_n;
     const int m_t = first_m + rem % gm;
-    const int n_t = rem / gm;
+    ti.n_t = rem / gm;
+    ti.row0 = static_cast<int64_t>(s_pad[ti.e]) + static_cast<int64_t>(m_t) * BM;
+    // rows_valid <= 0 only with inconsistent offsets: the tile then loads
+    // zeros (its row range is empty) and stores nothing
+    ti.rows_valid = static_cast<int>(
+        min(static_cast<int64_t>(min(BM, s_split[ti.e] - m_t * BM)), g.M_cap - ti.row0));
+    ti.col0 = ti.n_t * BN;
+    ti.cols_valid = min(BN, g.N - ti.col0);
+    return ti;
+  };
 
-    const int64_t row0 = static_cast<int64_t>(s_pad[e]) + static_cast<int64_t>(m_t) * BM;
-    const int rows_valid = static_cast<int>(
-        min(static_cast<int64_t>(min(BM, s_split[e] - m_t * BM)), g.M_cap - row0));
-    const int col0 = n_t * BN;
-    const int cols_valid = min(BN, g.N - col0);
-    if (rows_valid <= 0) continue;  // only with inconsistent offsets; stays in bounds
-
-    const uint16_t* Bexp = g.B + static_cast<int64_t>(e) * g.b_stride;
-    KLoader la;
-    la.init(g.A + row0 * g.K, g.M_cap - row0, g.K, wave, lane);
-    KLoader lb_k;
-    NLoader lb_n;
+  const int nk = g.K / BK;
+  KLoader la;
+  KLoader lb_k;
+  NLoader lb_n;
+  auto issue_stage = [&](uint16_t* a_st, uint16_t* b_st, int kt) {
+    const bool valid = kt < nk;
+    la.issue(a_st, kt * BK, wave_s, valid);
+    if constexpr (NN) lb_n.issue(b_st, kt * BK, wave_s, valid);
+    else lb_k.issue(b_st, kt * BK, wave_s, valid);
+  };
+  // point the loaders at a tile and start its first three K steps
+  auto start_tile = [&](const TileInfo& ti) {
+    const int64_t rows_avail = ti.rows_valid > 0 ? g.M_cap - ti.row0 : 0;
+    la.init(g.A + (ti.rows_valid > 0 ? ti.row0 : 0) * g.K, rows_avail, g.K, wave, lane);
+    const uint16_t* Bexp = g.B + static_cast<int64_t>(ti.e) * g.b_stride;
     if constexpr (NN) {
-      lb_n.init(Bexp, static_cast<uint32_t>(static_cast<int64_t>(g.K) * g.N * 2), g.N, col0,
+      lb_n.init(Bexp, static_cast<uint32_t>(static_cast<int64_t>(g.K) * g.N * 2), g.N, ti.col0,
                 wave, lane);
     } else {
-      lb_k.init(Bexp + static_cast<int64_t>(col0) * g.K, g.N - col0, g.K, wave, lane);
+      lb_k.init(Bexp + static_cast<int64_t>(ti.col0) * g.K, g.N - ti.col0, g.K, wave, lane);
     }
-    const int nk = g.K / BK;
-    auto issue_stage = [&](uint16_t* a_st, uint16_t* b_st, int kt) {
-      const bool valid = kt < nk;
-      la.issue(a_st, kt * BK, wave_s, valid);
-      if constexpr (NN) lb_n.issue(b_st, kt * BK, wave_s, valid);
-      else lb_k.issue(b_st, kt * BK, wave_s, valid);
-    };
-
-    f32x16 acc[4][4];
-    sfor<4>([&](auto mi) { sfor<4>([&](auto ni) { acc[mi][ni] = f32x16{}; }); });
-
-    bf16x8 fa[2][4], fb[2][4];
-    // operands of the 16-deep sub-step ks of stage s into register set buf
-    auto read_frags = [&](const uint16_t* a_st, const uint16_t* b_st, auto ks, auto buf) {
-      const char* ca = reinterpret_cast<const char*>(a_st);
-      const char* cb = reinterpret_cast<const char*>(b_st);
-      sfor<4>([&](auto i) {
-        fa[buf][i] = *reinterpret_cast<const bf16x8*>(ca + a_off[ks] + i * 32 * 64);
-      });
-      if constexpr (NN) {
-        sfor<4>([&](auto ni) {
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16_t*)(cb + btr_off[0][ni] + ks * 16 * 512));
-          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16_t*)(cb + btr_off[1][ni] + ks * 16 * 512));
-          const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          fb[buf][ni] = __builtin_bit_cast(bf16x8, both);
-        });
-      } else {
-        sfor<4>([&](auto i) {
-          fb[buf][i] = *reinterpret_cast<const bf16x8*>(cb + b_off[ks] + i * 32 * 64);
-        });
-      }
-    };
-    // C^T blocks: B fragment first, so a lane owns one output row
-    auto mfma_all = [&](auto buf) {
-      sfor<4>([&](auto mi) { sfor<4>([&](auto ni) {
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][ni], fa[buf][mi],
-                                                              acc[mi][ni], 0, 0, 0);
-      }); });
-    };
-    // Issue order inside a phase.  A DMA load blocks the wave until the
-    // address unit accepts it (about 16 cycles per 1 KB wave load, shared by
-    // the four waves), so the loads of the next stage are spread between
-    // MFMAs instead of issued in a burst; the operand reads of the next
-    // 16-deep sub-step go in between as well.
-    constexpr int kReadsPerPhase = NN ? 12 : 8;
-    auto pin_load_phase = [&]() {
-      sfor<8>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (DMA) load
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-      });
-      if constexpr (kReadsPerPhase > 8)
-        __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerPhase - 8, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    auto pin_phase = [&]() {
-      sfor<8>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerPhase / 8 + (NN ? 1 : 0), 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      });
-      __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // 4-stage pipeline, loads run 3 K steps ahead.  Every K step issues 8
-    // DMA loads per wave; before the barrier of step kt a wave waits until
-    // only the loads of steps kt+2 and kt+3 are outstanding.  The loop is
-    // unrolled by 4 so every stage is a distinct LDS array named statically
-    // (the compiler then sees that a load in flight never targets the stage
-    // being read); steps past the end of K load zeros.
-    constexpr int kLoadsPerStep = 8;
-    __syncthreads();  // all waves are done with the LDS of the previous tile
     issue_stage(sA0, sB0, 0);
     issue_stage(sA1, sB1, 1);
     issue_stage(sA2, sB2, 2);
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerStep));
+  };
+
+  bf16x8 fa[2][4], fb[2][4];
+  f32x16 acc[4][4];
+  // operands of the 16-deep sub-step ks of a stage into register set buf
+  auto read_frags = [&](const uint16_t* a_st, const uint16_t* b_st, auto ks, auto buf) {
+    const char* ca = reinterpret_cast<const char*>(a_st);
+    const char* cb = reinterpret_cast<const char*>(b_st);
+    sfor<4>([&](auto i) {
+      fa[buf][i] = *reinterpret_cast<const bf16x8*>(ca + a_off[ks] + i * 32 * 64);
+    });
+    if constexpr (NN) {
+      sfor<4>([&](auto ni) {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)(cb + btr_off[0][ni] + ks * 16 * 512));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)(cb + btr_off[1][ni] + ks * 16 * 512));
+        const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        fb[buf][ni] = __builtin_bit_cast(bf16x8, both);
+      });
+    } else {
+      sfor<4>([&](auto i) {
+        fb[buf][i] = *reinterpret_cast<const bf16x8*>(cb + b_off[ks] + i * 32 * 64);
+      });
+    }
+  };
+  // C^T blocks: B fragment first, so a lane owns one output row
+  auto mfma_all = [&](auto buf) {
+    sfor<4>([&](auto mi) { sfor<4>([&](auto ni) {
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][ni], fa[buf][mi],
+                                                            acc[mi][ni], 0, 0, 0);
+    }); });
+  };
+  // Issue order inside a phase.  A DMA load blocks the wave until the
+  // address unit accepts it (about 16 cycles per 1 KB wave load, shared by
+  // the four waves), so the loads of the next stage are spread between
+  // MFMAs instead of issued in a burst; the operand reads of the next
+  // 16-deep sub-step go in between as well.
+  constexpr int kReadsPerPhase = NN ? 12 : 8;
+  auto pin_load_phase = [&]() {
+    sfor<8>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (DMA) load
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+    });
+    if constexpr (kReadsPerPhase > 8)
+      __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerPhase - 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto pin_phase = [&]() {
+    sfor<8>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerPhase / 8 + (NN ? 1 : 0), 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto bare_barrier = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    read_frags(sA0, sB0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+  };
+  // One K step: MFMAs on stage cur, then the next stage; loads for step
+  // kt+3 go into stage ld.  Before the barrier a wave waits until only the
+  // loads of steps kt+2 and kt+3 are outstanding (8 DMA loads per step)
+  // and its reads of stage cur are done; the barrier carries no fence (a
+  // fence would also wait for the loads still in flight).
+  constexpr int kLoadsPerStep = 8;
+  auto kstep = [&](const uint16_t* a_cur, const uint16_t* b_cur, const uint16_t* a_nxt,
+                   const uint16_t* b_nxt, uint16_t* a_ld, uint16_t* b_ld, int kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue_stage(a_ld, b_ld, kt + 3);
+    read_frags(a_cur, b_cur, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+    mfma_all(std::integral_constant<int, 0>{});
+    pin_load_phase();
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerStep));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    bare_barrier();
+    read_frags(a_nxt, b_nxt, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    mfma_all(std::integral_constant<int, 1>{});
+    pin_phase();
+  };
 
-    // one K step on stage cur, next stage nxt, loads for step kt+3 into ld
-    auto kstep = [&](const uint16_t* a_cur, const uint16_t* b_cur, const uint16_t* a_nxt,
-                     const uint16_t* b_nxt, uint16_t* a_ld, uint16_t* b_ld, int kt) {
-      __builtin_amdgcn_sched_barrier(0);
-      issue_stage(a_ld, b_ld, kt + 3);
-      read_frags(a_cur, b_cur, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
-      mfma_all(std::integral_constant<int, 0>{});
-      pin_load_phase();
-      // the stage of step kt+1 has landed (only steps kt+2, kt+3 in flight)
-      // and this wave's reads of stage kt are done; then a bare barrier
-      // (no fence: a fence would also wait for the loads still in flight)
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerStep));
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      read_frags(a_nxt, b_nxt, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-      mfma_all(std::integral_constant<int, 1>{});
-      pin_phase();
-    };
-    // whole rounds of 4 steps; steps past K run on zero-filled stages
+  // ---- persistent tile loop -------------------------------------------
+  // 4-stage pipeline, loads run 3 K steps ahead.  The K loop is unrolled by
+  // 4 so every stage is a distinct LDS array named statically (the compiler
+  // then sees that a load in flight never targets the stage being read);
+  // steps past the end of K load zeros.  The first three steps of the next
+  // tile are issued before the epilogue of the current one, so the pipeline
+  // fills while the epilogue runs.
+  int tile = vid;
+  TileInfo cur{};
+  if (tile < total) {
+    cur = tile_info(tile);
+    start_tile(cur);
+  }
+  while (tile < total) {
+    sfor<4>([&](auto mi) { sfor<4>([&](auto ni) { acc[mi][ni] = f32x16{}; }); });
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerStep));
+    bare_barrier();
+    read_frags(sA0, sB0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
     for (int kt = 0; kt < nk; kt += 4) {
       kstep(sA0, sB0, sA1, sB1, sA3, sB3, kt);
       kstep(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
       kstep(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
       kstep(sA3, sB3, sA0, sB0, sA2, sB2, kt + 3);
     }
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // drain the tail reloads
+    // the loads still in flight are zero fills; then every wave is done
+    // with the stages and the next tile may start loading
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    __syncthreads();
+    const TileInfo t0 = cur;
+    tile += G;
+    if (tile < total) {
+      cur = tile_info(tile);
+      start_tile(cur);
+    }
 
     // ------------------------------------------------------ epilogues ---
     TileCtx t;
-    t.row0 = row0;
-    t.rows_valid = rows_valid;
-    t.col0 = col0;
-    t.cols_valid = cols_valid;
-    t.n_t = n_t;
+    t.row0 = t0.row0;
+    t.rows_valid = t0.rows_valid;
+    t.col0 = t0.col0;
+    t.cols_valid = t0.cols_valid;
+    t.n_t = t0.n_t;
     t.m_lane = wm * kWaveM + (lane & 31);
     t.n_lane = wn * kWaveN + 4 * (lane >> 5);
     if constexpr (EPI == EPI_STORE) {
@@ -686,11 +715,16 @@ void grouped_gemm_kernel(GemmArgs g) {
         const float v = dp[mi] + __shfl_xor(dp[mi], 32, kWave);
         if (lane < 32) s_red[wn * BM + t.m_lane + mi * 32] = v;
       });
-      __syncthreads();
+      // LDS-only handoff: no fence, so the next tile's loads keep flying
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      bare_barrier();
       {
         const int m = tid;  // BM == kThreads
-        if (m < rows_valid) g.dp_part[(row0 + m) * g.n_part + n_t] = s_red[m] + s_red[BM + m];
+        if (m < t.rows_valid)
+          g.dp_part[(t.row0 + m) * g.n_part + t.n_t] = s_red[m] + s_red[BM + m];
       }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      bare_barrier();  // s_red is reused by the next tile
     }
   }
 }
