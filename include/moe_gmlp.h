@@ -65,6 +65,22 @@ typedef enum moe_status {
 /* MXFP8 block length ([TE] § "Challenge 2", Fig. 3). */
 #define MOE_MX_BLOCK 32
 
+/* MXFP8 tensors ([TE] § "Challenge 2", Fig. 3: E4M3 values sharing one
+ * E8M0 scale per 32 consecutive values).  The MXFP8 copy of an [R][K]
+ * operand, blocked along its contraction axis K, is two device buffers:
+ *   codes   u8 [R][K], E4M3 (bias 7, largest finite 448, no infinities)
+ *   scales  u8, R*K/32 bytes, E8M0 (value 2^(code - 127)), in the tiled
+ *           order the grouped GEMM reads: the scale of row r, block b
+ *           (columns [32b, 32b + 32)) is byte moe_mx_scale_offset(r, b, K)
+ *             = ((r / 32) * (K / 64) + b / 2) * 64 + (b % 2) * 32 + r % 32,
+ *           so one 64-byte run holds what a 32-row slice needs for a 64-deep
+ *           K step.  Needs R % 32 == 0 and K % 64 == 0.
+ * Encoding of a block v[0..31] (the bf16 values as stored):
+ *   e = clamp(floor(log2 max|v|) - 8, -127, 127), e = -127 for an all-zero
+ *   block; scale code e + 127; code_i = E4M3 round-to-nearest-even of
+ *   v_i / 2^e, saturated to +-448, sign kept (-0 gives 0x80). */
+int64_t moe_mx_scale_offset(int64_t r, int64_t b, int64_t K);
+
 typedef enum moe_act {
   MOE_ACT_SWIGLU = 0, /* Swish_beta(g) * u   ([FK] § GLU epilogue, eq. SwiGLU) */
   MOE_ACT_GEGLU = 1,  /* GELU(g) * u, exact erf form                           */
@@ -132,8 +148,9 @@ moe_status moe_weight_repack_interleave(const void* w1, void* w1i, int E,
  *     are not written.  Reads the map built by this or an earlier call.
  *     Used for X in the forward and for dOut in the backward.
  *   MOE_PERMUTE_WRITE_MX: also (or, with xp == NULL, only) write the MXFP8
- *     encoding of the gathered rows along H: xp_q u8 [M_cap][H] E4M3 codes,
- *     xp_s u8 [M_cap][H/32] E8M0 scales.
+ *     copy of the gathered rows blocked along H (codes xp_q u8 [M_cap][H],
+ *     tiled scales xp_s of M_cap*H/32 bytes, see MOE_MX_BLOCK); pad rows
+ *     get zero codes and scale code 0.  Needs H % 64 == 0, M_cap % 128 == 0.
  *   Requires H % 32 == 0 for GATHER, M_cap >= T*k + E*(MOE_GROUP_ALIGN-1)
  *   unless the caller knows the padded total fits (else MOE_DEVERR_MCAP_
  *   OVERFLOW is raised and rows past M_cap are dropped).
@@ -156,8 +173,8 @@ typedef struct moe_permute_args {
   float* probs_p;              /* [M_cap] device */
   const void* x;               /* bf16 [T][H]     device (GATHER) */
   void* xp;                    /* bf16 [M_cap][H] device (GATHER) */
-  uint8_t* xp_q;               /* u8 [M_cap][H]     (WRITE_MX) */
-  uint8_t* xp_s;               /* u8 [M_cap][H/32]  (WRITE_MX) */
+  uint8_t* xp_q;               /* u8 [M_cap][H]          (WRITE_MX) */
+  uint8_t* xp_s;               /* u8 M_cap*H/32, tiled   (WRITE_MX) */
   int32_t* err_flag;           /* optional device int32 */
   void* workspace;             /* device, BUILD_MAP only */
   size_t workspace_bytes;
@@ -191,16 +208,20 @@ moe_status moe_unpermute(const moe_unpermute_args* args, void* stream);
 /* ------------------------------------------------------------------------
  * moe_quantize_mxfp8 -- bf16 -> MXFP8 ([TE] § "Challenge 2", Fig. 3;
  *   § "Challenge 3": bf16 master weights are quantized before the
- *   low-precision GEMM).  Per block of 32 values v along the chosen axis:
- *     scale exponent e = clamp(floor(log2 max|v|) - 8, -127, 127) (-127 for
- *     an all-zero block), scale code = e + 127,
- *     code = E4M3 round-to-nearest-even of v / 2^e, saturated to +-448.
- *   MOE_QUANT_ROW: blocks along cols.  q [b][rows][cols], s [b][rows][cols/32]
- *   MOE_QUANT_COL: blocks along rows, written transposed so the consumer's K
- *     is contiguous: q [b][cols][rows], s [b][cols][rows/32]
- *   x bf16 [b][rows][cols] with x_stride elements between batch entries;
- *   rows and cols must be multiples of 32.  If amax != NULL, *amax is raised
- *   to max|x| (the caller zeroes it first).
+ *   low-precision GEMM).  Encoding and scale layout as under MOE_MX_BLOCK.
+ *   x bf16 [batch][rows][cols], x_stride elements between batch entries
+ *   (0: rows*cols; a multiple of 8).
+ *   MOE_QUANT_ROW: blocks along cols (K = cols): q [batch][rows][cols],
+ *     scales rows*cols/32 bytes per batch entry, tiled with R = rows.
+ *   MOE_QUANT_COL: blocks along rows, written transposed so that the
+ *     consumer's K = rows is contiguous: q [batch][cols][rows], scales
+ *     tiled with R = cols, K = rows.
+ *   The weight copies the MXFP8 forward and backward read are
+ *     ROW of w1i (K = H), ROW of w2 (K = I), COL of w2 (K = H) and COL of
+ *     w1i (K = N1).
+ *   rows and cols must be multiples of 64.  If amax != NULL, *amax is raised
+ *   to max|x| (the caller zeroes it first).  Memory-bound: reads 2 bytes and
+ *   writes 33/32 bytes per element.
  * ---------------------------------------------------------------------- */
 #define MOE_QUANT_ROW 0
 #define MOE_QUANT_COL 1
@@ -242,9 +263,22 @@ moe_status moe_quantize_mxfp8(const moe_quant_args* args, void* stream);
  *     amax optional device float: raised to max|a| over written rows (the
  *          call zeroes it first, so it holds this call's value)
  *   Requires H % 64 == 0, I % 64 == 0, E >= 1.
- *   prec == MOE_PREC_MXFP8 is reserved (MOE_ERR_UNSUPPORTED in this build).
  *   timing_events: optional hipEvent_t handles; non-NULL entries are recorded
  *   on `stream` before FC1, between FC1 and FC2, and after FC2.
+ *
+ *   prec == MOE_PREC_MXFP8 ([TE] § "Challenge 2"/"Challenge 3"; [FK] §
+ *   "Fused MXFP8 and NVFP4 quantization"): both GEMMs take MXFP8 operands
+ *   (E4M3 x E4M3 with E8M0 scales per 32 along K, fp32 accumulation):
+ *     FC1: xp_q/xp_s (moe_permute WRITE_MX) x w1_q/w1_s (ROW of w1i)
+ *     FC2: a_q/a_s x w2_q/w2_s (ROW of w2)
+ *   xp, w1i and w2 are not read.  The FC1 epilogue writes z and a as in
+ *   bf16 (a may be NULL), amax, and the MXFP8 copies of a, quantized from the
+ *   stored bf16 a: a_q/a_s blocked along I (the FC2 operand) and, if aT_q
+ *   and aT_s are both set, the transposed copy aT_q [I][M_cap] blocked along
+ *   M inside each group (scales tiled with R = I, K = M_cap).  Pad rows of a
+ *   group (up to the next multiple of MOE_GROUP_ALIGN) get zero codes and
+ *   scale code 0 in both copies.  Weights are contiguous per expert
+ *   (w1_stride / w2_stride are ignored).  Needs M_cap % 128 == 0.
  * ---------------------------------------------------------------------- */
 typedef struct moe_fwd_args {
   int32_t E, H, I;
@@ -266,6 +300,12 @@ typedef struct moe_fwd_args {
   void* yp;
   int32_t* err_flag;
   void* timing_events[3];
+  /* MXFP8 operands and outputs (prec == MOE_PREC_MXFP8 only) */
+  const uint8_t* xp_q;  const uint8_t* xp_s;   /* [M_cap][H]            */
+  const uint8_t* w1_q;  const uint8_t* w1_s;   /* [E][N1][H], along H   */
+  const uint8_t* w2_q;  const uint8_t* w2_s;   /* [E][H][I],  along I   */
+  uint8_t* a_q;   uint8_t* a_s;                /* [M_cap][I], along I   */
+  uint8_t* aT_q;  uint8_t* aT_s;               /* [I][M_cap], along M (optional) */
 } moe_fwd_args;
 
 moe_status moe_grouped_mlp_fwd(const moe_fwd_args* args, void* stream);
@@ -288,6 +328,19 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* args, void* stream);
  *   Needs workspace of moe_grouped_mlp_workspace_size(...) bytes (partial
  *   sums of dprobs_p).  timing_events as in the forward (before FC2 dgrad,
  *   between, after FC1 dgrad).
+ *
+ *   prec == MOE_PREC_MXFP8: both GEMMs take MXFP8 operands blocked along
+ *   their K:
+ *     FC2 dgrad: dyp_q/dyp_s (moe_permute WRITE_MX of dOut, along H) x
+ *                w2t_q/w2t_s (COL of w2: [E][I][H], along H)
+ *     FC1 dgrad: dz_q/dz_s x w1t_q/w1t_s (COL of w1i: [E][H][N1], along N1)
+ *   dyp, w2 and w1i are not read; z is read (bf16).  The dActivation
+ *   epilogue writes dz (bf16, may be NULL), dprobs_p, and the MXFP8 copies
+ *   of the stored bf16 dz: dz_q/dz_s [M_cap][N1] blocked along N1 (in the
+ *   interleaved column order; with the 64-row interleave every block holds
+ *   only gate or only up columns) and, if dzT_q and dzT_s are both set, the
+ *   transposed dzT_q [N1][M_cap] blocked along M inside each group.  Pad
+ *   rows as in the forward.  Needs M_cap % 128 == 0.
  * ---------------------------------------------------------------------- */
 typedef struct moe_bwd_args {
   int32_t E, H, I;
@@ -311,6 +364,12 @@ typedef struct moe_bwd_args {
   void* workspace;
   size_t workspace_bytes;
   void* timing_events[3];
+  /* MXFP8 operands and outputs (prec == MOE_PREC_MXFP8 only) */
+  const uint8_t* dyp_q; const uint8_t* dyp_s;  /* [M_cap][H]            */
+  const uint8_t* w2t_q; const uint8_t* w2t_s;  /* [E][I][H],  along H   */
+  const uint8_t* w1t_q; const uint8_t* w1t_s;  /* [E][H][N1], along N1  */
+  uint8_t* dz_q;  uint8_t* dz_s;               /* [M_cap][N1], along N1 */
+  uint8_t* dzT_q; uint8_t* dzT_s;              /* [N1][M_cap], along M (optional) */
 } moe_bwd_args;
 
 moe_status moe_grouped_mlp_bwd(const moe_bwd_args* args, void* stream);

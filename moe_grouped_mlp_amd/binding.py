@@ -29,6 +29,7 @@ EXPORTED_SYMBOLS = (
     "moe_permute", "moe_unpermute", "moe_quantize_mxfp8",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd",
     "moe_grouped_mlp_workspace_size", "moe_status_string", "moe_gmlp_version",
+    "moe_mx_scale_offset",
 )
 
 
@@ -80,7 +81,12 @@ class FwdArgs(ctypes.Structure):
                 ("w1_stride", c_int64), ("w2_stride", c_int64),
                 ("z", c_void_p), ("a", c_void_p), ("amax", c_void_p),
                 ("yp", c_void_p), ("err_flag", c_void_p),
-                ("timing_events", c_void_p * 3)]
+                ("timing_events", c_void_p * 3),
+                ("xp_q", c_void_p), ("xp_s", c_void_p),
+                ("w1_q", c_void_p), ("w1_s", c_void_p),
+                ("w2_q", c_void_p), ("w2_s", c_void_p),
+                ("a_q", c_void_p), ("a_s", c_void_p),
+                ("aT_q", c_void_p), ("aT_s", c_void_p)]
 
 
 class BwdArgs(ctypes.Structure):
@@ -94,7 +100,12 @@ class BwdArgs(ctypes.Structure):
                 ("dprobs_p", c_void_p), ("dxp", c_void_p),
                 ("err_flag", c_void_p), ("workspace", c_void_p),
                 ("workspace_bytes", c_size_t),
-                ("timing_events", c_void_p * 3)]
+                ("timing_events", c_void_p * 3),
+                ("dyp_q", c_void_p), ("dyp_s", c_void_p),
+                ("w2t_q", c_void_p), ("w2t_s", c_void_p),
+                ("w1t_q", c_void_p), ("w1t_s", c_void_p),
+                ("dz_q", c_void_p), ("dz_s", c_void_p),
+                ("dzT_q", c_void_p), ("dzT_s", c_void_p)]
 
 
 # ---- library loading ------------------------------------------------------
@@ -119,6 +130,8 @@ def lib() -> ctypes.CDLL:
             c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_void_p]
         L.moe_permute_workspace_size.restype = c_size_t
         L.moe_permute_workspace_size.argtypes = [c_int, c_int]
+        L.moe_mx_scale_offset.restype = c_int64
+        L.moe_mx_scale_offset.argtypes = [c_int64, c_int64, c_int64]
         L.moe_grouped_mlp_workspace_size.restype = c_size_t
         L.moe_grouped_mlp_workspace_size.argtypes = [
             c_int, c_int, c_int, c_int64, c_int, c_int]
@@ -218,30 +231,43 @@ def moe_grouped_mlp_workspace_size(E, H, I, M_cap, prec=PREC_BF16,
     return lib().moe_grouped_mlp_workspace_size(E, H, I, M_cap, prec, act)
 
 
+def moe_mx_scale_offset(r, b, K) -> int:
+    return lib().moe_mx_scale_offset(r, b, K)
+
+
 def moe_grouped_mlp_fwd(*, E, H, I, M_cap, split_sizes, padded_offsets,
-                        probs_p, xp, w1i, w2, a, yp, z=None, amax=None,
-                        act=None, prec=PREC_BF16, cu_margin=0, w1_stride=0,
-                        w2_stride=0, err_flag=None, timing_events=None,
-                        stream=None):
+                        probs_p, yp, xp=None, w1i=None, w2=None, a=None,
+                        z=None, amax=None, act=None, prec=PREC_BF16,
+                        cu_margin=0, w1_stride=0, w2_stride=0, err_flag=None,
+                        timing_events=None, xp_q=None, xp_s=None, w1_q=None,
+                        w1_s=None, w2_q=None, w2_s=None, a_q=None, a_s=None,
+                        aT_q=None, aT_s=None, stream=None):
     args = FwdArgs(E, H, I, M_cap, prec, act or act_params(), cu_margin,
                    _ptr(split_sizes), _ptr(padded_offsets), _ptr(probs_p),
                    _ptr(xp), _ptr(w1i), _ptr(w2), w1_stride, w2_stride,
                    _ptr(z), _ptr(a), _ptr(amax), _ptr(yp), _ptr(err_flag),
-                   _events(timing_events))
+                   _events(timing_events), _ptr(xp_q), _ptr(xp_s), _ptr(w1_q),
+                   _ptr(w1_s), _ptr(w2_q), _ptr(w2_s), _ptr(a_q), _ptr(a_s),
+                   _ptr(aT_q), _ptr(aT_s))
     _check("moe_grouped_mlp_fwd",
            lib().moe_grouped_mlp_fwd(ctypes.byref(args), _stream(stream)))
 
 
 def moe_grouped_mlp_bwd(*, E, H, I, M_cap, split_sizes, padded_offsets,
-                        probs_p, dyp, w2, z, w1i, dz, dprobs_p, dxp,
-                        workspace, act=None, prec=PREC_BF16, cu_margin=0,
-                        w1_stride=0, w2_stride=0, err_flag=None,
-                        timing_events=None, stream=None):
+                        probs_p, z, dprobs_p, dxp, workspace, dyp=None,
+                        w2=None, w1i=None, dz=None, act=None, prec=PREC_BF16,
+                        cu_margin=0, w1_stride=0, w2_stride=0, err_flag=None,
+                        timing_events=None, dyp_q=None, dyp_s=None,
+                        w2t_q=None, w2t_s=None, w1t_q=None, w1t_s=None,
+                        dz_q=None, dz_s=None, dzT_q=None, dzT_s=None,
+                        stream=None):
     args = BwdArgs(E, H, I, M_cap, prec, act or act_params(), cu_margin,
                    _ptr(split_sizes), _ptr(padded_offsets), _ptr(probs_p),
                    _ptr(dyp), _ptr(w2), _ptr(z), _ptr(w1i), w1_stride,
                    w2_stride, _ptr(dz), _ptr(dprobs_p), _ptr(dxp),
                    _ptr(err_flag), _ptr(workspace), _nbytes(workspace),
-                   _events(timing_events))
+                   _events(timing_events), _ptr(dyp_q), _ptr(dyp_s),
+                   _ptr(w2t_q), _ptr(w2t_s), _ptr(w1t_q), _ptr(w1t_s),
+                   _ptr(dz_q), _ptr(dz_s), _ptr(dzT_q), _ptr(dzT_s))
     _check("moe_grouped_mlp_bwd",
            lib().moe_grouped_mlp_bwd(ctypes.byref(args), _stream(stream)))

@@ -9,6 +9,10 @@ of a training step on the current stream:
             (FC2 dgrad + dGLU epilogue, FC1 dgrad) -> moe_unpermute (dX and
             dprobs)
 
+With prec=PREC_MXFP8 the permutes write MXFP8 rows (no bf16 copy), the four
+GEMMs take MXFP8 operands, and quantize_weights() (once per weight update)
+makes the four weight copies the GEMMs read, each blocked along its K.
+
 No call reads device memory back or synchronises, so a whole step can be
 captured in a HIP graph.
 """
@@ -26,19 +30,26 @@ class ExpertBlock:
     def __init__(self, E: int, H: int, I: int, T: int, k: int, *,
                  act: Optional[B.ActParams] = None, first_expert: int = 0,
                  M_cap: Optional[int] = None, cu_margin: int = 0,
+                 prec: int = B.PREC_BF16, transposed_copies: bool = True,
                  device="cuda"):
         self.E, self.H, self.I, self.T, self.k = E, H, I, T, k
         self.act = act or B.act_params()
         self.gated = self.act.act != B.ACT_SRELU
         self.N1 = 2 * I if self.gated else I
         self.first_expert = first_expert
-        self.M_cap = M_cap if M_cap is not None else T * k + E * (B.GROUP_ALIGN - 1)
+        self.prec = prec
+        self.mx = prec == B.PREC_MXFP8
+        M_cap = M_cap if M_cap is not None else T * k + E * (B.GROUP_ALIGN - 1)
+        if self.mx:
+            M_cap = -(-M_cap // B.GROUP_ALIGN) * B.GROUP_ALIGN
+        self.M_cap = M_cap
         self.cu_margin = cu_margin
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         f32 = dict(dtype=torch.float32, device=dev)
         bf = dict(dtype=torch.bfloat16, device=dev)
-        M = self.M_cap
+        u8 = dict(dtype=torch.uint8, device=dev)
+        M, N1 = self.M_cap, self.N1
         self.split_sizes = torch.zeros(E, **i32)
         self.offsets = torch.zeros(E + 1, **i32)
         self.padded_offsets = torch.zeros(E + 1, **i32)
@@ -48,40 +59,82 @@ class ExpertBlock:
         self.err_flag = torch.zeros(1, **i32)
         self.ws_route = torch.empty(max(1, B.moe_permute_workspace_size(T, E)),
                                     dtype=torch.uint8, device=dev)
-        self.xp = torch.empty(M, H, **bf)
-        self.z = torch.empty(M, self.N1, **bf)
+        self.z = torch.empty(M, N1, **bf)
         self.a = torch.empty(M, I, **bf)
         self.yp = torch.empty(M, H, **bf)
         self.out = torch.empty(T, H, **bf)
         self.amax = torch.zeros(1, **f32)
-        self.dyp = torch.empty(M, H, **bf)
-        self.dz = torch.empty(M, self.N1, **bf)
+        self.dz = torch.empty(M, N1, **bf)
         self.dprobs_p = torch.zeros(M, **f32)
         self.dxp = torch.empty(M, H, **bf)
         self.dx = torch.empty(T, H, **bf)
         self.dprobs = torch.zeros(T, k, **f32)
         self.ws_bwd = torch.empty(
-            max(1, B.moe_grouped_mlp_workspace_size(E, H, I, M, B.PREC_BF16,
+            max(1, B.moe_grouped_mlp_workspace_size(E, H, I, M, prec,
                                                     self.act.act)),
             dtype=torch.uint8, device=dev)
-        self.w1i = torch.empty(E, self.N1, H, **bf)
+        self.w1i = torch.empty(E, N1, H, **bf)
         self.w2 = torch.empty(E, H, I, **bf)
+
+        def mx_pair(*shape):
+            n = 1
+            for d in shape:
+                n *= d
+            return torch.empty(*shape, **u8), torch.empty(n // B.MX_BLOCK, **u8)
+
+        if self.mx:
+            self.xp = self.dyp = None
+            self.xp_q, self.xp_s = mx_pair(M, H)
+            self.dyp_q, self.dyp_s = mx_pair(M, H)
+            self.w1_q, self.w1_s = mx_pair(E, N1, H)      # along H
+            self.w2_q, self.w2_s = mx_pair(E, H, I)       # along I
+            self.w2t_q, self.w2t_s = mx_pair(E, I, H)     # along H
+            self.w1t_q, self.w1t_s = mx_pair(E, H, N1)    # along N1
+            self.a_q, self.a_s = mx_pair(M, I)
+            self.dz_q, self.dz_s = mx_pair(M, N1)
+            if transposed_copies:
+                self.aT_q, self.aT_s = mx_pair(I, M)
+                self.dzT_q, self.dzT_s = mx_pair(N1, M)
+            else:
+                self.aT_q = self.aT_s = self.dzT_q = self.dzT_s = None
+        else:
+            self.xp = torch.empty(M, H, **bf)
+            self.dyp = torch.empty(M, H, **bf)
 
     # ------------------------------------------------------------ weights --
     def load_weights(self, w1: torch.Tensor, w2: torch.Tensor) -> None:
         """w1: bf16 [E][N1][H] (gate rows then up rows), w2: bf16 [E][H][I].
-        The gated FC1 weight is repacked into the interleaved layout."""
+        The gated FC1 weight is repacked into the interleaved layout; with
+        MXFP8 the weight copies are then quantized."""
         if self.gated:
             B.moe_weight_repack_interleave(w1, self.w1i, self.E, self.I,
                                            self.H)
         else:
             self.w1i.copy_(w1)
         self.w2.copy_(w2)
+        if self.mx:
+            self.quantize_weights()
+
+    def quantize_weights(self) -> None:
+        """MXFP8 copies of the bf16 weights, each blocked along the K of the
+        GEMM that reads it: W1i along H (FC1), W2 along I (FC2), W2 along H
+        (FC2 dgrad, stored [E][I][H]) and W1i along N1 (FC1 dgrad, stored
+        [E][H][N1])."""
+        E, H, I, N1 = self.E, self.H, self.I, self.N1
+        for mode, x, rows, cols, q, sc in (
+                (B.QUANT_ROW, self.w1i, N1, H, self.w1_q, self.w1_s),
+                (B.QUANT_ROW, self.w2, H, I, self.w2_q, self.w2_s),
+                (B.QUANT_COL, self.w2, H, I, self.w2t_q, self.w2t_s),
+                (B.QUANT_COL, self.w1i, N1, H, self.w1t_q, self.w1t_s)):
+            B.moe_quantize_mxfp8(mode=mode, batch=E, rows=rows, cols=cols, x=x,
+                                 q=q, s=sc)
 
     # ------------------------------------------------------------ forward --
     def route(self, expert_idx: torch.Tensor, probs: torch.Tensor,
               x: Optional[torch.Tensor] = None) -> None:
-        flags = B.PERMUTE_BUILD_MAP | (B.PERMUTE_GATHER if x is not None else 0)
+        flags = B.PERMUTE_BUILD_MAP
+        if x is not None:
+            flags |= B.PERMUTE_GATHER | (B.PERMUTE_WRITE_MX if self.mx else 0)
         B.moe_permute(flags=flags, T=self.T, k=self.k, E=self.E, H=self.H,
                       M_cap=self.M_cap, first_expert=self.first_expert,
                       expert_idx=expert_idx, probs=probs,
@@ -89,26 +142,39 @@ class ExpertBlock:
                       padded_offsets=self.padded_offsets,
                       row_id_map=self.row_id_map, row_src=self.row_src,
                       probs_p=self.probs_p, x=x, xp=self.xp,
+                      xp_q=self.xp_q if self.mx else None,
+                      xp_s=self.xp_s if self.mx else None,
                       err_flag=self.err_flag, workspace=self.ws_route)
 
-    def gather(self, src: torch.Tensor, dst: torch.Tensor) -> None:
-        B.moe_permute(flags=B.PERMUTE_GATHER, T=self.T, k=self.k, E=self.E,
+    def gather(self, src: torch.Tensor, dst: Optional[torch.Tensor],
+               dst_q: Optional[torch.Tensor] = None,
+               dst_s: Optional[torch.Tensor] = None) -> None:
+        flags = B.PERMUTE_GATHER | (B.PERMUTE_WRITE_MX if dst_q is not None else 0)
+        B.moe_permute(flags=flags, T=self.T, k=self.k, E=self.E,
                       H=self.H, M_cap=self.M_cap,
                       first_expert=self.first_expert,
                       split_sizes=self.split_sizes,
                       padded_offsets=self.padded_offsets,
-                      row_id_map=self.row_id_map, x=src, xp=dst)
+                      row_id_map=self.row_id_map, x=src, xp=dst, xp_q=dst_q,
+                      xp_s=dst_s)
 
     def experts_forward(self, timing_events=None) -> None:
+        kw = {}
+        if self.mx:
+            kw = dict(xp_q=self.xp_q, xp_s=self.xp_s, w1_q=self.w1_q,
+                      w1_s=self.w1_s, w2_q=self.w2_q, w2_s=self.w2_s,
+                      a_q=self.a_q, a_s=self.a_s, aT_q=self.aT_q,
+                      aT_s=self.aT_s)
+        else:
+            kw = dict(xp=self.xp, w1i=self.w1i, w2=self.w2)
         B.moe_grouped_mlp_fwd(E=self.E, H=self.H, I=self.I, M_cap=self.M_cap,
                               split_sizes=self.split_sizes,
                               padded_offsets=self.padded_offsets,
-                              probs_p=self.probs_p, xp=self.xp, w1i=self.w1i,
-                              w2=self.w2, z=self.z, a=self.a, yp=self.yp,
-                              amax=self.amax, act=self.act,
-                              cu_margin=self.cu_margin,
+                              probs_p=self.probs_p, z=self.z, a=self.a,
+                              yp=self.yp, amax=self.amax, act=self.act,
+                              prec=self.prec, cu_margin=self.cu_margin,
                               err_flag=self.err_flag,
-                              timing_events=timing_events)
+                              timing_events=timing_events, **kw)
 
     def combine(self, yp: torch.Tensor, out: torch.Tensor,
                 dprobs: bool = False) -> None:
@@ -125,19 +191,28 @@ class ExpertBlock:
 
     # ----------------------------------------------------------- backward --
     def experts_backward(self, timing_events=None) -> None:
+        if self.mx:
+            kw = dict(dyp_q=self.dyp_q, dyp_s=self.dyp_s, w2t_q=self.w2t_q,
+                      w2t_s=self.w2t_s, w1t_q=self.w1t_q, w1t_s=self.w1t_s,
+                      dz_q=self.dz_q, dz_s=self.dz_s, dzT_q=self.dzT_q,
+                      dzT_s=self.dzT_s)
+        else:
+            kw = dict(dyp=self.dyp, w2=self.w2, w1i=self.w1i)
         B.moe_grouped_mlp_bwd(E=self.E, H=self.H, I=self.I, M_cap=self.M_cap,
                               split_sizes=self.split_sizes,
                               padded_offsets=self.padded_offsets,
-                              probs_p=self.probs_p, dyp=self.dyp, w2=self.w2,
-                              z=self.z, w1i=self.w1i, dz=self.dz,
+                              probs_p=self.probs_p, z=self.z, dz=self.dz,
                               dprobs_p=self.dprobs_p, dxp=self.dxp,
                               workspace=self.ws_bwd, act=self.act,
-                              cu_margin=self.cu_margin,
+                              prec=self.prec, cu_margin=self.cu_margin,
                               err_flag=self.err_flag,
-                              timing_events=timing_events)
+                              timing_events=timing_events, **kw)
 
     def backward(self, dout, timing_events=None):
-        self.gather(dout, self.dyp)
+        if self.mx:
+            self.gather(dout, None, self.dyp_q, self.dyp_s)
+        else:
+            self.gather(dout, self.dyp)
         self.experts_backward(timing_events)
         self.combine(self.dxp, self.dx, dprobs=True)
         return self.dx, self.dprobs

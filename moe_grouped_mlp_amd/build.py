@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_gmlp.so")
 
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "quant.hip", "gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -126,13 +126,16 @@ moe_status moe_permute(const moe_permute_args* a, void* stream) {
   if (!a->split_sizes || !a->padded_offsets || !a->row_id_map) return MOE_ERR_INVALID_ARG;
   const bool build = a->flags & MOE_PERMUTE_BUILD_MAP;
   const bool gather = a->flags & MOE_PERMUTE_GATHER;
-  if (a->flags & MOE_PERMUTE_WRITE_MX) return MOE_ERR_UNSUPPORTED;
+  const bool write_mx = a->flags & MOE_PERMUTE_WRITE_MX;
+  if (write_mx && (!gather || !a->xp_q || !a->xp_s || a->H % 64 != 0 || a->M_cap % 128 != 0))
+    return MOE_ERR_INVALID_ARG;
   if (build) {
     if (!a->expert_idx || !a->probs || !a->row_src || !a->probs_p) return MOE_ERR_INVALID_ARG;
     if (!a->workspace || a->workspace_bytes < moe_permute_workspace_size(a->T, a->E))
       return MOE_ERR_WORKSPACE;
   }
-  if (gather && (!a->x || !a->xp || a->H < 8 || a->H % 8 != 0)) return MOE_ERR_INVALID_ARG;
+  if (gather && (!a->x || (!a->xp && !write_mx) || a->H < 8 || a->H % 8 != 0))
+    return MOE_ERR_INVALID_ARG;
   int cu = 0;
   if (moe_status st = device_info(&cu)) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -156,10 +159,23 @@ moe_status moe_unpermute(const moe_unpermute_args* a, void* stream) {
   return launched(moe::launch_unpermute(*a, static_cast<hipStream_t>(stream)));
 }
 
+int64_t moe_mx_scale_offset(int64_t r, int64_t b, int64_t K) {
+  return ((r / 32) * (K / 64) + b / 2) * 64 + (b % 2) * 32 + r % 32;
+}
+
 moe_status moe_quantize_mxfp8(const moe_quant_args* a, void* stream) {
-  (void)stream;
-  if (!a) return MOE_ERR_INVALID_ARG;
-  return MOE_ERR_UNSUPPORTED;
+  if (!a || (a->mode != MOE_QUANT_ROW && a->mode != MOE_QUANT_COL) || a->batch < 0 ||
+      a->rows < 64 || a->cols < 64 || a->rows % 64 != 0 || a->cols % 64 != 0 || !a->x || !a->q ||
+      !a->s)
+    return MOE_ERR_INVALID_ARG;
+  const int64_t n = static_cast<int64_t>(a->rows) * a->cols;
+  if (a->x_stride != 0 && (a->x_stride < n || a->x_stride % 8 != 0)) return MOE_ERR_INVALID_ARG;
+  int cu = 0;
+  if (moe_status st = device_info(&cu)) return st;
+  if (a->batch == 0) return MOE_OK;
+  moe_quant_args b = *a;
+  if (b.x_stride == 0) b.x_stride = n;
+  return launched(moe::launch_quantize_mxfp8(b, static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_grouped_mlp_workspace_size(int E, int H, int I, int64_t M_cap, int prec, int act) {
@@ -181,8 +197,8 @@ static moe_status check_common(int E, int H, int I, int64_t M_cap, int prec,
       M_cap < 1 || M_cap > INT32_MAX || !act_ok(act) || cu_margin < 0)
     return MOE_ERR_INVALID_ARG;
   if (!split || !padded || !probs_p) return MOE_ERR_INVALID_ARG;
-  if (prec == MOE_PREC_MXFP8) return MOE_ERR_UNSUPPORTED;
-  if (prec != MOE_PREC_BF16) return MOE_ERR_INVALID_ARG;
+  if (prec != MOE_PREC_BF16 && prec != MOE_PREC_MXFP8) return MOE_ERR_INVALID_ARG;
+  if (prec == MOE_PREC_MXFP8 && M_cap % 128 != 0) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -191,11 +207,20 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   if (moe_status st = check_common(a->E, a->H, a->I, a->M_cap, a->prec, a->act, a->cu_margin,
                                    a->split_sizes, a->padded_offsets, a->probs_p))
     return st;
-  if (!a->xp || !a->w1i || !a->w2 || !a->a || !a->yp) return MOE_ERR_INVALID_ARG;
+  const bool mx = a->prec == MOE_PREC_MXFP8;
   const bool gated = a->act.act != MOE_ACT_SRELU;
   const int N1 = gated ? 2 * a->I : a->I;
-  if (a->w1_stride != 0 && a->w1_stride < static_cast<int64_t>(N1) * a->H) return MOE_ERR_INVALID_ARG;
-  if (a->w2_stride != 0 && a->w2_stride < static_cast<int64_t>(a->H) * a->I) return MOE_ERR_INVALID_ARG;
+  if (mx) {
+    if (!a->xp_q || !a->xp_s || !a->w1_q || !a->w1_s || !a->w2_q || !a->w2_s || !a->a_q ||
+        !a->a_s || !a->yp || ((a->aT_q != nullptr) != (a->aT_s != nullptr)))
+      return MOE_ERR_INVALID_ARG;
+  } else {
+    if (!a->xp || !a->w1i || !a->w2 || !a->a || !a->yp) return MOE_ERR_INVALID_ARG;
+    if (a->w1_stride != 0 && a->w1_stride < static_cast<int64_t>(N1) * a->H)
+      return MOE_ERR_INVALID_ARG;
+    if (a->w2_stride != 0 && a->w2_stride < static_cast<int64_t>(a->H) * a->I)
+      return MOE_ERR_INVALID_ARG;
+  }
   int cu = 0;
   if (moe_status st = device_info(&cu)) return st;
   if (a->cu_margin >= cu) return MOE_ERR_INVALID_ARG;
@@ -216,9 +241,23 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   // FC1: z = xp . W1i^T with the activation epilogue
   g.N = N1;
   g.K = a->H;
-  g.A = static_cast<const uint16_t*>(a->xp);
-  g.B = static_cast<const uint16_t*>(a->w1i);
-  g.b_stride = a->w1_stride ? a->w1_stride : static_cast<int64_t>(N1) * a->H;
+  if (mx) {
+    g.A = a->xp_q;
+    g.a_s = a->xp_s;
+    g.B = a->w1_q;
+    g.b_stride = static_cast<int64_t>(N1) * a->H;
+    g.b_s = a->w1_s;
+    g.b_s_stride = g.b_stride / 32;
+    g.mx_q = a->a_q;
+    g.mx_s = a->a_s;
+    g.mx_qT = a->aT_q;
+    g.mx_sT = a->aT_s;
+    g.mx_n = a->I;
+  } else {
+    g.A = a->xp;
+    g.B = a->w1i;
+    g.b_stride = a->w1_stride ? a->w1_stride : static_cast<int64_t>(N1) * a->H;
+  }
   g.C = static_cast<uint16_t*>(a->z);
   g.ldc = N1;
   g.act_out = static_cast<uint16_t*>(a->a);
@@ -226,7 +265,7 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   g.amax = a->amax;
   record(a->timing_events[0], s);
   if (moe_status st = launched(moe::launch_grouped_gemm(
-          g, moe::EPI_GLU, false, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, g.N), s)))
+          g, moe::EPI_GLU, false, mx, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, g.N), s)))
     return st;
   record(a->timing_events[1], s);
 
@@ -234,15 +273,25 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   moe::GemmArgs f = g;
   f.N = a->H;
   f.K = a->I;
-  f.A = static_cast<const uint16_t*>(a->a);
-  f.B = static_cast<const uint16_t*>(a->w2);
-  f.b_stride = a->w2_stride ? a->w2_stride : static_cast<int64_t>(a->H) * a->I;
+  if (mx) {
+    f.A = a->a_q;
+    f.a_s = a->a_s;
+    f.B = a->w2_q;
+    f.b_stride = static_cast<int64_t>(a->H) * a->I;
+    f.b_s = a->w2_s;
+    f.b_s_stride = f.b_stride / 32;
+    f.mx_q = f.mx_s = f.mx_qT = f.mx_sT = nullptr;
+  } else {
+    f.A = a->a;
+    f.B = a->w2;
+    f.b_stride = a->w2_stride ? a->w2_stride : static_cast<int64_t>(a->H) * a->I;
+  }
   f.C = static_cast<uint16_t*>(a->yp);
   f.ldc = a->H;
   f.act_out = nullptr;
   f.amax = nullptr;
   if (moe_status st = launched(moe::launch_grouped_gemm(
-          f, moe::EPI_STORE, false, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, f.N), s)))
+          f, moe::EPI_STORE, false, mx, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, f.N), s)))
     return st;
   record(a->timing_events[2], s);
   return MOE_OK;
@@ -253,12 +302,21 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
   if (moe_status st = check_common(a->E, a->H, a->I, a->M_cap, a->prec, a->act, a->cu_margin,
                                    a->split_sizes, a->padded_offsets, a->probs_p))
     return st;
-  if (!a->dyp || !a->w2 || !a->z || !a->w1i || !a->dz || !a->dprobs_p || !a->dxp)
-    return MOE_ERR_INVALID_ARG;
+  const bool mx = a->prec == MOE_PREC_MXFP8;
   const bool gated = a->act.act != MOE_ACT_SRELU;
   const int N1 = gated ? 2 * a->I : a->I;
-  if (a->w1_stride != 0 && a->w1_stride < static_cast<int64_t>(N1) * a->H) return MOE_ERR_INVALID_ARG;
-  if (a->w2_stride != 0 && a->w2_stride < static_cast<int64_t>(a->H) * a->I) return MOE_ERR_INVALID_ARG;
+  if (!a->z || !a->dprobs_p || !a->dxp) return MOE_ERR_INVALID_ARG;
+  if (mx) {
+    if (!a->dyp_q || !a->dyp_s || !a->w2t_q || !a->w2t_s || !a->w1t_q || !a->w1t_s ||
+        !a->dz_q || !a->dz_s || ((a->dzT_q != nullptr) != (a->dzT_s != nullptr)))
+      return MOE_ERR_INVALID_ARG;
+  } else {
+    if (!a->dyp || !a->w2 || !a->w1i || !a->dz) return MOE_ERR_INVALID_ARG;
+    if (a->w1_stride != 0 && a->w1_stride < static_cast<int64_t>(N1) * a->H)
+      return MOE_ERR_INVALID_ARG;
+    if (a->w2_stride != 0 && a->w2_stride < static_cast<int64_t>(a->H) * a->I)
+      return MOE_ERR_INVALID_ARG;
+  }
   const size_t need = moe_grouped_mlp_workspace_size(a->E, a->H, a->I, a->M_cap, a->prec,
                                                      a->act.act);
   if (!a->workspace || a->workspace_bytes < need) return MOE_ERR_WORKSPACE;
@@ -276,13 +334,28 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
   g.probs = a->probs_p;
   g.act = moe::to_actp(a->act);
 
-  // FC2 dgrad: dA = dyp . W2 (W2 [H][I] read as [K=H][N=I]) + dActivation
+  // FC2 dgrad: dA = dyp . W2 (contracting over H) + dActivation.  bf16 reads
+  // W2 [H][I] as [K=H][N=I]; MXFP8 reads its copy quantized along H, [I][H].
   const int n_part = static_cast<int>(dgrad_parts(a->I));
   g.N = a->I;
   g.K = a->H;
-  g.A = static_cast<const uint16_t*>(a->dyp);
-  g.B = static_cast<const uint16_t*>(a->w2);
-  g.b_stride = a->w2_stride ? a->w2_stride : static_cast<int64_t>(a->H) * a->I;
+  if (mx) {
+    g.A = a->dyp_q;
+    g.a_s = a->dyp_s;
+    g.B = a->w2t_q;
+    g.b_stride = static_cast<int64_t>(a->I) * a->H;
+    g.b_s = a->w2t_s;
+    g.b_s_stride = g.b_stride / 32;
+    g.mx_q = a->dz_q;
+    g.mx_s = a->dz_s;
+    g.mx_qT = a->dzT_q;
+    g.mx_sT = a->dzT_s;
+    g.mx_n = N1;
+  } else {
+    g.A = a->dyp;
+    g.B = a->w2;
+    g.b_stride = a->w2_stride ? a->w2_stride : static_cast<int64_t>(a->H) * a->I;
+  }
   g.C = static_cast<uint16_t*>(a->dz);
   g.ldc = N1;
   g.zin = static_cast<const uint16_t*>(a->z);
@@ -291,7 +364,7 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
   g.n_part = n_part;
   record(a->timing_events[0], s);
   if (moe_status st = launched(moe::launch_grouped_gemm(
-          g, moe::EPI_DGLU, true, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, g.N), s)))
+          g, moe::EPI_DGLU, !mx, mx, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, g.N), s)))
     return st;
   if (moe_status st = launched(moe::launch_dprobs_reduce(g.dp_part, n_part, a->split_sizes,
                                                          a->padded_offsets, a->E, a->M_cap,
@@ -299,7 +372,8 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
     return st;
   record(a->timing_events[1], s);
 
-  // FC1 dgrad: dxp = dz . W1i (W1i [N1][H] read as [K=N1][N=H])
+  // FC1 dgrad: dxp = dz . W1i (contracting over N1).  bf16 reads W1i [N1][H]
+  // as [K=N1][N=H]; MXFP8 reads its copy quantized along N1, [H][N1].
   moe::GemmArgs f{};
   f.E = a->E;
   f.M_cap = a->M_cap;
@@ -309,13 +383,22 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
   f.act = g.act;
   f.N = a->H;
   f.K = N1;
-  f.A = static_cast<const uint16_t*>(a->dz);
-  f.B = static_cast<const uint16_t*>(a->w1i);
-  f.b_stride = a->w1_stride ? a->w1_stride : static_cast<int64_t>(N1) * a->H;
+  if (mx) {
+    f.A = a->dz_q;
+    f.a_s = a->dz_s;
+    f.B = a->w1t_q;
+    f.b_stride = static_cast<int64_t>(a->H) * N1;
+    f.b_s = a->w1t_s;
+    f.b_s_stride = f.b_stride / 32;
+  } else {
+    f.A = a->dz;
+    f.B = a->w1i;
+    f.b_stride = a->w1_stride ? a->w1_stride : static_cast<int64_t>(N1) * a->H;
+  }
   f.C = static_cast<uint16_t*>(a->dxp);
   f.ldc = a->H;
   if (moe_status st = launched(moe::launch_grouped_gemm(
-          f, moe::EPI_STORE, true, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, f.N), s)))
+          f, moe::EPI_STORE, !mx, mx, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, f.N), s)))
     return st;
   record(a->timing_events[2], s);
   return MOE_OK;

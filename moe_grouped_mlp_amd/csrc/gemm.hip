@@ -7,35 +7,48 @@
 // § "Eliminating host-device synchronization and CPU launch overhead").
 //
 // Work decomposition
-//   * Tile 256 x 256 x 64 (BM x BN x BK), 4 waves of 64 lanes in a 2 x 2
-//     layout, each wave owning a 128 x 128 sub-tile as 4 x 4 blocks of the
-//     v_mfma_f32_32x32x16_bf16 instruction (fp32 accumulators, 256 per lane).
-//   * K-contiguous operands (activations A, and the weights of the forward
-//     GEMMs) go from HBM straight into a double-buffered LDS tile
-//     (buffer_load_dwordx4 ... lds, 2 x 64 KB): each lane fetches the 16-byte
-//     chunk that belongs at its LDS slot of the swizzled layout, so no VGPR
-//     staging and no ds_write.  One barrier per K step; the loads of step
-//     k+1 are in flight while step k runs.
-//   * MFMA operands are double-buffered in registers across the four 16-deep
-//     sub-steps of a K step; the last sub-step's MFMAs are issued after the
-//     barrier and after the first operand reads of the next stage, so LDS
-//     latency hides behind matrix work.
-//   * B comes either as [N][K] ("NT": forward GEMMs, W1 and W2 as stored) or
-//     as [K][N] ("NN": the dgrad GEMMs read the same weights along their
-//     other axis).  NN tiles are loaded to registers and transposed there
-//     (8 x 8 blocks of bf16 with v_perm_b32) before the LDS store, so both
-//     layouts feed the MFMA from the same K-contiguous LDS image.
-//   * LDS rows are 128 B (64 bf16); the 16-byte chunk c of row r is stored
-//     at chunk c ^ ((r ^ r >> 3) & 7), which keeps the MFMA operand reads
-//     (8 consecutive rows, same chunk) and the transposed NN stores (rows
-//     8 apart) free of bank conflicts.
+//   * Output tile 256 x 256, 4 waves of 64 lanes in a 2 x 2 layout, each wave
+//     owning a 128 x 128 sub-tile as 4 x 4 blocks of 32 x 32 MFMA outputs
+//     (fp32 accumulators, 256 per lane).
+//       bf16:  v_mfma_f32_32x32x16_bf16, 32-deep K steps (two MFMA K steps)
+//       MXFP8: v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, one E8M0
+//              scale per 32 K values per row), 64-deep K steps
+//     Either way a K step moves 64 bytes per operand row, so both share the
+//     loaders and the LDS image; a lane's MXFP8 operand (32 bytes) is exactly
+//     the pair of 16-byte chunks a bf16 lane reads for its two K sub-steps.
+//   * Operands go from HBM straight into LDS (buffer_load_dwordx4 ... lds):
+//     four stages of 2 x 16 KB, loads three K steps ahead of the MFMAs.  Each
+//     lane fetches the 16-byte chunk that belongs at its slot of the swizzled
+//     image, so there is no VGPR staging and no ds_write.  MXFP8 scales ride
+//     along: 1 KB per stage (8 row groups x 64 bytes for A and for B, the
+//     tiled scale layout), one dword DMA per wave.
+//   * K-contiguous operands ([rows][K]: activations, and the weights of every
+//     GEMM except the bf16 dgrad ones): LDS rows of 64 bytes, 16-byte chunk c
+//     of row r stored at c ^ ((r >> 2) & 3), which keeps the operand reads (16
+//     consecutive rows, same chunk, per LDS cycle) free of bank conflicts.
+//   * bf16 dgrad GEMMs read the weight along its other axis ([K][N]): the tile
+//     is copied as is (512-byte rows, chunk c at c ^ 4 (k % 8)) and the MFMA
+//     operand is read with ds_read_b64_tr_b16 (LDS transpose read).  MXFP8
+//     dgrad GEMMs instead take weight copies quantized along their K, so all
+//     MXFP8 operands are K-contiguous.
+//   * The K loop is unrolled by four over statically named stages, barriers
+//     carry no fence (a fence would also wait for loads in flight), and the
+//     loads of later stages are interleaved with the MFMAs.
+//       bf16:  the operands of a stage's second sub-step are read while the
+//              first sub-step's MFMAs run; the next stage is waited for in
+//              the middle of a step.
+//       MXFP8: the whole next stage is read into a second register set while
+//              the current one feeds the MFMAs, so a stage's LDS slot is free
+//              as soon as the step starts and loads run a full three steps
+//              ahead.
 //   * Persistent scheduling: every workgroup first builds, in LDS, the tile
 //     prefix over the experts (ceil(M_e / BM) * ceil(N / BN) tiles each),
 //     then walks tile ids with stride gridDim.  Consecutive workgroup ids
 //     are dispatched round-robin over the 8 XCDs, so ids are remapped to give
 //     each XCD a contiguous run of tiles; inside an expert tiles are ordered
 //     in bands of `group_m` row tiles so that the tiles an XCD holds at one
-//     time share their weight panels in that XCD's L2.
+//     time share their weight panels in that XCD's L2.  The first K steps of
+//     the next tile are issued before the epilogue of the current one.
 //
 // Epilogues (fp32 math on the accumulators, bf16 round-to-nearest-even):
 //   STORE  C = bf16(acc)                                     (FC2, FC1 dgrad)
@@ -52,10 +65,20 @@
 //          routing probability), reduced in fixed order by a second kernel
 //          (same section: the backward epilogue applies dSwiGLU to the GEMM
 //          output).
+//   With MXFP8, GLU and DGLU also encode their stored bf16 output (a, dz) as
+//   MXFP8 blocked along the row (the next GEMM's operand) and, optionally,
+//   transposed and blocked along M inside each group (§ "Fused MXFP8 and
+//   NVFP4 quantization": the epilogue writes the quantized tensor and its
+//   transposed copy).  A row block's 32 values sit in a lane and its partner
+//   (lane ^ 32); a column's 32 values sit in the 32 lanes of a half-wave and
+//   are reduced with DPP, and the transposed codes are regrouped by a 4 x 4
+//   byte transpose inside each quad so that every lane stores 4 rows of one
+//   column at once.
 #include <utility>
 
 #include "common.h"
 #include "kernels.h"
+#include "mx.h"
 
 namespace moe {
 namespace {
@@ -74,6 +97,8 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+constexpr int kStageS = 1024;  // bytes of MXFP8 scales per stage (A then B)
 
 // Compile-time loop: f(integral_constant<int, 0>) ... f(<N-1>), so indices
 // into accumulator arrays stay constants (registers, never scratch).
@@ -138,32 +163,60 @@ MOE_DEV void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds_block, int voff, int 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_block, 16, voff, soff, 0, 0);
 }
 
-// K-contiguous [256][BK] tile (BK = 32) straight from HBM into one LDS stage.
-// LDS image: row r = 64 bytes, 16-byte chunk c stored at c ^ ((r >> 2) & 3).
-// A 16-byte LDS read serves 16 lanes per cycle over 64 banks (256 bytes);
-// the operand reads touch 16 consecutive rows in one chunk, which this
-// swizzle spreads over all 16 bank groups.  Wave w fills the 1 KB blocks
-// 4w .. 4w+3; lane l of block b lands on row 16 b + l / 4, stored chunk
-// l % 4, so it fetches logical chunk (l % 4) ^ ((l / 16) % 4).
+// K-contiguous tile of 256 rows x 64 bytes (32 bf16 or 64 E4M3 values) of
+// a [rows][K] operand straight from HBM into one LDS stage.  LDS image: row
+// r = 64 bytes, 16-byte chunk c stored at c ^ ((r >> 2) & 3).  A 16-byte LDS
+// read serves 16 lanes per cycle over 64 banks (256 bytes); the operand
+// reads touch 16 consecutive rows in one chunk, which this swizzle spreads
+// over all 16 bank groups.  Wave w fills the 1 KB blocks 4w .. 4w+3; lane l
+// of block b lands on row 16 b + l / 4, stored chunk l % 4, so it fetches
+// logical chunk (l % 4) ^ ((l / 16) % 4).
 struct KLoader {
   __amdgpu_buffer_rsrc_t rsrc;
   int voff[4];  // bytes
 
-  MOE_DEV void init(const uint16_t* base, int64_t rows_avail, int ld, int wave, int lane) {
+  MOE_DEV void init(const void* base, int64_t rows_avail, int ld_bytes, int wave, int lane) {
     const int64_t rows = rows_avail < 256 ? rows_avail : 256;
-    rsrc = make_rsrc(base, static_cast<uint32_t>(rows * ld * 2));
+    rsrc = make_rsrc(base, static_cast<uint32_t>(rows * ld_bytes));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = 64 * wave + 16 * j + (lane >> 2);
       const int kc = (lane & 3) ^ ((lane >> 4) & 3);
-      voff[j] = (row * ld + kc * 8) * 2;
+      voff[j] = row * ld_bytes + kc * 16;
     }
   }
-  // valid == false: fill the stage with zeros (out-of-range offset)
-  MOE_DEV void issue(uint16_t* stage, int k0, int wave_s, bool valid) {
+  // kt: K step (64 bytes per row); valid == false fills the stage with zeros
+  MOE_DEV void issue(uint16_t* stage, int kt, int wave_s, bool valid) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      dma16(rsrc, stage + (4 * wave_s + j) * 512, valid ? voff[j] : kOutOfRange, valid ? k0 * 2 : 0);
+      dma16(rsrc, stage + (4 * wave_s + j) * 512, valid ? voff[j] : kOutOfRange, valid ? kt * 64 : 0);
+  }
+};
+
+// MXFP8 scales of one K step for a 256-row A tile and a 256-row B tile, in
+// the tiled layout: 8 row groups x 64 bytes each, copied to a 1 KB LDS stage
+// (A groups 0..7, then B groups 0..7).  Waves 0, 1 copy A groups 4w .. 4w+3,
+// waves 2, 3 copy B groups 4(w - 2) ..; lane l fetches bytes 4 (l % 16) .. +3
+// of group 4 (w % 2) + l / 16, which lands at LDS byte 4 l of its quarter.
+MOE_DEV void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, voff, soff, 0, 0);
+}
+
+struct ScaleLoader {
+  __amdgpu_buffer_rsrc_t rsrc;
+  int voff;
+
+  // s_tile: scales of the tile's first row group; groups_avail: row groups
+  // of 32 that exist from there on
+  MOE_DEV void init(const uint8_t* s_tile, int64_t groups_avail, int K, int wave, int lane) {
+    const int64_t groups = groups_avail < 8 ? (groups_avail > 0 ? groups_avail : 0) : 8;
+    const int per_group = (K / 64) * 64;
+    rsrc = make_rsrc(s_tile, static_cast<uint32_t>(groups * per_group));
+    voff = (4 * (wave & 1) + (lane >> 4)) * per_group + 4 * (lane & 15);
+  }
+  MOE_DEV void issue(uint8_t* stage, int kt, int wave_s, bool valid) {
+    dma4(rsrc, stage + (wave_s >> 1) * 512 + (wave_s & 1) * 256, valid ? voff : kOutOfRange,
+         valid ? kt * 64 : 0);
   }
 };
 
@@ -237,6 +290,110 @@ MOE_DEV void load_bf16x4(const uint16_t* p, float* v) {
   v[3] = __uint_as_float(w.y & 0xffff0000u);
 }
 
+// ------------------------------------------------ MXFP8 epilogue helpers ---
+// The MXFP8 copies an epilogue writes of its [M_cap][n] bf16 output.
+struct MxOut {
+  uint8_t* q;     // rowwise codes [M_cap][n]
+  uint8_t* s;     // their scales, tiled (R = M_cap, K = n)
+  uint8_t* qT;    // transposed codes [n][M_cap] (nullable)
+  uint8_t* sT;    // their scales, tiled (R = n, K = M_cap)
+  int n;
+  int64_t M_cap;
+};
+
+template <int CTRL>
+MOE_DEV uint32_t dpp_u(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+MOE_DEV float dpp_f(float x) { return __uint_as_float(dpp_u<CTRL>(__float_as_uint(x))); }
+
+// Maximum over the 32 lanes of each half-wave: within quads (xor 1, xor 2),
+// then the mirrored quad of each 8 and the mirrored 8 of each 16 (DPP), then
+// the other 16 lanes of the half (ds_swizzle, lane ^ 16).
+MOE_DEV float half_wave_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  x = fmaxf(x, dpp_f<0x141>(x));
+  x = fmaxf(x, dpp_f<0x140>(x));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));
+  return x;
+}
+
+MOE_DEV uint32_t mx_codes4v(const float* v, const float* inv) {
+  float c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_fmed3f(v[i] * inv[i], -448.0f, 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// A lane's 16 values of one 32 x 32 output block: v[4 rg + i] is column
+// 8 rg + 4 hf + i (hf = lane / 32) of the lane's row (lane % 32), the
+// values being bf16 numbers (zero for rows that hold no data).
+//
+// Rowwise: the row's 32 values are this lane's and its partner's (lane ^ 32);
+// codes go to q_row[0 .. 31], the scale to *s_byte.
+MOE_DEV void mx_row_block(const float (&v)[16], uint8_t* q_row, uint8_t* s_byte, int hf) {
+  float am = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(v[r]));
+  am = fmaxf(am, __shfl_xor(am, 32, kWave));
+  const int e = mx_exponent(am);
+  const float inv = mx_inv_scale(e);
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg)
+    *reinterpret_cast<uint32_t*>(q_row + 8 * rg + 4 * hf) =
+        mx_codes4(v[4 * rg], v[4 * rg + 1], v[4 * rg + 2], v[4 * rg + 3], inv);
+  if (hf == 0) *s_byte = mx_scale_code(e);
+}
+
+// Transposed: column c of the block is one MX block of the transposed copy
+// (rows 32 rb .. 32 rb + 31), held by the 32 lanes of a half-wave.  Each lane
+// encodes its row's 4 columns of a run (one word), then a 4 x 4 byte
+// transpose inside the quad (DPP + v_perm_b32) leaves lane j of quad q4 with
+// column 8 rg + 4 hf + j of rows 4 q4 .. 4 q4 + 3, stored as one word.
+MOE_DEV void mx_col_block(const float (&v)[16], const MxOut& o, int64_t rb, int col0, int lane) {
+  const int hf = lane >> 5, j = lane & 3, q4 = (lane & 31) >> 2;
+  const uint32_t sel1 = (lane & 1) ? 0x03070105u : 0x06020400u;
+  const uint32_t sel2 = (lane & 2) ? 0x03020706u : 0x05040100u;
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) {
+    int e[4];
+    float inv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e[i] = mx_exponent(half_wave_max(fabsf(v[4 * rg + i])));
+      inv[i] = mx_inv_scale(e[i]);
+    }
+    const uint32_t d = mx_codes4v(&v[4 * rg], inv);
+    const uint32_t t = __builtin_amdgcn_perm(dpp_u<0xB1>(d), d, sel1);
+    const uint32_t w = __builtin_amdgcn_perm(dpp_u<0x4E>(t), t, sel2);
+    const int col = col0 + 8 * rg + 4 * hf + j;
+    *reinterpret_cast<uint32_t*>(o.qT + static_cast<int64_t>(col) * o.M_cap + rb * 32 + 4 * q4) = w;
+    if (q4 == 0) {
+      const int ej = j == 0 ? e[0] : j == 1 ? e[1] : j == 2 ? e[2] : e[3];
+      o.sT[mx_scale_off(col, rb, o.M_cap)] = mx_scale_code(ej);
+    }
+  }
+}
+
+// Both MXFP8 copies of one block whose rows all lie before the group's
+// padded end.
+MOE_DEV void mx_block_out(const float (&v)[16], const MxOut& o, int64_t row, int64_t rb, int col0,
+                          int lane) {
+  mx_row_block(v, o.q + row * o.n + col0, o.s + mx_scale_off(row, col0 / 32, o.n), lane >> 5);
+  if (o.qT) mx_col_block(v, o, rb, col0, lane);
+}
+
+MOE_DEV void bf16x4_to_f32(uint2 w, float* v) {
+  v[0] = __uint_as_float(w.x << 16);
+  v[1] = __uint_as_float(w.x & 0xffff0000u);
+  v[2] = __uint_as_float(w.y << 16);
+  v[3] = __uint_as_float(w.y & 0xffff0000u);
+}
+
 // ------------------------------------------------------------ epilogues ---
 // Where a tile's outputs sit in a lane.  The MFMA is issued with B as its
 // first operand, so each 32x32 block holds C^T: lane l owns output row
@@ -247,6 +404,7 @@ struct TileCtx {
   int rows_valid;   // rows of the tile that belong to the expert
   int col0;         // first output column
   int cols_valid;   // output columns inside N (multiple of 64)
+  int rows_pad;     // rows of the tile before the group's padded end
   int n_t;          // column-tile index
   int m_lane;       // row of this lane inside the tile, block mi = 0
   int n_lane;       // first column of this lane inside the tile, block 0
@@ -415,6 +573,178 @@ MOE_DEV void epi_dglu(const f32x16 (&acc)[4][4], const uint16_t* __restrict__ zi
   });
 }
 
+// EPI_GLU with MXFP8 copies of a (see epi_glu).  Rows of a 32-row block
+// past the group's data but before its padded end get zero codes; a block
+// past the padded end is not touched (it belongs to the next group).
+template <int ACT>
+MOE_DEV float epi_glu_mx(const f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz,
+                         uint16_t* __restrict__ a, int64_t lda, const float* __restrict__ probs,
+                         const ActP& act, const TileCtx& t, int wn, int wm, int lane,
+                         const MxOut& mo) {
+  constexpr bool gated = ACT != MOE_ACT_SRELU;
+  const int hf = lane >> 5;
+  float amax = 0.0f;
+  sfor<4>([&](auto mi) {
+    const int m = t.m_lane + mi * 32;
+    const bool row_ok = m < t.rows_valid;
+    const int blk = wm * kWaveM + mi * 32;
+    const bool blk_ok = blk < t.rows_pad;
+    const int64_t row = t.row0 + m;
+    const int64_t rb = (t.row0 + blk) / 32;
+    const float p = row_ok ? probs[row] : 0.0f;
+    if constexpr (gated) {
+      if (wn * kWaveN < t.cols_valid) {
+        const int q = (t.col0 + wn * kWaveN) / (2 * MOE_INTERLEAVE);
+        sfor<2>([&](auto h) {
+          float ab[16];
+          sfor<4>([&](auto rg) {
+            const int c = h * 32 + 8 * rg + 4 * hf;
+            if (row_ok && z) {
+              uint16_t* zrow = z + row * ldz + t.col0 + wn * kWaveN + c;
+              store_bf16x4(zrow, acc[mi][h], 4 * rg);
+              store_bf16x4(zrow + MOE_INTERLEAVE, acc[mi][h + 2], 4 * rg);
+            }
+            float av[4];
+            sfor<4>([&](auto i) {
+              av[i] = p * glu_eval<ACT>(acc[mi][h][4 * rg + i], acc[mi][h + 2][4 * rg + i], act).s;
+            });
+            uint2 w = make_uint2(pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]));
+            if (!row_ok) w = make_uint2(0, 0);
+            if (row_ok && a)
+              *reinterpret_cast<uint2*>(a + row * lda + q * MOE_INTERLEAVE + c) = w;
+            bf16x4_to_f32(w, &ab[4 * rg]);
+          });
+#pragma unroll
+          for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ab[r]));
+          if (blk_ok) mx_block_out(ab, mo, row, rb, q * MOE_INTERLEAVE + h * 32, lane);
+        });
+      }
+    } else {
+      sfor<4>([&](auto ni) {
+        if (wn * kWaveN + ni * 32 < t.cols_valid) {
+          const int cb = t.col0 + wn * kWaveN + ni * 32;
+          float ab[16];
+          sfor<4>([&](auto rg) {
+            const int n = cb + 8 * rg + 4 * hf;
+            if (row_ok && z) store_bf16x4(z + row * ldz + n, acc[mi][ni], 4 * rg);
+            float av[4];
+            sfor<4>([&](auto i) {
+              const float zc = fminf(fmaxf(acc[mi][ni][4 * rg + i], act.glo), act.ghi);
+              const float rl = fmaxf(zc, 0.0f);
+              av[i] = p * rl * rl;
+            });
+            uint2 w = make_uint2(pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]));
+            if (!row_ok) w = make_uint2(0, 0);
+            if (row_ok && a) *reinterpret_cast<uint2*>(a + row * lda + n) = w;
+            bf16x4_to_f32(w, &ab[4 * rg]);
+          });
+#pragma unroll
+          for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ab[r]));
+          if (blk_ok) mx_block_out(ab, mo, row, rb, cb, lane);
+        }
+      });
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  return amax;
+}
+
+// EPI_DGLU with MXFP8 copies of dz (see epi_dglu; pad rows as in
+// epi_glu_mx).  With the 64-column interleave a 32-column block of dz holds
+// only gate or only up columns.
+template <int ACT>
+MOE_DEV void epi_dglu_mx(const f32x16 (&acc)[4][4], const uint16_t* __restrict__ zin, int64_t ldz,
+                         uint16_t* __restrict__ dz, int64_t lddz, const float* __restrict__ probs,
+                         const ActP& act, const TileCtx& t, int wn, int wm, int lane,
+                         float (&dp_out)[4], const MxOut& mo) {
+  constexpr bool gated = ACT != MOE_ACT_SRELU;
+  const int h4 = 4 * (lane >> 5);
+  const int lane_col = gated ? 2 * t.col0 + 256 * wn + h4 : t.col0 + 128 * wn + h4;
+  sfor<4>([&](auto mi) {
+    const int m = t.m_lane + mi * 32;
+    const bool row_ok = m < t.rows_valid;
+    const int blk = wm * kWaveM + mi * 32;
+    const bool blk_ok = blk < t.rows_pad;
+    const int64_t row = t.row0 + m;
+    const int64_t rb = (t.row0 + blk) / 32;
+    const float p = row_ok ? probs[row] : 0.0f;
+    float dp = 0.0f;
+    uint2 zg[4][4], zu[4][4];
+    const uint16_t* zb = zin + row * ldz + lane_col;
+    sfor<4>([&](auto ni) { sfor<4>([&](auto rg) {
+      zg[ni][rg] = make_uint2(0, 0);
+      zu[ni][rg] = make_uint2(0, 0);
+      if (row_ok && wn * kWaveN + ni * 32 < t.cols_valid) {
+        if constexpr (gated) {
+          constexpr int off = 128 * (ni / 2) + 32 * (ni % 2) + 8 * rg;
+          zg[ni][rg] = *reinterpret_cast<const uint2*>(zb + off);
+          zu[ni][rg] = *reinterpret_cast<const uint2*>(zb + off + MOE_INTERLEAVE);
+        } else {
+          constexpr int off = 32 * ni + 8 * rg;
+          zg[ni][rg] = *reinterpret_cast<const uint2*>(zb + off);
+        }
+      }
+    }); });
+    sfor<4>([&](auto ni) {
+      if (wn * kWaveN + ni * 32 < t.cols_valid) {
+        float gv[16], uv[16];
+        sfor<4>([&](auto rg) {
+          float gz[4], uz[4];
+          bf16x4_to_f32(zg[ni][rg], gz);
+          if constexpr (gated) {
+            constexpr int off = 128 * (ni / 2) + 32 * (ni % 2) + 8 * rg;
+            bf16x4_to_f32(zu[ni][rg], uz);
+            float dg[4], du[4];
+            sfor<4>([&](auto i) {
+              const float da = acc[mi][ni][4 * rg + i];
+              const GluVal v = glu_eval<ACT>(gz[i], uz[i], act);
+              const float ds = p * da;
+              dg[i] = v.g_in ? ds * v.u * v.df : 0.0f;
+              du[i] = v.u_in ? ds * v.f : 0.0f;
+              dp += da * v.s;
+            });
+            uint2 wg = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+            uint2 wu = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+            if (!row_ok) wg = wu = make_uint2(0, 0);
+            if (row_ok && dz) {
+              uint16_t* db = dz + row * lddz + lane_col;
+              *reinterpret_cast<uint2*>(db + off) = wg;
+              *reinterpret_cast<uint2*>(db + off + MOE_INTERLEAVE) = wu;
+            }
+            bf16x4_to_f32(wg, &gv[4 * rg]);
+            bf16x4_to_f32(wu, &uv[4 * rg]);
+          } else {
+            constexpr int off = 32 * ni + 8 * rg;
+            float d[4];
+            sfor<4>([&](auto i) {
+              const float da = acc[mi][ni][4 * rg + i];
+              const bool in = (gz[i] >= act.glo) && (gz[i] <= act.ghi);
+              const float rl = fmaxf(fminf(fmaxf(gz[i], act.glo), act.ghi), 0.0f);
+              d[i] = in ? p * da * 2.0f * rl : 0.0f;
+              dp += da * rl * rl;
+            });
+            uint2 w = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+            if (!row_ok) w = make_uint2(0, 0);
+            if (row_ok && dz) *reinterpret_cast<uint2*>(dz + row * lddz + lane_col + off) = w;
+            bf16x4_to_f32(w, &gv[4 * rg]);
+          }
+        });
+        if (blk_ok) {
+          if constexpr (gated) {
+            const int cbg = 2 * t.col0 + 256 * wn + 128 * (ni / 2) + 32 * (ni % 2);
+            mx_block_out(gv, mo, row, rb, cbg, lane);
+            mx_block_out(uv, mo, row, rb, cbg + MOE_INTERLEAVE, lane);
+          } else {
+            mx_block_out(gv, mo, row, rb, t.col0 + 128 * wn + 32 * ni, lane);
+          }
+        }
+      }
+    });
+    dp_out[mi] = dp;
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
 // ------------------------------------------------------- block helpers ---
 // Exclusive scan of one int per thread over the 256-thread block.
 MOE_DEV int block_exclusive_scan(int v, int* s_tmp, int& total) {
@@ -440,11 +770,17 @@ MOE_DEV int block_exclusive_scan(int v, int* s_tmp, int& total) {
 }
 
 // ---------------------------------------------------------------- kernel --
-template <int EPI, bool NN, int ACT>
+// MX: A and B are E4M3 codes with tiled E8M0 scales (a_s, b_s); NN is then
+// false.  The GLU / DGLU epilogues also write the MXFP8 copies of their
+// output when MX.
+template <int EPI, bool NN, int ACT, bool MX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_kernel(GemmArgs g) {
+  static_assert(!(MX && NN), "MXFP8 operands are always K-contiguous");
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[kStageA], sA1[kStageA], sA2[kStageA], sA3[kStageA];
   __shared__ __attribute__((aligned(1024))) uint16_t sB0[kStageB], sB1[kStageB], sB2[kStageB], sB3[kStageB];
+  constexpr int kScaleBytes = MX ? kStageS : 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t sS0[kScaleBytes], sS1[kScaleBytes], sS2[kScaleBytes], sS3[kScaleBytes];
   __shared__ int s_start[kMaxExperts + 1];
   __shared__ int s_split[kMaxExperts];
   __shared__ int s_pad[kMaxExperts];
@@ -458,6 +794,7 @@ void grouped_gemm_kernel(GemmArgs g) {
   const int wm = wave >> 1, wn = wave & 1;
   const int E = g.E;
   const int tiles_n = (g.N + BN - 1) / BN;
+  constexpr int kElem = MX ? 1 : 2;  // bytes per operand element
 
   // ---- tile prefix over the experts (device-resident group sizes) ----
   const int per = (E + kThreads - 1) / kThreads;
@@ -516,10 +853,14 @@ void grouped_gemm_kernel(GemmArgs g) {
         btr_off[h][ni] = row * 512 + (c ^ (4 * (row & 7))) * 16 + 8 * (sl & 1);
       }
   }
+  // MXFP8 scale bytes of this lane's rows (row group 4 wm + mi of A, 4 wn + ni
+  // of B) for its K block (lane / 32) inside a scale stage
+  const int sa_off = 4 * wm * 64 + lane;
+  const int sb_off = 512 + 4 * wn * 64 + lane;
 
   // ---- per-tile geometry --------------------------------------------
   struct TileInfo {
-    int e, n_t, col0, cols_valid, rows_valid;
+    int e, n_t, col0, cols_valid, rows_valid, rows_pad;
     int64_t row0;
   };
   auto tile_info = [&](int tile) {
@@ -544,39 +885,68 @@ void grouped_gemm_kernel(GemmArgs g) {
     // zeros (its row range is empty) and stores nothing
     ti.rows_valid = static_cast<int>(
         min(static_cast<int64_t>(min(BM, s_split[ti.e] - m_t * BM)), g.M_cap - ti.row0));
+    const int padded_rows =
+        (s_split[ti.e] + MOE_GROUP_ALIGN - 1) / MOE_GROUP_ALIGN * MOE_GROUP_ALIGN;
+    ti.rows_pad = static_cast<int>(
+        min(static_cast<int64_t>(min(BM, padded_rows - m_t * BM)), g.M_cap - ti.row0));
     ti.col0 = ti.n_t * BN;
     ti.cols_valid = min(BN, g.N - ti.col0);
     return ti;
   };
 
-  const int nk = g.K / BK;
+  const int nk = g.K / (MX ? 64 : BK);
+  const char* A = static_cast<const char*>(g.A);
+  const char* B = static_cast<const char*>(g.B);
   KLoader la;
   KLoader lb_k;
   NLoader lb_n;
-  auto issue_stage = [&](uint16_t* a_st, uint16_t* b_st, int kt) {
+  ScaleLoader ls;
+  auto issue_stage = [&](uint16_t* a_st, uint16_t* b_st, uint8_t* s_st, int kt) {
     const bool valid = kt < nk;
-    la.issue(a_st, kt * BK, wave_s, valid);
+    la.issue(a_st, kt, wave_s, valid);
     if constexpr (NN) lb_n.issue(b_st, kt * BK, wave_s, valid);
-    else lb_k.issue(b_st, kt * BK, wave_s, valid);
+    else lb_k.issue(b_st, kt, wave_s, valid);
+    if constexpr (MX) ls.issue(s_st, kt, wave_s, valid);
   };
-  // point the loaders at a tile and start its first three K steps
+  // point the loaders at a tile and start its first K steps (three for
+  // bf16, four for MXFP8)
   auto start_tile = [&](const TileInfo& ti) {
     const int64_t rows_avail = ti.rows_valid > 0 ? g.M_cap - ti.row0 : 0;
-    la.init(g.A + (ti.rows_valid > 0 ? ti.row0 : 0) * g.K, rows_avail, g.K, wave, lane);
-    const uint16_t* Bexp = g.B + static_cast<int64_t>(ti.e) * g.b_stride;
+    const int64_t arow0 = ti.rows_valid > 0 ? ti.row0 : 0;
+    la.init(A + arow0 * g.K * kElem, rows_avail, g.K * kElem, wave, lane);
+    const char* Bexp = B + static_cast<int64_t>(ti.e) * g.b_stride * kElem;
     if constexpr (NN) {
-      lb_n.init(Bexp, static_cast<uint32_t>(static_cast<int64_t>(g.K) * g.N * 2), g.N, ti.col0,
-                wave, lane);
+      lb_n.init(reinterpret_cast<const uint16_t*>(Bexp),
+                static_cast<uint32_t>(static_cast<int64_t>(g.K) * g.N * 2), g.N, ti.col0, wave, lane);
     } else {
-      lb_k.init(Bexp + static_cast<int64_t>(ti.col0) * g.K, g.N - ti.col0, g.K, wave, lane);
+      lb_k.init(Bexp + static_cast<int64_t>(ti.col0) * g.K * kElem, g.N - ti.col0, g.K * kElem,
+                wave, lane);
     }
-    issue_stage(sA0, sB0, 0);
-    issue_stage(sA1, sB1, 1);
-    issue_stage(sA2, sB2, 2);
+    if constexpr (MX) {
+      // waves 0, 1 copy the A scales, waves 2, 3 the B scales (a uniform
+      // choice, so the buffer descriptor stays in scalar registers)
+      const int64_t per_group = (g.K / 64) * 64;
+      const bool a_side = wave_s < 2;
+      const uint8_t* sbase =
+          a_side ? g.a_s + (arow0 / 32) * per_group
+                 : g.b_s + static_cast<int64_t>(ti.e) * g.b_s_stride + (ti.col0 / 32) * per_group;
+      ls.init(sbase, a_side ? rows_avail / 32 : (g.N - ti.col0) / 32, g.K, wave, lane);
+    }
+    issue_stage(sA0, sB0, sS0, 0);
+    issue_stage(sA1, sB1, sS1, 1);
+    issue_stage(sA2, sB2, sS2, 2);
+    if constexpr (MX) issue_stage(sA3, sB3, sS3, 3);
   };
 
-  bf16x8 fa[2][4], fb[2][4];
   f32x16 acc[4][4];
+  auto bare_barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // ------------------------------------------------------ bf16 K loop ---
+  bf16x8 fa[2][4], fb[2][4];
   // operands of the 16-deep sub-step ks of a stage into register set buf
   auto read_frags = [&](const uint16_t* a_st, const uint16_t* b_st, auto ks, auto buf) {
     const char* ca = reinterpret_cast<const char*>(a_st);
@@ -629,11 +999,6 @@ void grouped_gemm_kernel(GemmArgs g) {
     });
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto bare_barrier = [&]() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
   // One K step: MFMAs on stage cur, then the next stage; loads for step
   // kt+3 go into stage ld.  Before the barrier a wave waits until only the
   // loads of steps kt+2 and kt+3 are outstanding (8 DMA loads per step)
@@ -643,7 +1008,7 @@ void grouped_gemm_kernel(GemmArgs g) {
   auto kstep = [&](const uint16_t* a_cur, const uint16_t* b_cur, const uint16_t* a_nxt,
                    const uint16_t* b_nxt, uint16_t* a_ld, uint16_t* b_ld, int kt) {
     __builtin_amdgcn_sched_barrier(0);
-    issue_stage(a_ld, b_ld, kt + 3);
+    issue_stage(a_ld, b_ld, nullptr, kt + 3);
     read_frags(a_cur, b_cur, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
     mfma_all(std::integral_constant<int, 0>{});
     pin_load_phase();
@@ -655,13 +1020,71 @@ void grouped_gemm_kernel(GemmArgs g) {
     pin_phase();
   };
 
+  // ----------------------------------------------------- MXFP8 K loop ---
+  // A lane's operand for one 64-deep step is the two 16-byte chunks at
+  // a_off[0] and a_off[1] (K 16h .. 16h+15 and 32+16h .. 32+16h+15, h =
+  // lane / 32), the layout v_mfma_scale_f32_32x32x64_f8f6f4 takes; its scale
+  // operand is the E8M0 byte of the lane's row for K block h.
+  i32x8 qa[2][4], qb[2][4];
+  int sca[2][4], scb[2][4];
+  auto read_frags_mx = [&](const uint16_t* a_st, const uint16_t* b_st, const uint8_t* s_st,
+                           auto buf) {
+    const char* ca = reinterpret_cast<const char*>(a_st);
+    const char* cb = reinterpret_cast<const char*>(b_st);
+    sfor<4>([&](auto i) {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(ca + a_off[0] + i * 32 * 64);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(ca + a_off[1] + i * 32 * 64);
+      qa[buf][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    });
+    sfor<4>([&](auto i) {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(cb + b_off[0] + i * 32 * 64);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(cb + b_off[1] + i * 32 * 64);
+      qb[buf][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    });
+    sfor<4>([&](auto i) {
+      sca[buf][i] = s_st[sa_off + i * 64];
+      scb[buf][i] = s_st[sb_off + i * 64];
+    });
+  };
+  auto mfma_all_mx = [&](auto buf) {
+    sfor<4>([&](auto mi) { sfor<4>([&](auto ni) {
+      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          qb[buf][ni], qa[buf][mi], acc[mi][ni], 0, 0, 0, scb[buf][ni], 0, sca[buf][mi]);
+    }); });
+  };
+  // per step: 9 DMA loads per wave (4 A, 4 B, 1 scale), 24 LDS reads,
+  // 16 MFMAs of 64 cycles
+  constexpr int kLoadsPerStepMx = 9;
+  auto pin_mx = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    sfor<8>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // One step: wait for stage kt+1 and for every wave to be done reading
+  // stage kt (its operands are already in registers set cur), then load
+  // step kt+4 into stage kt's slot, read stage kt+1 into the other register
+  // set and run the MFMAs of step kt.
+  auto kstep_mx = [&](auto cur, const uint16_t* a_nxt, const uint16_t* b_nxt,
+                      const uint8_t* s_nxt, uint16_t* a_ld, uint16_t* b_ld, uint8_t* s_ld,
+                      int kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerStepMx));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    bare_barrier();
+    issue_stage(a_ld, b_ld, s_ld, kt + 4);
+    read_frags_mx(a_nxt, b_nxt, s_nxt, std::integral_constant<int, 1 - decltype(cur)::value>{});
+    mfma_all_mx(cur);
+    pin_mx();
+  };
+
   // ---- persistent tile loop -------------------------------------------
-  // 4-stage pipeline, loads run 3 K steps ahead.  The K loop is unrolled by
-  // 4 so every stage is a distinct LDS array named statically (the compiler
-  // then sees that a load in flight never targets the stage being read);
-  // steps past the end of K load zeros.  The first three steps of the next
-  // tile are issued before the epilogue of the current one, so the pipeline
-  // fills while the epilogue runs.
+  // 4-stage pipeline, unrolled by 4 so every stage is a distinct LDS array
+  // named statically (the compiler then sees that a load in flight never
+  // targets the stage being read); steps past the end of K load zeros.
   int tile = vid;
   TileInfo cur{};
   if (tile < total) {
@@ -670,14 +1093,28 @@ void grouped_gemm_kernel(GemmArgs g) {
   }
   while (tile < total) {
     sfor<4>([&](auto mi) { sfor<4>([&](auto ni) { acc[mi][ni] = f32x16{}; }); });
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerStep));
-    bare_barrier();
-    read_frags(sA0, sB0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    for (int kt = 0; kt < nk; kt += 4) {
-      kstep(sA0, sB0, sA1, sB1, sA3, sB3, kt);
-      kstep(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
-      kstep(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
-      kstep(sA3, sB3, sA0, sB0, sA2, sB2, kt + 3);
+    if constexpr (MX) {
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * kLoadsPerStepMx));
+      bare_barrier();
+      read_frags_mx(sA0, sB0, sS0, std::integral_constant<int, 0>{});
+      using C0 = std::integral_constant<int, 0>;
+      using C1 = std::integral_constant<int, 1>;
+      for (int kt = 0; kt < nk; kt += 4) {
+        kstep_mx(C0{}, sA1, sB1, sS1, sA0, sB0, sS0, kt);
+        kstep_mx(C1{}, sA2, sB2, sS2, sA1, sB1, sS1, kt + 1);
+        kstep_mx(C0{}, sA3, sB3, sS3, sA2, sB2, sS2, kt + 2);
+        kstep_mx(C1{}, sA0, sB0, sS0, sA3, sB3, sS3, kt + 3);
+      }
+    } else {
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerStep));
+      bare_barrier();
+      read_frags(sA0, sB0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+      for (int kt = 0; kt < nk; kt += 4) {
+        kstep(sA0, sB0, sA1, sB1, sA3, sB3, kt);
+        kstep(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
+        kstep(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
+        kstep(sA3, sB3, sA0, sB0, sA2, sB2, kt + 3);
+      }
     }
     // the loads still in flight are zero fills; then every wave is done
     // with the stages and the next tile may start loading
@@ -694,22 +1131,32 @@ void grouped_gemm_kernel(GemmArgs g) {
     TileCtx t;
     t.row0 = t0.row0;
     t.rows_valid = t0.rows_valid;
+    t.rows_pad = t0.rows_pad;
     t.col0 = t0.col0;
     t.cols_valid = t0.cols_valid;
     t.n_t = t0.n_t;
     t.m_lane = wm * kWaveM + (lane & 31);
     t.n_lane = wn * kWaveN + 4 * (lane >> 5);
+    MxOut mo{g.mx_q, g.mx_s, g.mx_qT, g.mx_sT, g.mx_n, g.M_cap};
     if constexpr (EPI == EPI_STORE) {
       epi_store(acc, g.C, g.ldc, t);
     } else if constexpr (EPI == EPI_GLU) {
-      float amax = epi_glu<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, g.probs, g.act, t, wn, lane);
+      float amax;
+      if constexpr (MX)
+        amax = epi_glu_mx<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, g.probs, g.act, t, wn, wm,
+                               lane, mo);
+      else
+        amax = epi_glu<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, g.probs, g.act, t, wn, lane);
       if (g.amax) {
         amax = wave_max(amax);
         if (lane == 0) atomic_max_nonneg(g.amax, amax);
       }
     } else {
       float dp[4];
-      epi_dglu<ACT>(acc, g.zin, g.ldz, g.C, g.ldc, g.probs, g.act, t, wn, lane, dp);
+      if constexpr (MX)
+        epi_dglu_mx<ACT>(acc, g.zin, g.ldz, g.C, g.ldc, g.probs, g.act, t, wn, wm, lane, dp, mo);
+      else
+        epi_dglu<ACT>(acc, g.zin, g.ldz, g.C, g.ldc, g.probs, g.act, t, wn, lane, dp);
       sfor<4>([&](auto mi) {
         // lanes l and l ^ 32 hold the same row: fixed-order pair sum
         const float v = dp[mi] + __shfl_xor(dp[mi], 32, kWave);
@@ -763,28 +1210,36 @@ __global__ __launch_bounds__(256) void dprobs_reduce_kernel(
 int grouped_gemm_tile_n() { return BN; }
 int grouped_gemm_tile_m() { return BM; }
 
-template <int EPI, bool NN>
+template <int EPI, bool NN, bool MX>
 hipError_t launch_act(const GemmArgs& g, int grid, hipStream_t s) {
   dim3 blk(kThreads), grd(grid);
   switch (g.act.act) {
-    case MOE_ACT_SWIGLU: grouped_gemm_kernel<EPI, NN, MOE_ACT_SWIGLU><<<grd, blk, 0, s>>>(g); break;
-    case MOE_ACT_GEGLU: grouped_gemm_kernel<EPI, NN, MOE_ACT_GEGLU><<<grd, blk, 0, s>>>(g); break;
-    case MOE_ACT_SRELU: grouped_gemm_kernel<EPI, NN, MOE_ACT_SRELU><<<grd, blk, 0, s>>>(g); break;
+    case MOE_ACT_SWIGLU: grouped_gemm_kernel<EPI, NN, MOE_ACT_SWIGLU, MX><<<grd, blk, 0, s>>>(g); break;
+    case MOE_ACT_GEGLU: grouped_gemm_kernel<EPI, NN, MOE_ACT_GEGLU, MX><<<grd, blk, 0, s>>>(g); break;
+    case MOE_ACT_SRELU: grouped_gemm_kernel<EPI, NN, MOE_ACT_SRELU, MX><<<grd, blk, 0, s>>>(g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_gemm(const GemmArgs& g, int epi, bool b_nn, int grid, hipStream_t s) {
+hipError_t launch_grouped_gemm(const GemmArgs& g, int epi, bool b_nn, bool mx, int grid,
+                               hipStream_t s) {
   dim3 blk(kThreads), grd(grid);
+  if (mx && b_nn) return hipErrorInvalidValue;
   if (epi == EPI_STORE) {
     // the plain epilogue does not depend on the activation
-    if (b_nn) grouped_gemm_kernel<EPI_STORE, true, MOE_ACT_SWIGLU><<<grd, blk, 0, s>>>(g);
-    else grouped_gemm_kernel<EPI_STORE, false, MOE_ACT_SWIGLU><<<grd, blk, 0, s>>>(g);
+    if (mx) grouped_gemm_kernel<EPI_STORE, false, MOE_ACT_SWIGLU, true><<<grd, blk, 0, s>>>(g);
+    else if (b_nn) grouped_gemm_kernel<EPI_STORE, true, MOE_ACT_SWIGLU, false><<<grd, blk, 0, s>>>(g);
+    else grouped_gemm_kernel<EPI_STORE, false, MOE_ACT_SWIGLU, false><<<grd, blk, 0, s>>>(g);
     return hipGetLastError();
   }
-  if (epi == EPI_GLU && !b_nn) return launch_act<EPI_GLU, false>(g, grid, s);
-  if (epi == EPI_DGLU && b_nn) return launch_act<EPI_DGLU, true>(g, grid, s);
+  if (mx) {
+    if (epi == EPI_GLU) return launch_act<EPI_GLU, false, true>(g, grid, s);
+    if (epi == EPI_DGLU) return launch_act<EPI_DGLU, false, true>(g, grid, s);
+    return hipErrorInvalidValue;
+  }
+  if (epi == EPI_GLU && !b_nn) return launch_act<EPI_GLU, false, false>(g, grid, s);
+  if (epi == EPI_DGLU && b_nn) return launch_act<EPI_DGLU, true, false>(g, grid, s);
   return hipErrorInvalidValue;
 }
 

@@ -30,6 +30,7 @@ hipError_t launch_unpermute(const moe_unpermute_args& a, hipStream_t s);
 hipError_t launch_repack_interleave(const void* src, void* dst, int E, int I,
                                     int H, int block, int inverse, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
+hipError_t launch_quantize_mxfp8(const moe_quant_args& a, hipStream_t s);
 
 // ---- grouped GEMM --------------------------------------------------------
 enum Epi { EPI_STORE = 0, EPI_GLU = 1, EPI_DGLU = 2 };
@@ -39,14 +40,17 @@ struct GemmArgs {
   int64_t M_cap;
   const int32_t* split;
   const int32_t* padded;
-  const uint16_t* A;     // [M_cap][K] bf16
-  const uint16_t* B;     // per expert: B_NT [N][K], B_NN [K][N]
+  const void* A;         // [M_cap][K] bf16, or E4M3 codes (MXFP8)
+  const void* B;         // per expert: B_NT [N][K], B_NN [K][N] (bf16 only)
   int64_t b_stride;      // elements between experts of B
+  const uint8_t* a_s;    // MXFP8: tiled scales of A (R = M_cap)
+  const uint8_t* b_s;    // MXFP8: tiled scales of B per expert (R = N)
+  int64_t b_s_stride;    // bytes between experts of b_s
   int group_m;           // m-tiles per band of the tile order
   // epilogue
-  uint16_t* C;           // STORE: out [M_cap][N]; GLU: z (nullable); DGLU: dz
+  uint16_t* C;           // STORE: out [M_cap][N]; GLU: z (nullable); DGLU: dz (nullable with MX)
   int64_t ldc;
-  uint16_t* act_out;     // GLU: a [M_cap][ld_act]
+  uint16_t* act_out;     // GLU: a [M_cap][ld_act] (nullable with MX)
   int64_t ld_act;
   const float* probs;    // GLU, DGLU: probs_p [M_cap]
   float* amax;           // GLU (nullable)
@@ -55,9 +59,15 @@ struct GemmArgs {
   float* dp_part;        // DGLU: [M_cap][n_part]
   int n_part;
   ActP act;
+  // MXFP8 copies of the GLU / DGLU output ([M_cap][mx_n])
+  uint8_t* mx_q;
+  uint8_t* mx_s;
+  uint8_t* mx_qT;        // nullable
+  uint8_t* mx_sT;
+  int mx_n;
 };
 
-hipError_t launch_grouped_gemm(const GemmArgs& g, int epi, bool b_nn,
+hipError_t launch_grouped_gemm(const GemmArgs& g, int epi, bool b_nn, bool mx,
                                int grid, hipStream_t s);
 int grouped_gemm_tile_n();  // BN of the launched configuration
 int grouped_gemm_tile_m();  // BM

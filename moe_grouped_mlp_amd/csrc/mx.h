@@ -1,0 +1,52 @@
+// MXFP8 encoding helpers (E4M3 values, one E8M0 scale per 32 values).
+//
+// The block rule: e = clamp(floor(log2 max|v|) - 8, -127, 127) (-127 for an
+// all-zero block), scale code e + 127, code = E4M3 round-to-nearest-even of
+// v / 2^e saturated to +-448 (TE + BioNeMo Mixtral tutorial, § "Challenge 2:
+// model size and activation memory", Fig. 3).  The inputs are always bf16
+// values, so v / 2^e is exact in fp32 and the only rounding is the final
+// one, done by v_cvt_pk_fp8_f32 (E4M3 round-to-nearest-even; it turns values
+// past 464 into NaN, so they are clamped to +-448 first, which equals
+// saturating after rounding).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// e for a block whose largest magnitude is `amax` (a bf16 value, >= 0):
+// floor(log2 amax) read from the exponent field; a zero or subnormal amax
+// gives -127 after the clamp (the largest bf16 gives 119, so no upper clamp
+// is ever reached).
+MOE_DEV int mx_exponent(float amax) {
+  const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 127 - 8;
+  return e < -127 ? -127 : e;
+}
+
+// 2^-e as an fp32 (normal for every e mx_exponent returns).
+MOE_DEV float mx_inv_scale(int e) { return __uint_as_float(static_cast<uint32_t>(127 - e) << 23); }
+
+MOE_DEV uint8_t mx_scale_code(int e) { return static_cast<uint8_t>(e + 127); }
+
+// Four values times 2^-e -> four E4M3 codes, little-endian in one word.
+MOE_DEV uint32_t mx_codes4(float a, float b, float c, float d, float inv) {
+  a = __builtin_amdgcn_fmed3f(a * inv, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b * inv, -448.0f, 448.0f);
+  c = __builtin_amdgcn_fmed3f(c * inv, -448.0f, 448.0f);
+  d = __builtin_amdgcn_fmed3f(d * inv, -448.0f, 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// |v| of a bf16 pattern as an ordered integer (bf16 magnitudes compare like
+// their bit patterns).
+MOE_DEV uint32_t bf16_abs_bits(uint32_t b) { return b & 0x7fffu; }
+
+// Byte offset of the scale of row r, K-block b in the tiled scale layout of
+// an [R][K] operand (see MOE_MX_BLOCK in moe_gmlp.h).
+MOE_DEV int64_t mx_scale_off(int64_t r, int64_t b, int64_t K) {
+  return ((r >> 5) * (K >> 6) + (b >> 1)) * 64 + (b & 1) * 32 + (r & 31);
+}
+
+}  // namespace moe

@@ -12,6 +12,7 @@
 //              epilogues", Fig. 2).
 #include "common.h"
 #include "kernels.h"
+#include "mx.h"
 
 namespace moe {
 namespace {
@@ -20,22 +21,54 @@ constexpr int kBlock = 256;
 constexpr int kRowsPerBlock = kBlock / kWave;
 
 // ------------------------------------------------------------- gather ---
+// Each wave pushes one token row to its k rows.  With MXFP8 output the row
+// is encoded once (a quad of lanes holds one 32-value block: four 16-byte
+// chunks) and the same codes and scale go to every slot.
 __global__ __launch_bounds__(kBlock) void gather_kernel(
     const i32x4* __restrict__ x, int T, int k, int H8, const int32_t* __restrict__ row_id_map,
-    int64_t M_cap, i32x4* __restrict__ xp, int tok_blocks,
-    const int32_t* __restrict__ split, const int32_t* __restrict__ padded, int E) {
+    int64_t M_cap, i32x4* __restrict__ xp, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
+    int tok_blocks, const int32_t* __restrict__ split, const int32_t* __restrict__ padded, int E) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int H = 8 * H8;
   if (static_cast<int>(blockIdx.x) < tok_blocks) {
     for (int t = blockIdx.x * kRowsPerBlock + wave; t < T; t += tok_blocks * kRowsPerBlock) {
       int rows[kMaxTopK];
-      for (int s = 0; s < kMaxTopK; ++s)
-        rows[s] = s < k ? row_id_map[static_cast<int64_t>(t) * k + s] : -1;
+      for (int s = 0; s < kMaxTopK; ++s) {
+        const int r = s < k ? row_id_map[static_cast<int64_t>(t) * k + s] : -1;
+        rows[s] = (r >= 0 && r < M_cap) ? r : -1;
+      }
       const i32x4* src = x + static_cast<int64_t>(t) * H8;
       for (int c = lane; c < H8; c += kWave) {
         const i32x4 v = src[c];
+        if (xp) {
 #pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s)
-          if (rows[s] >= 0 && rows[s] < M_cap) xp[static_cast<int64_t>(rows[s]) * H8 + c] = v;
+          for (int s = 0; s < kMaxTopK; ++s)
+            if (rows[s] >= 0) xp[static_cast<int64_t>(rows[s]) * H8 + c] = v;
+        }
+        if (xq) {
+          uint32_t m = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t w = static_cast<uint32_t>(v[i]);
+            m = max(m, max(bf16_abs_bits(w), bf16_abs_bits(w >> 16)));
+          }
+          m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 1, kWave)));
+          m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 2, kWave)));
+          const int e = mx_exponent(__uint_as_float(m << 16));
+          const float inv = mx_inv_scale(e);
+          uint2 q;
+          const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
+          q.x = mx_codes4(__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xffff0000u),
+                          __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xffff0000u), inv);
+          q.y = mx_codes4(__uint_as_float(w2 << 16), __uint_as_float(w2 & 0xffff0000u),
+                          __uint_as_float(w3 << 16), __uint_as_float(w3 & 0xffff0000u), inv);
+#pragma unroll
+          for (int s = 0; s < kMaxTopK; ++s) {
+            if (rows[s] < 0) continue;
+            *reinterpret_cast<uint2*>(xq + static_cast<int64_t>(rows[s]) * H + 8 * c) = q;
+            if ((c & 3) == 0) xs[mx_scale_off(rows[s], c >> 2, H)] = mx_scale_code(e);
+          }
+        }
       }
     }
     return;
@@ -48,8 +81,13 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
     const int64_t r0 = static_cast<int64_t>(padded[e]) + split[e];
     const int64_t r1 = min(static_cast<int64_t>(padded[e + 1]), M_cap);
     for (int64_t r = r0 + wave; r < r1; r += kRowsPerBlock) {
-      i32x4* dst = xp + r * H8;
-      for (int c = lane; c < H8; c += kWave) dst[c] = zero;
+      for (int c = lane; c < H8; c += kWave) {
+        if (xp) xp[r * H8 + c] = zero;
+        if (xq) {
+          *reinterpret_cast<uint2*>(xq + r * H + 8 * c) = make_uint2(0, 0);
+          if ((c & 3) == 0) xs[mx_scale_off(r, c >> 2, H)] = 0;
+        }
+      }
     }
   }
 }
@@ -136,7 +174,9 @@ hipError_t launch_gather(const moe_permute_args& a, hipStream_t s) {
   const int pad_blocks = a.E < 256 ? a.E : 256;
   gather_kernel<<<tok_blocks + pad_blocks, kBlock, 0, s>>>(
       static_cast<const i32x4*>(a.x), a.T, a.k, H8, a.row_id_map, a.M_cap,
-      static_cast<i32x4*>(a.xp), tok_blocks, a.split_sizes, a.padded_offsets, a.E);
+      static_cast<i32x4*>(a.xp), (a.flags & MOE_PERMUTE_WRITE_MX) ? a.xp_q : nullptr,
+      (a.flags & MOE_PERMUTE_WRITE_MX) ? a.xp_s : nullptr, tok_blocks, a.split_sizes,
+      a.padded_offsets, a.E);
   return hipGetLastError();
 }
 

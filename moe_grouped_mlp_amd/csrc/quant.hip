@@ -1,0 +1,175 @@
+// Stand-alone bf16 -> MXFP8 quantization (memory-bound): the weight copies
+// the MXFP8 GEMMs read, from the bf16 master weights ("NVIDIA Transformer
+// Engine 优化 MoE 生物基础模型训练", § "Challenge 3: quantization overhead":
+// bf16 masters are cast before the low-precision GEMM; § "Challenge 2",
+// Fig. 3: E4M3 codes with one E8M0 scale per 32 values).
+//
+// Both kernels produce the tiled scale layout in units of 32 output rows x
+// 64 K positions (2 blocks per row); one wave encodes one such unit, each
+// lane one whole 32-value block, so the block maximum needs no cross-lane
+// reduction and the unit's 64 scale bytes are one contiguous store.
+//   ROW  blocks along the contiguous axis: lane l reads 64 contiguous bytes
+//        of row l % 32 (its block l / 32) with four 16-byte loads.
+//   COL  blocks along rows, output transposed: a workgroup stages a 64-row
+//        x 128-column slice of x in LDS; thread t encodes column t % 128 over
+//        rows 32 (t / 128) .. +31 and writes those 32 codes contiguously.
+#include "common.h"
+#include "kernels.h"
+#include "mx.h"
+
+namespace moe {
+namespace {
+
+// Encodes 32 bf16 values (as 16 packed words) into 32 codes (8 words);
+// returns the scale exponent.
+MOE_DEV int mx_encode32(const uint32_t (&w)[16], uint32_t (&codes)[8]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    m = max(m, bf16_abs_bits(w[i]));
+    m = max(m, bf16_abs_bits(w[i] >> 16));
+  }
+  const int e = mx_exponent(__uint_as_float(m << 16));
+  const float inv = mx_inv_scale(e);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t u = w[2 * i], v = w[2 * i + 1];
+    codes[i] = mx_codes4(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u),
+                         __uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u), inv);
+  }
+  return e;
+}
+
+MOE_DEV float amax_of_bits(uint32_t m) { return __uint_as_float(m << 16); }
+
+// x [batch][rows][cols] -> q [batch][rows][cols], s tiled (R = rows, K = cols)
+__global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restrict__ x,
+                                                        int64_t x_stride, int batch, int rows,
+                                                        int cols, uint8_t* __restrict__ q,
+                                                        uint8_t* __restrict__ s,
+                                                        float* __restrict__ amax) {
+  const int lane = threadIdx.x & 63;
+  const int units_r = rows / 32, units_c = cols / 64;
+  const int64_t units = static_cast<int64_t>(batch) * units_r * units_c;
+  const int64_t per_batch_q = static_cast<int64_t>(rows) * cols;
+  uint32_t wmax = 0;
+  for (int64_t u = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64; u < units;
+       u += static_cast<int64_t>(gridDim.x) * blockDim.x / 64) {
+    const int bi = static_cast<int>(u / (static_cast<int64_t>(units_r) * units_c));
+    const int rem = static_cast<int>(u % (static_cast<int64_t>(units_r) * units_c));
+    const int ur = rem / units_c, uc = rem % units_c;
+    const int row = ur * 32 + (lane & 31);
+    const int col = uc * 64 + 32 * (lane >> 5);
+    const uint4* src = reinterpret_cast<const uint4*>(x + bi * x_stride +
+                                                      static_cast<int64_t>(row) * cols + col);
+    uint32_t w[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = src[j];
+      w[4 * j] = v.x; w[4 * j + 1] = v.y; w[4 * j + 2] = v.z; w[4 * j + 3] = v.w;
+    }
+    uint32_t codes[8];
+    const int e = mx_encode32(w, codes);
+    uint4* dst = reinterpret_cast<uint4*>(q + bi * per_batch_q + static_cast<int64_t>(row) * cols + col);
+    dst[0] = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+    dst[1] = make_uint4(codes[4], codes[5], codes[6], codes[7]);
+    s[bi * (per_batch_q / 32) + (static_cast<int64_t>(ur) * units_c + uc) * 64 + lane] =
+        mx_scale_code(e);
+    if (amax) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        wmax = max(wmax, max(bf16_abs_bits(w[i]), bf16_abs_bits(w[i] >> 16)));
+    }
+  }
+  if (amax) {
+    const float m = wave_max(amax_of_bits(wmax));
+    if (lane == 0) atomic_max_nonneg(amax, m);
+  }
+}
+
+// x [batch][rows][cols] -> q [batch][cols][rows], s tiled (R = cols, K = rows)
+constexpr int kColTileR = 64, kColTileC = 128;
+constexpr int kColPitch = kColTileC + 2;  // bf16 per LDS row (odd word stride)
+
+__global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restrict__ x,
+                                                        int64_t x_stride, int batch, int rows,
+                                                        int cols, uint8_t* __restrict__ q,
+                                                        uint8_t* __restrict__ s,
+                                                        float* __restrict__ amax) {
+  __shared__ uint16_t tile[kColTileR * kColPitch];
+  const int t = threadIdx.x;
+  const int tiles_r = rows / kColTileR;
+  const int tiles_c = (cols + kColTileC - 1) / kColTileC;
+  const int64_t tiles = static_cast<int64_t>(batch) * tiles_r * tiles_c;
+  const int64_t per_batch_q = static_cast<int64_t>(rows) * cols;
+  uint32_t wmax = 0;
+  for (int64_t id = blockIdx.x; id < tiles; id += gridDim.x) {
+    const int bi = static_cast<int>(id / (static_cast<int64_t>(tiles_r) * tiles_c));
+    const int rem = static_cast<int>(id % (static_cast<int64_t>(tiles_r) * tiles_c));
+    const int r0 = (rem / tiles_c) * kColTileR, c0 = (rem % tiles_c) * kColTileC;
+    const int cw = min(kColTileC, cols - c0);  // multiple of 64
+    const uint16_t* xb = x + bi * x_stride;
+    // stage: 64 rows x cw columns, 8 bf16 per thread-iteration
+    for (int i = t; i < kColTileR * (cw / 8); i += 256) {
+      const int r = i / (cw / 8), c8 = i % (cw / 8);
+      const uint4 v = *reinterpret_cast<const uint4*>(xb + static_cast<int64_t>(r0 + r) * cols +
+                                                      c0 + 8 * c8);
+      uint32_t* d = reinterpret_cast<uint32_t*>(tile + r * kColPitch + 8 * c8);
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+    __syncthreads();
+    const int c = t % kColTileC, half = t / kColTileC;
+    if (c < cw) {
+      uint32_t w[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 32 * half + 2 * i;
+        w[i] = static_cast<uint32_t>(tile[r * kColPitch + c]) |
+               (static_cast<uint32_t>(tile[(r + 1) * kColPitch + c]) << 16);
+      }
+      uint32_t codes[8];
+      const int e = mx_encode32(w, codes);
+      const int cc = c0 + c;
+      uint4* dst = reinterpret_cast<uint4*>(q + bi * per_batch_q + static_cast<int64_t>(cc) * rows +
+                                            r0 + 32 * half);
+      dst[0] = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+      dst[1] = make_uint4(codes[4], codes[5], codes[6], codes[7]);
+      s[bi * (per_batch_q / 32) + mx_scale_off(cc, r0 / 32 + half, rows)] = mx_scale_code(e);
+      if (amax) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          wmax = max(wmax, max(bf16_abs_bits(w[i]), bf16_abs_bits(w[i] >> 16)));
+      }
+    }
+    __syncthreads();
+  }
+  if (amax) {
+    const float m = wave_max(amax_of_bits(wmax));
+    if ((t & 63) == 0) atomic_max_nonneg(amax, m);
+  }
+}
+
+int quant_grid(int64_t work_items, int per_block) {
+  int64_t b = (work_items + per_block - 1) / per_block;
+  if (b > 8192) b = 8192;
+  return b < 1 ? 1 : static_cast<int>(b);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_mxfp8(const moe_quant_args& a, hipStream_t st) {
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  if (a.mode == MOE_QUANT_ROW) {
+    const int64_t units = static_cast<int64_t>(a.batch) * (a.rows / 32) * (a.cols / 64);
+    quant_row_kernel<<<quant_grid(units, 4), 256, 0, st>>>(x, a.x_stride, a.batch, a.rows, a.cols,
+                                                           a.q, a.s, a.amax);
+  } else {
+    const int64_t tiles = static_cast<int64_t>(a.batch) * (a.rows / kColTileR) *
+                          ((a.cols + kColTileC - 1) / kColTileC);
+    quant_col_kernel<<<quant_grid(tiles, 1), 256, 0, st>>>(x, a.x_stride, a.batch, a.rows, a.cols,
+                                                           a.q, a.s, a.amax);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -61,11 +61,12 @@ def act_of(wl, prm_override=None):
     return gp, op
 
 
-def run_gpu_layer(wl, M_cap=None, backward=True, block=None):
-    """Run the HIP path on a workload; returns (block, host results)."""
+def run_gpu_layer(wl, M_cap=None, backward=True, block=None, prec=None):
+    """Run the HIP path on a workload; returns the block holding the results."""
     gp, _ = act_of(wl)
     blk = block or mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, act=gp,
-                                  first_expert=wl.first_expert, M_cap=M_cap)
+                                  first_expert=wl.first_expert, M_cap=M_cap,
+                                  prec=mg.PREC_BF16 if prec is None else prec)
     w1 = dev_bf16(wl.w1)
     w2 = dev_bf16(wl.w2)
     blk.load_weights(w1, w2)
@@ -87,12 +88,41 @@ def uninterleave_cols(packed: np.ndarray, I: int) -> np.ndarray:
     return out
 
 
-def oracle_layer(wl, M_cap, backward=True):
+def oracle_layer(wl, M_cap, backward=True, mx=False):
     _, op = act_of(wl)
     fw = om.forward(wl.x, wl.w1, wl.w2, wl.expert_idx, wl.probs, wl.E, op,
-                    first_expert=wl.first_expert, M_cap=M_cap)
-    bw = om.backward(fw, wl.dout, wl.w1, wl.w2, op) if backward else None
+                    first_expert=wl.first_expert, M_cap=M_cap, mx=mx)
+    bw = om.backward(fw, wl.dout, wl.w1, wl.w2, op, mx=mx) if backward else None
     return fw, bw
+
+
+# ---------------------------------------------------------------- MXFP8 ---
+def mx_scale_index(R: int, K: int) -> np.ndarray:
+    """[R][K/32] byte offsets of the tiled MXFP8 scale layout documented in
+    include/moe_gmlp.h (row r, block b)."""
+    r = np.arange(R)[:, None]
+    b = np.arange(K // 32)[None, :]
+    return ((r // 32) * (K // 64) + b // 2) * 64 + (b % 2) * 32 + r % 32
+
+
+def mx_scales_plain(s_tiled: torch.Tensor, R: int, K: int) -> np.ndarray:
+    """Tiled scale bytes (one [R][K] operand) -> plain [R][K/32]."""
+    s = s_tiled.detach().cpu().numpy().reshape(-1)
+    return s[mx_scale_index(R, K)]
+
+
+def assert_mx_equal(q_gpu, s_plain_gpu, ref, what):
+    """Codes and scales bit-exact against the oracle's (codes, scales)."""
+    codes, scales = ref
+    q = q_gpu.detach().cpu().numpy() if isinstance(q_gpu, torch.Tensor) else q_gpu
+    bad = np.flatnonzero(q.reshape(-1) != codes.reshape(-1))
+    assert bad.size == 0, (f"{what}: {bad.size} of {codes.size} codes differ; first at "
+                           f"{bad[:5]}: gpu {q.reshape(-1)[bad[:5]]} oracle "
+                           f"{codes.reshape(-1)[bad[:5]]}")
+    bad = np.flatnonzero(s_plain_gpu.reshape(-1) != scales.reshape(-1))
+    assert bad.size == 0, (f"{what}: {bad.size} of {scales.size} scales differ; first at "
+                           f"{bad[:5]}: gpu {s_plain_gpu.reshape(-1)[bad[:5]]} oracle "
+                           f"{scales.reshape(-1)[bad[:5]]}")
 
 
 def compare_routing(blk, rt):
@@ -139,3 +169,66 @@ def compare_layer(blk, wl, fw, bw):
     assert_close(host_f64(blk.dxp)[valid], bw.dxp[valid], "dxp")
     assert_close(host_f64(blk.dx), bw.dx, "dx")
     assert_close(blk.dprobs.cpu().numpy(), bw.dprobs, "dprobs")
+
+
+def e4m3_ordinal(codes: np.ndarray) -> np.ndarray:
+    """E4M3 codes -> signed ordinal (neighbouring values differ by 1, +0 and
+    -0 both map to 0)."""
+    c = np.asarray(codes).astype(np.int64)
+    m = c & 0x7F
+    return np.where(c & 0x80, -m, m)
+
+
+# MXFP8 outputs against the oracle fed the same MXFP8 operands.  The oracle
+# sums exactly; the scaled fp8 MFMA rounds its internal sums (about 16
+# significant bits of the block partial sums) and the stored bf16 results can
+# then differ from the oracle's by a unit in the last place, which moves the
+# MXFP8 code of such a value to a neighbouring code when it sits near a
+# rounding boundary of E4M3 (3 mantissa bits), and a flipped code changes one
+# term of the next GEMM by 2^-3 of its size.  So:
+#   * every element stays within the stated bar (rtol 2e-2, atol 1e-2);
+#   * at most MX_OUTLIER_FRAC of the elements leave the scale-aware bar of
+#     the bf16 path (rel_atol 1e-2 of the RMS);
+#   * the relative L2 error stays below MX_REL_L2.
+MX_OUTLIER_FRAC = 5e-3
+MX_REL_L2 = 1e-2
+
+
+def assert_close_mx(gpu, ora, what):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ora = np.asarray(ora, dtype=np.float64)
+    assert gpu.shape == ora.shape, (what, gpu.shape, ora.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU values"
+    d = np.abs(gpu - ora)
+    bad = d > ATOL + RTOL * np.abs(ora)
+    assert not bad.any(), f"{what}: {bad.sum()} elements outside rtol {RTOL} / atol {ATOL}"
+    rms = float(np.sqrt(np.mean(ora * ora))) if ora.size else 0.0
+    out = d > REL_ATOL * rms + RTOL * np.abs(ora)
+    assert out.mean() <= MX_OUTLIER_FRAC, \
+        f"{what}: {out.sum()} of {out.size} outside the scale-aware bar"
+    l2 = float(np.linalg.norm(d) / max(np.linalg.norm(ora), 1e-300))
+    assert l2 <= MX_REL_L2, f"{what}: relative L2 error {l2:.3e}"
+
+
+def assert_mx_near(q_gpu, s_plain_gpu, ref, what, code_frac=2e-3, far_frac=1e-4,
+                   scale_frac=1e-3):
+    """MXFP8 copies written by a fused epilogue against the oracle's encoding
+    of its own pre-cast values (which differ from the GPU's by the GEMM
+    rounding, see above): scales equal on all but `scale_frac` of the blocks
+    (and then one binade apart); where scales agree, codes equal on all but
+    `code_frac` of the values and more than one E4M3 step apart on at most
+    `far_frac`."""
+    codes, scales = ref
+    q = q_gpu.detach().cpu().numpy() if isinstance(q_gpu, torch.Tensor) else q_gpu
+    sd = np.abs(s_plain_gpu.astype(np.int64) - scales.astype(np.int64))
+    assert sd.max(initial=0) <= 1, f"{what}: a scale differs by {sd.max()} binades"
+    assert (sd > 0).mean() <= scale_frac, f"{what}: {(sd > 0).sum()} scales differ"
+    # compare codes inside blocks whose scales agree
+    K = codes.shape[-1]
+    same = np.repeat(sd == 0, 32, axis=-1).reshape(codes.shape)
+    dist = np.abs(e4m3_ordinal(q) - e4m3_ordinal(codes))[same]
+    if dist.size:
+        assert (dist > 0).mean() <= code_frac, \
+            f"{what}: {(dist > 0).sum()} of {dist.size} codes differ"
+        assert (dist > 1).mean() <= far_frac, \
+            f"{what}: {(dist > 1).sum()} codes differ by more than one step"

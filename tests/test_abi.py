@@ -186,3 +186,84 @@ def test_status_strings():
     for code in (0, -1, -2, -3, -4, -5):
         assert L.moe_status_string(code)
     assert L.moe_status_string(-99) == b"unknown status"
+
+
+# ------------------------------------------------------------------ MXFP8 --
+def test_mx_scale_offset_is_the_documented_tiled_layout():
+    """Byte of (row r, K-block b) of an [R][K] operand: a bijection onto
+    [0, R*K/32), and each 32-row x 64-column unit owns one 64-byte run."""
+    for R, K in ((32, 64), (96, 192), (128, 2880), (64, 4096)):
+        offs = [[B.moe_mx_scale_offset(r, b, K) for b in range(K // 32)]
+                for r in range(R)]
+        flat = sorted(o for row in offs for o in row)
+        assert flat == list(range(R * K // 32))
+        for r in range(R):
+            for b in range(K // 32):
+                o = offs[r][b]
+                unit = (r // 32) * (K // 64) + b // 2
+                assert o // 64 == unit
+                assert o % 64 == (b % 2) * 32 + r % 32
+
+
+def _quant_args(**kw):
+    a = B.QuantArgs(B.QUANT_ROW, 2, 128, 192, 0, 64, 64, 64, None)
+    for key, v in kw.items():
+        setattr(a, key, v)
+    return a
+
+
+def test_quantize_validation():
+    assert _call("moe_quantize_mxfp8", _quant_args()) == DEVICE
+    assert _call("moe_quantize_mxfp8", _quant_args(mode=B.QUANT_COL)) == DEVICE
+    assert _call("moe_quantize_mxfp8", _quant_args(mode=2)) == INVALID
+    assert _call("moe_quantize_mxfp8", _quant_args(rows=96)) == INVALID    # % 64
+    assert _call("moe_quantize_mxfp8", _quant_args(cols=160)) == INVALID   # % 64
+    assert _call("moe_quantize_mxfp8", _quant_args(batch=-1)) == INVALID
+    assert _call("moe_quantize_mxfp8", _quant_args(x=None)) == INVALID
+    assert _call("moe_quantize_mxfp8", _quant_args(s=None)) == INVALID
+    assert _call("moe_quantize_mxfp8", _quant_args(x_stride=128 * 192 - 8)) == INVALID
+    assert _call("moe_quantize_mxfp8", _quant_args(x_stride=128 * 192 + 4)) == INVALID
+    assert _call("moe_quantize_mxfp8", _quant_args(x_stride=128 * 192 + 8)) == DEVICE
+
+
+def test_permute_write_mx_validation():
+    mx = B.PERMUTE_BUILD_MAP | B.PERMUTE_GATHER | B.PERMUTE_WRITE_MX
+    ok = dict(flags=mx, xp_q=64, xp_s=64, M_cap=640)
+    assert _call("moe_permute", _permute_args(**ok)) == DEVICE
+    assert _call("moe_permute", _permute_args(**{**ok, "xp": None})) == DEVICE
+    assert _call("moe_permute", _permute_args(**{**ok, "xp_s": None})) == INVALID
+    assert _call("moe_permute", _permute_args(**{**ok, "M_cap": 600})) == INVALID
+    assert _call("moe_permute", _permute_args(**{**ok, "H": 96})) == INVALID
+    # WRITE_MX modifies a gather
+    assert _call("moe_permute", _permute_args(
+        **{**ok, "flags": B.PERMUTE_BUILD_MAP | B.PERMUTE_WRITE_MX})) == INVALID
+
+
+def test_fwd_bwd_mx_validation():
+    mx_fwd = ("xp_q", "xp_s", "w1_q", "w1_s", "w2_q", "w2_s", "a_q", "a_s")
+    base = {f: 64 for f in mx_fwd}
+    base.update(prec=B.PREC_MXFP8, xp=None, w1i=None, w2=None, a=None)
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(**base)) == DEVICE
+    for f in mx_fwd:
+        assert _call("moe_grouped_mlp_fwd", _fwd_args(**{**base, f: None})) == INVALID, f
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(**{**base, "aT_q": 64})) == INVALID
+    assert _call("moe_grouped_mlp_fwd",
+                 _fwd_args(**{**base, "aT_q": 64, "aT_s": 64})) == DEVICE
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(**{**base, "M_cap": 1000})) == INVALID
+
+    a = B.BwdArgs()
+    a.E, a.H, a.I, a.M_cap, a.prec = 4, 128, 256, 1024, B.PREC_MXFP8
+    a.act = B.act_params()
+    mx_bwd = ("dyp_q", "dyp_s", "w2t_q", "w2t_s", "w1t_q", "w1t_s", "dz_q", "dz_s")
+    for f in ("split_sizes", "padded_offsets", "probs_p", "z", "dprobs_p",
+              "dxp", "workspace") + mx_bwd:
+        setattr(a, f, 64)
+    a.workspace_bytes = B.moe_grouped_mlp_workspace_size(4, 128, 256, 1024,
+                                                         B.PREC_MXFP8)
+    assert _call("moe_grouped_mlp_bwd", a) == DEVICE      # dz (bf16) optional
+    for f in mx_bwd:
+        setattr(a, f, None)
+        assert _call("moe_grouped_mlp_bwd", a) == INVALID, f
+        setattr(a, f, 64)
+    a.dzT_s = 64
+    assert _call("moe_grouped_mlp_bwd", a) == INVALID
