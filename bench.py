@@ -1,14 +1,19 @@
 """Benchmark of the fused grouped-MLP MoE expert block on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mixtral]
+                    [--prec bf16|mxfp8]
 
 One step = the whole hot path of a training step of one expert layer:
 route + permute (X), FC1 grouped GEMM with the fused SwiGLU + prob-scale
 epilogue, FC2 grouped GEMM, unpermute; permute (dOut), FC2 dgrad grouped GEMM
 with the fused dSwiGLU epilogue, FC1 dgrad grouped GEMM, unpermute (dX) +
-dprobs.  Inputs are synthetic (seeded), already resident in HBM when the
-timed region starts.  The value is algorithmic GEMM TFLOP/s of the step:
-12 * M * H * I flops (M = routed rows; no padding counted).
+dprobs.  With --prec mxfp8 the permutes write MXFP8 rows, the four GEMMs take
+MXFP8 operands and the epilogues also write MXFP8 copies (rowwise and
+transposed) of a and dz; the MXFP8 weight copies are made once, outside the
+step (once per weight update), and timed on their own.  Inputs are
+synthetic (seeded), already resident in HBM when the timed region starts.
+The value is algorithmic GEMM TFLOP/s of the step: 12 * M * H * I flops
+(M = routed rows; no padding counted).
 
 Prints one JSON line (stdout).  Progress goes to stderr.
 """
@@ -26,15 +31,16 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}   # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0
 
-WORKLOADS = {
-    # name: (E, k, T, H, I, beta, clamp, logit routing)
-    "mixtral": dict(E=8, k=2, T=8192, H=4096, I=14336, beta=1.0, clamp=None),
-    "gptoss": dict(E=128, k=4, T=16384, H=2880, I=2880, beta=1.702, clamp=7.0),
+# name -> workload config (workloads.gen.CONFIGS) and default precision
+BENCH_CONFIGS = {
+    "mixtral": ("mixtral", "bf16"),
+    "mixtral_mx": ("mixtral_mx", "mxfp8"),
+    "dsv3": ("dsv3", "bf16"),
+    "gptoss": ("gptoss", "bf16"),
 }
-
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -49,11 +55,15 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [
             ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.ev = []
         for _ in range(n):
             h = ctypes.c_void_p()
             assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
             self.ev.append(h.value)
+
+    def record(self, i, stream):
+        assert self.hip.hipEventRecord(self.ev[i], stream) == 0
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -88,43 +98,46 @@ def measured_traffic():
 
 
 def device_inputs(cfg, seed, device):
-    """Seeded synthetic inputs drawn on the device: X, dOut ~ N(0,1) bf16,
-    weights ~ N(0, 0.02^2) bf16, router logits ~ N(0,1) -> fp32 softmax ->
-    top-k (descending probability, no renormalisation)."""
+    """Seeded synthetic inputs: routing (expert_idx, probs) from the same
+    host generator the parity tests use (workloads.gen.route_inputs); X,
+    dOut ~ N(0,1) and weights ~ N(0, 0.02^2) drawn on the device, in bf16."""
     import torch
+    from workloads.gen import route_inputs
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     E, k, T, H, I = (cfg[n] for n in ("E", "k", "T", "H", "I"))
+    n1 = 2 * I if cfg["act"] != "srelu" else I
     bf = torch.bfloat16
     x = torch.randn(T, H, generator=g, device=device).to(bf)
     dout = torch.randn(T, H, generator=g, device=device).to(bf)
-    w1 = torch.empty(E, 2 * I, H, dtype=bf, device=device)
+    w1 = torch.empty(E, n1, H, dtype=bf, device=device)
     w2 = torch.empty(E, H, I, dtype=bf, device=device)
     for e in range(E):
-        w1[e] = (torch.randn(2 * I, H, generator=g, device=device) * 0.02).to(bf)
+        w1[e] = (torch.randn(n1, H, generator=g, device=device) * 0.02).to(bf)
         w2[e] = (torch.randn(H, I, generator=g, device=device) * 0.02).to(bf)
-    logits = torch.randn(T, E, generator=g, device=device)
-    p = torch.softmax(logits, dim=1)
-    probs, idx = torch.topk(p, k, dim=1)
-    return x, dout, w1, w2, idx.to(torch.int32).contiguous(), probs.contiguous()
+    idx, probs = route_inputs(cfg, seed, T, E, k)
+    return (x, dout, w1, w2, torch.from_numpy(idx).to(device),
+            torch.from_numpy(probs).to(device))
 
 
-def cpu_baseline(cfg, seed, target_s=15.0):
+def cpu_baseline(cfg, seed, mx=False, target_s=15.0):
     """Time the CPU oracle (as it stands) on a bounded sample of the same
-    workload: the rows routed to expert 0, full H and I, forward + backward."""
+    workload: the rows routed to expert 0, full H and I, forward + backward
+    (with MXFP8 operands when mx)."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import moe as om
-    from workloads.gen import _normal_bf16, route_inputs, CONFIGS
+    from workloads.gen import _normal_bf16, route_inputs
 
     E, k, T, H, I = (cfg[n] for n in ("E", "k", "T", "H", "I"))
-    idx, probs = route_inputs(dict(CONFIGS["mixtral"]), seed, T, E, k)
-    t_sel, s_sel = np.nonzero(idx == 0)
+    idx, probs = route_inputs(cfg, seed, T, E, k)
+    e0 = int(np.bincount(idx.reshape(-1), minlength=E).argmax())
+    t_sel, s_sel = np.nonzero(idx == e0)
     rows = 64
     rng = np.random.default_rng(seed + 7)
     w1 = _normal_bf16(rng, (1, 2 * I, H), 0.02)
     w2 = _normal_bf16(rng, (1, H, I), 0.02)
-    prm = om.ActParams.clamped(cfg["clamp"], beta=cfg["beta"])
+    prm = om.ActParams.clamped(cfg["clamp"], beta=cfg["beta"], act=cfg["act"])
     done_flops, t_used, runs = 0.0, 0.0, 0
     while True:
         n = min(rows, len(t_sel))
@@ -133,8 +146,8 @@ def cpu_baseline(cfg, seed, target_s=15.0):
         sub_idx = np.zeros((n, 1), np.int32)
         sub_p = probs[t_sel[:n], s_sel[:n]].reshape(n, 1)
         t0 = time.perf_counter()
-        fw = om.forward(x, w1, w2, sub_idx, sub_p, 1, prm)
-        om.backward(fw, dout, w1, w2, prm)
+        fw = om.forward(x, w1, w2, sub_idx, sub_p, 1, prm, mx=mx)
+        om.backward(fw, dout, w1, w2, prm, mx=mx)
         dt = time.perf_counter() - t0
         done_flops += 12.0 * n * H * I
         t_used += dt
@@ -149,8 +162,9 @@ def cpu_baseline(cfg, seed, target_s=15.0):
     cores = threads or len(os.sched_getaffinity(0))
     return {"value": done_flops / t_used / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
-            "sample": (f"oracle forward+backward on rows routed to expert 0 of the "
-                       f"{E}-expert layer (H={H}, I={I}, bf16 storage, fp64 math), "
+            "sample": (f"oracle forward+backward on rows routed to expert {e0} of the "
+                       f"{E}-expert layer (H={H}, I={I}, "
+                       f"{'MXFP8 operands' if mx else 'bf16 storage'}, fp64 math), "
                        f"{runs} runs, {done_flops / 1e12:.3f} TFLOP in {t_used:.1f} s")}
 
 
@@ -159,7 +173,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="mixtral", choices=sorted(WORKLOADS))
+    ap.add_argument("--config", default="mixtral", choices=sorted(BENCH_CONFIGS))
+    ap.add_argument("--prec", choices=("bf16", "mxfp8"), default=None,
+                    help="operand precision (default: the config's)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -173,24 +189,54 @@ def main():
 
     import torch
     import moe_grouped_mlp_amd as mg
+    from workloads.gen import CONFIGS
 
-    cfg = WORKLOADS[args.config]
+    wl_name, prec_default = BENCH_CONFIGS[args.config]
+    prec = args.prec or prec_default
+    mx = prec == "mxfp8"
+    cfg = dict(CONFIGS[wl_name])
     E, k, T, H, I = (cfg[n] for n in ("E", "k", "T", "H", "I"))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    log(f"generating {args.config} inputs on the device")
+    log(f"generating {args.config} inputs ({prec})")
     x, dout, w1, w2, idx, probs = device_inputs(cfg, args.seed, dev)
-    act = mg.act_params(mg.ACT_SWIGLU, beta=cfg["beta"], clamp=cfg["clamp"])
-    blk = mg.ExpertBlock(E, H, I, T, k, act=act)
+    act_kind = {"swiglu": mg.ACT_SWIGLU, "geglu": mg.ACT_GEGLU, "srelu": mg.ACT_SRELU}[cfg["act"]]
+    act = mg.act_params(act_kind, beta=cfg["beta"], clamp=cfg["clamp"])
+    blk = mg.ExpertBlock(E, H, I, T, k, act=act,
+                         prec=mg.PREC_MXFP8 if mx else mg.PREC_BF16)
     blk.load_weights(w1, w2)
     del w1, w2
-    M = T * k
-    flops_step = 12.0 * M * H * I
-    flops_fc1 = 4.0 * M * H * I
+    torch.cuda.synchronize()
+    M = T * k                       # every expert is local
+    gated = cfg["act"] != "srelu"
+    n1 = 2 * I if gated else I
+    flops = {"fc1": 2.0 * M * H * n1, "fc2": 2.0 * M * H * I,
+             "fc2_dgrad": 2.0 * M * H * I, "fc1_dgrad": 2.0 * M * H * n1}
+    flops_step = sum(flops.values())
+    stream = torch.cuda.current_stream().cuda_stream
 
-    def step(ev=None):
-        blk.forward(x, idx, probs, timing_events=ev)
-        blk.backward(dout)
+    # events per step: 0 start, 1-3 forward GEMMs (library), 4 after
+    # unpermute, 5-7 backward GEMMs (library), 8 after dX unpermute
+    n_ev = 9
+
+    def step(evs=None, base=0):
+        if evs is not None:
+            evs.record(base + 0, stream)
+        blk.route(idx, probs, x)
+        blk.experts_forward(None if evs is None else
+                            [evs.ev[base + 1], evs.ev[base + 2], evs.ev[base + 3]])
+        blk.combine(blk.yp, blk.out)
+        if evs is not None:
+            evs.record(base + 4, stream)
+        if mx:
+            blk.gather(dout, None, blk.dyp_q, blk.dyp_s)
+        else:
+            blk.gather(dout, blk.dyp)
+        blk.experts_backward(None if evs is None else
+                             [evs.ev[base + 5], evs.ev[base + 6], evs.ev[base + 7]])
+        blk.combine(blk.dxp, blk.dx, dprobs=True)
+        if evs is not None:
+            evs.record(base + 8, stream)
 
     if args.calib_copy_mb:
         n = args.calib_copy_mb << 20
@@ -206,28 +252,69 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = HipEvents(2 * args.steps)
+    evs = HipEvents(n_ev * args.steps)
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step((evs.ev[2 * i], evs.ev[2 * i + 1], None))
+        step(evs, n_ev * i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
-    fc1_ms = sum(evs.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)) / args.steps
+
+    def seg(a, b):
+        return sum(evs.elapsed_ms(n_ev * i + a, n_ev * i + b) for i in range(args.steps)) / args.steps
+
+    seg_ms = {"route_permute_x": seg(0, 1), "fc1": seg(1, 2), "fc2": seg(2, 3),
+              "unpermute_out": seg(3, 4), "permute_dout": seg(4, 5),
+              "fc2_dgrad": seg(5, 6), "fc1_dgrad": seg(6, 7), "unpermute_dx": seg(7, 8)}
     evs.close()
     assert int(blk.err_flag.cpu()[0]) == 0
     value = flops_step / (ms_step * 1e-3) / 1e12
-    achieved = flops_fc1 / (fc1_ms * 1e-3) / 1e12
-    log(f"step {ms_step:.3f} ms, {value:.1f} TFLOP/s; FC1 {fc1_ms:.3f} ms {achieved:.1f} TFLOP/s")
+    peak = PEAK_TFLOPS[prec]
+
+    # HBM-bound steps: algorithmic bytes
+    row_bytes = H * (1 + 1 / 32) if mx else 2 * H
+    idx_bytes = T * k * 4 * 2 + T * k * 4 + M * 8
+    kernels = {}
+    for name in ("fc1", "fc2", "fc2_dgrad", "fc1_dgrad"):
+        kernels[name] = {"ms": round(seg_ms[name], 4), "unit": "TFLOP/s",
+                         "rate": round(flops[name] / (seg_ms[name] * 1e-3) / 1e12, 2)}
+    mem = {"route_permute_x": T * H * 2 + M * row_bytes + idx_bytes,
+           "unpermute_out": M * H * 2 + T * H * 2 + T * k * 4,
+           "permute_dout": T * H * 2 + M * row_bytes + T * k * 4,
+           "unpermute_dx": M * H * 2 + T * H * 2 + T * k * 12}
+    for name, b in mem.items():
+        kernels[name] = {"ms": round(seg_ms[name], 4), "unit": "GB/s",
+                         "rate": round(b / (seg_ms[name] * 1e-3) / 1e9, 1)}
+    if mx:
+        # MXFP8 weight copies (once per weight update; not part of the step)
+        qe = HipEvents(2)
+        reps = 5
+        qe.record(0, stream)
+        for _ in range(reps):
+            blk.quantize_weights()
+        qe.record(1, stream)
+        torch.cuda.synchronize()
+        q_ms = qe.elapsed_ms(0, 1) / reps
+        qe.close()
+        n_w = 2 * (E * n1 * H + E * H * I)        # elements quantized (4 copies)
+        q_bytes = n_w * (2 + 1 + 1 / 32)
+        kernels["quantize_weights"] = {"ms": round(q_ms, 4), "unit": "GB/s",
+                                       "rate": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+                                       "outside_step": True}
+    fc1_ms = seg_ms["fc1"]
+    achieved = flops["fc1"] / (fc1_ms * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms, {value:.1f} TFLOP/s; " +
+        ", ".join(f"{n} {v['ms']:.3f} ms {v['rate']} {v['unit']}" for n, v in kernels.items()))
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(cfg, args.seed)
+        cpu = cpu_baseline(cfg, args.seed, mx=mx)
         log(f"cpu oracle {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads")
 
+    traffic = measured_traffic() if (args.config == "mixtral" and not mx) else None
     out = {
         "metric": "fused grouped-MLP fwd/bwd TFLOP/s and % MFMA peak, Mixtral-shaped "
                   "layer, 1 GPU",
@@ -237,21 +324,23 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "pct_mfma_peak": round(100.0 * value / peak, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8-e4m3" if mx else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{args.config} expert layer: E={E} top-{k} T={T} H={H} "
-                               f"I={I} SwiGLU, bf16, route+permute+FC1+FC2+unpermute "
-                               f"and backward (FC2 dgrad+dSwiGLU, FC1 dgrad, dX, dprobs)",
+                               f"I={I} {cfg['act']} beta={cfg['beta']} clamp={cfg['clamp']}, "
+                               f"{prec}, route+permute+FC1+FC2+unpermute and backward "
+                               f"(FC2 dgrad+dAct, FC1 dgrad, dX, dprobs)",
                    "E": E, "k": k, "T": T, "H": H, "I": I, "routed_rows": M,
-                   "flops_per_step": flops_step},
-        "roofline": {"bound": "mfma", "kernel": "FC1 grouped GEMM + SwiGLU epilogue",
-                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(), "avg_launch_ms": round(fc1_ms, 4)},
+                   "prec": prec, "flops_per_step": flops_step},
+        "kernels": kernels,
+        "roofline": {"bound": "mfma", "kernel": "FC1 grouped GEMM + activation epilogue",
+                     "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "avg_launch_ms": round(fc1_ms, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
