@@ -4,7 +4,9 @@
 // the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
+#include <cstdlib>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -52,6 +54,23 @@ moe_status device_info(int* cu_count) {
 }
 
 moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+// Tile-order parameters of the grouped GEMM (performance only; results
+// differ at most in fp32 summation order): m-tiles per band, and the K-order
+// rotation stride.  Read once from MOE_GEMM_GROUP_M / MOE_GEMM_KROT.
+struct GemmTuning {
+  int group_m = 16;  // measured best on MI355X with k_rot = 2 (FC1/FC2, bf16 and MXFP8)
+  int k_rot = 2;
+};
+const GemmTuning& tuning() {
+  static const GemmTuning t = [] {
+    GemmTuning v;
+    if (const char* e = std::getenv("MOE_GEMM_GROUP_M")) v.group_m = std::max(1, std::atoi(e));
+    if (const char* e = std::getenv("MOE_GEMM_KROT")) v.k_rot = std::max(0, std::atoi(e));
+    return v;
+  }();
+  return t;
+}
 
 bool act_ok(const moe_act_params& a) {
   if (a.act != MOE_ACT_SWIGLU && a.act != MOE_ACT_GEGLU && a.act != MOE_ACT_SRELU) return false;
@@ -234,7 +253,8 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   g.M_cap = a->M_cap;
   g.split = a->split_sizes;
   g.padded = a->padded_offsets;
-  g.group_m = 8;
+  g.group_m = tuning().group_m;
+  g.k_rot_stride = tuning().k_rot;
   g.probs = a->probs_p;
   g.act = moe::to_actp(a->act);
 
@@ -330,7 +350,8 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
   g.M_cap = a->M_cap;
   g.split = a->split_sizes;
   g.padded = a->padded_offsets;
-  g.group_m = 8;
+  g.group_m = tuning().group_m;
+  g.k_rot_stride = tuning().k_rot;
   g.probs = a->probs_p;
   g.act = moe::to_actp(a->act);
 
@@ -379,7 +400,8 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
   f.M_cap = a->M_cap;
   f.split = a->split_sizes;
   f.padded = a->padded_offsets;
-  f.group_m = 8;
+  f.group_m = tuning().group_m;
+  f.k_rot_stride = tuning().k_rot;
   f.act = g.act;
   f.N = a->H;
   f.K = N1;

@@ -229,11 +229,9 @@ struct ScaleLoader {
 struct NLoader {
   __amdgpu_buffer_rsrc_t rsrc;
   int voff[4];   // bytes
-  int pitch2;    // N * 2
 
   MOE_DEV void init(const uint16_t* mat, uint32_t mat_bytes, int N, int col0, int wave, int lane) {
     rsrc = make_rsrc(mat, mat_bytes);
-    pitch2 = N * 2;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = 8 * wave + 2 * j + (lane >> 5);
@@ -242,11 +240,12 @@ struct NLoader {
       voff[j] = (row * N + col) * 2;
     }
   }
-  MOE_DEV void issue(uint16_t* stage, int k0, int wave_s, bool valid) {
+  // soff: byte offset of the tile's first row, k0 * N * 2 (a wave-uniform
+  // value the caller computes from the kernel arguments)
+  MOE_DEV void issue(uint16_t* stage, int soff, int wave_s, bool valid) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      dma16(rsrc, stage + (4 * wave_s + j) * 512, valid ? voff[j] : kOutOfRange,
-            valid ? k0 * pitch2 : 0);
+      dma16(rsrc, stage + (4 * wave_s + j) * 512, valid ? voff[j] : kOutOfRange, valid ? soff : 0);
   }
 };
 
@@ -860,7 +859,7 @@ void grouped_gemm_kernel(GemmArgs g) {
 
   // ---- per-tile geometry --------------------------------------------
   struct TileInfo {
-    int e, n_t, col0, cols_valid, rows_valid, rows_pad;
+    int e, m_t, n_t, col0, cols_valid, rows_valid, rows_pad;
     int64_t row0;
   };
   auto tile_info = [&](int tile) {
@@ -879,6 +878,7 @@ void grouped_gemm_kernel(GemmArgs g) {
     const int gm = min(g.group_m, tm_e - first_m);
     const int rem = local - band * g.group_m * tiles_n;
     const int m_t = first_m + rem % gm;
+    ti.m_t = m_t;
     ti.n_t = rem / gm;
     ti.row0 = static_cast<int64_t>(s_pad[ti.e]) + static_cast<int64_t>(m_t) * BM;
     // rows_valid <= 0 only with inconsistent offsets: the tile then loads
@@ -901,16 +901,26 @@ void grouped_gemm_kernel(GemmArgs g) {
   KLoader lb_k;
   NLoader lb_n;
   ScaleLoader ls;
+  // K order of a tile: steps k_rot, k_rot + 1, ..., nk - 1, 0, ..., k_rot - 1
+  // with k_rot = stride * (m_t + n_t) mod nk.  Tiles that share an operand
+  // panel (same m_t or same n_t; an XCD holds a band of neighbouring tiles
+  // at once) then reach a given K slice of it one or more steps apart rather
+  // than in lockstep: the first one's L2 miss brings the slice in and the
+  // others hit, instead of all of them waiting on the same MALL/HBM fetch.
+  int k_rot = 0;
   auto issue_stage = [&](uint16_t* a_st, uint16_t* b_st, uint8_t* s_st, int kt) {
     const bool valid = kt < nk;
-    la.issue(a_st, kt, wave_s, valid);
-    if constexpr (NN) lb_n.issue(b_st, kt * BK, wave_s, valid);
-    else lb_k.issue(b_st, kt, wave_s, valid);
-    if constexpr (MX) ls.issue(s_st, kt, wave_s, valid);
+    int kk = kt + k_rot;
+    if (kk >= nk) kk -= nk;
+    la.issue(a_st, kk, wave_s, valid);
+    if constexpr (NN) lb_n.issue(b_st, kk * BK * (g.N * 2), wave_s, valid);
+    else lb_k.issue(b_st, kk, wave_s, valid);
+    if constexpr (MX) ls.issue(s_st, kk, wave_s, valid);
   };
   // point the loaders at a tile and start its first K steps (three for
   // bf16, four for MXFP8)
   auto start_tile = [&](const TileInfo& ti) {
+    k_rot = nk > 0 ? (g.k_rot_stride * (ti.m_t + ti.n_t)) % nk : 0;
     const int64_t rows_avail = ti.rows_valid > 0 ? g.M_cap - ti.row0 : 0;
     const int64_t arow0 = ti.rows_valid > 0 ? ti.row0 : 0;
     la.init(A + arow0 * g.K * kElem, rows_avail, g.K * kElem, wave, lane);

@@ -47,6 +47,7 @@ struct GemmArgs {
   const uint8_t* b_s;    // MXFP8: tiled scales of B per expert (R = N)
   int64_t b_s_stride;    // bytes between experts of b_s
   int group_m;           // m-tiles per band of the tile order
+  int k_rot_stride;      // K-order rotation per (m_t + n_t) step (0: none)
   // epilogue
   uint16_t* C;           // STORE: out [M_cap][N]; GLU: z (nullable); DGLU: dz (nullable with MX)
   int64_t ldc;
