@@ -59,8 +59,8 @@ moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LA
 // differ at most in fp32 summation order): m-tiles per band, and the K-order
 // rotation stride.  Read once from MOE_GEMM_GROUP_M / MOE_GEMM_KROT.
 struct GemmTuning {
-  int group_m = 16;  // measured best on MI355X with k_rot = 2 (FC1/FC2, bf16 and MXFP8)
-  int k_rot = 2;
+  int group_m = 16;  // measured best on MI355X with k_rot = 1 (bf16 and MXFP8)
+  int k_rot = 1;
 };
 const GemmTuning& tuning() {
   static const GemmTuning t = [] {

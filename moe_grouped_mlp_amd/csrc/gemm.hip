@@ -85,10 +85,10 @@ namespace {
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 32;
-constexpr int kStages = 4;
-constexpr int kStageA = BM * BK;  // bf16 elements per A stage (16 KB)
-constexpr int kStageB = BN * BK;
+constexpr int kRowBytes = 128;        // bytes of every operand row per stage
+constexpr int BK = kRowBytes / 2;     // bf16 K values per stage (64)
+constexpr int BKQ = kRowBytes;        // E4M3 K values per stage (128)
+constexpr int kStageBytes = BM * kRowBytes;  // 32 KB per operand per stage
 constexpr int kThreads = 256;
 constexpr int kWaveM = 128;  // rows of a wave's sub-tile
 constexpr int kWaveN = 128;  // cols of a wave's sub-tile
@@ -98,7 +98,7 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-constexpr int kStageS = 1024;  // bytes of MXFP8 scales per stage (A then B)
+constexpr int kStageS = 2048;  // bytes of MXFP8 scales per stage (A then B)
 
 // Compile-time loop: f(integral_constant<int, 0>) ... f(<N-1>), so indices
 // into accumulator arrays stay constants (registers, never scratch).
@@ -151,7 +151,8 @@ MOE_DEV GluVal glu_eval(float g_pre, float u_pre, const ActP& p) {
 // Buffer resource over `bytes` bytes at `base`.  Raw (untyped) loads whose
 // VGPR offset reaches num_records return zero without touching memory; row
 // indices therefore always go into the VGPR offset (the scalar offset only
-// carries the K position), so partial tiles need no clamping.
+// carries the K position, and never takes a valid row past its end), so
+// partial tiles need no clamping.
 MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            static_cast<int>(bytes), 0x00020000);
@@ -159,52 +160,99 @@ MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 
 constexpr int kOutOfRange = 0x7fffffff;  // VGPR offset past any num_records
 
-MOE_DEV void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds_block, int voff, int soff) {
+MOE_DEV void dma16(__amdgpu_buffer_rsrc_t r, void* lds_block, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_block, 16, voff, soff, 0, 0);
 }
+MOE_DEV void dma4(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, voff, soff, 0, 0);
+}
 
-// K-contiguous tile of 256 rows x 64 bytes (32 bf16 or 64 E4M3 values) of
-// a [rows][K] operand straight from HBM into one LDS stage.  LDS image: row
-// r = 64 bytes, 16-byte chunk c stored at c ^ ((r >> 2) & 3).  A 16-byte LDS
-// read serves 16 lanes per cycle over 64 banks (256 bytes); the operand
-// reads touch 16 consecutive rows in one chunk, which this swizzle spreads
-// over all 16 bank groups.  Wave w fills the 1 KB blocks 4w .. 4w+3; lane l
-// of block b lands on row 16 b + l / 4, stored chunk l % 4, so it fetches
-// logical chunk (l % 4) ^ ((l / 16) % 4).
+// Chunk swizzle of the K-contiguous LDS image: 16-byte chunk c of row r is
+// stored at c ^ ((r >> 1) & 7).  An operand read (ds_read_b128) serves 16
+// lanes per cycle: 16 consecutive rows, one logical chunk; rows 128 bytes
+// apart land on bank groups 32 (r % 2) + 4 (c ^ ((r >> 1) & 7)), all 16
+// distinct.
+MOE_DEV int kswz(int row) { return (row >> 1) & 7; }
+
+// K-contiguous tile of 256 rows x 128 bytes (64 bf16 or 128 E4M3 values) of
+// a [rows][K] operand straight from HBM into one LDS stage.  Whole 128-byte
+// lines: one DMA instruction moves 8 rows x 128 bytes (1 KB), so every L2
+// request returns a full line (a 64-byte-per-row pattern halves what the L1
+// can stream).  Wave w fills 1 KB blocks 8w .. 8w+7; lane l of block b
+// lands on row 8 b + l / 8, stored chunk l % 8, so it fetches logical chunk
+// (l % 8) ^ kswz(row).  With MXFP8 and K % 128 == 64 the chunks past K of
+// the last stage are zero-filled per lane.
 struct KLoader {
   __amdgpu_buffer_rsrc_t rsrc;
-  int voff[4];  // bytes
+  int voff[8];    // bytes
+  int kbyte[2];   // byte position of the lane's chunk in a stage row (even / odd j)
 
   MOE_DEV void init(const void* base, int64_t rows_avail, int ld_bytes, int wave, int lane) {
     const int64_t rows = rows_avail < 256 ? rows_avail : 256;
     rsrc = make_rsrc(base, static_cast<uint32_t>(rows * ld_bytes));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 64 * wave + 16 * j + (lane >> 2);
-      const int kc = (lane & 3) ^ ((lane >> 4) & 3);
+    for (int j = 0; j < 8; ++j) {
+      const int row = 64 * wave + 8 * j + (lane >> 3);
+      const int kc = (lane & 7) ^ kswz(row);   // depends on j only through j % 2
+      if (j < 2) kbyte[j] = kc * 16;
       voff[j] = row * ld_bytes + kc * 16;
     }
   }
-  // kt: K step (64 bytes per row); valid == false fills the stage with zeros
-  MOE_DEV void issue(uint16_t* stage, int kt, int wave_s, bool valid) {
+  // kt: stage (128 bytes per row); valid == false fills the stage with
+  // zeros; k_bytes: bytes per row of the operand (for the per-lane K tail)
+  template <bool TAIL>
+  MOE_DEV void issue(uint16_t* stage, int kt, int wave_s, bool valid, int k_bytes) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dma16(rsrc, stage + (4 * wave_s + j) * 512, valid ? voff[j] : kOutOfRange, valid ? kt * 64 : 0);
+    for (int j = 0; j < 8; ++j) {
+      bool ok = valid;
+      if constexpr (TAIL) ok = ok && (kt * kRowBytes + kbyte[j & 1] < k_bytes);
+      dma16(rsrc, stage + (8 * wave_s + j) * 512, ok ? voff[j] : kOutOfRange,
+            valid ? kt * kRowBytes : 0);
+    }
   }
 };
 
-// MXFP8 scales of one K step for a 256-row A tile and a 256-row B tile, in
-// the tiled layout: 8 row groups x 64 bytes each, copied to a 1 KB LDS stage
-// (A groups 0..7, then B groups 0..7).  Waves 0, 1 copy A groups 4w .. 4w+3,
-// waves 2, 3 copy B groups 4(w - 2) ..; lane l fetches bytes 4 (l % 16) .. +3
-// of group 4 (w % 2) + l / 16, which lands at LDS byte 4 l of its quarter.
-MOE_DEV void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, voff, soff, 0, 0);
-}
+// N-contiguous tile of 64 K rows x 256 columns of a [K][N] bf16 matrix,
+// copied as is (512-byte rows, whole lines) into one LDS stage: 16-byte chunk
+// c of row k stored at c ^ (4 (k % 8)).  The MFMA operand is then read with
+// the LDS transpose load.  Wave w fills 1 KB blocks 8w .. 8w+7 (two rows
+// each).  Column chunks past N are clamped to the last chunk (their results
+// are discarded), so every address lies inside the matrix.
+struct NLoader {
+  __amdgpu_buffer_rsrc_t rsrc;
+  int voff[8];   // bytes
 
+  MOE_DEV void init(const uint16_t* mat, uint32_t mat_bytes, int N, int col0, int wave, int lane) {
+    rsrc = make_rsrc(mat, mat_bytes);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 16 * wave + 2 * j + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (row & 7));
+      const int col = min(col0 + 8 * c, N - 8);
+      voff[j] = (row * N + col) * 2;
+    }
+  }
+  // soff: byte offset of the stage's first row, k0 * N * 2 (a wave-uniform
+  // value the caller computes from the kernel arguments)
+  MOE_DEV void issue(uint16_t* stage, int soff, int wave_s, bool valid) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      dma16(rsrc, stage + (8 * wave_s + j) * 512, valid ? voff[j] : kOutOfRange, valid ? soff : 0);
+  }
+};
+
+// MXFP8 scales of one stage (two 64-deep K steps) for a 256-row A tile and
+// a 256-row B tile.  In the tiled layout the scales of a 32-row group for
+// steps 2 kt and 2 kt + 1 are one contiguous 128-byte run; the stage image
+// is [A | B] x 8 row groups x [step][64 bytes] = 2 KB.  Waves 0, 1 copy A
+// groups 4w .. 4w+3, waves 2, 3 copy B's, two dword DMAs each: lane l of
+// instruction i fetches bytes 4 (l % 32) .. +3 of the run of group
+// 4 (w % 2) + 2 i + l / 32, which lands at byte 4 l of the instruction's
+// 256 bytes.  A step past K (K % 128 == 64) is zero-filled per lane.
 struct ScaleLoader {
   __amdgpu_buffer_rsrc_t rsrc;
-  int voff;
+  int voff[2];
+  int step;       // step (0 or 1) inside the stage this lane fetches
 
   // s_tile: scales of the tile's first row group; groups_avail: row groups
   // of 32 that exist from there on
@@ -212,40 +260,17 @@ struct ScaleLoader {
     const int64_t groups = groups_avail < 8 ? (groups_avail > 0 ? groups_avail : 0) : 8;
     const int per_group = (K / 64) * 64;
     rsrc = make_rsrc(s_tile, static_cast<uint32_t>(groups * per_group));
-    voff = (4 * (wave & 1) + (lane >> 4)) * per_group + 4 * (lane & 15);
-  }
-  MOE_DEV void issue(uint8_t* stage, int kt, int wave_s, bool valid) {
-    dma4(rsrc, stage + (wave_s >> 1) * 512 + (wave_s & 1) * 256, valid ? voff : kOutOfRange,
-         valid ? kt * 64 : 0);
-  }
-};
-
-// N-contiguous [BK][256] tile of a [K][N] matrix, copied as is into one LDS
-// stage: row k = 512 bytes, 16-byte chunk c stored at c ^ (4 (k % 8)).  The
-// MFMA operand is then read with the LDS transpose load.  Wave w fills the
-// 1 KB blocks 4w .. 4w+3 (two rows each).  Column chunks past N are clamped
-// to the last chunk (their results are discarded), so every address lies
-// inside the matrix.
-struct NLoader {
-  __amdgpu_buffer_rsrc_t rsrc;
-  int voff[4];   // bytes
-
-  MOE_DEV void init(const uint16_t* mat, uint32_t mat_bytes, int N, int col0, int wave, int lane) {
-    rsrc = make_rsrc(mat, mat_bytes);
+    step = (lane >> 4) & 1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 8 * wave + 2 * j + (lane >> 5);
-      const int c = (lane & 31) ^ (4 * (row & 7));
-      const int col = min(col0 + 8 * c, N - 8);
-      voff[j] = (row * N + col) * 2;
-    }
+    for (int i = 0; i < 2; ++i)
+      voff[i] = (4 * (wave & 1) + 2 * i + (lane >> 5)) * per_group + 4 * (lane & 31);
   }
-  // soff: byte offset of the tile's first row, k0 * N * 2 (a wave-uniform
-  // value the caller computes from the kernel arguments)
-  MOE_DEV void issue(uint16_t* stage, int soff, int wave_s, bool valid) {
+  MOE_DEV void issue(uint8_t* stage, int kt, int wave_s, bool valid, int k_steps64) {
+    const bool ok = valid && (2 * kt + step < k_steps64);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dma16(rsrc, stage + (4 * wave_s + j) * 512, valid ? voff[j] : kOutOfRange, valid ? soff : 0);
+    for (int i = 0; i < 2; ++i)
+      dma4(rsrc, stage + (wave_s >> 1) * 1024 + (wave_s & 1) * 512 + i * 256,
+           ok ? voff[i] : kOutOfRange, valid ? kt * 128 : 0);
   }
 };
 
@@ -776,10 +801,10 @@ template <int EPI, bool NN, int ACT, bool MX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_kernel(GemmArgs g) {
   static_assert(!(MX && NN), "MXFP8 operands are always K-contiguous");
-  __shared__ __attribute__((aligned(1024))) uint16_t sA0[kStageA], sA1[kStageA], sA2[kStageA], sA3[kStageA];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB0[kStageB], sB1[kStageB], sB2[kStageB], sB3[kStageB];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[kStageBytes / 2], sA1[kStageBytes / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[kStageBytes / 2], sB1[kStageBytes / 2];
   constexpr int kScaleBytes = MX ? kStageS : 4;
-  __shared__ __attribute__((aligned(1024))) uint8_t sS0[kScaleBytes], sS1[kScaleBytes], sS2[kScaleBytes], sS3[kScaleBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sS0[kScaleBytes], sS1[kScaleBytes];
   __shared__ int s_start[kMaxExperts + 1];
   __shared__ int s_split[kMaxExperts];
   __shared__ int s_pad[kMaxExperts];
@@ -825,20 +850,21 @@ void grouped_gemm_kernel(GemmArgs g) {
   if (G % kNumXcd == 0) vid = (blockIdx.x % kNumXcd) * (G / kNumXcd) + blockIdx.x / kNumXcd;
 
   // per-lane LDS byte offsets of the MFMA operands.  K-contiguous image:
-  // row base + 16-byte chunk (2 ks + lane / 32) ^ ((row >> 2) & 3), the
-  // swizzle term being the same for rows 32 apart.  [K][N] image (B of the
-  // dgrad GEMMs, read with ds_read_b64_tr_b16): in each 16-lane group g,
-  // source lane s = 4 r + q points at 4 consecutive columns
-  // nb + 16 (g % 2) + 4 q of row 16 ks + 8 (g / 2) + 4 h + r, h selecting
-  // the first or second 4 of the lane's 8 K values.
+  // row base + 16-byte chunk (2 ks + lane / 32) ^ kswz(row) for the
+  // 16-deep bf16 sub-step ks (0..3); the swizzle term is the same for rows
+  // 32 apart.  [K][N] image (B of the bf16 dgrad GEMMs, read with
+  // ds_read_b64_tr_b16): in each 16-lane group g, source lane s = 4 r + q
+  // points at 4 consecutive columns nb + 16 (g % 2) + 4 q of row
+  // 16 ks + 8 (g / 2) + 4 h + r, h selecting the first or second 4 of the
+  // lane's 8 K values.
   const int khalf = lane >> 5;
   const int arow = wm * kWaveM + (lane & 31);
   const int brow = wn * kWaveN + (lane & 31);
-  int a_off[2], b_off[2];
+  int a_off[4], b_off[4];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    a_off[ks] = (arow * 4 + ((2 * ks + khalf) ^ ((arow >> 2) & 3))) * 16;
-    b_off[ks] = (brow * 4 + ((2 * ks + khalf) ^ ((brow >> 2) & 3))) * 16;
+  for (int ks = 0; ks < 4; ++ks) {
+    a_off[ks] = arow * kRowBytes + ((2 * ks + khalf) ^ kswz(arow)) * 16;
+    b_off[ks] = brow * kRowBytes + ((2 * ks + khalf) ^ kswz(brow)) * 16;
   }
   int btr_off[2][4];
   {
@@ -852,10 +878,10 @@ void grouped_gemm_kernel(GemmArgs g) {
         btr_off[h][ni] = row * 512 + (c ^ (4 * (row & 7))) * 16 + 8 * (sl & 1);
       }
   }
-  // MXFP8 scale bytes of this lane's rows (row group 4 wm + mi of A, 4 wn + ni
-  // of B) for its K block (lane / 32) inside a scale stage
-  const int sa_off = 4 * wm * 64 + lane;
-  const int sb_off = 512 + 4 * wn * 64 + lane;
+  // MXFP8 scale byte of this lane's row (row group 4 wm + mi of A, 4 wn + ni
+  // of B) for its K block (lane / 32) of 64-deep step j of a scale stage
+  const int sa_off = 4 * wm * 128 + lane;
+  const int sb_off = 1024 + 4 * wn * 128 + lane;
 
   // ---- per-tile geometry --------------------------------------------
   struct TileInfo {
@@ -894,31 +920,34 @@ void grouped_gemm_kernel(GemmArgs g) {
     return ti;
   };
 
-  const int nk = g.K / (MX ? 64 : BK);
+  // stages of 128 bytes per row: 64 bf16 or 128 E4M3 K values; an MXFP8 K
+  // with K % 128 == 64 ends in a half stage whose second half is zero-filled
+  const int k_bytes = g.K * kElem;
+  const int nk = (k_bytes + kRowBytes - 1) / kRowBytes;
+  const int k_steps64 = g.K / 64;  // MXFP8 64-deep MFMA steps
   const char* A = static_cast<const char*>(g.A);
   const char* B = static_cast<const char*>(g.B);
   KLoader la;
   KLoader lb_k;
   NLoader lb_n;
   ScaleLoader ls;
-  // K order of a tile: steps k_rot, k_rot + 1, ..., nk - 1, 0, ..., k_rot - 1
+  // K order of a tile: stages k_rot, k_rot + 1, ..., nk - 1, 0, ..., k_rot - 1
   // with k_rot = stride * (m_t + n_t) mod nk.  Tiles that share an operand
   // panel (same m_t or same n_t; an XCD holds a band of neighbouring tiles
-  // at once) then reach a given K slice of it one or more steps apart rather
-  // than in lockstep: the first one's L2 miss brings the slice in and the
-  // others hit, instead of all of them waiting on the same MALL/HBM fetch.
+  // at once) then reach a given K slice of it one or more stages apart
+  // rather than in lockstep: the first one's L2 miss brings the slice in and
+  // the others hit, instead of all of them waiting on the same MALL/HBM fetch.
   int k_rot = 0;
   auto issue_stage = [&](uint16_t* a_st, uint16_t* b_st, uint8_t* s_st, int kt) {
     const bool valid = kt < nk;
     int kk = kt + k_rot;
     if (kk >= nk) kk -= nk;
-    la.issue(a_st, kk, wave_s, valid);
+    la.template issue<MX>(a_st, kk, wave_s, valid, k_bytes);
     if constexpr (NN) lb_n.issue(b_st, kk * BK * (g.N * 2), wave_s, valid);
-    else lb_k.issue(b_st, kk, wave_s, valid);
-    if constexpr (MX) ls.issue(s_st, kk, wave_s, valid);
+    else lb_k.template issue<MX>(b_st, kk, wave_s, valid, k_bytes);
+    if constexpr (MX) ls.issue(s_st, kk, wave_s, valid, k_steps64);
   };
-  // point the loaders at a tile and start its first K steps (three for
-  // bf16, four for MXFP8)
+  // point the loaders at a tile and start its first two stages
   auto start_tile = [&](const TileInfo& ti) {
     k_rot = nk > 0 ? (g.k_rot_stride * (ti.m_t + ti.n_t)) % nk : 0;
     const int64_t rows_avail = ti.rows_valid > 0 ? g.M_cap - ti.row0 : 0;
@@ -944,8 +973,6 @@ void grouped_gemm_kernel(GemmArgs g) {
     }
     issue_stage(sA0, sB0, sS0, 0);
     issue_stage(sA1, sB1, sS1, 1);
-    issue_stage(sA2, sB2, sS2, 2);
-    if constexpr (MX) issue_stage(sA3, sB3, sS3, 3);
   };
 
   f32x16 acc[4][4];
@@ -955,146 +982,122 @@ void grouped_gemm_kernel(GemmArgs g) {
     asm volatile("" ::: "memory");
   };
 
-  // ------------------------------------------------------ bf16 K loop ---
-  bf16x8 fa[2][4], fb[2][4];
-  // operands of the 16-deep sub-step ks of a stage into register set buf
-  auto read_frags = [&](const uint16_t* a_st, const uint16_t* b_st, auto ks, auto buf) {
+  // ------------------------------------------------------------ K loop ---
+  // A stage holds NS MFMA sub-steps: four 16-deep bf16 steps or two 64-deep
+  // MXFP8 steps.  Operands are double-buffered in registers across
+  // sub-steps; the operands of sub-step j + 1 are read while the MFMAs of
+  // sub-step j run.  Before the last sub-step of a stage every wave waits
+  // for its reads of the stage and for the next stage's loads (the only
+  // ones in flight), a barrier follows, the freed buffer starts loading the
+  // stage after next, and the first operands of the next stage are read
+  // while the last MFMAs of this one run.  So a stage's loads have a whole
+  // stage of MFMA work (2048 cycles at full rate) to land.
+  constexpr int NS = MX ? 2 : 4;
+  bf16x8 fa[2][4], fb[2][4];   // bf16 operands
+  i32x8 qa[2][4], qb[2][4];    // MXFP8 operands
+  int sca[2][4], scb[2][4];    // MXFP8 scales
+  // operands of sub-step j of a stage into register set buf
+  auto read_frags = [&](const uint16_t* a_st, const uint16_t* b_st, const uint8_t* s_st, auto j,
+                        auto buf) {
     const char* ca = reinterpret_cast<const char*>(a_st);
     const char* cb = reinterpret_cast<const char*>(b_st);
-    sfor<4>([&](auto i) {
-      fa[buf][i] = *reinterpret_cast<const bf16x8*>(ca + a_off[ks] + i * 32 * 64);
-    });
-    if constexpr (NN) {
-      sfor<4>([&](auto ni) {
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_t*)(cb + btr_off[0][ni] + ks * 16 * 512));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_t*)(cb + btr_off[1][ni] + ks * 16 * 512));
-        const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        fb[buf][ni] = __builtin_bit_cast(bf16x8, both);
+    constexpr int jj = decltype(j)::value;
+    if constexpr (MX) {
+      // a lane's 32-byte operand of a 64-deep step: chunks 4 j + h and
+      // 4 j + 2 + h, the layout v_mfma_scale_f32_32x32x64_f8f6f4 takes
+      sfor<4>([&](auto i) {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(ca + a_off[2 * jj] + i * 32 * kRowBytes);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(ca + a_off[2 * jj + 1] + i * 32 * kRowBytes);
+        qa[buf][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      });
+      sfor<4>([&](auto i) {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(cb + b_off[2 * jj] + i * 32 * kRowBytes);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(cb + b_off[2 * jj + 1] + i * 32 * kRowBytes);
+        qb[buf][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      });
+      sfor<4>([&](auto i) {
+        sca[buf][i] = s_st[sa_off + i * 128 + jj * 64];
+        scb[buf][i] = s_st[sb_off + i * 128 + jj * 64];
       });
     } else {
       sfor<4>([&](auto i) {
-        fb[buf][i] = *reinterpret_cast<const bf16x8*>(cb + b_off[ks] + i * 32 * 64);
+        fa[buf][i] = *reinterpret_cast<const bf16x8*>(ca + a_off[jj] + i * 32 * kRowBytes);
       });
+      if constexpr (NN) {
+        sfor<4>([&](auto ni) {
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_t*)(cb + btr_off[0][ni] + jj * 16 * 512));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_t*)(cb + btr_off[1][ni] + jj * 16 * 512));
+          const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          fb[buf][ni] = __builtin_bit_cast(bf16x8, both);
+        });
+      } else {
+        sfor<4>([&](auto i) {
+          fb[buf][i] = *reinterpret_cast<const bf16x8*>(cb + b_off[jj] + i * 32 * kRowBytes);
+        });
+      }
     }
   };
-  // C^T blocks: B fragment first, so a lane owns one output row
+  // C^T blocks: B operand first, so a lane owns one output row
   auto mfma_all = [&](auto buf) {
     sfor<4>([&](auto mi) { sfor<4>([&](auto ni) {
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][ni], fa[buf][mi],
-                                                            acc[mi][ni], 0, 0, 0);
+      if constexpr (MX)
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            qb[buf][ni], qa[buf][mi], acc[mi][ni], 0, 0, 0, scb[buf][ni], 0, sca[buf][mi]);
+      else
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][ni], fa[buf][mi],
+                                                              acc[mi][ni], 0, 0, 0);
     }); });
   };
-  // Issue order inside a phase.  A DMA load blocks the wave until the
-  // address unit accepts it (about 16 cycles per 1 KB wave load, shared by
-  // the four waves), so the loads of the next stage are spread between
-  // MFMAs instead of issued in a burst; the operand reads of the next
-  // 16-deep sub-step go in between as well.
-  constexpr int kReadsPerPhase = NN ? 12 : 8;
-  auto pin_load_phase = [&]() {
+  // LDS reads per sub-step and DMA loads per stage (per wave)
+  constexpr int kReads = MX ? 24 : (NN ? 12 : 8);
+  constexpr int kLoads = 16 + (MX ? 2 : 0);
+  // issue order: reads spread between the 16 MFMAs of a sub-step; in the
+  // last sub-step of a stage the next stage's DMA loads go in between too
+  // (a DMA load blocks the wave until the address unit takes it)
+  auto pin = [&]() {
     sfor<8>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (DMA) load
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, (kReads + 7) / 8, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);           // MFMA
     });
-    if constexpr (kReadsPerPhase > 8)
-      __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerPhase - 8, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto pin_phase = [&]() {
+  auto pin_load = [&]() {
+    if constexpr (kLoads > 16) __builtin_amdgcn_sched_group_barrier(0x020, kLoads - 16, 0);
     sfor<8>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerPhase / 8 + (NN ? 1 : 0), 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);           // VMEM (DMA)
+      __builtin_amdgcn_sched_group_barrier(0x100, (kReads + 7) / 8, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     });
     __builtin_amdgcn_sched_barrier(0);
   };
-  // One K step: MFMAs on stage cur, then the next stage; loads for step
-  // kt+3 go into stage ld.  Before the barrier a wave waits until only the
-  // loads of steps kt+2 and kt+3 are outstanding (8 DMA loads per step)
-  // and its reads of stage cur are done; the barrier carries no fence (a
-  // fence would also wait for the loads still in flight).
-  constexpr int kLoadsPerStep = 8;
-  auto kstep = [&](const uint16_t* a_cur, const uint16_t* b_cur, const uint16_t* a_nxt,
-                   const uint16_t* b_nxt, uint16_t* a_ld, uint16_t* b_ld, int kt) {
+  // One stage (kt): cur = its buffers, nxt = the next stage's; the freed
+  // cur buffers take stage kt + 2.
+  auto stage = [&](const uint16_t* a_cur, const uint16_t* b_cur, const uint8_t* s_cur,
+                   uint16_t* a_nxt, uint16_t* b_nxt, uint8_t* s_nxt, int kt) {
+    sfor<NS - 1>([&](auto j) {
+      __builtin_amdgcn_sched_barrier(0);
+      constexpr int jj = decltype(j)::value;
+      read_frags(a_cur, b_cur, s_cur, std::integral_constant<int, jj + 1>{},
+                 std::integral_constant<int, (jj + 1) % 2>{});
+      mfma_all(std::integral_constant<int, jj % 2>{});
+      pin();
+    });
     __builtin_amdgcn_sched_barrier(0);
-    issue_stage(a_ld, b_ld, nullptr, kt + 3);
-    read_frags(a_cur, b_cur, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
-    mfma_all(std::integral_constant<int, 0>{});
-    pin_load_phase();
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerStep));
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     bare_barrier();
-    read_frags(a_nxt, b_nxt, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    mfma_all(std::integral_constant<int, 1>{});
-    pin_phase();
+    issue_stage(const_cast<uint16_t*>(a_cur), const_cast<uint16_t*>(b_cur),
+                const_cast<uint8_t*>(s_cur), kt + 2);
+    read_frags(a_nxt, b_nxt, s_nxt, std::integral_constant<int, 0>{},
+               std::integral_constant<int, NS % 2>{});
+    mfma_all(std::integral_constant<int, (NS - 1) % 2>{});
+    pin_load();
   };
-
-  // ----------------------------------------------------- MXFP8 K loop ---
-  // A lane's operand for one 64-deep step is the two 16-byte chunks at
-  // a_off[0] and a_off[1] (K 16h .. 16h+15 and 32+16h .. 32+16h+15, h =
-  // lane / 32), the layout v_mfma_scale_f32_32x32x64_f8f6f4 takes; its scale
-  // operand is the E8M0 byte of the lane's row for K block h.
-  i32x8 qa[2][4], qb[2][4];
-  int sca[2][4], scb[2][4];
-  auto read_frags_mx = [&](const uint16_t* a_st, const uint16_t* b_st, const uint8_t* s_st,
-                           auto buf) {
-    const char* ca = reinterpret_cast<const char*>(a_st);
-    const char* cb = reinterpret_cast<const char*>(b_st);
-    sfor<4>([&](auto i) {
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(ca + a_off[0] + i * 32 * 64);
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(ca + a_off[1] + i * 32 * 64);
-      qa[buf][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    });
-    sfor<4>([&](auto i) {
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(cb + b_off[0] + i * 32 * 64);
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(cb + b_off[1] + i * 32 * 64);
-      qb[buf][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    });
-    sfor<4>([&](auto i) {
-      sca[buf][i] = s_st[sa_off + i * 64];
-      scb[buf][i] = s_st[sb_off + i * 64];
-    });
-  };
-  auto mfma_all_mx = [&](auto buf) {
-    sfor<4>([&](auto mi) { sfor<4>([&](auto ni) {
-      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          qb[buf][ni], qa[buf][mi], acc[mi][ni], 0, 0, 0, scb[buf][ni], 0, sca[buf][mi]);
-    }); });
-  };
-  // per step: 9 DMA loads per wave (4 A, 4 B, 1 scale), 24 LDS reads,
-  // 16 MFMAs of 64 cycles
-  constexpr int kLoadsPerStepMx = 9;
-  auto pin_mx = [&]() {
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    sfor<8>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    });
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // One step: wait for stage kt+1 and for every wave to be done reading
-  // stage kt (its operands are already in registers set cur), then load
-  // step kt+4 into stage kt's slot, read stage kt+1 into the other register
-  // set and run the MFMAs of step kt.
-  auto kstep_mx = [&](auto cur, const uint16_t* a_nxt, const uint16_t* b_nxt,
-                      const uint8_t* s_nxt, uint16_t* a_ld, uint16_t* b_ld, uint8_t* s_ld,
-                      int kt) {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerStepMx));
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    bare_barrier();
-    issue_stage(a_ld, b_ld, s_ld, kt + 4);
-    read_frags_mx(a_nxt, b_nxt, s_nxt, std::integral_constant<int, 1 - decltype(cur)::value>{});
-    mfma_all_mx(cur);
-    pin_mx();
-  };
+  static_assert(NS % 2 == 0, "sub-step register sets alternate 0, 1 across stages");
 
   // ---- persistent tile loop -------------------------------------------
-  // 4-stage pipeline, unrolled by 4 so every stage is a distinct LDS array
-  // named statically (the compiler then sees that a load in flight never
-  // targets the stage being read); steps past the end of K load zeros.
   int tile = vid;
   TileInfo cur{};
   if (tile < total) {
@@ -1103,28 +1106,12 @@ void grouped_gemm_kernel(GemmArgs g) {
   }
   while (tile < total) {
     sfor<4>([&](auto mi) { sfor<4>([&](auto ni) { acc[mi][ni] = f32x16{}; }); });
-    if constexpr (MX) {
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * kLoadsPerStepMx));
-      bare_barrier();
-      read_frags_mx(sA0, sB0, sS0, std::integral_constant<int, 0>{});
-      using C0 = std::integral_constant<int, 0>;
-      using C1 = std::integral_constant<int, 1>;
-      for (int kt = 0; kt < nk; kt += 4) {
-        kstep_mx(C0{}, sA1, sB1, sS1, sA0, sB0, sS0, kt);
-        kstep_mx(C1{}, sA2, sB2, sS2, sA1, sB1, sS1, kt + 1);
-        kstep_mx(C0{}, sA3, sB3, sS3, sA2, sB2, sS2, kt + 2);
-        kstep_mx(C1{}, sA0, sB0, sS0, sA3, sB3, sS3, kt + 3);
-      }
-    } else {
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerStep));
-      bare_barrier();
-      read_frags(sA0, sB0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-      for (int kt = 0; kt < nk; kt += 4) {
-        kstep(sA0, sB0, sA1, sB1, sA3, sB3, kt);
-        kstep(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
-        kstep(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
-        kstep(sA3, sB3, sA0, sB0, sA2, sB2, kt + 3);
-      }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLoads));   // stage 0 landed
+    bare_barrier();
+    read_frags(sA0, sB0, sS0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    for (int kt = 0; kt < nk; kt += 2) {
+      stage(sA0, sB0, sS0, sA1, sB1, sS1, kt);
+      stage(sA1, sB1, sS1, sA0, sB0, sS0, kt + 1);
     }
     // the loads still in flight are zero fills; then every wave is done
     // with the stages and the next tile may start loading
