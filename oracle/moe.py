@@ -422,12 +422,28 @@ def backward(fw: Forward, dout_bits, w1_bits, w2_bits, prm: ActParams, *,
 def sample_rows_forward(xp_rows, w1_e, w2_e, p_rows, prm: ActParams,
                         mx=False):
     """FC1 -> activation -> prob scale -> FC2 for a few rows of one expert
-    (for spot checks at sizes where the whole layer is too slow)."""
+    (for spot checks at sizes where the whole layer is too slow).
+    xp_rows float64 [n][H]; w1_e [N1][H] logical layout; w2_e [H][I];
+    p_rows [n].  Returns the stored (bf16) z, a and y rows."""
     xe = _mx_operand(xp_rows, 1, mx)
     ze = xe @ _mx_operand(w1_e, 1, mx).T
     ae = round_bf16(p_rows[:, None] * act_forward(ze, prm))
     ye = _mx_operand(ae, 1, mx) @ _mx_operand(w2_e, 1, mx).T
     return round_bf16(ze), ae, round_bf16(ye)
+
+
+def sample_rows_backward(dyp_rows, z_rows, w1_e, w2_e, p_rows,
+                         prm: ActParams):
+    """The backward of `backward` for a few rows of one expert (bf16
+    operands): dA = dyp W2, the activation gradient from the stored z rows,
+    dp = sum(dA * s), dxp = dz W1.  Returns the stored dz and dxp rows and
+    dp."""
+    da = dyp_rows @ w2_e
+    s = act_forward(z_rows, prm)
+    dp = np.sum(da * s, axis=1)
+    dz = round_bf16(act_backward(z_rows, p_rows[:, None] * da, prm))
+    dxp = round_bf16(dz @ w1_e)
+    return dz, dxp, dp
 
 
 def flops(M: int, H: int, I: int, gated: bool = True) -> dict:

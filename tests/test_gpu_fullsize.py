@@ -1,0 +1,221 @@
+"""Parity at the benchmark's full sizes and launch configuration (needs an
+MI355X).
+
+The inputs are bench.py's own (bench.device_inputs: routing from the host
+generator, activations and weights drawn on the device), the block is built
+exactly as bench.py builds it, and one forward + backward step runs.  The
+whole-layer oracle is too slow at these sizes, so:
+  * routing metadata (split sizes, offsets, row map, row sources, permuted
+    probabilities) is compared in full, bit-exact;
+  * bf16: every stored tensor of sampled tokens (both of their slots) is
+    recomputed one row at a time by the oracle (oracle.moe.sample_rows_*):
+    z, a, yp, out, dz, dxp, dprobs_p, dx and dprobs;
+  * MXFP8: the oracle's cost is in encoding whole weight matrices, so the
+    checks use sampled (row, column) outputs that need only the weight rows
+    or columns involved: the MXFP8 copy of the permuted input rows
+    (bit-exact), FC1 outputs z, the activation a, its MXFP8 copy on sampled
+    blocks, the FC2-dgrad + dActivation output dz and its MXFP8 copy on
+    sampled blocks;
+  * amax equals max |a| over the valid rows (a property at any size).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+import moe_grouped_mlp_amd as mg
+from oracle import moe as om
+from oracle import numerics as nu
+from workloads.gen import CONFIGS
+
+from .gpu_util import (assert_close, assert_close_mx, assert_mx_equal, assert_mx_near,
+                       compare_routing, mx_scale_index, uninterleave_cols)
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    mg.lib()
+
+
+def _run(name, prec):
+    cfg = dict(CONFIGS[name])
+    E, k, T, H, I = (cfg[n] for n in ("E", "k", "T", "H", "I"))
+    dev = torch.device("cuda")
+    print(f"full-size {name} {prec}: generating inputs", flush=True)
+    x, dout, w1, w2, idx, probs = bench.device_inputs(cfg, 0, dev)
+    kind = {"swiglu": mg.ACT_SWIGLU, "geglu": mg.ACT_GEGLU, "srelu": mg.ACT_SRELU}[cfg["act"]]
+    act = mg.act_params(kind, beta=cfg["beta"], clamp=cfg["clamp"])
+    blk = mg.ExpertBlock(E, H, I, T, k, act=act,
+                         prec=mg.PREC_MXFP8 if prec == "mxfp8" else mg.PREC_BF16)
+    blk.load_weights(w1, w2)
+    blk.forward(x, idx, probs)
+    blk.backward(dout)
+    torch.cuda.synchronize()
+    assert int(blk.err_flag.cpu()[0]) == 0
+    idx_h, probs_h = idx.cpu().numpy(), probs.cpu().numpy()
+    rt = om.route(idx_h, probs_h, E, 0, blk.M_cap)
+    compare_routing(blk, rt)
+    op = om.ActParams.clamped(cfg["clamp"], beta=cfg["beta"], act=cfg["act"])
+    return cfg, blk, (x, dout, w1, w2, idx_h, probs_h), rt, op
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _rows_f64(t, rows):
+    return nu.bf16_to_f64(_bits(t[torch.as_tensor(rows, device=t.device)]))
+
+
+def _amax_property(blk):
+    valid = blk.row_src >= 0
+    a_max = blk.a[valid].float().abs().max().item()
+    assert float(blk.amax.cpu()[0]) == a_max
+
+
+def _sample_tokens(rt, idx, n, seed):
+    """The first and last token, a token routed to the largest group, one
+    routed to the smallest non-empty group, and n random tokens."""
+    sizes = rt.split_sizes
+    live = np.flatnonzero(sizes > 0)
+    big, small = int(live[np.argmax(sizes[live])]), int(live[np.argmin(sizes[live])])
+    T = idx.shape[0]
+    t_big = int(np.flatnonzero(np.any(idx == big, axis=1))[0])
+    t_small = int(np.flatnonzero(np.any(idx == small, axis=1))[-1])
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, T - 1, t_big, t_small], rng.choice(T, n, replace=False)]))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["mixtral", "gptoss", "dsv3"])
+def test_full_size_bf16_sampled_tokens(name):
+    cfg, blk, (x, dout, w1, w2, idx, probs), rt, op = _run(name, "bf16")
+    E, k, I = cfg["E"], cfg["k"], cfg["I"]
+    if name == "dsv3":
+        assert rt.split_sizes[0] == 0 and rt.split_sizes[-1] == 0
+    _amax_property(blk)
+    tokens = _sample_tokens(rt, idx, 4 if name == "mixtral" else 8, seed=len(name))
+    chosen = np.unique(idx[tokens])
+    print(f"checking {len(tokens)} tokens on experts {chosen.tolist()}", flush=True)
+    x_h = nu.bf16_to_f64(_bits(x[torch.as_tensor(tokens, device=x.device)]))
+    d_h = nu.bf16_to_f64(_bits(dout[torch.as_tensor(tokens, device=x.device)]))
+    res = {}
+    for e in chosen.tolist():
+        sel = [(i, s) for i, t in enumerate(tokens) for s in range(k) if idx[t, s] == e]
+        if not sel:
+            continue
+        w1e = nu.bf16_to_f64(_bits(w1[e]))
+        w2e = nu.bf16_to_f64(_bits(w2[e]))
+        xi = np.stack([x_h[i] for i, _ in sel])
+        di = np.stack([d_h[i] for i, _ in sel])
+        p = np.array([float(probs[tokens[i], s]) for i, s in sel])
+        z, a, y = om.sample_rows_forward(xi, w1e, w2e, p, op)
+        dz, dxp, dp = om.sample_rows_backward(di, z, w1e, w2e, p, op)
+        for n_, (i, s) in enumerate(sel):
+            res[(i, s)] = (z[n_], a[n_], y[n_], dz[n_], dxp[n_], dp[n_])
+        del w1e, w2e
+    keys = sorted(res)
+    rows = [int(rt.row_id_map[tokens[i], s]) for i, s in keys]
+    z_g = nu.bf16_to_f64(_bits(blk.z[torch.as_tensor(rows, device="cuda")]))
+    if cfg["act"] != "srelu":
+        z_g = uninterleave_cols(z_g, I)
+    dz_g = nu.bf16_to_f64(_bits(blk.dz[torch.as_tensor(rows, device="cuda")]))
+    if cfg["act"] != "srelu":
+        dz_g = uninterleave_cols(dz_g, I)
+    assert_close(z_g, np.stack([res[kk][0] for kk in keys]), "z rows")
+    assert_close(_rows_f64(blk.a, rows), np.stack([res[kk][1] for kk in keys]), "a rows")
+    assert_close(_rows_f64(blk.yp, rows), np.stack([res[kk][2] for kk in keys]), "yp rows")
+    assert_close(dz_g, np.stack([res[kk][3] for kk in keys]), "dz rows")
+    assert_close(_rows_f64(blk.dxp, rows), np.stack([res[kk][4] for kk in keys]), "dxp rows")
+    dpp = blk.dprobs_p[torch.as_tensor(rows, device="cuda")].cpu().numpy().astype(np.float64)
+    assert_close(dpp, np.array([res[kk][5] for kk in keys]), "dprobs_p rows")
+    # combined outputs of the sampled tokens (all their slots were computed)
+    out_ref = np.stack([om.round_bf16(sum(res[(i, s)][2] for s in range(k)))
+                        for i in range(len(tokens))])
+    dx_ref = np.stack([om.round_bf16(sum(res[(i, s)][4] for s in range(k)))
+                       for i in range(len(tokens))])
+    assert_close(_rows_f64(blk.out, tokens), out_ref, "out tokens")
+    assert_close(_rows_f64(blk.dx, tokens), dx_ref, "dx tokens")
+    dpr = blk.dprobs.cpu().numpy()[tokens].astype(np.float64)
+    assert_close(dpr, np.array([[res[(i, s)][5] for s in range(k)] for i in range(len(tokens))]),
+                 "dprobs tokens")
+
+
+@pytest.mark.timeout(900)
+def test_mixtral_mx_full_size_sampled():
+    cfg, blk, (x, dout, w1, w2, idx, probs), rt, op = _run("mixtral_mx", "mxfp8")
+    E, k, H, I = cfg["E"], cfg["k"], cfg["H"], cfg["I"]
+    M_cap = blk.M_cap
+    _amax_property(blk)
+    rng = np.random.default_rng(11)
+    valid_rows = np.flatnonzero(rt.row_src >= 0)
+    rows = np.sort(rng.choice(valid_rows, size=6, replace=False))
+    blocks = np.sort(rng.choice(I // 32, size=2, replace=False))   # 32-column blocks of a
+    cols = np.concatenate([32 * b + np.arange(32) for b in blocks])
+    expert = om.expert_of_rows(rt)
+    packed = np.argsort(om.interleave_rows(I))   # packed position of each logical column
+    sidx_x = mx_scale_index(M_cap, H)
+    sidx_a = mx_scale_index(M_cap, I)
+    sidx_dz = mx_scale_index(M_cap, 2 * I)
+    xq_g = blk.xp_q.cpu().numpy()
+    xs_g = blk.xp_s.cpu().numpy()
+    z_g = nu.bf16_to_f64(_bits(blk.z[torch.as_tensor(rows, device="cuda")]))
+    a_g = nu.bf16_to_f64(_bits(blk.a[torch.as_tensor(rows, device="cuda")]))
+    dz_g = nu.bf16_to_f64(_bits(blk.dz[torch.as_tensor(rows, device="cuda")]))
+    aq_g = blk.a_q[torch.as_tensor(rows, device="cuda")].cpu().numpy()
+    as_g = blk.a_s.cpu().numpy()
+    dzq_g = blk.dz_q[torch.as_tensor(rows, device="cuda")].cpu().numpy()
+    dzs_g = blk.dz_s.cpu().numpy()
+    z_ref, z_got, a_ref, a_got, dz_ref, dz_got = [], [], [], [], [], []
+    mx_checks = []   # run after the value checks, which localise a problem better
+    for n_, r in enumerate(rows):
+        t, e = int(rt.row_src[r]), int(expert[r])
+        p = float(rt.probs_p[r])
+        xr = nu.bf16_to_f64(_bits(x[t]))
+        # permuted input row, MXFP8 along H: bit-exact
+        assert_mx_equal(xq_g[r], xs_g[sidx_x[r]], nu.mx_quantize(xr[None, :], axis=1),
+                        f"xp MX row {r}")
+        xq = nu.mx_round(xr[None, :], axis=1)[0]
+        w1e = w1[e]
+        g_rows = nu.mx_round(nu.bf16_to_f64(_bits(w1e[torch.as_tensor(cols, device="cuda")])), 1)
+        u_rows = nu.mx_round(nu.bf16_to_f64(_bits(w1e[torch.as_tensor(I + cols, device="cuda")])), 1)
+        zg, zu = g_rows @ xq, u_rows @ xq
+        z_ref += [om.round_bf16(zg), om.round_bf16(zu)]
+        z_got += [z_g[n_][packed[cols]], z_g[n_][packed[I + cols]]]
+        s_half = om.act_forward(np.concatenate([zg, zu])[None, :], op)[0]
+        a_cols = om.round_bf16(p * s_half)
+        a_ref.append(a_cols)
+        a_got.append(a_g[n_][cols])
+        # the fused MXFP8 copy of a on the sampled blocks
+        for bi, b in enumerate(blocks):
+            ref = nu.mx_quantize(a_cols[None, 32 * bi:32 * bi + 32], axis=1)
+            mx_checks.append((aq_g[n_][32 * b:32 * b + 32][None, :],
+                              as_g[sidx_a[r, b:b + 1]][None, :], ref, f"a MX row {r} block {b}"))
+        # FC2 dgrad + dActivation on the same columns: dA needs the columns
+        # of W2 (along H) and the quantized dOut row
+        dr = nu.bf16_to_f64(_bits(dout[t]))
+        dq = nu.mx_round(dr[None, :], axis=1)[0]
+        w2c = nu.bf16_to_f64(_bits(w2[e][:, torch.as_tensor(cols, device="cuda")].contiguous()))
+        da = dq @ nu.mx_round(w2c, axis=0)
+        zs = np.concatenate([om.round_bf16(zg), om.round_bf16(zu)])[None, :]
+        d = om.act_backward(zs, p * da[None, :], op)[0]
+        dzc = om.round_bf16(d)
+        dz_ref.append(dzc)
+        dz_got.append(np.concatenate([dz_g[n_][packed[cols]], dz_g[n_][packed[I + cols]]]))
+        for bi, b in enumerate(blocks):
+            for half, off in ((0, 0), (1, I)):
+                pk = packed[off + 32 * b]          # first packed column of the block
+                ref = nu.mx_quantize(dzc[None, half * len(cols) + 32 * bi:
+                                          half * len(cols) + 32 * bi + 32], axis=1)
+                mx_checks.append((dzq_g[n_][pk:pk + 32][None, :],
+                                  dzs_g[sidx_dz[r, pk // 32:pk // 32 + 1]][None, :], ref,
+                                  f"dz MX row {r} block {pk // 32} (gpu dz "
+                                  f"{dz_g[n_][pk:pk + 4]} oracle {dzc[half * len(cols) + 32 * bi:][:4]})"))
+    assert_close_mx(np.concatenate(z_got), np.concatenate(z_ref), "z samples")
+    assert_close_mx(np.concatenate(a_got), np.concatenate(a_ref), "a samples")
+    assert_close_mx(np.concatenate(dz_got), np.concatenate(dz_ref), "dz samples")
+    for q, sc, ref, what in mx_checks:
+        assert_mx_near(q, sc, ref, what, code_frac=0.1, far_frac=0.05, scale_frac=1.0)

@@ -316,3 +316,33 @@ def test_rounded_layer_stores_bf16_values():
     assert 0 < err < 0.1
     c, s = fm.aT_mx
     assert c.shape == (wl.I, int(fm.rt.padded_offsets[-1]))
+
+
+@pytest.mark.parametrize("act,mx", [("swiglu", False), ("srelu", False), ("swiglu", True)])
+def test_sampled_rows_equal_the_full_layer(act, mx):
+    """The per-row forward/backward used by the full-size spot checks
+    reproduce the full layer's stored rows exactly (same arithmetic on a
+    subset of rows)."""
+    wl = make_workload("tiny", seed=4, act=act, T=200)
+    prm = moe.ActParams.clamped(None, act=act)
+    fw = moe.forward(wl.x, wl.w1, wl.w2, wl.expert_idx, wl.probs, wl.E, prm, mx=mx)
+    bw = moe.backward(fw, wl.dout, wl.w1, wl.w2, prm)
+    x = nu.bf16_to_f64(wl.x)
+    dout = nu.bf16_to_f64(wl.dout)
+    w1 = nu.bf16_to_f64(wl.w1)
+    w2 = nu.bf16_to_f64(wl.w2)
+    rng = np.random.default_rng(0)
+    for t in rng.choice(wl.T, size=12, replace=False):
+        for s in range(wl.k):
+            e, r = int(wl.expert_idx[t, s]), int(fw.rt.row_id_map[t, s])
+            p = np.array([float(wl.probs[t, s])])
+            z, a, y = moe.sample_rows_forward(x[t:t + 1], w1[e], w2[e], p, prm, mx=mx)
+            np.testing.assert_array_equal(z[0], fw.z[r])
+            np.testing.assert_array_equal(a[0], fw.a[r])
+            np.testing.assert_array_equal(y[0], fw.y[r])
+            if not mx:
+                dz, dxp, dp = moe.sample_rows_backward(dout[t:t + 1], fw.z[r:r + 1], w1[e],
+                                                       w2[e], p, prm)
+                np.testing.assert_array_equal(dz[0], bw.dz[r])
+                np.testing.assert_array_equal(dxp[0], bw.dxp[r])
+                assert dp[0] == bw.dp[r]
