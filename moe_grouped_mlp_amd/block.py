@@ -11,7 +11,10 @@ of a training step on the current stream:
 
 With prec=PREC_MXFP8 the permutes write MXFP8 rows (no bf16 copy), the four
 GEMMs take MXFP8 operands, and quantize_weights() (once per weight update)
-makes the four weight copies the GEMMs read, each blocked along its K.
+makes the four weight copies the GEMMs read, each blocked along its K.  The
+epilogues then write only the MXFP8 copies of a and dz that the next GEMMs
+(and weight-gradient GEMMs) read, unless bf16_copies=True also asks for the
+bf16 tensors.
 
 No call reads device memory back or synchronises, so a whole step can be
 captured in a HIP graph.
@@ -31,7 +34,7 @@ class ExpertBlock:
                  act: Optional[B.ActParams] = None, first_expert: int = 0,
                  M_cap: Optional[int] = None, cu_margin: int = 0,
                  prec: int = B.PREC_BF16, transposed_copies: bool = True,
-                 device="cuda"):
+                 bf16_copies: Optional[bool] = None, device="cuda"):
         self.E, self.H, self.I, self.T, self.k = E, H, I, T, k
         self.act = act or B.act_params()
         self.gated = self.act.act != B.ACT_SRELU
@@ -59,12 +62,14 @@ class ExpertBlock:
         self.err_flag = torch.zeros(1, **i32)
         self.ws_route = torch.empty(max(1, B.moe_permute_workspace_size(T, E)),
                                     dtype=torch.uint8, device=dev)
+        # bf16 a and dz: operands of the bf16 GEMMs; optional with MXFP8
+        keep = (not self.mx) if bf16_copies is None else (bf16_copies or not self.mx)
         self.z = torch.empty(M, N1, **bf)
-        self.a = torch.empty(M, I, **bf)
+        self.a = torch.empty(M, I, **bf) if keep else None
         self.yp = torch.empty(M, H, **bf)
         self.out = torch.empty(T, H, **bf)
         self.amax = torch.zeros(1, **f32)
-        self.dz = torch.empty(M, N1, **bf)
+        self.dz = torch.empty(M, N1, **bf) if keep else None
         self.dprobs_p = torch.zeros(M, **f32)
         self.dxp = torch.empty(M, H, **bf)
         self.dx = torch.empty(T, H, **bf)

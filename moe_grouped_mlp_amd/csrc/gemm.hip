@@ -325,34 +325,6 @@ struct MxOut {
   int64_t M_cap;
 };
 
-template <int CTRL>
-MOE_DEV uint32_t dpp_u(uint32_t x) {
-  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, true));
-}
-template <int CTRL>
-MOE_DEV float dpp_f(float x) { return __uint_as_float(dpp_u<CTRL>(__float_as_uint(x))); }
-
-// Maximum over the 32 lanes of each half-wave: within quads (xor 1, xor 2),
-// then the mirrored quad of each 8 and the mirrored 8 of each 16 (DPP), then
-// the other 16 lanes of the half (ds_swizzle, lane ^ 16).
-MOE_DEV float half_wave_max(float x) {
-  x = fmaxf(x, dpp_f<0xB1>(x));
-  x = fmaxf(x, dpp_f<0x4E>(x));
-  x = fmaxf(x, dpp_f<0x141>(x));
-  x = fmaxf(x, dpp_f<0x140>(x));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));
-  return x;
-}
-
-MOE_DEV uint32_t mx_codes4v(const float* v, const float* inv) {
-  float c[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_fmed3f(v[i] * inv[i], -448.0f, 448.0f);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
-  return static_cast<uint32_t>(w);
-}
-
 // A lane's 16 values of one 32 x 32 output block: v[4 rg + i] is column
 // 8 rg + 4 hf + i (hf = lane / 32) of the lane's row (lane % 32), the
 // values being bf16 numbers (zero for rows that hold no data).
@@ -374,41 +346,51 @@ MOE_DEV void mx_row_block(const float (&v)[16], uint8_t* q_row, uint8_t* s_byte,
 }
 
 // Transposed: column c of the block is one MX block of the transposed copy
-// (rows 32 rb .. 32 rb + 31), held by the 32 lanes of a half-wave.  Each lane
-// encodes its row's 4 columns of a run (one word), then a 4 x 4 byte
-// transpose inside the quad (DPP + v_perm_b32) leaves lane j of quad q4 with
-// column 8 rg + 4 hf + j of rows 4 q4 .. 4 q4 + 3, stored as one word.
-MOE_DEV void mx_col_block(const float (&v)[16], const MxOut& o, int64_t rb, int col0, int lane) {
-  const int hf = lane >> 5, j = lane & 3, q4 = (lane & 31) >> 2;
-  const uint32_t sel1 = (lane & 1) ? 0x03070105u : 0x06020400u;
-  const uint32_t sel2 = (lane & 2) ? 0x03020706u : 0x05040100u;
+// (rows 32 rb .. 32 rb + 31).  The wave stages its 32 x 32 bf16 block in a
+// private LDS tile (row pitch kTrPitch), then lane l reads rows
+// 16 (l / 32) .. +15 of column l % 32, so a column's block maximum is one
+// partner exchange (lane ^ 32) and its 16 codes are one 16-byte store.  LDS
+// operations of one wave complete in order, so no barrier is needed and the
+// tile is reused block after block.
+constexpr int kTrPitch = 36;   // bf16 per staged row (8-byte aligned rows)
+constexpr int kTrTile = 32 * kTrPitch;
+
+MOE_DEV void mx_col_block(const float (&v)[16], uint16_t* tr, const MxOut& o, int64_t rb,
+                          int col0, int lane) {
+  const int row = lane & 31, hf = lane >> 5;
 #pragma unroll
-  for (int rg = 0; rg < 4; ++rg) {
-    int e[4];
-    float inv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      e[i] = mx_exponent(half_wave_max(fabsf(v[4 * rg + i])));
-      inv[i] = mx_inv_scale(e[i]);
-    }
-    const uint32_t d = mx_codes4v(&v[4 * rg], inv);
-    const uint32_t t = __builtin_amdgcn_perm(dpp_u<0xB1>(d), d, sel1);
-    const uint32_t w = __builtin_amdgcn_perm(dpp_u<0x4E>(t), t, sel2);
-    const int col = col0 + 8 * rg + 4 * hf + j;
-    *reinterpret_cast<uint32_t*>(o.qT + static_cast<int64_t>(col) * o.M_cap + rb * 32 + 4 * q4) = w;
-    if (q4 == 0) {
-      const int ej = j == 0 ? e[0] : j == 1 ? e[1] : j == 2 ? e[2] : e[3];
-      o.sT[mx_scale_off(col, rb, o.M_cap)] = mx_scale_code(ej);
-    }
+  for (int rg = 0; rg < 4; ++rg) {   // the values are bf16 numbers: keep their high halves
+    uint2 w;
+    w.x = (__float_as_uint(v[4 * rg]) >> 16) | (__float_as_uint(v[4 * rg + 1]) & 0xffff0000u);
+    w.y = (__float_as_uint(v[4 * rg + 2]) >> 16) | (__float_as_uint(v[4 * rg + 3]) & 0xffff0000u);
+    *reinterpret_cast<uint2*>(tr + row * kTrPitch + 8 * rg + 4 * hf) = w;
   }
+  float c[16];
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    c[i] = __uint_as_float(static_cast<uint32_t>(tr[(16 * hf + i) * kTrPitch + row]) << 16);
+    am = fmaxf(am, fabsf(c[i]));
+  }
+  am = fmaxf(am, __shfl_xor(am, 32, kWave));
+  const int e = mx_exponent(am);
+  const float inv = mx_inv_scale(e);
+  uint4 q;
+  q.x = mx_codes4(c[0], c[1], c[2], c[3], inv);
+  q.y = mx_codes4(c[4], c[5], c[6], c[7], inv);
+  q.z = mx_codes4(c[8], c[9], c[10], c[11], inv);
+  q.w = mx_codes4(c[12], c[13], c[14], c[15], inv);
+  const int col = col0 + row;
+  *reinterpret_cast<uint4*>(o.qT + static_cast<int64_t>(col) * o.M_cap + rb * 32 + 16 * hf) = q;
+  if (hf == 0) o.sT[mx_scale_off(col, rb, o.M_cap)] = mx_scale_code(e);
 }
 
 // Both MXFP8 copies of one block whose rows all lie before the group's
 // padded end.
-MOE_DEV void mx_block_out(const float (&v)[16], const MxOut& o, int64_t row, int64_t rb, int col0,
-                          int lane) {
+MOE_DEV void mx_block_out(const float (&v)[16], const MxOut& o, uint16_t* tr, int64_t row,
+                          int64_t rb, int col0, int lane) {
   mx_row_block(v, o.q + row * o.n + col0, o.s + mx_scale_off(row, col0 / 32, o.n), lane >> 5);
-  if (o.qT) mx_col_block(v, o, rb, col0, lane);
+  if (o.qT) mx_col_block(v, tr, o, rb, col0, lane);
 }
 
 MOE_DEV void bf16x4_to_f32(uint2 w, float* v) {
@@ -604,7 +586,7 @@ template <int ACT>
 MOE_DEV float epi_glu_mx(const f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz,
                          uint16_t* __restrict__ a, int64_t lda, const float* __restrict__ probs,
                          const ActP& act, const TileCtx& t, int wn, int wm, int lane,
-                         const MxOut& mo) {
+                         const MxOut& mo, uint16_t* tr) {
   constexpr bool gated = ACT != MOE_ACT_SRELU;
   const int hf = lane >> 5;
   float amax = 0.0f;
@@ -640,7 +622,7 @@ MOE_DEV float epi_glu_mx(const f32x16 (&acc)[4][4], uint16_t* __restrict__ z, in
           });
 #pragma unroll
           for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ab[r]));
-          if (blk_ok) mx_block_out(ab, mo, row, rb, q * MOE_INTERLEAVE + h * 32, lane);
+          if (blk_ok) mx_block_out(ab, mo, tr, row, rb, q * MOE_INTERLEAVE + h * 32, lane);
         });
       }
     } else {
@@ -664,7 +646,7 @@ MOE_DEV float epi_glu_mx(const f32x16 (&acc)[4][4], uint16_t* __restrict__ z, in
           });
 #pragma unroll
           for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ab[r]));
-          if (blk_ok) mx_block_out(ab, mo, row, rb, cb, lane);
+          if (blk_ok) mx_block_out(ab, mo, tr, row, rb, cb, lane);
         }
       });
     }
@@ -680,7 +662,7 @@ template <int ACT>
 MOE_DEV void epi_dglu_mx(const f32x16 (&acc)[4][4], const uint16_t* __restrict__ zin, int64_t ldz,
                          uint16_t* __restrict__ dz, int64_t lddz, const float* __restrict__ probs,
                          const ActP& act, const TileCtx& t, int wn, int wm, int lane,
-                         float (&dp_out)[4], const MxOut& mo) {
+                         float (&dp_out)[4], const MxOut& mo, uint16_t* tr) {
   constexpr bool gated = ACT != MOE_ACT_SRELU;
   const int h4 = 4 * (lane >> 5);
   const int lane_col = gated ? 2 * t.col0 + 256 * wn + h4 : t.col0 + 128 * wn + h4;
@@ -756,10 +738,10 @@ MOE_DEV void epi_dglu_mx(const f32x16 (&acc)[4][4], const uint16_t* __restrict__
         if (blk_ok) {
           if constexpr (gated) {
             const int cbg = 2 * t.col0 + 256 * wn + 128 * (ni / 2) + 32 * (ni % 2);
-            mx_block_out(gv, mo, row, rb, cbg, lane);
-            mx_block_out(uv, mo, row, rb, cbg + MOE_INTERLEAVE, lane);
+            mx_block_out(gv, mo, tr, row, rb, cbg, lane);
+            mx_block_out(uv, mo, tr, row, rb, cbg + MOE_INTERLEAVE, lane);
           } else {
-            mx_block_out(gv, mo, row, rb, t.col0 + 128 * wn + 32 * ni, lane);
+            mx_block_out(gv, mo, tr, row, rb, t.col0 + 128 * wn + 32 * ni, lane);
           }
         }
       }
@@ -810,6 +792,9 @@ void grouped_gemm_kernel(GemmArgs g) {
   __shared__ int s_pad[kMaxExperts];
   __shared__ int s_tmp[kThreads / 64];
   __shared__ float s_red[2 * BM];
+  // per-wave staging tiles of the transposed MXFP8 copies (MX epilogues)
+  constexpr int kTrWords = (MX && EPI != EPI_STORE) ? 4 * kTrTile : 4;
+  __shared__ __attribute__((aligned(16))) uint16_t s_tr[kTrWords];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1141,7 +1126,7 @@ void grouped_gemm_kernel(GemmArgs g) {
       float amax;
       if constexpr (MX)
         amax = epi_glu_mx<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, g.probs, g.act, t, wn, wm,
-                               lane, mo);
+                               lane, mo, s_tr + wave * kTrTile);
       else
         amax = epi_glu<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, g.probs, g.act, t, wn, lane);
       if (g.amax) {
@@ -1151,7 +1136,8 @@ void grouped_gemm_kernel(GemmArgs g) {
     } else {
       float dp[4];
       if constexpr (MX)
-        epi_dglu_mx<ACT>(acc, g.zin, g.ldz, g.C, g.ldc, g.probs, g.act, t, wn, wm, lane, dp, mo);
+        epi_dglu_mx<ACT>(acc, g.zin, g.ldz, g.C, g.ldc, g.probs, g.act, t, wn, wm, lane, dp, mo,
+                         s_tr + wave * kTrTile);
       else
         epi_dglu<ACT>(acc, g.zin, g.ldz, g.C, g.ldc, g.probs, g.act, t, wn, lane, dp);
       sfor<4>([&](auto mi) {

@@ -61,12 +61,15 @@ def act_of(wl, prm_override=None):
     return gp, op
 
 
-def run_gpu_layer(wl, M_cap=None, backward=True, block=None, prec=None):
-    """Run the HIP path on a workload; returns the block holding the results."""
+def run_gpu_layer(wl, M_cap=None, backward=True, block=None, prec=None,
+                  bf16_copies=True):
+    """Run the HIP path on a workload; returns the block holding the results
+    (with MXFP8, also the optional bf16 a and dz unless bf16_copies=False)."""
     gp, _ = act_of(wl)
     blk = block or mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, act=gp,
                                   first_expert=wl.first_expert, M_cap=M_cap,
-                                  prec=mg.PREC_BF16 if prec is None else prec)
+                                  prec=mg.PREC_BF16 if prec is None else prec,
+                                  bf16_copies=bf16_copies)
     w1 = dev_bf16(wl.w1)
     w2 = dev_bf16(wl.w2)
     blk.load_weights(w1, w2)

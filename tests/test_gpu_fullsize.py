@@ -48,8 +48,11 @@ def _run(name, prec):
     x, dout, w1, w2, idx, probs = bench.device_inputs(cfg, 0, dev)
     kind = {"swiglu": mg.ACT_SWIGLU, "geglu": mg.ACT_GEGLU, "srelu": mg.ACT_SRELU}[cfg["act"]]
     act = mg.act_params(kind, beta=cfg["beta"], clamp=cfg["clamp"])
+    # bench.py's block; with MXFP8 the bf16 a and dz are kept for the checks
+    # (they do not change what is computed)
     blk = mg.ExpertBlock(E, H, I, T, k, act=act,
-                         prec=mg.PREC_MXFP8 if prec == "mxfp8" else mg.PREC_BF16)
+                         prec=mg.PREC_MXFP8 if prec == "mxfp8" else mg.PREC_BF16,
+                         bf16_copies=True)
     blk.load_weights(w1, w2)
     blk.forward(x, idx, probs)
     blk.backward(dout)

@@ -274,3 +274,21 @@ def test_mx_graph_capture_replays_match_eager():
             if i >= 3:
                 t, e = t[:mp], e[:mp]
             assert torch.equal(t, e)
+
+
+def test_mx_outputs_do_not_depend_on_bf16_copies():
+    """Without the optional bf16 a and dz the MXFP8 outputs are bit-identical."""
+    wl = make_workload("tiny", seed=21, E=8, T=768, H=256, I=192)
+    M_cap = -(-wl.m_cap() // 128) * 128
+    b1 = run_gpu_layer(wl, M_cap, prec=mg.PREC_MXFP8, bf16_copies=True)
+    r1 = [t.clone() for t in (b1.a_q, b1.aT_q, b1.dz_q, b1.dzT_q, b1.out, b1.dx, b1.dprobs)]
+    b2 = run_gpu_layer(wl, M_cap, prec=mg.PREC_MXFP8, bf16_copies=False)
+    assert b2.a is None and b2.dz is None
+    mp = int(b2.padded_offsets[-1].item())
+    for i, (u, v) in enumerate(zip(r1, (b2.a_q, b2.aT_q, b2.dz_q, b2.dzT_q, b2.out, b2.dx,
+                                         b2.dprobs))):
+        if i in (0, 2):
+            u, v = u[:mp], v[:mp]
+        elif i in (1, 3):
+            u, v = u[:, :mp], v[:, :mp]
+        assert torch.equal(u, v), i
