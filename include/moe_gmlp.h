@@ -306,6 +306,10 @@ typedef struct moe_fwd_args {
   const uint8_t* w2_q;  const uint8_t* w2_s;   /* [E][H][I],  along I   */
   uint8_t* a_q;   uint8_t* a_s;                /* [M_cap][I], along I   */
   uint8_t* aT_q;  uint8_t* aT_s;               /* [I][M_cap], along M (optional) */
+  /* optional workspace (moe_grouped_mlp_workspace_size bytes): lets FC2
+   * split its last, partial round of tiles along K; NULL disables that */
+  void* workspace;
+  size_t workspace_bytes;
 } moe_fwd_args;
 
 moe_status moe_grouped_mlp_fwd(const moe_fwd_args* args, void* stream);
@@ -374,7 +378,11 @@ typedef struct moe_bwd_args {
 
 moe_status moe_grouped_mlp_bwd(const moe_bwd_args* args, void* stream);
 
-/* Workspace bytes moe_grouped_mlp_bwd needs for these sizes. */
+/* Workspace bytes for these sizes: the backward needs at least the dprobs
+ * partials (fp32 M_cap x ceil(I / 256)); the full size adds the area where
+ * the plain-store GEMMs (FC2, FC1 dgrad) split their last, partial round of
+ * tiles along K (partial tiles reduced in a fixed order, so results stay
+ * deterministic).  One buffer may serve the forward and the backward. */
 size_t moe_grouped_mlp_workspace_size(int E, int H, int I, int64_t M_cap,
                                       int prec, int act);
 

@@ -86,7 +86,8 @@ class FwdArgs(ctypes.Structure):
                 ("w1_q", c_void_p), ("w1_s", c_void_p),
                 ("w2_q", c_void_p), ("w2_s", c_void_p),
                 ("a_q", c_void_p), ("a_s", c_void_p),
-                ("aT_q", c_void_p), ("aT_s", c_void_p)]
+                ("aT_q", c_void_p), ("aT_s", c_void_p),
+                ("workspace", c_void_p), ("workspace_bytes", c_size_t)]
 
 
 class BwdArgs(ctypes.Structure):
@@ -241,14 +242,14 @@ def moe_grouped_mlp_fwd(*, E, H, I, M_cap, split_sizes, padded_offsets,
                         cu_margin=0, w1_stride=0, w2_stride=0, err_flag=None,
                         timing_events=None, xp_q=None, xp_s=None, w1_q=None,
                         w1_s=None, w2_q=None, w2_s=None, a_q=None, a_s=None,
-                        aT_q=None, aT_s=None, stream=None):
+                        aT_q=None, aT_s=None, workspace=None, stream=None):
     args = FwdArgs(E, H, I, M_cap, prec, act or act_params(), cu_margin,
                    _ptr(split_sizes), _ptr(padded_offsets), _ptr(probs_p),
                    _ptr(xp), _ptr(w1i), _ptr(w2), w1_stride, w2_stride,
                    _ptr(z), _ptr(a), _ptr(amax), _ptr(yp), _ptr(err_flag),
                    _events(timing_events), _ptr(xp_q), _ptr(xp_s), _ptr(w1_q),
                    _ptr(w1_s), _ptr(w2_q), _ptr(w2_s), _ptr(a_q), _ptr(a_s),
-                   _ptr(aT_q), _ptr(aT_s))
+                   _ptr(aT_q), _ptr(aT_s), _ptr(workspace), _nbytes(workspace))
     _check("moe_grouped_mlp_fwd",
            lib().moe_grouped_mlp_fwd(ctypes.byref(args), _stream(stream)))
 

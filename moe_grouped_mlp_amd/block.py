@@ -74,7 +74,7 @@ class ExpertBlock:
         self.dxp = torch.empty(M, H, **bf)
         self.dx = torch.empty(T, H, **bf)
         self.dprobs = torch.zeros(T, k, **f32)
-        self.ws_bwd = torch.empty(
+        self.ws = torch.empty(
             max(1, B.moe_grouped_mlp_workspace_size(E, H, I, M, prec,
                                                     self.act.act)),
             dtype=torch.uint8, device=dev)
@@ -178,7 +178,7 @@ class ExpertBlock:
                               probs_p=self.probs_p, z=self.z, a=self.a,
                               yp=self.yp, amax=self.amax, act=self.act,
                               prec=self.prec, cu_margin=self.cu_margin,
-                              err_flag=self.err_flag,
+                              err_flag=self.err_flag, workspace=self.ws,
                               timing_events=timing_events, **kw)
 
     def combine(self, yp: torch.Tensor, out: torch.Tensor,
@@ -208,7 +208,7 @@ class ExpertBlock:
                               padded_offsets=self.padded_offsets,
                               probs_p=self.probs_p, z=self.z, dz=self.dz,
                               dprobs_p=self.dprobs_p, dxp=self.dxp,
-                              workspace=self.ws_bwd, act=self.act,
+                              workspace=self.ws, act=self.act,
                               prec=self.prec, cu_margin=self.cu_margin,
                               err_flag=self.err_flag,
                               timing_events=timing_events, **kw)

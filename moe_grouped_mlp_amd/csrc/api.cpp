@@ -61,12 +61,18 @@ moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LA
 struct GemmTuning {
   int group_m = 16;  // measured best on MI355X with k_rot = 1 (bf16 and MXFP8)
   int k_rot = 1;
+  int split_max = 4;    // K parts of a split tail tile (1: no split-K); 3-4 measured best
+  int split_min_k = 2;  // K steps each part keeps at least
 };
 const GemmTuning& tuning() {
   static const GemmTuning t = [] {
     GemmTuning v;
     if (const char* e = std::getenv("MOE_GEMM_GROUP_M")) v.group_m = std::max(1, std::atoi(e));
     if (const char* e = std::getenv("MOE_GEMM_KROT")) v.k_rot = std::max(0, std::atoi(e));
+    if (const char* e = std::getenv("MOE_GEMM_SPLIT_MAX"))
+      v.split_max = std::min(std::max(1, std::atoi(e)), moe::grouped_gemm_split_limit());
+    if (const char* e = std::getenv("MOE_GEMM_SPLIT_MIN_K"))
+      v.split_min_k = std::max(1, std::atoi(e));
     return v;
   }();
   return t;
@@ -197,13 +203,42 @@ moe_status moe_quantize_mxfp8(const moe_quant_args* a, void* stream) {
   return launched(moe::launch_quantize_mxfp8(b, static_cast<hipStream_t>(stream)));
 }
 
+// Workspace layout: [dprobs partials, fp32 M_cap x ceil(I / 256)] then, at a
+// 256-byte boundary, the split-K area of the plain-store GEMMs (partial tiles
+// and arrival counters for a grid of one workgroup per CU).
+static size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+static int ws_grid() {
+  int cu = 0;
+  return device_info(&cu) == MOE_OK ? cu : 256;
+}
+
 size_t moe_grouped_mlp_workspace_size(int E, int H, int I, int64_t M_cap, int prec, int act) {
   (void)E;
   (void)H;
   (void)prec;
   (void)act;
   if (I < 1 || M_cap < 0) return 0;
-  return static_cast<size_t>(M_cap * dgrad_parts(I) * sizeof(float));
+  const size_t dp = align256(static_cast<size_t>(M_cap * dgrad_parts(I) * sizeof(float)));
+  return dp + moe::grouped_gemm_split_bytes(ws_grid());
+}
+
+// Point a plain-store GEMM at the split-K area of the workspace (if it is
+// large enough for `grid`) and zero its counters; returns the launch status.
+static moe_status attach_split(moe::GemmArgs& f, void* ws, size_t ws_bytes, size_t offset,
+                               int grid, hipStream_t s) {
+  f.split_ws = nullptr;
+  f.split_cnt = nullptr;
+  f.split_slots = 0;
+  const size_t need = moe::grouped_gemm_split_bytes(grid);
+  if (!ws || ws_bytes < offset + need) return MOE_OK;
+  char* base = static_cast<char*>(ws) + offset;
+  f.split_ws = reinterpret_cast<float*>(base);
+  f.split_slots = grid;
+  f.split_max = tuning().split_max;
+  f.split_min_k = tuning().split_min_k;
+  f.split_cnt = reinterpret_cast<int*>(base + static_cast<size_t>(grid) * 256 * 256 * sizeof(float));
+  // 0.0f has the bit pattern of int 0
+  return launched(moe::launch_fill_f32(reinterpret_cast<float*>(f.split_cnt), 0.0f, grid, s));
 }
 
 // Host-side checks shared by the forward and the backward (no HIP calls, so
@@ -310,8 +345,9 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   f.ldc = a->H;
   f.act_out = nullptr;
   f.amax = nullptr;
-  if (moe_status st = launched(moe::launch_grouped_gemm(
-          f, moe::EPI_STORE, false, mx, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, f.N), s)))
+  const int grid2 = gemm_grid(cu, a->cu_margin, a->M_cap, a->E, f.N);
+  if (moe_status st = attach_split(f, a->workspace, a->workspace_bytes, 0, grid2, s)) return st;
+  if (moe_status st = launched(moe::launch_grouped_gemm(f, moe::EPI_STORE, false, mx, grid2, s)))
     return st;
   record(a->timing_events[2], s);
   return MOE_OK;
@@ -337,8 +373,8 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
     if (a->w2_stride != 0 && a->w2_stride < static_cast<int64_t>(a->H) * a->I)
       return MOE_ERR_INVALID_ARG;
   }
-  const size_t need = moe_grouped_mlp_workspace_size(a->E, a->H, a->I, a->M_cap, a->prec,
-                                                     a->act.act);
+  // the dprobs partials are required; the split-K area is used when present
+  const size_t need = static_cast<size_t>(a->M_cap * dgrad_parts(a->I) * sizeof(float));
   if (!a->workspace || a->workspace_bytes < need) return MOE_ERR_WORKSPACE;
   int cu = 0;
   if (moe_status st = device_info(&cu)) return st;
@@ -419,8 +455,12 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
   }
   f.C = static_cast<uint16_t*>(a->dxp);
   f.ldc = a->H;
-  if (moe_status st = launched(moe::launch_grouped_gemm(
-          f, moe::EPI_STORE, !mx, mx, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, f.N), s)))
+  const int grid2 = gemm_grid(cu, a->cu_margin, a->M_cap, a->E, f.N);
+  const size_t dp_bytes =
+      align256(static_cast<size_t>(a->M_cap * dgrad_parts(a->I) * sizeof(float)));
+  if (moe_status st = attach_split(f, a->workspace, a->workspace_bytes, dp_bytes, grid2, s))
+    return st;
+  if (moe_status st = launched(moe::launch_grouped_gemm(f, moe::EPI_STORE, !mx, mx, grid2, s)))
     return st;
   record(a->timing_events[2], s);
   return MOE_OK;

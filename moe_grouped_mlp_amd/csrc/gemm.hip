@@ -92,6 +92,7 @@ constexpr int kStageBytes = BM * kRowBytes;  // 32 KB per operand per stage
 constexpr int kThreads = 256;
 constexpr int kWaveM = 128;  // rows of a wave's sub-tile
 constexpr int kWaveN = 128;  // cols of a wave's sub-tile
+constexpr int kMaxSplit = 8;  // K parts of a split tail tile
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -871,6 +872,8 @@ void grouped_gemm_kernel(GemmArgs g) {
   // ---- per-tile geometry --------------------------------------------
   struct TileInfo {
     int e, m_t, n_t, col0, cols_valid, rows_valid, rows_pad;
+    int kbeg, kend;   // K stages of this work item
+    int part, slot;   // split-K part and partial-tile slot (parts > 1)
     int64_t row0;
   };
   auto tile_info = [&](int tile) {
@@ -922,11 +925,12 @@ void grouped_gemm_kernel(GemmArgs g) {
   // at once) then reach a given K slice of it one or more stages apart
   // rather than in lockstep: the first one's L2 miss brings the slice in and
   // the others hit, instead of all of them waiting on the same MALL/HBM fetch.
-  int k_rot = 0;
+  int k_rot = 0, k_beg = 0, k_len = nk;
   auto issue_stage = [&](uint16_t* a_st, uint16_t* b_st, uint8_t* s_st, int kt) {
-    const bool valid = kt < nk;
+    const bool valid = kt < k_len;
     int kk = kt + k_rot;
-    if (kk >= nk) kk -= nk;
+    if (kk >= k_len) kk -= k_len;
+    kk += k_beg;
     la.template issue<MX>(a_st, kk, wave_s, valid, k_bytes);
     if constexpr (NN) lb_n.issue(b_st, kk * BK * (g.N * 2), wave_s, valid);
     else lb_k.template issue<MX>(b_st, kk, wave_s, valid, k_bytes);
@@ -934,7 +938,10 @@ void grouped_gemm_kernel(GemmArgs g) {
   };
   // point the loaders at a tile and start its first two stages
   auto start_tile = [&](const TileInfo& ti) {
-    k_rot = nk > 0 ? (g.k_rot_stride * (ti.m_t + ti.n_t)) % nk : 0;
+    const int nk_item = ti.kend - ti.kbeg;
+    k_rot = nk_item > 0 ? (g.k_rot_stride * (ti.m_t + ti.n_t)) % nk_item : 0;
+    k_beg = ti.kbeg;
+    k_len = nk_item;
     const int64_t rows_avail = ti.rows_valid > 0 ? g.M_cap - ti.row0 : 0;
     const int64_t arow0 = ti.rows_valid > 0 ? ti.row0 : 0;
     la.init(A + arow0 * g.K * kElem, rows_avail, g.K * kElem, wave, lane);
@@ -1083,29 +1090,60 @@ void grouped_gemm_kernel(GemmArgs g) {
   static_assert(NS % 2 == 0, "sub-step register sets alternate 0, 1 across stages");
 
   // ---- persistent tile loop -------------------------------------------
-  int tile = vid;
+  // Work items.  Tiles fill `full` = floor(total / G) whole rounds; when the
+  // remaining tail tiles would leave at least half the grid idle in a last
+  // round, each tail tile is split along K into S parts (plain-store GEMMs
+  // with a workspace only).  Every workgroup derives the same split from the
+  // device-computed tile count, so the host never needs it.
+  const int full = (total / G) * G;
+  const int tail = total - full;
+  int S = 1;
+  if constexpr (EPI == EPI_STORE) {
+    if (g.split_ws && tail > 0 && 2 * tail <= G) {
+      S = min(min(G / tail, g.split_max), max(1, nk / max(1, g.split_min_k)));
+      if (tail * S > g.split_slots) S = max(1, g.split_slots / tail);
+    }
+  }
+  const int items = full + tail * S;
+  auto item_info = [&](int w) {
+    int tile = w, part = 0;
+    if (w >= full) {
+      tile = full + (w - full) / S;
+      part = (w - full) % S;
+    }
+    TileInfo ti = tile_info(tile);
+    const int parts = w >= full ? S : 1;
+    ti.part = part;
+    ti.slot = tile - full;
+    ti.kbeg = part * nk / parts;
+    ti.kend = (part + 1) * nk / parts;
+    return ti;
+  };
+
+  int w = vid;
   TileInfo cur{};
-  if (tile < total) {
-    cur = tile_info(tile);
+  if (w < items) {
+    cur = item_info(w);
     start_tile(cur);
   }
-  while (tile < total) {
+  while (w < items) {
     sfor<4>([&](auto mi) { sfor<4>([&](auto ni) { acc[mi][ni] = f32x16{}; }); });
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLoads));   // stage 0 landed
     bare_barrier();
     read_frags(sA0, sB0, sS0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    for (int kt = 0; kt < nk; kt += 2) {
+    for (int kt = 0; kt < k_len; kt += 2) {
       stage(sA0, sB0, sS0, sA1, sB1, sS1, kt);
       stage(sA1, sB1, sS1, sA0, sB0, sS0, kt + 1);
     }
     // the loads still in flight are zero fills; then every wave is done
-    // with the stages and the next tile may start loading
+    // with the stages and the next item may start loading
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     __syncthreads();
     const TileInfo t0 = cur;
-    tile += G;
-    if (tile < total) {
-      cur = tile_info(tile);
+    const bool split = w >= full && S > 1;
+    w += G;
+    if (w < items) {
+      cur = item_info(w);
       start_tile(cur);
     }
 
@@ -1121,7 +1159,44 @@ void grouped_gemm_kernel(GemmArgs g) {
     t.n_lane = wn * kWaveN + 4 * (lane >> 5);
     MxOut mo{g.mx_q, g.mx_s, g.mx_qT, g.mx_sT, g.mx_n, g.M_cap};
     if constexpr (EPI == EPI_STORE) {
-      epi_store(acc, g.C, g.ldc, t);
+      if (split) {
+        // partial tile to slot (t0.slot, part); the part that arrives last
+        // sums all S partials in part order (deterministic) and stores
+        float4* ws = reinterpret_cast<float4*>(g.split_ws) +
+                     static_cast<int64_t>(t0.slot * S + t0.part) * (64 * kThreads);
+        sfor<4>([&](auto mi) { sfor<4>([&](auto ni) { sfor<4>([&](auto q) {
+          const f32x16& a = acc[mi][ni];
+          ws[((mi * 4 + ni) * 4 + q) * kThreads + tid] =
+              make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+        }); }); });
+        // release: the partials reach memory before this part is counted
+        // (another XCD's L2 may hold the tile that reads them)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (tid == 0) s_tmp[0] = atomicAdd(&g.split_cnt[t0.slot], 1);
+        __syncthreads();
+        if (s_tmp[0] == S - 1) {
+          // acquire: drop stale cached copies before reading the partials
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          const float4* base = reinterpret_cast<const float4*>(g.split_ws) +
+                               static_cast<int64_t>(t0.slot * S) * (64 * kThreads);
+          sfor<4>([&](auto mi) { sfor<4>([&](auto ni) { acc[mi][ni] = f32x16{}; }); });
+          for (int p = 0; p < S; ++p) {
+            const float4* src = base + static_cast<int64_t>(p) * (64 * kThreads);
+            sfor<4>([&](auto mi) { sfor<4>([&](auto ni) { sfor<4>([&](auto q) {
+              const float4 v = src[((mi * 4 + ni) * 4 + q) * kThreads + tid];
+              acc[mi][ni][4 * q] += v.x;
+              acc[mi][ni][4 * q + 1] += v.y;
+              acc[mi][ni][4 * q + 2] += v.z;
+              acc[mi][ni][4 * q + 3] += v.w;
+            }); }); });
+          }
+          epi_store(acc, g.C, g.ldc, t);
+        }
+        __syncthreads();   // s_tmp is read by every thread above
+      } else {
+        epi_store(acc, g.C, g.ldc, t);
+      }
     } else if constexpr (EPI == EPI_GLU) {
       float amax;
       if constexpr (MX)
@@ -1191,7 +1266,12 @@ __global__ __launch_bounds__(256) void dprobs_reduce_kernel(
 }  // namespace
 
 int grouped_gemm_tile_n() { return BN; }
+size_t grouped_gemm_split_bytes(int grid) {
+  // one fp32 256 x 256 partial tile per slot, slots <= grid, plus counters
+  return static_cast<size_t>(grid) * (BM * BN * sizeof(float) + sizeof(int));
+}
 int grouped_gemm_tile_m() { return BM; }
+int grouped_gemm_split_limit() { return kMaxSplit; }
 
 template <int EPI, bool NN, bool MX>
 hipError_t launch_act(const GemmArgs& g, int grid, hipStream_t s) {

@@ -60,6 +60,14 @@ struct GemmArgs {
   float* dp_part;        // DGLU: [M_cap][n_part]
   int n_part;
   ActP act;
+  // split-K of the last, partial round of tiles (plain-store epilogue only):
+  // fp32 partial tiles and one arrival counter per split tile (zeroed before
+  // the launch); null disables splitting
+  float* split_ws;
+  int* split_cnt;
+  int split_slots;       // partial tiles split_ws holds
+  int split_max;         // K parts per split tile (<= grouped_gemm_split_limit())
+  int split_min_k;       // K steps each part keeps at least
   // MXFP8 copies of the GLU / DGLU output ([M_cap][mx_n])
   uint8_t* mx_q;
   uint8_t* mx_s;
@@ -71,6 +79,9 @@ struct GemmArgs {
 hipError_t launch_grouped_gemm(const GemmArgs& g, int epi, bool b_nn, bool mx,
                                int grid, hipStream_t s);
 int grouped_gemm_tile_n();  // BN of the launched configuration
+// bytes of split_ws + split_cnt for a grid of `grid` workgroups
+size_t grouped_gemm_split_bytes(int grid);
+int grouped_gemm_split_limit();  // largest split_max the kernel accepts
 int grouped_gemm_tile_m();  // BM
 hipError_t launch_dprobs_reduce(const float* part, int n_part, const int32_t* split,
                                 const int32_t* padded, int E, int64_t M_cap,

@@ -83,6 +83,29 @@ def run_gpu_layer(wl, M_cap=None, backward=True, block=None, prec=None,
     return blk
 
 
+def tail_split_parts(split_sizes, N: int, K: int, grid: int, k_step: int,
+                     split_max: int = 4, split_min_k: int = 2) -> int:
+    """K parts the plain-store grouped GEMM gives each tile of its last,
+    partial round (the kernel's default rule: split only when the tail
+    leaves at least half the grid idle).  Used to make sure a test really
+    reaches the split-K path; 1 means no split."""
+    total = sum(-(-int(s) // 256) for s in split_sizes) * (-(-N // 256))
+    tail = total % grid
+    if tail == 0 or 2 * tail > grid:
+        return 1
+    return min(grid // tail, split_max, max(1, -(-K // k_step) // split_min_k))
+
+
+def gemm_grid(cu_margin: int, M_cap: int, E: int, N: int) -> int:
+    """Workgroups of a grouped GEMM launch (one per CU, minus the margin, a
+    multiple of 8, at most the tiles that can exist)."""
+    g = torch.cuda.get_device_properties(0).multi_processor_count - cu_margin
+    if g >= 8:
+        g -= g % 8
+    ub = (-(-M_cap // 256) + E) * (-(-N // 256))
+    return max(1, min(g, ub))
+
+
 def uninterleave_cols(packed: np.ndarray, I: int) -> np.ndarray:
     """Packed (gate/up interleaved) columns -> logical gate|up columns."""
     src = om.interleave_rows(I)

@@ -161,8 +161,14 @@ def test_bwd_validation():
     for f in ("split_sizes", "padded_offsets", "probs_p", "dyp", "w2", "z",
               "w1i", "dz", "dprobs_p", "dxp", "workspace"):
         setattr(a, f, 64)
-    need = B.moe_grouped_mlp_workspace_size(4, 128, 256, 1024)
-    assert need == 1024 * 1 * 4   # one partial per 256-column tile of I
+    # the dprobs partials (one per 256-column tile of I) are required; the
+    # full size adds the split-K area (one fp32 256 x 256 tile and a counter
+    # per workgroup of a one-per-CU grid; 256 CUs assumed without a device)
+    need = 1024 * 1 * 4
+    full = B.moe_grouped_mlp_workspace_size(4, 128, 256, 1024)
+    assert full == need + 256 * (256 * 256 * 4 + 4)
+    a.workspace_bytes = full
+    assert _call("moe_grouped_mlp_bwd", a) == DEVICE
     a.workspace_bytes = need
     assert _call("moe_grouped_mlp_bwd", a) == DEVICE
     a.workspace_bytes = need - 1

@@ -24,10 +24,10 @@ from oracle import moe as om
 from oracle import numerics as nu
 from workloads import make_workload
 
-from .gpu_util import (assert_close, assert_close_mx, assert_mx_equal,
-                       assert_mx_near, compare_routing, dev_bf16, host_bits,
-                       host_f64, mx_scales_plain, oracle_layer, run_gpu_layer,
-                       uninterleave_cols)
+from .gpu_util import (act_of, assert_close, assert_close_mx, assert_mx_equal,
+                       assert_mx_near, compare_routing, dev_bf16, gemm_grid,
+                       host_bits, host_f64, mx_scales_plain, oracle_layer,
+                       run_gpu_layer, tail_split_parts, uninterleave_cols)
 
 pytestmark = pytest.mark.gpu
 
@@ -181,6 +181,26 @@ def test_layer_mx_parity(case):
     wl = make_workload(kw.pop("name"), seed=5, **kw)
     M_cap = -(-wl.m_cap() // 128) * 128
     blk = run_gpu_layer(wl, M_cap, prec=mg.PREC_MXFP8)
+    fw, bw = oracle_layer(wl, M_cap, mx=True)
+    compare_layer_mx(blk, wl, fw, bw)
+    assert int(blk.err_flag.cpu()[0]) == 0
+
+
+def test_layer_mx_split_k_tail_parity():
+    """MXFP8 operands through the split-K tail of FC2 and FC1 dgrad (a grid
+    of 8 workgroups over 26 output tiles)."""
+    wl = make_workload("tiny", seed=13, E=4, k=2, T=1536, H=512, I=512)
+    M_cap = -(-wl.m_cap() // 128) * 128
+    margin = torch.cuda.get_device_properties(0).multi_processor_count - 8
+    G = gemm_grid(margin, M_cap, wl.E, wl.H)
+    sizes = [int((wl.expert_idx == e).sum()) for e in range(wl.E)]
+    assert G == 8
+    assert tail_split_parts(sizes, wl.H, wl.I, G, 128) > 1         # FC2
+    assert tail_split_parts(sizes, wl.H, 2 * wl.I, G, 128) > 1     # FC1 dgrad
+    gp, _ = act_of(wl)
+    blk = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, act=gp, M_cap=M_cap,
+                         cu_margin=margin, prec=mg.PREC_MXFP8, bf16_copies=True)
+    run_gpu_layer(wl, M_cap, block=blk)
     fw, bw = oracle_layer(wl, M_cap, mx=True)
     compare_layer_mx(blk, wl, fw, bw)
     assert int(blk.err_flag.cpu()[0]) == 0

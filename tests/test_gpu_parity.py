@@ -16,7 +16,8 @@ from oracle import numerics as nu
 from workloads import make_workload
 
 from .gpu_util import (act_of, compare_layer, compare_routing, dev_bf16,
-                       host_bits, oracle_layer, run_gpu_layer)
+                       gemm_grid, host_bits, oracle_layer, run_gpu_layer,
+                       tail_split_parts)
 
 pytestmark = pytest.mark.gpu
 
@@ -168,6 +169,32 @@ def test_layer_all_tokens_one_expert_and_empty_groups():
     fw, bw = oracle_layer(wl, M_cap)
     assert list(fw.rt.split_sizes) == [0, 700, 700, 0]
     compare_layer(blk, wl, fw, bw)
+
+
+def test_layer_split_k_tail_parity():
+    """A grid of 8 workgroups over 26 output tiles: FC2 and FC1 dgrad run
+    three whole rounds, then split the last two tiles along K (partial tiles
+    in the workspace, summed by the part that arrives last).  Results must
+    match the oracle and repeat bit for bit."""
+    wl = make_workload("tiny", seed=13, E=4, k=2, T=1536, H=512, I=512)
+    M_cap = wl.m_cap()
+    margin = torch.cuda.get_device_properties(0).multi_processor_count - 8
+    G = gemm_grid(margin, M_cap, wl.E, wl.H)
+    sizes = [int((wl.expert_idx == e).sum()) for e in range(wl.E)]
+    assert G == 8
+    assert tail_split_parts(sizes, wl.H, wl.I, G, 64) > 1          # FC2
+    assert tail_split_parts(sizes, wl.H, 2 * wl.I, G, 64) > 1      # FC1 dgrad
+    gp, _ = act_of(wl)
+    blk = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, act=gp, M_cap=M_cap,
+                         cu_margin=margin)
+    run_gpu_layer(wl, M_cap, block=blk)
+    r1 = [host_bits(t).copy() for t in (blk.yp, blk.dxp)]
+    fw, bw = oracle_layer(wl, M_cap)
+    compare_layer(blk, wl, fw, bw)
+    run_gpu_layer(wl, M_cap, block=blk)
+    for u, t in zip(r1, (blk.yp, blk.dxp)):
+        np.testing.assert_array_equal(u, host_bits(t))
+    assert int(blk.err_flag.cpu()[0]) == 0
 
 
 def test_layer_is_deterministic():
