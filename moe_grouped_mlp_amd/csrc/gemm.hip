@@ -275,6 +275,62 @@ struct ScaleLoader {
   }
 };
 
+// z rows of a dGLU tile, staged for its epilogue in the two stage buffers
+// (the K loop is done with them): chunk c holds tile rows wm * 128 + 32 c +
+// r (r < 32) of both wave rows wm, rows of wm = 0 in the A buffer and of
+// wm = 1 in the B buffer, ROWB bytes each (the tile's 512 gated or 256
+// sReLU z columns).  Whole rows per DMA instruction (one 1 KB row, or two
+// 512-byte rows), 16-byte chunk c of staged row r stored at c ^ (r % 16):
+// the epilogue's 8-byte reads of one chunk by 32 rows then fall on 16
+// distinct bank groups.  Rows past the group's data and chunks past the z
+// row are zero-filled.  Wave w fills rows 16 (w % 2) .. +15 of half w / 2.
+template <int ROWB>
+struct ZLoader {
+  static constexpr int kRowsPerInstr = 1024 / ROWB;   // 1 or 2
+  static constexpr int kInstr = 16 / kRowsPerInstr;   // DMA loads per wave
+  __amdgpu_buffer_rsrc_t rsrc;
+  int rows;      // rows of the tile with data
+  int ld_bytes;  // bytes per z row
+  int col_byte;  // byte of the tile's first z column in a z row
+
+  MOE_DEV void init(const uint16_t* zin, int64_t ldz, int64_t row0, int rows_valid, int zc0) {
+    rows = rows_valid > 0 ? rows_valid : 0;
+    ld_bytes = static_cast<int>(ldz * 2);
+    col_byte = zc0 * 2;
+    rsrc = make_rsrc(zin + row0 * ldz, static_cast<uint32_t>(static_cast<int64_t>(rows) * ldz * 2));
+  }
+  MOE_DEV void issue(uint16_t* a_st, uint16_t* b_st, int c, int wave_s, int lane) {
+    uint16_t* st = wave_s < 2 ? a_st : b_st;
+    const int wm = wave_s >> 1, r0 = 16 * (wave_s & 1);
+#pragma unroll
+    for (int j = 0; j < kInstr; ++j) {
+      const int r = r0 + kRowsPerInstr * j + (kRowsPerInstr == 2 ? (lane >> 5) : 0);
+      const int chunk = (kRowsPerInstr == 2 ? (lane & 31) : lane) ^ (r & 15);
+      const int trow = wm * 128 + 32 * c + r;
+      const int cb = col_byte + 16 * chunk;
+      const bool ok = trow < rows && cb < ld_bytes;
+      dma16(rsrc, st + (r0 + kRowsPerInstr * j) * (ROWB / 2), ok ? trow * ld_bytes + cb : kOutOfRange,
+            0);
+    }
+  }
+};
+
+// 4 bf16 of a staged z row.  zb: the row's staged bytes plus the lane's
+// column base (the 16-byte chunk 32 wn, gated, or 16 wn, and its 8-byte
+// half); k < 32 (gated) or 16: the chunk within the lane's columns.  The
+// swizzle r16 < 16 leaves the column base's chunk bits alone.
+MOE_DEV uint2 zread(const char* zb, int r16, int k) {
+  return *reinterpret_cast<const uint2*>(zb + ((k ^ r16) << 4));
+}
+
+// Makes v opaque to the optimizer at this point, so address arithmetic
+// derived from it is recomputed where it is used instead of being hoisted
+// out of the tile loop and kept live (spilled) across the K loop.
+MOE_DEV int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // s_waitcnt immediate (gfx9 encoding) that waits until at most `n` vector
 // memory loads of this wave are outstanding.
 constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
@@ -493,91 +549,70 @@ MOE_DEV float epi_glu(const f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64
   return amax;
 }
 
-// EPI_DGLU: acc = dA over logical columns [col0, col0 + BN).  Reads the
-// saved z (both halves), writes dz in the layout of z and returns, per row
-// block mi, this lane's partial sum of dA * s.  The z loads of a row block
-// are all issued before any arithmetic so their latency overlaps.
+// EPI_DGLU, row block MI of the tile: acc = dA over logical columns
+// [col0, col0 + BN).  Reads the lane's row of z (both halves) from its
+// staged copy (zrow, see ZLoader), writes dz in the layout of z and returns
+// this lane's partial sum of dA * s over the block; p is the row's
+// probability.
 //
 // Addresses: the lane's logical columns are col0 + 128 wn + 4 h + 32 ni +
 // 8 rg + i (h = lane / 32); with the 64-column interleave their gate
 // columns are 2 col0 + 256 wn + 4 h + [128 (ni / 2) + 32 (ni % 2) + 8 rg] + i,
-// a lane base plus a compile-time constant, and the up column is 64 further.
-// Whether a 32-column block lies inside N is uniform across the wave.
-template <int ACT>
-MOE_DEV void epi_dglu(const f32x16 (&acc)[4][4], const uint16_t* __restrict__ zin, int64_t ldz,
-                      uint16_t* __restrict__ dz, int64_t lddz,
-                      const float* __restrict__ probs, const ActP& act, const TileCtx& t,
-                      int wn, int lane, float (&dp_out)[4]) {
+// a lane base plus a compile-time constant, and the up column is 64
+// further: staged chunk 32 wn + 16 (ni / 2) + 4 (ni % 2) + rg (up: + 8),
+// half h.  Whether a 32-column block lies inside N is uniform across the
+// wave.
+template <int ACT, int MI>
+MOE_DEV float dglu_rows(const f32x16 (&acc)[4][4], const char* zrow, uint16_t* __restrict__ dz,
+                        int64_t lddz, float p, const ActP& act, const TileCtx& t, int wn,
+                        int lane) {
   constexpr bool gated = ACT != MOE_ACT_SRELU;
-  const int h4 = 4 * (lane >> 5);
-  const int lane_col = gated ? 2 * t.col0 + 256 * wn + h4 : t.col0 + 128 * wn + h4;
-  sfor<4>([&](auto mi) {
-    const int m = t.m_lane + mi * 32;
-    const bool row_ok = m < t.rows_valid;
-    float dp = 0.0f;
-    if (row_ok) {
-      const int64_t row = t.row0 + m;
-      const float p = probs[row];
-      const uint16_t* zb = zin + row * ldz + lane_col;
-      uint16_t* db = dz + row * lddz + lane_col;
-      uint2 zg[4][4], zu[4][4];
-      sfor<4>([&](auto ni) {
-        if (wn * kWaveN + ni * 32 < t.cols_valid) {
-          sfor<4>([&](auto rg) {
-            if constexpr (gated) {
-              constexpr int off = 128 * (ni / 2) + 32 * (ni % 2) + 8 * rg;
-              zg[ni][rg] = *reinterpret_cast<const uint2*>(zb + off);
-              zu[ni][rg] = *reinterpret_cast<const uint2*>(zb + off + MOE_INTERLEAVE);
-            } else {
-              constexpr int off = 32 * ni + 8 * rg;
-              zg[ni][rg] = *reinterpret_cast<const uint2*>(zb + off);
-            }
+  const int m = t.m_lane + MI * 32;
+  if (m >= t.rows_valid) return 0.0f;
+  const int h = lane >> 5, r16 = opaque(lane & 15);
+  const int64_t row = t.row0 + m;
+  const int lane_col = gated ? 2 * t.col0 + 256 * wn + 4 * h : t.col0 + 128 * wn + 4 * h;
+  const char* zb = zrow + (gated ? 512 : 256) * wn + 8 * h;
+  uint16_t* db = dz + row * lddz + lane_col;
+  float dp = 0.0f;
+  sfor<4>([&](auto ni) {
+    if (wn * kWaveN + ni * 32 < t.cols_valid) {
+      sfor<4>([&](auto rg) {
+        float gz[4];
+        if constexpr (gated) {
+          constexpr int off = 128 * (ni / 2) + 32 * (ni % 2) + 8 * rg;
+          constexpr int k = 16 * (ni / 2) + 4 * (ni % 2) + rg;
+          float uz[4];
+          bf16x4_to_f32(zread(zb, r16, k), gz);
+          bf16x4_to_f32(zread(zb, r16, k + 8), uz);
+          float dg[4], du[4];
+          sfor<4>([&](auto i) {
+            const float da = acc[MI][ni][4 * rg + i];
+            const GluVal v = glu_eval<ACT>(gz[i], uz[i], act);
+            const float ds = p * da;
+            dg[i] = v.g_in ? ds * v.u * v.df : 0.0f;
+            du[i] = v.u_in ? ds * v.f : 0.0f;
+            dp += da * v.s;
           });
-        }
-      });
-      sfor<4>([&](auto ni) {
-        if (wn * kWaveN + ni * 32 < t.cols_valid) {
-          sfor<4>([&](auto rg) {
-            const float gz[4] = {__uint_as_float(zg[ni][rg].x << 16),
-                                 __uint_as_float(zg[ni][rg].x & 0xffff0000u),
-                                 __uint_as_float(zg[ni][rg].y << 16),
-                                 __uint_as_float(zg[ni][rg].y & 0xffff0000u)};
-            if constexpr (gated) {
-              constexpr int off = 128 * (ni / 2) + 32 * (ni % 2) + 8 * rg;
-              const float uz[4] = {__uint_as_float(zu[ni][rg].x << 16),
-                                   __uint_as_float(zu[ni][rg].x & 0xffff0000u),
-                                   __uint_as_float(zu[ni][rg].y << 16),
-                                   __uint_as_float(zu[ni][rg].y & 0xffff0000u)};
-              float dg[4], du[4];
-              sfor<4>([&](auto i) {
-                const float da = acc[mi][ni][4 * rg + i];
-                const GluVal v = glu_eval<ACT>(gz[i], uz[i], act);
-                const float ds = p * da;
-                dg[i] = v.g_in ? ds * v.u * v.df : 0.0f;
-                du[i] = v.u_in ? ds * v.f : 0.0f;
-                dp += da * v.s;
-              });
-              store_f32x4_bf16(db + off, dg);
-              store_f32x4_bf16(db + off + MOE_INTERLEAVE, du);
-            } else {
-              constexpr int off = 32 * ni + 8 * rg;
-              float d[4];
-              sfor<4>([&](auto i) {
-                const float da = acc[mi][ni][4 * rg + i];
-                const bool in = (gz[i] >= act.glo) && (gz[i] <= act.ghi);
-                const float rl = fmaxf(fminf(fmaxf(gz[i], act.glo), act.ghi), 0.0f);
-                d[i] = in ? p * da * 2.0f * rl : 0.0f;
-                dp += da * rl * rl;
-              });
-              store_f32x4_bf16(db + off, d);
-            }
+          store_f32x4_bf16(db + off, dg);
+          store_f32x4_bf16(db + off + MOE_INTERLEAVE, du);
+        } else {
+          constexpr int off = 32 * ni + 8 * rg;
+          bf16x4_to_f32(zread(zb, r16, 4 * ni + rg), gz);
+          float d[4];
+          sfor<4>([&](auto i) {
+            const float da = acc[MI][ni][4 * rg + i];
+            const bool in = (gz[i] >= act.glo) && (gz[i] <= act.ghi);
+            const float rl = fmaxf(fminf(fmaxf(gz[i], act.glo), act.ghi), 0.0f);
+            d[i] = in ? p * da * 2.0f * rl : 0.0f;
+            dp += da * rl * rl;
           });
+          store_f32x4_bf16(db + off, d);
         }
       });
     }
-    dp_out[mi] = dp;
-    __builtin_amdgcn_sched_barrier(0);
   });
+  return dp;
 }
 
 // EPI_GLU with MXFP8 copies of a (see epi_glu).  Rows of a 32-row block
@@ -656,100 +691,84 @@ MOE_DEV float epi_glu_mx(const f32x16 (&acc)[4][4], uint16_t* __restrict__ z, in
   return amax;
 }
 
-// EPI_DGLU with MXFP8 copies of dz (see epi_dglu; pad rows as in
-// epi_glu_mx).  With the 64-column interleave a 32-column block of dz holds
-// only gate or only up columns.
-template <int ACT>
-MOE_DEV void epi_dglu_mx(const f32x16 (&acc)[4][4], const uint16_t* __restrict__ zin, int64_t ldz,
-                         uint16_t* __restrict__ dz, int64_t lddz, const float* __restrict__ probs,
-                         const ActP& act, const TileCtx& t, int wn, int wm, int lane,
-                         float (&dp_out)[4], const MxOut& mo, uint16_t* tr) {
+// EPI_DGLU with MXFP8 copies of dz, row block MI (see dglu_rows; pad rows
+// as in epi_glu_mx).  With the 64-column interleave a 32-column block of dz
+// holds only gate or only up columns.
+template <int ACT, int MI>
+MOE_DEV float dglu_rows_mx(const f32x16 (&acc)[4][4], const char* zrow,
+                           uint16_t* __restrict__ dz, int64_t lddz, float p, const ActP& act,
+                           const TileCtx& t, int wn, int wm, int lane, const MxOut& mo,
+                           uint16_t* tr) {
   constexpr bool gated = ACT != MOE_ACT_SRELU;
-  const int h4 = 4 * (lane >> 5);
-  const int lane_col = gated ? 2 * t.col0 + 256 * wn + h4 : t.col0 + 128 * wn + h4;
-  sfor<4>([&](auto mi) {
-    const int m = t.m_lane + mi * 32;
-    const bool row_ok = m < t.rows_valid;
-    const int blk = wm * kWaveM + mi * 32;
-    const bool blk_ok = blk < t.rows_pad;
-    const int64_t row = t.row0 + m;
-    const int64_t rb = (t.row0 + blk) / 32;
-    const float p = row_ok ? probs[row] : 0.0f;
-    float dp = 0.0f;
-    uint2 zg[4][4], zu[4][4];
-    const uint16_t* zb = zin + row * ldz + lane_col;
-    sfor<4>([&](auto ni) { sfor<4>([&](auto rg) {
-      zg[ni][rg] = make_uint2(0, 0);
-      zu[ni][rg] = make_uint2(0, 0);
-      if (row_ok && wn * kWaveN + ni * 32 < t.cols_valid) {
+  const int h = lane >> 5, r16 = opaque(lane & 15);
+  const int lane_col = gated ? 2 * t.col0 + 256 * wn + 4 * h : t.col0 + 128 * wn + 4 * h;
+  const char* zb = zrow + (gated ? 512 : 256) * wn + 8 * h;
+  const int m = t.m_lane + MI * 32;
+  const bool row_ok = m < t.rows_valid;
+  const int blk = wm * kWaveM + MI * 32;
+  const bool blk_ok = blk < t.rows_pad;
+  const int64_t row = t.row0 + m;
+  const int64_t rb = (t.row0 + blk) / 32;
+  float dp = 0.0f;
+  sfor<4>([&](auto ni) {
+    if (wn * kWaveN + ni * 32 < t.cols_valid) {
+      float gv[16], uv[16];
+      sfor<4>([&](auto rg) {
+        float gz[4];
         if constexpr (gated) {
           constexpr int off = 128 * (ni / 2) + 32 * (ni % 2) + 8 * rg;
-          zg[ni][rg] = *reinterpret_cast<const uint2*>(zb + off);
-          zu[ni][rg] = *reinterpret_cast<const uint2*>(zb + off + MOE_INTERLEAVE);
+          constexpr int k = 16 * (ni / 2) + 4 * (ni % 2) + rg;
+          float uz[4];
+          bf16x4_to_f32(zread(zb, r16, k), gz);
+          bf16x4_to_f32(zread(zb, r16, k + 8), uz);
+          float dg[4], du[4];
+          sfor<4>([&](auto i) {
+            const float da = acc[MI][ni][4 * rg + i];
+            const GluVal v = glu_eval<ACT>(gz[i], uz[i], act);
+            const float ds = p * da;
+            dg[i] = v.g_in ? ds * v.u * v.df : 0.0f;
+            du[i] = v.u_in ? ds * v.f : 0.0f;
+            dp += da * v.s;
+          });
+          uint2 wg = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+          uint2 wu = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+          if (!row_ok) wg = wu = make_uint2(0, 0);
+          if (row_ok && dz) {
+            uint16_t* db = dz + row * lddz + lane_col;
+            *reinterpret_cast<uint2*>(db + off) = wg;
+            *reinterpret_cast<uint2*>(db + off + MOE_INTERLEAVE) = wu;
+          }
+          bf16x4_to_f32(wg, &gv[4 * rg]);
+          bf16x4_to_f32(wu, &uv[4 * rg]);
         } else {
           constexpr int off = 32 * ni + 8 * rg;
-          zg[ni][rg] = *reinterpret_cast<const uint2*>(zb + off);
+          bf16x4_to_f32(zread(zb, r16, 4 * ni + rg), gz);
+          float d[4];
+          sfor<4>([&](auto i) {
+            const float da = acc[MI][ni][4 * rg + i];
+            const bool in = (gz[i] >= act.glo) && (gz[i] <= act.ghi);
+            const float rl = fmaxf(fminf(fmaxf(gz[i], act.glo), act.ghi), 0.0f);
+            d[i] = in ? p * da * 2.0f * rl : 0.0f;
+            dp += da * rl * rl;
+          });
+          uint2 w = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+          if (!row_ok) w = make_uint2(0, 0);
+          if (row_ok && dz) *reinterpret_cast<uint2*>(dz + row * lddz + lane_col + off) = w;
+          bf16x4_to_f32(w, &gv[4 * rg]);
+        }
+      });
+      if (blk_ok) {
+        if constexpr (gated) {
+          const int cbg = 2 * t.col0 + 256 * wn + 128 * (ni / 2) + 32 * (ni % 2);
+          mx_block_out(gv, mo, tr, row, rb, cbg, lane);
+          mx_block_out(uv, mo, tr, row, rb, cbg + MOE_INTERLEAVE, lane);
+        } else {
+          mx_block_out(gv, mo, tr, row, rb, t.col0 + 128 * wn + 32 * ni, lane);
         }
       }
-    }); });
-    sfor<4>([&](auto ni) {
-      if (wn * kWaveN + ni * 32 < t.cols_valid) {
-        float gv[16], uv[16];
-        sfor<4>([&](auto rg) {
-          float gz[4], uz[4];
-          bf16x4_to_f32(zg[ni][rg], gz);
-          if constexpr (gated) {
-            constexpr int off = 128 * (ni / 2) + 32 * (ni % 2) + 8 * rg;
-            bf16x4_to_f32(zu[ni][rg], uz);
-            float dg[4], du[4];
-            sfor<4>([&](auto i) {
-              const float da = acc[mi][ni][4 * rg + i];
-              const GluVal v = glu_eval<ACT>(gz[i], uz[i], act);
-              const float ds = p * da;
-              dg[i] = v.g_in ? ds * v.u * v.df : 0.0f;
-              du[i] = v.u_in ? ds * v.f : 0.0f;
-              dp += da * v.s;
-            });
-            uint2 wg = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-            uint2 wu = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-            if (!row_ok) wg = wu = make_uint2(0, 0);
-            if (row_ok && dz) {
-              uint16_t* db = dz + row * lddz + lane_col;
-              *reinterpret_cast<uint2*>(db + off) = wg;
-              *reinterpret_cast<uint2*>(db + off + MOE_INTERLEAVE) = wu;
-            }
-            bf16x4_to_f32(wg, &gv[4 * rg]);
-            bf16x4_to_f32(wu, &uv[4 * rg]);
-          } else {
-            constexpr int off = 32 * ni + 8 * rg;
-            float d[4];
-            sfor<4>([&](auto i) {
-              const float da = acc[mi][ni][4 * rg + i];
-              const bool in = (gz[i] >= act.glo) && (gz[i] <= act.ghi);
-              const float rl = fmaxf(fminf(fmaxf(gz[i], act.glo), act.ghi), 0.0f);
-              d[i] = in ? p * da * 2.0f * rl : 0.0f;
-              dp += da * rl * rl;
-            });
-            uint2 w = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
-            if (!row_ok) w = make_uint2(0, 0);
-            if (row_ok && dz) *reinterpret_cast<uint2*>(dz + row * lddz + lane_col + off) = w;
-            bf16x4_to_f32(w, &gv[4 * rg]);
-          }
-        });
-        if (blk_ok) {
-          if constexpr (gated) {
-            const int cbg = 2 * t.col0 + 256 * wn + 128 * (ni / 2) + 32 * (ni % 2);
-            mx_block_out(gv, mo, tr, row, rb, cbg, lane);
-            mx_block_out(uv, mo, tr, row, rb, cbg + MOE_INTERLEAVE, lane);
-          } else {
-            mx_block_out(gv, mo, tr, row, rb, t.col0 + 128 * wn + 32 * ni, lane);
-          }
-        }
-      }
-    });
-    dp_out[mi] = dp;
-    __builtin_amdgcn_sched_barrier(0);
+    }
   });
+  return dp;
 }
 
 // ------------------------------------------------------- block helpers ---
@@ -936,14 +955,19 @@ void grouped_gemm_kernel(GemmArgs g) {
     else lb_k.template issue<MX>(b_st, kk, wave_s, valid, k_bytes);
     if constexpr (MX) ls.issue(s_st, kk, wave_s, valid, k_steps64);
   };
-  // point the loaders at a tile and start its first two stages
-  auto start_tile = [&](const TileInfo& ti) {
+  // point the loaders at a tile (its first two stages are issued next)
+  const int lane_k = lane, wave_k = wave;
+  auto point_tile = [&](const TileInfo& ti) {
     const int nk_item = ti.kend - ti.kbeg;
     k_rot = nk_item > 0 ? (g.k_rot_stride * (ti.m_t + ti.n_t)) % nk_item : 0;
     k_beg = ti.kbeg;
     k_len = nk_item;
     const int64_t rows_avail = ti.rows_valid > 0 ? g.M_cap - ti.row0 : 0;
     const int64_t arow0 = ti.rows_valid > 0 ? ti.row0 : 0;
+    // the dGLU kernel recomputes the lane offsets per tile (hoisted, they
+    // are spilled and reloaded in its epilogue)
+    const int lane = EPI == EPI_DGLU ? opaque(lane_k) : lane_k;
+    const int wave = EPI == EPI_DGLU ? opaque(wave_k) : wave_k;
     la.init(A + arow0 * g.K * kElem, rows_avail, g.K * kElem, wave, lane);
     const char* Bexp = B + static_cast<int64_t>(ti.e) * g.b_stride * kElem;
     if constexpr (NN) {
@@ -963,6 +987,9 @@ void grouped_gemm_kernel(GemmArgs g) {
                  : g.b_s + static_cast<int64_t>(ti.e) * g.b_s_stride + (ti.col0 / 32) * per_group;
       ls.init(sbase, a_side ? rows_avail / 32 : (g.N - ti.col0) / 32, g.K, wave, lane);
     }
+  };
+  auto start_tile = [&](const TileInfo& ti) {
+    point_tile(ti);
     issue_stage(sA0, sB0, sS0, 0);
     issue_stage(sA1, sB1, sS1, 1);
   };
@@ -1142,9 +1169,12 @@ void grouped_gemm_kernel(GemmArgs g) {
     const TileInfo t0 = cur;
     const bool split = w >= full && S > 1;
     w += G;
-    if (w < items) {
+    const bool more = w < items;
+    if (more) {
       cur = item_info(w);
-      start_tile(cur);
+      // the dGLU epilogue stages z in the stage buffers first and starts
+      // the next tile's loads itself
+      if constexpr (EPI != EPI_DGLU) start_tile(cur);
     }
 
     // ------------------------------------------------------ epilogues ---
@@ -1209,12 +1239,68 @@ void grouped_gemm_kernel(GemmArgs g) {
         if (lane == 0) atomic_max_nonneg(g.amax, amax);
       }
     } else {
+      // z of the tile's rows, 64 rows (row block mi of both wave rows) per
+      // chunk, streams through the two stage buffers: chunks mi + 1 (and
+      // from mi = 0 to 1 also mi + 2) load while block mi is computed; the
+      // buffers then take the next tile's first two stages during the last
+      // two blocks.
+      constexpr bool kGated = ACT != MOE_ACT_SRELU;
+      constexpr int kZRow = kGated ? 1024 : 512;
+      using ZL = ZLoader<kZRow>;
+      // the row probabilities first: a load issued after the chunks would
+      // wait for them (vector memory operations complete in order)
+      float pr[4];
+      sfor<4>([&](auto mi) {
+        const int m = t.m_lane + mi * 32;
+        pr[mi] = m < t.rows_valid ? g.probs[t.row0 + m] : 0.0f;
+      });
+      ZL zl;
+      zl.init(g.zin, g.ldz, t.row0, t.rows_valid, kGated ? 2 * t.col0 : t.col0);
+      zl.issue(sA0, sB0, 0, wave_s, lane);
+      zl.issue(sA1, sB1, 1, wave_s, lane);
+      // lane-derived values are re-derived here rather than kept live (and
+      // spilled) across the K loop
+      const int lane_e = opaque(lane), wave_e = opaque(wave);
+      const int wm_e = wave_e >> 1, wn_e = wave_e & 1;
+      TileCtx te = t;
+      te.m_lane = wm_e * kWaveM + (lane_e & 31);
+      te.n_lane = wn_e * kWaveN + 4 * (lane_e >> 5);
       float dp[4];
-      if constexpr (MX)
-        epi_dglu_mx<ACT>(acc, g.zin, g.ldz, g.C, g.ldc, g.probs, g.act, t, wn, wm, lane, dp, mo,
-                         s_tr + wave * kTrTile);
-      else
-        epi_dglu<ACT>(acc, g.zin, g.ldz, g.C, g.ldc, g.probs, g.act, t, wn, lane, dp);
+      sfor<4>([&](auto mi) {
+        constexpr int MI = decltype(mi)::value;
+        uint16_t* za = MI % 2 ? sA1 : sA0;
+        uint16_t* zb = MI % 2 ? sB1 : sB0;
+        // chunk MI has landed once at most the loads issued after it are
+        // outstanding: chunk MI + 1 (MI < 3), or stage 0 of the next tile
+        if constexpr (MI < 3) {
+          __builtin_amdgcn_s_waitcnt(wait_vmcnt(ZL::kInstr));
+        } else {
+          if (more) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLoads));
+          else __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+        }
+        bare_barrier();
+        const char* zrow =
+            reinterpret_cast<const char*>(wm_e ? zb : za) + (lane_e & 31) * kZRow;
+        if constexpr (MX)
+          dp[MI] = dglu_rows_mx<ACT, MI>(acc, zrow, g.C, g.ldc, pr[MI], g.act, te, wn_e, wm_e,
+                                         lane_e, mo, s_tr + wave_e * kTrTile);
+        else
+          dp[MI] = dglu_rows<ACT, MI>(acc, zrow, g.C, g.ldc, pr[MI], g.act, te, wn_e, lane_e);
+        __builtin_amdgcn_sched_barrier(0);
+        // every wave is done reading the chunk before its buffer is reused
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        bare_barrier();
+        if constexpr (MI < 2) {
+          zl.issue(za, zb, MI + 2, wave_s, lane);
+        } else if constexpr (MI == 2) {
+          if (more) {
+            point_tile(cur);
+            issue_stage(sA0, sB0, sS0, 0);
+          }
+        } else {
+          if (more) issue_stage(sA1, sB1, sS1, 1);
+        }
+      });
       sfor<4>([&](auto mi) {
         // lanes l and l ^ 32 hold the same row: fixed-order pair sum
         const float v = dp[mi] + __shfl_xor(dp[mi], 32, kWave);
