@@ -387,7 +387,10 @@ struct MxOut {
 // values being bf16 numbers (zero for rows that hold no data).
 //
 // Rowwise: the row's 32 values are this lane's and its partner's (lane ^ 32);
-// codes go to q_row[0 .. 31], the scale to *s_byte.
+// codes go to q_row[0 .. 31], the scale to *s_byte.  The lane's four code
+// words (columns 8 rg + 4 hf ..) are exchanged with the partner's
+// (v_permlane32_swap) so that each lane stores 16 contiguous codes: the
+// low lane columns 0 .. 15, the high lane 16 .. 31.
 MOE_DEV void mx_row_block(const float (&v)[16], uint8_t* q_row, uint8_t* s_byte, int hf) {
   float am = 0.0f;
 #pragma unroll
@@ -395,17 +398,26 @@ MOE_DEV void mx_row_block(const float (&v)[16], uint8_t* q_row, uint8_t* s_byte,
   am = fmaxf(am, __shfl_xor(am, 32, kWave));
   const int e = mx_exponent(am);
   const float inv = mx_inv_scale(e);
+  uint32_t w[4];
 #pragma unroll
   for (int rg = 0; rg < 4; ++rg)
-    *reinterpret_cast<uint32_t*>(q_row + 8 * rg + 4 * hf) =
-        mx_codes4(v[4 * rg], v[4 * rg + 1], v[4 * rg + 2], v[4 * rg + 3], inv);
+    w[rg] = mx_codes4(v[4 * rg], v[4 * rg + 1], v[4 * rg + 2], v[4 * rg + 3], inv);
+  // swap(a, b): the high half of a takes the low half of b and the low half
+  // of b the high half of a.  Low lanes end with (own w0, partner w0, own
+  // w1, partner w1), high lanes with (partner w2, own w2, partner w3, own w3)
+  const auto s0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+  *reinterpret_cast<uint4*>(q_row + 16 * hf) = make_uint4(s0[0], s0[1], s1[0], s1[1]);
   if (hf == 0) *s_byte = mx_scale_code(e);
 }
 
 // Transposed: column c of the block is one MX block of the transposed copy
 // (rows 32 rb .. 32 rb + 31).  The wave stages its 32 x 32 bf16 block in a
-// private LDS tile (row pitch kTrPitch), then lane l reads rows
-// 16 (l / 32) .. +15 of column l % 32, so a column's block maximum is one
+// private LDS tile (row pitch kTrPitch), then lane l gathers rows
+// 16 (l / 32) .. +15 of column l % 32 with four LDS transpose loads
+// (ds_read_b64_tr_b16: the 16 lanes of a group fetch a 4-row x 16-column
+// piece, lane s taking row s / 4, columns 4 (s % 4) ..; lane i of the group
+// receives column i of it, rows 0 .. 3), so a column's block maximum is one
 // partner exchange (lane ^ 32) and its 16 codes are one 16-byte store.  LDS
 // operations of one wave complete in order, so no barrier is needed and the
 // tile is reused block after block.
@@ -424,10 +436,19 @@ MOE_DEV void mx_col_block(const float (&v)[16], uint16_t* tr, const MxOut& o, in
   }
   float c[16];
   float am = 0.0f;
+  {
+    const int g = lane >> 4, s = lane & 15;
+    const uint16_t* src = tr + (16 * (g >> 1) + (s >> 2)) * kTrPitch + 16 * (g & 1) + 4 * (s & 3);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    c[i] = __uint_as_float(static_cast<uint32_t>(tr[(16 * hf + i) * kTrPitch + row]) << 16);
-    am = fmaxf(am, fabsf(c[i]));
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_t*)(src + 4 * t4 * kTrPitch));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[4 * t4 + j] = __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(x[j])) << 16);
+        am = fmaxf(am, fabsf(c[4 * t4 + j]));
+      }
+    }
   }
   am = fmaxf(am, __shfl_xor(am, 32, kWave));
   const int e = mx_exponent(am);
@@ -1229,10 +1250,16 @@ void grouped_gemm_kernel(GemmArgs g) {
       }
     } else if constexpr (EPI == EPI_GLU) {
       float amax;
-      if constexpr (MX)
-        amax = epi_glu_mx<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, g.probs, g.act, t, wn, wm,
-                               lane, mo, s_tr + wave * kTrTile);
-      else
+      if constexpr (MX) {
+        // lane values re-derived here, not kept live (and spilled) across
+        // the K loop: a spill reload would wait on the next tile's loads
+        const int lane_e = opaque(lane), wave_e = opaque(wave);
+        TileCtx te = t;
+        te.m_lane = (wave_e >> 1) * kWaveM + (lane_e & 31);
+        te.n_lane = (wave_e & 1) * kWaveN + 4 * (lane_e >> 5);
+        amax = epi_glu_mx<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, g.probs, g.act, te,
+                               wave_e & 1, wave_e >> 1, lane_e, mo, s_tr + wave_e * kTrTile);
+      } else
         amax = epi_glu<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, g.probs, g.act, t, wn, lane);
       if (g.amax) {
         amax = wave_max(amax);
