@@ -371,6 +371,17 @@ MOE_DEV void load_bf16x4(const uint16_t* p, float* v) {
   v[3] = __uint_as_float(w.y & 0xffff0000u);
 }
 
+// Value of lane l ^ 32 (hf = l / 32) by v_permlane32_swap, a VALU
+// exchange between the wave halves (no LDS round trip as with a shuffle).
+// swap(a, b) gives the high half of a the low half of b and the low half of
+// b the high half of a; with a = b = v a high lane finds its partner's value
+// in the new a, a low lane in the new b.
+MOE_DEV float partner32(float v, int hf) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(hf ? r[0] : r[1]);
+}
+
 // ------------------------------------------------ MXFP8 epilogue helpers ---
 // The MXFP8 copies an epilogue writes of its [M_cap][n] bf16 output.
 struct MxOut {
@@ -395,7 +406,7 @@ MOE_DEV void mx_row_block(const float (&v)[16], uint8_t* q_row, uint8_t* s_byte,
   float am = 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(v[r]));
-  am = fmaxf(am, __shfl_xor(am, 32, kWave));
+  am = fmaxf(am, partner32(am, hf));
   const int e = mx_exponent(am);
   const float inv = mx_inv_scale(e);
   uint32_t w[4];
@@ -450,7 +461,7 @@ MOE_DEV void mx_col_block(const float (&v)[16], uint16_t* tr, const MxOut& o, in
       }
     }
   }
-  am = fmaxf(am, __shfl_xor(am, 32, kWave));
+  am = fmaxf(am, partner32(am, hf));
   const int e = mx_exponent(am);
   const float inv = mx_inv_scale(e);
   uint4 q;
@@ -1330,7 +1341,7 @@ void grouped_gemm_kernel(GemmArgs g) {
       });
       sfor<4>([&](auto mi) {
         // lanes l and l ^ 32 hold the same row: fixed-order pair sum
-        const float v = dp[mi] + __shfl_xor(dp[mi], 32, kWave);
+        const float v = dp[mi] + partner32(dp[mi], lane_e >> 5);
         if (lane < 32) s_red[wn * BM + t.m_lane + mi * 32] = v;
       });
       // LDS-only handoff: no fence, so the next tile's loads keep flying
