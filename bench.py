@@ -76,13 +76,17 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-GEMM_SRC = os.path.join(ROOT, "moe_grouped_mlp_amd", "csrc", "gemm.hip")
+GEMM_SRCS = [os.path.join(ROOT, "moe_grouped_mlp_amd", "csrc", f)
+             for f in ("gemm_kernel.h", "common.h", "mx.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fc1_mixtral_traffic.json")
 
 
 def gemm_source_hash():
-    with open(GEMM_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for src in GEMM_SRCS:
+        with open(src, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():

@@ -21,17 +21,31 @@ MOE_DEV float bf16_to_f32(bf16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even on the bit pattern (NaN kept quiet).
-MOE_DEV bf16_t f32_to_bf16(float f) {
+// fp32 -> bf16, round to nearest even done on the bit pattern with integer
+// VALU operations (NaN kept quiet).  Same results as pack_bf16x2 for every
+// finite value; the plain-store epilogue uses it because with it the register
+// allocator keeps the MXFP8 K loop free of spill reloads.
+MOE_DEV bf16_t f32_to_bf16_sw(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40);
   u += 0x7fffu + ((u >> 16) & 1u);
   return static_cast<bf16_t>(u >> 16);
 }
 
+MOE_DEV uint32_t pack_bf16x2_sw(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_sw(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16_sw(hi)) << 16);
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (lo in bits 0..15), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.  The kernels run with fp32 denormals enabled,
+// so denormal inputs round like any other value; NaN stays NaN.
 MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) |
-         (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // ---------------------------------------------------------------- waves --
