@@ -528,6 +528,13 @@ struct TileCtx {
   int n_lane;       // first column of this lane inside the tile, block 0
 };
 
+// Keeps a block of accumulators in AGPRs up to this point of the epilogue.
+// Without it the register allocator copies all 256 accumulators to VGPRs as
+// soon as the K loop ends and spills part of them to scratch; a spill reload
+// is a vector memory load, so waiting for it also waits for every store the
+// epilogue has issued before it.
+MOE_DEV void acc_hold(f32x16& v) { asm volatile("" : "+a"(v)); }
+
 // EPI_STORE: C = bf16(acc)
 MOE_DEV void epi_store(const f32x16 (&acc)[4][4], uint16_t* __restrict__ C, int64_t ldc,
                        const TileCtx& t) {
@@ -551,22 +558,34 @@ MOE_DEV void epi_store(const f32x16 (&acc)[4][4], uint16_t* __restrict__ C, int6
   });
 }
 
-// EPI_GLU: z = bf16(acc) (may be null), a = bf16(p * act(gate, up)); returns
+// The routing probabilities of the lane's four rows (0 for rows past the
+// group's data), loaded before the epilogue's first store: vector memory
+// operations complete in order, so waiting for a load issued after stores
+// would also wait for those stores.
+MOE_DEV void row_probs(const float* __restrict__ probs, const TileCtx& t, float (&pr)[4]) {
+  sfor<4>([&](auto mi) {
+    const int m = t.m_lane + mi * 32;
+    pr[mi] = m < t.rows_valid ? probs[t.row0 + m] : 0.0f;
+  });
+}
+
+// EPI_GLU: z = bf16(acc) (may be null), a = bf16(p * act(gate, up)) with pr
+// the probabilities of the lane's four rows (0 past the data); returns
 // max |a| over this lane's outputs.  Gated: this wave's 128 packed columns
 // [col0 + 128 wn, +128) are gate block q (blocks ni = 0, 1) then up block q
 // (ni = 2, 3), so both halves of an output are in the same lane.
 template <int ACT>
-MOE_DEV float epi_glu(const f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz,
-                      uint16_t* __restrict__ a, int64_t lda,
-                      const float* __restrict__ probs, const ActP& act, const TileCtx& t,
-                      int wn, int lane) {
+MOE_DEV float epi_glu(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz,
+                      uint16_t* __restrict__ a, int64_t lda, const float (&pr)[4],
+                      const ActP& act, const TileCtx& t, int wn, int lane) {
   float amax = 0.0f;
   if constexpr (ACT == MOE_ACT_SRELU) {
     sfor<4>([&](auto mi) {
+      sfor<4>([&](auto ni) { acc_hold(acc[mi][ni]); });
       const int m = t.m_lane + mi * 32;
       if (m < t.rows_valid) {
         const int64_t row = t.row0 + m;
-        const float p = probs[row];
+        const float p = pr[mi];
         sfor<4>([&](auto ni) { sfor<4>([&](auto rg) {
           const int n = t.n_lane + ni * 32 + 8 * rg;
           if (n < t.cols_valid) {
@@ -586,10 +605,11 @@ MOE_DEV float epi_glu(const f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64
   } else if (wn * kWaveN < t.cols_valid) {
     const int q = (t.col0 + wn * kWaveN) / (2 * MOE_INTERLEAVE);
     sfor<4>([&](auto mi) {
+      sfor<4>([&](auto ni) { acc_hold(acc[mi][ni]); });
       const int m = t.m_lane + mi * 32;
       if (m < t.rows_valid) {
         const int64_t row = t.row0 + m;
-        const float p = probs[row];
+        const float p = pr[mi];
         sfor<2>([&](auto h) { sfor<4>([&](auto rg) {
           const int c = h * 32 + 8 * rg + 4 * (lane >> 5);  // 0..63 in the block
           if (z) {
@@ -624,10 +644,11 @@ MOE_DEV float epi_glu(const f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64
 // half h.  Whether a 32-column block lies inside N is uniform across the
 // wave.
 template <int ACT, int MI>
-MOE_DEV float dglu_rows(const f32x16 (&acc)[4][4], const char* zrow, uint16_t* __restrict__ dz,
+MOE_DEV float dglu_rows(f32x16 (&acc)[4][4], const char* zrow, uint16_t* __restrict__ dz,
                         int64_t lddz, float p, const ActP& act, const TileCtx& t, int wn,
                         int lane) {
   constexpr bool gated = ACT != MOE_ACT_SRELU;
+  sfor<4>([&](auto ni) { acc_hold(acc[MI][ni]); });
   const int m = t.m_lane + MI * 32;
   if (m >= t.rows_valid) return 0.0f;
   const int h = lane >> 5, r16 = opaque(lane & 15);
@@ -680,21 +701,22 @@ MOE_DEV float dglu_rows(const f32x16 (&acc)[4][4], const char* zrow, uint16_t* _
 // past the group's data but before its padded end get zero codes; a block
 // past the padded end is not touched (it belongs to the next group).
 template <int ACT>
-MOE_DEV float epi_glu_mx(const f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz,
-                         uint16_t* __restrict__ a, int64_t lda, const float* __restrict__ probs,
+MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz,
+                         uint16_t* __restrict__ a, int64_t lda, const float (&pr)[4],
                          const ActP& act, const TileCtx& t, int wn, int wm, int lane,
                          const MxOut& mo, uint16_t* tr) {
   constexpr bool gated = ACT != MOE_ACT_SRELU;
   const int hf = lane >> 5;
   float amax = 0.0f;
   sfor<4>([&](auto mi) {
+    sfor<4>([&](auto ni) { acc_hold(acc[mi][ni]); });
     const int m = t.m_lane + mi * 32;
     const bool row_ok = m < t.rows_valid;
     const int blk = wm * kWaveM + mi * 32;
     const bool blk_ok = blk < t.rows_pad;
     const int64_t row = t.row0 + m;
     const int64_t rb = (t.row0 + blk) / 32;
-    const float p = row_ok ? probs[row] : 0.0f;
+    const float p = pr[mi];
     if constexpr (gated) {
       if (wn * kWaveN < t.cols_valid) {
         const int q = (t.col0 + wn * kWaveN) / (2 * MOE_INTERLEAVE);
@@ -756,11 +778,12 @@ MOE_DEV float epi_glu_mx(const f32x16 (&acc)[4][4], uint16_t* __restrict__ z, in
 // as in epi_glu_mx).  With the 64-column interleave a 32-column block of dz
 // holds only gate or only up columns.
 template <int ACT, int MI>
-MOE_DEV float dglu_rows_mx(const f32x16 (&acc)[4][4], const char* zrow,
+MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
                            uint16_t* __restrict__ dz, int64_t lddz, float p, const ActP& act,
                            const TileCtx& t, int wn, int wm, int lane, const MxOut& mo,
                            uint16_t* tr) {
   constexpr bool gated = ACT != MOE_ACT_SRELU;
+  sfor<4>([&](auto ni) { acc_hold(acc[MI][ni]); });
   const int h = lane >> 5, r16 = opaque(lane & 15);
   const int lane_col = gated ? 2 * t.col0 + 256 * wn + 4 * h : t.col0 + 128 * wn + 4 * h;
   const char* zb = zrow + (gated ? 512 : 256) * wn + 8 * h;
@@ -1208,13 +1231,30 @@ void grouped_gemm_kernel(GemmArgs g) {
     return ti;
   };
 
+  // GLU: a tile's row probabilities are loaded just before its first stages,
+  // so the wait for stage 0 covers them and the epilogue, which runs with
+  // its stores in flight, never waits on a load
+  float pr_next[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto load_probs = [&](const TileInfo& ti) {
+    if constexpr (EPI == EPI_GLU) {
+      const int ml = wm * kWaveM + (lane & 31);
+      sfor<4>([&](auto mi) {
+        const int m = ml + mi * 32;
+        pr_next[mi] = m < ti.rows_valid ? g.probs[ti.row0 + m] : 0.0f;
+      });
+    }
+  };
+
   int w = vid;
   TileInfo cur{};
   if (w < items) {
     cur = item_info(w);
+    load_probs(cur);
     start_tile(cur);
   }
   while (w < items) {
+    float pr_tile[4];
+    sfor<4>([&](auto mi) { pr_tile[mi] = pr_next[mi]; });
     sfor<4>([&](auto mi) { sfor<4>([&](auto ni) { acc[mi][ni] = f32x16{}; }); });
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLoads));   // stage 0 landed
     bare_barrier();
@@ -1235,7 +1275,10 @@ void grouped_gemm_kernel(GemmArgs g) {
       cur = item_info(w);
       // the dGLU epilogue stages z in the stage buffers first and starts
       // the next tile's loads itself
-      if constexpr (EPI != EPI_DGLU) start_tile(cur);
+      if constexpr (EPI != EPI_DGLU) {
+        load_probs(cur);
+        start_tile(cur);
+      }
     }
 
     // ------------------------------------------------------ epilogues ---
@@ -1297,10 +1340,10 @@ void grouped_gemm_kernel(GemmArgs g) {
         TileCtx te = t;
         te.m_lane = (wave_e >> 1) * kWaveM + (lane_e & 31);
         te.n_lane = (wave_e & 1) * kWaveN + 4 * (lane_e >> 5);
-        amax = epi_glu_mx<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, g.probs, g.act, te,
+        amax = epi_glu_mx<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, pr_tile, g.act, te,
                                wave_e & 1, wave_e >> 1, lane_e, mo, s_tr + wave_e * kTrTile);
       } else
-        amax = epi_glu<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, g.probs, g.act, t, wn, lane);
+        amax = epi_glu<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, pr_tile, g.act, t, wn, lane);
       if (g.amax) {
         amax = wave_max(amax);
         if (lane == 0) atomic_max_nonneg(g.amax, amax);
@@ -1317,10 +1360,7 @@ void grouped_gemm_kernel(GemmArgs g) {
       // the row probabilities first: a load issued after the chunks would
       // wait for them (vector memory operations complete in order)
       float pr[4];
-      sfor<4>([&](auto mi) {
-        const int m = t.m_lane + mi * 32;
-        pr[mi] = m < t.rows_valid ? g.probs[t.row0 + m] : 0.0f;
-      });
+      row_probs(g.probs, t, pr);
       ZL zl;
       zl.init(g.zin, g.ldz, t.row0, t.rows_valid, kGated ? 2 * t.col0 : t.col0);
       zl.issue(sA0, sB0, 0, wave_s, lane);
