@@ -421,11 +421,12 @@ struct MxOut {
 // values being bf16 numbers (zero for rows that hold no data).
 //
 // Rowwise: the row's 32 values are this lane's and its partner's (lane ^ 32);
-// codes go to q_row[0 .. 31], the scale to *s_byte.  The lane's four code
+// codes go to the block's 32 bytes of the row (q_lane: its half 16 hf ..),
+// the scale to *s_byte.  The lane's four code
 // words (columns 8 rg + 4 hf ..) are exchanged with the partner's
 // (v_permlane32_swap) so that each lane stores 16 contiguous codes: the
 // low lane columns 0 .. 15, the high lane 16 .. 31.
-MOE_DEV void mx_row_block(const float (&v)[16], uint8_t* q_row, uint8_t* s_byte, int hf) {
+MOE_DEV void mx_row_block(const float (&v)[16], uint8_t* q_lane, uint8_t* s_byte, int hf) {
   float am = 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(v[r]));
@@ -441,7 +442,7 @@ MOE_DEV void mx_row_block(const float (&v)[16], uint8_t* q_row, uint8_t* s_byte,
   // w1, partner w1), high lanes with (partner w2, own w2, partner w3, own w3)
   const auto s0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
   const auto s1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
-  *reinterpret_cast<uint4*>(q_row + 16 * hf) = make_uint4(s0[0], s0[1], s1[0], s1[1]);
+  *reinterpret_cast<uint4*>(q_lane) = make_uint4(s0[0], s0[1], s1[0], s1[1]);
   if (hf == 0) *s_byte = mx_scale_code(e);
 }
 
@@ -458,8 +459,10 @@ MOE_DEV void mx_row_block(const float (&v)[16], uint8_t* q_row, uint8_t* s_byte,
 constexpr int kTrPitch = 36;   // bf16 per staged row (8-byte aligned rows)
 constexpr int kTrTile = 32 * kTrPitch;
 
-MOE_DEV void mx_col_block(const float (&v)[16], uint16_t* tr, const MxOut& o, int64_t rb,
-                          int col0, int lane) {
+// q_lane: the lane's 16 codes of its column (rows 32 rb + 16 hf ..), s_byte:
+// the column's scale.
+MOE_DEV void mx_col_block(const float (&v)[16], uint16_t* tr, uint8_t* q_lane, uint8_t* s_byte,
+                          int lane) {
   const int row = lane & 31, hf = lane >> 5;
 #pragma unroll
   for (int rg = 0; rg < 4; ++rg) {   // the values are bf16 numbers: keep their high halves
@@ -492,17 +495,41 @@ MOE_DEV void mx_col_block(const float (&v)[16], uint16_t* tr, const MxOut& o, in
   q.y = mx_codes4(c[4], c[5], c[6], c[7], inv);
   q.z = mx_codes4(c[8], c[9], c[10], c[11], inv);
   q.w = mx_codes4(c[12], c[13], c[14], c[15], inv);
-  const int col = col0 + row;
-  *reinterpret_cast<uint4*>(o.qT + static_cast<int64_t>(col) * o.M_cap + rb * 32 + 16 * hf) = q;
-  if (hf == 0) o.sT[mx_scale_off(col, rb, o.M_cap)] = mx_scale_code(e);
+  *reinterpret_cast<uint4*>(q_lane) = q;
+  if (hf == 0) *s_byte = mx_scale_code(e);
 }
 
-// Both MXFP8 copies of one block whose rows all lie before the group's
-// padded end.
-MOE_DEV void mx_block_out(const float (&v)[16], const MxOut& o, uint16_t* tr, int64_t row,
-                          int64_t rb, int col0, int lane) {
-  mx_row_block(v, o.q + row * o.n + col0, o.s + mx_scale_off(row, col0 / 32, o.n), lane >> 5);
-  if (o.qT) mx_col_block(v, tr, o, rb, col0, lane);
+// The lane's store addresses of its row block (32 rows starting at row
+// block rb, the lane's row `row`) for the block at column 0; the block at a
+// column col0 (a multiple of 32) adds wave-uniform offsets only (mx_block_out),
+// so no per-lane 64-bit address arithmetic is repeated block by block.
+struct MxBase {
+  uint8_t* q;    // rowwise codes: o.q + row * n + 16 hf
+  uint8_t* s;    // rowwise scale of (row, K block 0)
+  uint8_t* qT;   // transposed codes of column lane % 32, rows 32 rb + 16 hf ..
+  uint8_t* sT;   // transposed scale of (column lane % 32, row block rb)
+};
+
+MOE_DEV MxBase mx_base(const MxOut& o, int64_t row, int64_t rb, int lane) {
+  const int hf = lane >> 5, c = lane & 31;
+  MxBase b;
+  b.q = o.q + row * o.n + 16 * hf;
+  b.s = o.s + mx_scale_off(row, 0, o.n);
+  b.qT = o.qT + static_cast<int64_t>(c) * o.M_cap + rb * 32 + 16 * hf;
+  b.sT = o.sT + mx_scale_off(c, rb, o.M_cap);
+  return b;
+}
+
+// Both MXFP8 copies of the block at columns col0 .. col0 + 31 (col0 % 32 == 0)
+// of a row block whose rows all lie before the group's padded end.  With
+// col0 a multiple of 32, the tiled scale offsets of (row, col0 / 32) and
+// (col0 + lane % 32, rb) are those of block 0 plus terms in col0 alone.
+MOE_DEV void mx_block_out(const float (&v)[16], const MxOut& o, const MxBase& b, uint16_t* tr,
+                          int col0, int lane) {
+  mx_row_block(v, b.q + col0, b.s + (col0 >> 6) * 64 + ((col0 >> 5) & 1) * 32, lane >> 5);
+  if (o.qT)
+    mx_col_block(v, tr, b.qT + static_cast<int64_t>(col0) * o.M_cap,
+                 b.sT + static_cast<int64_t>(col0 >> 5) * (o.M_cap >> 6) * 64, lane);
 }
 
 MOE_DEV void bf16x4_to_f32(uint2 w, float* v) {
@@ -717,6 +744,7 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
     const int64_t row = t.row0 + m;
     const int64_t rb = (t.row0 + blk) / 32;
     const float p = pr[mi];
+    const MxBase mb = mx_base(mo, row, rb, lane);
     if constexpr (gated) {
       if (wn * kWaveN < t.cols_valid) {
         const int q = (t.col0 + wn * kWaveN) / (2 * MOE_INTERLEAVE);
@@ -741,7 +769,7 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
           });
 #pragma unroll
           for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ab[r]));
-          if (blk_ok) mx_block_out(ab, mo, tr, row, rb, q * MOE_INTERLEAVE + h * 32, lane);
+          if (blk_ok) mx_block_out(ab, mo, mb, tr, q * MOE_INTERLEAVE + h * 32, lane);
         });
       }
     } else {
@@ -765,7 +793,7 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
           });
 #pragma unroll
           for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ab[r]));
-          if (blk_ok) mx_block_out(ab, mo, tr, row, rb, cb, lane);
+          if (blk_ok) mx_block_out(ab, mo, mb, tr, cb, lane);
         }
       });
     }
@@ -793,6 +821,7 @@ MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
   const bool blk_ok = blk < t.rows_pad;
   const int64_t row = t.row0 + m;
   const int64_t rb = (t.row0 + blk) / 32;
+  const MxBase mb = mx_base(mo, row, rb, lane);
   float dp = 0.0f;
   sfor<4>([&](auto ni) {
     if (wn * kWaveN + ni * 32 < t.cols_valid) {
@@ -844,10 +873,10 @@ MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
       if (blk_ok) {
         if constexpr (gated) {
           const int cbg = 2 * t.col0 + 256 * wn + 128 * (ni / 2) + 32 * (ni % 2);
-          mx_block_out(gv, mo, tr, row, rb, cbg, lane);
-          mx_block_out(uv, mo, tr, row, rb, cbg + MOE_INTERLEAVE, lane);
+          mx_block_out(gv, mo, mb, tr, cbg, lane);
+          mx_block_out(uv, mo, mb, tr, cbg + MOE_INTERLEAVE, lane);
         } else {
-          mx_block_out(gv, mo, tr, row, rb, t.col0 + 128 * wn + 32 * ni, lane);
+          mx_block_out(gv, mo, mb, tr, t.col0 + 128 * wn + 32 * ni, lane);
         }
       }
     }
