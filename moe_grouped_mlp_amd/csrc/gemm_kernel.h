@@ -1388,12 +1388,6 @@ void grouped_gemm_kernel(GemmArgs g) {
       using ZL = ZLoader<kZRow>;
       // the row probabilities first: a load issued after the chunks would
       // wait for them (vector memory operations complete in order)
-      float pr[4];
-      row_probs(g.probs, t, pr);
-      ZL zl;
-      zl.init(g.zin, g.ldz, t.row0, t.rows_valid, kGated ? 2 * t.col0 : t.col0);
-      zl.issue(sA0, sB0, 0, wave_s, lane);
-      zl.issue(sA1, sB1, 1, wave_s, lane);
       // lane-derived values are re-derived here rather than kept live (and
       // spilled) across the K loop
       const int lane_e = opaque(lane), wave_e = opaque(wave);
@@ -1401,6 +1395,12 @@ void grouped_gemm_kernel(GemmArgs g) {
       TileCtx te = t;
       te.m_lane = wm_e * kWaveM + (lane_e & 31);
       te.n_lane = wn_e * kWaveN + 4 * (lane_e >> 5);
+      float pr[4];
+      row_probs(g.probs, te, pr);
+      ZL zl;
+      zl.init(g.zin, g.ldz, t.row0, t.rows_valid, kGated ? 2 * t.col0 : t.col0);
+      zl.issue(sA0, sB0, 0, wave_s, lane_e);
+      zl.issue(sA1, sB1, 1, wave_s, lane_e);
       float dp[4];
       sfor<4>([&](auto mi) {
         constexpr int MI = decltype(mi)::value;
@@ -1408,10 +1408,11 @@ void grouped_gemm_kernel(GemmArgs g) {
         uint16_t* zb = MI % 2 ? sB1 : sB0;
         // chunk MI has landed once at most the loads issued after it are
         // outstanding: chunk MI + 1 (MI < 3), or stage 0 of the next tile
+        // (bf16; with MXFP8 nothing is issued after chunk 3 but stores)
         if constexpr (MI < 3) {
           __builtin_amdgcn_s_waitcnt(wait_vmcnt(ZL::kInstr));
         } else {
-          if (more) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLoads));
+          if (!MX && more) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLoads));
           else __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
         }
         bare_barrier();
@@ -1427,26 +1428,36 @@ void grouped_gemm_kernel(GemmArgs g) {
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         bare_barrier();
         if constexpr (MI < 2) {
-          zl.issue(za, zb, MI + 2, wave_s, lane);
+          zl.issue(za, zb, MI + 2, wave_s, lane_e);
         } else if constexpr (MI == 2) {
-          if (more) {
-            point_tile(cur);
-            issue_stage(sA0, sB0, sS0, 0);
+          // MXFP8: stage 0 waits for the last block, whose LDS transpose
+          // reads the compiler would otherwise order behind these loads
+          if constexpr (!MX) {
+            if (more) {
+              point_tile(cur);
+              issue_stage(sA0, sB0, sS0, 0);
+            }
           }
         } else {
-          if (more) issue_stage(sA1, sB1, sS1, 1);
+          if (more) {
+            if constexpr (MX) {
+              point_tile(cur);
+              issue_stage(sA0, sB0, sS0, 0);
+            }
+            issue_stage(sA1, sB1, sS1, 1);
+          }
         }
       });
       sfor<4>([&](auto mi) {
         // lanes l and l ^ 32 hold the same row: fixed-order pair sum
         const float v = dp[mi] + partner32(dp[mi], lane_e >> 5);
-        if (lane < 32) s_red[wn * BM + t.m_lane + mi * 32] = v;
+        if (lane_e < 32) s_red[wn_e * BM + te.m_lane + mi * 32] = v;
       });
       // LDS-only handoff: no fence, so the next tile's loads keep flying
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       bare_barrier();
       {
-        const int m = tid;  // BM == kThreads
+        const int m = lane_e + 64 * wave_e;  // the thread's id; BM == kThreads
         if (m < t.rows_valid)
           g.dp_part[(t.row0 + m) * g.n_part + t.n_t] = s_red[m] + s_red[BM + m];
       }
