@@ -152,10 +152,13 @@ MOE_DEV GluVal glu_eval(float g_pre, float u_pre, const ActP& p) {
     r.s = r.f * r.u;
     return r;
   }
+  // a finite input lies inside [lo, hi] (bounds included) exactly when
+  // clamping leaves it unchanged: one compare instead of two and an and
   float g = fminf(fmaxf(g_pre, p.glo), p.ghi);
-  r.u = fminf(fmaxf(u_pre, p.llo), p.lhi) + p.loff;
-  r.g_in = (g_pre >= p.glo) && (g_pre <= p.ghi);
-  r.u_in = (u_pre >= p.llo) && (u_pre <= p.lhi);
+  const float uc = fminf(fmaxf(u_pre, p.llo), p.lhi);
+  r.u = uc + p.loff;
+  r.g_in = g == g_pre;
+  r.u_in = uc == u_pre;
   if constexpr (ACT == MOE_ACT_GEGLU) {
     const float kInvSqrt2 = 0.70710678118654752f;
     const float kInvSqrt2Pi = 0.39894228040143268f;
