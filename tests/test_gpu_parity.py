@@ -160,6 +160,29 @@ def test_layer_forward_backward_parity(case):
     assert int(blk.err_flag.cpu()[0]) == 0
 
 
+def test_layer_one_sided_clamp_and_linear_offset():
+    """The other reading of the clamping option, at this scale's magnitudes:
+    the gate half clamped from above only (at 0.15) and the linear half
+    clamped to [-0.25, 0.25] with +1 added after the clamp (Swish slope
+    1.702).  A linear offset takes the general SwiGLU kernel, not the
+    unclamped one."""
+    wl = make_workload("gptoss", seed=21, T=512, H=128, I=192, E=16)
+    M_cap = wl.m_cap()
+    kw = dict(gate_lo=-np.inf, gate_hi=0.15, lin_lo=-0.25, lin_hi=0.25, lin_offset=1.0)
+    gp = mg.act_params(mg.ACT_SWIGLU, beta=wl.beta, **kw)
+    op = om.ActParams(act="swiglu", beta=wl.beta, **kw)
+    blk = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, act=gp, M_cap=M_cap)
+    run_gpu_layer(wl, M_cap, block=blk)
+    fw = om.forward(wl.x, wl.w1, wl.w2, wl.expert_idx, wl.probs, wl.E, op, M_cap=M_cap)
+    bw = om.backward(fw, wl.dout, wl.w1, wl.w2, op)
+    # both bounds bind on a good share of the FC1 outputs at this scale
+    zv = fw.z[fw.expert >= 0]
+    assert np.mean(zv[:, :wl.I] > 0.15) > 0.1
+    assert np.mean(np.abs(zv[:, wl.I:]) > 0.25) > 0.1
+    compare_layer(blk, wl, fw, bw)
+    assert int(blk.err_flag.cpu()[0]) == 0
+
+
 def test_layer_all_tokens_one_expert_and_empty_groups():
     wl = make_workload("tiny", seed=5, T=700)
     wl.expert_idx[:, 0] = 2
