@@ -49,6 +49,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, int epi, bool b_nn, bool mx, i
                                hipStream_t s) {
   if (mx && b_nn) return hipErrorInvalidValue;
   if (epi == EPI_STORE) return launch_gemm_store(g, b_nn, mx, grid, s);
+  if (epi == EPI_WGRAD) return b_nn ? hipErrorInvalidValue : launch_gemm_wgrad(g, mx, grid, s);
   if (mx) {
     if (epi == EPI_GLU) return launch_gemm_glu_mx(g, grid, s);
     if (epi == EPI_DGLU) return launch_gemm_dglu_mx(g, grid, s);

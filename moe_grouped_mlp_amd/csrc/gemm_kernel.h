@@ -929,7 +929,7 @@ void grouped_gemm_kernel(GemmArgs g) {
   __shared__ int s_tmp[kThreads / 64];
   __shared__ float s_red[2 * BM];
   // per-wave staging tiles of the transposed MXFP8 copies (MX epilogues)
-  constexpr int kTrWords = (MX && EPI != EPI_STORE) ? 4 * kTrTile : 4;
+  constexpr int kTrWords = (MX && (EPI == EPI_GLU || EPI == EPI_DGLU)) ? 4 * kTrTile : 4;
   __shared__ __attribute__((aligned(16))) uint16_t s_tr[kTrWords];
 
   const int tid = threadIdx.x;
@@ -942,6 +942,11 @@ void grouped_gemm_kernel(GemmArgs g) {
   constexpr int kElem = MX ? 1 : 2;  // bytes per operand element
 
   // ---- tile prefix over the experts (device-resident group sizes) ----
+  // row tiles of an expert with n routed rows: ceil(n / BM), or for the
+  // weight gradient ceil(P / BM) whatever n (an empty group stores zeros)
+  auto tiles_m_of = [&](int n) {
+    return EPI == EPI_WGRAD ? (g.wg_rows + BM - 1) / BM : (n + BM - 1) / BM;
+  };
   const int per = (E + kThreads - 1) / kThreads;
   int mine = 0;
   for (int i = 0; i < per; ++i) {
@@ -950,7 +955,7 @@ void grouped_gemm_kernel(GemmArgs g) {
       int n = max(g.split[e], 0);
       s_split[e] = n;
       s_pad[e] = g.padded[e];
-      mine += ((n + BM - 1) / BM) * tiles_n;
+      mine += tiles_m_of(n) * tiles_n;
     }
   }
   int total;
@@ -959,7 +964,7 @@ void grouped_gemm_kernel(GemmArgs g) {
     int e = tid * per + i;
     if (e < E) {
       s_start[e] = run;
-      run += ((s_split[e] + BM - 1) / BM) * tiles_n;
+      run += tiles_m_of(s_split[e]) * tiles_n;
     }
   }
   if (tid == 0) s_start[E] = total;
@@ -1009,7 +1014,8 @@ void grouped_gemm_kernel(GemmArgs g) {
     int e, m_t, n_t, col0, cols_valid, rows_valid, rows_pad;
     int kbeg, kend;   // K stages of this work item
     int part, slot;   // split-K part and partial-tile slot (parts > 1)
-    int64_t row0;
+    int64_t row0;     // first row of A
+    int64_t orow0;    // first row of C (row0, or e * P + row0 for EPI_WGRAD)
   };
   auto tile_info = [&](int tile) {
     // expert owning this tile: last e with s_start[e] <= tile
@@ -1021,7 +1027,7 @@ void grouped_gemm_kernel(GemmArgs g) {
     TileInfo ti;
     ti.e = lo;
     const int local = tile - s_start[ti.e];
-    const int tm_e = (s_split[ti.e] + BM - 1) / BM;
+    const int tm_e = tiles_m_of(s_split[ti.e]);
     const int band = local / (g.group_m * tiles_n);
     const int first_m = band * g.group_m;
     const int gm = min(g.group_m, tm_e - first_m);
@@ -1029,7 +1035,21 @@ void grouped_gemm_kernel(GemmArgs g) {
     const int m_t = first_m + rem % gm;
     ti.m_t = m_t;
     ti.n_t = rem / gm;
+    ti.col0 = ti.n_t * BN;
+    ti.cols_valid = min(BN, g.N - ti.col0);
+    if constexpr (EPI == EPI_WGRAD) {
+      // rows of A^T are output rows; K is the group's padded row span of
+      // the transposed copies (pad rows there hold zeros), whole stages
+      ti.row0 = static_cast<int64_t>(m_t) * BM;
+      ti.orow0 = static_cast<int64_t>(ti.e) * g.wg_rows + ti.row0;
+      ti.rows_valid = min(BM, g.wg_rows - m_t * BM);
+      ti.rows_pad = ti.rows_valid;
+      ti.kbeg = s_pad[ti.e] * kElem / kRowBytes;
+      ti.kend = ti.kbeg + (s_split[ti.e] * kElem + kRowBytes - 1) / kRowBytes;
+      return ti;
+    }
     ti.row0 = static_cast<int64_t>(s_pad[ti.e]) + static_cast<int64_t>(m_t) * BM;
+    ti.orow0 = ti.row0;
     // rows_valid <= 0 only with inconsistent offsets: the tile then loads
     // zeros (its row range is empty) and stores nothing
     ti.rows_valid = static_cast<int>(
@@ -1038,8 +1058,6 @@ void grouped_gemm_kernel(GemmArgs g) {
         (s_split[ti.e] + MOE_GROUP_ALIGN - 1) / MOE_GROUP_ALIGN * MOE_GROUP_ALIGN;
     ti.rows_pad = static_cast<int>(
         min(static_cast<int64_t>(min(BM, padded_rows - m_t * BM)), g.M_cap - ti.row0));
-    ti.col0 = ti.n_t * BN;
-    ti.cols_valid = min(BN, g.N - ti.col0);
     return ti;
   };
 
@@ -1078,7 +1096,8 @@ void grouped_gemm_kernel(GemmArgs g) {
     k_rot = nk_item > 0 ? (g.k_rot_stride * (ti.m_t + ti.n_t)) % nk_item : 0;
     k_beg = ti.kbeg;
     k_len = nk_item;
-    const int64_t rows_avail = ti.rows_valid > 0 ? g.M_cap - ti.row0 : 0;
+    const int64_t a_rows = EPI == EPI_WGRAD ? g.wg_rows : g.M_cap;
+    const int64_t rows_avail = ti.rows_valid > 0 ? a_rows - ti.row0 : 0;
     const int64_t arow0 = ti.rows_valid > 0 ? ti.row0 : 0;
     // the dGLU kernel recomputes the lane offsets per tile (hoisted, they
     // are spilled and reloaded in its epilogue)
@@ -1258,8 +1277,10 @@ void grouped_gemm_kernel(GemmArgs g) {
     const int parts = w >= full ? S : 1;
     ti.part = part;
     ti.slot = tile - full;
-    ti.kbeg = part * nk / parts;
-    ti.kend = (part + 1) * nk / parts;
+    if constexpr (EPI != EPI_WGRAD) {   // the weight gradient's range is the group's
+      ti.kbeg = part * nk / parts;
+      ti.kend = (part + 1) * nk / parts;
+    }
     return ti;
   };
 
@@ -1315,7 +1336,7 @@ void grouped_gemm_kernel(GemmArgs g) {
 
     // ------------------------------------------------------ epilogues ---
     TileCtx t;
-    t.row0 = t0.row0;
+    t.row0 = t0.orow0;
     t.rows_valid = t0.rows_valid;
     t.rows_pad = t0.rows_pad;
     t.col0 = t0.col0;
@@ -1324,7 +1345,7 @@ void grouped_gemm_kernel(GemmArgs g) {
     t.m_lane = wm * kWaveM + (lane & 31);
     t.n_lane = wn * kWaveN + 4 * (lane >> 5);
     MxOut mo{g.mx_q, g.mx_s, g.mx_qT, g.mx_sT, g.mx_n, g.M_cap};
-    if constexpr (EPI == EPI_STORE) {
+    if constexpr (EPI == EPI_STORE || EPI == EPI_WGRAD) {
       if (split) {
         // partial tile to slot (t0.slot, part); the part that arrives last
         // sums all S partials in part order (deterministic) and stores
@@ -1493,12 +1514,13 @@ hipError_t launch_act(const GemmArgs& g, int grid, hipStream_t s) {
 }  // namespace
 
 // One launcher per kernel family, each instantiated in a source file of its
-// own (gemm_store.hip, gemm_glu_*.hip, gemm_dglu_*.hip) so the families
+// own (gemm_store.hip, gemm_glu_*.hip, gemm_dglu_*.hip, gemm_wgrad.hip) so the families
 // compile in parallel.
 hipError_t launch_gemm_store(const GemmArgs& g, bool b_nn, bool mx, int grid, hipStream_t s);
 hipError_t launch_gemm_glu_bf16(const GemmArgs& g, int grid, hipStream_t s);
 hipError_t launch_gemm_glu_mx(const GemmArgs& g, int grid, hipStream_t s);
 hipError_t launch_gemm_dglu_bf16(const GemmArgs& g, int grid, hipStream_t s);
 hipError_t launch_gemm_dglu_mx(const GemmArgs& g, int grid, hipStream_t s);
+hipError_t launch_gemm_wgrad(const GemmArgs& g, bool mx, int grid, hipStream_t s);
 
 }  // namespace moe

@@ -33,7 +33,10 @@ hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const moe_quant_args& a, hipStream_t s);
 
 // ---- grouped GEMM --------------------------------------------------------
-enum Epi { EPI_STORE = 0, EPI_GLU = 1, EPI_DGLU = 2 };
+// EPI_WGRAD: weight gradient C_e = A_e . B_e^T with A = A^T-copy [P][M_cap]
+// and B = B^T-copy [Q][M_cap] (K-contiguous along the routed rows), K running
+// over expert e's padded row span, C [E][P][Q] stored as in EPI_STORE.
+enum Epi { EPI_STORE = 0, EPI_GLU = 1, EPI_DGLU = 2, EPI_WGRAD = 3 };
 
 struct GemmArgs {
   int E, N, K;
@@ -46,6 +49,7 @@ struct GemmArgs {
   const uint8_t* a_s;    // MXFP8: tiled scales of A (R = M_cap)
   const uint8_t* b_s;    // MXFP8: tiled scales of B per expert (R = N)
   int64_t b_s_stride;    // bytes between experts of b_s
+  int wg_rows;           // EPI_WGRAD: P, rows of A and of each expert's C
   int group_m;           // m-tiles per band of the tile order
   int k_rot_stride;      // K-order rotation per (m_t + n_t) step (0: none)
   // epilogue

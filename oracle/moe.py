@@ -28,6 +28,8 @@ between:
              activations]; routing-probability scaling (ScaledSwiGLU)
              [TE § Challenge 3]
   unpermute  weighted combine by index-add [TE § Challenge 1]
+  wgrad      per-expert weight gradients dW1 = dZ^T Xp, dW2 = dYp^T a
+             [FK § Overcoming training bottlenecks, Fig. 1]
   backward   FC2 dgrad + dActivation [FK § Overcoming training bottlenecks,
              Fig. 1; § Optimizing GLU activations, backward epilogue], FC1
              dgrad, and the gradient of the routing probabilities
@@ -416,6 +418,42 @@ def backward(fw: Forward, dout_bits, w1_bits, w2_bits, prm: ActParams, *,
         bw.dz_mx = mx_quantize(dz[:mp], 1)
         bw.dzT_mx = mx_quantize(dz[:mp].T, 1)
     return bw
+
+
+# ======================================================= weight gradients ===
+def weight_grads(fw: Forward, bw: Backward, *, mx=False, exact=False):
+    """Weight gradients of the loss sum(out * dOut), expert by expert: the
+    weight-gradient GEMMs of the MoE backward, which [FK § Overcoming
+    training bottlenecks in MoE blocks, Fig. 1] keeps outside the fused
+    kernels.  For expert e over its routed rows r (GroupedLinear's per-expert
+    weights [TE § Challenge 1]):
+
+        dW1[e] = sum_r dZ[r]^T Xp[r]     [N1][H], logical FC1 layout
+        dW2[e] = sum_r dYp[r]^T a[r]     [H][I]
+
+    from the stored dZ, Xp, dYp and a, each result rounded to bf16 once.
+    With mx every operand is its MXFP8 copy blocked along the routed rows,
+    the contraction axis, with blocks starting at the group's padded start
+    (the transposed copies of [FK § Fused MXFP8 and NVFP4 quantization]);
+    pad rows hold zeros.  exact skips the rounding (finite-difference pins).
+    """
+    rnd = not exact
+    rt = fw.rt
+    E = len(rt.split_sizes)
+    N1, H, I = bw.dz.shape[1], fw.xp.shape[1], fw.a.shape[1]
+    dw1 = np.zeros((E, N1, H))
+    dw2 = np.zeros((E, H, I))
+    for e in range(E):
+        s0, n = int(rt.padded_offsets[e]), int(rt.split_sizes[e])
+        if n == 0:
+            continue
+        span = slice(s0, s0 + -(-n // ALIGN) * ALIGN)   # zero past row n
+        dz, xp = bw.dz[span], fw.xp[span]
+        dy, a = bw.dyp[span], fw.a[span]
+        on = mx and rnd
+        dw1[e] = _maybe_bf16(_mx_operand(dz, 0, on).T @ _mx_operand(xp, 0, on), rnd)
+        dw2[e] = _maybe_bf16(_mx_operand(dy, 0, on).T @ _mx_operand(a, 0, on), rnd)
+    return dw1, dw2
 
 
 # ============================================== per-row sampled checks ====

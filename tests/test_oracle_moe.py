@@ -221,14 +221,17 @@ def test_dense_special_case_matches_torch():
     fw = moe.forward(x, w1, w2, idx, p, 1, prm, exact=True)
     bw = moe.backward(fw, dout, w1, w2, prm, exact=True)
     xt = torch.tensor(x, requires_grad=True)
-    W1 = torch.tensor(w1[0])
-    W2 = torch.tensor(w2[0])
+    W1 = torch.tensor(w1[0], requires_grad=True)
+    W2 = torch.tensor(w2[0], requires_grad=True)
     h = xt @ W1.T
     o = (torch.nn.functional.silu(h[:, :I]) * h[:, I:]) @ W2.T
     (o * torch.tensor(dout)).sum().backward()
     np.testing.assert_allclose(fw.out, o.detach().numpy(), rtol=1e-12,
                                atol=1e-14)
     np.testing.assert_allclose(bw.dx, xt.grad.numpy(), rtol=1e-12, atol=1e-14)
+    dw1, dw2 = moe.weight_grads(fw, bw, exact=True)
+    np.testing.assert_allclose(dw1[0], W1.grad.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dw2[0], W2.grad.numpy(), rtol=1e-12, atol=1e-14)
 
 
 def _loss(x, w1, w2, idx, p, E, prm, dout):
@@ -269,6 +272,37 @@ def test_layer_backward_matches_finite_differences(prm):
             num_dp[i, s] = (_loss(x, w1, w2, idx, pp_, E, prm, dout) -
                             _loss(x, w1, w2, idx, pm_, E, prm, dout)) / (2 * h)
     np.testing.assert_allclose(bw.dprobs, num_dp, rtol=1e-5, atol=1e-8)
+
+
+@pytest.mark.parametrize("prm", [moe.ActParams(),
+                                 moe.ActParams.clamped(0.8, beta=1.702)])
+def test_weight_grads_match_finite_differences(prm):
+    """dW1, dW2 against central differences of the float64 layer loss on
+    every weight entry; expert 3 gets no rows, so its gradients are 0."""
+    rng = np.random.default_rng(6)
+    T, H, I, E, k = 7, 5, 4, 4, 2
+    x = rng.standard_normal((T, H))
+    w1 = rng.standard_normal((E, 2 * I, H)) * 0.5
+    w2 = rng.standard_normal((E, H, I)) * 0.5
+    idx = np.stack([rng.permutation(E - 1)[:k] for _ in range(T)])
+    p = rng.random((T, k))
+    dout = rng.standard_normal((T, H))
+    fw = moe.forward(x, w1, w2, idx, p, E, prm, exact=True)
+    bw = moe.backward(fw, dout, w1, w2, prm, exact=True)
+    dw1, dw2 = moe.weight_grads(fw, bw, exact=True)
+    h = 1e-6
+    for w, dw, is_w1 in ((w1, dw1, True), (w2, dw2, False)):
+        num = np.zeros_like(w)
+        for ix in np.ndindex(*w.shape):
+            wp_, wm_ = w.copy(), w.copy()
+            wp_[ix] += h
+            wm_[ix] -= h
+            args_p = (wp_, w2) if is_w1 else (w1, wp_)
+            args_m = (wm_, w2) if is_w1 else (w1, wm_)
+            num[ix] = (_loss(x, *args_p, idx, p, E, prm, dout) -
+                       _loss(x, *args_m, idx, p, E, prm, dout)) / (2 * h)
+        np.testing.assert_allclose(dw, num, rtol=1e-5, atol=1e-8)
+        assert np.all(dw[E - 1] == 0)
 
 
 def test_prob_linearity_token_equivariance_and_empty_group():
