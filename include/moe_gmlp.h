@@ -378,6 +378,54 @@ typedef struct moe_bwd_args {
 
 moe_status moe_grouped_mlp_bwd(const moe_bwd_args* args, void* stream);
 
+/* ------------------------------------------------------------------------
+ * moe_grouped_mlp_wgrad -- the weight-gradient grouped GEMMs of the backward
+ *   ([FK] § "Overcoming training bottlenecks", Fig. 1: the weight gradients
+ *   stay in separate blocks outside the fused kernels; § "Fused MXFP8 and
+ *   NVFP4 quantization": the transposed copies the epilogues write are their
+ *   operands).
+ *
+ *   For every local expert e, over its rows r in [padded_offsets[e],
+ *   padded_offsets[e] + split_sizes[e]):
+ *     dw1[e] = bf16( sum_r dz[r]^T xp[r] )   [N1][H], rows in the column
+ *                                            order of dz (that of w1i)
+ *     dw2[e] = bf16( sum_r dyp[r]^T a[r] )   [H][I]
+ *   fp32 accumulation, one rounding; an expert with no rows gets zeros.
+ *   Operands are transposed copies [rows][M_cap] of the routed activations,
+ *   so the contraction over the routed rows runs along contiguous memory:
+ *   dzT [N1][M_cap], xpT [H][M_cap], dypT [H][M_cap], aT [I][M_cap].
+ *   Columns [padded_offsets[e], padded_offsets[e + 1]) belong to expert e
+ *   and must hold zeros past its split_sizes[e] rows (the pad rows).
+ *     prec == MOE_PREC_BF16: bf16 copies; the *_s pointers are not read.
+ *     prec == MOE_PREC_MXFP8: E4M3 codes blocked along M, scales tiled with
+ *       R = rows, K = M_cap: aT from moe_grouped_mlp_fwd, dzT from
+ *       moe_grouped_mlp_bwd, xpT and dypT from moe_quantize_mxfp8
+ *       (MOE_QUANT_COL of xp and dyp, rows = M_cap).
+ *   dw1 or dw2 may be NULL to skip that GEMM; the caller owns every buffer.
+ *   Needs M_cap % 128 == 0 and M_cap <= 4194304; H, I multiples of 64.
+ *   Invalid arguments return MOE_ERR_INVALID_ARG before any launch.
+ *   timing_events: optional hipEvent_t handles recorded before dw1, between,
+ *   and after dw2.
+ * ---------------------------------------------------------------------- */
+typedef struct moe_wgrad_args {
+  int32_t E, H, I;
+  int32_t gated;                  /* 1: N1 = 2 I (GLU), 0: N1 = I (sReLU) */
+  int64_t M_cap;
+  int32_t prec;
+  int32_t cu_margin;
+  const int32_t* split_sizes;     /* [E]   device */
+  const int32_t* padded_offsets;  /* [E+1] device */
+  const void* dzT;  const uint8_t* dzT_s;   /* [N1][M_cap] */
+  const void* xpT;  const uint8_t* xpT_s;   /* [H][M_cap]  */
+  const void* dypT; const uint8_t* dypT_s;  /* [H][M_cap]  */
+  const void* aT;   const uint8_t* aT_s;    /* [I][M_cap]  */
+  void* dw1;                      /* bf16 [E][N1][H] or NULL */
+  void* dw2;                      /* bf16 [E][H][I] or NULL  */
+  void* timing_events[3];
+} moe_wgrad_args;
+
+moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* args, void* stream);
+
 /* Workspace bytes for these sizes: the backward needs at least the dprobs
  * partials (fp32 M_cap x ceil(I / 256)); the full size adds the area where
  * the plain-store GEMMs (FC2, FC1 dgrad) split their last, partial round of

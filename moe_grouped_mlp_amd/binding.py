@@ -27,7 +27,7 @@ DEVERR_MCAP_OVERFLOW, DEVERR_DUP_EXPERT = 0x1, 0x2
 EXPORTED_SYMBOLS = (
     "moe_weight_repack_interleave", "moe_permute_workspace_size",
     "moe_permute", "moe_unpermute", "moe_quantize_mxfp8",
-    "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd",
+    "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_mlp_wgrad",
     "moe_grouped_mlp_workspace_size", "moe_status_string", "moe_gmlp_version",
     "moe_mx_scale_offset",
 )
@@ -109,6 +109,19 @@ class BwdArgs(ctypes.Structure):
                 ("dzT_q", c_void_p), ("dzT_s", c_void_p)]
 
 
+class WgradArgs(ctypes.Structure):
+    _fields_ = [("E", c_int32), ("H", c_int32), ("I", c_int32),
+                ("gated", c_int32), ("M_cap", c_int64), ("prec", c_int32),
+                ("cu_margin", c_int32), ("split_sizes", c_void_p),
+                ("padded_offsets", c_void_p),
+                ("dzT", c_void_p), ("dzT_s", c_void_p),
+                ("xpT", c_void_p), ("xpT_s", c_void_p),
+                ("dypT", c_void_p), ("dypT_s", c_void_p),
+                ("aT", c_void_p), ("aT_s", c_void_p),
+                ("dw1", c_void_p), ("dw2", c_void_p),
+                ("timing_events", c_void_p * 3)]
+
+
 # ---- library loading ------------------------------------------------------
 _LIB = None
 
@@ -140,7 +153,8 @@ def lib() -> ctypes.CDLL:
                          ("moe_unpermute", UnpermuteArgs),
                          ("moe_quantize_mxfp8", QuantArgs),
                          ("moe_grouped_mlp_fwd", FwdArgs),
-                         ("moe_grouped_mlp_bwd", BwdArgs)):
+                         ("moe_grouped_mlp_bwd", BwdArgs),
+                         ("moe_grouped_mlp_wgrad", WgradArgs)):
             f = getattr(L, name)
             f.restype = c_int
             f.argtypes = [ctypes.POINTER(st), c_void_p]
@@ -272,3 +286,17 @@ def moe_grouped_mlp_bwd(*, E, H, I, M_cap, split_sizes, padded_offsets,
                    _ptr(dz_q), _ptr(dz_s), _ptr(dzT_q), _ptr(dzT_s))
     _check("moe_grouped_mlp_bwd",
            lib().moe_grouped_mlp_bwd(ctypes.byref(args), _stream(stream)))
+
+
+def moe_grouped_mlp_wgrad(*, E, H, I, M_cap, split_sizes, padded_offsets,
+                          gated=True, prec=PREC_BF16, cu_margin=0, dzT=None,
+                          dzT_s=None, xpT=None, xpT_s=None, dypT=None,
+                          dypT_s=None, aT=None, aT_s=None, dw1=None, dw2=None,
+                          timing_events=None, stream=None):
+    args = WgradArgs(E, H, I, int(bool(gated)), M_cap, prec, cu_margin,
+                     _ptr(split_sizes), _ptr(padded_offsets), _ptr(dzT),
+                     _ptr(dzT_s), _ptr(xpT), _ptr(xpT_s), _ptr(dypT),
+                     _ptr(dypT_s), _ptr(aT), _ptr(aT_s), _ptr(dw1), _ptr(dw2),
+                     _events(timing_events))
+    _check("moe_grouped_mlp_wgrad",
+           lib().moe_grouped_mlp_wgrad(ctypes.byref(args), _stream(stream)))

@@ -466,4 +466,63 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
   return MOE_OK;
 }
 
+moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* a, void* stream) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  if (a->E < 1 || a->E > kMaxExperts || a->H < 64 || a->I < 64 || a->H % 64 != 0 ||
+      a->I % 64 != 0 || (a->gated != 0 && a->gated != 1) || a->M_cap < 128 ||
+      a->M_cap % 128 != 0 || a->M_cap > (int64_t{1} << 22) || a->cu_margin < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (!a->split_sizes || !a->padded_offsets) return MOE_ERR_INVALID_ARG;
+  if (a->prec != MOE_PREC_BF16 && a->prec != MOE_PREC_MXFP8) return MOE_ERR_INVALID_ARG;
+  const bool mx = a->prec == MOE_PREC_MXFP8;
+  if (a->dw1 && (!a->dzT || !a->xpT || (mx && (!a->dzT_s || !a->xpT_s))))
+    return MOE_ERR_INVALID_ARG;
+  if (a->dw2 && (!a->dypT || !a->aT || (mx && (!a->dypT_s || !a->aT_s))))
+    return MOE_ERR_INVALID_ARG;
+  int cu = 0;
+  if (moe_status st = device_info(&cu)) return st;
+  if (a->cu_margin >= cu) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int N1 = a->gated ? 2 * a->I : a->I;
+
+  // C_e [P][Q] = A^T-copy [P][M_cap] . (B^T-copy [Q][M_cap])^T over e's rows
+  auto run = [&](const void* A, const uint8_t* As, int P, const void* Bm, const uint8_t* Bs,
+                 int Q, void* C) -> moe_status {
+    moe::GemmArgs g{};
+    g.E = a->E;
+    g.N = Q;
+    g.K = static_cast<int>(a->M_cap);
+    g.M_cap = a->M_cap;
+    g.split = a->split_sizes;
+    g.padded = a->padded_offsets;
+    g.A = A;
+    g.a_s = As;
+    g.B = Bm;
+    g.b_stride = 0;
+    g.b_s = Bs;
+    g.b_s_stride = 0;
+    g.wg_rows = P;
+    g.group_m = tuning().group_m;
+    g.k_rot_stride = tuning().k_rot;
+    g.C = static_cast<uint16_t*>(C);
+    g.ldc = Q;
+    const int bm = moe::grouped_gemm_tile_m(), bn = moe::grouped_gemm_tile_n();
+    const int64_t tiles = static_cast<int64_t>(a->E) * ((P + bm - 1) / bm) * ((Q + bn - 1) / bn);
+    int grid = cu - a->cu_margin;
+    if (grid >= 8) grid -= grid % 8;
+    if (tiles < grid) grid = static_cast<int>(tiles);
+    return launched(moe::launch_grouped_gemm(g, moe::EPI_WGRAD, false, mx, grid, s));
+  };
+  record(a->timing_events[0], s);
+  if (a->dw1) {
+    if (moe_status st = run(a->dzT, a->dzT_s, N1, a->xpT, a->xpT_s, a->H, a->dw1)) return st;
+  }
+  record(a->timing_events[1], s);
+  if (a->dw2) {
+    if (moe_status st = run(a->dypT, a->dypT_s, a->H, a->aT, a->aT_s, a->I, a->dw2)) return st;
+  }
+  record(a->timing_events[2], s);
+  return MOE_OK;
+}
+
 }  // extern "C"

@@ -566,9 +566,14 @@ struct TileCtx {
 MOE_DEV void acc_hold(f32x16& v) { asm volatile("" : "+a"(v)); }
 
 // EPI_STORE: C = bf16(acc)
-MOE_DEV void epi_store(const f32x16 (&acc)[4][4], uint16_t* __restrict__ C, int64_t ldc,
+// HOLD: keep each row block's accumulators in AGPRs until it is stored (the
+// bf16 kernels; with it the MXFP8 kernel's allocation spills inside its K
+// loop instead, so that one goes without).
+template <bool HOLD>
+MOE_DEV void epi_store(f32x16 (&acc)[4][4], uint16_t* __restrict__ C, int64_t ldc,
                        const TileCtx& t) {
   sfor<4>([&](auto mi) {
+    if constexpr (HOLD) sfor<4>([&](auto ni) { acc_hold(acc[mi][ni]); });
     const int m = t.m_lane + mi * 32;
     if (m < t.rows_valid) {
       uint16_t* crow = C + (t.row0 + m) * ldc + t.col0 + t.n_lane;
@@ -1044,8 +1049,11 @@ void grouped_gemm_kernel(GemmArgs g) {
       ti.orow0 = static_cast<int64_t>(ti.e) * g.wg_rows + ti.row0;
       ti.rows_valid = min(BM, g.wg_rows - m_t * BM);
       ti.rows_pad = ti.rows_valid;
-      ti.kbeg = s_pad[ti.e] * kElem / kRowBytes;
-      ti.kend = ti.kbeg + (s_split[ti.e] * kElem + kRowBytes - 1) / kRowBytes;
+      // clamped to the copies' width, so inconsistent offsets read zeros
+      // (every stage then lies inside its row) instead of past a row's end
+      const int nk_all = g.K * kElem / kRowBytes;
+      ti.kbeg = min(max(s_pad[ti.e], 0) * kElem / kRowBytes, nk_all);
+      ti.kend = min(ti.kbeg + (s_split[ti.e] * kElem + kRowBytes - 1) / kRowBytes, nk_all);
       return ti;
     }
     ti.row0 = static_cast<int64_t>(s_pad[ti.e]) + static_cast<int64_t>(m_t) * BM;
@@ -1351,11 +1359,14 @@ void grouped_gemm_kernel(GemmArgs g) {
         // sums all S partials in part order (deterministic) and stores
         float4* ws = reinterpret_cast<float4*>(g.split_ws) +
                      static_cast<int64_t>(t0.slot * S + t0.part) * (64 * kThreads);
-        sfor<4>([&](auto mi) { sfor<4>([&](auto ni) { sfor<4>([&](auto q) {
-          const f32x16& a = acc[mi][ni];
-          ws[((mi * 4 + ni) * 4 + q) * kThreads + tid] =
-              make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
-        }); }); });
+        sfor<4>([&](auto mi) { sfor<4>([&](auto ni) {
+          if constexpr (!MX) acc_hold(acc[mi][ni]);
+          sfor<4>([&](auto q) {
+            const f32x16& a = acc[mi][ni];
+            ws[((mi * 4 + ni) * 4 + q) * kThreads + tid] =
+                make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+          });
+        }); });
         // release: the partials reach memory before this part is counted
         // (another XCD's L2 may hold the tile that reads them)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -1378,11 +1389,11 @@ void grouped_gemm_kernel(GemmArgs g) {
               acc[mi][ni][4 * q + 3] += v.w;
             }); }); });
           }
-          epi_store(acc, g.C, g.ldc, t);
+          epi_store<!MX>(acc, g.C, g.ldc, t);
         }
         __syncthreads();   // s_tmp is read by every thread above
       } else {
-        epi_store(acc, g.C, g.ldc, t);
+        epi_store<!MX>(acc, g.C, g.ldc, t);
       }
     } else if constexpr (EPI == EPI_GLU) {
       float amax;
