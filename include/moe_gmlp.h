@@ -382,8 +382,8 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* args, void* stream);
  * moe_grouped_mlp_wgrad -- the weight-gradient grouped GEMMs of the backward
  *   ([FK] § "Overcoming training bottlenecks", Fig. 1: the weight gradients
  *   stay in separate blocks outside the fused kernels; § "Fused MXFP8 and
- *   NVFP4 quantization": the transposed copies the epilogues write are their
- *   operands).
+ *   NVFP4 quantization": the transposed copies the epilogues write are the
+ *   MXFP8 operands).
  *
  *   For every local expert e, over its rows r in [padded_offsets[e],
  *   padded_offsets[e] + split_sizes[e]):
@@ -391,16 +391,17 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* args, void* stream);
  *                                            order of dz (that of w1i)
  *     dw2[e] = bf16( sum_r dyp[r]^T a[r] )   [H][I]
  *   fp32 accumulation, one rounding; an expert with no rows gets zeros.
- *   Operands are transposed copies [rows][M_cap] of the routed activations,
- *   so the contraction over the routed rows runs along contiguous memory:
- *   dzT [N1][M_cap], xpT [H][M_cap], dypT [H][M_cap], aT [I][M_cap].
- *   Columns [padded_offsets[e], padded_offsets[e + 1]) belong to expert e
- *   and must hold zeros past its split_sizes[e] rows (the pad rows).
- *     prec == MOE_PREC_BF16: bf16 copies; the *_s pointers are not read.
- *     prec == MOE_PREC_MXFP8: E4M3 codes blocked along M, scales tiled with
- *       R = rows, K = M_cap: aT from moe_grouped_mlp_fwd, dzT from
- *       moe_grouped_mlp_bwd, xpT and dypT from moe_quantize_mxfp8
- *       (MOE_QUANT_COL of xp and dyp, rows = M_cap).
+ *     prec == MOE_PREC_BF16: dz [M_cap][N1], xp [M_cap][H], dyp [M_cap][H]
+ *       and a [M_cap][I] as the forward and backward store them (bf16,
+ *       row-major).  Only the rows of the groups' data are read, so pad rows
+ *       may hold anything.  Needs M_cap * max(N1, H, I) * 2 < 2^31.
+ *     prec == MOE_PREC_MXFP8: their transposed copies [n][M_cap], E4M3
+ *       codes blocked along M with scales tiled (R = n, K = M_cap): aT_q from
+ *       moe_grouped_mlp_fwd, dzT_q from moe_grouped_mlp_bwd, xpT_q and
+ *       dypT_q from moe_quantize_mxfp8 (MOE_QUANT_COL of xp and dyp, rows =
+ *       M_cap).  Columns [padded_offsets[e], padded_offsets[e + 1]) belong to
+ *       expert e and are read whole, so the pad rows there must encode zero
+ *       (as the producers above write them).
  *   dw1 or dw2 may be NULL to skip that GEMM; the caller owns every buffer.
  *   Needs M_cap % 128 == 0 and M_cap <= 4194304; H, I multiples of 64.
  *   Invalid arguments return MOE_ERR_INVALID_ARG before any launch.
@@ -415,10 +416,11 @@ typedef struct moe_wgrad_args {
   int32_t cu_margin;
   const int32_t* split_sizes;     /* [E]   device */
   const int32_t* padded_offsets;  /* [E+1] device */
-  const void* dzT;  const uint8_t* dzT_s;   /* [N1][M_cap] */
-  const void* xpT;  const uint8_t* xpT_s;   /* [H][M_cap]  */
-  const void* dypT; const uint8_t* dypT_s;  /* [H][M_cap]  */
-  const void* aT;   const uint8_t* aT_s;    /* [I][M_cap]  */
+  const void* dz;  const void* xp;  const void* dyp;  const void* a;   /* bf16 */
+  const uint8_t* dzT_q;  const uint8_t* dzT_s;    /* MXFP8 [N1][M_cap] */
+  const uint8_t* xpT_q;  const uint8_t* xpT_s;    /* MXFP8 [H][M_cap]  */
+  const uint8_t* dypT_q; const uint8_t* dypT_s;   /* MXFP8 [H][M_cap]  */
+  const uint8_t* aT_q;   const uint8_t* aT_s;     /* MXFP8 [I][M_cap]  */
   void* dw1;                      /* bf16 [E][N1][H] or NULL */
   void* dw2;                      /* bf16 [E][H][I] or NULL  */
   void* timing_events[3];

@@ -114,10 +114,12 @@ class WgradArgs(ctypes.Structure):
                 ("gated", c_int32), ("M_cap", c_int64), ("prec", c_int32),
                 ("cu_margin", c_int32), ("split_sizes", c_void_p),
                 ("padded_offsets", c_void_p),
-                ("dzT", c_void_p), ("dzT_s", c_void_p),
-                ("xpT", c_void_p), ("xpT_s", c_void_p),
-                ("dypT", c_void_p), ("dypT_s", c_void_p),
-                ("aT", c_void_p), ("aT_s", c_void_p),
+                ("dz", c_void_p), ("xp", c_void_p), ("dyp", c_void_p),
+                ("a", c_void_p),
+                ("dzT_q", c_void_p), ("dzT_s", c_void_p),
+                ("xpT_q", c_void_p), ("xpT_s", c_void_p),
+                ("dypT_q", c_void_p), ("dypT_s", c_void_p),
+                ("aT_q", c_void_p), ("aT_s", c_void_p),
                 ("dw1", c_void_p), ("dw2", c_void_p),
                 ("timing_events", c_void_p * 3)]
 
@@ -289,14 +291,16 @@ def moe_grouped_mlp_bwd(*, E, H, I, M_cap, split_sizes, padded_offsets,
 
 
 def moe_grouped_mlp_wgrad(*, E, H, I, M_cap, split_sizes, padded_offsets,
-                          gated=True, prec=PREC_BF16, cu_margin=0, dzT=None,
-                          dzT_s=None, xpT=None, xpT_s=None, dypT=None,
-                          dypT_s=None, aT=None, aT_s=None, dw1=None, dw2=None,
+                          gated=True, prec=PREC_BF16, cu_margin=0, dz=None,
+                          xp=None, dyp=None, a=None, dzT_q=None, dzT_s=None,
+                          xpT_q=None, xpT_s=None, dypT_q=None, dypT_s=None,
+                          aT_q=None, aT_s=None, dw1=None, dw2=None,
                           timing_events=None, stream=None):
     args = WgradArgs(E, H, I, int(bool(gated)), M_cap, prec, cu_margin,
-                     _ptr(split_sizes), _ptr(padded_offsets), _ptr(dzT),
-                     _ptr(dzT_s), _ptr(xpT), _ptr(xpT_s), _ptr(dypT),
-                     _ptr(dypT_s), _ptr(aT), _ptr(aT_s), _ptr(dw1), _ptr(dw2),
+                     _ptr(split_sizes), _ptr(padded_offsets), _ptr(dz),
+                     _ptr(xp), _ptr(dyp), _ptr(a), _ptr(dzT_q), _ptr(dzT_s),
+                     _ptr(xpT_q), _ptr(xpT_s), _ptr(dypT_q), _ptr(dypT_s),
+                     _ptr(aT_q), _ptr(aT_s), _ptr(dw1), _ptr(dw2),
                      _events(timing_events))
     _check("moe_grouped_mlp_wgrad",
            lib().moe_grouped_mlp_wgrad(ctypes.byref(args), _stream(stream)))

@@ -475,17 +475,25 @@ moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* a, void* stream) {
   if (!a->split_sizes || !a->padded_offsets) return MOE_ERR_INVALID_ARG;
   if (a->prec != MOE_PREC_BF16 && a->prec != MOE_PREC_MXFP8) return MOE_ERR_INVALID_ARG;
   const bool mx = a->prec == MOE_PREC_MXFP8;
-  if (a->dw1 && (!a->dzT || !a->xpT || (mx && (!a->dzT_s || !a->xpT_s))))
-    return MOE_ERR_INVALID_ARG;
-  if (a->dw2 && (!a->dypT || !a->aT || (mx && (!a->dypT_s || !a->aT_s))))
-    return MOE_ERR_INVALID_ARG;
+  const int N1 = a->gated ? 2 * a->I : a->I;
+  if (mx) {
+    if (a->dw1 && (!a->dzT_q || !a->dzT_s || !a->xpT_q || !a->xpT_s)) return MOE_ERR_INVALID_ARG;
+    if (a->dw2 && (!a->dypT_q || !a->dypT_s || !a->aT_q || !a->aT_s)) return MOE_ERR_INVALID_ARG;
+  } else {
+    if (a->dw1 && (!a->dz || !a->xp)) return MOE_ERR_INVALID_ARG;
+    if (a->dw2 && (!a->dyp || !a->a)) return MOE_ERR_INVALID_ARG;
+    // the loaders address a whole [M_cap][n] activation with 31-bit offsets
+    // (0x7fffffff, the offset of a masked lane, must lie past its end)
+    const int64_t widest = std::max(std::max(N1, a->H), a->I);
+    if (a->M_cap * widest * 2 > int64_t{INT32_MAX}) return MOE_ERR_INVALID_ARG;
+  }
   int cu = 0;
   if (moe_status st = device_info(&cu)) return st;
   if (a->cu_margin >= cu) return MOE_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int N1 = a->gated ? 2 * a->I : a->I;
 
-  // C_e [P][Q] = A^T-copy [P][M_cap] . (B^T-copy [Q][M_cap])^T over e's rows
+  // C_e [P][Q] = sum over e's rows m of A[m][p] B[m][q]: bf16 A [M_cap][P],
+  // B [M_cap][Q]; MXFP8 their transposed copies
   auto run = [&](const void* A, const uint8_t* As, int P, const void* Bm, const uint8_t* Bs,
                  int Q, void* C) -> moe_status {
     moe::GemmArgs g{};
@@ -515,11 +523,15 @@ moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* a, void* stream) {
   };
   record(a->timing_events[0], s);
   if (a->dw1) {
-    if (moe_status st = run(a->dzT, a->dzT_s, N1, a->xpT, a->xpT_s, a->H, a->dw1)) return st;
+    if (moe_status st = mx ? run(a->dzT_q, a->dzT_s, N1, a->xpT_q, a->xpT_s, a->H, a->dw1)
+                           : run(a->dz, nullptr, N1, a->xp, nullptr, a->H, a->dw1))
+      return st;
   }
   record(a->timing_events[1], s);
   if (a->dw2) {
-    if (moe_status st = run(a->dypT, a->dypT_s, a->H, a->aT, a->aT_s, a->I, a->dw2)) return st;
+    if (moe_status st = mx ? run(a->dypT_q, a->dypT_s, a->H, a->aT_q, a->aT_s, a->I, a->dw2)
+                           : run(a->dyp, nullptr, a->H, a->a, nullptr, a->I, a->dw2))
+      return st;
   }
   record(a->timing_events[2], s);
   return MOE_OK;

@@ -266,6 +266,16 @@ struct NLoader {
     for (int j = 0; j < 8; ++j)
       dma16(rsrc, stage + (8 * wave_s + j) * 512, valid ? voff[j] : kOutOfRange, valid ? soff : 0);
   }
+  // Same, reading zeros for K rows at or past row_end: stage kk holds rows
+  // 64 kk .. 64 kk + 63, lane l of instruction j row 16 w + 2 j + l / 32.
+  MOE_DEV void issue_lim(uint16_t* stage, int soff, int wave_s, bool valid, int kk, int row_end,
+                         int lane) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = valid && 64 * kk + 16 * wave_s + 2 * j + (lane >> 5) < row_end;
+      dma16(rsrc, stage + (8 * wave_s + j) * 512, ok ? voff[j] : kOutOfRange, valid ? soff : 0);
+    }
+  }
 };
 
 // MXFP8 scales of one stage (two 64-deep K steps) for a 256-row A tile and
@@ -1009,6 +1019,21 @@ void grouped_gemm_kernel(GemmArgs g) {
         btr_off[h][ni] = row * 512 + (c ^ (4 * (row & 7))) * 16 + 8 * (sl & 1);
       }
   }
+  // the bf16 weight gradient reads A from a [K][M] image too (rows of the
+  // routed activations), with the same transpose reads, wave row wm
+  constexpr bool kTN = EPI == EPI_WGRAD && !MX;
+  int atr_off[2][4];
+  if constexpr (kTN) {
+    const int gq = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const int row = 8 * (gq >> 1) + 4 * h + (sl >> 2);
+        const int c = wm * 16 + mi * 4 + 2 * (gq & 1) + ((sl & 3) >> 1);
+        atr_off[h][mi] = row * 512 + (c ^ (4 * (row & 7))) * 16 + 8 * (sl & 1);
+      }
+  }
   // MXFP8 scale byte of this lane's row (row group 4 wm + mi of A, 4 wn + ni
   // of B) for its K block (lane / 32) of 64-deep step j of a scale stage
   const int sa_off = 4 * wm * 128 + lane;
@@ -1077,9 +1102,11 @@ void grouped_gemm_kernel(GemmArgs g) {
   const char* A = static_cast<const char*>(g.A);
   const char* B = static_cast<const char*>(g.B);
   KLoader la;
+  NLoader la_n;     // A of the bf16 weight gradient
   KLoader lb_k;
   NLoader lb_n;
   ScaleLoader ls;
+  int row_end = 0;  // weight gradient: end of the group's rows (bf16 loads stop there)
   // K order of a tile: stages k_rot, k_rot + 1, ..., nk - 1, 0, ..., k_rot - 1
   // with k_rot = stride * (m_t + n_t) mod nk.  Tiles that share an operand
   // panel (same m_t or same n_t; an XCD holds a band of neighbouring tiles
@@ -1092,9 +1119,14 @@ void grouped_gemm_kernel(GemmArgs g) {
     int kk = kt + k_rot;
     if (kk >= k_len) kk -= k_len;
     kk += k_beg;
-    la.template issue<MX>(a_st, kk, wave_s, valid, k_bytes);
-    if constexpr (NN) lb_n.issue(b_st, kk * BK * (g.N * 2), wave_s, valid);
-    else lb_k.template issue<MX>(b_st, kk, wave_s, valid, k_bytes);
+    if constexpr (kTN) {
+      la_n.issue_lim(a_st, kk * BK * (g.wg_rows * 2), wave_s, valid, kk, row_end, lane);
+      lb_n.issue_lim(b_st, kk * BK * (g.N * 2), wave_s, valid, kk, row_end, lane);
+    } else {
+      la.template issue<MX>(a_st, kk, wave_s, valid, k_bytes);
+      if constexpr (NN) lb_n.issue(b_st, kk * BK * (g.N * 2), wave_s, valid);
+      else lb_k.template issue<MX>(b_st, kk, wave_s, valid, k_bytes);
+    }
     if constexpr (MX) ls.issue(s_st, kk, wave_s, valid, k_steps64);
   };
   // point the loaders at a tile (its first two stages are issued next)
@@ -1111,7 +1143,16 @@ void grouped_gemm_kernel(GemmArgs g) {
     // are spilled and reloaded in its epilogue)
     const int lane = EPI == EPI_DGLU ? opaque(lane_k) : lane_k;
     const int wave = EPI == EPI_DGLU ? opaque(wave_k) : wave_k;
-    la.init(A + arow0 * g.K * kElem, rows_avail, g.K * kElem, wave, lane);
+    if constexpr (kTN) {
+      // A and B are the routed activations [M_cap][P] and [M_cap][Q]; the
+      // tile's P columns of A start at row0, its rows (K) are the group's
+      row_end = s_pad[ti.e] + s_split[ti.e];
+      la_n.init(reinterpret_cast<const uint16_t*>(A),
+                static_cast<uint32_t>(static_cast<int64_t>(g.K) * g.wg_rows * 2), g.wg_rows,
+                static_cast<int>(ti.row0), wave, lane);
+    } else {
+      la.init(A + arow0 * g.K * kElem, rows_avail, g.K * kElem, wave, lane);
+    }
     const char* Bexp = B + static_cast<int64_t>(ti.e) * g.b_stride * kElem;
     if constexpr (NN) {
       lb_n.init(reinterpret_cast<const uint16_t*>(Bexp),
@@ -1182,9 +1223,20 @@ void grouped_gemm_kernel(GemmArgs g) {
         scb[buf][i] = s_st[sb_off + i * 128 + jj * 64];
       });
     } else {
-      sfor<4>([&](auto i) {
-        fa[buf][i] = *reinterpret_cast<const bf16x8*>(ca + a_off[jj] + i * 32 * kRowBytes);
-      });
+      if constexpr (kTN) {
+        sfor<4>([&](auto mi) {
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_t*)(ca + atr_off[0][mi] + jj * 16 * 512));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_t*)(ca + atr_off[1][mi] + jj * 16 * 512));
+          const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          fa[buf][mi] = __builtin_bit_cast(bf16x8, both);
+        });
+      } else {
+        sfor<4>([&](auto i) {
+          fa[buf][i] = *reinterpret_cast<const bf16x8*>(ca + a_off[jj] + i * 32 * kRowBytes);
+        });
+      }
       if constexpr (NN) {
         sfor<4>([&](auto ni) {
           const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -1213,7 +1265,7 @@ void grouped_gemm_kernel(GemmArgs g) {
     }); });
   };
   // LDS reads per sub-step and DMA loads per stage (per wave)
-  constexpr int kReads = MX ? 24 : (NN ? 12 : 8);
+  constexpr int kReads = MX ? 24 : (kTN ? 16 : (NN ? 12 : 8));
   constexpr int kLoads = 16 + (MX ? 2 : 0);
   // issue order: reads spread between the 16 MFMAs of a sub-step; in the
   // last sub-step of a stage the next stage's DMA loads go in between too

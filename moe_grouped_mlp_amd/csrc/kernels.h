@@ -33,9 +33,11 @@ hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const moe_quant_args& a, hipStream_t s);
 
 // ---- grouped GEMM --------------------------------------------------------
-// EPI_WGRAD: weight gradient C_e = A_e . B_e^T with A = A^T-copy [P][M_cap]
-// and B = B^T-copy [Q][M_cap] (K-contiguous along the routed rows), K running
-// over expert e's padded row span, C [E][P][Q] stored as in EPI_STORE.
+// EPI_WGRAD: weight gradient C_e [P][Q] = sum over expert e's routed rows m
+// of A[m][p] B[m][q], C [E][P][Q] stored as in EPI_STORE.  bf16: A and B are
+// the routed activations [M_cap][P], [M_cap][Q] (rows past the group's data
+// read as zero); MXFP8: their transposed copies [P][M_cap], [Q][M_cap],
+// blocked along M, over the group's padded span (pad rows hold zeros).
 enum Epi { EPI_STORE = 0, EPI_GLU = 1, EPI_DGLU = 2, EPI_WGRAD = 3 };
 
 struct GemmArgs {

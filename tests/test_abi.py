@@ -159,24 +159,29 @@ def test_wgrad_validation():
     def args(**kw):
         a = B.WgradArgs()
         a.E, a.H, a.I, a.gated, a.M_cap, a.prec = 4, 128, 256, 1, 1024, B.PREC_BF16
-        for f in ("split_sizes", "padded_offsets", "dzT", "xpT", "dypT", "aT",
+        for f in ("split_sizes", "padded_offsets", "dz", "xp", "dyp", "a",
                   "dw1", "dw2"):
             setattr(a, f, 64)
         for k, v in kw.items():
             setattr(a, k, v)
         return a
     assert _call("moe_grouped_mlp_wgrad", args()) == DEVICE
-    assert _call("moe_grouped_mlp_wgrad", args(dw1=None, dzT=None, xpT=None)) == DEVICE
-    assert _call("moe_grouped_mlp_wgrad", args(dw2=None, dypT=None, aT=None)) == DEVICE
+    assert _call("moe_grouped_mlp_wgrad", args(dw1=None, dz=None, xp=None)) == DEVICE
+    assert _call("moe_grouped_mlp_wgrad", args(dw2=None, dyp=None, a=None)) == DEVICE
     for bad in (dict(M_cap=1000), dict(M_cap=1 << 23), dict(H=96), dict(I=32),
                 dict(E=0), dict(gated=2), dict(prec=7), dict(cu_margin=-1),
-                dict(split_sizes=None), dict(padded_offsets=None), dict(aT=None),
-                dict(xpT=None), dict(prec=B.PREC_MXFP8)):
+                dict(split_sizes=None), dict(padded_offsets=None), dict(a=None),
+                dict(xp=None), dict(prec=B.PREC_MXFP8),
+                # bf16 addresses a whole [M_cap][n] activation with 32-bit offsets
+                dict(M_cap=1 << 17, I=16384)):
         assert _call("moe_grouped_mlp_wgrad", args(**bad)) == INVALID, bad
-    # MXFP8 needs the scales of every operand it reads
-    mx = dict(prec=B.PREC_MXFP8, dzT_s=64, xpT_s=64, dypT_s=64, aT_s=64)
+    # MXFP8 reads the transposed copies and needs the scales of every one
+    mx = dict(prec=B.PREC_MXFP8, dz=None, xp=None, dyp=None, a=None,
+              dzT_q=64, dzT_s=64, xpT_q=64, xpT_s=64, dypT_q=64, dypT_s=64,
+              aT_q=64, aT_s=64)
     assert _call("moe_grouped_mlp_wgrad", args(**mx)) == DEVICE
     assert _call("moe_grouped_mlp_wgrad", args(**{**mx, "aT_s": None})) == INVALID
+    assert _call("moe_grouped_mlp_wgrad", args(**{**mx, "xpT_q": None})) == INVALID
 
 
 def test_bwd_validation():

@@ -1,11 +1,11 @@
 """Weight-gradient grouped GEMMs (moe_grouped_mlp_wgrad) against the oracle's
 weight_grads, through the C ABI.
 
-bf16: the transposed copies of Xp, dYp, a and dz are made here with torch
-(test plumbing; pad rows set to zero).  MXFP8: a and dz come from the
-epilogues' transposed copies, Xp and dYp from moe_quantize_mxfp8 (MOE_QUANT_COL)
-of their bf16 rows, which the permutes produce exactly (bit for bit the
-oracle's values).  The MXFP8 GEMMs are checked against the oracle's
+bf16: the GEMMs read dz, Xp, dYp and a as the layer stored them (rows
+outside the groups' data, which the epilogues never write, are not read).
+MXFP8: a and dz come from the epilogues' transposed copies, Xp and dYp from
+moe_quantize_mxfp8 (MOE_QUANT_COL) of their bf16 rows, which the permutes
+produce exactly (bit for bit the oracle's values).  The MXFP8 GEMMs are checked against the oracle's
 contraction of the very MXFP8 operands the GPU read (the epilogues' copies
 can differ from the oracle's own encoding by a code where a bf16 value
 differs by an ulp, which the fused-epilogue tests bound), and against the
@@ -40,12 +40,6 @@ def _m_cap(wl):
     return -(-wl.m_cap() // 128) * 128
 
 
-def _transposed(t, rows_ok):
-    """[M_cap][n] bf16 -> [n][M_cap] with every row outside rows_ok zero."""
-    keep = torch.from_numpy(rows_ok).to(t.device)[:, None]
-    return torch.where(keep, t, torch.zeros((), dtype=t.dtype, device=t.device)).t().contiguous()
-
-
 def _logical_dw1(dw1, wl):
     """GPU dW1 rows follow dz's (interleaved) column order; the oracle's are
     logical (gate | up)."""
@@ -62,7 +56,10 @@ def test_wgrad_bf16_parity(case):
     M_cap = _m_cap(wl)
     blk = run_gpu_layer(wl, M_cap)
     fw, bw = oracle_layer(wl, M_cap)
-    ok = fw.expert >= 0
+    # rows the layer never wrote hold NaN: they must not be read
+    pad = torch.from_numpy(fw.expert < 0).cuda()
+    for t in (blk.a, blk.dz):
+        t[pad] = float("nan")
     gated = wl.act != "srelu"
     N1 = 2 * wl.I if gated else wl.I
     dw1 = torch.empty(wl.E, N1, wl.H, dtype=torch.bfloat16, device="cuda")
@@ -70,8 +67,7 @@ def test_wgrad_bf16_parity(case):
     mg.moe_grouped_mlp_wgrad(
         E=wl.E, H=wl.H, I=wl.I, M_cap=M_cap, gated=gated,
         split_sizes=blk.split_sizes, padded_offsets=blk.padded_offsets,
-        prec=mg.PREC_BF16, dzT=_transposed(blk.dz, ok), xpT=_transposed(blk.xp, ok),
-        dypT=_transposed(blk.dyp, ok), aT=_transposed(blk.a, ok), dw1=dw1, dw2=dw2)
+        prec=mg.PREC_BF16, dz=blk.dz, xp=blk.xp, dyp=blk.dyp, a=blk.a, dw1=dw1, dw2=dw2)
     torch.cuda.synchronize()
     ow1, ow2 = om.weight_grads(fw, bw)
     assert_close(_logical_dw1(dw1, wl), ow1, "dw1")
@@ -105,10 +101,10 @@ def test_wgrad_mxfp8_parity(case):
     mg.moe_grouped_mlp_wgrad(
         E=wl.E, H=wl.H, I=wl.I, M_cap=M_cap, gated=True,
         split_sizes=blk.split_sizes, padded_offsets=blk.padded_offsets,
-        prec=mg.PREC_MXFP8, dzT=blk.dzT_q, dzT_s=blk.dzT_s,
-        xpT=copies["xp"][0], xpT_s=copies["xp"][1],
-        dypT=copies["dyp"][0], dypT_s=copies["dyp"][1],
-        aT=blk.aT_q, aT_s=blk.aT_s, dw1=dw1, dw2=dw2)
+        prec=mg.PREC_MXFP8, dzT_q=blk.dzT_q, dzT_s=blk.dzT_s,
+        xpT_q=copies["xp"][0], xpT_s=copies["xp"][1],
+        dypT_q=copies["dyp"][0], dypT_s=copies["dyp"][1],
+        aT_q=blk.aT_q, aT_s=blk.aT_s, dw1=dw1, dw2=dw2)
     torch.cuda.synchronize()
 
     def deq(q, s_, R):     # a GPU MXFP8 copy [R][M_cap] -> its values
@@ -141,9 +137,9 @@ def test_wgrad_rejects_bad_arguments():
     pad = torch.zeros(wl.E + 1, **i32)
     t = torch.zeros(wl.H, M_cap, dtype=torch.bfloat16, device="cuda")
     base = dict(E=wl.E, H=wl.H, I=wl.I, M_cap=M_cap, split_sizes=split,
-                padded_offsets=pad, dypT=t, aT=t,
+                padded_offsets=pad, dyp=t, a=t,
                 dw2=torch.empty(wl.E, wl.H, wl.I, dtype=torch.bfloat16, device="cuda"))
-    for bad in (dict(M_cap=M_cap + 64), dict(H=100), dict(aT=None),
+    for bad in (dict(M_cap=M_cap + 64), dict(H=100), dict(a=None),
                 dict(prec=mg.PREC_MXFP8), dict(E=0)):
         with pytest.raises(mg.MoeError):
             mg.moe_grouped_mlp_wgrad(**{**base, **bad})
