@@ -12,7 +12,8 @@ MXFP8 operands and the epilogues also write MXFP8 copies (rowwise and
 transposed) of a and dz; the MXFP8 weight copies are made once, outside the
 step (once per weight update), and timed on their own.  Inputs are
 synthetic (seeded), already resident in HBM when the timed region starts.
-The value is algorithmic GEMM TFLOP/s of the step: 12 * M * H * I flops
+The value is algorithmic GEMM TFLOP/s of the step: 12 * M * H * I flops (18 with
+--wgrad, which adds the weight-gradient GEMMs)
 (M = routed rows; no padding counted).
 
 Prints one JSON line (stdout).  Progress goes to stderr.
@@ -182,6 +183,9 @@ def main():
                     help="operand precision (default: the config's)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--wgrad", action="store_true",
+                    help="add the weight-gradient grouped GEMMs (dW1, dW2) to the "
+                         "step: a full training step of the layer")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before timing, run one device copy of this many MB "
                          "(a known-size kernel for scaling HBM counters)")
@@ -207,7 +211,7 @@ def main():
     act_kind = {"swiglu": mg.ACT_SWIGLU, "geglu": mg.ACT_GEGLU, "srelu": mg.ACT_SRELU}[cfg["act"]]
     act = mg.act_params(act_kind, beta=cfg["beta"], clamp=cfg["clamp"])
     blk = mg.ExpertBlock(E, H, I, T, k, act=act,
-                         prec=mg.PREC_MXFP8 if mx else mg.PREC_BF16)
+                         prec=mg.PREC_MXFP8 if mx else mg.PREC_BF16, wgrad=args.wgrad)
     blk.load_weights(w1, w2)
     del w1, w2
     torch.cuda.synchronize()
@@ -216,12 +220,15 @@ def main():
     n1 = 2 * I if gated else I
     flops = {"fc1": 2.0 * M * H * n1, "fc2": 2.0 * M * H * I,
              "fc2_dgrad": 2.0 * M * H * I, "fc1_dgrad": 2.0 * M * H * n1}
+    if args.wgrad:
+        flops.update(wgrad_dw1=2.0 * M * H * n1, wgrad_dw2=2.0 * M * H * I)
     flops_step = sum(flops.values())
     stream = torch.cuda.current_stream().cuda_stream
 
     # events per step: 0 start, 1-3 forward GEMMs (library), 4 after
-    # unpermute, 5-7 backward GEMMs (library), 8 after dX unpermute
-    n_ev = 9
+    # unpermute, 5-7 backward GEMMs (library), 8 after dX unpermute; with
+    # --wgrad 9-11 around the weight-gradient GEMMs (library)
+    n_ev = 12 if args.wgrad else 9
 
     def step(evs=None, base=0):
         if evs is not None:
@@ -233,7 +240,7 @@ def main():
         if evs is not None:
             evs.record(base + 4, stream)
         if mx:
-            blk.gather(dout, None, blk.dyp_q, blk.dyp_s)
+            blk.gather(dout, blk.dyp, blk.dyp_q, blk.dyp_s)
         else:
             blk.gather(dout, blk.dyp)
         blk.experts_backward(None if evs is None else
@@ -241,6 +248,9 @@ def main():
         blk.combine(blk.dxp, blk.dx, dprobs=True)
         if evs is not None:
             evs.record(base + 8, stream)
+        if args.wgrad:
+            blk.weight_grads(None if evs is None else
+                             [evs.ev[base + 9], evs.ev[base + 10], evs.ev[base + 11]])
 
     if args.calib_copy_mb:
         n = args.calib_copy_mb << 20
@@ -272,6 +282,8 @@ def main():
     seg_ms = {"route_permute_x": seg(0, 1), "fc1": seg(1, 2), "fc2": seg(2, 3),
               "unpermute_out": seg(3, 4), "permute_dout": seg(4, 5),
               "fc2_dgrad": seg(5, 6), "fc1_dgrad": seg(6, 7), "unpermute_dx": seg(7, 8)}
+    if args.wgrad:
+        seg_ms.update(wgrad_quantize=seg(8, 9), wgrad_dw1=seg(9, 10), wgrad_dw2=seg(10, 11))
     evs.close()
     assert int(blk.err_flag.cpu()[0]) == 0
     value = flops_step / (ms_step * 1e-3) / 1e12
@@ -281,13 +293,17 @@ def main():
     row_bytes = H * (1 + 1 / 32) if mx else 2 * H
     idx_bytes = T * k * 4 * 2 + T * k * 4 + M * 8
     kernels = {}
-    for name in ("fc1", "fc2", "fc2_dgrad", "fc1_dgrad"):
+    for name in ("fc1", "fc2", "fc2_dgrad", "fc1_dgrad") + (
+            ("wgrad_dw1", "wgrad_dw2") if args.wgrad else ()):
         kernels[name] = {"ms": round(seg_ms[name], 4), "unit": "TFLOP/s",
                          "rate": round(flops[name] / (seg_ms[name] * 1e-3) / 1e12, 2)}
     mem = {"route_permute_x": T * H * 2 + M * row_bytes + idx_bytes,
            "unpermute_out": M * H * 2 + T * H * 2 + T * k * 4,
            "permute_dout": T * H * 2 + M * row_bytes + T * k * 4,
            "unpermute_dx": M * H * 2 + T * H * 2 + T * k * 12}
+    if args.wgrad and mx:
+        # MXFP8 transposed copies of Xp and dYp (bf16 in, codes + scales out)
+        mem["wgrad_quantize"] = 2 * M * H * (2 + 1 + 1 / 32)
     for name, b in mem.items():
         kernels[name] = {"ms": round(seg_ms[name], 4), "unit": "GB/s",
                          "rate": round(b / (seg_ms[name] * 1e-3) / 1e9, 1)}
@@ -337,7 +353,8 @@ def main():
         "config": {"workload": f"{args.config} expert layer: E={E} top-{k} T={T} H={H} "
                                f"I={I} {cfg['act']} beta={cfg['beta']} clamp={cfg['clamp']}, "
                                f"{prec}, route+permute+FC1+FC2+unpermute and backward "
-                               f"(FC2 dgrad+dAct, FC1 dgrad, dX, dprobs)",
+                               f"(FC2 dgrad+dAct, FC1 dgrad, dX, dprobs"
+                               f"{', dW1, dW2' if args.wgrad else ''})",
                    "E": E, "k": k, "T": T, "H": H, "I": I, "routed_rows": M,
                    "prec": prec, "flops_per_step": flops_step},
         "kernels": kernels,

@@ -403,7 +403,7 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* args, void* stream);
  *       expert e and are read whole, so the pad rows there must encode zero
  *       (as the producers above write them).
  *   dw1 or dw2 may be NULL to skip that GEMM; the caller owns every buffer.
- *   Needs M_cap % 128 == 0 and M_cap <= 4194304; H, I multiples of 64.
+ *   Needs M_cap <= 4194304 (MXFP8: M_cap % 128 == 0); H, I multiples of 64.
  *   Invalid arguments return MOE_ERR_INVALID_ARG before any launch.
  *   timing_events: optional hipEvent_t handles recorded before dw1, between,
  *   and after dw2.

@@ -16,6 +16,12 @@ epilogues then write only the MXFP8 copies of a and dz that the next GEMMs
 (and weight-gradient GEMMs) read, unless bf16_copies=True also asks for the
 bf16 tensors.
 
+With wgrad=True, weight_grads() adds the weight-gradient grouped GEMMs
+(moe_grouped_mlp_wgrad): dW1 [E][N1][H] in the interleaved row order of w1i
+and dW2 [E][H][I].  bf16 reads dz, Xp, dYp and a as stored; MXFP8 reads the
+transposed copies of a and dz the epilogues wrote and makes those of Xp and
+dYp with moe_quantize_mxfp8 (the permutes then also keep bf16 Xp and dYp).
+
 No call reads device memory back or synchronises, so a whole step can be
 captured in a HIP graph.
 """
@@ -34,7 +40,8 @@ class ExpertBlock:
                  act: Optional[B.ActParams] = None, first_expert: int = 0,
                  M_cap: Optional[int] = None, cu_margin: int = 0,
                  prec: int = B.PREC_BF16, transposed_copies: bool = True,
-                 bf16_copies: Optional[bool] = None, device="cuda"):
+                 bf16_copies: Optional[bool] = None, wgrad: bool = False,
+                 device="cuda"):
         self.E, self.H, self.I, self.T, self.k = E, H, I, T, k
         self.act = act or B.act_params()
         self.gated = self.act.act != B.ACT_SRELU
@@ -105,6 +112,18 @@ class ExpertBlock:
         else:
             self.xp = torch.empty(M, H, **bf)
             self.dyp = torch.empty(M, H, **bf)
+        self.wgrad = wgrad
+        if wgrad:
+            if self.mx:
+                if not transposed_copies:
+                    raise ValueError("MXFP8 weight gradients read the transposed "
+                                     "copies of a and dz (transposed_copies=True)")
+                self.xp = torch.empty(M, H, **bf)
+                self.dyp = torch.empty(M, H, **bf)
+                self.xpT_q, self.xpT_s = mx_pair(H, M)
+                self.dypT_q, self.dypT_s = mx_pair(H, M)
+            self.dw1 = torch.empty(E, N1, H, **bf)
+            self.dw2 = torch.empty(E, H, I, **bf)
 
     # ------------------------------------------------------------ weights --
     def load_weights(self, w1: torch.Tensor, w2: torch.Tensor) -> None:
@@ -215,9 +234,33 @@ class ExpertBlock:
 
     def backward(self, dout, timing_events=None):
         if self.mx:
-            self.gather(dout, None, self.dyp_q, self.dyp_s)
+            self.gather(dout, self.dyp, self.dyp_q, self.dyp_s)
         else:
             self.gather(dout, self.dyp)
         self.experts_backward(timing_events)
         self.combine(self.dxp, self.dx, dprobs=True)
         return self.dx, self.dprobs
+
+    def weight_grads(self, timing_events=None):
+        """dW1 (rows in w1i's interleaved order) and dW2 of the last
+        forward + backward; needs wgrad=True."""
+        if not self.wgrad:
+            raise RuntimeError("ExpertBlock was built without wgrad=True")
+        kw = {}
+        if self.mx:
+            for src, q, s in ((self.xp, self.xpT_q, self.xpT_s),
+                              (self.dyp, self.dypT_q, self.dypT_s)):
+                B.moe_quantize_mxfp8(mode=B.QUANT_COL, batch=1, rows=self.M_cap,
+                                     cols=self.H, x=src, q=q, s=s)
+            kw = dict(dzT_q=self.dzT_q, dzT_s=self.dzT_s, xpT_q=self.xpT_q,
+                      xpT_s=self.xpT_s, dypT_q=self.dypT_q, dypT_s=self.dypT_s,
+                      aT_q=self.aT_q, aT_s=self.aT_s)
+        else:
+            kw = dict(dz=self.dz, xp=self.xp, dyp=self.dyp, a=self.a)
+        B.moe_grouped_mlp_wgrad(E=self.E, H=self.H, I=self.I, M_cap=self.M_cap,
+                                gated=self.gated, split_sizes=self.split_sizes,
+                                padded_offsets=self.padded_offsets,
+                                prec=self.prec, cu_margin=self.cu_margin,
+                                dw1=self.dw1, dw2=self.dw2,
+                                timing_events=timing_events, **kw)
+        return self.dw1, self.dw2

@@ -469,9 +469,10 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
 moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* a, void* stream) {
   if (!a) return MOE_ERR_INVALID_ARG;
   if (a->E < 1 || a->E > kMaxExperts || a->H < 64 || a->I < 64 || a->H % 64 != 0 ||
-      a->I % 64 != 0 || (a->gated != 0 && a->gated != 1) || a->M_cap < 128 ||
-      a->M_cap % 128 != 0 || a->M_cap > (int64_t{1} << 22) || a->cu_margin < 0)
+      a->I % 64 != 0 || (a->gated != 0 && a->gated != 1) || a->M_cap < 1 ||
+      a->M_cap > (int64_t{1} << 22) || a->cu_margin < 0)
     return MOE_ERR_INVALID_ARG;
+  if (a->prec == MOE_PREC_MXFP8 && a->M_cap % 128 != 0) return MOE_ERR_INVALID_ARG;
   if (!a->split_sizes || !a->padded_offsets) return MOE_ERR_INVALID_ARG;
   if (a->prec != MOE_PREC_BF16 && a->prec != MOE_PREC_MXFP8) return MOE_ERR_INVALID_ARG;
   const bool mx = a->prec == MOE_PREC_MXFP8;

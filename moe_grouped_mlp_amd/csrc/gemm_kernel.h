@@ -1074,9 +1074,10 @@ void grouped_gemm_kernel(GemmArgs g) {
       ti.orow0 = static_cast<int64_t>(ti.e) * g.wg_rows + ti.row0;
       ti.rows_valid = min(BM, g.wg_rows - m_t * BM);
       ti.rows_pad = ti.rows_valid;
-      // clamped to the copies' width, so inconsistent offsets read zeros
-      // (every stage then lies inside its row) instead of past a row's end
-      const int nk_all = g.K * kElem / kRowBytes;
+      // clamped to the stages of M_cap rows, so inconsistent offsets stay
+      // inside the operands (bf16 stages are 64 rows; a last partial one is
+      // cut by the row limit, and MXFP8 needs M_cap % 128 == 0)
+      const int nk_all = (g.K * kElem + kRowBytes - 1) / kRowBytes;
       ti.kbeg = min(max(s_pad[ti.e], 0) * kElem / kRowBytes, nk_all);
       ti.kend = min(ti.kbeg + (s_split[ti.e] * kElem + kRowBytes - 1) / kRowBytes, nk_all);
       return ti;

@@ -168,7 +168,8 @@ def test_wgrad_validation():
     assert _call("moe_grouped_mlp_wgrad", args()) == DEVICE
     assert _call("moe_grouped_mlp_wgrad", args(dw1=None, dz=None, xp=None)) == DEVICE
     assert _call("moe_grouped_mlp_wgrad", args(dw2=None, dyp=None, a=None)) == DEVICE
-    for bad in (dict(M_cap=1000), dict(M_cap=1 << 23), dict(H=96), dict(I=32),
+    assert _call("moe_grouped_mlp_wgrad", args(M_cap=1000)) == DEVICE   # bf16: any M_cap
+    for bad in (dict(M_cap=0), dict(M_cap=1 << 23), dict(H=96), dict(I=32),
                 dict(E=0), dict(gated=2), dict(prec=7), dict(cu_margin=-1),
                 dict(split_sizes=None), dict(padded_offsets=None), dict(a=None),
                 dict(xp=None), dict(prec=B.PREC_MXFP8),
@@ -182,6 +183,7 @@ def test_wgrad_validation():
     assert _call("moe_grouped_mlp_wgrad", args(**mx)) == DEVICE
     assert _call("moe_grouped_mlp_wgrad", args(**{**mx, "aT_s": None})) == INVALID
     assert _call("moe_grouped_mlp_wgrad", args(**{**mx, "xpT_q": None})) == INVALID
+    assert _call("moe_grouped_mlp_wgrad", args(**{**mx, "M_cap": 1000})) == INVALID
 
 
 def test_bwd_validation():

@@ -53,7 +53,8 @@ def _logical_dw1(dw1, wl):
 def test_wgrad_bf16_parity(case):
     kw = dict(CASES[case])
     wl = make_workload(kw.pop("name"), seed=3, **kw)
-    M_cap = _m_cap(wl)
+    # bf16 takes any M_cap (here T k + E (A - 1), as ExpertBlock allocates)
+    M_cap = wl.m_cap()
     blk = run_gpu_layer(wl, M_cap)
     fw, bw = oracle_layer(wl, M_cap)
     # rows the layer never wrote hold NaN: they must not be read
@@ -139,7 +140,34 @@ def test_wgrad_rejects_bad_arguments():
     base = dict(E=wl.E, H=wl.H, I=wl.I, M_cap=M_cap, split_sizes=split,
                 padded_offsets=pad, dyp=t, a=t,
                 dw2=torch.empty(wl.E, wl.H, wl.I, dtype=torch.bfloat16, device="cuda"))
-    for bad in (dict(M_cap=M_cap + 64), dict(H=100), dict(a=None),
+    for bad in (dict(M_cap=0), dict(H=100), dict(a=None),
                 dict(prec=mg.PREC_MXFP8), dict(E=0)):
         with pytest.raises(mg.MoeError):
             mg.moe_grouped_mlp_wgrad(**{**base, **bad})
+
+
+@pytest.mark.parametrize("prec", [mg.PREC_BF16, mg.PREC_MXFP8])
+def test_block_weight_grads(prec):
+    """ExpertBlock(wgrad=True).weight_grads() after a forward + backward: the
+    bf16 path against the oracle's bf16 weight gradients, the MXFP8 path
+    (transposed copies of Xp and dYp made by the block) against the MXFP8
+    oracle by relative L2 error."""
+    wl = make_workload("tiny", seed=8, E=8, k=2, T=1024, H=640, I=320)
+    M_cap = _m_cap(wl)
+    gp = mg.act_params(mg.ACT_SWIGLU, beta=wl.beta)
+    blk = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, act=gp, M_cap=M_cap,
+                         prec=prec, wgrad=True)
+    run_gpu_layer(wl, M_cap, block=blk)
+    dw1, dw2 = blk.weight_grads()
+    torch.cuda.synchronize()
+    mx = prec == mg.PREC_MXFP8
+    fw, bw = oracle_layer(wl, M_cap, mx=mx)
+    ow1, ow2 = om.weight_grads(fw, bw, mx=mx)
+    g1, g2 = _logical_dw1(dw1, wl), host_f64(dw2)
+    if mx:
+        for g, o, what in ((g1, ow1, "dw1"), (g2, ow2, "dw2")):
+            l2 = np.linalg.norm(g - o) / np.linalg.norm(o)
+            assert l2 <= MX_REL_L2, f"{what}: relative L2 error {l2:.3e}"
+    else:
+        assert_close(g1, ow1, "dw1")
+        assert_close(g2, ow2, "dw2")
