@@ -576,9 +576,7 @@ struct TileCtx {
 MOE_DEV void acc_hold(f32x16& v) { asm volatile("" : "+a"(v)); }
 
 // EPI_STORE: C = bf16(acc)
-// HOLD: keep each row block's accumulators in AGPRs until it is stored (the
-// bf16 kernels; with it the MXFP8 kernel's allocation spills inside its K
-// loop instead, so that one goes without).
+// HOLD: keep each row block's accumulators in AGPRs until it is stored.
 template <bool HOLD>
 MOE_DEV void epi_store(f32x16 (&acc)[4][4], uint16_t* __restrict__ C, int64_t ldc,
                        const TileCtx& t) {
@@ -1315,13 +1313,15 @@ void grouped_gemm_kernel(GemmArgs g) {
   // ---- persistent tile loop -------------------------------------------
   // Work items.  Tiles fill `full` = floor(total / G) whole rounds; when the
   // remaining tail tiles would leave at least half the grid idle in a last
-  // round, each tail tile is split along K into S parts (plain-store GEMMs
-  // with a workspace only).  Every workgroup derives the same split from the
-  // device-computed tile count, so the host never needs it.
+  // round, each tail tile is split along K into S parts (bf16 plain-store
+  // GEMMs with a workspace only: for MXFP8 the split measured no faster and
+  // its code made the allocator spill accumulators in the epilogue).  Every
+  // workgroup derives the same split from the device-computed tile count,
+  // so the host never needs it.
   const int full = (total / G) * G;
   const int tail = total - full;
   int S = 1;
-  if constexpr (EPI == EPI_STORE) {
+  if constexpr (EPI == EPI_STORE && !MX) {
     if (g.split_ws && tail > 0 && 2 * tail <= G) {
       S = min(min(G / tail, g.split_max), max(1, nk / max(1, g.split_min_k)));
       if (tail * S > g.split_slots) S = max(1, g.split_slots / tail);
@@ -1407,13 +1407,13 @@ void grouped_gemm_kernel(GemmArgs g) {
     t.n_lane = wn * kWaveN + 4 * (lane >> 5);
     MxOut mo{g.mx_q, g.mx_s, g.mx_qT, g.mx_sT, g.mx_n, g.M_cap};
     if constexpr (EPI == EPI_STORE || EPI == EPI_WGRAD) {
-      if (split) {
+      if (!MX && split) {
         // partial tile to slot (t0.slot, part); the part that arrives last
         // sums all S partials in part order (deterministic) and stores
         float4* ws = reinterpret_cast<float4*>(g.split_ws) +
                      static_cast<int64_t>(t0.slot * S + t0.part) * (64 * kThreads);
         sfor<4>([&](auto mi) { sfor<4>([&](auto ni) {
-          if constexpr (!MX) acc_hold(acc[mi][ni]);
+          acc_hold(acc[mi][ni]);
           sfor<4>([&](auto q) {
             const f32x16& a = acc[mi][ni];
             ws[((mi * 4 + ni) * 4 + q) * kThreads + tid] =
@@ -1442,11 +1442,11 @@ void grouped_gemm_kernel(GemmArgs g) {
               acc[mi][ni][4 * q + 3] += v.w;
             }); }); });
           }
-          epi_store<!MX>(acc, g.C, g.ldc, t);
+          epi_store<true>(acc, g.C, g.ldc, t);
         }
         __syncthreads();   // s_tmp is read by every thread above
       } else {
-        epi_store<!MX>(acc, g.C, g.ldc, t);
+        epi_store<true>(acc, g.C, g.ldc, t);
       }
     } else if constexpr (EPI == EPI_GLU) {
       float amax;

@@ -186,15 +186,17 @@ def test_layer_mx_parity(case):
     assert int(blk.err_flag.cpu()[0]) == 0
 
 
-def test_layer_mx_split_k_tail_parity():
-    """MXFP8 operands through the split-K tail of FC2 and FC1 dgrad (a grid
-    of 8 workgroups over 26 output tiles)."""
+def test_layer_mx_partial_last_round_parity():
+    """MXFP8 plain-store GEMMs (FC2, FC1 dgrad) with a partial last round (a
+    grid of 8 workgroups over 26 output tiles): the tail tiles run whole (the
+    K split of the last round is bf16 only), results against the oracle."""
     wl = make_workload("tiny", seed=13, E=4, k=2, T=1536, H=512, I=512)
     M_cap = -(-wl.m_cap() // 128) * 128
     margin = torch.cuda.get_device_properties(0).multi_processor_count - 8
     G = gemm_grid(margin, M_cap, wl.E, wl.H)
     sizes = [int((wl.expert_idx == e).sum()) for e in range(wl.E)]
     assert G == 8
+    # the bf16 kernels would split this tail (the case stays a split-sized one)
     assert tail_split_parts(sizes, wl.H, wl.I, G, 128) > 1         # FC2
     assert tail_split_parts(sizes, wl.H, 2 * wl.I, G, 128) > 1     # FC1 dgrad
     gp, _ = act_of(wl)
