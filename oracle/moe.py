@@ -28,6 +28,7 @@ between:
              activations]; routing-probability scaling (ScaledSwiGLU)
              [TE § Challenge 3]
   unpermute  weighted combine by index-add [TE § Challenge 1]
+  router     softmax over the experts, top-k [TE § dense vs sparse MoE block, Fig. 1]
   wgrad      per-expert weight gradients dW1 = dZ^T Xp, dW2 = dYp^T a
              [FK § Overcoming training bottlenecks, Fig. 1]
   backward   FC2 dgrad + dActivation [FK § Overcoming training bottlenecks,
@@ -418,6 +419,28 @@ def backward(fw: Forward, dout_bits, w1_bits, w2_bits, prm: ActParams, *,
         bw.dz_mx = mx_quantize(dz[:mp], 1)
         bw.dzT_mx = mx_quantize(dz[:mp].T, 1)
     return bw
+
+
+# ================================================================ router ===
+def router_topk(logits: np.ndarray, k: int):
+    """Top-k router of the sparse MoE block: each token goes to k of the E
+    experts, whose outputs are combined weighted by the router's
+    probabilities [TE § the dense vs sparse MoE block, Fig. 1, a top-2 router
+    over eight experts].  Probabilities are the softmax of the token's logits
+    over all E experts, the k largest kept without renormalisation, in
+    descending order, ties to the lower expert id.  The selection compares
+    the fp32 logits themselves (softmax is monotone), so it is exact; the
+    kept probabilities are computed in float64 from them.
+
+    Returns (expert_idx int32 [T][k], probs float64 [T][k])."""
+    lg = np.asarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    x = lg.astype(np.float64)
+    p = np.exp(x - x.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    ids = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((ids, -x), axis=1)[:, :k]    # logit descending, then id
+    return order.astype(np.int32), np.take_along_axis(p, order, axis=1)
 
 
 # ======================================================= weight gradients ===

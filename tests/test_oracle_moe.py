@@ -380,3 +380,38 @@ def test_sampled_rows_equal_the_full_layer(act, mx):
                 np.testing.assert_array_equal(dz[0], bw.dz[r])
                 np.testing.assert_array_equal(dxp[0], bw.dxp[r])
                 assert dp[0] == bw.dp[r]
+
+
+# ---------------------------------------------------------------- router --
+def test_router_matches_brute_force():
+    """Pure-Python softmax and a full sort of (-logit, id) per token."""
+    import math
+    rng = np.random.default_rng(11)
+    for T, E, k in ((5, 4, 2), (7, 8, 2), (3, 16, 8), (4, 6, 6)):
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        lg[0, 1] = lg[0, 2]                      # a tie: the lower id first
+        idx, pr = moe.router_topk(lg, k)
+        for t in range(T):
+            row = [float(v) for v in lg[t]]
+            m = max(row)
+            z = sum(math.exp(v - m) for v in row)
+            best = sorted(range(E), key=lambda e: (-row[e], e))[:k]
+            assert list(idx[t]) == best
+            for j, e in enumerate(best):
+                assert abs(pr[t, j] - math.exp(row[e] - m) / z) <= 1e-15
+
+
+def test_router_closed_forms_and_invariants():
+    # equal logits: every probability 1/E, ids 0..k-1 (ties to the lower id)
+    idx, pr = moe.router_topk(np.full((3, 8), 0.7, np.float32), 2)
+    assert np.all(idx == [0, 1]) and np.allclose(pr, 1 / 8, rtol=0, atol=1e-16)
+    # k = E keeps the whole softmax: rows sum to 1, descending
+    rng = np.random.default_rng(12)
+    lg = (rng.standard_normal((50, 16)) * 3).astype(np.float32)
+    idx, pr = moe.router_topk(lg, 16)
+    assert np.allclose(pr.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    assert np.all(np.diff(pr, axis=1) <= 0)
+    assert all(sorted(r) == list(range(16)) for r in idx)
+    # shifting a token's logits by a constant changes nothing
+    i2, p2 = moe.router_topk(lg + np.float32(4.0), 16)
+    assert np.array_equal(i2, idx) and np.allclose(p2, pr, rtol=1e-6)
