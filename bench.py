@@ -323,6 +323,36 @@ def main():
         kernels["quantize_weights"] = {"ms": round(q_ms, 4), "unit": "GB/s",
                                        "rate": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
                                        "outside_step": True}
+    # the top-k router (softmax over the experts, top-k) on logits of the
+    # config's shape: outside the step, whose routing is an input
+    lg = torch.randn(T, E, device=dev, dtype=torch.float32)
+    r_idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    r_p = torch.empty(T, k, dtype=torch.float32, device=dev)
+    # a few microseconds of GPU work: launched from a captured graph so the
+    # host's launch overhead is not what is timed
+    reps = 20
+    gstream = torch.cuda.Stream()
+    gstream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gstream):
+        mg.moe_router_topk(T=T, E=E, k=k, logits=lg, expert_idx=r_idx, probs=r_p,
+                           stream=gstream.cuda_stream)
+        with torch.cuda.graph(graph, stream=gstream):
+            for _ in range(reps):
+                mg.moe_router_topk(T=T, E=E, k=k, logits=lg, expert_idx=r_idx,
+                                   probs=r_p, stream=gstream.cuda_stream)
+    torch.cuda.synchronize()
+    re = HipEvents(2)
+    re.record(0, stream)
+    graph.replay()
+    re.record(1, stream)
+    torch.cuda.synchronize()
+    r_ms = re.elapsed_ms(0, 1) / reps
+    re.close()
+    del graph
+    kernels["router_topk"] = {"ms": round(r_ms, 4), "unit": "GB/s",
+                              "rate": round((T * E * 4 + T * k * 8) / (r_ms * 1e-3) / 1e9, 1),
+                              "outside_step": True}
     fc1_ms = seg_ms["fc1"]
     achieved = flops["fc1"] / (fc1_ms * 1e-3) / 1e12
     log(f"step {ms_step:.3f} ms, {value:.1f} TFLOP/s; " +

@@ -428,6 +428,31 @@ typedef struct moe_wgrad_args {
 
 moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* args, void* stream);
 
+/* ------------------------------------------------------------------------
+ * moe_router_topk -- the top-k router of the sparse MoE block ([TE] Fig. 1:
+ *   a top-2 router sends each token to two of eight experts, whose outputs
+ *   are combined as a weighted sum; the layer's configs route by "softmax
+ *   then top-k").
+ *
+ *   For every token t: p = softmax(logits[t]) over all E experts (fp32);
+ *   expert_idx[t][0..k-1] = the experts of the k largest logits, in
+ *   descending order, ties to the lower id; probs[t][j] = p[expert_idx[t][j]]
+ *   (not renormalised).  The selection compares the logits themselves, so
+ *   it is exact.  These are the expert_idx / probs moe_permute takes.
+ *   logits float [T][E], expert_idx int32 [T][k], probs float [T][k], all
+ *   device memory owned by the caller; logits must be finite.
+ *   Needs T >= 1, 1 <= E <= 1024, 1 <= k <= min(E, 8); invalid arguments
+ *   return MOE_ERR_INVALID_ARG before any launch.
+ * ---------------------------------------------------------------------- */
+typedef struct moe_router_args {
+  int32_t T, E, k;
+  const float* logits;
+  int32_t* expert_idx;
+  float* probs;
+} moe_router_args;
+
+moe_status moe_router_topk(const moe_router_args* args, void* stream);
+
 /* Workspace bytes for these sizes: the backward needs at least the dprobs
  * partials (fp32 M_cap x ceil(I / 256)); the full size adds the area where
  * the plain-store GEMMs (FC2, FC1 dgrad) split their last, partial round of

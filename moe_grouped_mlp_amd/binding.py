@@ -28,6 +28,7 @@ EXPORTED_SYMBOLS = (
     "moe_weight_repack_interleave", "moe_permute_workspace_size",
     "moe_permute", "moe_unpermute", "moe_quantize_mxfp8",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_mlp_wgrad",
+    "moe_router_topk",
     "moe_grouped_mlp_workspace_size", "moe_status_string", "moe_gmlp_version",
     "moe_mx_scale_offset",
 )
@@ -109,6 +110,12 @@ class BwdArgs(ctypes.Structure):
                 ("dzT_q", c_void_p), ("dzT_s", c_void_p)]
 
 
+class RouterArgs(ctypes.Structure):
+    _fields_ = [("T", c_int32), ("E", c_int32), ("k", c_int32),
+                ("logits", c_void_p), ("expert_idx", c_void_p),
+                ("probs", c_void_p)]
+
+
 class WgradArgs(ctypes.Structure):
     _fields_ = [("E", c_int32), ("H", c_int32), ("I", c_int32),
                 ("gated", c_int32), ("M_cap", c_int64), ("prec", c_int32),
@@ -156,7 +163,8 @@ def lib() -> ctypes.CDLL:
                          ("moe_quantize_mxfp8", QuantArgs),
                          ("moe_grouped_mlp_fwd", FwdArgs),
                          ("moe_grouped_mlp_bwd", BwdArgs),
-                         ("moe_grouped_mlp_wgrad", WgradArgs)):
+                         ("moe_grouped_mlp_wgrad", WgradArgs),
+                         ("moe_router_topk", RouterArgs)):
             f = getattr(L, name)
             f.restype = c_int
             f.argtypes = [ctypes.POINTER(st), c_void_p]
@@ -304,3 +312,8 @@ def moe_grouped_mlp_wgrad(*, E, H, I, M_cap, split_sizes, padded_offsets,
                      _events(timing_events))
     _check("moe_grouped_mlp_wgrad",
            lib().moe_grouped_mlp_wgrad(ctypes.byref(args), _stream(stream)))
+
+
+def moe_router_topk(*, T, E, k, logits, expert_idx, probs, stream=None):
+    args = RouterArgs(T, E, k, _ptr(logits), _ptr(expert_idx), _ptr(probs))
+    _check("moe_router_topk", lib().moe_router_topk(ctypes.byref(args), _stream(stream)))

@@ -170,6 +170,20 @@ class ExpertBlock:
                       xp_s=self.xp_s if self.mx else None,
                       err_flag=self.err_flag, workspace=self.ws_route)
 
+    def route_logits(self, logits: torch.Tensor,
+                     x: Optional[torch.Tensor] = None) -> None:
+        """Top-k router on the device (softmax over the experts of fp32
+        logits [T][E_total], k largest, ties to the lower id) into
+        self.expert_idx / self.probs, then route() on them."""
+        T, E_all = logits.shape
+        if not hasattr(self, "expert_idx"):
+            dev = logits.device
+            self.expert_idx = torch.empty(T, self.k, dtype=torch.int32, device=dev)
+            self.probs = torch.empty(T, self.k, dtype=torch.float32, device=dev)
+        B.moe_router_topk(T=T, E=E_all, k=self.k, logits=logits,
+                          expert_idx=self.expert_idx, probs=self.probs)
+        self.route(self.expert_idx, self.probs, x)
+
     def gather(self, src: torch.Tensor, dst: Optional[torch.Tensor],
                dst_q: Optional[torch.Tensor] = None,
                dst_s: Optional[torch.Tensor] = None) -> None:

@@ -466,6 +466,17 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
   return MOE_OK;
 }
 
+moe_status moe_router_topk(const moe_router_args* a, void* stream) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  if (a->T < 1 || a->E < 1 || a->E > kMaxExperts || a->k < 1 || a->k > kMaxTopK ||
+      a->k > a->E || !a->logits || !a->expert_idx || !a->probs)
+    return MOE_ERR_INVALID_ARG;
+  int cu = 0;
+  if (moe_status st = device_info(&cu)) return st;
+  return launched(moe::launch_router_topk(a->logits, a->T, a->E, a->k, a->expert_idx, a->probs,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* a, void* stream) {
   if (!a) return MOE_ERR_INVALID_ARG;
   if (a->E < 1 || a->E > kMaxExperts || a->H < 64 || a->I < 64 || a->H % 64 != 0 ||

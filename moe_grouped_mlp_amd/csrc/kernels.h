@@ -31,6 +31,8 @@ hipError_t launch_repack_interleave(const void* src, void* dst, int E, int I,
                                     int H, int block, int inverse, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const moe_quant_args& a, hipStream_t s);
+hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t* idx,
+                              float* probs, hipStream_t s);
 
 // ---- grouped GEMM --------------------------------------------------------
 // EPI_WGRAD: weight gradient C_e [P][Q] = sum over expert e's routed rows m

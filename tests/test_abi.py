@@ -50,6 +50,7 @@ STRUCTS = {
     "moe_fwd_args": B.FwdArgs,
     "moe_bwd_args": B.BwdArgs,
     "moe_wgrad_args": B.WgradArgs,
+    "moe_router_args": B.RouterArgs,
 }
 
 
@@ -153,6 +154,21 @@ def test_fwd_validation():
     assert _call("moe_grouped_mlp_fwd", _fwd_args(w1_stride=5)) == INVALID
     # z may be NULL (no backward follows)
     assert _call("moe_grouped_mlp_fwd", _fwd_args(z=None)) == DEVICE
+
+
+def test_router_validation():
+    def args(**kw):
+        a = B.RouterArgs(16, 8, 2, 64, 64, 64)
+        for f, v in kw.items():
+            setattr(a, f, v)
+        return a
+    assert _call("moe_router_topk", args()) == DEVICE
+    assert _call("moe_router_topk", args(E=1024, k=8)) == DEVICE
+    assert _call("moe_router_topk", args(E=3, k=3)) == DEVICE
+    for bad in (dict(T=0), dict(E=0), dict(E=1025), dict(k=0), dict(k=9),
+                dict(E=2, k=3), dict(logits=None), dict(expert_idx=None),
+                dict(probs=None)):
+        assert _call("moe_router_topk", args(**bad)) == INVALID, bad
 
 
 def test_wgrad_validation():
