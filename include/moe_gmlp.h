@@ -429,6 +429,65 @@ typedef struct moe_wgrad_args {
 moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* args, void* stream);
 
 /* ------------------------------------------------------------------------
+ * The unfused baseline: a plain grouped GEMM and separate activation passes,
+ * the layer as it runs without the fused epilogues ([FK] § "Overcoming
+ * training bottlenecks": unfused, activation and quantization are separate
+ * memory-bound kernels; Fig. 3 compares fused with unfused kernels).  The
+ * fused entry points above are the product; these measure what fusion buys.
+ *
+ * moe_grouped_gemm -- C[r] = bf16(A[r] . B_e^T) for every routed row r of
+ *   expert e (bf16, fp32 accumulation): A [M_cap][K], C [M_cap][N]; B_e at
+ *   b + e * b_stride, [N][K] (b_kn = 0) or [K][N] (b_kn = 1); pad rows of C
+ *   are not written.  Needs N, K multiples of 64.  workspace (optional, the
+ *   size moe_grouped_mlp_workspace_size gives) enables the K split of a
+ *   partial last round.
+ * ---------------------------------------------------------------------- */
+typedef struct moe_gemm_args {
+  int32_t E, N, K;
+  int64_t M_cap;
+  int32_t b_kn;
+  int32_t cu_margin;
+  const int32_t* split_sizes;
+  const int32_t* padded_offsets;
+  const void* a;
+  const void* b;
+  int64_t b_stride;               /* elements; 0: N * K */
+  void* c;
+  void* workspace;
+  size_t workspace_bytes;
+} moe_gemm_args;
+
+moe_status moe_grouped_gemm(const moe_gemm_args* args, void* stream);
+
+/* moe_glu_unfused -- the activation of the FC1 output as its own pass.
+ *   direction 0: a[r] = bf16(probs_p[r] * act(z[r])) and amax = max |a|
+ *     (amax optional; it is reset by the call);
+ *   direction 1: with dA = da[r]: dz[r] = bf16(dact(z[r], probs_p[r] dA))
+ *     and dprobs_p[r] = sum_j dA[j] s[j] (fixed order); pad rows get
+ *     dprobs_p 0.
+ *   Same meaning as the fused epilogues of moe_grouped_mlp_fwd / _bwd: z, dz
+ *   bf16 [M_cap][N1] in the interleaved column order (N1 = 2 I gated, I for
+ *   sReLU); a, da bf16 [M_cap][I].  Only rows holding data are written.
+ * ---------------------------------------------------------------------- */
+typedef struct moe_glu_args {
+  int32_t direction;
+  int32_t E, I;
+  int64_t M_cap;
+  moe_act_params act;
+  const int32_t* split_sizes;
+  const int32_t* padded_offsets;
+  const float* probs_p;
+  const void* z;
+  void* a;
+  float* amax;
+  const void* da;
+  void* dz;
+  float* dprobs_p;
+} moe_glu_args;
+
+moe_status moe_glu_unfused(const moe_glu_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_router_topk -- the top-k router of the sparse MoE block ([TE] Fig. 1:
  *   a top-2 router sends each token to two of eight experts, whose outputs
  *   are combined as a weighted sum; the layer's configs route by "softmax

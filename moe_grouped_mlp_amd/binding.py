@@ -28,7 +28,7 @@ EXPORTED_SYMBOLS = (
     "moe_weight_repack_interleave", "moe_permute_workspace_size",
     "moe_permute", "moe_unpermute", "moe_quantize_mxfp8",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_mlp_wgrad",
-    "moe_router_topk",
+    "moe_router_topk", "moe_grouped_gemm", "moe_glu_unfused",
     "moe_grouped_mlp_workspace_size", "moe_status_string", "moe_gmlp_version",
     "moe_mx_scale_offset",
 )
@@ -110,6 +110,24 @@ class BwdArgs(ctypes.Structure):
                 ("dzT_q", c_void_p), ("dzT_s", c_void_p)]
 
 
+class GemmArgs(ctypes.Structure):
+    _fields_ = [("E", c_int32), ("N", c_int32), ("K", c_int32),
+                ("M_cap", c_int64), ("b_kn", c_int32), ("cu_margin", c_int32),
+                ("split_sizes", c_void_p), ("padded_offsets", c_void_p),
+                ("a", c_void_p), ("b", c_void_p), ("b_stride", c_int64),
+                ("c", c_void_p), ("workspace", c_void_p),
+                ("workspace_bytes", c_size_t)]
+
+
+class GluArgs(ctypes.Structure):
+    _fields_ = [("direction", c_int32), ("E", c_int32), ("I", c_int32),
+                ("M_cap", c_int64), ("act", ActParams),
+                ("split_sizes", c_void_p), ("padded_offsets", c_void_p),
+                ("probs_p", c_void_p), ("z", c_void_p), ("a", c_void_p),
+                ("amax", c_void_p), ("da", c_void_p), ("dz", c_void_p),
+                ("dprobs_p", c_void_p)]
+
+
 class RouterArgs(ctypes.Structure):
     _fields_ = [("T", c_int32), ("E", c_int32), ("k", c_int32),
                 ("logits", c_void_p), ("expert_idx", c_void_p),
@@ -164,7 +182,9 @@ def lib() -> ctypes.CDLL:
                          ("moe_grouped_mlp_fwd", FwdArgs),
                          ("moe_grouped_mlp_bwd", BwdArgs),
                          ("moe_grouped_mlp_wgrad", WgradArgs),
-                         ("moe_router_topk", RouterArgs)):
+                         ("moe_router_topk", RouterArgs),
+                         ("moe_grouped_gemm", GemmArgs),
+                         ("moe_glu_unfused", GluArgs)):
             f = getattr(L, name)
             f.restype = c_int
             f.argtypes = [ctypes.POINTER(st), c_void_p]
@@ -317,3 +337,21 @@ def moe_grouped_mlp_wgrad(*, E, H, I, M_cap, split_sizes, padded_offsets,
 def moe_router_topk(*, T, E, k, logits, expert_idx, probs, stream=None):
     args = RouterArgs(T, E, k, _ptr(logits), _ptr(expert_idx), _ptr(probs))
     _check("moe_router_topk", lib().moe_router_topk(ctypes.byref(args), _stream(stream)))
+
+
+def moe_grouped_gemm(*, E, N, K, M_cap, split_sizes, padded_offsets, a, b, c,
+                     b_kn=False, b_stride=0, cu_margin=0, workspace=None,
+                     stream=None):
+    args = GemmArgs(E, N, K, M_cap, int(bool(b_kn)), cu_margin,
+                    _ptr(split_sizes), _ptr(padded_offsets), _ptr(a), _ptr(b),
+                    b_stride, _ptr(c), _ptr(workspace), _nbytes(workspace))
+    _check("moe_grouped_gemm", lib().moe_grouped_gemm(ctypes.byref(args), _stream(stream)))
+
+
+def moe_glu_unfused(*, direction, E, I, M_cap, split_sizes, padded_offsets,
+                    probs_p, z, act=None, a=None, amax=None, da=None, dz=None,
+                    dprobs_p=None, stream=None):
+    args = GluArgs(direction, E, I, M_cap, act or act_params(), _ptr(split_sizes),
+                   _ptr(padded_offsets), _ptr(probs_p), _ptr(z), _ptr(a),
+                   _ptr(amax), _ptr(da), _ptr(dz), _ptr(dprobs_p))
+    _check("moe_glu_unfused", lib().moe_glu_unfused(ctypes.byref(args), _stream(stream)))

@@ -255,6 +255,53 @@ class ExpertBlock:
         self.combine(self.dxp, self.dx, dprobs=True)
         return self.dx, self.dprobs
 
+    # ------------------------------------------------- unfused baseline --
+    # The same layer without the fused epilogues (bf16): FC1 and FC2 dgrad as
+    # plain grouped GEMMs, the activation and its gradient as separate passes
+    # (moe_glu_unfused).  It measures what the fused path gains; outputs have
+    # the meaning of the fused ones (dA is stored in bf16 in between).
+    def experts_forward_unfused(self, events=None) -> None:
+        if self.mx:
+            raise NotImplementedError("the unfused baseline is bf16")
+        g = dict(E=self.E, M_cap=self.M_cap, split_sizes=self.split_sizes,
+                 padded_offsets=self.padded_offsets, cu_margin=self.cu_margin,
+                 workspace=self.ws)
+        rec = (lambda i: events.record(i)) if events else (lambda i: None)
+        rec(0)
+        B.moe_grouped_gemm(N=self.N1, K=self.H, a=self.xp, b=self.w1i, c=self.z, **g)
+        rec(1)
+        B.moe_glu_unfused(direction=0, E=self.E, I=self.I, M_cap=self.M_cap,
+                          split_sizes=self.split_sizes,
+                          padded_offsets=self.padded_offsets, probs_p=self.probs_p,
+                          z=self.z, a=self.a, amax=self.amax, act=self.act)
+        rec(2)
+        B.moe_grouped_gemm(N=self.H, K=self.I, a=self.a, b=self.w2, c=self.yp, **g)
+        rec(3)
+
+    def experts_backward_unfused(self, events=None) -> None:
+        if self.mx:
+            raise NotImplementedError("the unfused baseline is bf16")
+        if getattr(self, "da", None) is None:
+            self.da = torch.empty(self.M_cap, self.I, dtype=torch.bfloat16,
+                                  device=self.z.device)
+        g = dict(E=self.E, M_cap=self.M_cap, split_sizes=self.split_sizes,
+                 padded_offsets=self.padded_offsets, cu_margin=self.cu_margin,
+                 workspace=self.ws)
+        rec = (lambda i: events.record(i)) if events else (lambda i: None)
+        rec(0)
+        B.moe_grouped_gemm(N=self.I, K=self.H, a=self.dyp, b=self.w2, b_kn=True,
+                           c=self.da, **g)
+        rec(1)
+        B.moe_glu_unfused(direction=1, E=self.E, I=self.I, M_cap=self.M_cap,
+                          split_sizes=self.split_sizes,
+                          padded_offsets=self.padded_offsets, probs_p=self.probs_p,
+                          z=self.z, da=self.da, dz=self.dz,
+                          dprobs_p=self.dprobs_p, act=self.act)
+        rec(2)
+        B.moe_grouped_gemm(N=self.H, K=self.N1, a=self.dz, b=self.w1i, b_kn=True,
+                           c=self.dxp, **g)
+        rec(3)
+
     def weight_grads(self, timing_events=None):
         """dW1 (rows in w1i's interleaved order) and dW2 of the last
         forward + backward; needs wgrad=True."""

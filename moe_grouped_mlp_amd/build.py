@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_gmlp.so")
 
-SOURCES = ["api.cpp", "route.hip", "router.hip", "permute.hip", "quant.hip", "gemm.hip", "gemm_store.hip",
+SOURCES = ["api.cpp", "route.hip", "router.hip", "unfused.hip", "permute.hip", "quant.hip", "gemm.hip", "gemm_store.hip",
            "gemm_glu_bf16.hip", "gemm_glu_mx.hip", "gemm_dglu_bf16.hip", "gemm_dglu_mx.hip", "gemm_wgrad.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -466,6 +466,57 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
   return MOE_OK;
 }
 
+moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  if (a->E < 1 || a->E > kMaxExperts || a->N < 64 || a->K < 64 || a->N % 64 != 0 ||
+      a->K % 64 != 0 || a->M_cap < 1 || a->M_cap > INT32_MAX || a->cu_margin < 0 ||
+      (a->b_kn != 0 && a->b_kn != 1) || !a->split_sizes || !a->padded_offsets || !a->a ||
+      !a->b || !a->c)
+    return MOE_ERR_INVALID_ARG;
+  if (a->b_stride != 0 && a->b_stride < static_cast<int64_t>(a->N) * a->K)
+    return MOE_ERR_INVALID_ARG;
+  int cu = 0;
+  if (moe_status st = device_info(&cu)) return st;
+  if (a->cu_margin >= cu) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  moe::GemmArgs g{};
+  g.E = a->E;
+  g.N = a->N;
+  g.K = a->K;
+  g.M_cap = a->M_cap;
+  g.split = a->split_sizes;
+  g.padded = a->padded_offsets;
+  g.A = a->a;
+  g.B = a->b;
+  g.b_stride = a->b_stride ? a->b_stride : static_cast<int64_t>(a->N) * a->K;
+  g.group_m = tuning().group_m;
+  g.k_rot_stride = tuning().k_rot;
+  g.C = static_cast<uint16_t*>(a->c);
+  g.ldc = a->N;
+  const int grid = gemm_grid(cu, a->cu_margin, a->M_cap, a->E, a->N);
+  if (moe_status st = attach_split(g, a->workspace, a->workspace_bytes, 0, grid, s)) return st;
+  return launched(moe::launch_grouped_gemm(g, moe::EPI_STORE, a->b_kn != 0, false, grid, s));
+}
+
+moe_status moe_glu_unfused(const moe_glu_args* a, void* stream) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  if ((a->direction != 0 && a->direction != 1) || a->E < 1 || a->E > kMaxExperts ||
+      a->I < 64 || a->I % 64 != 0 || a->M_cap < 1 || a->M_cap > INT32_MAX || !act_ok(a->act) ||
+      !a->split_sizes || !a->padded_offsets || !a->probs_p || !a->z)
+    return MOE_ERR_INVALID_ARG;
+  if (a->direction == 0 && !a->a) return MOE_ERR_INVALID_ARG;
+  if (a->direction == 1 && (!a->da || !a->dz || !a->dprobs_p)) return MOE_ERR_INVALID_ARG;
+  int cu = 0;
+  if (moe_status st = device_info(&cu)) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a->direction == 0 && a->amax) {
+    if (moe_status st = launched(moe::launch_fill_f32(a->amax, 0.0f, 1, s))) return st;
+  }
+  return launched(moe::launch_glu_unfused(a->direction, a->split_sizes, a->padded_offsets, a->E,
+                                          a->I, a->M_cap, moe::to_actp(a->act), a->probs_p,
+                                          a->z, a->a, a->amax, a->da, a->dz, a->dprobs_p, s));
+}
+
 moe_status moe_router_topk(const moe_router_args* a, void* stream) {
   if (!a) return MOE_ERR_INVALID_ARG;
   if (a->T < 1 || a->E < 1 || a->E > kMaxExperts || a->k < 1 || a->k > kMaxTopK ||

@@ -31,6 +31,11 @@ hipError_t launch_repack_interleave(const void* src, void* dst, int E, int I,
                                     int H, int block, int inverse, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const moe_quant_args& a, hipStream_t s);
+// direction 0: a = bf16(p * act(z)) (+ amax); 1: dz, dprobs from dA and z
+hipError_t launch_glu_unfused(int direction, const int32_t* split, const int32_t* padded, int E,
+                              int I, int64_t rows, const ActP& act, const float* probs,
+                              const void* z, void* a, float* amax, const void* da, void* dz,
+                              float* dprobs, hipStream_t s);
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t* idx,
                               float* probs, hipStream_t s);
 

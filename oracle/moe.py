@@ -325,7 +325,7 @@ def _mx_operand(v, axis, on):
 
 def forward(x_bits, w1_bits, w2_bits, expert_idx, probs, E, prm: ActParams,
             *, first_expert=0, M_cap=None, mx=False, exact=False,
-            bias1=None) -> Forward:
+            bias1=None, unfused=False) -> Forward:
     """Fused grouped-MLP forward, expert by expert.
 
     x_bits   uint16 bf16 [T][H]
@@ -335,6 +335,10 @@ def forward(x_bits, w1_bits, w2_bits, expert_idx, probs, E, prm: ActParams,
     mx       feed MXFP8 operands to both GEMMs (blocks of 32 along K)
     exact    skip every bf16/MX storage rounding (pure float64; used by the
              finite-difference pins)
+    unfused  the layer run as separate kernels, each reading what the one
+             before stored: the activation takes the stored (bf16) z instead
+             of FC1's unrounded result [FK § Overcoming training bottlenecks:
+             unfused, the activation is a separate kernel after the GEMM]
     """
     rnd = not exact
     rt = route(expert_idx, probs, E, first_expert, M_cap)
@@ -359,7 +363,8 @@ def forward(x_bits, w1_bits, w2_bits, expert_idx, probs, E, prm: ActParams,
         w1e = _mx_operand(w1[e], 1, mx and rnd)
         ze = xe @ w1e.T                                      # FC1
         b = None if bias1 is None else bias1[e]
-        ae = pp[rows, None] * act_forward(ze, prm, b)        # act + prob scale
+        ain_z = _maybe_bf16(ze, rnd) if unfused else ze
+        ae = pp[rows, None] * act_forward(ain_z, prm, b)     # act + prob scale
         z[rows] = _maybe_bf16(ze, rnd)
         a[rows] = _maybe_bf16(ae, rnd)
         ain = _mx_operand(a[rows], 1, mx and rnd)
@@ -378,8 +383,9 @@ def forward(x_bits, w1_bits, w2_bits, expert_idx, probs, E, prm: ActParams,
 
 
 def backward(fw: Forward, dout_bits, w1_bits, w2_bits, prm: ActParams, *,
-             mx=False, exact=False, bias1=None) -> Backward:
-    """Backward of `forward` for the loss sum(out * dOut)."""
+             mx=False, exact=False, bias1=None, unfused=False) -> Backward:
+    """Backward of `forward` for the loss sum(out * dOut).  unfused: FC2
+    dgrad stores dA (bf16) and the activation gradient reads it."""
     rnd = not exact
     rt = fw.rt
     E = len(rt.split_sizes)
@@ -402,6 +408,8 @@ def backward(fw: Forward, dout_bits, w1_bits, w2_bits, prm: ActParams, *,
         dye = _mx_operand(dyp[rows], 1, mx and rnd)          # along H
         w2e = _mx_operand(w2[e], 0, mx and rnd)              # along H
         da = dye @ w2e                                       # FC2 dgrad
+        if unfused:
+            da = _maybe_bf16(da, rnd)
         b = None if bias1 is None else bias1[e]
         ze = fw.z[rows]
         s = act_forward(ze, prm, b)

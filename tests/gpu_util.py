@@ -114,11 +114,12 @@ def uninterleave_cols(packed: np.ndarray, I: int) -> np.ndarray:
     return out
 
 
-def oracle_layer(wl, M_cap, backward=True, mx=False):
+def oracle_layer(wl, M_cap, backward=True, mx=False, unfused=False):
     _, op = act_of(wl)
     fw = om.forward(wl.x, wl.w1, wl.w2, wl.expert_idx, wl.probs, wl.E, op,
-                    first_expert=wl.first_expert, M_cap=M_cap, mx=mx)
-    bw = om.backward(fw, wl.dout, wl.w1, wl.w2, op, mx=mx) if backward else None
+                    first_expert=wl.first_expert, M_cap=M_cap, mx=mx, unfused=unfused)
+    bw = om.backward(fw, wl.dout, wl.w1, wl.w2, op, mx=mx,
+                     unfused=unfused) if backward else None
     return fw, bw
 
 

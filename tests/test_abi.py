@@ -51,6 +51,8 @@ STRUCTS = {
     "moe_bwd_args": B.BwdArgs,
     "moe_wgrad_args": B.WgradArgs,
     "moe_router_args": B.RouterArgs,
+    "moe_gemm_args": B.GemmArgs,
+    "moe_glu_args": B.GluArgs,
 }
 
 
@@ -154,6 +156,36 @@ def test_fwd_validation():
     assert _call("moe_grouped_mlp_fwd", _fwd_args(w1_stride=5)) == INVALID
     # z may be NULL (no backward follows)
     assert _call("moe_grouped_mlp_fwd", _fwd_args(z=None)) == DEVICE
+
+
+def test_unfused_baseline_validation():
+    def gemm(**kw):
+        a = B.GemmArgs(4, 256, 128, 1024, 0, 0, 64, 64, 64, 64, 0, 64, None, 0)
+        for f, v in kw.items():
+            setattr(a, f, v)
+        return a
+    assert _call("moe_grouped_gemm", gemm()) == DEVICE
+    assert _call("moe_grouped_gemm", gemm(b_kn=1, b_stride=256 * 128)) == DEVICE
+    for bad in (dict(N=100), dict(K=32), dict(E=0), dict(b_kn=2), dict(a=None),
+                dict(c=None), dict(b_stride=5), dict(cu_margin=-1), dict(M_cap=0)):
+        assert _call("moe_grouped_gemm", gemm(**bad)) == INVALID, bad
+
+    def glu(**kw):
+        a = B.GluArgs()
+        a.direction, a.E, a.I, a.M_cap = 0, 4, 256, 1024
+        a.act = B.act_params()
+        for f in ("split_sizes", "padded_offsets", "probs_p", "z", "a", "da", "dz",
+                  "dprobs_p"):
+            setattr(a, f, 64)
+        for f, v in kw.items():
+            setattr(a, f, v)
+        return a
+    assert _call("moe_glu_unfused", glu()) == DEVICE
+    assert _call("moe_glu_unfused", glu(direction=1, a=None)) == DEVICE
+    for bad in (dict(direction=2), dict(I=96), dict(z=None), dict(a=None),
+                dict(direction=1, dz=None), dict(direction=1, da=None),
+                dict(act=B.act_params(gate_lo=1.0, gate_hi=-1.0))):
+        assert _call("moe_glu_unfused", glu(**bad)) == INVALID, bad
 
 
 def test_router_validation():

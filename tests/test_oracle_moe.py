@@ -415,3 +415,25 @@ def test_router_closed_forms_and_invariants():
     # shifting a token's logits by a constant changes nothing
     i2, p2 = moe.router_topk(lg + np.float32(4.0), 16)
     assert np.array_equal(i2, idx) and np.allclose(p2, pr, rtol=1e-6)
+
+
+def test_unfused_reading_only_moves_rounding_points():
+    """The unfused layer differs from the fused one only in where values are
+    rounded to bf16: with rounding off both are the same float64 layer, and
+    with rounding on the unfused activation equals the fused formula applied
+    to the stored z."""
+    wl = make_workload("tiny", T=64, H=32, I=64, E=4)
+    prm = moe.ActParams()
+    f0 = moe.forward(wl.x, wl.w1, wl.w2, wl.expert_idx, wl.probs, wl.E, prm, exact=True)
+    f1 = moe.forward(wl.x, wl.w1, wl.w2, wl.expert_idx, wl.probs, wl.E, prm, exact=True,
+                     unfused=True)
+    b0 = moe.backward(f0, wl.dout, wl.w1, wl.w2, prm, exact=True)
+    b1 = moe.backward(f1, wl.dout, wl.w1, wl.w2, prm, exact=True, unfused=True)
+    for u, v in ((f0.a, f1.a), (f0.out, f1.out), (b0.dz, b1.dz), (b0.dx, b1.dx),
+                 (b0.dprobs, b1.dprobs)):
+        np.testing.assert_array_equal(u, v)
+    fr = moe.forward(wl.x, wl.w1, wl.w2, wl.expert_idx, wl.probs, wl.E, prm, unfused=True)
+    v = fr.expert >= 0
+    pp = fr.rt.probs_p.astype(np.float64)[v, None]
+    expect = nu.round_bf16(pp * moe.act_forward(fr.z[v], prm))
+    np.testing.assert_array_equal(fr.a[v], expect)
