@@ -183,6 +183,9 @@ def main():
                     help="operand precision (default: the config's)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="the unfused baseline (bf16): plain grouped GEMMs with the "
+                         "activation and its gradient as separate passes")
     ap.add_argument("--wgrad", action="store_true",
                     help="add the weight-gradient grouped GEMMs (dW1, dW2) to the "
                          "step: a full training step of the layer")
@@ -202,6 +205,10 @@ def main():
     wl_name, prec_default = BENCH_CONFIGS[args.config]
     prec = args.prec or prec_default
     mx = prec == "mxfp8"
+    if args.unfused and (mx or args.wgrad):
+        print("--unfused is the bf16 baseline of the fused step (no MXFP8, no --wgrad)",
+              file=sys.stderr)
+        sys.exit(2)
     cfg = dict(CONFIGS[wl_name])
     E, k, T, H, I = (cfg[n] for n in ("E", "k", "T", "H", "I"))
     dev = torch.device("cuda:0")
@@ -229,8 +236,35 @@ def main():
     # unpermute, 5-7 backward GEMMs (library), 8 after dX unpermute; with
     # --wgrad 9-11 around the weight-gradient GEMMs (library)
     n_ev = 12 if args.wgrad else 9
+    if args.unfused:
+        n_ev = 11
+
+    class _Rec:   # events of one step, recorded on the library's stream
+        def __init__(self, evs, base):
+            self.evs, self.base = evs, base
+
+        def record(self, i):
+            self.evs.record(self.base + i, stream)
+
+    def step_unfused(evs=None, base=0):
+        # 0 start; 1-4 forward GEMM / act / GEMM boundaries; 5 after the
+        # unpermute; 6-9 backward boundaries; 10 after the dX unpermute
+        if evs is not None:
+            evs.record(base + 0, stream)
+        blk.route(idx, probs, x)
+        blk.experts_forward_unfused(None if evs is None else _Rec(evs, base + 1))
+        blk.combine(blk.yp, blk.out)
+        if evs is not None:
+            evs.record(base + 5, stream)
+        blk.gather(dout, blk.dyp)
+        blk.experts_backward_unfused(None if evs is None else _Rec(evs, base + 6))
+        blk.combine(blk.dxp, blk.dx, dprobs=True)
+        if evs is not None:
+            evs.record(base + 10, stream)
 
     def step(evs=None, base=0):
+        if args.unfused:
+            return step_unfused(evs, base)
         if evs is not None:
             evs.record(base + 0, stream)
         blk.route(idx, probs, x)
@@ -279,9 +313,15 @@ def main():
     def seg(a, b):
         return sum(evs.elapsed_ms(n_ev * i + a, n_ev * i + b) for i in range(args.steps)) / args.steps
 
-    seg_ms = {"route_permute_x": seg(0, 1), "fc1": seg(1, 2), "fc2": seg(2, 3),
-              "unpermute_out": seg(3, 4), "permute_dout": seg(4, 5),
-              "fc2_dgrad": seg(5, 6), "fc1_dgrad": seg(6, 7), "unpermute_dx": seg(7, 8)}
+    if args.unfused:
+        seg_ms = {"route_permute_x": seg(0, 1), "fc1": seg(1, 2), "act_fwd": seg(2, 3),
+                  "fc2": seg(3, 4), "unpermute_out": seg(4, 5), "permute_dout": seg(5, 6),
+                  "fc2_dgrad": seg(6, 7), "act_bwd": seg(7, 8), "fc1_dgrad": seg(8, 9),
+                  "unpermute_dx": seg(9, 10)}
+    else:
+        seg_ms = {"route_permute_x": seg(0, 1), "fc1": seg(1, 2), "fc2": seg(2, 3),
+                  "unpermute_out": seg(3, 4), "permute_dout": seg(4, 5),
+                  "fc2_dgrad": seg(5, 6), "fc1_dgrad": seg(6, 7), "unpermute_dx": seg(7, 8)}
     if args.wgrad:
         seg_ms.update(wgrad_quantize=seg(8, 9), wgrad_dw1=seg(9, 10), wgrad_dw2=seg(10, 11))
     evs.close()
@@ -301,6 +341,10 @@ def main():
            "unpermute_out": M * H * 2 + T * H * 2 + T * k * 4,
            "permute_dout": T * H * 2 + M * row_bytes + T * k * 4,
            "unpermute_dx": M * H * 2 + T * H * 2 + T * k * 12}
+    if args.unfused:
+        # the separate activation passes: z in, a out; dA and z in, dz out
+        mem["act_fwd"] = M * n1 * 2 + M * I * 2
+        mem["act_bwd"] = M * I * 2 + 2 * M * n1 * 2 + M * 4
     if args.wgrad and mx:
         # MXFP8 transposed copies of Xp and dYp (bf16 in, codes + scales out)
         mem["wgrad_quantize"] = 2 * M * H * (2 + 1 + 1 / 32)
@@ -384,7 +428,8 @@ def main():
                                f"I={I} {cfg['act']} beta={cfg['beta']} clamp={cfg['clamp']}, "
                                f"{prec}, route+permute+FC1+FC2+unpermute and backward "
                                f"(FC2 dgrad+dAct, FC1 dgrad, dX, dprobs"
-                               f"{', dW1, dW2' if args.wgrad else ''})",
+                               f"{', dW1, dW2' if args.wgrad else ''})"
+                               f"{'; unfused baseline (plain GEMMs + separate activation passes)' if args.unfused else ''}",
                    "E": E, "k": k, "T": T, "H": H, "I": I, "routed_rows": M,
                    "prec": prec, "flops_per_step": flops_step},
         "kernels": kernels,

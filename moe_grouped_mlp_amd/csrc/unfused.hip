@@ -174,7 +174,9 @@ hipError_t launch_glu_unfused(int direction, const int32_t* split, const int32_t
                               int I, int64_t rows, const ActP& act, const float* probs,
                               const void* z, void* a, float* amax, const void* da, void* dz,
                               float* dprobs, hipStream_t s) {
-  const int blocks = static_cast<int>(rows < 65536 ? rows : 65536);
+  // a bounded grid striding over the rows: the forward pass ends with one
+  // amax atomic per workgroup, which contend on one address
+  const int blocks = static_cast<int>(rows < 2048 ? rows : 2048);
   const dim3 grd(blocks > 0 ? blocks : 1), blk(kGluThreads);
   const auto* zz = static_cast<const uint16_t*>(z);
 #define MOE_GLU_CASE(ACT)                                                                  \
