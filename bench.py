@@ -78,7 +78,7 @@ class HipEvents:
 
 
 GEMM_SRCS = [os.path.join(ROOT, "moe_grouped_mlp_amd", "csrc", f)
-             for f in ("gemm_kernel.h", "common.h", "mx.h")]
+             for f in ("gemm_kernel.h", "act.h", "common.h", "mx.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fc1_mixtral_traffic.json")
 
 
@@ -205,9 +205,8 @@ def main():
     wl_name, prec_default = BENCH_CONFIGS[args.config]
     prec = args.prec or prec_default
     mx = prec == "mxfp8"
-    if args.unfused and (mx or args.wgrad):
-        print("--unfused is the bf16 baseline of the fused step (no MXFP8, no --wgrad)",
-              file=sys.stderr)
+    if args.unfused and args.wgrad:
+        print("--unfused is the baseline of the fused step (no --wgrad)", file=sys.stderr)
         sys.exit(2)
     cfg = dict(CONFIGS[wl_name])
     E, k, T, H, I = (cfg[n] for n in ("E", "k", "T", "H", "I"))
@@ -218,7 +217,8 @@ def main():
     act_kind = {"swiglu": mg.ACT_SWIGLU, "geglu": mg.ACT_GEGLU, "srelu": mg.ACT_SRELU}[cfg["act"]]
     act = mg.act_params(act_kind, beta=cfg["beta"], clamp=cfg["clamp"])
     blk = mg.ExpertBlock(E, H, I, T, k, act=act,
-                         prec=mg.PREC_MXFP8 if mx else mg.PREC_BF16, wgrad=args.wgrad)
+                         prec=mg.PREC_MXFP8 if mx else mg.PREC_BF16, wgrad=args.wgrad,
+                         bf16_copies=True if (args.unfused and mx) else None)
     blk.load_weights(w1, w2)
     del w1, w2
     torch.cuda.synchronize()
@@ -256,7 +256,10 @@ def main():
         blk.combine(blk.yp, blk.out)
         if evs is not None:
             evs.record(base + 5, stream)
-        blk.gather(dout, blk.dyp)
+        if mx:
+            blk.gather(dout, None, blk.dyp_q, blk.dyp_s)
+        else:
+            blk.gather(dout, blk.dyp)
         blk.experts_backward_unfused(None if evs is None else _Rec(evs, base + 6))
         blk.combine(blk.dxp, blk.dx, dprobs=True)
         if evs is not None:
@@ -343,8 +346,11 @@ def main():
            "unpermute_dx": M * H * 2 + T * H * 2 + T * k * 12}
     if args.unfused:
         # the separate activation passes: z in, a out; dA and z in, dz out
-        mem["act_fwd"] = M * n1 * 2 + M * I * 2
-        mem["act_bwd"] = M * I * 2 + 2 * M * n1 * 2 + M * 4
+        # (MXFP8: plus the quantize passes, bf16 read twice, codes + scales
+        # written rowwise and transposed)
+        q = (2 * 2 + 2 * (1 + 1 / 32)) if mx else 0.0
+        mem["act_fwd"] = M * n1 * 2 + M * I * 2 + M * I * q
+        mem["act_bwd"] = M * I * 2 + 2 * M * n1 * 2 + M * 4 + M * n1 * q
     if args.wgrad and mx:
         # MXFP8 transposed copies of Xp and dYp (bf16 in, codes + scales out)
         mem["wgrad_quantize"] = 2 * M * H * (2 + 1 + 1 / 32)

@@ -436,11 +436,14 @@ moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* args, void* stream);
  * fused entry points above are the product; these measure what fusion buys.
  *
  * moe_grouped_gemm -- C[r] = bf16(A[r] . B_e^T) for every routed row r of
- *   expert e (bf16, fp32 accumulation): A [M_cap][K], C [M_cap][N]; B_e at
+ *   expert e (fp32 accumulation): A [M_cap][K], C [M_cap][N] bf16; B_e at
  *   b + e * b_stride, [N][K] (b_kn = 0) or [K][N] (b_kn = 1); pad rows of C
  *   are not written.  Needs N, K multiples of 64.  workspace (optional, the
  *   size moe_grouped_mlp_workspace_size gives) enables the K split of a
- *   partial last round.
+ *   partial last round (bf16).
+ *   prec == MOE_PREC_MXFP8: A and B are E4M3 codes with tiled E8M0 scales
+ *   blocked along K (a_s: R = M_cap; b_s per expert: R = N, b_s_stride bytes
+ *   apart, 0 = N * K / 32); b_kn must be 0 and M_cap % 128 == 0.
  * ---------------------------------------------------------------------- */
 typedef struct moe_gemm_args {
   int32_t E, N, K;
@@ -455,6 +458,10 @@ typedef struct moe_gemm_args {
   void* c;
   void* workspace;
   size_t workspace_bytes;
+  int32_t prec;                   /* MOE_PREC_BF16 or MOE_PREC_MXFP8 */
+  const uint8_t* a_s;
+  const uint8_t* b_s;
+  int64_t b_s_stride;             /* bytes; 0: N * K / 32 */
 } moe_gemm_args;
 
 moe_status moe_grouped_gemm(const moe_gemm_args* args, void* stream);
@@ -467,7 +474,9 @@ moe_status moe_grouped_gemm(const moe_gemm_args* args, void* stream);
  *     dprobs_p 0.
  *   Same meaning as the fused epilogues of moe_grouped_mlp_fwd / _bwd: z, dz
  *   bf16 [M_cap][N1] in the interleaved column order (N1 = 2 I gated, I for
- *   sReLU); a, da bf16 [M_cap][I].  Only rows holding data are written.
+ *   sReLU); a, da bf16 [M_cap][I].  Rows holding data are written as
+ *   above; pad rows inside the groups' padded spans get zeros (so column
+ *   blocks of 32 rows quantized from them encode zeros there).
  * ---------------------------------------------------------------------- */
 typedef struct moe_glu_args {
   int32_t direction;

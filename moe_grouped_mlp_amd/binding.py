@@ -116,7 +116,8 @@ class GemmArgs(ctypes.Structure):
                 ("split_sizes", c_void_p), ("padded_offsets", c_void_p),
                 ("a", c_void_p), ("b", c_void_p), ("b_stride", c_int64),
                 ("c", c_void_p), ("workspace", c_void_p),
-                ("workspace_bytes", c_size_t)]
+                ("workspace_bytes", c_size_t), ("prec", c_int32),
+                ("a_s", c_void_p), ("b_s", c_void_p), ("b_s_stride", c_int64)]
 
 
 class GluArgs(ctypes.Structure):
@@ -341,10 +342,12 @@ def moe_router_topk(*, T, E, k, logits, expert_idx, probs, stream=None):
 
 def moe_grouped_gemm(*, E, N, K, M_cap, split_sizes, padded_offsets, a, b, c,
                      b_kn=False, b_stride=0, cu_margin=0, workspace=None,
+                     prec=PREC_BF16, a_s=None, b_s=None, b_s_stride=0,
                      stream=None):
     args = GemmArgs(E, N, K, M_cap, int(bool(b_kn)), cu_margin,
                     _ptr(split_sizes), _ptr(padded_offsets), _ptr(a), _ptr(b),
-                    b_stride, _ptr(c), _ptr(workspace), _nbytes(workspace))
+                    b_stride, _ptr(c), _ptr(workspace), _nbytes(workspace), prec,
+                    _ptr(a_s), _ptr(b_s), b_s_stride)
     _check("moe_grouped_gemm", lib().moe_grouped_gemm(ctypes.byref(args), _stream(stream)))
 
 

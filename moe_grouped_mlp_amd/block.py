@@ -256,50 +256,76 @@ class ExpertBlock:
         return self.dx, self.dprobs
 
     # ------------------------------------------------- unfused baseline --
-    # The same layer without the fused epilogues (bf16): FC1 and FC2 dgrad as
-    # plain grouped GEMMs, the activation and its gradient as separate passes
-    # (moe_glu_unfused).  It measures what the fused path gains; outputs have
-    # the meaning of the fused ones (dA is stored in bf16 in between).
+    # The same layer without the fused epilogues: FC1 and FC2 dgrad as plain
+    # grouped GEMMs, the activation and its gradient as separate passes
+    # (moe_glu_unfused) and, with MXFP8, the rowwise and transposed copies of
+    # a and dz made by moe_quantize_mxfp8.  It measures what the fused path
+    # gains; outputs have the meaning of the fused ones (dA is stored in bf16
+    # in between).  MXFP8 needs the block built with bf16_copies=True.
+    def _gemm(self, N, K, a, b, c, a_s=None, b_s=None, b_kn=False):
+        B.moe_grouped_gemm(E=self.E, N=N, K=K, M_cap=self.M_cap,
+                           split_sizes=self.split_sizes,
+                           padded_offsets=self.padded_offsets, a=a, b=b, c=c,
+                           b_kn=b_kn, cu_margin=self.cu_margin, workspace=self.ws,
+                           prec=self.prec, a_s=a_s, b_s=b_s)
+
+    def _quantize(self, x, cols, q, s, qT, sT):
+        B.moe_quantize_mxfp8(mode=B.QUANT_ROW, batch=1, rows=self.M_cap, cols=cols,
+                             x=x, q=q, s=s)
+        if qT is not None:
+            B.moe_quantize_mxfp8(mode=B.QUANT_COL, batch=1, rows=self.M_cap,
+                                 cols=cols, x=x, q=qT, s=sT)
+
     def experts_forward_unfused(self, events=None) -> None:
-        if self.mx:
-            raise NotImplementedError("the unfused baseline is bf16")
-        g = dict(E=self.E, M_cap=self.M_cap, split_sizes=self.split_sizes,
-                 padded_offsets=self.padded_offsets, cu_margin=self.cu_margin,
-                 workspace=self.ws)
+        if self.mx and self.a is None:
+            raise RuntimeError("the MXFP8 unfused baseline needs bf16_copies=True")
         rec = (lambda i: events.record(i)) if events else (lambda i: None)
         rec(0)
-        B.moe_grouped_gemm(N=self.N1, K=self.H, a=self.xp, b=self.w1i, c=self.z, **g)
+        if self.mx:
+            self._gemm(self.N1, self.H, self.xp_q, self.w1_q, self.z, self.xp_s, self.w1_s)
+        else:
+            self._gemm(self.N1, self.H, self.xp, self.w1i, self.z)
         rec(1)
         B.moe_glu_unfused(direction=0, E=self.E, I=self.I, M_cap=self.M_cap,
                           split_sizes=self.split_sizes,
                           padded_offsets=self.padded_offsets, probs_p=self.probs_p,
                           z=self.z, a=self.a, amax=self.amax, act=self.act)
+        if self.mx:
+            self._quantize(self.a, self.I, self.a_q, self.a_s, self.aT_q, self.aT_s)
         rec(2)
-        B.moe_grouped_gemm(N=self.H, K=self.I, a=self.a, b=self.w2, c=self.yp, **g)
+        if self.mx:
+            self._gemm(self.H, self.I, self.a_q, self.w2_q, self.yp, self.a_s, self.w2_s)
+        else:
+            self._gemm(self.H, self.I, self.a, self.w2, self.yp)
         rec(3)
 
     def experts_backward_unfused(self, events=None) -> None:
-        if self.mx:
-            raise NotImplementedError("the unfused baseline is bf16")
+        if self.mx and self.dz is None:
+            raise RuntimeError("the MXFP8 unfused baseline needs bf16_copies=True")
         if getattr(self, "da", None) is None:
             self.da = torch.empty(self.M_cap, self.I, dtype=torch.bfloat16,
                                   device=self.z.device)
-        g = dict(E=self.E, M_cap=self.M_cap, split_sizes=self.split_sizes,
-                 padded_offsets=self.padded_offsets, cu_margin=self.cu_margin,
-                 workspace=self.ws)
         rec = (lambda i: events.record(i)) if events else (lambda i: None)
         rec(0)
-        B.moe_grouped_gemm(N=self.I, K=self.H, a=self.dyp, b=self.w2, b_kn=True,
-                           c=self.da, **g)
+        if self.mx:
+            self._gemm(self.I, self.H, self.dyp_q, self.w2t_q, self.da, self.dyp_s,
+                       self.w2t_s)
+        else:
+            self._gemm(self.I, self.H, self.dyp, self.w2, self.da, b_kn=True)
         rec(1)
         B.moe_glu_unfused(direction=1, E=self.E, I=self.I, M_cap=self.M_cap,
                           split_sizes=self.split_sizes,
                           padded_offsets=self.padded_offsets, probs_p=self.probs_p,
                           z=self.z, da=self.da, dz=self.dz,
                           dprobs_p=self.dprobs_p, act=self.act)
+        if self.mx:
+            self._quantize(self.dz, self.N1, self.dz_q, self.dz_s, self.dzT_q, self.dzT_s)
         rec(2)
-        B.moe_grouped_gemm(N=self.H, K=self.N1, a=self.dz, b=self.w1i, b_kn=True,
-                           c=self.dxp, **g)
+        if self.mx:
+            self._gemm(self.H, self.N1, self.dz_q, self.w1t_q, self.dxp, self.dz_s,
+                       self.w1t_s)
+        else:
+            self._gemm(self.H, self.N1, self.dz, self.w1i, self.dxp, b_kn=True)
         rec(3)
 
     def weight_grads(self, timing_events=None):

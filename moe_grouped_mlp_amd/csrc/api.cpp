@@ -475,11 +475,21 @@ moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
     return MOE_ERR_INVALID_ARG;
   if (a->b_stride != 0 && a->b_stride < static_cast<int64_t>(a->N) * a->K)
     return MOE_ERR_INVALID_ARG;
+  if (a->prec != MOE_PREC_BF16 && a->prec != MOE_PREC_MXFP8) return MOE_ERR_INVALID_ARG;
+  const bool mx = a->prec == MOE_PREC_MXFP8;
+  if (mx && (a->b_kn != 0 || !a->a_s || !a->b_s || a->M_cap % 128 != 0 ||
+             (a->b_s_stride != 0 && a->b_s_stride < static_cast<int64_t>(a->N) * a->K / 32)))
+    return MOE_ERR_INVALID_ARG;
   int cu = 0;
   if (moe_status st = device_info(&cu)) return st;
   if (a->cu_margin >= cu) return MOE_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   moe::GemmArgs g{};
+  if (mx) {
+    g.a_s = a->a_s;
+    g.b_s = a->b_s;
+    g.b_s_stride = a->b_s_stride ? a->b_s_stride : static_cast<int64_t>(a->N) * a->K / 32;
+  }
   g.E = a->E;
   g.N = a->N;
   g.K = a->K;
@@ -495,7 +505,7 @@ moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   g.ldc = a->N;
   const int grid = gemm_grid(cu, a->cu_margin, a->M_cap, a->E, a->N);
   if (moe_status st = attach_split(g, a->workspace, a->workspace_bytes, 0, grid, s)) return st;
-  return launched(moe::launch_grouped_gemm(g, moe::EPI_STORE, a->b_kn != 0, false, grid, s));
+  return launched(moe::launch_grouped_gemm(g, moe::EPI_STORE, a->b_kn != 0, mx, grid, s));
 }
 
 moe_status moe_glu_unfused(const moe_glu_args* a, void* stream) {

@@ -8,8 +8,8 @@
 //
 // One workgroup per routed row (grid-stride); a thread takes 4 consecutive
 // logical columns, which lie inside one 64-column block of the gate/up
-// interleave, so its gate and up values are 8-byte loads.  Pad rows are
-// skipped (their dprobs is 0).  dprobs sums each thread's columns in order
+// interleave, so its gate and up values are 8-byte loads.  Pad rows inside
+// the groups' padded spans are written as zeros (their dprobs is 0).  dprobs sums each thread's columns in order
 // and reduces over the workgroup in a fixed tree, so it is deterministic.
 #include "act.h"
 #include "common.h"
@@ -68,11 +68,18 @@ __global__ __launch_bounds__(kGluThreads) void glu_fwd_kernel(
   constexpr bool gated = ACT != MOE_ACT_SRELU;
   const int64_t ldz = gated ? 2 * I : I;
   float m = 0.0f;
+  const int64_t padded_end = min(static_cast<int64_t>(s_pad[E]), rows);
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-    if (!row_valid(r, s_pad, s_split, E)) continue;
+    uint16_t* ar = a + r * static_cast<int64_t>(I);
+    if (!row_valid(r, s_pad, s_split, E)) {
+      // pad rows of a group hold zeros (MXFP8 column blocks span them)
+      if (r < padded_end)
+        for (int j = 4 * threadIdx.x; j < I; j += 4 * kGluThreads)
+          *reinterpret_cast<uint2*>(ar + j) = make_uint2(0, 0);
+      continue;
+    }
     const float p = probs[r];
     const uint16_t* zr = z + r * ldz;
-    uint16_t* ar = a + r * static_cast<int64_t>(I);
     for (int j = 4 * threadIdx.x; j < I; j += 4 * kGluThreads) {
       float g[4], u[4], o[4];
       if constexpr (gated) {
@@ -119,9 +126,15 @@ __global__ __launch_bounds__(kGluThreads) void glu_bwd_kernel(
   load_groups(split, padded, E, s_pad, s_split);
   constexpr bool gated = ACT != MOE_ACT_SRELU;
   const int64_t ldz = gated ? 2 * I : I;
+  const int64_t padded_end = min(static_cast<int64_t>(s_pad[E]), rows);
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
     if (!row_valid(r, s_pad, s_split, E)) {
       if (threadIdx.x == 0) dprobs[r] = 0.0f;
+      if (r < padded_end) {   // pad rows of a group hold zeros
+        uint16_t* dzr = dz + r * ldz;
+        for (int64_t j = 4 * threadIdx.x; j < ldz; j += 4 * kGluThreads)
+          *reinterpret_cast<uint2*>(dzr + j) = make_uint2(0, 0);
+      }
       continue;
     }
     const float p = probs[r];

@@ -160,14 +160,19 @@ def test_fwd_validation():
 
 def test_unfused_baseline_validation():
     def gemm(**kw):
-        a = B.GemmArgs(4, 256, 128, 1024, 0, 0, 64, 64, 64, 64, 0, 64, None, 0)
+        a = B.GemmArgs(4, 256, 128, 1024, 0, 0, 64, 64, 64, 64, 0, 64, None, 0,
+                       B.PREC_BF16, None, None, 0)
         for f, v in kw.items():
             setattr(a, f, v)
         return a
     assert _call("moe_grouped_gemm", gemm()) == DEVICE
     assert _call("moe_grouped_gemm", gemm(b_kn=1, b_stride=256 * 128)) == DEVICE
+    mx = dict(prec=B.PREC_MXFP8, a_s=64, b_s=64)
+    assert _call("moe_grouped_gemm", gemm(**mx)) == DEVICE
     for bad in (dict(N=100), dict(K=32), dict(E=0), dict(b_kn=2), dict(a=None),
-                dict(c=None), dict(b_stride=5), dict(cu_margin=-1), dict(M_cap=0)):
+                dict(c=None), dict(b_stride=5), dict(cu_margin=-1), dict(M_cap=0),
+                dict(prec=9), dict(mx, b_kn=1), dict(mx, a_s=None),
+                dict(mx, M_cap=1000), dict(mx, b_s_stride=3)):
         assert _call("moe_grouped_gemm", gemm(**bad)) == INVALID, bad
 
     def glu(**kw):

@@ -44,3 +44,28 @@ def test_unfused_layer_parity(case):
     torch.cuda.synchronize()
     fw, bw = oracle_layer(wl, M_cap, unfused=True)
     compare_layer(blk, wl, fw, bw)
+
+
+@pytest.mark.parametrize("case", ["multi_tile_ragged", "gptoss_act", "dsv3_zipf_empty"])
+def test_unfused_layer_mx_parity(case):
+    """MXFP8: plain MXFP8 grouped GEMMs, the activation passes and
+    moe_quantize_mxfp8 for the rowwise and transposed copies of a and dz,
+    against the oracle's MXFP8 unfused reading (MXFP8 bounds)."""
+    from .test_gpu_mx import compare_layer_mx
+    kw = dict(CASES[case])
+    wl = make_workload(kw.pop("name"), seed=4, **kw)
+    M_cap = -(-wl.m_cap() // 128) * 128
+    gp, _ = act_of(wl)
+    blk = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, act=gp, M_cap=M_cap,
+                         prec=mg.PREC_MXFP8, bf16_copies=True)
+    blk.load_weights(dev_bf16(wl.w1), dev_bf16(wl.w2))
+    blk.route(torch.from_numpy(wl.expert_idx).cuda(),
+              torch.from_numpy(wl.probs).cuda(), dev_bf16(wl.x))
+    blk.experts_forward_unfused()
+    blk.combine(blk.yp, blk.out)
+    blk.gather(dev_bf16(wl.dout), None, blk.dyp_q, blk.dyp_s)
+    blk.experts_backward_unfused()
+    blk.combine(blk.dxp, blk.dx, dprobs=True)
+    torch.cuda.synchronize()
+    fw, bw = oracle_layer(wl, M_cap, mx=True, unfused=True)
+    compare_layer_mx(blk, wl, fw, bw)
