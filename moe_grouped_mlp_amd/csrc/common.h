@@ -57,6 +57,23 @@ MOE_DEV float wave_max(float v) {
   return v;
 }
 
+// Wave maximum with no lane-address registers: xor 1 .. 16 inside each half
+// wave by ds_swizzle (bit-mask mode: and 0x1f, xor m, an immediate pattern)
+// and xor 32 by v_permlane32_swap.  Used in epilogues, where the address
+// registers of a ds_bpermute-based shuffle would be kept across the K loop
+// (spilled and reloaded after the stores).
+MOE_DEV float wave_max_imm(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1f | (1 << 10))));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1f | (2 << 10))));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1f | (4 << 10))));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1f | (8 << 10))));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1f | (16 << 10))));
+  // one of the two swapped words is the partner half's value, the other ours
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(v, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
 MOE_DEV int wave_sum_i(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -1405,7 +1405,7 @@ void grouped_gemm_kernel(GemmArgs g) {
       } else
         amax = epi_glu<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, pr_tile, g.act, t, wn, lane);
       if (g.amax) {
-        amax = wave_max(amax);
+        amax = wave_max_imm(amax);
         if (lane == 0) atomic_max_nonneg(g.amax, amax);
       }
     } else {
