@@ -14,7 +14,9 @@ step (once per weight update), and timed on their own.  Inputs are
 synthetic (seeded), already resident in HBM when the timed region starts.
 The value is algorithmic GEMM TFLOP/s of the step: 12 * M * H * I flops (18 with
 --wgrad, which adds the weight-gradient GEMMs)
-(M = routed rows; no padding counted).
+(M = routed rows; no padding counted).  --recompute (activation recompute)
+keeps no z in the forward and rebuilds it with FC1's GEMM in the backward;
+that GEMM is timed but its flops are not counted, being no model work.
 
 Prints one JSON line (stdout).  Progress goes to stderr.
 """
@@ -186,6 +188,9 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="the unfused baseline (bf16): plain grouped GEMMs with the "
                          "activation and its gradient as separate passes")
+    ap.add_argument("--recompute", action="store_true",
+                    help="activation recompute: the forward stores no z, the backward "
+                         "rebuilds it with FC1's GEMM (timed as fc1_recompute)")
     ap.add_argument("--wgrad", action="store_true",
                     help="add the weight-gradient grouped GEMMs (dW1, dW2) to the "
                          "step: a full training step of the layer")
@@ -205,8 +210,9 @@ def main():
     wl_name, prec_default = BENCH_CONFIGS[args.config]
     prec = args.prec or prec_default
     mx = prec == "mxfp8"
-    if args.unfused and args.wgrad:
-        print("--unfused is the baseline of the fused step (no --wgrad)", file=sys.stderr)
+    if args.unfused and (args.wgrad or args.recompute):
+        print("--unfused is the baseline of the fused step (no --wgrad, --recompute)",
+              file=sys.stderr)
         sys.exit(2)
     cfg = dict(CONFIGS[wl_name])
     E, k, T, H, I = (cfg[n] for n in ("E", "k", "T", "H", "I"))
@@ -218,7 +224,7 @@ def main():
     act = mg.act_params(act_kind, beta=cfg["beta"], clamp=cfg["clamp"])
     blk = mg.ExpertBlock(E, H, I, T, k, act=act,
                          prec=mg.PREC_MXFP8 if mx else mg.PREC_BF16, wgrad=args.wgrad,
-                         bf16_copies=True if (args.unfused and mx) else None)
+                         recompute=args.recompute, bf16_copies=True if (args.unfused and mx) else None)
     blk.load_weights(w1, w2)
     del w1, w2
     torch.cuda.synchronize()
@@ -234,10 +240,15 @@ def main():
 
     # events per step: 0 start, 1-3 forward GEMMs (library), 4 after
     # unpermute, 5-7 backward GEMMs (library), 8 after dX unpermute; with
-    # --wgrad 9-11 around the weight-gradient GEMMs (library)
+    # --wgrad 9-11 around the weight-gradient GEMMs (library); with
+    # --recompute the last one before the z rebuild (which ends at 5)
     n_ev = 12 if args.wgrad else 9
     if args.unfused:
         n_ev = 11
+    ev_rc = None
+    if args.recompute:
+        ev_rc = n_ev
+        n_ev += 1
 
     class _Rec:   # events of one step, recorded on the library's stream
         def __init__(self, evs, base):
@@ -280,6 +291,10 @@ def main():
             blk.gather(dout, blk.dyp, blk.dyp_q, blk.dyp_s)
         else:
             blk.gather(dout, blk.dyp)
+        if args.recompute:
+            if evs is not None:
+                evs.record(base + ev_rc, stream)
+            blk.recompute_z()
         blk.experts_backward(None if evs is None else
                              [evs.ev[base + 5], evs.ev[base + 6], evs.ev[base + 7]])
         blk.combine(blk.dxp, blk.dx, dprobs=True)
@@ -327,6 +342,8 @@ def main():
                   "fc2_dgrad": seg(5, 6), "fc1_dgrad": seg(6, 7), "unpermute_dx": seg(7, 8)}
     if args.wgrad:
         seg_ms.update(wgrad_quantize=seg(8, 9), wgrad_dw1=seg(9, 10), wgrad_dw2=seg(10, 11))
+    if args.recompute:
+        seg_ms.update(permute_dout=seg(4, ev_rc), fc1_recompute=seg(ev_rc, 5))
     evs.close()
     assert int(blk.err_flag.cpu()[0]) == 0
     value = flops_step / (ms_step * 1e-3) / 1e12
@@ -336,10 +353,15 @@ def main():
     row_bytes = H * (1 + 1 / 32) if mx else 2 * H
     idx_bytes = T * k * 4 * 2 + T * k * 4 + M * 8
     kernels = {}
+    if args.recompute:
+        flops_k = dict(flops, fc1_recompute=flops["fc1"])   # not model work
+    else:
+        flops_k = flops
     for name in ("fc1", "fc2", "fc2_dgrad", "fc1_dgrad") + (
-            ("wgrad_dw1", "wgrad_dw2") if args.wgrad else ()):
+            ("wgrad_dw1", "wgrad_dw2") if args.wgrad else ()) + (
+            ("fc1_recompute",) if args.recompute else ()):
         kernels[name] = {"ms": round(seg_ms[name], 4), "unit": "TFLOP/s",
-                         "rate": round(flops[name] / (seg_ms[name] * 1e-3) / 1e12, 2)}
+                         "rate": round(flops_k[name] / (seg_ms[name] * 1e-3) / 1e12, 2)}
     mem = {"route_permute_x": T * H * 2 + M * row_bytes + idx_bytes,
            "unpermute_out": M * H * 2 + T * H * 2 + T * k * 4,
            "permute_dout": T * H * 2 + M * row_bytes + T * k * 4,
@@ -414,7 +436,9 @@ def main():
         cpu = cpu_baseline(cfg, args.seed, mx=mx)
         log(f"cpu oracle {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads")
 
-    traffic = measured_traffic() if (args.config == "mixtral" and not mx) else None
+    # the recorded counters are those of FC1 storing z
+    traffic = (measured_traffic() if (args.config == "mixtral" and not mx
+                                      and not args.recompute) else None)
     out = {
         "metric": "fused grouped-MLP fwd/bwd TFLOP/s and % MFMA peak, Mixtral-shaped "
                   "layer, 1 GPU",
@@ -435,7 +459,8 @@ def main():
                                f"{prec}, route+permute+FC1+FC2+unpermute and backward "
                                f"(FC2 dgrad+dAct, FC1 dgrad, dX, dprobs"
                                f"{', dW1, dW2' if args.wgrad else ''})"
-                               f"{'; unfused baseline (plain GEMMs + separate activation passes)' if args.unfused else ''}",
+                               f"{'; unfused baseline (plain GEMMs + separate activation passes)' if args.unfused else ''}"
+                               f"{'; activation recompute (z rebuilt in the backward, its FLOPs not counted)' if args.recompute else ''}",
                    "E": E, "k": k, "T": T, "H": H, "I": I, "routed_rows": M,
                    "prec": prec, "flops_per_step": flops_step},
         "kernels": kernels,

@@ -257,7 +257,8 @@ moe_status moe_quantize_mxfp8(const moe_quant_args* args, void* stream);
  *     w1i  bf16 [E][N1][H], gated: interleaved by moe_weight_repack_interleave
  *     w2   bf16 [E][H][I]
  *     z    bf16 [M_cap][N1] in the same (interleaved) column order as w1i rows;
- *          may be NULL when no backward follows
+ *          may be NULL when no backward follows, or when the backward
+ *          rebuilds it (activation recompute, see moe_grouped_gemm)
  *     a    bf16 [M_cap][I] logical column order
  *     yp   bf16 [M_cap][H]
  *     amax optional device float: raised to max|a| over written rows (the
@@ -444,6 +445,11 @@ moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* args, void* stream);
  *   prec == MOE_PREC_MXFP8: A and B are E4M3 codes with tiled E8M0 scales
  *   blocked along K (a_s: R = M_cap; b_s per expert: R = N, b_s_stride bytes
  *   apart, 0 = N * K / 32); b_kn must be 0 and M_cap % 128 == 0.
+ *   Activation recompute ([FK] § "What's next" names it as planned work):
+ *   with workspace NULL, A = xp (or xp_q/xp_s), B = w1i (or w1_q/w1_s),
+ *   N = N1, K = H, every tile sums K in the order moe_grouped_mlp_fwd's FC1
+ *   uses, so C is bit for bit the z FC1 stores; a forward called with z NULL
+ *   can then be followed by moe_grouped_mlp_bwd on this rebuilt z.
  * ---------------------------------------------------------------------- */
 typedef struct moe_gemm_args {
   int32_t E, N, K;

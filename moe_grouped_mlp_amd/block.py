@@ -22,6 +22,12 @@ and dW2 [E][H][I].  bf16 reads dz, Xp, dYp and a as stored; MXFP8 reads the
 transposed copies of a and dz the epilogues wrote and makes those of Xp and
 dYp with moe_quantize_mxfp8 (the permutes then also keep bf16 Xp and dYp).
 
+With recompute=True (activation recompute) the forward stores no z and the
+backward first rebuilds it with moe_grouped_gemm from the saved Xp and W1
+(recompute_z): z's write moves from the forward to the backward, at the cost
+of one more FC1-sized GEMM, and gradients are bit for bit those of the path
+that keeps z.
+
 No call reads device memory back or synchronises, so a whole step can be
 captured in a HIP graph.
 """
@@ -41,13 +47,17 @@ class ExpertBlock:
                  M_cap: Optional[int] = None, cu_margin: int = 0,
                  prec: int = B.PREC_BF16, transposed_copies: bool = True,
                  bf16_copies: Optional[bool] = None, wgrad: bool = False,
-                 device="cuda"):
+                 recompute: bool = False, device="cuda"):
         self.E, self.H, self.I, self.T, self.k = E, H, I, T, k
         self.act = act or B.act_params()
         self.gated = self.act.act != B.ACT_SRELU
         self.N1 = 2 * I if self.gated else I
         self.first_expert = first_expert
         self.prec = prec
+        # activation recompute: the forward keeps no z; the backward rebuilds
+        # it from xp and W1 before the dActivation pass (recompute_z)
+        self.recompute = recompute
+        self._z_valid = False
         self.mx = prec == B.PREC_MXFP8
         M_cap = M_cap if M_cap is not None else T * k + E * (B.GROUP_ALIGN - 1)
         if self.mx:
@@ -208,11 +218,25 @@ class ExpertBlock:
         B.moe_grouped_mlp_fwd(E=self.E, H=self.H, I=self.I, M_cap=self.M_cap,
                               split_sizes=self.split_sizes,
                               padded_offsets=self.padded_offsets,
-                              probs_p=self.probs_p, z=self.z, a=self.a,
+                              probs_p=self.probs_p,
+                              z=None if self.recompute else self.z, a=self.a,
                               yp=self.yp, amax=self.amax, act=self.act,
                               prec=self.prec, cu_margin=self.cu_margin,
                               err_flag=self.err_flag, workspace=self.ws,
                               timing_events=timing_events, **kw)
+        self._z_valid = not self.recompute
+
+    def recompute_z(self) -> None:
+        """Rebuilds z = xp . W1i^T after a forward that kept none: FC1's
+        grouped GEMM without its epilogue and without split-K, so every tile
+        sums K in the order FC1 used and z is bit for bit the one FC1 would
+        have stored (MXFP8: from the same xp and W1 codes and scales)."""
+        if self.mx:
+            self._gemm(self.N1, self.H, self.xp_q, self.w1_q, self.z, self.xp_s,
+                       self.w1_s, split=False)
+        else:
+            self._gemm(self.N1, self.H, self.xp, self.w1i, self.z, split=False)
+        self._z_valid = True
 
     def combine(self, yp: torch.Tensor, out: torch.Tensor,
                 dprobs: bool = False) -> None:
@@ -229,6 +253,8 @@ class ExpertBlock:
 
     # ----------------------------------------------------------- backward --
     def experts_backward(self, timing_events=None) -> None:
+        if self.recompute and not self._z_valid:
+            self.recompute_z()
         if self.mx:
             kw = dict(dyp_q=self.dyp_q, dyp_s=self.dyp_s, w2t_q=self.w2t_q,
                       w2t_s=self.w2t_s, w1t_q=self.w1t_q, w1t_s=self.w1t_s,
@@ -262,11 +288,12 @@ class ExpertBlock:
     # a and dz made by moe_quantize_mxfp8.  It measures what the fused path
     # gains; outputs have the meaning of the fused ones (dA is stored in bf16
     # in between).  MXFP8 needs the block built with bf16_copies=True.
-    def _gemm(self, N, K, a, b, c, a_s=None, b_s=None, b_kn=False):
+    def _gemm(self, N, K, a, b, c, a_s=None, b_s=None, b_kn=False, split=True):
         B.moe_grouped_gemm(E=self.E, N=N, K=K, M_cap=self.M_cap,
                            split_sizes=self.split_sizes,
                            padded_offsets=self.padded_offsets, a=a, b=b, c=c,
-                           b_kn=b_kn, cu_margin=self.cu_margin, workspace=self.ws,
+                           b_kn=b_kn, cu_margin=self.cu_margin,
+                           workspace=self.ws if split else None,
                            prec=self.prec, a_s=a_s, b_s=b_s)
 
     def _quantize(self, x, cols, q, s, qT, sT):
