@@ -89,7 +89,9 @@ typedef enum moe_act {
 
 typedef enum moe_prec {
   MOE_PREC_BF16 = 0,  /* bf16 operands, fp32 accumulation                  */
-  MOE_PREC_MXFP8 = 1  /* E4M3 operands with E8M0 scales per 32 along K     */
+  MOE_PREC_MXFP8 = 1, /* E4M3 operands with E8M0 scales per 32 along K     */
+  MOE_PREC_MXFP4 = 2  /* E2M1 operands with E8M0 scales per 32 along K;
+                         moe_grouped_gemm and moe_quantize_mxfp4 only      */
 } moe_prec;
 
 /* Activation options: the supported GLU family with clamping and scaling
@@ -237,6 +239,25 @@ typedef struct moe_quant_args {
 } moe_quant_args;
 
 moe_status moe_quantize_mxfp8(const moe_quant_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_quantize_mxfp4 -- bf16 -> MXFP4, the 4-bit microscaling format of
+ *   gfx950's scaled MFMA, standing where [FK] § "Fused MXFP8 and NVFP4
+ *   quantization" names a 4-bit recipe (NVFP4's E4M3 scales per 16 values
+ *   have no MFMA form; MXFP4 keeps E8M0 scales per 32).
+ *   Elements E2M1 (exponent bias 1, one mantissa bit, values 0, 0.5, 1,
+ *   1.5, 2, 3, 4, 6 and their negatives); block scale 2^e with
+ *   e = clamp(floor(log2 max|v|) - 2, -127, 127) (-127 for an all-zero
+ *   block), code e + 127; element code = E2M1 round-to-nearest-even of
+ *   v / 2^e, magnitudes past 6 saturated, sign kept (-0 -> 0x8).
+ *   MOE_QUANT_ROW only (any other mode is MOE_ERR_INVALID_ARG): x bf16
+ *   [batch][rows][cols] -> q [batch][rows][cols / 2] bytes, two codes a
+ *   byte, element 2 i in the low nibble of byte i; scales rows*cols/32 bytes
+ *   per batch entry in the tiled layout of MOE_MX_BLOCK (R = rows, K = cols).
+ *   rows % 32 == 0, cols % 64 == 0; amax must be NULL.  Memory-bound: reads
+ *   2 bytes, writes 17/32 bytes per element.
+ * ---------------------------------------------------------------------- */
+moe_status moe_quantize_mxfp4(const moe_quant_args* args, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_grouped_mlp_fwd -- FC1 grouped GEMM with the fused activation epilogue,
@@ -445,6 +466,9 @@ moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* args, void* stream);
  *   prec == MOE_PREC_MXFP8: A and B are E4M3 codes with tiled E8M0 scales
  *   blocked along K (a_s: R = M_cap; b_s per expert: R = N, b_s_stride bytes
  *   apart, 0 = N * K / 32); b_kn must be 0 and M_cap % 128 == 0.
+ *   prec == MOE_PREC_MXFP4: A and B are packed E2M1 codes (K / 2 bytes a
+ *   row, moe_quantize_mxfp4's layout) with tiled E8M0 scales as for MXFP8;
+ *   b_stride counts values (even); no split-K.  Same limits as MXFP8.
  *   Activation recompute ([FK] § "What's next" names it as planned work):
  *   with workspace NULL, A = xp (or xp_q/xp_s), B = w1i (or w1_q/w1_s),
  *   N = N1, K = H, every tile sums K in the order moe_grouped_mlp_fwd's FC1

@@ -16,7 +16,7 @@ lib_path = os.path.join(HERE, "libmoe_gmlp.so")
 
 # ---- constants mirrored from include/moe_gmlp.h ---------------------------
 ACT_SWIGLU, ACT_GEGLU, ACT_SRELU = 0, 1, 2
-PREC_BF16, PREC_MXFP8 = 0, 1
+PREC_BF16, PREC_MXFP8, PREC_MXFP4 = 0, 1, 2
 PERMUTE_BUILD_MAP, PERMUTE_GATHER, PERMUTE_WRITE_MX = 0x1, 0x2, 0x4
 QUANT_ROW, QUANT_COL = 0, 1
 GROUP_ALIGN = 128
@@ -26,7 +26,7 @@ DEVERR_MCAP_OVERFLOW, DEVERR_DUP_EXPERT = 0x1, 0x2
 
 EXPORTED_SYMBOLS = (
     "moe_weight_repack_interleave", "moe_permute_workspace_size",
-    "moe_permute", "moe_unpermute", "moe_quantize_mxfp8",
+    "moe_permute", "moe_unpermute", "moe_quantize_mxfp8", "moe_quantize_mxfp4",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_mlp_wgrad",
     "moe_router_topk", "moe_grouped_gemm", "moe_glu_unfused",
     "moe_grouped_mlp_workspace_size", "moe_status_string", "moe_gmlp_version",
@@ -180,6 +180,7 @@ def lib() -> ctypes.CDLL:
         for name, st in (("moe_permute", PermuteArgs),
                          ("moe_unpermute", UnpermuteArgs),
                          ("moe_quantize_mxfp8", QuantArgs),
+                         ("moe_quantize_mxfp4", QuantArgs),
                          ("moe_grouped_mlp_fwd", FwdArgs),
                          ("moe_grouped_mlp_bwd", BwdArgs),
                          ("moe_grouped_mlp_wgrad", WgradArgs),
@@ -270,6 +271,13 @@ def moe_quantize_mxfp8(*, mode, batch, rows, cols, x, q, s, x_stride=0,
                   _ptr(amax))
     _check("moe_quantize_mxfp8",
            lib().moe_quantize_mxfp8(ctypes.byref(a), _stream(stream)))
+
+
+def moe_quantize_mxfp4(*, batch, rows, cols, x, q, s, x_stride=0, stream=None):
+    a = QuantArgs(QUANT_ROW, batch, rows, cols, x_stride, _ptr(x), _ptr(q), _ptr(s),
+                  None)
+    _check("moe_quantize_mxfp4",
+           lib().moe_quantize_mxfp4(ctypes.byref(a), _stream(stream)))
 
 
 def moe_grouped_mlp_workspace_size(E, H, I, M_cap, prec=PREC_BF16,

@@ -203,6 +203,20 @@ moe_status moe_quantize_mxfp8(const moe_quant_args* a, void* stream) {
   return launched(moe::launch_quantize_mxfp8(b, static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_quantize_mxfp4(const moe_quant_args* a, void* stream) {
+  if (!a || a->mode != MOE_QUANT_ROW || a->batch < 0 || a->rows < 32 || a->cols < 64 ||
+      a->rows % 32 != 0 || a->cols % 64 != 0 || !a->x || !a->q || !a->s || a->amax)
+    return MOE_ERR_INVALID_ARG;
+  const int64_t n = static_cast<int64_t>(a->rows) * a->cols;
+  if (a->x_stride != 0 && (a->x_stride < n || a->x_stride % 8 != 0)) return MOE_ERR_INVALID_ARG;
+  int cu = 0;
+  if (moe_status st = device_info(&cu)) return st;
+  if (a->batch == 0) return MOE_OK;
+  moe_quant_args b = *a;
+  if (b.x_stride == 0) b.x_stride = n;
+  return launched(moe::launch_quantize_mxfp4(b, static_cast<hipStream_t>(stream)));
+}
+
 // Workspace layout: [dprobs partials, fp32 M_cap x ceil(I / 256)] then, at a
 // 256-byte boundary, the split-K area of the plain-store GEMMs (partial tiles
 // and arrival counters for a grid of one workgroup per CU).
@@ -475,11 +489,14 @@ moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
     return MOE_ERR_INVALID_ARG;
   if (a->b_stride != 0 && a->b_stride < static_cast<int64_t>(a->N) * a->K)
     return MOE_ERR_INVALID_ARG;
-  if (a->prec != MOE_PREC_BF16 && a->prec != MOE_PREC_MXFP8) return MOE_ERR_INVALID_ARG;
-  const bool mx = a->prec == MOE_PREC_MXFP8;
+  if (a->prec != MOE_PREC_BF16 && a->prec != MOE_PREC_MXFP8 && a->prec != MOE_PREC_MXFP4)
+    return MOE_ERR_INVALID_ARG;
+  const bool f4 = a->prec == MOE_PREC_MXFP4;
+  const bool mx = a->prec == MOE_PREC_MXFP8 || f4;
   if (mx && (a->b_kn != 0 || !a->a_s || !a->b_s || a->M_cap % 128 != 0 ||
              (a->b_s_stride != 0 && a->b_s_stride < static_cast<int64_t>(a->N) * a->K / 32)))
     return MOE_ERR_INVALID_ARG;
+  if (f4 && a->b_stride % 2 != 0) return MOE_ERR_INVALID_ARG;
   int cu = 0;
   if (moe_status st = device_info(&cu)) return st;
   if (a->cu_margin >= cu) return MOE_ERR_INVALID_ARG;
@@ -504,6 +521,7 @@ moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   g.C = static_cast<uint16_t*>(a->c);
   g.ldc = a->N;
   const int grid = gemm_grid(cu, a->cu_margin, a->M_cap, a->E, a->N);
+  if (f4) return launched(moe::launch_gemm_store_f4(g, grid, s));
   if (moe_status st = attach_split(g, a->workspace, a->workspace_bytes, 0, grid, s)) return st;
   return launched(moe::launch_grouped_gemm(g, moe::EPI_STORE, a->b_kn != 0, mx, grid, s));
 }

@@ -229,10 +229,15 @@ struct NLoader {
 // instruction i fetches bytes 4 (l % 32) .. +3 of the run of group
 // 4 (w % 2) + 2 i + l / 32, which lands at byte 4 l of the instruction's
 // 256 bytes.  A step past K (K % 128 == 64) is zero-filled per lane.
+template <bool F4>
 struct ScaleLoader {
+  // MXFP4: a stage holds four 64-deep steps (256 bytes per row group): lane
+  // l of instruction i fetches bytes 4 l .. +3 of group 4 (w % 2) + i's run,
+  // landing at byte 4 l of the instruction's 256 bytes; step l / 16.
+  static constexpr int kInstr = F4 ? 4 : 2;
   __amdgpu_buffer_rsrc_t rsrc;
-  int voff[2];
-  int step;       // step (0 or 1) inside the stage this lane fetches
+  int voff[kInstr];
+  int step;       // step inside the stage this lane fetches
 
   // s_tile: scales of the tile's first row group; groups_avail: row groups
   // of 32 that exist from there on
@@ -240,17 +245,25 @@ struct ScaleLoader {
     const int64_t groups = groups_avail < 8 ? (groups_avail > 0 ? groups_avail : 0) : 8;
     const int per_group = (K / 64) * 64;
     rsrc = make_rsrc(s_tile, static_cast<uint32_t>(groups * per_group));
-    step = (lane >> 4) & 1;
+    if constexpr (F4) {
+      step = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      voff[i] = (4 * (wave & 1) + 2 * i + (lane >> 5)) * per_group + 4 * (lane & 31);
+      for (int i = 0; i < 4; ++i) voff[i] = (4 * (wave & 1) + i) * per_group + 4 * lane;
+    } else {
+      step = (lane >> 4) & 1;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        voff[i] = (4 * (wave & 1) + 2 * i + (lane >> 5)) * per_group + 4 * (lane & 31);
+    }
   }
   MOE_DEV void issue(uint8_t* stage, int kt, int wave_s, bool valid, int k_steps64) {
-    const bool ok = valid && (2 * kt + step < k_steps64);
+    constexpr int kSteps = F4 ? 4 : 2;        // 64-deep steps per stage
+    constexpr int kHalf = 8 * kSteps * 64;    // one operand's scales: 8 row groups
+    const bool ok = valid && (kSteps * kt + step < k_steps64);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma4(rsrc, stage + (wave_s >> 1) * 1024 + (wave_s & 1) * 512 + i * 256,
-           ok ? voff[i] : kOutOfRange, valid ? kt * 128 : 0);
+    for (int i = 0; i < kInstr; ++i)
+      dma4(rsrc, stage + (wave_s >> 1) * kHalf + (wave_s & 1) * (kHalf / 2) + i * 256,
+           ok ? voff[i] : kOutOfRange, valid ? kt * kSteps * 64 : 0);
   }
 };
 
@@ -871,13 +884,18 @@ MOE_DEV int block_exclusive_scan(int v, int* s_tmp, int& total) {
 // MX: A and B are E4M3 codes with tiled E8M0 scales (a_s, b_s); NN is then
 // false.  The GLU / DGLU epilogues also write the MXFP8 copies of their
 // output when MX.
-template <int EPI, bool NN, int ACT, bool MX>
+// F4 (with MX, plain store only): MXFP4 operands, E2M1 codes packed two per
+// byte (element 2 i in the low nibble of byte i) with the same tiled E8M0
+// scales; K counts values, so a row holds K / 2 bytes and a 128-byte stage
+// four 64-deep steps.
+template <int EPI, bool NN, int ACT, bool MX, bool F4 = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_kernel(GemmArgs g) {
   static_assert(!(MX && NN), "MXFP8 operands are always K-contiguous");
+  static_assert(!F4 || (MX && EPI == EPI_STORE), "MXFP4 runs the plain-store GEMM");
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[kStageBytes / 2], sA1[kStageBytes / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t sB0[kStageBytes / 2], sB1[kStageBytes / 2];
-  constexpr int kScaleBytes = MX ? kStageS : 4;
+  constexpr int kScaleBytes = MX ? (F4 ? 2 * kStageS : kStageS) : 4;
   __shared__ __attribute__((aligned(1024))) uint8_t sS0[kScaleBytes], sS1[kScaleBytes];
   __shared__ int s_start[kMaxExperts + 1];
   __shared__ int s_split[kMaxExperts];
@@ -979,6 +997,9 @@ void grouped_gemm_kernel(GemmArgs g) {
   // of B) for its K block (lane / 32) of 64-deep step j of a scale stage
   const int sa_off = 4 * wm * 128 + lane;
   const int sb_off = 1024 + 4 * wn * 128 + lane;
+  // MXFP4: [A | B] x 8 row groups x [step (4)][64 bytes]
+  const int sa_off4 = 4 * wm * 256 + lane;
+  const int sb_off4 = 2048 + 4 * wn * 256 + lane;
 
   // ---- per-tile geometry --------------------------------------------
   struct TileInfo {
@@ -1038,7 +1059,9 @@ void grouped_gemm_kernel(GemmArgs g) {
 
   // stages of 128 bytes per row: 64 bf16 or 128 E4M3 K values; an MXFP8 K
   // with K % 128 == 64 ends in a half stage whose second half is zero-filled
-  const int k_bytes = g.K * kElem;
+  // bytes of an operand row, and between experts of B
+  const int k_bytes = F4 ? g.K / 2 : g.K * kElem;
+  const int64_t b_stride_bytes = F4 ? g.b_stride / 2 : g.b_stride * kElem;
   const int nk = (k_bytes + kRowBytes - 1) / kRowBytes;
   const int k_steps64 = g.K / 64;  // MXFP8 64-deep MFMA steps
   const char* A = static_cast<const char*>(g.A);
@@ -1047,7 +1070,7 @@ void grouped_gemm_kernel(GemmArgs g) {
   NLoader la_n;     // A of the bf16 weight gradient
   KLoader lb_k;
   NLoader lb_n;
-  ScaleLoader ls;
+  ScaleLoader<F4> ls;
   int row_end = 0;  // weight gradient: end of the group's rows (bf16 loads stop there)
   // K order of a tile: stages k_rot, k_rot + 1, ..., nk - 1, 0, ..., k_rot - 1
   // with k_rot = stride * (m_t + n_t) mod nk.  Tiles that share an operand
@@ -1093,15 +1116,14 @@ void grouped_gemm_kernel(GemmArgs g) {
                 static_cast<uint32_t>(static_cast<int64_t>(g.K) * g.wg_rows * 2), g.wg_rows,
                 static_cast<int>(ti.row0), wave, lane);
     } else {
-      la.init(A + arow0 * g.K * kElem, rows_avail, g.K * kElem, wave, lane);
+      la.init(A + arow0 * k_bytes, rows_avail, k_bytes, wave, lane);
     }
-    const char* Bexp = B + static_cast<int64_t>(ti.e) * g.b_stride * kElem;
+    const char* Bexp = B + static_cast<int64_t>(ti.e) * b_stride_bytes;
     if constexpr (NN) {
       lb_n.init(reinterpret_cast<const uint16_t*>(Bexp),
                 static_cast<uint32_t>(static_cast<int64_t>(g.K) * g.N * 2), g.N, ti.col0, wave, lane);
     } else {
-      lb_k.init(Bexp + static_cast<int64_t>(ti.col0) * g.K * kElem, g.N - ti.col0, g.K * kElem,
-                wave, lane);
+      lb_k.init(Bexp + static_cast<int64_t>(ti.col0) * k_bytes, g.N - ti.col0, k_bytes, wave, lane);
     }
     if constexpr (MX) {
       // waves 0, 1 copy the A scales, waves 2, 3 the B scales (a uniform
@@ -1137,9 +1159,10 @@ void grouped_gemm_kernel(GemmArgs g) {
   // stage after next, and the first operands of the next stage are read
   // while the last MFMAs of this one run.  So a stage's loads have a whole
   // stage of MFMA work (2048 cycles at full rate) to land.
-  constexpr int NS = MX ? 2 : 4;
+  constexpr int NS = (MX && !F4) ? 2 : 4;
   bf16x8 fa[2][4], fb[2][4];   // bf16 operands
   i32x8 qa[2][4], qb[2][4];    // MXFP8 operands
+  i32x4 pa[2][4], pb[2][4];    // MXFP4 operands
   int sca[2][4], scb[2][4];    // MXFP8 scales
   // operands of sub-step j of a stage into register set buf
   auto read_frags = [&](const uint16_t* a_st, const uint16_t* b_st, const uint8_t* s_st, auto j,
@@ -1147,7 +1170,19 @@ void grouped_gemm_kernel(GemmArgs g) {
     const char* ca = reinterpret_cast<const char*>(a_st);
     const char* cb = reinterpret_cast<const char*>(b_st);
     constexpr int jj = decltype(j)::value;
-    if constexpr (MX) {
+    if constexpr (F4) {
+      // a lane's 16-byte operand of a 64-deep step: 32 values, the whole
+      // E8M0 block 2 j + h of the stage row (chunk 2 j + h, as a bf16
+      // sub-step reads), scaled by that block's scale
+      sfor<4>([&](auto i) {
+        pa[buf][i] = *reinterpret_cast<const i32x4*>(ca + a_off[jj] + i * 32 * kRowBytes);
+        pb[buf][i] = *reinterpret_cast<const i32x4*>(cb + b_off[jj] + i * 32 * kRowBytes);
+      });
+      sfor<4>([&](auto i) {
+        sca[buf][i] = s_st[sa_off4 + i * 256 + jj * 64];
+        scb[buf][i] = s_st[sb_off4 + i * 256 + jj * 64];
+      });
+    } else if constexpr (MX) {
       // a lane's 32-byte operand of a 64-deep step: chunks 4 j + h and
       // 4 j + 2 + h, the layout v_mfma_scale_f32_32x32x64_f8f6f4 takes
       sfor<4>([&](auto i) {
@@ -1198,7 +1233,12 @@ void grouped_gemm_kernel(GemmArgs g) {
   // C^T blocks: B operand first, so a lane owns one output row
   auto mfma_all = [&](auto buf) {
     sfor<4>([&](auto mi) { sfor<4>([&](auto ni) {
-      if constexpr (MX)
+      if constexpr (F4)
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            __builtin_shufflevector(pb[buf][ni], pb[buf][ni], 0, 1, 2, 3, -1, -1, -1, -1),
+            __builtin_shufflevector(pa[buf][mi], pa[buf][mi], 0, 1, 2, 3, -1, -1, -1, -1),
+            acc[mi][ni], 4, 4, 0, scb[buf][ni], 0, sca[buf][mi]);
+      else if constexpr (MX)
         acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             qb[buf][ni], qa[buf][mi], acc[mi][ni], 0, 0, 0, scb[buf][ni], 0, sca[buf][mi]);
       else
@@ -1207,8 +1247,8 @@ void grouped_gemm_kernel(GemmArgs g) {
     }); });
   };
   // LDS reads per sub-step and DMA loads per stage (per wave)
-  constexpr int kReads = MX ? 24 : (kTN ? 16 : (NN ? 12 : 8));
-  constexpr int kLoads = 16 + (MX ? 2 : 0);
+  constexpr int kReads = F4 ? 16 : (MX ? 24 : (kTN ? 16 : (NN ? 12 : 8)));
+  constexpr int kLoads = 16 + (MX ? ScaleLoader<F4>::kInstr : 0);
   // issue order: reads spread between the 16 MFMAs of a sub-step; in the
   // last sub-step of a stage the next stage's DMA loads go in between too
   // (a DMA load blocks the wave until the address unit takes it)

@@ -31,6 +31,7 @@ hipError_t launch_repack_interleave(const void* src, void* dst, int E, int I,
                                     int H, int block, int inverse, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const moe_quant_args& a, hipStream_t s);
+hipError_t launch_quantize_mxfp4(const moe_quant_args& a, hipStream_t s);  // ROW only
 // direction 0: a = bf16(p * act(z)) (+ amax); 1: dz, dprobs from dA and z
 hipError_t launch_glu_unfused(int direction, const int32_t* split, const int32_t* padded, int E,
                               int I, int64_t rows, const ActP& act, const float* probs,
@@ -91,6 +92,9 @@ struct GemmArgs {
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, int epi, bool b_nn, bool mx,
                                int grid, hipStream_t s);
+// MXFP4 operands (A, B: packed E2M1 codes, K / 2 bytes per row; b_stride
+// in values), plain store, no split-K
+hipError_t launch_gemm_store_f4(const GemmArgs& g, int grid, hipStream_t s);
 int grouped_gemm_tile_n();  // BN of the launched configuration
 // bytes of split_ws + split_cnt for a grid of `grid` workgroups
 size_t grouped_gemm_split_bytes(int grid);

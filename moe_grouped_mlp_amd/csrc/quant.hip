@@ -155,7 +155,79 @@ int quant_grid(int64_t work_items, int per_block) {
   return b < 1 ? 1 : static_cast<int>(b);
 }
 
+// E2M1 code of a scaled value |v| < 8, round to nearest even, 6 for (5, 8):
+// one step up at each midpoint, ties (0.25, 1.25, 2.5, 5) staying on the
+// even code and (0.75, 1.75, 3.5) moving up to it.
+MOE_DEV uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+               (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// x [batch][rows][cols] -> q [batch][rows][cols / 2] (two E2M1 codes a byte,
+// element 2 i in the low nibble), s tiled (R = rows, K = cols); the MXFP8
+// row kernel's unit walk, a lane encoding one 32-value block into 16 bytes.
+// Scale 2^(floor(log2 amax) - 2), 2 being the exponent of E2M1's largest
+// value 6; the bf16 input times 2^-e is exact in fp32.
+__global__ __launch_bounds__(256) void quant_row_fp4_kernel(const uint16_t* __restrict__ x,
+                                                            int64_t x_stride, int batch,
+                                                            int rows, int cols,
+                                                            uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ s) {
+  const int lane = threadIdx.x & 63;
+  const int units_r = rows / 32, units_c = cols / 64;
+  const int64_t units = static_cast<int64_t>(batch) * units_r * units_c;
+  const int64_t per_batch = static_cast<int64_t>(rows) * cols;
+  for (int64_t u = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64; u < units;
+       u += static_cast<int64_t>(gridDim.x) * blockDim.x / 64) {
+    const int bi = static_cast<int>(u / (static_cast<int64_t>(units_r) * units_c));
+    const int rem = static_cast<int>(u % (static_cast<int64_t>(units_r) * units_c));
+    const int ur = rem / units_c, uc = rem % units_c;
+    const int row = ur * 32 + (lane & 31);
+    const int col = uc * 64 + 32 * (lane >> 5);
+    const uint4* src = reinterpret_cast<const uint4*>(x + bi * x_stride +
+                                                      static_cast<int64_t>(row) * cols + col);
+    uint32_t w[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = src[j];
+      w[4 * j] = v.x; w[4 * j + 1] = v.y; w[4 * j + 2] = v.z; w[4 * j + 3] = v.w;
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = max(m, max(bf16_abs_bits(w[i]), bf16_abs_bits(w[i] >> 16)));
+    int e = static_cast<int>((m >> 7) & 0xffu) - 127 - 2;
+    e = e < -127 ? -127 : e;
+    const float inv = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+    uint32_t packed[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t p = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t b = w[4 * i + j];
+        p |= e2m1_code(__uint_as_float(b << 16) * inv) << (8 * j);
+        p |= e2m1_code(__uint_as_float(b & 0xffff0000u) * inv) << (8 * j + 4);
+      }
+      packed[i] = p;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(q + bi * (per_batch / 2) +
+                                          (static_cast<int64_t>(row) * cols + col) / 2);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    s[bi * (per_batch / 32) + (static_cast<int64_t>(ur) * units_c + uc) * 64 + lane] =
+        static_cast<uint8_t>(e + 127);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_mxfp4(const moe_quant_args& a, hipStream_t st) {
+  const int64_t units = static_cast<int64_t>(a.batch) * (a.rows / 32) * (a.cols / 64);
+  quant_row_fp4_kernel<<<quant_grid(units, 4), 256, 0, st>>>(
+      static_cast<const uint16_t*>(a.x), a.x_stride, a.batch, a.rows, a.cols, a.q, a.s);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_mxfp8(const moe_quant_args& a, hipStream_t st) {
   const uint16_t* x = static_cast<const uint16_t*>(a.x);

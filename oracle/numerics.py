@@ -14,6 +14,14 @@ Formats (sources):
   * Scale rule (the pages only say "one scale per 32 values"; the rule
     taken is 2^(floor(log2 amax) - 8), 8 being the exponent of E4M3's
     largest finite value), clamped to E8M0's range 2^-127 .. 2^127.
+  * MXFP4: E2M1 elements with one E8M0 scale per 32 values -- the 4-bit
+    member of the same microscaling family, the MI355X counterpart of the
+    NVFP4 recipe of the fusion-kernels blog ("Boosting MoE Training
+    Throughput with Advanced Fusion Kernels", § "Fused MXFP8 and NVFP4
+    quantization"), which names the format but not its rules.  E2M1:
+    exponent bias 1, 1 mantissa bit, subnormals m * 0.5, no infinities or
+    NaN, largest value 6 = 1.5 * 2^2.  Scale 2^(floor(log2 amax) - 2) (2
+    being the exponent of 6); scaled values in (6, 8) saturate to 6.
 
 Every conversion here works on exponents taken from the floating-point
 representation (numpy.frexp / numpy.ldexp), never on a floating log2, and
@@ -174,3 +182,86 @@ def mx_round(x: np.ndarray, axis: int = -1) -> np.ndarray:
     """dequant(quant(x)): the values an MXFP8 operand carries."""
     c, s = mx_quantize(x, axis)
     return mx_dequantize(c, s, axis)
+
+
+# ---------------------------------------------------------------- MXFP4 ---
+E2M1_MAX = 6.0
+E2M1_EMAX = 2              # exponent of the largest value
+E2M1_MIN_EXP = 0           # smallest normal exponent (1.0)
+E2M1_MANT_BITS = 1
+
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """4-bit E2M1 codes (0..15, in any integer array) -> float64."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    ef = (c >> 1) & 0x3
+    m = c & 0x1
+    mag = np.where(ef == 0, m * 0.5, np.ldexp(1.0 + m / 2.0, ef - 1))
+    return sign * mag
+
+
+def e2m1_encode(v: np.ndarray) -> np.ndarray:
+    """float64 -> E2M1 code (uint8 0..15), round to nearest even,
+    saturating at +-6; the sign is kept (-0 gives 0x8).  Inputs must be
+    finite."""
+    v = np.asarray(v, dtype=np.float64)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("E2M1 has no encoding for NaN or inf")
+    neg = np.signbit(v)
+    r = _round_to_grid(np.abs(v), E2M1_MANT_BITS + 1, E2M1_MIN_EXP)
+    r = np.minimum(r, E2M1_MAX)
+    _, e = np.frexp(r)
+    e2 = e - 1                              # r in [2^e2, 2^(e2+1))
+    sub = r < 1.0
+    m_sub = r * 2.0                         # 0 or 1 (0.5 steps)
+    m_norm = np.ldexp(r, -e2) * 2.0 - 2.0   # mantissa bit
+    code = np.where(sub, m_sub, ((e2 + 1) << 1) + m_norm).astype(np.int64)
+    return (code | np.where(neg, 0x8, 0)).astype(np.uint8)
+
+
+def mxfp4_quantize(x: np.ndarray, axis: int = -1, block: int = MX_BLOCK):
+    """MXFP4-encode finite float64 `x` in blocks of `block` along `axis`.
+
+    Returns (codes uint8 0..15, one per value, same shape as x; scales
+    uint8 E8M0 codes, that axis divided by `block`).  The scale exponent is
+    floor(log2 amax) - 2, clamped to [-127, 127]; an all-zero block gets
+    scale code 0 and zero codes."""
+    x = np.asarray(x, dtype=np.float64)
+    xm = np.moveaxis(x, axis, -1)
+    n = xm.shape[-1]
+    if n % block:
+        raise ValueError(f"axis length {n} is not a multiple of {block}")
+    blk = xm.reshape(xm.shape[:-1] + (n // block, block))
+    amax = np.max(np.abs(blk), axis=-1)
+    _, e = np.frexp(amax)                   # amax in [2^(e-1), 2^e)
+    ex = np.where(amax > 0, (e - 1) - E2M1_EMAX, -127)
+    ex = np.clip(ex, -127, 127).astype(np.int64)
+    codes = e2m1_encode(np.ldexp(blk, -ex[..., None]))
+    scales = (ex + 127).astype(np.uint8)
+    codes = np.moveaxis(codes.reshape(xm.shape), -1, axis)
+    return codes, np.moveaxis(scales, -1, axis)
+
+
+def mxfp4_dequantize(codes: np.ndarray, scales: np.ndarray, axis: int = -1,
+                     block: int = MX_BLOCK) -> np.ndarray:
+    """Inverse of mxfp4_quantize (exact, float64)."""
+    cm = np.moveaxis(np.asarray(codes), axis, -1)
+    sm = np.moveaxis(np.asarray(scales, dtype=np.uint8), axis, -1)
+    n = cm.shape[-1]
+    vals = e2m1_decode(cm).reshape(cm.shape[:-1] + (n // block, block))
+    out = np.ldexp(vals, (sm.astype(np.int64) - 127)[..., None])
+    return np.moveaxis(out.reshape(cm.shape), -1, axis)
+
+
+def mxfp4_round(x: np.ndarray, axis: int = -1) -> np.ndarray:
+    """dequant(quant(x)): the values an MXFP4 operand carries."""
+    c, s = mxfp4_quantize(x, axis)
+    return mxfp4_dequantize(c, s, axis)
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """4-bit codes along the last axis -> bytes, element 2i in the low
+    nibble of byte i."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)

@@ -169,6 +169,11 @@ def test_unfused_baseline_validation():
     assert _call("moe_grouped_gemm", gemm(b_kn=1, b_stride=256 * 128)) == DEVICE
     mx = dict(prec=B.PREC_MXFP8, a_s=64, b_s=64)
     assert _call("moe_grouped_gemm", gemm(**mx)) == DEVICE
+    f4 = dict(prec=B.PREC_MXFP4, a_s=64, b_s=64)
+    assert _call("moe_grouped_gemm", gemm(**f4)) == DEVICE
+    for bad in (dict(f4, b_kn=1), dict(f4, b_s=None), dict(f4, M_cap=1000),
+                dict(f4, b_stride=256 * 128 + 1)):
+        assert _call("moe_grouped_gemm", gemm(**bad)) == INVALID, bad
     for bad in (dict(N=100), dict(K=32), dict(E=0), dict(b_kn=2), dict(a=None),
                 dict(c=None), dict(b_stride=5), dict(cu_margin=-1), dict(M_cap=0),
                 dict(prec=9), dict(mx, b_kn=1), dict(mx, a_s=None),
@@ -315,6 +320,17 @@ def test_quantize_validation():
     assert _call("moe_quantize_mxfp8", _quant_args(x_stride=128 * 192 - 8)) == INVALID
     assert _call("moe_quantize_mxfp8", _quant_args(x_stride=128 * 192 + 4)) == INVALID
     assert _call("moe_quantize_mxfp8", _quant_args(x_stride=128 * 192 + 8)) == DEVICE
+
+
+def test_quantize_mxfp4_validation():
+    assert _call("moe_quantize_mxfp4", _quant_args()) == DEVICE
+    assert _call("moe_quantize_mxfp4", _quant_args(rows=96)) == DEVICE      # % 32 is enough
+    assert _call("moe_quantize_mxfp4", _quant_args(mode=B.QUANT_COL)) == INVALID
+    assert _call("moe_quantize_mxfp4", _quant_args(rows=80)) == INVALID     # % 32
+    assert _call("moe_quantize_mxfp4", _quant_args(cols=160)) == INVALID    # % 64
+    assert _call("moe_quantize_mxfp4", _quant_args(amax=64)) == INVALID
+    assert _call("moe_quantize_mxfp4", _quant_args(q=None)) == INVALID
+    assert _call("moe_quantize_mxfp4", _quant_args(x_stride=128 * 192 + 4)) == INVALID
 
 
 def test_permute_write_mx_validation():

@@ -203,3 +203,72 @@ def test_mx_roundtrip_and_nonfinite_blocks():
     bad[0, 5] = np.nan
     c, s = nu.mx_quantize(bad, axis=1)
     assert s[0, 0] == 0xFF and np.all((c & 0x7F) == 0x7F)
+
+
+# ---------------------------------------------------------------- MXFP4 ---
+# E2M1 magnitudes of codes 0..7 as the OCP microscaling format lists them
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_decode_matches_value_table():
+    vals = nu.e2m1_decode(np.arange(16))
+    np.testing.assert_array_equal(vals[:8], E2M1_TABLE)
+    np.testing.assert_array_equal(vals[8:], [-v for v in E2M1_TABLE])
+    assert np.signbit(vals[8])
+
+
+def _e2m1_brute(v):
+    """Nearest of the 16 codes by search; ties to the code whose mantissa
+    bit is 0; magnitudes past 6 saturate."""
+    out = []
+    for x in v:
+        a = min(abs(x), 6.0)
+        d = [abs(a - t) for t in E2M1_TABLE]
+        best = min(d)
+        cands = [c for c in range(8) if d[c] == best]
+        c = cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0]
+        out.append(c | (8 if np.signbit(x) else 0))
+    return np.array(out, dtype=np.uint8)
+
+
+def test_e2m1_encode_matches_brute_force():
+    rng = np.random.default_rng(0)
+    mids = [(a + b) / 2 for a, b in zip(E2M1_TABLE, E2M1_TABLE[1:])]
+    v = np.concatenate([rng.uniform(-9, 9, 4000), mids, [-m for m in mids],
+                        E2M1_TABLE, [7.0, 8.0, 100.0, -0.0, 1e-9]])
+    np.testing.assert_array_equal(nu.e2m1_encode(v), _e2m1_brute(v))
+
+
+@pytest.mark.parametrize("k", [-130, -20, 0, 5, 120])
+def test_mxfp4_scale_rule_closed_form(k):
+    """A block whose largest magnitude lies in [4, 8) * 2^k gets scale 2^k
+    (clamped to E8M0's range), and values on the E2M1 grid times that scale
+    come back exactly."""
+    rng = np.random.default_rng(k + 200)
+    kc = max(k, -127)
+    codes = rng.integers(0, 16, size=(3, 64)).astype(np.uint8)
+    codes[:, 0] = 0x7          # 6: amax in every block
+    codes[:, 32] = 0xE         # -4
+    x = np.ldexp(nu.e2m1_decode(codes), kc)
+    q, s = nu.mxfp4_quantize(x, axis=1)
+    assert np.all(s == kc + 127)
+    np.testing.assert_array_equal(nu.mxfp4_dequantize(q, s, axis=1), x)
+    # amax 7.9 * 2^k still takes scale 2^k and saturates to 6
+    y = x.copy()
+    y[:, 0] = np.ldexp(7.9, kc)
+    q2, s2 = nu.mxfp4_quantize(y, axis=1)
+    assert np.all(s2 == kc + 127) and np.all(q2[:, 0] == 0x7)
+
+
+def test_mxfp4_zero_block_and_blocks_along_axis():
+    x = np.zeros((64, 2))
+    x[33, 1] = 3.0
+    q, s = nu.mxfp4_quantize(x, axis=0)
+    assert s.shape == (2, 2) and s[0, 0] == 0 and s[0, 1] == 0 and s[1, 0] == 0
+    assert s[1, 1] == 126      # amax 3: 2^(floor(log2 3) - 2) = 2^-1
+    np.testing.assert_array_equal(nu.mxfp4_dequantize(q, s, axis=0), x)
+
+
+def test_pack_nibbles_low_first():
+    c = np.array([[1, 2, 3, 15]], dtype=np.uint8)
+    np.testing.assert_array_equal(nu.pack_nibbles(c), [[0x21, 0xF3]])
