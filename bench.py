@@ -34,7 +34,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}   # MI355X dense MFMA, published
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0,    # MI355X dense MFMA, published
+               "mxfp4": 10100.0}
 PEAK_HBM_GBS = 8000.0
 
 # name -> workload config (workloads.gen.CONFIGS) and default precision
@@ -175,6 +176,103 @@ def cpu_baseline(cfg, seed, mx=False, target_s=15.0):
                        f"{runs} runs, {done_flops / 1e12:.3f} TFLOP in {t_used:.1f} s")}
 
 
+def gemm_bench(args):
+    """--gemm: the FC2-shaped plain grouped GEMM (A = a [M][I], B = W2
+    [E][H][I], the config's routed group sizes) through moe_grouped_gemm in
+    bf16, MXFP8 and MXFP4, operands quantized before the timed region (the
+    weights once per update; a by moe_quantize_mxfp8 / _mxfp4, timed on its
+    own).  Prints one JSON line whose value is the MXFP4 rate."""
+    import numpy as np
+    import torch
+    import moe_grouped_mlp_amd as mg
+    from workloads.gen import CONFIGS, route_inputs
+    wl_name, _ = BENCH_CONFIGS[args.config]
+    cfg = dict(CONFIGS[wl_name])
+    E, k, T, H, I = (cfg[n] for n in ("E", "k", "T", "H", "I"))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    idx, _ = route_inputs(cfg, args.seed, T, E, k)
+    flat = idx.reshape(-1)
+    sizes = np.bincount(flat[(flat >= 0) & (flat < E)], minlength=E).tolist()
+    pad = [0]
+    for n in sizes:
+        pad.append(pad[-1] + -(-n // mg.GROUP_ALIGN) * mg.GROUP_ALIGN)
+    M, M_cap, N, K = sum(sizes), max(pad[-1], 128), H, I
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    a = torch.randn(M_cap, K, generator=g, device=dev).to(torch.bfloat16)
+    w = (torch.randn(E, N, K, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    out = torch.empty(M_cap, N, dtype=torch.bfloat16, device=dev)
+    split = torch.tensor(sizes, dtype=torch.int32, device=dev)
+    padded = torch.tensor(pad, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, mg.moe_grouped_mlp_workspace_size(E, N, K, M_cap)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    u8 = dict(dtype=torch.uint8, device=dev)
+    flops = 2.0 * M * N * K
+    evs = HipEvents(2)
+    kernels = {}
+
+    def timed(fn, n):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs.record(0, stream)
+        for _ in range(n):
+            fn()
+        evs.record(1, stream)
+        torch.cuda.synchronize()
+        return evs.elapsed_ms(0, 1) / n
+
+    for prec in ("bf16", "mxfp8", "mxfp4"):
+        log(f"grouped GEMM {prec}: E={E} M={M} N={N} K={K}")
+        if prec == "bf16":
+            args_ = dict(a=a, b=w, prec=mg.PREC_BF16, workspace=ws)
+        else:
+            f4 = prec == "mxfp4"
+            div = 2 if f4 else 1
+            a_q, a_s = torch.empty(M_cap * K // div, **u8), torch.empty(M_cap * K // 32, **u8)
+            b_q, b_s = torch.empty(E * N * K // div, **u8), torch.empty(E * N * K // 32, **u8)
+            if f4:
+                qa = lambda: mg.moe_quantize_mxfp4(batch=1, rows=M_cap, cols=K, x=a, q=a_q,
+                                                   s=a_s)
+                mg.moe_quantize_mxfp4(batch=E, rows=N, cols=K, x=w, q=b_q, s=b_s)
+            else:
+                qa = lambda: mg.moe_quantize_mxfp8(mode=mg.QUANT_ROW, batch=1, rows=M_cap,
+                                                   cols=K, x=a, q=a_q, s=a_s)
+                mg.moe_quantize_mxfp8(mode=mg.QUANT_ROW, batch=E, rows=N, cols=K, x=w,
+                                      q=b_q, s=b_s)
+            qms = timed(qa, args.steps)
+            kernels[f"quantize_a_{prec}"] = {
+                "ms": round(qms, 4), "unit": "GB/s",
+                "rate": round(M_cap * K * (2 + 1 / div + 1 / 32) / (qms * 1e-3) / 1e9, 1)}
+            args_ = dict(a=a_q, b=b_q, a_s=a_s, b_s=b_s,
+                         prec=mg.PREC_MXFP4 if f4 else mg.PREC_MXFP8)
+        ms = timed(lambda: mg.moe_grouped_gemm(E=E, N=N, K=K, M_cap=M_cap, split_sizes=split,
+                                               padded_offsets=padded, c=out, **args_),
+                   args.steps)
+        tf = flops / (ms * 1e-3) / 1e12
+        kernels[f"gemm_{prec}"] = {"ms": round(ms, 4), "unit": "TFLOP/s", "rate": round(tf, 2),
+                                   "pct_peak": round(100 * tf / PEAK_TFLOPS[prec], 2)}
+        log(f"  {ms:.3f} ms, {tf:.1f} TFLOP/s ({100 * tf / PEAK_TFLOPS[prec]:.1f}% of peak)")
+    evs.close()
+    f4 = kernels["gemm_mxfp4"]
+    print(json.dumps({
+        "metric": "FC2-shaped grouped GEMM TFLOP/s, MXFP4 operands, 1 GPU",
+        "value": f4["rate"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": f4["ms"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4-e2m1", "data": "synthetic",
+        "config": {"workload": f"{args.config} FC2 grouped GEMM: E={E} routed rows {M} "
+                               f"(group sizes of the layer's routing) x N={N} x K={K}",
+                   "E": E, "M": M, "N": N, "K": K},
+        "kernels": kernels,
+        "roofline": {"bound": "mfma", "kernel": "MXFP4 grouped GEMM (plain store)",
+                     "achieved": f4["rate"], "peak": PEAK_TFLOPS["mxfp4"], "unit": "TFLOP/s",
+                     "frac": round(f4["rate"] / PEAK_TFLOPS["mxfp4"], 4), "traffic": None,
+                     "avg_launch_ms": f4["ms"]},
+        "cpu_baseline": None}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +286,8 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="the unfused baseline (bf16): plain grouped GEMMs with the "
                          "activation and its gradient as separate passes")
+    ap.add_argument("--gemm", action="store_true",
+                    help="time the FC2-shaped plain grouped GEMM in bf16, MXFP8 and MXFP4")
     ap.add_argument("--recompute", action="store_true",
                     help="activation recompute: the forward stores no z, the backward "
                          "rebuilds it with FC1's GEMM (timed as fc1_recompute)")
@@ -202,6 +302,8 @@ def main():
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.gemm:
+        return gemm_bench(args)
 
     import torch
     import moe_grouped_mlp_amd as mg
