@@ -115,3 +115,50 @@ def test_grouped_gemm_mxfp4_parity(case):
         assert_close(got[rows], ref, f"expert {e}")
     # rows outside the groups are not written
     assert np.all(got[~valid] == -7.0)
+
+
+@pytest.mark.timeout(600)
+def test_mixtral_fc2_mxfp4_full_size_sampled():
+    """The Mixtral-shaped FC2 GEMM at full size (E = 8, 16384 routed rows
+    with the layer's group sizes, N = 4096, K = 14336), in the launch
+    configuration bench.py --gemm times: sampled rows' codes and scales bit
+    for bit, and 256 sampled outputs against the oracle's float64 dot
+    products of its own MXFP4 encoding of the same bf16 rows."""
+    from workloads.gen import CONFIGS, route_inputs
+    cfg = dict(CONFIGS["mixtral"])
+    E, k, T, N, K = cfg["E"], cfg["k"], cfg["T"], cfg["H"], cfg["I"]
+    idx, _ = route_inputs(cfg, 0, T, E, k)
+    flat = idx.reshape(-1)
+    sizes = np.bincount(flat[(flat >= 0) & (flat < E)], minlength=E).tolist()
+    pad = _groups(sizes)
+    M_cap = pad[-1]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    a = torch.randn(M_cap, K, generator=g, device="cuda").to(torch.bfloat16)
+    w = (torch.randn(E, N, K, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    a_q, a_s = torch.empty(M_cap, K // 2, **u8), torch.empty(M_cap * K // 32, **u8)
+    b_q, b_s = torch.empty(E * N * K // 2, **u8), torch.empty(E * N * K // 32, **u8)
+    mg.moe_quantize_mxfp4(batch=1, rows=M_cap, cols=K, x=a, q=a_q, s=a_s)
+    mg.moe_quantize_mxfp4(batch=E, rows=N, cols=K, x=w, q=b_q, s=b_s)
+    out = torch.empty(M_cap, N, dtype=torch.bfloat16, device="cuda")
+    mg.moe_grouped_gemm(E=E, N=N, K=K, M_cap=M_cap,
+                        split_sizes=torch.tensor(sizes, dtype=torch.int32, device="cuda"),
+                        padded_offsets=torch.tensor(pad, dtype=torch.int32, device="cuda"),
+                        a=a_q, b=b_q, c=out, prec=mg.PREC_MXFP4, a_s=a_s, b_s=b_s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    got, ref = [], []
+    s_plain = mx_scales_plain(a_s, M_cap, K)
+    for e in range(E):
+        rows = pad[e] + rng.choice(sizes[e], 4, replace=False)
+        cols = rng.choice(N, 8, replace=False)
+        a_rows = nu.bf16_to_f64(a[rows].view(torch.int16).cpu().numpy().view(np.uint16))
+        codes, scales = nu.mxfp4_quantize(a_rows, axis=1)
+        np.testing.assert_array_equal(a_q[rows].cpu().numpy(), nu.pack_nibbles(codes))
+        np.testing.assert_array_equal(s_plain[rows], scales)
+        w_rows = nu.bf16_to_f64(w[e, cols].view(torch.int16).cpu().numpy().view(np.uint16))
+        prod = nu.mxfp4_round(a_rows, axis=1) @ nu.mxfp4_round(w_rows, axis=1).T
+        ref.append(nu.round_bf16(prod).reshape(-1))
+        got.append(out[rows][:, cols].float().cpu().numpy().astype(np.float64).reshape(-1))
+    assert_close(np.concatenate(got), np.concatenate(ref), "sampled outputs")
