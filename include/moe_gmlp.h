@@ -250,10 +250,14 @@ moe_status moe_quantize_mxfp8(const moe_quant_args* args, void* stream);
  *   e = clamp(floor(log2 max|v|) - 2, -127, 127) (-127 for an all-zero
  *   block), code e + 127; element code = E2M1 round-to-nearest-even of
  *   v / 2^e, magnitudes past 6 saturated, sign kept (-0 -> 0x8).
- *   MOE_QUANT_ROW only (any other mode is MOE_ERR_INVALID_ARG): x bf16
- *   [batch][rows][cols] -> q [batch][rows][cols / 2] bytes, two codes a
- *   byte, element 2 i in the low nibble of byte i; scales rows*cols/32 bytes
- *   per batch entry in the tiled layout of MOE_MX_BLOCK (R = rows, K = cols).
+ *   x bf16 [batch][rows][cols]; codes two a byte, element 2 i in the low
+ *   nibble of byte i; scales rows*cols/32 bytes per batch entry in the tiled
+ *   layout of MOE_MX_BLOCK.
+ *   MOE_QUANT_ROW: blocks along cols: q [batch][rows][cols / 2], scales
+ *     tiled with R = rows, K = cols.
+ *   MOE_QUANT_COL: blocks along rows, written transposed: q
+ *     [batch][cols][rows / 2], scales tiled with R = cols, K = rows
+ *     (rows % 64 == 0).
  *   rows % 32 == 0, cols % 64 == 0; amax must be NULL.  Memory-bound: reads
  *   2 bytes, writes 17/32 bytes per element.
  * ---------------------------------------------------------------------- */

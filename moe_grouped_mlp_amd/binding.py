@@ -273,9 +273,9 @@ def moe_quantize_mxfp8(*, mode, batch, rows, cols, x, q, s, x_stride=0,
            lib().moe_quantize_mxfp8(ctypes.byref(a), _stream(stream)))
 
 
-def moe_quantize_mxfp4(*, batch, rows, cols, x, q, s, x_stride=0, stream=None):
-    a = QuantArgs(QUANT_ROW, batch, rows, cols, x_stride, _ptr(x), _ptr(q), _ptr(s),
-                  None)
+def moe_quantize_mxfp4(*, batch, rows, cols, x, q, s, mode=QUANT_ROW, x_stride=0,
+                       stream=None):
+    a = QuantArgs(mode, batch, rows, cols, x_stride, _ptr(x), _ptr(q), _ptr(s), None)
     _check("moe_quantize_mxfp4",
            lib().moe_quantize_mxfp4(ctypes.byref(a), _stream(stream)))
 

@@ -87,10 +87,47 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restri
   }
 }
 
-// x [batch][rows][cols] -> q [batch][cols][rows], s tiled (R = cols, K = rows)
+// E2M1 code of a scaled value |v| < 8, round to nearest even, 6 for (5, 8):
+// one step up at each midpoint, ties (0.25, 1.25, 2.5, 5) staying on the
+// even code and (0.75, 1.75, 3.5) moving up to it.
+MOE_DEV uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+               (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// Encodes 32 bf16 values (16 packed words) into 32 E2M1 codes (4 words,
+// element 2 i in the low nibble of byte i); returns the scale exponent
+// floor(log2 amax) - 2 (2 being the exponent of E2M1's largest value 6),
+// clamped to -127.  The bf16 input times 2^-e is exact in fp32.
+MOE_DEV int mx4_encode32(const uint32_t (&w)[16], uint32_t (&packed)[4]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = max(m, max(bf16_abs_bits(w[i]), bf16_abs_bits(w[i] >> 16)));
+  int e = static_cast<int>((m >> 7) & 0xffu) - 127 - 2;
+  e = e < -127 ? -127 : e;
+  const float inv = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t p = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t b = w[4 * i + j];
+      p |= e2m1_code(__uint_as_float(b << 16) * inv) << (8 * j);
+      p |= e2m1_code(__uint_as_float(b & 0xffff0000u) * inv) << (8 * j + 4);
+    }
+    packed[i] = p;
+  }
+  return e;
+}
+
+// x [batch][rows][cols] -> q [batch][cols][rows], s tiled (R = cols, K = rows);
+// F4: MXFP4 codes, q [batch][cols][rows / 2], no amax
 constexpr int kColTileR = 64, kColTileC = 128;
 constexpr int kColPitch = kColTileC + 2;  // bf16 per LDS row (odd word stride)
 
+template <bool F4>
 __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restrict__ x,
                                                         int64_t x_stride, int batch, int rows,
                                                         int cols, uint8_t* __restrict__ q,
@@ -127,15 +164,24 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
         w[i] = static_cast<uint32_t>(tile[r * kColPitch + c]) |
                (static_cast<uint32_t>(tile[(r + 1) * kColPitch + c]) << 16);
       }
-      uint32_t codes[8];
-      const int e = mx_encode32(w, codes);
       const int cc = c0 + c;
-      uint4* dst = reinterpret_cast<uint4*>(q + bi * per_batch_q + static_cast<int64_t>(cc) * rows +
-                                            r0 + 32 * half);
-      dst[0] = make_uint4(codes[0], codes[1], codes[2], codes[3]);
-      dst[1] = make_uint4(codes[4], codes[5], codes[6], codes[7]);
-      s[bi * (per_batch_q / 32) + mx_scale_off(cc, r0 / 32 + half, rows)] = mx_scale_code(e);
-      if (amax) {
+      const int64_t qoff = bi * per_batch_q + static_cast<int64_t>(cc) * rows + r0 + 32 * half;
+      int e;
+      if constexpr (F4) {
+        uint32_t packed[4];
+        e = mx4_encode32(w, packed);
+        *reinterpret_cast<uint4*>(q + qoff / 2) =
+            make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      } else {
+        uint32_t codes[8];
+        e = mx_encode32(w, codes);
+        uint4* dst = reinterpret_cast<uint4*>(q + qoff);
+        dst[0] = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+        dst[1] = make_uint4(codes[4], codes[5], codes[6], codes[7]);
+      }
+      s[bi * (per_batch_q / 32) + mx_scale_off(cc, r0 / 32 + half, rows)] =
+          static_cast<uint8_t>(e + 127);
+      if (!F4 && amax) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           wmax = max(wmax, max(bf16_abs_bits(w[i]), bf16_abs_bits(w[i] >> 16)));
@@ -153,16 +199,6 @@ int quant_grid(int64_t work_items, int per_block) {
   int64_t b = (work_items + per_block - 1) / per_block;
   if (b > 8192) b = 8192;
   return b < 1 ? 1 : static_cast<int>(b);
-}
-
-// E2M1 code of a scaled value |v| < 8, round to nearest even, 6 for (5, 8):
-// one step up at each midpoint, ties (0.25, 1.25, 2.5, 5) staying on the
-// even code and (0.75, 1.75, 3.5) moving up to it.
-MOE_DEV uint32_t e2m1_code(float v) {
-  const float a = fabsf(v);
-  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
-               (a >= 3.5f) + (a > 5.0f);
-  return c | ((__float_as_uint(v) >> 28) & 8u);
 }
 
 // x [batch][rows][cols] -> q [batch][rows][cols / 2] (two E2M1 codes a byte,
@@ -194,24 +230,8 @@ __global__ __launch_bounds__(256) void quant_row_fp4_kernel(const uint16_t* __re
       const uint4 v = src[j];
       w[4 * j] = v.x; w[4 * j + 1] = v.y; w[4 * j + 2] = v.z; w[4 * j + 3] = v.w;
     }
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) m = max(m, max(bf16_abs_bits(w[i]), bf16_abs_bits(w[i] >> 16)));
-    int e = static_cast<int>((m >> 7) & 0xffu) - 127 - 2;
-    e = e < -127 ? -127 : e;
-    const float inv = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
     uint32_t packed[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t p = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t b = w[4 * i + j];
-        p |= e2m1_code(__uint_as_float(b << 16) * inv) << (8 * j);
-        p |= e2m1_code(__uint_as_float(b & 0xffff0000u) * inv) << (8 * j + 4);
-      }
-      packed[i] = p;
-    }
+    const int e = mx4_encode32(w, packed);
     uint4* dst = reinterpret_cast<uint4*>(q + bi * (per_batch / 2) +
                                           (static_cast<int64_t>(row) * cols + col) / 2);
     dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
@@ -223,9 +243,17 @@ __global__ __launch_bounds__(256) void quant_row_fp4_kernel(const uint16_t* __re
 }  // namespace
 
 hipError_t launch_quantize_mxfp4(const moe_quant_args& a, hipStream_t st) {
-  const int64_t units = static_cast<int64_t>(a.batch) * (a.rows / 32) * (a.cols / 64);
-  quant_row_fp4_kernel<<<quant_grid(units, 4), 256, 0, st>>>(
-      static_cast<const uint16_t*>(a.x), a.x_stride, a.batch, a.rows, a.cols, a.q, a.s);
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  if (a.mode == MOE_QUANT_ROW) {
+    const int64_t units = static_cast<int64_t>(a.batch) * (a.rows / 32) * (a.cols / 64);
+    quant_row_fp4_kernel<<<quant_grid(units, 4), 256, 0, st>>>(x, a.x_stride, a.batch, a.rows,
+                                                               a.cols, a.q, a.s);
+  } else {
+    const int64_t tiles = static_cast<int64_t>(a.batch) * (a.rows / kColTileR) *
+                          ((a.cols + kColTileC - 1) / kColTileC);
+    quant_col_kernel<true><<<quant_grid(tiles, 1), 256, 0, st>>>(x, a.x_stride, a.batch, a.rows,
+                                                                 a.cols, a.q, a.s, nullptr);
+  }
   return hipGetLastError();
 }
 
@@ -238,7 +266,7 @@ hipError_t launch_quantize_mxfp8(const moe_quant_args& a, hipStream_t st) {
   } else {
     const int64_t tiles = static_cast<int64_t>(a.batch) * (a.rows / kColTileR) *
                           ((a.cols + kColTileC - 1) / kColTileC);
-    quant_col_kernel<<<quant_grid(tiles, 1), 256, 0, st>>>(x, a.x_stride, a.batch, a.rows, a.cols,
+    quant_col_kernel<false><<<quant_grid(tiles, 1), 256, 0, st>>>(x, a.x_stride, a.batch, a.rows, a.cols,
                                                            a.q, a.s, a.amax);
   }
   return hipGetLastError();

@@ -60,7 +60,7 @@ from typing import Optional
 import numpy as np
 from scipy.special import erf
 
-from .numerics import bf16_to_f64, mx_quantize, mx_dequantize, round_bf16
+from .numerics import bf16_to_f64, mx_quantize, mx_dequantize, mxfp4_round, round_bf16
 
 ALIGN = 128          # group-start alignment of the padded row layout
 INTERLEAVE = 64      # gate/up interleave block of the repacked FC1 weight
@@ -319,8 +319,18 @@ class Backward:
     dzT_mx: Optional[tuple] = None
 
 
-def _mx_operand(v, axis, on):
-    return mx_dequantize(*mx_quantize(v, axis), axis) if on else v
+def _mx_operand(v, axis, fmt):
+    """The values a GEMM operand carries: v itself (fmt None), or its MXFP8
+    or MXFP4 encoding in blocks of 32 along `axis`, decoded."""
+    if fmt == "mxfp4":
+        return mxfp4_round(v, axis)
+    return mx_dequantize(*mx_quantize(v, axis), axis) if fmt else v
+
+
+def _operand_format(mx, rnd):
+    if not (mx and rnd):
+        return None
+    return "mxfp4" if mx == "mxfp4" else "mxfp8"
 
 
 def forward(x_bits, w1_bits, w2_bits, expert_idx, probs, E, prm: ActParams,
@@ -332,7 +342,10 @@ def forward(x_bits, w1_bits, w2_bits, expert_idx, probs, E, prm: ActParams,
     w1_bits  uint16 bf16 [E][N1][H], logical layout (N1 = 2I gated, I sReLU)
     w2_bits  uint16 bf16 [E][H][I]
     probs    float32 [T][k]
-    mx       feed MXFP8 operands to both GEMMs (blocks of 32 along K)
+    mx       feed MXFP8 operands to both GEMMs (blocks of 32 along K);
+             "mxfp4": MXFP4 operands instead [FK § Fused MXFP8 and NVFP4
+             quantization names a 4-bit recipe; E2M1 with E8M0 scales per
+             32 is its counterpart on MI355X]
     exact    skip every bf16/MX storage rounding (pure float64; used by the
              finite-difference pins)
     unfused  the layer run as separate kernels, each reading what the one
@@ -341,6 +354,7 @@ def forward(x_bits, w1_bits, w2_bits, expert_idx, probs, E, prm: ActParams,
              unfused, the activation is a separate kernel after the GEMM]
     """
     rnd = not exact
+    fmt = _operand_format(mx, rnd)
     rt = route(expert_idx, probs, E, first_expert, M_cap)
     M_cap = rt.row_src.shape[0]
     x = bf16_to_f64(x_bits) if x_bits.dtype == np.uint16 else x_bits
@@ -359,23 +373,23 @@ def forward(x_bits, w1_bits, w2_bits, expert_idx, probs, E, prm: ActParams,
         if n == 0:
             continue
         rows = slice(s0, s0 + n)
-        xe = _mx_operand(xp[rows], 1, mx and rnd)
-        w1e = _mx_operand(w1[e], 1, mx and rnd)
+        xe = _mx_operand(xp[rows], 1, fmt)
+        w1e = _mx_operand(w1[e], 1, fmt)
         ze = xe @ w1e.T                                      # FC1
         b = None if bias1 is None else bias1[e]
         ain_z = _maybe_bf16(ze, rnd) if unfused else ze
         ae = pp[rows, None] * act_forward(ain_z, prm, b)     # act + prob scale
         z[rows] = _maybe_bf16(ze, rnd)
         a[rows] = _maybe_bf16(ae, rnd)
-        ain = _mx_operand(a[rows], 1, mx and rnd)
-        w2e = _mx_operand(w2[e], 1, mx and rnd)
+        ain = _mx_operand(a[rows], 1, fmt)
+        w2e = _mx_operand(w2[e], 1, fmt)
         y[rows] = _maybe_bf16(ain @ w2e.T, rnd)              # FC2
     out = unpermute(y, rt.row_id_map, round_out=rnd)
     ex = expert_of_rows(rt)
     valid = ex >= 0
     amax = float(np.max(np.abs(a[valid]))) if valid.any() else 0.0
     fw = Forward(rt, xp, z, a, y, out, amax, ex)
-    if mx and rnd:
+    if fmt == "mxfp8":
         mp = int(rt.padded_offsets[-1])
         fw.a_mx = mx_quantize(a[:mp], 1)
         fw.aT_mx = mx_quantize(a[:mp].T, 1)
@@ -387,6 +401,7 @@ def backward(fw: Forward, dout_bits, w1_bits, w2_bits, prm: ActParams, *,
     """Backward of `forward` for the loss sum(out * dOut).  unfused: FC2
     dgrad stores dA (bf16) and the activation gradient reads it."""
     rnd = not exact
+    fmt = _operand_format(mx, rnd)
     rt = fw.rt
     E = len(rt.split_sizes)
     dout = bf16_to_f64(dout_bits) if dout_bits.dtype == np.uint16 \
@@ -405,8 +420,8 @@ def backward(fw: Forward, dout_bits, w1_bits, w2_bits, prm: ActParams, *,
         if n == 0:
             continue
         rows = slice(s0, s0 + n)
-        dye = _mx_operand(dyp[rows], 1, mx and rnd)          # along H
-        w2e = _mx_operand(w2[e], 0, mx and rnd)              # along H
+        dye = _mx_operand(dyp[rows], 1, fmt)                 # along H
+        w2e = _mx_operand(w2[e], 0, fmt)                     # along H
         da = dye @ w2e                                       # FC2 dgrad
         if unfused:
             da = _maybe_bf16(da, rnd)
@@ -416,13 +431,13 @@ def backward(fw: Forward, dout_bits, w1_bits, w2_bits, prm: ActParams, *,
         dp[rows] = np.sum(da * s, axis=1)                    # d probs_p
         dze = act_backward(ze, pp[rows, None] * da, prm, b)  # dActivation
         dz[rows] = _maybe_bf16(dze, rnd)
-        dzin = _mx_operand(dz[rows], 1, mx and rnd)          # along N1
-        w1e = _mx_operand(w1[e], 0, mx and rnd)              # along N1
+        dzin = _mx_operand(dz[rows], 1, fmt)                 # along N1
+        w1e = _mx_operand(w1[e], 0, fmt)                     # along N1
         dxp[rows] = _maybe_bf16(dzin @ w1e, rnd)             # FC1 dgrad
     dx = unpermute(dxp, rt.row_id_map, round_out=rnd)
     dprobs = gather_probs_grad(dp, rt.row_id_map)
     bw = Backward(dyp, dz, dp, dxp, dx, dprobs)
-    if mx and rnd:
+    if fmt == "mxfp8":
         mp = int(rt.padded_offsets[-1])
         bw.dz_mx = mx_quantize(dz[:mp], 1)
         bw.dzT_mx = mx_quantize(dz[:mp].T, 1)

@@ -325,7 +325,9 @@ def test_quantize_validation():
 def test_quantize_mxfp4_validation():
     assert _call("moe_quantize_mxfp4", _quant_args()) == DEVICE
     assert _call("moe_quantize_mxfp4", _quant_args(rows=96)) == DEVICE      # % 32 is enough
-    assert _call("moe_quantize_mxfp4", _quant_args(mode=B.QUANT_COL)) == INVALID
+    assert _call("moe_quantize_mxfp4", _quant_args(mode=B.QUANT_COL)) == DEVICE
+    assert _call("moe_quantize_mxfp4", _quant_args(mode=B.QUANT_COL, rows=96)) == INVALID
+    assert _call("moe_quantize_mxfp4", _quant_args(mode=2)) == INVALID
     assert _call("moe_quantize_mxfp4", _quant_args(rows=80)) == INVALID     # % 32
     assert _call("moe_quantize_mxfp4", _quant_args(cols=160)) == INVALID    # % 64
     assert _call("moe_quantize_mxfp4", _quant_args(amax=64)) == INVALID

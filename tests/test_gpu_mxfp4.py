@@ -36,9 +36,12 @@ def _with_ties(rng, bits, rows):
     return b
 
 
+@pytest.mark.parametrize("mode", [mg.QUANT_ROW, mg.QUANT_COL])
 @pytest.mark.parametrize("batch,rows,cols,pad", [(1, 32, 64, 0), (3, 128, 192, 0),
                                                  (2, 192, 2880, 40)])
-def test_quantize_mxfp4_bit_exact(batch, rows, cols, pad):
+def test_quantize_mxfp4_bit_exact(mode, batch, rows, cols, pad):
+    if mode == mg.QUANT_COL and rows % 64:
+        pytest.skip("the column mode takes rows in multiples of 64")
     rng = np.random.default_rng(rows + cols + 4)
     bits = _with_ties(rng, _hard_bf16(rng, (batch, rows, cols)), rows)
     stride = rows * cols + pad
@@ -48,17 +51,19 @@ def test_quantize_mxfp4_bit_exact(batch, rows, cols, pad):
     x = dev_bf16(flat)
     q = torch.full((batch * rows * cols // 2,), 0xAB, dtype=torch.uint8, device="cuda")
     s = torch.full((batch * rows * cols // 32,), 0xAB, dtype=torch.uint8, device="cuda")
-    mg.moe_quantize_mxfp4(batch=batch, rows=rows, cols=cols, x=x, q=q, s=s,
+    mg.moe_quantize_mxfp4(batch=batch, rows=rows, cols=cols, x=x, q=q, s=s, mode=mode,
                           x_stride=stride if pad else 0)
     torch.cuda.synchronize()
     v = nu.bf16_to_f64(bits)
-    qh = q.cpu().numpy().reshape(batch, rows, cols // 2)
+    R, K = (rows, cols) if mode == mg.QUANT_ROW else (cols, rows)
+    qh = q.cpu().numpy().reshape(batch, R, K // 2)
     sh = s.cpu().numpy().reshape(batch, -1)
     for b in range(batch):
-        codes, scales = nu.mxfp4_quantize(v[b], axis=1)
+        src = v[b] if mode == mg.QUANT_ROW else v[b].T
+        codes, scales = nu.mxfp4_quantize(src, axis=1)
         np.testing.assert_array_equal(_unpack(qh[b]), codes, f"codes, batch {b}")
         np.testing.assert_array_equal(qh[b], nu.pack_nibbles(codes))
-        np.testing.assert_array_equal(mx_scales_plain(torch.from_numpy(sh[b]), rows, cols),
+        np.testing.assert_array_equal(mx_scales_plain(torch.from_numpy(sh[b]), R, K),
                                       scales, f"scales, batch {b}")
 
 

@@ -437,3 +437,56 @@ def test_unfused_reading_only_moves_rounding_points():
     pp = fr.rt.probs_p.astype(np.float64)[v, None]
     expect = nu.round_bf16(pp * moe.act_forward(fr.z[v], prm))
     np.testing.assert_array_equal(fr.a[v], expect)
+
+
+def _mxfp4_exact_layer():
+    """A layer on which MXFP4 rounds nothing: one-hot tokens and dOut,
+    weights in {-1, 0, 1} and probabilities 1/2 with sReLU, so every GEMM
+    operand (x, W1, a = p z+^2 in {0, 1/2}, W2, dOut, dZ in {0, +-1}) is an
+    exact E2M1 value times a power of two in every 32-block."""
+    rng = np.random.default_rng(3)
+    E, k, T, H, I = 4, 2, 96, 64, 64
+    x = np.zeros((T, H))
+    x[np.arange(T), rng.integers(0, H, T)] = 1.0
+    dout = np.zeros((T, H))
+    dout[np.arange(T), rng.integers(0, H, T)] = 1.0
+    w1 = rng.integers(-1, 2, (E, I, H)).astype(np.float64)
+    w2 = rng.integers(-1, 2, (E, H, I)).astype(np.float64)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    probs = np.full((T, k), 0.5, np.float32)
+    bits = [nu.f64_to_bf16_bits(v) for v in (x, w1, w2, dout)]
+    return bits, idx, probs, E
+
+
+def test_mxfp4_reading_is_exact_on_representable_data():
+    (x, w1, w2, dout), idx, probs, E = _mxfp4_exact_layer()
+    prm = moe.ActParams(act="srelu")
+    kw = dict(unfused=True)
+    fb = moe.forward(x, w1, w2, idx, probs, E, prm, **kw)
+    f4 = moe.forward(x, w1, w2, idx, probs, E, prm, mx="mxfp4", **kw)
+    bb = moe.backward(fb, dout, w1, w2, prm, **kw)
+    b4 = moe.backward(f4, dout, w1, w2, prm, mx="mxfp4", **kw)
+    assert np.abs(fb.out).max() > 0 and np.abs(bb.dx).max() > 0
+    for u, v in ((fb.z, f4.z), (fb.a, f4.a), (fb.out, f4.out), (bb.dz, b4.dz),
+                 (bb.dx, b4.dx), (bb.dprobs, b4.dprobs)):
+        np.testing.assert_array_equal(u, v)
+
+
+def test_mxfp4_reading_rounds_every_gemm_operand():
+    """On random data each operand's MXFP4 rounding moves the results, more
+    than MXFP8's does; forward and backward both see it."""
+    wl = make_workload("tiny", seed=8)
+    prm = moe.ActParams()
+    f16 = moe.forward(wl.x, wl.w1, wl.w2, wl.expert_idx, wl.probs, wl.E, prm)
+    f8 = moe.forward(wl.x, wl.w1, wl.w2, wl.expert_idx, wl.probs, wl.E, prm, mx=True)
+    f4 = moe.forward(wl.x, wl.w1, wl.w2, wl.expert_idx, wl.probs, wl.E, prm, mx="mxfp4")
+    b16 = moe.backward(f16, wl.dout, wl.w1, wl.w2, prm)
+    b8 = moe.backward(f8, wl.dout, wl.w1, wl.w2, prm, mx=True)
+    b4 = moe.backward(f4, wl.dout, wl.w1, wl.w2, prm, mx="mxfp4")
+
+    def rel(u, v):
+        return np.linalg.norm(u - v) / np.linalg.norm(v)
+    for q8, q4, ref in ((f8.z, f4.z, f16.z), (f8.out, f4.out, f16.out),
+                        (b8.dz, b4.dz, b16.dz), (b8.dx, b4.dx, b16.dx)):
+        assert 0 < rel(q8, ref) < rel(q4, ref) < 0.5
+    assert f4.a_mx is None and b4.dz_mx is None
