@@ -279,7 +279,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral", choices=sorted(BENCH_CONFIGS))
-    ap.add_argument("--prec", choices=("bf16", "mxfp8"), default=None,
+    ap.add_argument("--prec", choices=("bf16", "mxfp8", "mxfp4"), default=None,
                     help="operand precision (default: the config's)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -312,6 +312,9 @@ def main():
     wl_name, prec_default = BENCH_CONFIGS[args.config]
     prec = args.prec or prec_default
     mx = prec == "mxfp8"
+    if prec == "mxfp4" and not args.unfused:
+        print("the MXFP4 layer runs as separate passes: add --unfused", file=sys.stderr)
+        sys.exit(2)
     if args.unfused and (args.wgrad or args.recompute):
         print("--unfused is the baseline of the fused step (no --wgrad, --recompute)",
               file=sys.stderr)
@@ -325,7 +328,8 @@ def main():
     act_kind = {"swiglu": mg.ACT_SWIGLU, "geglu": mg.ACT_GEGLU, "srelu": mg.ACT_SRELU}[cfg["act"]]
     act = mg.act_params(act_kind, beta=cfg["beta"], clamp=cfg["clamp"])
     blk = mg.ExpertBlock(E, H, I, T, k, act=act,
-                         prec=mg.PREC_MXFP8 if mx else mg.PREC_BF16, wgrad=args.wgrad,
+                         prec={"bf16": mg.PREC_BF16, "mxfp8": mg.PREC_MXFP8,
+                               "mxfp4": mg.PREC_MXFP4}[prec], wgrad=args.wgrad,
                          recompute=args.recompute, bf16_copies=True if (args.unfused and mx) else None)
     blk.load_weights(w1, w2)
     del w1, w2
@@ -539,8 +543,9 @@ def main():
         log(f"cpu oracle {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads")
 
     # the recorded counters are those of FC1 storing z
-    traffic = (measured_traffic() if (args.config == "mixtral" and not mx
-                                      and not args.recompute) else None)
+    traffic = (measured_traffic() if (args.config == "mixtral" and prec == "bf16"
+                                      and not args.recompute and not args.unfused)
+               else None)
     out = {
         "metric": "fused grouped-MLP fwd/bwd TFLOP/s and % MFMA peak, Mixtral-shaped "
                   "layer, 1 GPU",
@@ -554,7 +559,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8-e4m3" if mx else "bf16",
+        "dtype": {"bf16": "bf16", "mxfp8": "mxfp8-e4m3", "mxfp4": "mxfp4-e2m1"}[prec],
         "data": "synthetic",
         "config": {"workload": f"{args.config} expert layer: E={E} top-{k} T={T} H={H} "
                                f"I={I} {cfg['act']} beta={cfg['beta']} clamp={cfg['clamp']}, "

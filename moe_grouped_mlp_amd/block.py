@@ -59,8 +59,12 @@ class ExpertBlock:
         self.recompute = recompute
         self._z_valid = False
         self.mx = prec == B.PREC_MXFP8
+        # MXFP4: the layer as separate passes (no fused epilogue writes
+        # MXFP4): bf16 routing and activations, each GEMM operand quantized
+        # by moe_quantize_mxfp4 before an MXFP4 grouped GEMM
+        self.mx4 = prec == B.PREC_MXFP4
         M_cap = M_cap if M_cap is not None else T * k + E * (B.GROUP_ALIGN - 1)
-        if self.mx:
+        if self.mx or self.mx4:
             M_cap = -(-M_cap // B.GROUP_ALIGN) * B.GROUP_ALIGN
         self.M_cap = M_cap
         self.cu_margin = cu_margin
@@ -81,6 +85,8 @@ class ExpertBlock:
                                     dtype=torch.uint8, device=dev)
         # bf16 a and dz: operands of the bf16 GEMMs; optional with MXFP8
         keep = (not self.mx) if bf16_copies is None else (bf16_copies or not self.mx)
+        if self.mx4 and (wgrad or recompute):
+            raise ValueError("the MXFP4 layer has no weight-gradient or recompute path")
         self.z = torch.empty(M, N1, **bf)
         self.a = torch.empty(M, I, **bf) if keep else None
         self.yp = torch.empty(M, H, **bf)
@@ -122,6 +128,20 @@ class ExpertBlock:
         else:
             self.xp = torch.empty(M, H, **bf)
             self.dyp = torch.empty(M, H, **bf)
+        if self.mx4:
+            def fp4_pair(*shape):
+                n = 1
+                for d in shape:
+                    n *= d
+                return (torch.empty(n // 2, **u8), torch.empty(n // B.MX_BLOCK, **u8))
+            self.xp_q4, self.xp_s4 = fp4_pair(M, H)
+            self.a_q4, self.a_s4 = fp4_pair(M, I)
+            self.dyp_q4, self.dyp_s4 = fp4_pair(M, H)
+            self.dz_q4, self.dz_s4 = fp4_pair(M, N1)
+            self.w1_q4, self.w1_s4 = fp4_pair(E, N1, H)     # along H
+            self.w2_q4, self.w2_s4 = fp4_pair(E, H, I)      # along I
+            self.w2t_q4, self.w2t_s4 = fp4_pair(E, I, H)    # along H
+            self.w1t_q4, self.w1t_s4 = fp4_pair(E, H, N1)   # along N1
         self.wgrad = wgrad
         if wgrad:
             if self.mx:
@@ -146,7 +166,7 @@ class ExpertBlock:
         else:
             self.w1i.copy_(w1)
         self.w2.copy_(w2)
-        if self.mx:
+        if self.mx or self.mx4:
             self.quantize_weights()
 
     def quantize_weights(self) -> None:
@@ -155,6 +175,15 @@ class ExpertBlock:
         (FC2 dgrad, stored [E][I][H]) and W1i along N1 (FC1 dgrad, stored
         [E][H][N1])."""
         E, H, I, N1 = self.E, self.H, self.I, self.N1
+        if self.mx4:
+            for mode, x, rows, cols, q, sc in (
+                    (B.QUANT_ROW, self.w1i, N1, H, self.w1_q4, self.w1_s4),
+                    (B.QUANT_ROW, self.w2, H, I, self.w2_q4, self.w2_s4),
+                    (B.QUANT_COL, self.w2, H, I, self.w2t_q4, self.w2t_s4),
+                    (B.QUANT_COL, self.w1i, N1, H, self.w1t_q4, self.w1t_s4)):
+                B.moe_quantize_mxfp4(mode=mode, batch=E, rows=rows, cols=cols, x=x, q=q,
+                                     s=sc)
+            return
         for mode, x, rows, cols, q, sc in (
                 (B.QUANT_ROW, self.w1i, N1, H, self.w1_q, self.w1_s),
                 (B.QUANT_ROW, self.w2, H, I, self.w2_q, self.w2_s),
@@ -247,7 +276,10 @@ class ExpertBlock:
 
     def forward(self, x, expert_idx, probs, timing_events=None):
         self.route(expert_idx, probs, x)
-        self.experts_forward(timing_events)
+        if self.mx4:
+            self.experts_forward_unfused()
+        else:
+            self.experts_forward(timing_events)
         self.combine(self.yp, self.out)
         return self.out
 
@@ -277,7 +309,10 @@ class ExpertBlock:
             self.gather(dout, self.dyp, self.dyp_q, self.dyp_s)
         else:
             self.gather(dout, self.dyp)
-        self.experts_backward(timing_events)
+        if self.mx4:
+            self.experts_backward_unfused()
+        else:
+            self.experts_backward(timing_events)
         self.combine(self.dxp, self.dx, dprobs=True)
         return self.dx, self.dprobs
 
@@ -296,6 +331,9 @@ class ExpertBlock:
                            workspace=self.ws if split else None,
                            prec=self.prec, a_s=a_s, b_s=b_s)
 
+    def _quantize4(self, x, cols, q, s):
+        B.moe_quantize_mxfp4(batch=1, rows=self.M_cap, cols=cols, x=x, q=q, s=s)
+
     def _quantize(self, x, cols, q, s, qT, sT):
         B.moe_quantize_mxfp8(mode=B.QUANT_ROW, batch=1, rows=self.M_cap, cols=cols,
                              x=x, q=q, s=s)
@@ -308,7 +346,11 @@ class ExpertBlock:
             raise RuntimeError("the MXFP8 unfused baseline needs bf16_copies=True")
         rec = (lambda i: events.record(i)) if events else (lambda i: None)
         rec(0)
-        if self.mx:
+        if self.mx4:
+            self._quantize4(self.xp, self.H, self.xp_q4, self.xp_s4)
+            self._gemm(self.N1, self.H, self.xp_q4, self.w1_q4, self.z, self.xp_s4,
+                       self.w1_s4)
+        elif self.mx:
             self._gemm(self.N1, self.H, self.xp_q, self.w1_q, self.z, self.xp_s, self.w1_s)
         else:
             self._gemm(self.N1, self.H, self.xp, self.w1i, self.z)
@@ -317,10 +359,14 @@ class ExpertBlock:
                           split_sizes=self.split_sizes,
                           padded_offsets=self.padded_offsets, probs_p=self.probs_p,
                           z=self.z, a=self.a, amax=self.amax, act=self.act)
-        if self.mx:
+        if self.mx4:
+            self._quantize4(self.a, self.I, self.a_q4, self.a_s4)
+        elif self.mx:
             self._quantize(self.a, self.I, self.a_q, self.a_s, self.aT_q, self.aT_s)
         rec(2)
-        if self.mx:
+        if self.mx4:
+            self._gemm(self.H, self.I, self.a_q4, self.w2_q4, self.yp, self.a_s4, self.w2_s4)
+        elif self.mx:
             self._gemm(self.H, self.I, self.a_q, self.w2_q, self.yp, self.a_s, self.w2_s)
         else:
             self._gemm(self.H, self.I, self.a, self.w2, self.yp)
@@ -334,7 +380,11 @@ class ExpertBlock:
                                   device=self.z.device)
         rec = (lambda i: events.record(i)) if events else (lambda i: None)
         rec(0)
-        if self.mx:
+        if self.mx4:
+            self._quantize4(self.dyp, self.H, self.dyp_q4, self.dyp_s4)
+            self._gemm(self.I, self.H, self.dyp_q4, self.w2t_q4, self.da, self.dyp_s4,
+                       self.w2t_s4)
+        elif self.mx:
             self._gemm(self.I, self.H, self.dyp_q, self.w2t_q, self.da, self.dyp_s,
                        self.w2t_s)
         else:
@@ -345,10 +395,15 @@ class ExpertBlock:
                           padded_offsets=self.padded_offsets, probs_p=self.probs_p,
                           z=self.z, da=self.da, dz=self.dz,
                           dprobs_p=self.dprobs_p, act=self.act)
-        if self.mx:
+        if self.mx4:
+            self._quantize4(self.dz, self.N1, self.dz_q4, self.dz_s4)
+        elif self.mx:
             self._quantize(self.dz, self.N1, self.dz_q, self.dz_s, self.dzT_q, self.dzT_s)
         rec(2)
-        if self.mx:
+        if self.mx4:
+            self._gemm(self.H, self.N1, self.dz_q4, self.w1t_q4, self.dxp, self.dz_s4,
+                       self.w1t_s4)
+        elif self.mx:
             self._gemm(self.H, self.N1, self.dz_q, self.w1t_q, self.dxp, self.dz_s,
                        self.w1t_s)
         else:

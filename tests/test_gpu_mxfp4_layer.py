@@ -1,0 +1,87 @@
+"""The MXFP4 layer (ExpertBlock(prec=PREC_MXFP4): the unfused passes with
+every GEMM operand quantized by moe_quantize_mxfp4 and multiplied by the
+MXFP4 grouped GEMM) against the oracle's MXFP4 unfused reading.  Where a
+GEMM reads the MXFP4 encoding of a tensor the GPU computed (a for FC2, dz
+for FC1 dgrad), a one-ulp difference in that bf16 tensor can move an E2M1
+code by a whole step; those outputs are checked element by element against
+the oracle fed the GPU's own tensor, and against the independent oracle by
+relative L2 error."""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_mlp_amd as mg
+from oracle import numerics as nu
+from workloads import make_workload
+
+from .gpu_util import (act_of, assert_close, compare_routing, host_bits, host_f64,
+                       oracle_layer, run_gpu_layer, uninterleave_cols)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "multi_tile_ragged": dict(name="tiny", E=8, k=2, T=1024, H=640, I=320),
+    "gptoss_act": dict(name="gptoss", T=512, H=128, I=192, E=16),
+    "dsv3_zipf_empty": dict(name="dsv3", T=2000, H=256, I=128),
+    "srelu": dict(name="tiny", act="srelu", T=384, I=192),
+}
+
+
+def _rel_l2(u, v):
+    return float(np.linalg.norm(u - v) / max(np.linalg.norm(v), 1e-30))
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_mxfp4_layer_parity(case):
+    kw = dict(CASES[case])
+    wl = make_workload(kw.pop("name"), seed=9, **kw)
+    M_cap = -(-wl.m_cap() // 128) * 128
+    gp, _ = act_of(wl)
+    blk = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, act=gp, first_expert=wl.first_expert,
+                         M_cap=M_cap, prec=mg.PREC_MXFP4)
+    run_gpu_layer(wl, M_cap, block=blk)
+    fw, bw = oracle_layer(wl, M_cap, mx="mxfp4", unfused=True)
+    compare_routing(blk, fw.rt)
+    gated = wl.act != "srelu"
+    valid = fw.expert >= 0
+    pad = fw.rt.padded_offsets
+    w1 = nu.bf16_to_f64(wl.w1)
+    w2 = nu.bf16_to_f64(wl.w2)
+    np.testing.assert_array_equal(host_bits(blk.xp)[valid], nu.f64_to_bf16_bits(fw.xp[valid]))
+    z = host_f64(blk.z)[valid]
+    assert_close(uninterleave_cols(z, wl.I) if gated else z, fw.z[valid], "z")
+    a = host_f64(blk.a)
+    assert_close(a[valid], fw.a[valid], "a")
+    # FC2 on the MXFP4 encoding of the GPU's a
+    yp = host_f64(blk.yp)
+    for e in range(wl.E):
+        rows = slice(int(pad[e]), int(pad[e]) + int(fw.rt.split_sizes[e]))
+        if rows.stop == rows.start:
+            continue
+        ref = nu.round_bf16(nu.mxfp4_round(a[rows], 1) @ nu.mxfp4_round(w2[e], 1).T)
+        assert_close(yp[rows], ref, f"yp expert {e}")
+    assert _rel_l2(yp[valid], fw.y[valid]) < 2e-2
+    assert _rel_l2(host_f64(blk.out), fw.out) < 2e-2
+    # backward
+    np.testing.assert_array_equal(host_bits(blk.dyp)[valid], nu.f64_to_bf16_bits(bw.dyp[valid]))
+    dz = host_f64(blk.dz)
+    dz = uninterleave_cols(dz, wl.I) if gated else dz
+    assert_close(dz[valid], bw.dz[valid], "dz")
+    dp = blk.dprobs_p.cpu().numpy().astype(np.float64)
+    assert_close(dp[valid], bw.dp[valid], "dprobs_p")
+    assert_close(blk.dprobs.cpu().numpy(), bw.dprobs, "dprobs")
+    dxp = host_f64(blk.dxp)
+    for e in range(wl.E):
+        rows = slice(int(pad[e]), int(pad[e]) + int(fw.rt.split_sizes[e]))
+        if rows.stop == rows.start:
+            continue
+        ref = nu.round_bf16(nu.mxfp4_round(dz[rows], 1) @ nu.mxfp4_round(w1[e], 0))
+        assert_close(dxp[rows], ref, f"dxp expert {e}")
+    assert _rel_l2(dxp[valid], bw.dxp[valid]) < 2e-2
+    assert _rel_l2(host_f64(blk.dx), bw.dx) < 2e-2
+
+
+def test_mxfp4_layer_rejects_fused_only_options():
+    with pytest.raises(ValueError):
+        mg.ExpertBlock(4, 256, 128, 64, 2, prec=mg.PREC_MXFP4, recompute=True)
