@@ -22,6 +22,12 @@ and dW2 [E][H][I].  bf16 reads dz, Xp, dYp and a as stored; MXFP8 reads the
 transposed copies of a and dz the epilogues wrote and makes those of Xp and
 dYp with moe_quantize_mxfp8 (the permutes then also keep bf16 Xp and dYp).
 
+With prec=PREC_MXFP4 the layer runs as the unfused passes below: bf16
+routing and activation passes, moe_quantize_mxfp4 before each of the four
+GEMMs and the MXFP4 grouped GEMM (weight copies made by quantize_weights,
+rowwise and, for the dgrads, transposed); no weight-gradient or recompute
+path.
+
 With recompute=True (activation recompute) the forward stores no z and the
 backward first rebuilds it with moe_grouped_gemm from the saved Xp and W1
 (recompute_z): z's write moves from the forward to the backward, at the cost
