@@ -571,7 +571,10 @@ def main():
                    "E": E, "k": k, "T": T, "H": H, "I": I, "routed_rows": M,
                    "prec": prec, "flops_per_step": flops_step},
         "kernels": kernels,
-        "roofline": {"bound": "mfma", "kernel": "FC1 grouped GEMM + activation epilogue",
+        "roofline": {"bound": "mfma",
+                     "kernel": ("FC1 grouped GEMM, plain store (unfused; with the operand "
+                                "quantization for MXFP4)" if args.unfused
+                                else "FC1 grouped GEMM + activation epilogue"),
                      "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "avg_launch_ms": round(fc1_ms, 4)},
