@@ -85,3 +85,59 @@ def test_mxfp4_layer_parity(case):
 def test_mxfp4_layer_rejects_fused_only_options():
     with pytest.raises(ValueError):
         mg.ExpertBlock(4, 256, 128, 64, 2, prec=mg.PREC_MXFP4, recompute=True)
+
+
+def _graph_replays_match_eager(blk, wl, rows_tensors):
+    """Eager step on a side stream, then the same step captured in one graph
+    and replayed three times with the outputs cleared before each replay:
+    every replay must reproduce the eager outputs bit for bit."""
+    from .gpu_util import dev_bf16
+    blk.load_weights(dev_bf16(wl.w1), dev_bf16(wl.w2))
+    x, dout = dev_bf16(wl.x), dev_bf16(wl.dout)
+    idx = torch.from_numpy(wl.expert_idx).cuda()
+    probs = torch.from_numpy(wl.probs).cuda()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        blk.forward(x, idx, probs)
+        blk.backward(dout)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    outs = [blk.out, blk.dx, blk.dprobs] + [getattr(blk, n) for n in rows_tensors]
+    # routed rows only: the GEMMs do not write pad rows
+    split = blk.split_sizes.cpu().numpy()
+    pad = blk.padded_offsets.cpu().numpy()
+    rows = np.zeros(blk.M_cap, dtype=bool)
+    for e in range(blk.E):
+        rows[pad[e]:pad[e] + split[e]] = True
+    rows = torch.from_numpy(rows).cuda()
+    eager = [t.clone() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="global"):
+        blk.forward(x, idx, probs)
+        blk.backward(dout)
+    for _ in range(3):
+        for t in outs:
+            t.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (t, e) in enumerate(zip(outs, eager)):
+            if i >= 3:
+                t, e = t[rows], e[rows]
+            assert torch.equal(t, e), f"output {i} differs on a replay"
+
+
+def test_mxfp4_layer_graph_capture_replays_match_eager():
+    wl = make_workload("tiny", seed=13, E=8, T=1024, H=256, I=256)
+    blk = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, prec=mg.PREC_MXFP4)
+    _graph_replays_match_eager(blk, wl, ("yp", "dxp"))
+
+
+@pytest.mark.parametrize("prec", [mg.PREC_BF16, mg.PREC_MXFP8])
+def test_recompute_graph_capture_replays_match_eager(prec):
+    """The recompute step (forward without z, z rebuilt in the backward) in
+    one graph."""
+    wl = make_workload("tiny", seed=14, E=8, T=1024, H=256, I=256)
+    blk = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, prec=prec, recompute=True)
+    _graph_replays_match_eager(blk, wl, ("z", "dxp"))
