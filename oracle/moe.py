@@ -47,7 +47,10 @@ rounding per stored tensor.
 
 Parity status: every function here is pinned by tests in tests/test_oracle_*.py
 (closed forms, brute force on tiny inputs, library special cases, finite
-differences, exhaustive format checks).  The grouped GEMMs at sizes beyond the
+differences, exhaustive format checks).  The blocking axis of every MX
+operand (forward, backward, weight gradients; MXFP8 and MXFP4) is pinned by
+data that MX blocks carry exactly along that axis and not along any other
+(tests/test_oracle_mx_axes.py).  The grouped GEMMs at sizes beyond the
 brute-force cases are pinned only through the E=1 dense special case and the
 exact-arithmetic invariants.
 """
