@@ -7,7 +7,9 @@ missing or fails to load, every call raises.
 """
 
 from .binding import (  # noqa: F401
-    ACT_GEGLU, ACT_SRELU, ACT_SWIGLU, GROUP_ALIGN, INTERLEAVE, MX_BLOCK,
+    ACT_GEGLU, ACT_SRELU, ACT_SWIGLU, DEVERR_DUP_EXPERT, DEVERR_MCAP_OVERFLOW,
+    ERR_DEVICE, ERR_INVALID_ARG, ERR_LAUNCH, ERR_UNSUPPORTED, ERR_WORKSPACE,
+    GROUP_ALIGN, INTERLEAVE, MX_BLOCK,
     PERMUTE_BUILD_MAP, PERMUTE_GATHER, PERMUTE_WRITE_MX, PREC_BF16,
     PREC_MXFP4, PREC_MXFP8, QUANT_COL, QUANT_ROW, MoeError, act_params, lib, lib_path,
     moe_grouped_mlp_bwd, moe_grouped_mlp_fwd, moe_grouped_mlp_wgrad, moe_router_topk,

@@ -23,6 +23,7 @@ GROUP_ALIGN = 128
 INTERLEAVE = 64
 MX_BLOCK = 32
 DEVERR_MCAP_OVERFLOW, DEVERR_DUP_EXPERT = 0x1, 0x2
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_DEVICE = 0, -1, -2, -3, -4, -5
 
 EXPORTED_SYMBOLS = (
     "moe_weight_repack_interleave", "moe_permute_workspace_size",

@@ -32,7 +32,11 @@ With recompute=True (activation recompute) the forward stores no z and the
 backward first rebuilds it with moe_grouped_gemm from the saved Xp and W1
 (recompute_z): z's write moves from the forward to the backward, at the cost
 of one more FC1-sized GEMM, and gradients are bit for bit those of the path
-that keeps z.
+that keeps z.  The block then holds no z between its forward and its
+backward: z lives in `z_scratch` (a bf16 tensor of at least M_cap * N1
+elements that many blocks may share, as their backwards run one after the
+other) or, without one, in a buffer allocated at the start of the backward
+and released at its end.
 
 No call reads device memory back or synchronises, so a whole step can be
 captured in a HIP graph.
@@ -53,7 +57,8 @@ class ExpertBlock:
                  M_cap: Optional[int] = None, cu_margin: int = 0,
                  prec: int = B.PREC_BF16, transposed_copies: bool = True,
                  bf16_copies: Optional[bool] = None, wgrad: bool = False,
-                 recompute: bool = False, device="cuda"):
+                 recompute: bool = False, z_scratch: Optional[torch.Tensor] = None,
+                 device="cuda"):
         self.E, self.H, self.I, self.T, self.k = E, H, I, T, k
         self.act = act or B.act_params()
         self.gated = self.act.act != B.ACT_SRELU
@@ -64,6 +69,8 @@ class ExpertBlock:
         # it from xp and W1 before the dActivation pass (recompute_z)
         self.recompute = recompute
         self._z_valid = False
+        # tests may keep the rebuilt z after the backward, to compare it
+        self.keep_recomputed_z = False
         self.mx = prec == B.PREC_MXFP8
         # MXFP4: the layer as separate passes (no fused epilogue writes
         # MXFP4): bf16 routing and activations, each GEMM operand quantized
@@ -93,7 +100,17 @@ class ExpertBlock:
         keep = (not self.mx) if bf16_copies is None else (bf16_copies or not self.mx)
         if self.mx4 and (wgrad or recompute):
             raise ValueError("the MXFP4 layer has no weight-gradient or recompute path")
-        self.z = torch.empty(M, N1, **bf)
+        if recompute:
+            # z exists only while the backward runs (see recompute_z)
+            if z_scratch is not None:
+                if (z_scratch.dtype != torch.bfloat16 or not z_scratch.is_contiguous()
+                        or z_scratch.numel() < M * N1):
+                    raise ValueError("z_scratch must be a contiguous bf16 tensor of at "
+                                     f"least M_cap * N1 = {M * N1} elements")
+            self._z_scratch = z_scratch
+            self.z = None
+        else:
+            self.z = torch.empty(M, N1, **bf)
         self.a = torch.empty(M, I, **bf) if keep else None
         self.yp = torch.empty(M, H, **bf)
         self.out = torch.empty(T, H, **bf)
@@ -266,12 +283,26 @@ class ExpertBlock:
         grouped GEMM without its epilogue and without split-K, so every tile
         sums K in the order FC1 used and z is bit for bit the one FC1 would
         have stored (MXFP8: from the same xp and W1 codes and scales)."""
+        if self.recompute and self.z is None:
+            if self._z_scratch is not None:
+                self.z = self._z_scratch.view(-1)[:self.M_cap * self.N1].view(self.M_cap,
+                                                                               self.N1)
+            else:
+                self.z = torch.empty(self.M_cap, self.N1, dtype=torch.bfloat16,
+                                     device=self.xp_q.device if self.mx else self.xp.device)
         if self.mx:
             self._gemm(self.N1, self.H, self.xp_q, self.w1_q, self.z, self.xp_s,
                        self.w1_s, split=False)
         else:
             self._gemm(self.N1, self.H, self.xp, self.w1i, self.z, split=False)
         self._z_valid = True
+
+    def release_z(self) -> None:
+        """With recompute, drop the rebuilt z (the backward no longer needs
+        it); experts_backward calls it at its end."""
+        if self.recompute:
+            self.z = None
+            self._z_valid = False
 
     def combine(self, yp: torch.Tensor, out: torch.Tensor,
                 dprobs: bool = False) -> None:
@@ -309,6 +340,8 @@ class ExpertBlock:
                               prec=self.prec, cu_margin=self.cu_margin,
                               err_flag=self.err_flag,
                               timing_events=timing_events, **kw)
+        if self.recompute and not self.keep_recomputed_z:
+            self.release_z()
 
     def backward(self, dout, timing_events=None):
         if self.mx:

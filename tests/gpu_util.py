@@ -259,3 +259,50 @@ def assert_mx_near(q_gpu, s_plain_gpu, ref, what, code_frac=2e-3, far_frac=1e-4,
             f"{what}: {(dist > 0).sum()} of {dist.size} codes differ"
         assert (dist > 1).mean() <= far_frac, \
             f"{what}: {(dist > 1).sum()} codes differ by more than one step"
+
+
+# The parity rule for the MXFP8 copies a fused epilogue writes: the oracle's
+# encoder applied to the GPU's own bf16 pre-cast tensor (the stored a or dz,
+# pad rows of each group as zeros) must give the same scales bit for bit,
+# and codes may differ by one E4M3 step on at most MX_CODE_FRAC of the
+# values.  Both sides encode the same bf16 numbers with the same rule, so no
+# difference is expected; the allowance is the stated bar.
+MX_CODE_FRAC = 1e-3
+
+
+def assert_mx_rule(q_gpu, s_plain_gpu, ref, what):
+    codes, scales = ref
+    q = q_gpu.detach().cpu().numpy() if isinstance(q_gpu, torch.Tensor) else q_gpu
+    q = np.asarray(q).reshape(codes.shape)
+    s_plain_gpu = np.asarray(s_plain_gpu).reshape(scales.shape)
+    bad = np.flatnonzero(s_plain_gpu.reshape(-1) != scales.reshape(-1))
+    assert bad.size == 0, (f"{what}: {bad.size} of {scales.size} scales differ; first at "
+                           f"{bad[:5]}: gpu {s_plain_gpu.reshape(-1)[bad[:5]]} oracle "
+                           f"{scales.reshape(-1)[bad[:5]]}")
+    dist = np.abs(e4m3_ordinal(q) - e4m3_ordinal(codes))
+    assert dist.max(initial=0) <= 1, f"{what}: a code differs by {dist.max()} steps"
+    assert (dist > 0).mean() <= MX_CODE_FRAC, \
+        f"{what}: {(dist > 0).sum()} of {dist.size} codes differ by one step"
+
+
+def rows_with_pad_zeroed(values: np.ndarray, valid: np.ndarray) -> np.ndarray:
+    """The pre-cast tensor the MXFP8 copies encode: the stored rows where
+    they hold data, zeros on the pad rows of each group."""
+    out = np.array(values, dtype=np.float64, copy=True)
+    out[~valid] = 0.0
+    return out
+
+
+def assert_fused_mx_copies(blk, prefix, values, valid, n, what):
+    """The rowwise ({prefix}_q/_s, blocks along n) and transposed
+    ({prefix}T_q/_s, blocks of 32 rows along M) MXFP8 copies of the GPU's
+    own [mp][n] tensor `values` (GPU column order), under assert_mx_rule."""
+    mp = values.shape[0]
+    v = rows_with_pad_zeroed(values, valid)
+    q, sc = getattr(blk, prefix + "_q"), getattr(blk, prefix + "_s")
+    assert_mx_rule(q.cpu().numpy()[:mp], mx_scales_plain(sc, blk.M_cap, n)[:mp],
+                   nu.mx_quantize(v, axis=1), f"{what} MX rowwise (self)")
+    qT, sT = getattr(blk, prefix + "T_q"), getattr(blk, prefix + "T_s")
+    if qT is not None:
+        assert_mx_rule(qT.cpu().numpy()[:, :mp], mx_scales_plain(sT, n, blk.M_cap)[:, :mp // 32],
+                       nu.mx_quantize(v.T, axis=1), f"{what} MX transposed (self)")

@@ -8,10 +8,12 @@
   epilogues write (a and dz, rowwise and transposed) must equal the oracle's
   bit for bit.
 * Layers on the configs' random data: outputs against the fp64 oracle fed the
-  same MXFP8 operands, and the fused MXFP8 copies against the oracle's
-  encoding of its own values, to the bounds explained in gpu_util (the fp8
-  MFMA's internal rounding moves a few values across E4M3 rounding
-  boundaries).
+  same MXFP8 operands; the fused MXFP8 copies of a and dz (rowwise and
+  transposed) against the oracle's encoder applied to the GPU's own bf16 a
+  and dz (scales bit-exact, codes within one E4M3 step on at most 0.1%),
+  and secondarily against the oracle's encoding of its own values, to the
+  bounds explained in gpu_util (the fp8 MFMA's internal rounding moves a
+  few values across E4M3 rounding boundaries).
 Every call goes through the C ABI.
 """
 
@@ -24,8 +26,8 @@ from oracle import moe as om
 from oracle import numerics as nu
 from workloads import make_workload
 
-from .gpu_util import (act_of, assert_close, assert_close_mx, assert_mx_equal,
-                       assert_mx_near, compare_routing, dev_bf16, gemm_grid,
+from .gpu_util import (act_of, assert_close, assert_close_mx, assert_fused_mx_copies,
+                       assert_mx_equal, assert_mx_near, compare_routing, dev_bf16, gemm_grid,
                        host_bits, host_f64, mx_scales_plain, oracle_layer,
                        run_gpu_layer, tail_split_parts, uninterleave_cols)
 
@@ -134,7 +136,11 @@ def compare_layer_mx(blk, wl, fw, bw, exact=False):
     amax = float(blk.amax.cpu()[0])
     assert amax == np.abs(a_gpu).max()
     assert abs(amax - fw.amax) <= 2.0 ** -7 * fw.amax + 1e-30
-    # MXFP8 copies of a (pad rows of each group encode zeros, as in the oracle)
+    # MXFP8 copies of a: the parity rule, the oracle's encoder applied to the
+    # GPU's own bf16 a (pad rows of each group as zeros)
+    assert blk.a is not None and blk.dz is not None, "run with bf16_copies=True"
+    assert_fused_mx_copies(blk, "a", host_f64(blk.a)[:mp], vmp, wl.I, "a")
+    # and, secondarily, against the oracle's encoding of its own a
     mx_cmp(blk.a_q.cpu().numpy()[:mp], mx_scales_plain(blk.a_s, M_cap, wl.I)[:mp],
            nu.mx_quantize(fw.a[:mp], axis=1), "a MX rowwise")
     mx_cmp(blk.aT_q.cpu().numpy()[:, :mp],
@@ -150,7 +156,9 @@ def compare_layer_mx(blk, wl, fw, bw, exact=False):
     if gated:
         dz = uninterleave_cols(dz, wl.I)
     same(dz, bw.dz[valid], "dz")
-    # the oracle's dz in the interleaved column order of the GPU's copies
+    # the parity rule on the GPU's own dz (GPU column order), then the
+    # oracle's dz in the interleaved column order of the GPU's copies
+    assert_fused_mx_copies(blk, "dz", host_f64(blk.dz)[:mp], vmp, N1, "dz")
     dz_or = bw.dz[:mp][:, om.interleave_rows(wl.I)] if gated else bw.dz[:mp]
     mx_cmp(blk.dz_q.cpu().numpy()[:mp], mx_scales_plain(blk.dz_s, M_cap, N1)[:mp],
            nu.mx_quantize(dz_or, axis=1), "dz MX rowwise")

@@ -40,8 +40,6 @@ def _with_ties(rng, bits, rows):
 @pytest.mark.parametrize("batch,rows,cols,pad", [(1, 32, 64, 0), (3, 128, 192, 0),
                                                  (2, 192, 2880, 40)])
 def test_quantize_mxfp4_bit_exact(mode, batch, rows, cols, pad):
-    if mode == mg.QUANT_COL and rows % 64:
-        pytest.skip("the column mode takes rows in multiples of 64")
     rng = np.random.default_rng(rows + cols + 4)
     bits = _with_ties(rng, _hard_bf16(rng, (batch, rows, cols)), rows)
     stride = rows * cols + pad
@@ -51,6 +49,16 @@ def test_quantize_mxfp4_bit_exact(mode, batch, rows, cols, pad):
     x = dev_bf16(flat)
     q = torch.full((batch * rows * cols // 2,), 0xAB, dtype=torch.uint8, device="cuda")
     s = torch.full((batch * rows * cols // 32,), 0xAB, dtype=torch.uint8, device="cuda")
+    if mode == mg.QUANT_COL and rows % 64:
+        # the column mode takes rows in multiples of 64: rejected before any
+        # launch, nothing written
+        with pytest.raises(mg.MoeError) as ei:
+            mg.moe_quantize_mxfp4(batch=batch, rows=rows, cols=cols, x=x, q=q, s=s, mode=mode,
+                                  x_stride=stride if pad else 0)
+        assert ei.value.status == mg.ERR_INVALID_ARG
+        torch.cuda.synchronize()
+        assert bool((q == 0xAB).all()) and bool((s == 0xAB).all())
+        return
     mg.moe_quantize_mxfp4(batch=batch, rows=rows, cols=cols, x=x, q=q, s=s, mode=mode,
                           x_stride=stride if pad else 0)
     torch.cuda.synchronize()

@@ -5,13 +5,16 @@ GEMM reads the MXFP4 encoding of a tensor the GPU computed (a for FC2, dz
 for FC1 dgrad), a one-ulp difference in that bf16 tensor can move an E2M1
 code by a whole step; those outputs are checked element by element against
 the oracle fed the GPU's own tensor, and against the independent oracle by
-relative L2 error."""
+relative L2 error.  The combines (out, dX) and the dprobs gather are checked
+bit for bit against the oracle's unpermute / gather of the GPU's own yp, dxp
+and dprobs_p."""
 
 import numpy as np
 import pytest
 import torch
 
 import moe_grouped_mlp_amd as mg
+from oracle import moe as om
 from oracle import numerics as nu
 from workloads import make_workload
 
@@ -63,6 +66,10 @@ def test_mxfp4_layer_parity(case):
         assert_close(yp[rows], ref, f"yp expert {e}")
     assert _rel_l2(yp[valid], fw.y[valid]) < 2e-2
     assert _rel_l2(host_f64(blk.out), fw.out) < 2e-2
+    # the combine, element by element: bit-exact against the oracle's
+    # unpermute of the GPU's own yp
+    np.testing.assert_array_equal(host_bits(blk.out),
+                                  nu.f64_to_bf16_bits(om.unpermute(yp, fw.rt.row_id_map)))
     # backward
     np.testing.assert_array_equal(host_bits(blk.dyp)[valid], nu.f64_to_bf16_bits(bw.dyp[valid]))
     dz = host_f64(blk.dz)
@@ -80,6 +87,13 @@ def test_mxfp4_layer_parity(case):
         assert_close(dxp[rows], ref, f"dxp expert {e}")
     assert _rel_l2(dxp[valid], bw.dxp[valid]) < 2e-2
     assert _rel_l2(host_f64(blk.dx), bw.dx) < 2e-2
+    # dX and dprobs, element by element: bit-exact against the oracle's
+    # unpermute of the GPU's dxp and gather of the GPU's dprobs_p
+    np.testing.assert_array_equal(host_bits(blk.dx),
+                                  nu.f64_to_bf16_bits(om.unpermute(dxp, fw.rt.row_id_map)))
+    np.testing.assert_array_equal(
+        blk.dprobs.cpu().numpy(),
+        om.gather_probs_grad(blk.dprobs_p.cpu().numpy(), fw.rt.row_id_map).astype(np.float32))
 
 
 def test_mxfp4_layer_rejects_fused_only_options():
@@ -139,5 +153,8 @@ def test_recompute_graph_capture_replays_match_eager(prec):
     """The recompute step (forward without z, z rebuilt in the backward) in
     one graph."""
     wl = make_workload("tiny", seed=14, E=8, T=1024, H=256, I=256)
-    blk = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, prec=prec, recompute=True)
+    blk = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, prec=prec, recompute=True,
+                         z_scratch=torch.empty((wl.m_cap() + 128) * 2 * wl.I,
+                                               dtype=torch.bfloat16, device="cuda"))
+    blk.keep_recomputed_z = True
     _graph_replays_match_eager(blk, wl, ("z", "dxp"))

@@ -58,14 +58,21 @@ def _block(wl, M_cap, prec, margin, recompute):
 
 def _run_recompute(wl, M_cap, prec, margin=0):
     blk = _block(wl, M_cap, prec, margin, True)
+    # z lives in a caller's scratch buffer during the backward; the test
+    # keeps it afterwards to compare it
+    n1 = 2 * wl.I if wl.act != "srelu" else wl.I
+    scratch = torch.empty(M_cap * n1, dtype=torch.bfloat16, device="cuda")
+    scratch.view(torch.int16).fill_(SENTINEL)
+    blk._z_scratch = scratch
+    blk.keep_recomputed_z = True
     blk.load_weights(dev_bf16(wl.w1), dev_bf16(wl.w2))
-    blk.z.view(torch.int16).fill_(SENTINEL)
     idx = torch.from_numpy(wl.expert_idx.astype(np.int32)).cuda()
     probs = torch.from_numpy(wl.probs.astype(np.float32)).cuda()
     blk.forward(dev_bf16(wl.x), idx, probs)
     torch.cuda.synchronize()
     # the forward kept no z
-    assert bool((blk.z.view(torch.int16) == SENTINEL).all())
+    assert blk.z is None
+    assert bool((scratch.view(torch.int16) == SENTINEL).all())
     blk.backward(dev_bf16(wl.dout))
     torch.cuda.synchronize()
     return blk
@@ -134,3 +141,35 @@ def test_recompute_z_repeatable():
     torch.cuda.synchronize()
     assert torch.equal(rc.z[rows].view(torch.int16), z1.view(torch.int16))
     assert torch.equal(rc.dx.view(torch.int16), dx1.view(torch.int16))
+
+
+def test_recompute_holds_no_z_between_forward_and_backward():
+    """The recompute block allocates no z: between its forward and its
+    backward it holds M_cap * N1 bf16 elements less than the block that
+    keeps z, and the z it rebuilds in the backward is released at the end."""
+    wl = make_workload("tiny", seed=8, E=4, k=2, T=512, H=256, I=256)
+    M_cap = wl.m_cap()
+    gp, _ = act_of(wl)
+    z_bytes = M_cap * 2 * wl.I * 2
+    torch.cuda.synchronize()
+    m0 = torch.cuda.memory_allocated()
+    rc = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, act=gp, M_cap=M_cap, recompute=True)
+    m1 = torch.cuda.memory_allocated()
+    keep = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, act=gp, M_cap=M_cap)
+    m2 = torch.cuda.memory_allocated()
+    assert (m2 - m1) - (m1 - m0) >= z_bytes
+    for blk in (rc, keep):
+        blk.load_weights(dev_bf16(wl.w1), dev_bf16(wl.w2))
+    idx = torch.from_numpy(wl.expert_idx.astype(np.int32)).cuda()
+    probs = torch.from_numpy(wl.probs.astype(np.float32)).cuda()
+    x, dout = dev_bf16(wl.x), dev_bf16(wl.dout)
+    rc.forward(x, idx, probs)
+    keep.forward(x, idx, probs)
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    rc.backward(dout)
+    keep.backward(dout)
+    torch.cuda.synchronize()
+    assert rc.z is None
+    assert torch.cuda.memory_allocated() == before
+    assert torch.equal(rc.dx.view(torch.int16), keep.dx.view(torch.int16))
