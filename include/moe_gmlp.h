@@ -405,6 +405,28 @@ typedef struct moe_bwd_args {
 moe_status moe_grouped_mlp_bwd(const moe_bwd_args* args, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_grouped_mlp_bwd_noalloc -- moe_grouped_mlp_bwd for callers that cannot
+ *   allocate device memory (code under stream capture, tight training loops,
+ *   harnesses that forbid hipMalloc): the same computation and arguments,
+ *   but the workspace fields of *args are ignored.  The workspace comes
+ *   instead from a fixed array of MOE_NOALLOC_SCRATCH_BYTES that the library
+ *   holds on every device it runs on, until the process ends.
+ *   Limit: M_cap * ceil(I / 256) * 4 <= MOE_NOALLOC_SCRATCH_BYTES (the fp32
+ *   dprobs partial sums), else MOE_ERR_UNSUPPORTED before any launch; the
+ *   FC1 dgrad splits its last round of tiles along K only when that area
+ *   also fits in the array.  Nothing in the array needs clearing between
+ *   calls (every partial read is written first in the same call).
+ *   All calls on one device share that device's array: calls that overlap
+ *   in time on one device (two streams, two threads) race and give wrong
+ *   results; order them on one stream.  The array's address is looked up on
+ *   the first call on each device (with that device current); make that
+ *   first call outside stream capture.  No hipMalloc, hipFree or host sync.
+ * ---------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+moe_status moe_grouped_mlp_bwd_noalloc(const moe_bwd_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_grouped_mlp_wgrad -- the weight-gradient grouped GEMMs of the backward
  *   ([FK] § "Overcoming training bottlenecks", Fig. 1: the weight gradients
  *   stay in separate blocks outside the fused kernels; § "Fused MXFP8 and

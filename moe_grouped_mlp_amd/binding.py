@@ -23,6 +23,7 @@ GROUP_ALIGN = 128
 INTERLEAVE = 64
 MX_BLOCK = 32
 DEVERR_MCAP_OVERFLOW, DEVERR_DUP_EXPERT = 0x1, 0x2
+NOALLOC_SCRATCH_BYTES = 16 << 20
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_DEVICE = 0, -1, -2, -3, -4, -5
 
 EXPORTED_SYMBOLS = (
@@ -31,7 +32,7 @@ EXPORTED_SYMBOLS = (
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_mlp_wgrad",
     "moe_router_topk", "moe_grouped_gemm", "moe_glu_unfused",
     "moe_grouped_mlp_workspace_size", "moe_status_string", "moe_gmlp_version",
-    "moe_mx_scale_offset",
+    "moe_mx_scale_offset", "moe_grouped_mlp_bwd_noalloc",
 )
 
 
@@ -184,6 +185,7 @@ def lib() -> ctypes.CDLL:
                          ("moe_quantize_mxfp4", QuantArgs),
                          ("moe_grouped_mlp_fwd", FwdArgs),
                          ("moe_grouped_mlp_bwd", BwdArgs),
+                         ("moe_grouped_mlp_bwd_noalloc", BwdArgs),
                          ("moe_grouped_mlp_wgrad", WgradArgs),
                          ("moe_router_topk", RouterArgs),
                          ("moe_grouped_gemm", GemmArgs),
@@ -326,6 +328,29 @@ def moe_grouped_mlp_bwd(*, E, H, I, M_cap, split_sizes, padded_offsets,
                    _ptr(dz_q), _ptr(dz_s), _ptr(dzT_q), _ptr(dzT_s))
     _check("moe_grouped_mlp_bwd",
            lib().moe_grouped_mlp_bwd(ctypes.byref(args), _stream(stream)))
+
+
+def moe_grouped_mlp_bwd_noalloc(*, E, H, I, M_cap, split_sizes, padded_offsets,
+                                probs_p, z, dprobs_p, dxp, dyp=None, w2=None, w1i=None,
+                                dz=None, act=None, prec=PREC_BF16, cu_margin=0,
+                                w1_stride=0, w2_stride=0, err_flag=None,
+                                timing_events=None, dyp_q=None, dyp_s=None,
+                                w2t_q=None, w2t_s=None, w1t_q=None, w1t_s=None,
+                                dz_q=None, dz_s=None, dzT_q=None, dzT_s=None,
+                                stream=None):
+    """moe_grouped_mlp_bwd without a workspace argument: the library's fixed
+    per-device scratch array serves as the workspace (for callers that
+    cannot allocate)."""
+    args = BwdArgs(E, H, I, M_cap, prec, act or act_params(), cu_margin,
+                   _ptr(split_sizes), _ptr(padded_offsets), _ptr(probs_p),
+                   _ptr(dyp), _ptr(w2), _ptr(z), _ptr(w1i), w1_stride,
+                   w2_stride, _ptr(dz), _ptr(dprobs_p), _ptr(dxp),
+                   _ptr(err_flag), None, 0,
+                   _events(timing_events), _ptr(dyp_q), _ptr(dyp_s),
+                   _ptr(w2t_q), _ptr(w2t_s), _ptr(w1t_q), _ptr(w1t_s),
+                   _ptr(dz_q), _ptr(dz_s), _ptr(dzT_q), _ptr(dzT_s))
+    _check("moe_grouped_mlp_bwd_noalloc",
+           lib().moe_grouped_mlp_bwd_noalloc(ctypes.byref(args), _stream(stream)))
 
 
 def moe_grouped_mlp_wgrad(*, E, H, I, M_cap, split_sizes, padded_offsets,

@@ -369,14 +369,17 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   return MOE_OK;
 }
 
-moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
+// The backward with its workspace given separately: the caller's
+// (moe_grouped_mlp_bwd) or the library's fixed scratch array
+// (moe_grouped_mlp_bwd_noalloc).
+// Host-side checks of the backward's arguments (no HIP call).
+static moe_status bwd_check(const moe_bwd_args* a) {
   if (!a) return MOE_ERR_INVALID_ARG;
   if (moe_status st = check_common(a->E, a->H, a->I, a->M_cap, a->prec, a->act, a->cu_margin,
                                    a->split_sizes, a->padded_offsets, a->probs_p))
     return st;
   const bool mx = a->prec == MOE_PREC_MXFP8;
-  const bool gated = a->act.act != MOE_ACT_SRELU;
-  const int N1 = gated ? 2 * a->I : a->I;
+  const int N1 = a->act.act != MOE_ACT_SRELU ? 2 * a->I : a->I;
   if (!a->z || !a->dprobs_p || !a->dxp) return MOE_ERR_INVALID_ARG;
   if (mx) {
     if (!a->dyp_q || !a->dyp_s || !a->w2t_q || !a->w2t_s || !a->w1t_q || !a->w1t_s ||
@@ -389,9 +392,17 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
     if (a->w2_stride != 0 && a->w2_stride < static_cast<int64_t>(a->H) * a->I)
       return MOE_ERR_INVALID_ARG;
   }
+  return MOE_OK;
+}
+
+static moe_status bwd_impl(const moe_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+  if (moe_status st = bwd_check(a)) return st;
+  const bool mx = a->prec == MOE_PREC_MXFP8;
+  const bool gated = a->act.act != MOE_ACT_SRELU;
+  const int N1 = gated ? 2 * a->I : a->I;
   // the dprobs partials are required; the split-K area is used when present
   const size_t need = static_cast<size_t>(a->M_cap * dgrad_parts(a->I) * sizeof(float));
-  if (!a->workspace || a->workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
   int cu = 0;
   if (moe_status st = device_info(&cu)) return st;
   if (a->cu_margin >= cu) return MOE_ERR_INVALID_ARG;
@@ -433,7 +444,7 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
   g.ldc = N1;
   g.zin = static_cast<const uint16_t*>(a->z);
   g.ldz = N1;
-  g.dp_part = static_cast<float*>(a->workspace);
+  g.dp_part = static_cast<float*>(ws);
   g.n_part = n_part;
   record(a->timing_events[0], s);
   if (moe_status st = launched(moe::launch_grouped_gemm(
@@ -474,12 +485,17 @@ moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
   const int grid2 = gemm_grid(cu, a->cu_margin, a->M_cap, a->E, f.N);
   const size_t dp_bytes =
       align256(static_cast<size_t>(a->M_cap * dgrad_parts(a->I) * sizeof(float)));
-  if (moe_status st = attach_split(f, a->workspace, a->workspace_bytes, dp_bytes, grid2, s))
+  if (moe_status st = attach_split(f, ws, ws_bytes, dp_bytes, grid2, s))
     return st;
   if (moe_status st = launched(moe::launch_grouped_gemm(f, moe::EPI_STORE, !mx, mx, grid2, s)))
     return st;
   record(a->timing_events[2], s);
   return MOE_OK;
+}
+
+moe_status moe_grouped_mlp_bwd(const moe_bwd_args* a, void* stream) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  return bwd_impl(a, a->workspace, a->workspace_bytes, stream);
 }
 
 moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
@@ -631,3 +647,13 @@ moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* a, void* stream) {
 }
 
 }  // extern "C"
+
+namespace moe {
+moe_status grouped_mlp_bwd_impl(const moe_bwd_args* a, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  return bwd_impl(a, ws, ws_bytes, stream);
+}
+moe_status grouped_mlp_bwd_check(const moe_bwd_args* a) { return bwd_check(a); }
+int64_t grouped_mlp_dprobs_parts(int I) { return dgrad_parts(I); }
+}  // namespace moe

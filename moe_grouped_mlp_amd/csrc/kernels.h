@@ -104,4 +104,11 @@ hipError_t launch_dprobs_reduce(const float* part, int n_part, const int32_t* sp
                                 const int32_t* padded, int E, int64_t M_cap,
                                 float* dprobs_p, hipStream_t s);
 
+// ---- entry-point bodies shared between C-ABI variants (api.cpp) ---------
+// moe_grouped_mlp_bwd with the workspace given apart from the arguments
+moe_status grouped_mlp_bwd_impl(const moe_bwd_args* a, void* ws, size_t ws_bytes,
+                                void* stream);
+moe_status grouped_mlp_bwd_check(const moe_bwd_args* a);  // host-side checks only
+int64_t grouped_mlp_dprobs_parts(int I);  // fp32 dprobs partials per row
+
 }  // namespace moe

@@ -268,6 +268,30 @@ def test_bwd_validation():
     assert _call("moe_grouped_mlp_bwd", a) == INVALID
 
 
+def test_bwd_noalloc_validation():
+    """The backward without a workspace argument: the same host checks
+    first, then the fixed scratch size (MOE_ERR_UNSUPPORTED past it), then
+    the device; the workspace fields are ignored."""
+    a = B.BwdArgs()
+    a.E, a.H, a.I, a.M_cap, a.prec = 4, 128, 256, 1024, B.PREC_BF16
+    a.act = B.act_params()
+    for f in ("split_sizes", "padded_offsets", "probs_p", "dyp", "w2", "z",
+              "w1i", "dz", "dprobs_p", "dxp"):
+        setattr(a, f, 64)
+    a.workspace, a.workspace_bytes = None, 0
+    assert _call("moe_grouped_mlp_bwd_noalloc", a) == DEVICE
+    a.z = None
+    assert _call("moe_grouped_mlp_bwd_noalloc", a) == INVALID
+    a.z = 64
+    # fp32 partials of M_cap rows x ceil(I / 256) tiles past 16 MiB
+    a.I = 1024
+    a.M_cap = B.NOALLOC_SCRATCH_BYTES // (4 * 4)
+    assert _call("moe_grouped_mlp_bwd_noalloc", a) == DEVICE
+    a.M_cap += 128
+    assert _call("moe_grouped_mlp_bwd_noalloc", a) == UNSUPPORTED
+    assert m.lib().moe_grouped_mlp_bwd_noalloc(None, None) == INVALID
+
+
 def test_unpermute_validation():
     a = B.UnpermuteArgs(8, 2, 64, 100, 64, 64, 64, None, None)
     assert _call("moe_unpermute", a) == DEVICE
