@@ -603,6 +603,90 @@ def router_timing(T, E, k, dev):
             "outside_step": True}
 
 
+# the router shapes: (T tokens, router experts, top-k, local experts)
+ROUTING_SHAPES = {
+    "mixtral": (8192, 8, 2, 8),
+    "gptoss": (16384, 128, 4, 128),
+    "dsv3_share": (16384, 256, 8, 32),   # 32 local experts of 256, top-8
+}
+
+
+def routing_timing(dev, reps=20):
+    """Router + routing metadata from logits: one launch (moe_router_route)
+    against moe_router_topk followed by moe_permute(BUILD_MAP) (four
+    launches), both replayed from a captured graph (so the host's launch
+    rate is not what is timed), at the Mixtral, GPT-OSS and DSv3-share
+    router shapes.  Microseconds per call."""
+    import torch
+    import moe_grouped_mlp_amd as mg
+    out = {}
+    for name, (T, E_all, k, E) in ROUTING_SHAPES.items():
+        g = torch.Generator(device=dev)
+        g.manual_seed(1)
+        lg = torch.randn(T, E_all, generator=g, device=dev, dtype=torch.float32)
+        M_cap = T * k + E * 127
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        bufs = dict(expert_idx=torch.empty(T, k, **i32), probs=torch.empty(T, k, **f32),
+                    split_sizes=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+                    padded_offsets=torch.empty(E + 1, **i32),
+                    row_id_map=torch.empty(T, k, **i32), row_src=torch.empty(M_cap, **i32),
+                    probs_p=torch.empty(M_cap, **f32), err_flag=torch.zeros(1, **i32))
+        ws_f = torch.zeros(mg.moe_router_route_workspace_size(T, E_all, E), dtype=torch.uint8,
+                           device=dev)
+        ws_p = torch.empty(mg.moe_permute_workspace_size(T, E), dtype=torch.uint8, device=dev)
+
+        def fused(st):
+            mg.moe_router_route(T=T, E_total=E_all, k=k, E=E, M_cap=M_cap, logits=lg,
+                                workspace=ws_f, stream=st, **bufs)
+
+        def separate(st):
+            mg.moe_router_topk(T=T, E=E_all, k=k, logits=lg, expert_idx=bufs["expert_idx"],
+                               probs=bufs["probs"], stream=st)
+            mg.moe_permute(flags=mg.PERMUTE_BUILD_MAP, T=T, k=k, E=E, H=64, M_cap=M_cap,
+                           expert_idx=bufs["expert_idx"], probs=bufs["probs"],
+                           split_sizes=bufs["split_sizes"], offsets=bufs["offsets"],
+                           padded_offsets=bufs["padded_offsets"],
+                           row_id_map=bufs["row_id_map"], row_src=bufs["row_src"],
+                           probs_p=bufs["probs_p"], err_flag=bufs["err_flag"],
+                           workspace=ws_p, stream=st)
+
+        def router_only(st):
+            mg.moe_router_topk(T=T, E=E_all, k=k, logits=lg, expert_idx=bufs["expert_idx"],
+                               probs=bufs["probs"], stream=st)
+
+        res = {}
+        for label, fn in (("fused_us", fused), ("router_plus_metadata_4_launches_us", separate),
+                          ("router_only_us", router_only)):
+            gs = torch.cuda.Stream()
+            gs.wait_stream(torch.cuda.current_stream())
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(gs):
+                fn(gs.cuda_stream)
+                with torch.cuda.graph(graph, stream=gs):
+                    for _ in range(reps):
+                        fn(gs.cuda_stream)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            stream = torch.cuda.current_stream().cuda_stream
+            ev = HipEvents(2)
+            ev.record(0, stream)
+            graph.replay()
+            ev.record(1, stream)
+            torch.cuda.synchronize()
+            res[label] = round(ev.elapsed_ms(0, 1) / reps * 1e3, 2)
+            ev.close()
+            del graph
+        assert int(bufs["err_flag"].cpu()[0]) == 0
+        res["shape"] = f"T={T} E_total={E_all} k={k} local E={E}"
+        out[name] = res
+        log(f"routing {name}: fused {res['fused_us']} us, four launches "
+            f"{res['router_plus_metadata_4_launches_us']} us, router alone "
+            f"{res['router_only_us']} us")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -655,6 +739,7 @@ def main():
     cfg = r["cfg"]
     kernels = r["kernels"]
     kernels["router_topk"] = router_timing(T, E, k, dev)
+    routing = routing_timing(dev)
     ceiling = copy_ceiling_gbs(dev)
     for name in ("route_permute_x", "unpermute_out", "permute_dout", "unpermute_dx"):
         kernels[name]["frac_of_copy"] = round(kernels[name]["rate"] / ceiling, 3)
@@ -725,6 +810,7 @@ def main():
         "value_at_median": round(r["flops_step"] / (r["timing"]["median_ms"] * 1e-3) / 1e12, 3),
         "kernels": kernels,
         "copy_ceiling_gbs": round(ceiling, 1),
+        "routing_from_logits": routing,
         "roofline": {"bound": "mfma",
                      "kernel": ("FC1 grouped GEMM, plain store (unfused; with the operand "
                                 "quantization for MXFP4)" if args.unfused

@@ -55,6 +55,9 @@ typedef enum moe_status {
 /* Bits OR-ed into *err_flag by kernels (never read back by the library). */
 #define MOE_DEVERR_MCAP_OVERFLOW 0x1  /* padded row count > M_cap          */
 #define MOE_DEVERR_DUP_EXPERT 0x2     /* a token lists one expert twice    */
+#define MOE_DEVERR_SYNC_TIMEOUT 0x4   /* a grid-wide wait of moe_router_route
+                                         ran out (the grid was not resident
+                                         at once); no rows were written     */
 
 /* Group-start alignment of the padded row layout (rows).  Every group of
  * the permuted layout starts at a multiple of it, so MXFP8 blocks of 32
@@ -576,6 +579,58 @@ typedef struct moe_router_args {
 } moe_router_args;
 
 moe_status moe_router_topk(const moe_router_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_router_route -- the router and the routing metadata in one launch
+ *   ([FK] § "Eliminating host-device synchronization and CPU launch
+ *   overhead": per-group counts stay on the device, no host round trip;
+ *   the AI-digest summary of the same work lists gating, top-k and routing
+ *   fused into one launch).
+ *
+ *   Computes exactly what moe_router_topk followed by moe_permute with
+ *   MOE_PERMUTE_BUILD_MAP computes, with the same router arithmetic (the
+ *   same bits):
+ *     expert_idx[T][k], probs[T][k]     as moe_router_topk, from
+ *                                       logits [T][E_total]
+ *     split_sizes, offsets (nullable), padded_offsets, row_id_map,
+ *     row_src, probs_p                  as moe_permute BUILD_MAP, for the
+ *                                       local experts first_expert ..
+ *                                       first_expert + E - 1
+ *   One workgroup per 256 tokens (64 when E_total > 32), all resident at
+ *   once, with two grid-wide barriers inside the launch (bounded waits; see
+ *   MOE_DEVERR_SYNC_TIMEOUT).
+ *   workspace: moe_router_route_workspace_size(T, E_total, E) bytes whose
+ *   first 4096 bytes (barrier counters) must be zero before the first call;
+ *   every call leaves them as the next call expects, so one buffer serves any
+ *   number of calls, of any sizes, and graph replays.  Calls that share a
+ *   workspace must not overlap in time.
+ *   Needs 1 <= T and at most min(512, 2 x the device's CU count) workgroups
+ *   (T <= 131072 for E_total <= 32, T <= 32768 beyond, on MI355X), else
+ *   MOE_ERR_UNSUPPORTED (moe_router_topk + moe_permute serve any size);
+ *   1 <= E_total <= 1024,
+ *   1 <= k <= min(E_total, 8), 1 <= E <= 1024, 0 <= first_expert, M_cap >= 1.
+ *   Device problems as in moe_permute (MOE_DEVERR_MCAP_OVERFLOW).
+ * ---------------------------------------------------------------------- */
+typedef struct moe_router_route_args {
+  int32_t T, E_total, k;          /* router: T tokens, top-k of E_total */
+  int32_t E, first_expert;        /* local experts */
+  int64_t M_cap;
+  const float* logits;            /* [T][E_total] device, finite */
+  int32_t* expert_idx;            /* [T][k]  device, out */
+  float* probs;                   /* [T][k]  device, out */
+  int32_t* split_sizes;           /* [E]     device, out */
+  int32_t* offsets;               /* [E+1]   device, out (may be NULL) */
+  int32_t* padded_offsets;        /* [E+1]   device, out */
+  int32_t* row_id_map;            /* [T][k]  device, out */
+  int32_t* row_src;               /* [M_cap] device, out */
+  float* probs_p;                 /* [M_cap] device, out */
+  int32_t* err_flag;              /* optional device int32 */
+  void* workspace;                /* device, see above */
+  size_t workspace_bytes;
+} moe_router_route_args;
+
+size_t moe_router_route_workspace_size(int T, int E_total, int E);
+moe_status moe_router_route(const moe_router_route_args* args, void* stream);
 
 /* Workspace bytes for these sizes: the backward needs at least the dprobs
  * partials (fp32 M_cap x ceil(I / 256)); the full size adds the area where

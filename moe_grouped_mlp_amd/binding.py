@@ -22,7 +22,7 @@ QUANT_ROW, QUANT_COL = 0, 1
 GROUP_ALIGN = 128
 INTERLEAVE = 64
 MX_BLOCK = 32
-DEVERR_MCAP_OVERFLOW, DEVERR_DUP_EXPERT = 0x1, 0x2
+DEVERR_MCAP_OVERFLOW, DEVERR_DUP_EXPERT, DEVERR_SYNC_TIMEOUT = 0x1, 0x2, 0x4
 NOALLOC_SCRATCH_BYTES = 16 << 20
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_DEVICE = 0, -1, -2, -3, -4, -5
 
@@ -32,7 +32,8 @@ EXPORTED_SYMBOLS = (
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_mlp_wgrad",
     "moe_router_topk", "moe_grouped_gemm", "moe_glu_unfused",
     "moe_grouped_mlp_workspace_size", "moe_status_string", "moe_gmlp_version",
-    "moe_mx_scale_offset", "moe_grouped_mlp_bwd_noalloc",
+    "moe_mx_scale_offset", "moe_grouped_mlp_bwd_noalloc", "moe_router_route",
+    "moe_router_route_workspace_size",
 )
 
 
@@ -137,6 +138,16 @@ class RouterArgs(ctypes.Structure):
                 ("probs", c_void_p)]
 
 
+class RouterRouteArgs(ctypes.Structure):
+    _fields_ = [("T", c_int32), ("E_total", c_int32), ("k", c_int32),
+                ("E", c_int32), ("first_expert", c_int32), ("M_cap", c_int64),
+                ("logits", c_void_p), ("expert_idx", c_void_p), ("probs", c_void_p),
+                ("split_sizes", c_void_p), ("offsets", c_void_p),
+                ("padded_offsets", c_void_p), ("row_id_map", c_void_p),
+                ("row_src", c_void_p), ("probs_p", c_void_p), ("err_flag", c_void_p),
+                ("workspace", c_void_p), ("workspace_bytes", c_size_t)]
+
+
 class WgradArgs(ctypes.Structure):
     _fields_ = [("E", c_int32), ("H", c_int32), ("I", c_int32),
                 ("gated", c_int32), ("M_cap", c_int64), ("prec", c_int32),
@@ -174,6 +185,8 @@ def lib() -> ctypes.CDLL:
             c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_void_p]
         L.moe_permute_workspace_size.restype = c_size_t
         L.moe_permute_workspace_size.argtypes = [c_int, c_int]
+        L.moe_router_route_workspace_size.restype = c_size_t
+        L.moe_router_route_workspace_size.argtypes = [c_int, c_int, c_int]
         L.moe_mx_scale_offset.restype = c_int64
         L.moe_mx_scale_offset.argtypes = [c_int64, c_int64, c_int64]
         L.moe_grouped_mlp_workspace_size.restype = c_size_t
@@ -188,6 +201,7 @@ def lib() -> ctypes.CDLL:
                          ("moe_grouped_mlp_bwd_noalloc", BwdArgs),
                          ("moe_grouped_mlp_wgrad", WgradArgs),
                          ("moe_router_topk", RouterArgs),
+                         ("moe_router_route", RouterRouteArgs),
                          ("moe_grouped_gemm", GemmArgs),
                          ("moe_glu_unfused", GluArgs)):
             f = getattr(L, name)
@@ -372,6 +386,22 @@ def moe_grouped_mlp_wgrad(*, E, H, I, M_cap, split_sizes, padded_offsets,
 def moe_router_topk(*, T, E, k, logits, expert_idx, probs, stream=None):
     args = RouterArgs(T, E, k, _ptr(logits), _ptr(expert_idx), _ptr(probs))
     _check("moe_router_topk", lib().moe_router_topk(ctypes.byref(args), _stream(stream)))
+
+
+def moe_router_route_workspace_size(T, E_total, E) -> int:
+    return lib().moe_router_route_workspace_size(T, E_total, E)
+
+
+def moe_router_route(*, T, E_total, k, E, M_cap, logits, expert_idx, probs, split_sizes,
+                     padded_offsets, row_id_map, row_src, probs_p, workspace, offsets=None,
+                     first_expert=0, err_flag=None, stream=None):
+    """Router and routing metadata in one launch; the workspace's first 256
+    bytes must be zero before the first call (each call leaves them zero)."""
+    args = RouterRouteArgs(T, E_total, k, E, first_expert, M_cap, _ptr(logits),
+                           _ptr(expert_idx), _ptr(probs), _ptr(split_sizes), _ptr(offsets),
+                           _ptr(padded_offsets), _ptr(row_id_map), _ptr(row_src),
+                           _ptr(probs_p), _ptr(err_flag), _ptr(workspace), _nbytes(workspace))
+    _check("moe_router_route", lib().moe_router_route(ctypes.byref(args), _stream(stream)))
 
 
 def moe_grouped_gemm(*, E, N, K, M_cap, split_sizes, padded_offsets, a, b, c,

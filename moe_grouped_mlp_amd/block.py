@@ -233,18 +233,38 @@ class ExpertBlock:
                       err_flag=self.err_flag, workspace=self.ws_route)
 
     def route_logits(self, logits: torch.Tensor,
-                     x: Optional[torch.Tensor] = None) -> None:
+                     x: Optional[torch.Tensor] = None, fused: bool = True) -> None:
         """Top-k router on the device (softmax over the experts of fp32
         logits [T][E_total], k largest, ties to the lower id) into
-        self.expert_idx / self.probs, then route() on them."""
+        self.expert_idx / self.probs, and the routing metadata of the local
+        experts.  fused: router and metadata in one launch
+        (moe_router_route), then the gather of x if given; else
+        moe_router_topk followed by route() (four launches before the
+        gather).  Both give the same bits."""
         T, E_all = logits.shape
         if not hasattr(self, "expert_idx"):
             dev = logits.device
             self.expert_idx = torch.empty(T, self.k, dtype=torch.int32, device=dev)
             self.probs = torch.empty(T, self.k, dtype=torch.float32, device=dev)
-        B.moe_router_topk(T=T, E=E_all, k=self.k, logits=logits,
-                          expert_idx=self.expert_idx, probs=self.probs)
-        self.route(self.expert_idx, self.probs, x)
+        if not fused:
+            B.moe_router_topk(T=T, E=E_all, k=self.k, logits=logits,
+                              expert_idx=self.expert_idx, probs=self.probs)
+            self.route(self.expert_idx, self.probs, x)
+            return
+        if getattr(self, "ws_router", None) is None:
+            # its counters start at zero; every call leaves them at zero
+            self.ws_router = torch.zeros(B.moe_router_route_workspace_size(T, E_all, self.E),
+                                         dtype=torch.uint8, device=logits.device)
+        B.moe_router_route(T=T, E_total=E_all, k=self.k, E=self.E,
+                           first_expert=self.first_expert, M_cap=self.M_cap,
+                           logits=logits, expert_idx=self.expert_idx, probs=self.probs,
+                           split_sizes=self.split_sizes, offsets=self.offsets,
+                           padded_offsets=self.padded_offsets, row_id_map=self.row_id_map,
+                           row_src=self.row_src, probs_p=self.probs_p,
+                           err_flag=self.err_flag, workspace=self.ws_router)
+        if x is not None:
+            self.gather(x, self.xp, self.xp_q if self.mx else None,
+                        self.xp_s if self.mx else None)
 
     def gather(self, src: torch.Tensor, dst: Optional[torch.Tensor],
                dst_q: Optional[torch.Tensor] = None,

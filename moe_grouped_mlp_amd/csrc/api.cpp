@@ -574,6 +574,32 @@ moe_status moe_router_topk(const moe_router_args* a, void* stream) {
                                           static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_router_route_workspace_size(int T, int E_total, int E) {
+  if (T < 1 || E_total < 1 || E < 1) return 0;
+  return moe::router_route_workspace_bytes(T, E_total, E);
+}
+
+moe_status moe_router_route(const moe_router_route_args* a, void* stream) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  if (a->T < 1 || a->E_total < 1 || a->E_total > kMaxExperts || a->k < 1 || a->k > kMaxTopK ||
+      a->k > a->E_total || a->E < 1 || a->E > kMaxExperts || a->first_expert < 0 ||
+      a->M_cap < 1 || a->M_cap > INT32_MAX || !a->logits || !a->expert_idx || !a->probs ||
+      !a->split_sizes || !a->padded_offsets || !a->row_id_map || !a->row_src || !a->probs_p)
+    return MOE_ERR_INVALID_ARG;
+  if (!a->workspace ||
+      a->workspace_bytes < moe::router_route_workspace_bytes(a->T, a->E_total, a->E))
+    return MOE_ERR_WORKSPACE;
+  int cu = 0;
+  if (moe_status st = device_info(&cu)) return st;
+  // every workgroup must be resident at once (grid-wide barriers): a
+  // workgroup takes 256 threads and at most 53 KB of LDS, so a CU holds at
+  // least three; allow two per CU, and at most 512 (a column of chunk
+  // counts is scanned by one wave, eight chunks a lane)
+  const int64_t G = moe::router_route_chunks(a->T, a->E_total);
+  if (G > 2 * cu || G > 512) return MOE_ERR_UNSUPPORTED;
+  return launched(moe::launch_router_route(*a, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* a, void* stream) {
   if (!a) return MOE_ERR_INVALID_ARG;
   if (a->E < 1 || a->E > kMaxExperts || a->H < 64 || a->I < 64 || a->H % 64 != 0 ||

@@ -39,6 +39,10 @@ hipError_t launch_glu_unfused(int direction, const int32_t* split, const int32_t
                               float* dprobs, hipStream_t s);
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t* idx,
                               float* probs, hipStream_t s);
+// router + routing metadata in one launch (router_route.hip)
+hipError_t launch_router_route(const moe_router_route_args& a, hipStream_t s);
+int router_route_chunks(int T, int E_total);     // workgroups of the launch
+size_t router_route_workspace_bytes(int T, int E_total, int E);
 
 // ---- grouped GEMM --------------------------------------------------------
 // EPI_WGRAD: weight gradient C_e [P][Q] = sum over expert e's routed rows m

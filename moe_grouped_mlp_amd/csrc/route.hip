@@ -12,11 +12,11 @@
 //   scan     one workgroup: per expert, exclusive scan of the chunk counts
 //            over chunks (chunk bases, in place), split sizes, offsets and
 //            padded offsets (group starts aligned to MOE_GROUP_ALIGN rows).
-//   scatter  one workgroup per chunk: each wave ranks its 64 tokens per
-//            expert with ballots (the row order inside a group is ascending
-//            token id), adds the chunk base and the bases of earlier waves,
-//            and writes row_id_map / row_src / probs_p.  Extra workgroups
-//            mark pad rows (row_src = -1, probs_p = 0).
+//   scatter  one workgroup per chunk: a bitmap per expert of the chunk's
+//            tokens that picked it gives each slot its rank in the chunk
+//            (the row order inside a group is ascending token id); adds the
+//            chunk base and writes row_id_map / row_src / probs_p.  Extra
+//            workgroups mark pad rows (row_src = -1, probs_p = 0).
 #include "common.h"
 #include "kernels.h"
 
@@ -24,7 +24,6 @@ namespace moe {
 namespace {
 
 constexpr int kChunk = kRouteChunk;
-constexpr int kWavesPerChunk = kChunk / kWave;
 
 MOE_DEV int local_expert(int id, int first, int E) {
   int e = id - first;
@@ -65,11 +64,19 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   __shared__ int s_split[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int run = 0;
-    for (int c = 0; c < n_chunks; ++c) {
-      int64_t i = static_cast<int64_t>(c) * E + e;
-      int v = counts[i];
-      counts[i] = run;  // chunk base
-      run += v;
+    for (int c0 = 0; c0 < n_chunks; c0 += 16) {
+      // sixteen independent loads in flight, then the bases (in place)
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        v[j] = c0 + j < n_chunks ? counts[static_cast<int64_t>(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (c0 + j < n_chunks) {
+          counts[static_cast<int64_t>(c0 + j) * E + e] = run;  // chunk base
+          run += v[j];
+        }
+      }
     }
     s_split[e] = run;
     split[e] = run;
@@ -126,57 +133,46 @@ __global__ __launch_bounds__(kChunk) void route_scatter_kernel(
   }
 
   // ---- token rows ----
-  __shared__ int s_wcnt[kWavesPerChunk][kMaxExperts];
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  for (int i = threadIdx.x; i < kWavesPerChunk * E; i += blockDim.x)
-    s_wcnt[i / E][i % E] = 0;
+  // tokens of the chunk that picked each expert, one bit per token (LDS
+  // atomic OR: the result does not depend on arrival order); a slot's rank
+  // in the chunk is the count of bits below its token, so rows inside a
+  // group follow ascending token id, and a token that lists an expert twice
+  // maps both slots to one row (the first slot's)
+  __shared__ uint64_t s_mask[kMaxExperts][kChunk / 64];
+  for (int i = threadIdx.x; i < E * (kChunk / 64); i += blockDim.x)
+    s_mask[i / (kChunk / 64)][i % (kChunk / 64)] = 0;
   __syncthreads();
 
-  const int t = blockIdx.x * kChunk + threadIdx.x;
+  const int tl = threadIdx.x;
+  const int t = blockIdx.x * kChunk + tl;
   int my_e[kMaxTopK];
-  int my_rank[kMaxTopK];
-  unsigned pending = 0;  // bit s: slot s is local and not yet ranked
   for (int s = 0; s < kMaxTopK; ++s) {
     my_e[s] = -1;
-    my_rank[s] = 0;
     if (s < k && t < T) {
       my_e[s] = local_expert(idx[static_cast<int64_t>(t) * k + s], first, E);
-      if (my_e[s] >= 0) pending |= 1u << s;
+      if (my_e[s] >= 0)
+        atomicOr(reinterpret_cast<unsigned long long*>(&s_mask[my_e[s]][tl >> 6]),
+                 1ull << (tl & 63));
     }
-  }
-  // Rank per expert inside the wave: one iteration per distinct expert.
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  while (true) {
-    const uint64_t any = __ballot(pending != 0);
-    if (any == 0) break;
-    const int leader = __ffsll(static_cast<unsigned long long>(any)) - 1;
-    int cand = -1;
-    for (int s = 0; s < kMaxTopK; ++s)
-      if (cand < 0 && ((pending >> s) & 1u)) cand = my_e[s];
-    const int e = __shfl(cand, leader, kWave);
-    int hit = -1;  // first pending slot of this lane holding e
-    for (int s = 0; s < kMaxTopK; ++s)
-      if (((pending >> s) & 1u) && my_e[s] == e && hit < 0) hit = s;
-    const uint64_t mask = __ballot(hit >= 0);
-    const int rank = __popcll(mask & lt_mask);
-    for (int s = 0; s < kMaxTopK; ++s) {
-      if (((pending >> s) & 1u) && my_e[s] == e) {
-        my_rank[s] = rank;           // duplicates share the first slot's row
-        pending &= ~(1u << s);
-      }
-    }
-    if (lane == leader) s_wcnt[wave][e] = __popcll(mask);
   }
   __syncthreads();
+  int my_rank[kMaxTopK];
+  for (int s = 0; s < kMaxTopK; ++s) {
+    my_rank[s] = 0;
+    if (my_e[s] >= 0) {
+      const uint64_t* mk = s_mask[my_e[s]];
+      int rank = __popcll(mk[tl >> 6] & ((1ull << (tl & 63)) - 1));
+      for (int w = 0; w < (tl >> 6); ++w) rank += __popcll(mk[w]);
+      my_rank[s] = rank;
+    }
+  }
 
   if (t < T) {
     for (int s = 0; s < k; ++s) {
       const int e = my_e[s];
       int32_t r = -1;
       if (e >= 0) {
-        int base = padded[e] + chunk_base[static_cast<int64_t>(blockIdx.x) * E + e];
-        for (int w = 0; w < wave; ++w) base += s_wcnt[w][e];
+        const int base = padded[e] + chunk_base[static_cast<int64_t>(blockIdx.x) * E + e];
         const int64_t row = static_cast<int64_t>(base) + my_rank[s];
         if (row < M_cap) {
           r = static_cast<int32_t>(row);

@@ -51,6 +51,7 @@ STRUCTS = {
     "moe_bwd_args": B.BwdArgs,
     "moe_wgrad_args": B.WgradArgs,
     "moe_router_args": B.RouterArgs,
+    "moe_router_route_args": B.RouterRouteArgs,
     "moe_gemm_args": B.GemmArgs,
     "moe_glu_args": B.GluArgs,
 }
@@ -266,6 +267,36 @@ def test_bwd_validation():
     a.workspace_bytes = need
     a.z = None
     assert _call("moe_grouped_mlp_bwd", a) == INVALID
+
+
+def test_router_route_validation():
+    a = B.RouterRouteArgs()
+    a.T, a.E_total, a.k, a.E, a.first_expert, a.M_cap = 1000, 64, 4, 32, 0, 5000
+    for f in ("logits", "expert_idx", "probs", "split_sizes", "padded_offsets",
+              "row_id_map", "row_src", "probs_p", "workspace"):
+        setattr(a, f, 64)
+    need = B.moe_router_route_workspace_size(1000, 64, 32)
+    assert need == 4096 + 16 * 4 * 32        # counters + [ceil(T / 64)][E] counts
+    assert B.moe_router_route_workspace_size(1000, 32, 32) == 4096 + 4 * 4 * 32
+    a.workspace_bytes = need
+    assert _call("moe_router_route", a) == DEVICE
+    a.workspace_bytes = need - 1
+    assert _call("moe_router_route", a) == WORKSPACE
+    a.workspace_bytes = need
+    for field, bad in (("k", 9), ("k", 0), ("E_total", 1025), ("E", 0), ("T", 0),
+                       ("first_expert", -1), ("M_cap", 0)):
+        old = getattr(a, field)
+        setattr(a, field, bad)
+        assert _call("moe_router_route", a) == INVALID, field
+        setattr(a, field, old)
+    a.k, a.E_total = 8, 6                       # k > E_total
+    assert _call("moe_router_route", a) == INVALID
+    a.k, a.E_total = 4, 64
+    a.row_src = None
+    assert _call("moe_router_route", a) == INVALID
+    a.row_src = 64
+    a.offsets = None                            # optional
+    assert _call("moe_router_route", a) == DEVICE
 
 
 def test_bwd_noalloc_validation():
