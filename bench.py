@@ -224,16 +224,25 @@ def gemm_bench(args):
     flops = 2.0 * M * N * K
     evs = HipEvents(2)
     kernels = {}
+    clocks = {}
 
-    def timed(fn, n):
+    def timed(fn, n, tag=None):
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize()
-        evs.record(0, stream)
-        for _ in range(n):
-            fn()
-        evs.record(1, stream)
-        torch.cuda.synchronize()
+        trace = GemmClockTrace(dev, 1)
+        if tag:   # every launch rewrites the one record area: the last one stays
+            mg.moe_gemm_clock_trace(trace.buf, 1)
+        try:
+            evs.record(0, stream)
+            for _ in range(n):
+                fn()
+            evs.record(1, stream)
+            torch.cuda.synchronize()
+        finally:
+            trace.stop()
+        if tag:
+            clocks[tag] = trace.clocks()[0] if trace.buf[0].any() else None
         return evs.elapsed_ms(0, 1) / n
 
     for prec in ("bf16", "mxfp8", "mxfp4"):
@@ -262,11 +271,33 @@ def gemm_bench(args):
                          prec=mg.PREC_MXFP4 if f4 else mg.PREC_MXFP8)
         ms = timed(lambda: mg.moe_grouped_gemm(E=E, N=N, K=K, M_cap=M_cap, split_sizes=split,
                                                padded_offsets=padded, c=out, **args_),
-                   args.steps)
+                   args.steps, tag=prec)
         tf = flops / (ms * 1e-3) / 1e12
         kernels[f"gemm_{prec}"] = {"ms": round(ms, 4), "unit": "TFLOP/s", "rate": round(tf, 2),
                                    "pct_peak": round(100 * tf / PEAK_TFLOPS[prec], 2)}
-        log(f"  {ms:.3f} ms, {tf:.1f} TFLOP/s ({100 * tf / PEAK_TFLOPS[prec]:.1f}% of peak)")
+        ck = clocks.get(prec)
+        if ck:
+            kernels[f"gemm_{prec}"]["shader_clock_ghz"] = round(ck, 4)
+            kernels[f"gemm_{prec}"]["pct_peak_at_measured_clock"] = round(
+                100 * tf / (PEAK_TFLOPS[prec] * ck / 2.4), 2)
+        log(f"  {ms:.3f} ms, {tf:.1f} TFLOP/s ({100 * tf / PEAK_TFLOPS[prec]:.1f}% of peak)"
+            f"{f', clock {ck:.3f} GHz' if ck else ''}")
+    del a, w, out
+    torch.cuda.empty_cache()
+    # reference point: the vendor BLAS (hipBLASLt through torch.matmul) on one
+    # dense bf16 product of the same FLOPs, [M][K] x [K][N], both operands
+    # contiguous (no grouping, no epilogue)
+    xa = torch.randn(M, K, generator=g, device=dev).to(torch.bfloat16)
+    xb = (torch.randn(K, N, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    xc = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda: torch.matmul(xa, xb, out=xc), args.steps)
+    tf = flops / (ms * 1e-3) / 1e12
+    kernels["library_dense_bf16"] = {
+        "what": "torch.matmul (vendor BLAS) on one dense bf16 [M][K] x [K][N] product, same FLOPs",
+        "ms": round(ms, 4), "unit": "TFLOP/s", "rate": round(tf, 2),
+        "pct_peak": round(100 * tf / PEAK_TFLOPS["bf16"], 2)}
+    log(f"library dense bf16: {ms:.3f} ms, {tf:.1f} TFLOP/s")
+    del xa, xb, xc
     evs.close()
     f4 = kernels["gemm_mxfp4"]
     print(json.dumps({
@@ -285,18 +316,43 @@ def gemm_bench(args):
         "cpu_baseline": None}))
 
 
-CLOCK_FILE = os.path.join(ROOT, "profiles", "gemm_clock_mixtral.json")
+class GemmClockTrace:
+    """The shader clock the grouped GEMMs ran at.  While the library's GEMM
+    clock trace is set, each grouped-GEMM launch takes the next record area
+    and its persistent workgroups write their shader cycles and
+    constant-rate ticks from start to end; a launch's clock is the mean of
+    cycles / ticks x tick rate over its workgroups.  One area more than the
+    expected launches is set up: if it gets written, the launches were not
+    the expected ones and no clock is reported."""
 
+    def __init__(self, dev, launches):
+        import torch
+        import moe_grouped_mlp_amd as mg
+        self.mg = mg
+        self.n = launches
+        self.buf = torch.zeros(launches + 1, mg.CLOCK_MAX_WORKGROUPS, 2, dtype=torch.int64,
+                               device=dev)
+        self.rate = mg.moe_clock_tick_rate_hz()
 
-def measured_clock():
-    """The shader clock during the grouped GEMMs (GHz), from the committed
-    rocprofv3 GRBM_GUI_ACTIVE run (busy GPU cycles per dispatch over the
-    dispatch's duration), or None."""
-    try:
-        rec = json.load(open(CLOCK_FILE))
-    except (OSError, ValueError):
-        return None
-    return rec.get("clock_ghz")
+    def start(self):
+        self.mg.moe_gemm_clock_trace(self.buf, self.n + 1)
+
+    def stop(self):
+        self.mg.moe_gemm_clock_trace(None)
+
+    def clocks(self):
+        """Clock of each launch in GHz (None where nothing was recorded), or
+        None if the launches were not the expected ones."""
+        b = self.buf.cpu().numpy()
+        if self.rate <= 0 or b[self.n].any():
+            return None
+        out = []
+        for j in range(self.n):
+            r = b[j]
+            ok = (r[:, 0] > 0) & (r[:, 1] > 0)
+            out.append(float((r[ok, 0] / (r[ok, 1] / self.rate)).mean() / 1e9)
+                       if ok.any() else None)
+        return out
 
 
 def copy_ceiling_gbs(dev, mb=1024, reps=10):
@@ -448,13 +504,23 @@ def measure(args, config, prec, log_prefix=""):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the grouped GEMMs of one step, in launch order: the captured launches
+    # keep their clock-trace record areas, so every replay rewrites them
+    gemm_names = (["fc1", "fc2"] + (["fc1_recompute"] if args.recompute else []) +
+                  ["fc2_dgrad", "fc1_dgrad"] + (["wgrad_dw1", "wgrad_dw2"] if args.wgrad else []))
+    trace = GemmClockTrace(dev, len(gemm_names))
     gstream = torch.cuda.Stream()
     gstream.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(gstream):
         step()
-        with torch.cuda.graph(graph, stream=gstream, capture_error_mode="global"):
-            step()
+        torch.cuda.synchronize()
+        trace.start()
+        try:
+            with torch.cuda.graph(graph, stream=gstream, capture_error_mode="global"):
+                step()
+        finally:
+            trace.stop()
     torch.cuda.synchronize()
     log(f"{log_prefix}graph warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -474,7 +540,11 @@ def measure(args, config, prec, log_prefix=""):
     ms_step = elapsed * 1e3 / args.steps
     per = sorted(ge.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps))
     ge.close()
-    del graph
+    # the GEMMs' clocks in the last timed replay
+    clk_list = trace.clocks()
+    gemm_clock = (dict(zip(gemm_names, clk_list)) if clk_list is not None
+                  else {n: None for n in gemm_names})
+    del graph, trace
     timing = {"method": "HIP graph replays of the whole step (global capture mode)",
               "mean_ms": round(ms_step, 4), "median_ms": round(_pct(per, 0.5), 4),
               "p10_ms": round(_pct(per, 0.1), 4), "p90_ms": round(_pct(per, 0.9), 4)}
@@ -522,6 +592,8 @@ def measure(args, config, prec, log_prefix=""):
             ("fc1_recompute",) if args.recompute else ()):
         kernels[name] = {"ms": round(seg_ms[name], 4), "unit": "TFLOP/s",
                          "rate": round(flops_k[name] / (seg_ms[name] * 1e-3) / 1e12, 2)}
+        if gemm_clock.get(name):
+            kernels[name]["shader_clock_ghz"] = round(gemm_clock[name], 4)
     mem = {"route_permute_x": T * H * 2 + M * row_bytes + idx_bytes,
            "unpermute_out": M * H * 2 + T * H * 2 + T * k * 4,
            "permute_dout": T * H * 2 + M * row_bytes + T * k * 4,
@@ -555,6 +627,14 @@ def measure(args, config, prec, log_prefix=""):
         kernels["quantize_weights"] = {"ms": round(q_ms, 4), "unit": "GB/s",
                                        "rate": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
                                        "outside_step": True}
+    # the clock of the step's GEMMs, weighted by their times
+    gk = [(kernels[n]["ms"], gemm_clock[n]) for n in gemm_names if gemm_clock.get(n)]
+    timing["gemm_shader_clock_ghz"] = (
+        round(sum(ms * c for ms, c in gk) / sum(ms for ms, _ in gk), 4)
+        if len(gk) == len(gemm_names) else None)
+    timing["clock_method"] = ("each grouped-GEMM launch of the last timed replay: shader "
+                              "cycles over constant-rate ticks of its persistent workgroups, "
+                              "weighted by the GEMMs' times")
     sizes = blk.split_sizes.cpu().tolist()
     del blk
     torch.cuda.empty_cache()
@@ -745,7 +825,7 @@ def main():
         kernels[name]["frac_of_copy"] = round(kernels[name]["rate"] / ceiling, 3)
     peak = PEAK_TFLOPS[prec]
     value, ms_step = r["value"], r["ms_step"]
-    clock = measured_clock()
+    clock = r["timing"]["gemm_shader_clock_ghz"]
     log(f"step {ms_step:.3f} ms (median {r['timing']['median_ms']:.3f}), {value:.1f} TFLOP/s; " +
         ", ".join(f"{n} {v['ms']:.3f} ms {v['rate']} {v['unit']}" for n, v in kernels.items()))
 
@@ -761,6 +841,9 @@ def main():
                       "epilogues",
             "value": round(s["value"], 3), "unit": "TFLOP/s", "ms_per_step": round(s["ms_step"], 4),
             "pct_mfma_peak": round(100.0 * s["value"] / pk8, 2), "timing": s["timing"],
+            "pct_mfma_peak_at_measured_clock": (
+                round(100.0 * s["value"] / (pk8 * s["timing"]["gemm_shader_clock_ghz"] / 2.4), 2)
+                if s["timing"]["gemm_shader_clock_ghz"] else None),
             "kernels": s["kernels"],
             "roofline": {"bound": "mfma", "kernel": "FC1 grouped GEMM + activation epilogue "
                                                     "(MXFP8)",
@@ -822,7 +905,7 @@ def main():
     }
     if clock:
         # the dense MFMA peak scales with the shader clock: 2.4 GHz for the
-        # published figure
+        # published figure; `clock` is the average over the timed replays
         out["measured_clock_ghz"] = clock
         out["pct_mfma_peak_at_measured_clock"] = round(100.0 * value / (peak * clock / 2.4), 2)
         out["roofline"]["frac_at_measured_clock"] = round(

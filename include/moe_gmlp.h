@@ -640,6 +640,35 @@ moe_status moe_router_route(const moe_router_route_args* args, void* stream);
 size_t moe_grouped_mlp_workspace_size(int E, int H, int I, int64_t M_cap,
                                       int prec, int act);
 
+/* ------------------------------------------------------------------------
+ * Measurement: the shader clock the grouped GEMMs ran at.
+ *
+ * The dense MFMA peak is quoted at the 2.4 GHz maximum shader clock; under
+ * a sustained GEMM load the power manager runs the clock lower, so
+ * throughput is also judged against the peak at the clock the work ran at.
+ *
+ * Clock trace of the grouped GEMMs.  While set, every
+ * grouped-GEMM launch that follows (inside moe_grouped_mlp_fwd, _bwd,
+ * _bwd_noalloc, _wgrad and moe_grouped_gemm) takes the next of `slots`
+ * record areas in turn, and its workgroup i writes, as it ends,
+ * area[2 i] = shader cycles and area[2 i + 1] = constant-rate ticks
+ * (moe_clock_tick_rate_hz) since it started; area j starts at
+ * records + j x 2 x MOE_CLOCK_MAX_WORKGROUPS.  Workgroups live for the
+ * whole launch (persistent), so cycles / ticks x the tick rate is the clock
+ * the GEMM ran at, on that workgroup's compute unit.  Launches with more
+ * workgroups than MOE_CLOCK_MAX_WORKGROUPS record nothing.
+ *   records: device int64 [slots][MOE_CLOCK_MAX_WORKGROUPS][2], caller-owned,
+ *   kept until the trace is cleared; NULL clears the trace (slots ignored).
+ *   1 <= slots <= 64, else MOE_ERR_INVALID_ARG.  Launches captured into a
+ *   graph keep the area they were captured with.  The setting is global to
+ *   the process; the slot counter restarts at 0 on every call. */
+#define MOE_CLOCK_MAX_WORKGROUPS 1024
+moe_status moe_gemm_clock_trace(int64_t* records, int slots);
+
+/* Frequency of the constant-rate counter on the current device (Hz), 0 if
+ * it cannot be read. */
+int64_t moe_clock_tick_rate_hz(void);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);
 

@@ -33,7 +33,8 @@ EXPORTED_SYMBOLS = (
     "moe_router_topk", "moe_grouped_gemm", "moe_glu_unfused",
     "moe_grouped_mlp_workspace_size", "moe_status_string", "moe_gmlp_version",
     "moe_mx_scale_offset", "moe_grouped_mlp_bwd_noalloc", "moe_router_route",
-    "moe_router_route_workspace_size",
+    "moe_router_route_workspace_size", "moe_clock_tick_rate_hz",
+    "moe_gemm_clock_trace",
 )
 
 
@@ -189,6 +190,10 @@ def lib() -> ctypes.CDLL:
         L.moe_router_route_workspace_size.argtypes = [c_int, c_int, c_int]
         L.moe_mx_scale_offset.restype = c_int64
         L.moe_mx_scale_offset.argtypes = [c_int64, c_int64, c_int64]
+        L.moe_clock_tick_rate_hz.restype = c_int64
+        L.moe_clock_tick_rate_hz.argtypes = []
+        L.moe_gemm_clock_trace.restype = c_int
+        L.moe_gemm_clock_trace.argtypes = [c_void_p, c_int]
         L.moe_grouped_mlp_workspace_size.restype = c_size_t
         L.moe_grouped_mlp_workspace_size.argtypes = [
             c_int, c_int, c_int, c_int64, c_int, c_int]
@@ -395,13 +400,28 @@ def moe_router_route_workspace_size(T, E_total, E) -> int:
 def moe_router_route(*, T, E_total, k, E, M_cap, logits, expert_idx, probs, split_sizes,
                      padded_offsets, row_id_map, row_src, probs_p, workspace, offsets=None,
                      first_expert=0, err_flag=None, stream=None):
-    """Router and routing metadata in one launch; the workspace's first 256
-    bytes must be zero before the first call (each call leaves them zero)."""
+    """Router and routing metadata in one launch; the workspace's first 4096
+    bytes must be zero before the first call (each call leaves them as the
+    next call expects)."""
     args = RouterRouteArgs(T, E_total, k, E, first_expert, M_cap, _ptr(logits),
                            _ptr(expert_idx), _ptr(probs), _ptr(split_sizes), _ptr(offsets),
                            _ptr(padded_offsets), _ptr(row_id_map), _ptr(row_src),
                            _ptr(probs_p), _ptr(err_flag), _ptr(workspace), _nbytes(workspace))
     _check("moe_router_route", lib().moe_router_route(ctypes.byref(args), _stream(stream)))
+
+
+def moe_clock_tick_rate_hz() -> int:
+    return lib().moe_clock_tick_rate_hz()
+
+
+CLOCK_MAX_WORKGROUPS = 1024
+
+
+def moe_gemm_clock_trace(records=None, slots=1):
+    """Grouped-GEMM launches that follow write per-workgroup {cycles, ticks}
+    into records (device int64 [slots][CLOCK_MAX_WORKGROUPS][2]) in turn;
+    records=None clears the trace."""
+    _check("moe_gemm_clock_trace", lib().moe_gemm_clock_trace(_ptr(records), slots))
 
 
 def moe_grouped_gemm(*, E, N, K, M_cap, split_sizes, padded_offsets, a, b, c,

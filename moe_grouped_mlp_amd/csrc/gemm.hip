@@ -1,10 +1,18 @@
 // Grouped GEMM: launch dispatch over the kernel families, tile geometry
 // queries, and the fixed-order reduction of the per-N-tile dprobs partials
 // written by the dGLU epilogue.  The kernel itself is in gemm_kernel.h.
+#include <atomic>
+
+#include "../../include/moe_gmlp.h"
 #include "gemm_kernel.h"
 
 namespace moe {
 namespace {
+
+// clock trace (moe_gemm_clock_trace): record area, its slots, next slot
+std::atomic<int64_t*> g_clk_records{nullptr};
+std::atomic<int> g_clk_slots{0};
+std::atomic<unsigned> g_clk_next{0};
 
 // dprobs_p[r] = sum_n part[r][n] for valid rows (fixed order), 0 for pad rows.
 __global__ __launch_bounds__(256) void dprobs_reduce_kernel(
@@ -45,8 +53,18 @@ size_t grouped_gemm_split_bytes(int grid) {
 int grouped_gemm_tile_m() { return BM; }
 int grouped_gemm_split_limit() { return kMaxSplit; }
 
-hipError_t launch_grouped_gemm(const GemmArgs& g, int epi, bool b_nn, bool mx, int grid,
+int64_t* gemm_clock_slot(int grid) {
+  int64_t* rec = g_clk_records.load(std::memory_order_acquire);
+  const int slots = g_clk_slots.load(std::memory_order_acquire);
+  if (!rec || slots < 1 || grid > MOE_CLOCK_MAX_WORKGROUPS) return nullptr;
+  const unsigned i = g_clk_next.fetch_add(1, std::memory_order_relaxed) % slots;
+  return rec + static_cast<int64_t>(i) * MOE_CLOCK_MAX_WORKGROUPS * 2;
+}
+
+hipError_t launch_grouped_gemm(const GemmArgs& g_in, int epi, bool b_nn, bool mx, int grid,
                                hipStream_t s) {
+  GemmArgs g = g_in;
+  g.clk = gemm_clock_slot(grid);
   if (mx && b_nn) return hipErrorInvalidValue;
   if (epi == EPI_STORE) return launch_gemm_store(g, b_nn, mx, grid, s);
   if (epi == EPI_WGRAD) return b_nn ? hipErrorInvalidValue : launch_gemm_wgrad(g, mx, grid, s);
@@ -72,3 +90,22 @@ hipError_t launch_dprobs_reduce(const float* part, int n_part, const int32_t* sp
 }
 
 }  // namespace moe
+
+extern "C" int64_t moe_clock_tick_rate_hz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return static_cast<int64_t>(khz) * 1000;
+}
+
+extern "C" moe_status moe_gemm_clock_trace(int64_t* records, int slots) {
+  if (records && (slots < 1 || slots > 64)) return MOE_ERR_INVALID_ARG;
+  moe::g_clk_records.store(nullptr, std::memory_order_release);
+  moe::g_clk_slots.store(records ? slots : 0, std::memory_order_release);
+  moe::g_clk_next.store(0, std::memory_order_relaxed);
+  moe::g_clk_records.store(records, std::memory_order_release);
+  return MOE_OK;
+}

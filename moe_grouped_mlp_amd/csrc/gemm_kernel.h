@@ -907,6 +907,12 @@ void grouped_gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t s_tr[kTrWords];
 
   const int tid = threadIdx.x;
+  // measurement: the workgroup's shader cycles and constant-rate ticks
+  int64_t clk_c0 = 0, clk_t0 = 0;
+  if (g.clk) {
+    clk_c0 = static_cast<int64_t>(__builtin_amdgcn_s_memtime());
+    clk_t0 = static_cast<int64_t>(__builtin_amdgcn_s_memrealtime());
+  }
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
@@ -1535,6 +1541,12 @@ void grouped_gemm_kernel(GemmArgs g) {
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       bare_barrier();  // s_red is reused by the next tile
     }
+  }
+  if (g.clk && tid == 0) {
+    const int64_t c1 = static_cast<int64_t>(__builtin_amdgcn_s_memtime());
+    const int64_t t1 = static_cast<int64_t>(__builtin_amdgcn_s_memrealtime());
+    g.clk[2 * blockIdx.x] = c1 - clk_c0;
+    g.clk[2 * blockIdx.x + 1] = t1 - clk_t0;
   }
 }
 

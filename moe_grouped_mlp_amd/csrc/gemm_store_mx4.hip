@@ -7,7 +7,9 @@
 
 namespace moe {
 
-hipError_t launch_gemm_store_f4(const GemmArgs& g, int grid, hipStream_t s) {
+hipError_t launch_gemm_store_f4(const GemmArgs& g_in, int grid, hipStream_t s) {
+  GemmArgs g = g_in;
+  g.clk = gemm_clock_slot(grid);
   grouped_gemm_kernel<EPI_STORE, false, MOE_ACT_SWIGLU, true, true>
       <<<dim3(grid), dim3(kThreads), 0, s>>>(g);
   return hipGetLastError();

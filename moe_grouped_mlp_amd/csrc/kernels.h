@@ -92,10 +92,16 @@ struct GemmArgs {
   uint8_t* mx_qT;        // nullable
   uint8_t* mx_sT;
   int mx_n;
+  // measurement (nullable): workgroup i writes clk[2 i] = shader cycles and
+  // clk[2 i + 1] = constant-rate ticks between its start and its end
+  int64_t* clk;
 };
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, int epi, bool b_nn, bool mx,
                                int grid, hipStream_t s);
+// the record area of the next grouped-GEMM launch while a clock trace is set
+// (moe_gemm_clock_trace), else null
+int64_t* gemm_clock_slot(int grid);
 // MXFP4 operands (A, B: packed E2M1 codes, K / 2 bytes per row; b_stride
 // in values), plain store, no split-K
 hipError_t launch_gemm_store_f4(const GemmArgs& g, int grid, hipStream_t s);

@@ -5,6 +5,11 @@
   offsetof of every field, read from a C program built with gcc);
 * argument validation rejects bad calls before touching a device, and a
   valid call without a gfx950 device reports MOE_ERR_DEVICE.
+
+The validation checks pass placeholder addresses (8, 16, 64) for device
+buffers, so they run only where no HIP device is present: with one, a valid
+call would launch kernels on those addresses.  The GPU tests cover valid
+calls with real buffers.
 """
 
 import ctypes
@@ -22,6 +27,20 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_gmlp.h")
 
 INVALID, UNSUPPORTED, WORKSPACE, DEVICE = -1, -2, -3, -5
+
+
+def _hip_device_present():
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return False
+    n = ctypes.c_int(0)
+    return hip.hipGetDeviceCount(ctypes.byref(n)) == 0 and n.value > 0
+
+
+no_device = pytest.mark.skipif(
+    _hip_device_present(),
+    reason="placeholder device addresses: valid calls would launch on a present device")
 
 
 def _header_functions():
@@ -89,6 +108,7 @@ def _call(fn, st):
     return getattr(m.lib(), fn)(ctypes.byref(st), None)
 
 
+@no_device
 def test_repack_validation():
     L = m.lib()
     assert L.moe_weight_repack_interleave(None, 8, 1, 64, 64, 64, 0, None) == INVALID
@@ -112,6 +132,7 @@ def _permute_args(**kw):
     return a
 
 
+@no_device
 def test_permute_validation():
     assert _call("moe_permute", _permute_args()) == DEVICE
     assert _call("moe_permute", _permute_args(flags=0)) == INVALID
@@ -141,6 +162,7 @@ def _fwd_args(**kw):
     return a
 
 
+@no_device
 def test_fwd_validation():
     assert _call("moe_grouped_mlp_fwd", _fwd_args()) == DEVICE
     assert _call("moe_grouped_mlp_fwd", _fwd_args(H=96)) == INVALID
@@ -159,6 +181,7 @@ def test_fwd_validation():
     assert _call("moe_grouped_mlp_fwd", _fwd_args(z=None)) == DEVICE
 
 
+@no_device
 def test_unfused_baseline_validation():
     def gemm(**kw):
         a = B.GemmArgs(4, 256, 128, 1024, 0, 0, 64, 64, 64, 64, 0, 64, None, 0,
@@ -199,6 +222,7 @@ def test_unfused_baseline_validation():
         assert _call("moe_glu_unfused", glu(**bad)) == INVALID, bad
 
 
+@no_device
 def test_router_validation():
     def args(**kw):
         a = B.RouterArgs(16, 8, 2, 64, 64, 64)
@@ -214,6 +238,7 @@ def test_router_validation():
         assert _call("moe_router_topk", args(**bad)) == INVALID, bad
 
 
+@no_device
 def test_wgrad_validation():
     def args(**kw):
         a = B.WgradArgs()
@@ -245,6 +270,7 @@ def test_wgrad_validation():
     assert _call("moe_grouped_mlp_wgrad", args(**{**mx, "M_cap": 1000})) == INVALID
 
 
+@no_device
 def test_bwd_validation():
     a = B.BwdArgs()
     a.E, a.H, a.I, a.M_cap, a.prec = 4, 128, 256, 1024, B.PREC_BF16
@@ -269,6 +295,7 @@ def test_bwd_validation():
     assert _call("moe_grouped_mlp_bwd", a) == INVALID
 
 
+@no_device
 def test_router_route_validation():
     a = B.RouterRouteArgs()
     a.T, a.E_total, a.k, a.E, a.first_expert, a.M_cap = 1000, 64, 4, 32, 0, 5000
@@ -299,6 +326,7 @@ def test_router_route_validation():
     assert _call("moe_router_route", a) == DEVICE
 
 
+@no_device
 def test_bwd_noalloc_validation():
     """The backward without a workspace argument: the same host checks
     first, then the fixed scratch size (MOE_ERR_UNSUPPORTED past it), then
@@ -323,6 +351,7 @@ def test_bwd_noalloc_validation():
     assert m.lib().moe_grouped_mlp_bwd_noalloc(None, None) == INVALID
 
 
+@no_device
 def test_unpermute_validation():
     a = B.UnpermuteArgs(8, 2, 64, 100, 64, 64, 64, None, None)
     assert _call("moe_unpermute", a) == DEVICE
@@ -330,6 +359,15 @@ def test_unpermute_validation():
     assert _call("moe_unpermute", a) == INVALID
     a.dprobs, a.H = None, 12
     assert _call("moe_unpermute", a) == INVALID
+
+
+@no_device
+def test_gemm_clock_trace_validation():
+    L = m.lib()
+    assert L.moe_gemm_clock_trace(64, 0) == INVALID
+    assert L.moe_gemm_clock_trace(64, 65) == INVALID
+    assert L.moe_gemm_clock_trace(None, 0) == 0      # clearing needs no slots
+    assert L.moe_gemm_clock_trace(None, 5) == 0
 
 
 def test_status_strings():
@@ -363,6 +401,7 @@ def _quant_args(**kw):
     return a
 
 
+@no_device
 def test_quantize_validation():
     assert _call("moe_quantize_mxfp8", _quant_args()) == DEVICE
     assert _call("moe_quantize_mxfp8", _quant_args(mode=B.QUANT_COL)) == DEVICE
@@ -377,6 +416,7 @@ def test_quantize_validation():
     assert _call("moe_quantize_mxfp8", _quant_args(x_stride=128 * 192 + 8)) == DEVICE
 
 
+@no_device
 def test_quantize_mxfp4_validation():
     assert _call("moe_quantize_mxfp4", _quant_args()) == DEVICE
     assert _call("moe_quantize_mxfp4", _quant_args(rows=96)) == DEVICE      # % 32 is enough
@@ -390,6 +430,7 @@ def test_quantize_mxfp4_validation():
     assert _call("moe_quantize_mxfp4", _quant_args(x_stride=128 * 192 + 4)) == INVALID
 
 
+@no_device
 def test_permute_write_mx_validation():
     mx = B.PERMUTE_BUILD_MAP | B.PERMUTE_GATHER | B.PERMUTE_WRITE_MX
     ok = dict(flags=mx, xp_q=64, xp_s=64, M_cap=640)
@@ -403,6 +444,7 @@ def test_permute_write_mx_validation():
         **{**ok, "flags": B.PERMUTE_BUILD_MAP | B.PERMUTE_WRITE_MX})) == INVALID
 
 
+@no_device
 def test_fwd_bwd_mx_validation():
     mx_fwd = ("xp_q", "xp_s", "w1_q", "w1_s", "w2_q", "w2_s", "a_q", "a_s")
     base = {f: 64 for f in mx_fwd}
