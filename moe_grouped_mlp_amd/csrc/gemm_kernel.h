@@ -19,11 +19,13 @@
 //     loaders and the LDS image; a lane's MXFP8 operand (32 bytes) is exactly
 //     the pair of 16-byte chunks a bf16 lane reads for its two K sub-steps.
 //   * Operands go from HBM straight into LDS (buffer_load_dwordx4 ... lds):
-//     four stages of 2 x 16 KB, loads three K steps ahead of the MFMAs.  Each
-//     lane fetches the 16-byte chunk that belongs at its slot of the swizzled
-//     image, so there is no VGPR staging and no ds_write.  MXFP8 scales ride
-//     along: 1 KB per stage (8 row groups x 64 bytes for A and for B, the
-//     tiled scale layout), one dword DMA per wave.
+//     two stages of 2 x 32 KB (128 bytes of every operand row each); the
+//     loads of stage k + 2 go out as soon as every wave is done with stage k,
+//     into its buffer, one stage ahead of their use.  Each lane fetches the
+//     16-byte chunk that belongs at its slot of the swizzled image, so there
+//     is no VGPR staging and no ds_write.  MXFP8 scales ride along: 2 KB per
+//     stage (8 row groups x 128 bytes for A and for B, the tiled scale
+//     layout).
 //   * K-contiguous operands ([rows][K]: activations, and the weights of every
 //     GEMM except the bf16 dgrad ones): LDS rows of 64 bytes, 16-byte chunk c
 //     of row r stored at c ^ ((r >> 2) & 3), which keeps the operand reads (16
