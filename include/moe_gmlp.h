@@ -277,9 +277,14 @@ moe_status moe_quantize_mxfp4(const moe_quant_args* args, void* stream);
  *   For every local expert e and row r in [padded_offsets[e],
  *   padded_offsets[e] + split_sizes[e]):
  *     z[r]  = xp[r] . W1i_e^T                 (fp32 accumulate, stored bf16)
- *     a[r]  = bf16( probs_p[r] * act(z[r]) )   (act on the fp32 accumulator)
+ *     a[r]  = bf16( probs_p[r] * act(z[r] + b_e) )  (act on the fp32 accumulator)
  *     yp[r] = bf16( a[r] . W2_e^T )
  *   Rows outside those ranges are not written.
+ *   b_e is the optional FC1 bias ([FK] § "Optimizing GLU activations with
+ *   fused GEMM epilogues": the epilogue also folds in a bias-vector add):
+ *   bias1 fp32 [E][N1] in LOGICAL column order (gated: the gate half, then
+ *   the up half; not interleaved), added to the fp32 accumulator before the
+ *   activation; z is stored without it.  NULL: no bias.
  *   Shapes: N1 = 2I (gated) or I (sReLU).
  *     xp   bf16 [M_cap][H]
  *     w1i  bf16 [E][N1][H], gated: interleaved by moe_weight_repack_interleave
@@ -339,6 +344,7 @@ typedef struct moe_fwd_args {
    * split its last, partial round of tiles along K; NULL disables that */
   void* workspace;
   size_t workspace_bytes;
+  const float* bias1;          /* optional [E][N1] fp32, logical order (see above) */
 } moe_fwd_args;
 
 moe_status moe_grouped_mlp_fwd(const moe_fwd_args* args, void* stream);
@@ -352,9 +358,12 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* args, void* stream);
  *
  *   For every valid row r of expert e:
  *     dA[r]       = dyp[r] . W2_e                   (fp32, not stored)
- *     s[r]        = act(z[r])                       (recomputed from bf16 z)
+ *     s[r]        = act(z[r] + b_e)                 (recomputed from bf16 z)
  *     dprobs_p[r] = sum_j dA[r][j] * s[r][j]        (fixed-order, deterministic)
- *     dz[r]       = bf16( dact(z[r], probs_p[r] * dA[r]) )  (layout of z)
+ *     dz[r]       = bf16( dact(z[r] + b_e, probs_p[r] * dA[r]) )  (layout of z)
+ *   with b_e the forward's optional bias1 (NULL: none); dz is also the
+ *   gradient of b_e's summands (sum dz over an expert's rows, in logical
+ *   order, is dL/db_e).
  *     dxp[r]      = bf16( dz[r] . W1i_e )           (contracts over N1)
  *   Shapes as in moe_grouped_mlp_fwd; dyp bf16 [M_cap][H]; dz bf16
  *   [M_cap][N1]; dprobs_p float [M_cap]; dxp bf16 [M_cap][H].
@@ -403,6 +412,7 @@ typedef struct moe_bwd_args {
   const uint8_t* w1t_q; const uint8_t* w1t_s;  /* [E][H][N1], along N1  */
   uint8_t* dz_q;  uint8_t* dz_s;               /* [M_cap][N1], along N1 */
   uint8_t* dzT_q; uint8_t* dzT_s;              /* [N1][M_cap], along M (optional) */
+  const float* bias1;          /* optional [E][N1] fp32, as in the forward */
 } moe_bwd_args;
 
 moe_status moe_grouped_mlp_bwd(const moe_bwd_args* args, void* stream);

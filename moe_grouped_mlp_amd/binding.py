@@ -92,7 +92,8 @@ class FwdArgs(ctypes.Structure):
                 ("w2_q", c_void_p), ("w2_s", c_void_p),
                 ("a_q", c_void_p), ("a_s", c_void_p),
                 ("aT_q", c_void_p), ("aT_s", c_void_p),
-                ("workspace", c_void_p), ("workspace_bytes", c_size_t)]
+                ("workspace", c_void_p), ("workspace_bytes", c_size_t),
+                ("bias1", c_void_p)]
 
 
 class BwdArgs(ctypes.Structure):
@@ -111,7 +112,7 @@ class BwdArgs(ctypes.Structure):
                 ("w2t_q", c_void_p), ("w2t_s", c_void_p),
                 ("w1t_q", c_void_p), ("w1t_s", c_void_p),
                 ("dz_q", c_void_p), ("dz_s", c_void_p),
-                ("dzT_q", c_void_p), ("dzT_s", c_void_p)]
+                ("dzT_q", c_void_p), ("dzT_s", c_void_p), ("bias1", c_void_p)]
 
 
 class GemmArgs(ctypes.Structure):
@@ -317,14 +318,15 @@ def moe_grouped_mlp_fwd(*, E, H, I, M_cap, split_sizes, padded_offsets,
                         cu_margin=0, w1_stride=0, w2_stride=0, err_flag=None,
                         timing_events=None, xp_q=None, xp_s=None, w1_q=None,
                         w1_s=None, w2_q=None, w2_s=None, a_q=None, a_s=None,
-                        aT_q=None, aT_s=None, workspace=None, stream=None):
+                        aT_q=None, aT_s=None, workspace=None, bias1=None, stream=None):
     args = FwdArgs(E, H, I, M_cap, prec, act or act_params(), cu_margin,
                    _ptr(split_sizes), _ptr(padded_offsets), _ptr(probs_p),
                    _ptr(xp), _ptr(w1i), _ptr(w2), w1_stride, w2_stride,
                    _ptr(z), _ptr(a), _ptr(amax), _ptr(yp), _ptr(err_flag),
                    _events(timing_events), _ptr(xp_q), _ptr(xp_s), _ptr(w1_q),
                    _ptr(w1_s), _ptr(w2_q), _ptr(w2_s), _ptr(a_q), _ptr(a_s),
-                   _ptr(aT_q), _ptr(aT_s), _ptr(workspace), _nbytes(workspace))
+                   _ptr(aT_q), _ptr(aT_s), _ptr(workspace), _nbytes(workspace),
+                   _ptr(bias1))
     _check("moe_grouped_mlp_fwd",
            lib().moe_grouped_mlp_fwd(ctypes.byref(args), _stream(stream)))
 
@@ -336,7 +338,7 @@ def moe_grouped_mlp_bwd(*, E, H, I, M_cap, split_sizes, padded_offsets,
                         timing_events=None, dyp_q=None, dyp_s=None,
                         w2t_q=None, w2t_s=None, w1t_q=None, w1t_s=None,
                         dz_q=None, dz_s=None, dzT_q=None, dzT_s=None,
-                        stream=None):
+                        bias1=None, stream=None):
     args = BwdArgs(E, H, I, M_cap, prec, act or act_params(), cu_margin,
                    _ptr(split_sizes), _ptr(padded_offsets), _ptr(probs_p),
                    _ptr(dyp), _ptr(w2), _ptr(z), _ptr(w1i), w1_stride,
@@ -344,7 +346,7 @@ def moe_grouped_mlp_bwd(*, E, H, I, M_cap, split_sizes, padded_offsets,
                    _ptr(err_flag), _ptr(workspace), _nbytes(workspace),
                    _events(timing_events), _ptr(dyp_q), _ptr(dyp_s),
                    _ptr(w2t_q), _ptr(w2t_s), _ptr(w1t_q), _ptr(w1t_s),
-                   _ptr(dz_q), _ptr(dz_s), _ptr(dzT_q), _ptr(dzT_s))
+                   _ptr(dz_q), _ptr(dz_s), _ptr(dzT_q), _ptr(dzT_s), _ptr(bias1))
     _check("moe_grouped_mlp_bwd",
            lib().moe_grouped_mlp_bwd(ctypes.byref(args), _stream(stream)))
 
@@ -356,7 +358,7 @@ def moe_grouped_mlp_bwd_noalloc(*, E, H, I, M_cap, split_sizes, padded_offsets,
                                 timing_events=None, dyp_q=None, dyp_s=None,
                                 w2t_q=None, w2t_s=None, w1t_q=None, w1t_s=None,
                                 dz_q=None, dz_s=None, dzT_q=None, dzT_s=None,
-                                stream=None):
+                                bias1=None, stream=None):
     """moe_grouped_mlp_bwd without a workspace argument: the library's fixed
     per-device scratch array serves as the workspace (for callers that
     cannot allocate)."""
@@ -367,7 +369,7 @@ def moe_grouped_mlp_bwd_noalloc(*, E, H, I, M_cap, split_sizes, padded_offsets,
                    _ptr(err_flag), None, 0,
                    _events(timing_events), _ptr(dyp_q), _ptr(dyp_s),
                    _ptr(w2t_q), _ptr(w2t_s), _ptr(w1t_q), _ptr(w1t_s),
-                   _ptr(dz_q), _ptr(dz_s), _ptr(dzT_q), _ptr(dzT_s))
+                   _ptr(dz_q), _ptr(dz_s), _ptr(dzT_q), _ptr(dzT_s), _ptr(bias1))
     _check("moe_grouped_mlp_bwd_noalloc",
            lib().moe_grouped_mlp_bwd_noalloc(ctypes.byref(args), _stream(stream)))
 

@@ -94,6 +94,7 @@ class ExpertBlock:
         self.row_src = torch.zeros(M, **i32)
         self.probs_p = torch.zeros(M, **f32)
         self.err_flag = torch.zeros(1, **i32)
+        self.bias1 = None            # optional FC1 bias, fp32 [E][N1] (load_weights)
         self.ws_route = torch.empty(max(1, B.moe_permute_workspace_size(T, E)),
                                     dtype=torch.uint8, device=dev)
         # bf16 a and dz: operands of the bf16 GEMMs; optional with MXFP8
@@ -179,10 +180,20 @@ class ExpertBlock:
             self.dw2 = torch.empty(E, H, I, **bf)
 
     # ------------------------------------------------------------ weights --
-    def load_weights(self, w1: torch.Tensor, w2: torch.Tensor) -> None:
+    def load_weights(self, w1: torch.Tensor, w2: torch.Tensor,
+                     bias1: Optional[torch.Tensor] = None) -> None:
         """w1: bf16 [E][N1][H] (gate rows then up rows), w2: bf16 [E][H][I].
         The gated FC1 weight is repacked into the interleaved layout; with
-        MXFP8 the weight copies are then quantized."""
+        MXFP8 the weight copies are then quantized.  bias1: optional FC1
+        bias, [E][N1] in the same logical order as w1's rows (kept as fp32;
+        the fused forward and backward add it to the activation's input)."""
+        if bias1 is None:
+            self.bias1 = None
+        else:
+            if tuple(bias1.shape) != (self.E, self.N1):
+                raise ValueError(f"bias1 must be [{self.E}][{self.N1}]")
+            self.bias1 = bias1.detach().to(device=self.w2.device,
+                                           dtype=torch.float32).contiguous()
         if self.gated:
             B.moe_weight_repack_interleave(w1, self.w1i, self.E, self.I,
                                            self.H)
@@ -295,7 +306,7 @@ class ExpertBlock:
                               yp=self.yp, amax=self.amax, act=self.act,
                               prec=self.prec, cu_margin=self.cu_margin,
                               err_flag=self.err_flag, workspace=self.ws,
-                              timing_events=timing_events, **kw)
+                              timing_events=timing_events, bias1=self.bias1, **kw)
         self._z_valid = not self.recompute
 
     def recompute_z(self) -> None:
@@ -359,7 +370,7 @@ class ExpertBlock:
                               workspace=self.ws, act=self.act,
                               prec=self.prec, cu_margin=self.cu_margin,
                               err_flag=self.err_flag,
-                              timing_events=timing_events, **kw)
+                              timing_events=timing_events, bias1=self.bias1, **kw)
         if self.recompute and not self.keep_recomputed_z:
             self.release_z()
 
@@ -401,6 +412,8 @@ class ExpertBlock:
                                  cols=cols, x=x, q=qT, s=sT)
 
     def experts_forward_unfused(self, events=None) -> None:
+        if self.bias1 is not None:
+            raise RuntimeError("the FC1 bias is applied by the fused path only")
         if self.mx and self.a is None:
             raise RuntimeError("the MXFP8 unfused baseline needs bf16_copies=True")
         rec = (lambda i: events.record(i)) if events else (lambda i: None)

@@ -19,6 +19,8 @@ MOE_DEV float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x
 // gate_hi = lin_hi = +inf, lin_offset = 0): an internal activation code with
 // its own kernel instantiation that skips the clamps and range flags.
 constexpr int kActSwigluFree = 0x100;
+// flag on a GEMM kernel's activation parameter: the layer has an FC1 bias
+constexpr int kActBias = 0x200;
 inline bool act_unclamped(const ActP& p) {
   return p.glo == -__builtin_inff() && p.llo == -__builtin_inff() &&
          p.ghi == __builtin_inff() && p.lhi == __builtin_inff() && p.loff == 0.0f;

@@ -308,6 +308,7 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   g.k_rot_stride = tuning().k_rot;
   g.probs = a->probs_p;
   g.act = moe::to_actp(a->act);
+  g.bias = a->bias1;
 
   // FC1: z = xp . W1i^T with the activation epilogue
   g.N = N1;
@@ -361,6 +362,7 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   f.ldc = a->H;
   f.act_out = nullptr;
   f.amax = nullptr;
+  f.bias = nullptr;
   const int grid2 = gemm_grid(cu, a->cu_margin, a->M_cap, a->E, f.N);
   if (moe_status st = attach_split(f, a->workspace, a->workspace_bytes, 0, grid2, s)) return st;
   if (moe_status st = launched(moe::launch_grouped_gemm(f, moe::EPI_STORE, false, mx, grid2, s)))
@@ -417,6 +419,7 @@ static moe_status bwd_impl(const moe_bwd_args* a, void* ws, size_t ws_bytes, voi
   g.k_rot_stride = tuning().k_rot;
   g.probs = a->probs_p;
   g.act = moe::to_actp(a->act);
+  g.bias = a->bias1;
 
   // FC2 dgrad: dA = dyp . W2 (contracting over H) + dActivation.  bf16 reads
   // W2 [H][I] as [K=H][N=I]; MXFP8 reads its copy quantized along H, [I][H].

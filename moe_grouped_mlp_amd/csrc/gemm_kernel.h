@@ -533,6 +533,20 @@ struct TileCtx {
 // epilogue has issued before it.
 MOE_DEV void acc_hold(f32x16& v) { asm volatile("" : "+a"(v)); }
 
+// The FC1 bias of four consecutive tile columns from its LDS copy (sb:
+// null when the layer has no bias; off: the first column's slot, a multiple
+// of 4), and the activation input with the bias added.  Without a bias the
+// accumulator is used as is (adding 0 would turn -0 into +0).
+MOE_DEV void bias4(const float* sb, int off, float (&b)[4]) {
+  if (sb) {
+    const float4 v = *reinterpret_cast<const float4*>(sb + off);
+    b[0] = v.x; b[1] = v.y; b[2] = v.z; b[3] = v.w;
+  } else {
+    b[0] = b[1] = b[2] = b[3] = 0.0f;
+  }
+}
+MOE_DEV float with_bias(float v, const float* sb, float b) { return sb ? v + b : v; }
+
 // EPI_STORE: C = bf16(acc)
 // HOLD: keep each row block's accumulators in AGPRs until it is stored.
 template <bool HOLD>
@@ -575,10 +589,12 @@ MOE_DEV void row_probs(const float* __restrict__ probs, const TileCtx& t, float 
 // max |a| over this lane's outputs.  Gated: this wave's 128 packed columns
 // [col0 + 128 wn, +128) are gate block q (blocks ni = 0, 1) then up block q
 // (ni = 2, 3), so both halves of an output are in the same lane.
+// sb: the tile's bias in LDS (null: none), see the kernel's bias staging.
 template <int ACT>
 MOE_DEV float epi_glu(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz,
                       uint16_t* __restrict__ a, int64_t lda, const float (&pr)[4],
-                      const ActP& act, const TileCtx& t, int wn, int lane) {
+                      const ActP& act, const TileCtx& t, int wn, int lane,
+                      const float* sb) {
   float amax = 0.0f;
   if constexpr (ACT == MOE_ACT_SRELU) {
     sfor<4>([&](auto mi) {
@@ -591,9 +607,11 @@ MOE_DEV float epi_glu(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz
           const int n = t.n_lane + ni * 32 + 8 * rg;
           if (n < t.cols_valid) {
             if (z) store_bf16x4(z + row * ldz + t.col0 + n, acc[mi][ni], 4 * rg);
-            float av[4];
+            float av[4], b[4];
+            bias4(sb, n, b);
             sfor<4>([&](auto i) {
-              const float zc = fminf(fmaxf(acc[mi][ni][4 * rg + i], act.glo), act.ghi);
+              const float zb = with_bias(acc[mi][ni][4 * rg + i], sb, b[i]);
+              const float zc = fminf(fmaxf(zb, act.glo), act.ghi);
               const float rl = fmaxf(zc, 0.0f);
               av[i] = p * rl * rl;
             });
@@ -618,9 +636,12 @@ MOE_DEV float epi_glu(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz
             store_bf16x4(zrow, acc[mi][h], 4 * rg);
             store_bf16x4(zrow + MOE_INTERLEAVE, acc[mi][h + 2], 4 * rg);
           }
-          float av[4];
+          float av[4], bg[4], bu[4];
+          bias4(sb, wn * 64 + c, bg);
+          bias4(sb, 128 + wn * 64 + c, bu);
           sfor<4>([&](auto i) {
-            av[i] = p * glu_eval<ACT>(acc[mi][h][4 * rg + i], acc[mi][h + 2][4 * rg + i], act).s;
+            av[i] = p * glu_eval<ACT>(with_bias(acc[mi][h][4 * rg + i], sb, bg[i]),
+                                      with_bias(acc[mi][h + 2][4 * rg + i], sb, bu[i]), act).s;
           });
           amax = fmaxf(amax, store_bf16x4_amax(a + row * lda + q * MOE_INTERLEAVE + c, av));
         }); });
@@ -644,10 +665,12 @@ MOE_DEV float epi_glu(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz
 // further: staged chunk 32 wn + 16 (ni / 2) + 4 (ni % 2) + rg (up: + 8),
 // half h.  Whether a 32-column block lies inside N is uniform across the
 // wave.
+// sb: the tile's bias in LDS (null: none): gate half at [0, 256), up half
+// at [256, 512), by column of the dA tile.
 template <int ACT, int MI>
 MOE_DEV float dglu_rows(f32x16 (&acc)[4][4], const char* zrow, uint16_t* __restrict__ dz,
                         int64_t lddz, float p, const ActP& act, const TileCtx& t, int wn,
-                        int lane) {
+                        int lane, const float* sb) {
   constexpr bool gated = ACT != MOE_ACT_SRELU;
   sfor<4>([&](auto ni) { acc_hold(acc[MI][ni]); });
   const int m = t.m_lane + MI * 32;
@@ -665,13 +688,16 @@ MOE_DEV float dglu_rows(f32x16 (&acc)[4][4], const char* zrow, uint16_t* __restr
         if constexpr (gated) {
           constexpr int off = 128 * (ni / 2) + 32 * (ni % 2) + 8 * rg;
           constexpr int k = 16 * (ni / 2) + 4 * (ni % 2) + rg;
-          float uz[4];
+          float uz[4], bg[4], bu[4];
           bf16x4_to_f32(zread(zb, r16, k), gz);
           bf16x4_to_f32(zread(zb, r16, k + 8), uz);
+          bias4(sb, 128 * wn + 32 * ni + 8 * rg + 4 * h, bg);
+          bias4(sb, 256 + 128 * wn + 32 * ni + 8 * rg + 4 * h, bu);
           float dg[4], du[4];
           sfor<4>([&](auto i) {
             const float da = acc[MI][ni][4 * rg + i];
-            const GluVal v = glu_eval<ACT>(gz[i], uz[i], act);
+            const GluVal v =
+                glu_eval<ACT>(with_bias(gz[i], sb, bg[i]), with_bias(uz[i], sb, bu[i]), act);
             const float ds = p * da;
             dg[i] = v.g_in ? ds * v.u * v.df : 0.0f;
             du[i] = v.u_in ? ds * v.f : 0.0f;
@@ -682,11 +708,13 @@ MOE_DEV float dglu_rows(f32x16 (&acc)[4][4], const char* zrow, uint16_t* __restr
         } else {
           constexpr int off = 32 * ni + 8 * rg;
           bf16x4_to_f32(zread(zb, r16, 4 * ni + rg), gz);
-          float d[4];
+          float d[4], b[4];
+          bias4(sb, 128 * wn + 32 * ni + 8 * rg + 4 * h, b);
           sfor<4>([&](auto i) {
             const float da = acc[MI][ni][4 * rg + i];
-            const bool in = (gz[i] >= act.glo) && (gz[i] <= act.ghi);
-            const float rl = fmaxf(fminf(fmaxf(gz[i], act.glo), act.ghi), 0.0f);
+            const float zi = with_bias(gz[i], sb, b[i]);
+            const bool in = (zi >= act.glo) && (zi <= act.ghi);
+            const float rl = fmaxf(fminf(fmaxf(zi, act.glo), act.ghi), 0.0f);
             d[i] = in ? p * da * 2.0f * rl : 0.0f;
             dp += da * rl * rl;
           });
@@ -705,7 +733,7 @@ template <int ACT>
 MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz,
                          uint16_t* __restrict__ a, int64_t lda, const float (&pr)[4],
                          const ActP& act, const TileCtx& t, int wn, int wm, int lane,
-                         const MxOut& mo, uint16_t* tr) {
+                         const MxOut& mo, uint16_t* tr, const float* sb) {
   constexpr bool gated = ACT != MOE_ACT_SRELU;
   const int hf = lane >> 5;
   float amax = 0.0f;
@@ -731,9 +759,12 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
               store_bf16x4(zrow, acc[mi][h], 4 * rg);
               store_bf16x4(zrow + MOE_INTERLEAVE, acc[mi][h + 2], 4 * rg);
             }
-            float av[4];
+            float av[4], bg[4], bu[4];
+            bias4(sb, wn * 64 + c, bg);
+            bias4(sb, 128 + wn * 64 + c, bu);
             sfor<4>([&](auto i) {
-              av[i] = p * glu_eval<ACT>(acc[mi][h][4 * rg + i], acc[mi][h + 2][4 * rg + i], act).s;
+              av[i] = p * glu_eval<ACT>(with_bias(acc[mi][h][4 * rg + i], sb, bg[i]),
+                                        with_bias(acc[mi][h + 2][4 * rg + i], sb, bu[i]), act).s;
             });
             uint2 w = make_uint2(pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]));
             if (!row_ok) w = make_uint2(0, 0);
@@ -754,9 +785,11 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
           sfor<4>([&](auto rg) {
             const int n = cb + 8 * rg + 4 * hf;
             if (row_ok && z) store_bf16x4(z + row * ldz + n, acc[mi][ni], 4 * rg);
-            float av[4];
+            float av[4], b[4];
+            bias4(sb, n - t.col0, b);
             sfor<4>([&](auto i) {
-              const float zc = fminf(fmaxf(acc[mi][ni][4 * rg + i], act.glo), act.ghi);
+              const float zc =
+                  fminf(fmaxf(with_bias(acc[mi][ni][4 * rg + i], sb, b[i]), act.glo), act.ghi);
               const float rl = fmaxf(zc, 0.0f);
               av[i] = p * rl * rl;
             });
@@ -783,7 +816,7 @@ template <int ACT, int MI>
 MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
                            uint16_t* __restrict__ dz, int64_t lddz, float p, const ActP& act,
                            const TileCtx& t, int wn, int wm, int lane, const MxOut& mo,
-                           uint16_t* tr) {
+                           uint16_t* tr, const float* sb) {
   constexpr bool gated = ACT != MOE_ACT_SRELU;
   sfor<4>([&](auto ni) { acc_hold(acc[MI][ni]); });
   const int h = lane >> 5, r16 = opaque(lane & 15);
@@ -805,13 +838,16 @@ MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
         if constexpr (gated) {
           constexpr int off = 128 * (ni / 2) + 32 * (ni % 2) + 8 * rg;
           constexpr int k = 16 * (ni / 2) + 4 * (ni % 2) + rg;
-          float uz[4];
+          float uz[4], bg[4], bu[4];
           bf16x4_to_f32(zread(zb, r16, k), gz);
           bf16x4_to_f32(zread(zb, r16, k + 8), uz);
+          bias4(sb, 128 * wn + 32 * ni + 8 * rg + 4 * h, bg);
+          bias4(sb, 256 + 128 * wn + 32 * ni + 8 * rg + 4 * h, bu);
           float dg[4], du[4];
           sfor<4>([&](auto i) {
             const float da = acc[MI][ni][4 * rg + i];
-            const GluVal v = glu_eval<ACT>(gz[i], uz[i], act);
+            const GluVal v =
+                glu_eval<ACT>(with_bias(gz[i], sb, bg[i]), with_bias(uz[i], sb, bu[i]), act);
             const float ds = p * da;
             dg[i] = v.g_in ? ds * v.u * v.df : 0.0f;
             du[i] = v.u_in ? ds * v.f : 0.0f;
@@ -830,11 +866,13 @@ MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
         } else {
           constexpr int off = 32 * ni + 8 * rg;
           bf16x4_to_f32(zread(zb, r16, 4 * ni + rg), gz);
-          float d[4];
+          float d[4], b[4];
+          bias4(sb, 128 * wn + 32 * ni + 8 * rg + 4 * h, b);
           sfor<4>([&](auto i) {
             const float da = acc[MI][ni][4 * rg + i];
-            const bool in = (gz[i] >= act.glo) && (gz[i] <= act.ghi);
-            const float rl = fmaxf(fminf(fmaxf(gz[i], act.glo), act.ghi), 0.0f);
+            const float zi = with_bias(gz[i], sb, b[i]);
+            const bool in = (zi >= act.glo) && (zi <= act.ghi);
+            const float rl = fmaxf(fminf(fmaxf(zi, act.glo), act.ghi), 0.0f);
             d[i] = in ? p * da * 2.0f * rl : 0.0f;
             dp += da * rl * rl;
           });
@@ -890,9 +928,13 @@ MOE_DEV int block_exclusive_scan(int v, int* s_tmp, int& total) {
 // byte (element 2 i in the low nibble of byte i) with the same tiled E8M0
 // scales; K counts values, so a row holds K / 2 bytes and a 128-byte stage
 // four 64-deep steps.
-template <int EPI, bool NN, int ACT, bool MX, bool F4 = false>
+// ACTF: the activation (ACT), plus kActBias when the layer has an FC1 bias
+// (g.bias non-null; GLU and DGLU epilogues only).
+template <int EPI, bool NN, int ACTF, bool MX, bool F4 = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_kernel(GemmArgs g) {
+  constexpr int ACT = ACTF & ~kActBias;
+  constexpr bool kBias = (ACTF & kActBias) != 0 && (EPI == EPI_GLU || EPI == EPI_DGLU);
   static_assert(!(MX && NN), "MXFP8 operands are always K-contiguous");
   static_assert(!F4 || (MX && EPI == EPI_STORE), "MXFP4 runs the plain-store GEMM");
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[kStageBytes / 2], sA1[kStageBytes / 2];
@@ -903,7 +945,7 @@ void grouped_gemm_kernel(GemmArgs g) {
   __shared__ int s_split[kMaxExperts];
   __shared__ int s_pad[kMaxExperts];
   __shared__ int s_tmp[kThreads / 64];
-  __shared__ float s_red[2 * BM];
+  __shared__ __attribute__((aligned(16))) float s_red[2 * BM];  // dprobs sums; the tile's bias
   // per-wave staging tiles of the transposed MXFP8 copies (MX epilogues)
   constexpr int kTrWords = (MX && (EPI == EPI_GLU || EPI == EPI_DGLU)) ? 4 * kTrTile : 4;
   __shared__ __attribute__((aligned(16))) uint16_t s_tr[kTrWords];
@@ -1339,7 +1381,15 @@ void grouped_gemm_kernel(GemmArgs g) {
   // GLU: a tile's row probabilities are loaded just before its first stages,
   // so the wait for stage 0 covers them and the epilogue, which runs with
   // its stores in flight, never waits on a load
+  //
+  // FC1 bias (instantiations with kActBias): the epilogue reads the tile's
+  // bias from LDS (s_red).  GLU: thread t holds one value, loaded with the
+  // row probabilities, for slot t: gated, the gate (t < 128) or up
+  // (t >= 128) bias of logical column col0 / 2 + t % 128; sReLU, column
+  // col0 + t.
+  constexpr bool kGatedAct = ACT != MOE_ACT_SRELU;
   float pr_next[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float bias_next = 0.0f;
   auto load_probs = [&](const TileInfo& ti) {
     if constexpr (EPI == EPI_GLU) {
       const int ml = wm * kWaveM + (lane & 31);
@@ -1347,6 +1397,16 @@ void grouped_gemm_kernel(GemmArgs g) {
         const int m = ml + mi * 32;
         pr_next[mi] = m < ti.rows_valid ? g.probs[ti.row0 + m] : 0.0f;
       });
+      if constexpr (kBias) {
+        const float* be = g.bias + static_cast<int64_t>(ti.e) * g.N;
+        if constexpr (kGatedAct) {
+          const int half = g.N / 2, j = ti.col0 / 2 + (tid & 127);
+          bias_next = j < half ? be[(tid < 128 ? 0 : half) + j] : 0.0f;
+        } else {
+          const int j = ti.col0 + tid;
+          bias_next = j < g.N ? be[j] : 0.0f;
+        }
+      }
     }
   };
 
@@ -1360,6 +1420,7 @@ void grouped_gemm_kernel(GemmArgs g) {
   while (w < items) {
     float pr_tile[4];
     sfor<4>([&](auto mi) { pr_tile[mi] = pr_next[mi]; });
+    const float bias_tile = bias_next;
     sfor<4>([&](auto mi) { sfor<4>([&](auto ni) { acc[mi][ni] = f32x16{}; }); });
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLoads));   // stage 0 landed
     bare_barrier();
@@ -1441,6 +1502,12 @@ void grouped_gemm_kernel(GemmArgs g) {
       }
     } else if constexpr (EPI == EPI_GLU) {
       float amax;
+      const float* sb = kBias ? s_red : nullptr;   // the tile's bias in LDS
+      if constexpr (kBias) {
+        s_red[tid] = bias_tile;
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        bare_barrier();
+      }
       if constexpr (MX) {
         // lane values re-derived here, not kept live (and spilled) across
         // the K loop: a spill reload would wait on the next tile's loads
@@ -1449,9 +1516,11 @@ void grouped_gemm_kernel(GemmArgs g) {
         te.m_lane = (wave_e >> 1) * kWaveM + (lane_e & 31);
         te.n_lane = (wave_e & 1) * kWaveN + 4 * (lane_e >> 5);
         amax = epi_glu_mx<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, pr_tile, g.act, te,
-                               wave_e & 1, wave_e >> 1, lane_e, mo, s_tr + wave_e * kTrTile);
+                               wave_e & 1, wave_e >> 1, lane_e, mo, s_tr + wave_e * kTrTile,
+                               sb);
       } else
-        amax = epi_glu<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, pr_tile, g.act, t, wn, lane);
+        amax = epi_glu<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, pr_tile, g.act, t, wn, lane,
+                            sb);
       if (g.amax) {
         amax = wave_max_imm(amax);
         if (lane == 0) atomic_max_nonneg(g.amax, amax);
@@ -1476,6 +1545,20 @@ void grouped_gemm_kernel(GemmArgs g) {
       te.n_lane = wn_e * kWaveN + 4 * (lane_e >> 5);
       float pr[4];
       row_probs(g.probs, te, pr);
+      // the tile's bias (before the chunks, like the probabilities): thread t
+      // holds the gate (or sReLU) bias of dA column col0 + t and the up bias
+      // of the same column, for LDS slots t and 256 + t
+      float bz[2] = {0.0f, 0.0f};
+      if constexpr (kBias) {
+        const int tid_e = lane_e + 64 * wave_e;
+        const int j = t.col0 + tid_e;
+        const float* be = g.bias + static_cast<int64_t>(t0.e) * (kGated ? 2 * g.N : g.N);
+        if (j < g.N) {
+          bz[0] = be[j];
+          if constexpr (kGated) bz[1] = be[g.N + j];
+        }
+      }
+      const float* sb = kBias ? s_red : nullptr;
       ZL zl;
       zl.init(g.zin, g.ldz, t.row0, t.rows_valid, kGated ? 2 * t.col0 : t.col0);
       zl.issue(sA0, sB0, 0, wave_s, lane_e);
@@ -1494,14 +1577,24 @@ void grouped_gemm_kernel(GemmArgs g) {
           if (!MX && more) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLoads));
           else __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
         }
+        if constexpr (kBias && MI == 0) {
+          // the bias loads are older than chunk 0's, so they have landed;
+          // the previous tile's last reads of s_red were before its final
+          // barrier
+          const int tid_e = lane_e + 64 * wave_e;
+          s_red[tid_e] = bz[0];
+          if constexpr (kGated) s_red[256 + tid_e] = bz[1];
+          __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        }
         bare_barrier();
         const char* zrow =
             reinterpret_cast<const char*>(wm_e ? zb : za) + (lane_e & 31) * kZRow;
         if constexpr (MX)
           dp[MI] = dglu_rows_mx<ACT, MI>(acc, zrow, g.C, g.ldc, pr[MI], g.act, te, wn_e, wm_e,
-                                         lane_e, mo, s_tr + wave_e * kTrTile);
+                                         lane_e, mo, s_tr + wave_e * kTrTile, sb);
         else
-          dp[MI] = dglu_rows<ACT, MI>(acc, zrow, g.C, g.ldc, pr[MI], g.act, te, wn_e, lane_e);
+          dp[MI] = dglu_rows<ACT, MI>(acc, zrow, g.C, g.ldc, pr[MI], g.act, te, wn_e, lane_e,
+                                      sb);
         __builtin_amdgcn_sched_barrier(0);
         // every wave is done reading the chunk before its buffer is reused
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -1554,22 +1647,33 @@ void grouped_gemm_kernel(GemmArgs g) {
 
 
 // Launch of one kernel family for the activation in g.act (SwiGLU with no
-// clamp and no linear offset takes its own instantiation).
-template <int EPI, bool NN, bool MX>
-hipError_t launch_act(const GemmArgs& g, int grid, hipStream_t s) {
+// clamp and no linear offset takes its own instantiation when there is no
+// bias; a bias takes the instantiations flagged kActBias).
+template <int EPI, bool NN, bool MX, int BIAS>
+hipError_t launch_act_b(const GemmArgs& g, int grid, hipStream_t s) {
   dim3 blk(kThreads), grd(grid);
   switch (g.act.act) {
     case MOE_ACT_SWIGLU:
-      if (act_unclamped(g.act))
+      if (!BIAS && act_unclamped(g.act))
         grouped_gemm_kernel<EPI, NN, kActSwigluFree, MX><<<grd, blk, 0, s>>>(g);
       else
-        grouped_gemm_kernel<EPI, NN, MOE_ACT_SWIGLU, MX><<<grd, blk, 0, s>>>(g);
+        grouped_gemm_kernel<EPI, NN, MOE_ACT_SWIGLU | BIAS, MX><<<grd, blk, 0, s>>>(g);
       break;
-    case MOE_ACT_GEGLU: grouped_gemm_kernel<EPI, NN, MOE_ACT_GEGLU, MX><<<grd, blk, 0, s>>>(g); break;
-    case MOE_ACT_SRELU: grouped_gemm_kernel<EPI, NN, MOE_ACT_SRELU, MX><<<grd, blk, 0, s>>>(g); break;
+    case MOE_ACT_GEGLU:
+      grouped_gemm_kernel<EPI, NN, MOE_ACT_GEGLU | BIAS, MX><<<grd, blk, 0, s>>>(g);
+      break;
+    case MOE_ACT_SRELU:
+      grouped_gemm_kernel<EPI, NN, MOE_ACT_SRELU | BIAS, MX><<<grd, blk, 0, s>>>(g);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int EPI, bool NN, bool MX>
+hipError_t launch_act(const GemmArgs& g, int grid, hipStream_t s) {
+  return g.bias ? launch_act_b<EPI, NN, MX, kActBias>(g, grid, s)
+                : launch_act_b<EPI, NN, MX, 0>(g, grid, s);
 }
 
 }  // namespace

@@ -78,6 +78,9 @@ struct GemmArgs {
   float* dp_part;        // DGLU: [M_cap][n_part]
   int n_part;
   ActP act;
+  // GLU, DGLU (nullable): FC1 bias [E][N1] fp32 in logical column order
+  // (gated: gate half, then up half), added to the activation's input
+  const float* bias;
   // split-K of the last, partial round of tiles (plain-store epilogue only):
   // fp32 partial tiles and one arrival counter per split tile (zeroed before
   // the launch); null disables splitting

@@ -62,7 +62,7 @@ def act_of(wl, prm_override=None):
 
 
 def run_gpu_layer(wl, M_cap=None, backward=True, block=None, prec=None,
-                  bf16_copies=True):
+                  bf16_copies=True, bias1=None):
     """Run the HIP path on a workload; returns the block holding the results
     (with MXFP8, also the optional bf16 a and dz unless bf16_copies=False)."""
     gp, _ = act_of(wl)
@@ -72,7 +72,8 @@ def run_gpu_layer(wl, M_cap=None, backward=True, block=None, prec=None,
                                   bf16_copies=bf16_copies)
     w1 = dev_bf16(wl.w1)
     w2 = dev_bf16(wl.w2)
-    blk.load_weights(w1, w2)
+    blk.load_weights(w1, w2, None if bias1 is None else
+                     torch.from_numpy(np.asarray(bias1, dtype=np.float32)).cuda())
     x = dev_bf16(wl.x)
     idx = torch.from_numpy(wl.expert_idx.astype(np.int32)).cuda()
     probs = torch.from_numpy(wl.probs.astype(np.float32)).cuda()
@@ -114,12 +115,14 @@ def uninterleave_cols(packed: np.ndarray, I: int) -> np.ndarray:
     return out
 
 
-def oracle_layer(wl, M_cap, backward=True, mx=False, unfused=False):
+def oracle_layer(wl, M_cap, backward=True, mx=False, unfused=False, bias1=None):
     _, op = act_of(wl)
+    b = None if bias1 is None else np.asarray(bias1, dtype=np.float64)
     fw = om.forward(wl.x, wl.w1, wl.w2, wl.expert_idx, wl.probs, wl.E, op,
-                    first_expert=wl.first_expert, M_cap=M_cap, mx=mx, unfused=unfused)
+                    first_expert=wl.first_expert, M_cap=M_cap, mx=mx, unfused=unfused,
+                    bias1=b)
     bw = om.backward(fw, wl.dout, wl.w1, wl.w2, op, mx=mx,
-                     unfused=unfused) if backward else None
+                     unfused=unfused, bias1=b) if backward else None
     return fw, bw
 
 

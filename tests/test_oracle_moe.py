@@ -490,3 +490,91 @@ def test_mxfp4_reading_rounds_every_gemm_operand():
                         (b8.dz, b4.dz, b16.dz), (b8.dx, b4.dx, b16.dx)):
         assert 0 < rel(q8, ref) < rel(q4, ref) < 0.5
     assert f4.a_mx is None and b4.dz_mx is None
+
+
+# ------------------------------------------------------------ FC1 bias ----
+def _augment(x, w1, w2, dout, bias):
+    """The bias as one more input column: x' = [x, 1], W1'_e = [W1_e, b_e],
+    so x' . W1'_e^T = x . W1_e^T + b_e exactly (float64).  The layer's
+    output width follows its input width, so W2 gets a zero output row and
+    dOut a zero column: the first H output columns are the original ones."""
+    T = x.shape[0]
+    xa = np.concatenate([x, np.ones((T, 1))], axis=1)
+    w1a = np.concatenate([w1, bias[:, :, None]], axis=2)
+    w2a = np.concatenate([w2, np.zeros((w2.shape[0], 1, w2.shape[2]))], axis=1)
+    da = np.concatenate([dout, np.zeros((T, 1))], axis=1)
+    return xa, w1a, w2a, da
+
+
+@pytest.mark.parametrize("prm", [moe.ActParams(),
+                                 moe.ActParams(act="geglu"),
+                                 moe.ActParams.clamped(0.8, beta=1.702),
+                                 moe.ActParams(act="srelu")])
+def test_bias_is_an_activation_input_offset(prm):
+    """FC1 bias (one vector per expert, logical gate|up order): the layer
+    with bias b equals the bias-free layer with b as the weight of an extra
+    all-ones input column, except that z is stored without b.  Pins where b
+    enters (the activation's input, both halves in logical order, per
+    expert) and that the backward's dz, dprobs and dx see the same offset."""
+    rng = np.random.default_rng(11)
+    T, H, I, E, k = 7, 5, 4, 3, 2
+    n1 = 2 * I if prm.gated else I
+    x = rng.standard_normal((T, H))
+    w1 = rng.standard_normal((E, n1, H)) * 0.5
+    w2 = rng.standard_normal((E, H, I)) * 0.5
+    bias = rng.standard_normal((E, n1))
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    p = rng.random((T, k))
+    dout = rng.standard_normal((T, H))
+    fb = moe.forward(x, w1, w2, idx, p, E, prm, exact=True, bias1=bias)
+    xa, w1a, w2a, da = _augment(x, w1, w2, dout, bias)
+    fa = moe.forward(xa, w1a, w2a, idx, p, E, prm, exact=True)
+    valid = fb.expert >= 0
+    ex = fb.expert[valid]
+    np.testing.assert_allclose(fb.z[valid] + bias[ex], fa.z[valid], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(fb.a[valid], fa.a[valid], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(fb.out, fa.out[:, :H], rtol=1e-12, atol=1e-14)
+    assert not fa.out[:, H].any()
+    bb = moe.backward(fb, dout, w1, w2, prm, exact=True, bias1=bias)
+    ba = moe.backward(fa, da, w1a, w2a, prm, exact=True)
+    np.testing.assert_allclose(bb.dz[valid], ba.dz[valid], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(bb.dprobs, ba.dprobs, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(bb.dx, ba.dx[:, :H], rtol=1e-12, atol=1e-14)
+    # a wrong reading is caught: the bias on the other half, or stored in z
+    if prm.gated:
+        swapped = np.concatenate([bias[:, I:], bias[:, :I]], axis=1)
+        fs = moe.forward(x, w1, w2, idx, p, E, prm, exact=True, bias1=swapped)
+        assert np.abs(fs.a[valid] - fa.a[valid]).max() > 1e-3
+    assert np.abs(fb.z[valid] - fa.z[valid]).max() > 1e-3
+
+
+def test_bias_gradient_is_the_sum_of_dz_over_the_expert_rows():
+    """dL/db_e = sum of dz over expert e's rows (central differences of the
+    float64 layer loss), the reading the C ABI documents for dz."""
+    rng = np.random.default_rng(12)
+    T, H, I, E, k = 6, 4, 4, 2, 2
+    prm = moe.ActParams.clamped(1.5, beta=1.702)
+    x = rng.standard_normal((T, H))
+    w1 = rng.standard_normal((E, 2 * I, H)) * 0.5
+    w2 = rng.standard_normal((E, H, I)) * 0.5
+    bias = rng.standard_normal((E, 2 * I)) * 0.3
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    p = rng.random((T, k))
+    dout = rng.standard_normal((T, H))
+
+    def loss(b):
+        fw = moe.forward(x, w1, w2, idx, p, E, prm, exact=True, bias1=b)
+        return float(np.sum(fw.out * dout))
+
+    fw = moe.forward(x, w1, w2, idx, p, E, prm, exact=True, bias1=bias)
+    bw = moe.backward(fw, dout, w1, w2, prm, exact=True, bias1=bias)
+    h = 1e-6
+    for e in range(E):
+        rows = fw.expert == e
+        db = bw.dz[rows].sum(axis=0)
+        for n in range(2 * I):
+            bp, bm = bias.copy(), bias.copy()
+            bp[e, n] += h
+            bm[e, n] -= h
+            num = (loss(bp) - loss(bm)) / (2 * h)
+            assert abs(db[n] - num) <= 1e-5 * max(1.0, abs(num)), (e, n, db[n], num)
