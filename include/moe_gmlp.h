@@ -28,9 +28,10 @@
  *   - Host-checkable problems (NULL pointers, unsupported sizes, small
  *     workspace) return a negative moe_status before anything is launched.
  *     Problems only visible on the device (padded rows exceeding M_cap,
- *     duplicate experts in a token's top-k list) OR a bit into the optional
- *     device int32 *err_flag (MOE_DEVERR_*); kernels then clamp so that no
- *     access leaves the caller's buffers.
+ *     duplicate experts in a token's top-k list, inconsistent group offsets
+ *     handed to a grouped GEMM) OR a bit into the optional device int32
+ *     *err_flag (MOE_DEVERR_*); kernels then clamp so that no access leaves
+ *     the caller's buffers.
  *   - Calls are re-entrant; a per-device attribute cache is filled once.
  */
 #ifndef MOE_GMLP_H
@@ -58,6 +59,12 @@ typedef enum moe_status {
 #define MOE_DEVERR_SYNC_TIMEOUT 0x4   /* a grid-wide wait of moe_router_route
                                          ran out (the grid was not resident
                                          at once); no rows were written     */
+#define MOE_DEVERR_BAD_OFFSETS 0x8    /* a grouped GEMM found split_sizes /
+                                         padded_offsets inconsistent: a
+                                         negative size or start, or a group
+                                         running past the next group's start
+                                         or past M_cap (its rows there are
+                                         not computed)                       */
 
 /* Group-start alignment of the padded row layout (rows).  Every group of
  * the permuted layout starts at a multiple of it, so MXFP8 blocks of 32
@@ -485,6 +492,7 @@ typedef struct moe_wgrad_args {
   void* dw1;                      /* bf16 [E][N1][H] or NULL */
   void* dw2;                      /* bf16 [E][H][I] or NULL  */
   void* timing_events[3];
+  int32_t* err_flag;              /* optional device int32 (MOE_DEVERR_BAD_OFFSETS) */
 } moe_wgrad_args;
 
 moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* args, void* stream);
@@ -531,6 +539,7 @@ typedef struct moe_gemm_args {
   const uint8_t* a_s;
   const uint8_t* b_s;
   int64_t b_s_stride;             /* bytes; 0: N * K / 32 */
+  int32_t* err_flag;              /* optional device int32 (MOE_DEVERR_BAD_OFFSETS) */
 } moe_gemm_args;
 
 moe_status moe_grouped_gemm(const moe_gemm_args* args, void* stream);

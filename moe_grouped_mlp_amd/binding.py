@@ -23,6 +23,7 @@ GROUP_ALIGN = 128
 INTERLEAVE = 64
 MX_BLOCK = 32
 DEVERR_MCAP_OVERFLOW, DEVERR_DUP_EXPERT, DEVERR_SYNC_TIMEOUT = 0x1, 0x2, 0x4
+DEVERR_BAD_OFFSETS = 0x8
 NOALLOC_SCRATCH_BYTES = 16 << 20
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_DEVICE = 0, -1, -2, -3, -4, -5
 
@@ -122,7 +123,8 @@ class GemmArgs(ctypes.Structure):
                 ("a", c_void_p), ("b", c_void_p), ("b_stride", c_int64),
                 ("c", c_void_p), ("workspace", c_void_p),
                 ("workspace_bytes", c_size_t), ("prec", c_int32),
-                ("a_s", c_void_p), ("b_s", c_void_p), ("b_s_stride", c_int64)]
+                ("a_s", c_void_p), ("b_s", c_void_p), ("b_s_stride", c_int64),
+                ("err_flag", c_void_p)]
 
 
 class GluArgs(ctypes.Structure):
@@ -162,7 +164,7 @@ class WgradArgs(ctypes.Structure):
                 ("dypT_q", c_void_p), ("dypT_s", c_void_p),
                 ("aT_q", c_void_p), ("aT_s", c_void_p),
                 ("dw1", c_void_p), ("dw2", c_void_p),
-                ("timing_events", c_void_p * 3)]
+                ("timing_events", c_void_p * 3), ("err_flag", c_void_p)]
 
 
 # ---- library loading ------------------------------------------------------
@@ -379,13 +381,13 @@ def moe_grouped_mlp_wgrad(*, E, H, I, M_cap, split_sizes, padded_offsets,
                           xp=None, dyp=None, a=None, dzT_q=None, dzT_s=None,
                           xpT_q=None, xpT_s=None, dypT_q=None, dypT_s=None,
                           aT_q=None, aT_s=None, dw1=None, dw2=None,
-                          timing_events=None, stream=None):
+                          timing_events=None, err_flag=None, stream=None):
     args = WgradArgs(E, H, I, int(bool(gated)), M_cap, prec, cu_margin,
                      _ptr(split_sizes), _ptr(padded_offsets), _ptr(dz),
                      _ptr(xp), _ptr(dyp), _ptr(a), _ptr(dzT_q), _ptr(dzT_s),
                      _ptr(xpT_q), _ptr(xpT_s), _ptr(dypT_q), _ptr(dypT_s),
                      _ptr(aT_q), _ptr(aT_s), _ptr(dw1), _ptr(dw2),
-                     _events(timing_events))
+                     _events(timing_events), _ptr(err_flag))
     _check("moe_grouped_mlp_wgrad",
            lib().moe_grouped_mlp_wgrad(ctypes.byref(args), _stream(stream)))
 
@@ -429,11 +431,11 @@ def moe_gemm_clock_trace(records=None, slots=1):
 def moe_grouped_gemm(*, E, N, K, M_cap, split_sizes, padded_offsets, a, b, c,
                      b_kn=False, b_stride=0, cu_margin=0, workspace=None,
                      prec=PREC_BF16, a_s=None, b_s=None, b_s_stride=0,
-                     stream=None):
+                     err_flag=None, stream=None):
     args = GemmArgs(E, N, K, M_cap, int(bool(b_kn)), cu_margin,
                     _ptr(split_sizes), _ptr(padded_offsets), _ptr(a), _ptr(b),
                     b_stride, _ptr(c), _ptr(workspace), _nbytes(workspace), prec,
-                    _ptr(a_s), _ptr(b_s), b_s_stride)
+                    _ptr(a_s), _ptr(b_s), b_s_stride, _ptr(err_flag))
     _check("moe_grouped_gemm", lib().moe_grouped_gemm(ctypes.byref(args), _stream(stream)))
 
 

@@ -399,7 +399,7 @@ class ExpertBlock:
                            padded_offsets=self.padded_offsets, a=a, b=b, c=c,
                            b_kn=b_kn, cu_margin=self.cu_margin,
                            workspace=self.ws if split else None,
-                           prec=self.prec, a_s=a_s, b_s=b_s)
+                           prec=self.prec, a_s=a_s, b_s=b_s, err_flag=self.err_flag)
 
     def _quantize4(self, x, cols, q, s):
         B.moe_quantize_mxfp4(batch=1, rows=self.M_cap, cols=cols, x=x, q=q, s=s)
@@ -503,5 +503,6 @@ class ExpertBlock:
                                 padded_offsets=self.padded_offsets,
                                 prec=self.prec, cu_margin=self.cu_margin,
                                 dw1=self.dw1, dw2=self.dw2,
-                                timing_events=timing_events, **kw)
+                                timing_events=timing_events, err_flag=self.err_flag,
+                                **kw)
         return self.dw1, self.dw2

@@ -309,6 +309,7 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   g.probs = a->probs_p;
   g.act = moe::to_actp(a->act);
   g.bias = a->bias1;
+  g.err = a->err_flag;
 
   // FC1: z = xp . W1i^T with the activation epilogue
   g.N = N1;
@@ -420,6 +421,7 @@ static moe_status bwd_impl(const moe_bwd_args* a, void* ws, size_t ws_bytes, voi
   g.probs = a->probs_p;
   g.act = moe::to_actp(a->act);
   g.bias = a->bias1;
+  g.err = a->err_flag;
 
   // FC2 dgrad: dA = dyp . W2 (contracting over H) + dActivation.  bf16 reads
   // W2 [H][I] as [K=H][N=I]; MXFP8 reads its copy quantized along H, [I][H].
@@ -469,6 +471,7 @@ static moe_status bwd_impl(const moe_bwd_args* a, void* ws, size_t ws_bytes, voi
   f.group_m = tuning().group_m;
   f.k_rot_stride = tuning().k_rot;
   f.act = g.act;
+  f.err = a->err_flag;
   f.N = a->H;
   f.K = N1;
   if (mx) {
@@ -541,6 +544,7 @@ moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   g.k_rot_stride = tuning().k_rot;
   g.C = static_cast<uint16_t*>(a->c);
   g.ldc = a->N;
+  g.err = a->err_flag;
   const int grid = gemm_grid(cu, a->cu_margin, a->M_cap, a->E, a->N);
   if (f4) return launched(moe::launch_gemm_store_f4(g, grid, s));
   if (moe_status st = attach_split(g, a->workspace, a->workspace_bytes, 0, grid, s)) return st;
@@ -635,6 +639,7 @@ moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* a, void* stream) {
   auto run = [&](const void* A, const uint8_t* As, int P, const void* Bm, const uint8_t* Bs,
                  int Q, void* C) -> moe_status {
     moe::GemmArgs g{};
+    g.err = a->err_flag;
     g.E = a->E;
     g.N = Q;
     g.K = static_cast<int>(a->M_cap);

@@ -976,10 +976,18 @@ void grouped_gemm_kernel(GemmArgs g) {
   for (int i = 0; i < per; ++i) {
     int e = tid * per + i;
     if (e < E) {
-      int n = max(g.split[e], 0);
+      const int n_raw = g.split[e];
+      const int n = max(n_raw, 0);
       s_split[e] = n;
       s_pad[e] = g.padded[e];
       mine += tiles_m_of(n) * tiles_n;
+      if (g.err && blockIdx.x == 0) {
+        // the group [padded[e], padded[e] + n) must start at 0 or later and
+        // end before the next group's start and inside M_cap
+        const int64_t p0 = g.padded[e], p1 = g.padded[e + 1];
+        if (n_raw < 0 || p0 < 0 || p0 + n > p1 || p0 + n > g.M_cap)
+          set_err(g.err, MOE_DEVERR_BAD_OFFSETS);
+      }
     }
   }
   int total;

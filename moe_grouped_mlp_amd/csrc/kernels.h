@@ -95,6 +95,7 @@ struct GemmArgs {
   uint8_t* mx_qT;        // nullable
   uint8_t* mx_sT;
   int mx_n;
+  int32_t* err;          // nullable: MOE_DEVERR_BAD_OFFSETS when the offsets are inconsistent
   // measurement (nullable): workgroup i writes clk[2 i] = shader cycles and
   // clk[2 i + 1] = constant-rate ticks between its start and its end
   int64_t* clk;
