@@ -240,6 +240,35 @@ def assert_close_mx(gpu, ora, what):
     assert l2 <= MX_REL_L2, f"{what}: relative L2 error {l2:.3e}"
 
 
+# A contraction over MXFP8 operands that the GPU and the oracle encoded from
+# values an ulp apart: a code can move by one E4M3 step (2^-3 of its value's
+# binade) in either operand, and a block whose amax crosses a power of two
+# moves all 32 codes, so one product can change by up to (1 + 2^-3)^2 - 1 <
+# 0.27 of |a| |b|.  Every element then lies within 0.27 (|A|^T |B|) of the
+# oracle's (plus bf16 output rounding); the scale-aware bar of
+# assert_close_mx holds on all but MX_OUTLIER_FRAC of the elements and the
+# relative L2 error stays below MX_REL_L2.
+MX_PRODUCT_STEP = (1 + 2.0 ** -3) ** 2 - 1
+
+
+def assert_close_mx_contraction(gpu, ora, abs_prod, what):
+    """abs_prod: |A|^T |B| of the contraction, elementwise (same shape)."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ora = np.asarray(ora, dtype=np.float64)
+    assert gpu.shape == ora.shape == abs_prod.shape, (what, gpu.shape, ora.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU values"
+    d = np.abs(gpu - ora)
+    bound = MX_PRODUCT_STEP * abs_prod + 2.0 ** -8 * np.abs(ora) + 1e-30
+    over = d > bound
+    assert not over.any(), f"{what}: {over.sum()} elements beyond the MXFP8 step bound"
+    rms = float(np.sqrt(np.mean(ora * ora))) if ora.size else 0.0
+    out = d > REL_ATOL * rms + RTOL * np.abs(ora)
+    assert out.mean() <= MX_OUTLIER_FRAC, \
+        f"{what}: {out.sum()} of {out.size} outside the scale-aware bar"
+    l2 = float(np.linalg.norm(d) / max(np.linalg.norm(ora), 1e-300))
+    assert l2 <= MX_REL_L2, f"{what}: relative L2 error {l2:.3e}"
+
+
 def assert_mx_near(q_gpu, s_plain_gpu, ref, what, code_frac=2e-3, far_frac=1e-4,
                    scale_frac=1e-3):
     """MXFP8 copies written by a fused epilogue against the oracle's encoding
