@@ -282,6 +282,42 @@ def gemm_bench(args):
                 100 * tf / (PEAK_TFLOPS[prec] * ck / 2.4), 2)
         log(f"  {ms:.3f} ms, {tf:.1f} TFLOP/s ({100 * tf / PEAK_TFLOPS[prec]:.1f}% of peak)"
             f"{f', clock {ck:.3f} GHz' if ck else ''}")
+    # overlap with another kernel (the pages' reason for dynamic scheduling):
+    # a kernel holds 64 of the CUs for the first 1 ms of the bf16 GEMM; with
+    # the work counters the other workgroups take the busy CUs' tiles, with
+    # the static walk those tiles wait for their CUs
+    ws_dyn = torch.zeros(mg.moe_grouped_gemm_workspace_size(True), **u8)
+    ws_sta = torch.zeros(mg.moe_grouped_gemm_workspace_size(False), **u8)
+    side = torch.cuda.Stream()
+    busy_ticks = int(mg.moe_clock_tick_rate_hz() * 1e-3)
+    ev2 = HipEvents(2)
+
+    def overlapped(ws, busy, reps=5):
+        gemm = lambda: mg.moe_grouped_gemm(E=E, N=N, K=K, M_cap=M_cap, split_sizes=split,
+                                           padded_offsets=padded, a=a, b=w, c=out,
+                                           workspace=ws)
+        gemm()
+        torch.cuda.synchronize()
+        tot = 0.0
+        for _ in range(reps):
+            if busy:
+                with torch.cuda.stream(side):
+                    mg.moe_bench_occupy(workgroups=64, ticks=busy_ticks)
+            ev2.record(0, stream)
+            gemm()
+            ev2.record(1, stream)
+            torch.cuda.synchronize()
+            tot += ev2.elapsed_ms(0, 1)
+        return tot / reps
+
+    ov = {"what": "bf16 FC2 GEMM while another kernel holds 64 of the CUs for its first 1 ms",
+          "alone_ms": round(overlapped(ws_dyn, False), 4),
+          "static_ms": round(overlapped(ws_sta, True), 4),
+          "dynamic_ms": round(overlapped(ws_dyn, True), 4)}
+    kernels["overlap_busy_cus"] = ov
+    log(f"overlap: alone {ov['alone_ms']:.3f} ms, beside a 64-CU 1 ms kernel: static "
+        f"{ov['static_ms']:.3f} ms, dynamic {ov['dynamic_ms']:.3f} ms")
+    ev2.close()
     del a, w, out
     torch.cuda.empty_cache()
     # reference point: the vendor BLAS (hipBLASLt through torch.matmul) on one

@@ -544,6 +544,18 @@ typedef struct moe_gemm_args {
 
 moe_status moe_grouped_gemm(const moe_gemm_args* args, void* stream);
 
+/* Workspace bytes for moe_grouped_gemm: with dynamic == 0 the K split of
+ * the last round only; otherwise also the per-XCD work counters of dynamic
+ * tile scheduling ([FK] § "From kernel-level to pre-training speedups":
+ * dynamic scheduling, for efficient overlap with other kernels).  With the
+ * counters, workgroups take tiles from them after a static first round, so
+ * a workgroup that starts late (its CU busy with another kernel) leaves its
+ * share to the others; without them every workgroup walks a fixed list.
+ * Results do not depend on the scheduling (each tile's sum runs in one
+ * fixed order).  The fused forward and backward use the counters when
+ * their workspace has moe_grouped_mlp_workspace_size bytes. */
+size_t moe_grouped_gemm_workspace_size(int dynamic);
+
 /* moe_glu_unfused -- the activation of the FC1 output as its own pass.
  *   direction 0: a[r] = bf16(probs_p[r] * act(z[r])) and amax = max |a|
  *     (amax optional; it is reset by the call);
@@ -687,6 +699,14 @@ moe_status moe_gemm_clock_trace(int64_t* records, int slots);
 /* Frequency of the constant-rate counter on the current device (Hz), 0 if
  * it cannot be read. */
 int64_t moe_clock_tick_rate_hz(void);
+
+/* Measurement: keeps `workgroups` compute units busy (one workgroup per CU,
+ * holding 96 KB of LDS so that no grouped-GEMM workgroup fits beside it)
+ * for `ticks` of the constant-rate counter, as a stand-in for a concurrent
+ * kernel (expert- or data-parallel communication) when measuring how the
+ * grouped GEMMs overlap with other work.  1 <= workgroups <= 1024 and
+ * 1 <= ticks <= 1e8, else MOE_ERR_INVALID_ARG. */
+moe_status moe_bench_occupy(int workgroups, int64_t ticks, void* stream);
 
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);

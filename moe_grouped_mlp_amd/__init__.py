@@ -17,7 +17,8 @@ from .binding import (  # noqa: F401
     moe_grouped_mlp_wgrad, moe_router_topk, moe_router_route,
     moe_router_route_workspace_size, moe_grouped_gemm, moe_glu_unfused,
     moe_grouped_mlp_workspace_size, moe_clock_tick_rate_hz,
-    moe_gemm_clock_trace, CLOCK_MAX_WORKGROUPS,
+    moe_gemm_clock_trace, CLOCK_MAX_WORKGROUPS, moe_bench_occupy,
+    moe_grouped_gemm_workspace_size,
     moe_permute, moe_permute_workspace_size, moe_quantize_mxfp4, moe_quantize_mxfp8,
     moe_unpermute, moe_weight_repack_interleave, EXPORTED_SYMBOLS,
 )

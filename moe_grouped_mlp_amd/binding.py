@@ -35,7 +35,7 @@ EXPORTED_SYMBOLS = (
     "moe_grouped_mlp_workspace_size", "moe_status_string", "moe_gmlp_version",
     "moe_mx_scale_offset", "moe_grouped_mlp_bwd_noalloc", "moe_router_route",
     "moe_router_route_workspace_size", "moe_clock_tick_rate_hz",
-    "moe_gemm_clock_trace",
+    "moe_gemm_clock_trace", "moe_bench_occupy", "moe_grouped_gemm_workspace_size",
 )
 
 
@@ -197,6 +197,10 @@ def lib() -> ctypes.CDLL:
         L.moe_clock_tick_rate_hz.argtypes = []
         L.moe_gemm_clock_trace.restype = c_int
         L.moe_gemm_clock_trace.argtypes = [c_void_p, c_int]
+        L.moe_bench_occupy.restype = c_int
+        L.moe_bench_occupy.argtypes = [c_int, c_int64, c_void_p]
+        L.moe_grouped_gemm_workspace_size.restype = c_size_t
+        L.moe_grouped_gemm_workspace_size.argtypes = [c_int]
         L.moe_grouped_mlp_workspace_size.restype = c_size_t
         L.moe_grouped_mlp_workspace_size.argtypes = [
             c_int, c_int, c_int, c_int64, c_int, c_int]
@@ -426,6 +430,15 @@ def moe_gemm_clock_trace(records=None, slots=1):
     into records (device int64 [slots][CLOCK_MAX_WORKGROUPS][2]) in turn;
     records=None clears the trace."""
     _check("moe_gemm_clock_trace", lib().moe_gemm_clock_trace(_ptr(records), slots))
+
+
+def moe_bench_occupy(*, workgroups, ticks, stream=None):
+    """Hold `workgroups` CUs busy for `ticks` of the constant-rate counter."""
+    _check("moe_bench_occupy", lib().moe_bench_occupy(workgroups, ticks, _stream(stream)))
+
+
+def moe_grouped_gemm_workspace_size(dynamic=True) -> int:
+    return lib().moe_grouped_gemm_workspace_size(int(bool(dynamic)))
 
 
 def moe_grouped_gemm(*, E, N, K, M_cap, split_sizes, padded_offsets, a, b, c,

@@ -63,6 +63,7 @@ struct GemmTuning {
   int k_rot = 1;
   int split_max = 4;    // K parts of a split tail tile (1: no split-K); 3-4 measured best
   int split_min_k = 2;  // K steps each part keeps at least
+  bool dynamic = true;  // work counters when the workspace holds them (MOE_GEMM_DYNAMIC=0: off)
 };
 const GemmTuning& tuning() {
   static const GemmTuning t = [] {
@@ -73,6 +74,7 @@ const GemmTuning& tuning() {
       v.split_max = std::min(std::max(1, std::atoi(e)), moe::grouped_gemm_split_limit());
     if (const char* e = std::getenv("MOE_GEMM_SPLIT_MIN_K"))
       v.split_min_k = std::max(1, std::atoi(e));
+    if (const char* e = std::getenv("MOE_GEMM_DYNAMIC")) v.dynamic = std::atoi(e) != 0;
     return v;
   }();
   return t;
@@ -228,14 +230,40 @@ static int ws_grid() {
   return device_info(&cu) == MOE_OK ? cu : 256;
 }
 
+static size_t dprobs_bytes(int I, int64_t M_cap) {
+  return align256(static_cast<size_t>(M_cap * dgrad_parts(I) * sizeof(float)));
+}
+
 size_t moe_grouped_mlp_workspace_size(int E, int H, int I, int64_t M_cap, int prec, int act) {
   (void)E;
   (void)H;
   (void)prec;
   (void)act;
   if (I < 1 || M_cap < 0) return 0;
-  const size_t dp = align256(static_cast<size_t>(M_cap * dgrad_parts(I) * sizeof(float)));
-  return dp + moe::grouped_gemm_split_bytes(ws_grid());
+  return dprobs_bytes(I, M_cap) + align256(moe::grouped_gemm_split_bytes(ws_grid())) +
+         2 * moe::kTileCtrBytes;
+}
+
+size_t moe_grouped_gemm_workspace_size(int dynamic) {
+  return align256(moe::grouped_gemm_split_bytes(ws_grid())) + (dynamic ? moe::kTileCtrBytes : 0);
+}
+
+// The dynamic-scheduling counters of `launches` GEMM launches: the last
+// launches x kTileCtrBytes of the workspace layout, after the split-K area
+// sized for a full grid, at `offset` + that area.  Zeroed here (a fill
+// kernel, so graph capture records no memset).  Null (static scheduling)
+// when the workspace is smaller or the knob is off.
+static int* tile_counters(void* ws, size_t ws_bytes, size_t offset, int launches,
+                          hipStream_t s, moe_status* st) {
+  *st = MOE_OK;
+  if (!ws || !tuning().dynamic) return nullptr;
+  const size_t at = offset + align256(moe::grouped_gemm_split_bytes(ws_grid()));
+  const size_t need = static_cast<size_t>(launches) * moe::kTileCtrBytes;
+  if (ws_bytes < at + need) return nullptr;
+  int* c = reinterpret_cast<int*>(static_cast<char*>(ws) + at);
+  *st = launched(moe::launch_fill_f32(reinterpret_cast<float*>(c), 0.0f,
+                                      static_cast<int64_t>(need / sizeof(float)), s));
+  return c;
 }
 
 // Point a plain-store GEMM at the split-K area of the workspace (if it is
@@ -310,6 +338,11 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   g.act = moe::to_actp(a->act);
   g.bias = a->bias1;
   g.err = a->err_flag;
+  moe_status cst;
+  int* ctr = tile_counters(a->workspace, a->workspace_bytes, dprobs_bytes(a->I, a->M_cap), 2,
+                           s, &cst);
+  if (cst) return cst;
+  g.tile_ctr = ctr;
 
   // FC1: z = xp . W1i^T with the activation epilogue
   g.N = N1;
@@ -364,6 +397,7 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   f.act_out = nullptr;
   f.amax = nullptr;
   f.bias = nullptr;
+  f.tile_ctr = ctr ? ctr + moe::kTileCtrBytes / sizeof(int) : nullptr;
   const int grid2 = gemm_grid(cu, a->cu_margin, a->M_cap, a->E, f.N);
   if (moe_status st = attach_split(f, a->workspace, a->workspace_bytes, 0, grid2, s)) return st;
   if (moe_status st = launched(moe::launch_grouped_gemm(f, moe::EPI_STORE, false, mx, grid2, s)))
@@ -422,6 +456,10 @@ static moe_status bwd_impl(const moe_bwd_args* a, void* ws, size_t ws_bytes, voi
   g.act = moe::to_actp(a->act);
   g.bias = a->bias1;
   g.err = a->err_flag;
+  moe_status cst;
+  int* ctr = tile_counters(ws, ws_bytes, dprobs_bytes(a->I, a->M_cap), 2, s, &cst);
+  if (cst) return cst;
+  g.tile_ctr = ctr;
 
   // FC2 dgrad: dA = dyp . W2 (contracting over H) + dActivation.  bf16 reads
   // W2 [H][I] as [K=H][N=I]; MXFP8 reads its copy quantized along H, [I][H].
@@ -472,6 +510,7 @@ static moe_status bwd_impl(const moe_bwd_args* a, void* ws, size_t ws_bytes, voi
   f.k_rot_stride = tuning().k_rot;
   f.act = g.act;
   f.err = a->err_flag;
+  f.tile_ctr = ctr ? ctr + moe::kTileCtrBytes / sizeof(int) : nullptr;
   f.N = a->H;
   f.K = N1;
   if (mx) {
@@ -545,6 +584,9 @@ moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   g.C = static_cast<uint16_t*>(a->c);
   g.ldc = a->N;
   g.err = a->err_flag;
+  moe_status cst;
+  g.tile_ctr = tile_counters(a->workspace, a->workspace_bytes, 0, 1, s, &cst);
+  if (cst) return cst;
   const int grid = gemm_grid(cu, a->cu_margin, a->M_cap, a->E, a->N);
   if (f4) return launched(moe::launch_gemm_store_f4(g, grid, s));
   if (moe_status st = attach_split(g, a->workspace, a->workspace_bytes, 0, grid, s)) return st;

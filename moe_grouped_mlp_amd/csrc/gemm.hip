@@ -91,6 +91,38 @@ hipError_t launch_dprobs_reduce(const float* part, int n_part, const int32_t* sp
 
 }  // namespace moe
 
+namespace {
+
+// One workgroup per CU (96 KB of LDS each, so no two share a CU and no
+// grouped-GEMM workgroup fits beside one), idle until the constant-rate
+// counter has advanced by `ticks` or a fixed number of polls has passed.
+constexpr int kOccupyLds = 96 * 1024;
+constexpr int kOccupyMaxPolls = 1 << 24;
+
+__global__ __launch_bounds__(64) void occupy_kernel(int64_t ticks, int* sink) {
+  extern __shared__ int lds_hold[];
+  const int64_t t0 = static_cast<int64_t>(__builtin_amdgcn_s_memrealtime());
+  int64_t t = t0;
+  int polls = 0;
+  while (t - t0 < ticks && polls < kOccupyMaxPolls) {
+    __builtin_amdgcn_s_sleep(8);
+    t = static_cast<int64_t>(__builtin_amdgcn_s_memrealtime());
+    ++polls;
+  }
+  // keep the LDS allocation (and so the CU) with a use the compiler cannot drop
+  if (threadIdx.x == 0 && polls < 0) sink[0] = lds_hold[0];
+}
+
+}  // namespace
+
+extern "C" moe_status moe_bench_occupy(int workgroups, int64_t ticks, void* stream) {
+  if (workgroups < 1 || workgroups > 1024 || ticks < 1 || ticks > 100000000)
+    return MOE_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(occupy_kernel, dim3(workgroups), dim3(64), kOccupyLds,
+                     static_cast<hipStream_t>(stream), ticks, static_cast<int*>(nullptr));
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
 extern "C" int64_t moe_clock_tick_rate_hz(void) {
   int dev = 0, khz = 0;
   if (hipGetDevice(&dev) != hipSuccess ||

@@ -1418,6 +1418,31 @@ void grouped_gemm_kernel(GemmArgs g) {
     }
   };
 
+  // Dynamic scheduling (g.tile_ctr set and G a multiple of the XCD count):
+  // the first round is static (item vid), later items come from work
+  // counters, one per XCD, so a workgroup that starts late (its CU busy with
+  // another kernel) leaves its share to the others.  XCD x's counter hands
+  // out, in order, the items the static order gives XCD x (slot j of round
+  // r >= 1: r G + x (G / 8) + j), keeping the XCD's band of tiles together
+  // in its L2; once they are exhausted the workgroup takes from the other
+  // XCDs' counters in turn.  Each item is handed out once.  Thread 0 fetches
+  // the next item while the current one's K loop runs (the atomic is older
+  // than the loop's last wait) and passes it on through LDS.
+  const bool dyn = g.tile_ctr != nullptr && G % kNumXcd == 0;
+  const int per_x = G / kNumXcd;
+  const int my_x = blockIdx.x % kNumXcd;
+  __shared__ int s_wnext;
+  int fetched = 0;   // thread 0: the last counter value it took
+  auto slot_item = [&](int x, int i) { return (1 + i / per_x) * G + x * per_x + i % per_x; };
+  auto next_item = [&](int i) {
+    int id = slot_item(my_x, i);
+    for (int d = 1; d < kNumXcd && id >= items; ++d) {
+      const int x = (my_x + d) % kNumXcd;
+      id = slot_item(x, atomicAdd(g.tile_ctr + 16 * x, 1));
+    }
+    return id;
+  };
+
   int w = vid;
   TileInfo cur{};
   if (w < items) {
@@ -1432,6 +1457,7 @@ void grouped_gemm_kernel(GemmArgs g) {
     sfor<4>([&](auto mi) { sfor<4>([&](auto ni) { acc[mi][ni] = f32x16{}; }); });
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLoads));   // stage 0 landed
     bare_barrier();
+    if (dyn && tid == 0) fetched = atomicAdd(g.tile_ctr + 16 * my_x, 1);
     read_frags(sA0, sB0, sS0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
     for (int kt = 0; kt < k_len; kt += 2) {
       stage(sA0, sB0, sS0, sA1, sB1, sS1, kt);
@@ -1440,10 +1466,11 @@ void grouped_gemm_kernel(GemmArgs g) {
     // the loads still in flight are zero fills; then every wave is done
     // with the stages and the next item may start loading
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    if (dyn && tid == 0) s_wnext = next_item(fetched);
     __syncthreads();
     const TileInfo t0 = cur;
     const bool split = w >= full && S > 1;
-    w += G;
+    w = dyn ? s_wnext : w + G;
     const bool more = w < items;
     if (more) {
       cur = item_info(w);

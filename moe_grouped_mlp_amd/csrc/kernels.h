@@ -96,6 +96,9 @@ struct GemmArgs {
   uint8_t* mx_sT;
   int mx_n;
   int32_t* err;          // nullable: MOE_DEVERR_BAD_OFFSETS when the offsets are inconsistent
+  // dynamic tile scheduling (nullable: static): one work counter per XCD,
+  // tile_ctr[16 x] (64 bytes apart), zero before the launch
+  int* tile_ctr;
   // measurement (nullable): workgroup i writes clk[2 i] = shader cycles and
   // clk[2 i + 1] = constant-rate ticks between its start and its end
   int64_t* clk;
@@ -112,6 +115,8 @@ hipError_t launch_gemm_store_f4(const GemmArgs& g, int grid, hipStream_t s);
 int grouped_gemm_tile_n();  // BN of the launched configuration
 // bytes of split_ws + split_cnt for a grid of `grid` workgroups
 size_t grouped_gemm_split_bytes(int grid);
+// bytes of one launch's dynamic-scheduling counters (GemmArgs::tile_ctr)
+constexpr size_t kTileCtrBytes = 8 * 64;
 int grouped_gemm_split_limit();  // largest split_max the kernel accepts
 int grouped_gemm_tile_m();  // BM
 hipError_t launch_dprobs_reduce(const float* part, int n_part, const int32_t* split,

@@ -280,10 +280,15 @@ def test_bwd_validation():
         setattr(a, f, 64)
     # the dprobs partials (one per 256-column tile of I) are required; the
     # full size adds the split-K area (one fp32 256 x 256 tile and a counter
-    # per workgroup of a one-per-CU grid; 256 CUs assumed without a device)
+    # per workgroup of a one-per-CU grid; 256 CUs assumed without a device,
+    # rounded up to 256 bytes) and the work counters of dynamic tile
+    # scheduling (8 XCDs x 64 bytes for each of the two GEMMs)
     need = 1024 * 1 * 4
     full = B.moe_grouped_mlp_workspace_size(4, 128, 256, 1024)
-    assert full == need + 256 * (256 * 256 * 4 + 4)
+    split = -(-256 * (256 * 256 * 4 + 4) // 256) * 256
+    assert full == need + split + 2 * 8 * 64
+    assert B.moe_grouped_gemm_workspace_size(False) == split
+    assert B.moe_grouped_gemm_workspace_size(True) == split + 8 * 64
     a.workspace_bytes = full
     assert _call("moe_grouped_mlp_bwd", a) == DEVICE
     a.workspace_bytes = need
@@ -359,6 +364,15 @@ def test_unpermute_validation():
     assert _call("moe_unpermute", a) == INVALID
     a.dprobs, a.H = None, 12
     assert _call("moe_unpermute", a) == INVALID
+
+
+@no_device
+def test_bench_occupy_validation():
+    L = m.lib()
+    assert L.moe_bench_occupy(0, 1000, None) == INVALID
+    assert L.moe_bench_occupy(1025, 1000, None) == INVALID
+    assert L.moe_bench_occupy(8, 0, None) == INVALID
+    assert L.moe_bench_occupy(8, 100000001, None) == INVALID
 
 
 @no_device
