@@ -64,6 +64,7 @@ struct GemmTuning {
   int split_max = 4;    // K parts of a split tail tile (1: no split-K); 3-4 measured best
   int split_min_k = 2;  // K steps each part keeps at least
   bool dynamic = true;  // work counters when the workspace holds them (MOE_GEMM_DYNAMIC=0: off)
+  bool half_tiles = true;  // half-height last tiles of an expert (MOE_GEMM_HALF=0: off)
 };
 const GemmTuning& tuning() {
   static const GemmTuning t = [] {
@@ -75,6 +76,7 @@ const GemmTuning& tuning() {
     if (const char* e = std::getenv("MOE_GEMM_SPLIT_MIN_K"))
       v.split_min_k = std::max(1, std::atoi(e));
     if (const char* e = std::getenv("MOE_GEMM_DYNAMIC")) v.dynamic = std::atoi(e) != 0;
+    if (const char* e = std::getenv("MOE_GEMM_HALF")) v.half_tiles = std::atoi(e) != 0;
     return v;
   }();
   return t;
@@ -333,6 +335,7 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   g.split = a->split_sizes;
   g.padded = a->padded_offsets;
   g.group_m = tuning().group_m;
+  g.half_tiles = tuning().half_tiles;
   g.k_rot_stride = tuning().k_rot;
   g.probs = a->probs_p;
   g.act = moe::to_actp(a->act);
@@ -451,6 +454,7 @@ static moe_status bwd_impl(const moe_bwd_args* a, void* ws, size_t ws_bytes, voi
   g.split = a->split_sizes;
   g.padded = a->padded_offsets;
   g.group_m = tuning().group_m;
+  g.half_tiles = tuning().half_tiles;
   g.k_rot_stride = tuning().k_rot;
   g.probs = a->probs_p;
   g.act = moe::to_actp(a->act);
@@ -507,6 +511,7 @@ static moe_status bwd_impl(const moe_bwd_args* a, void* ws, size_t ws_bytes, voi
   f.split = a->split_sizes;
   f.padded = a->padded_offsets;
   f.group_m = tuning().group_m;
+  f.half_tiles = tuning().half_tiles;
   f.k_rot_stride = tuning().k_rot;
   f.act = g.act;
   f.err = a->err_flag;
@@ -580,6 +585,7 @@ moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   g.B = a->b;
   g.b_stride = a->b_stride ? a->b_stride : static_cast<int64_t>(a->N) * a->K;
   g.group_m = tuning().group_m;
+  g.half_tiles = tuning().half_tiles;
   g.k_rot_stride = tuning().k_rot;
   g.C = static_cast<uint16_t*>(a->c);
   g.ldc = a->N;
@@ -696,6 +702,7 @@ moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* a, void* stream) {
     g.b_s_stride = 0;
     g.wg_rows = P;
     g.group_m = tuning().group_m;
+    g.half_tiles = tuning().half_tiles;
     g.k_rot_stride = tuning().k_rot;
     g.C = static_cast<uint16_t*>(C);
     g.ldc = Q;

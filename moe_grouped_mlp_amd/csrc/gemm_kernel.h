@@ -524,6 +524,8 @@ struct TileCtx {
   int n_t;          // column-tile index
   int m_lane;       // row of this lane inside the tile, block mi = 0
   int n_lane;       // first column of this lane inside the tile, block 0
+  int mi_n;         // row blocks per wave: 4, or 2 in a half-height tile
+  int wrow;         // rows per wave row: kWaveM, or kWaveM / 2 in a half-height tile
 };
 
 // Keeps a block of accumulators in AGPRs up to this point of the epilogue.
@@ -555,7 +557,7 @@ MOE_DEV void epi_store(f32x16 (&acc)[4][4], uint16_t* __restrict__ C, int64_t ld
   sfor<4>([&](auto mi) {
     if constexpr (HOLD) sfor<4>([&](auto ni) { acc_hold(acc[mi][ni]); });
     const int m = t.m_lane + mi * 32;
-    if (m < t.rows_valid) {
+    if (mi < t.mi_n && m < t.rows_valid) {
       uint16_t* crow = C + (t.row0 + m) * ldc + t.col0 + t.n_lane;
       sfor<4>([&](auto ni) {
         if (t.n_lane - (t.n_lane & 31) + ni * 32 < t.cols_valid) {
@@ -600,7 +602,7 @@ MOE_DEV float epi_glu(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz
     sfor<4>([&](auto mi) {
       sfor<4>([&](auto ni) { acc_hold(acc[mi][ni]); });
       const int m = t.m_lane + mi * 32;
-      if (m < t.rows_valid) {
+      if (mi < t.mi_n && m < t.rows_valid) {
         const int64_t row = t.row0 + m;
         const float p = pr[mi];
         sfor<4>([&](auto ni) { sfor<4>([&](auto rg) {
@@ -626,7 +628,7 @@ MOE_DEV float epi_glu(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz
     sfor<4>([&](auto mi) {
       sfor<4>([&](auto ni) { acc_hold(acc[mi][ni]); });
       const int m = t.m_lane + mi * 32;
-      if (m < t.rows_valid) {
+      if (mi < t.mi_n && m < t.rows_valid) {
         const int64_t row = t.row0 + m;
         const float p = pr[mi];
         sfor<2>([&](auto h) { sfor<4>([&](auto rg) {
@@ -739,9 +741,10 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
   float amax = 0.0f;
   sfor<4>([&](auto mi) {
     sfor<4>([&](auto ni) { acc_hold(acc[mi][ni]); });
+    if (mi >= t.mi_n) return;   // a half-height tile's waves own two row blocks
     const int m = t.m_lane + mi * 32;
     const bool row_ok = m < t.rows_valid;
-    const int blk = wm * kWaveM + mi * 32;
+    const int blk = wm * t.wrow + mi * 32;
     const bool blk_ok = blk < t.rows_pad;
     const int64_t row = t.row0 + m;
     const int64_t rb = (t.row0 + blk) / 32;
@@ -935,6 +938,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void grouped_gemm_kernel(GemmArgs g) {
   constexpr int ACT = ACTF & ~kActBias;
   constexpr bool kBias = (ACTF & kActBias) != 0 && (EPI == EPI_GLU || EPI == EPI_DGLU);
+  // half-height tiles (an expert's last 128 rows or fewer) in the plain-store
+  // and GLU kernels with K-contiguous weights: the dGLU epilogue streams z in
+  // 64-row chunks laid out for full tiles, the weight gradient's rows are not
+  // routed rows, and with [K][N] weights (the bf16 FC1 dgrad) a half tile
+  // measured slower than a full one (its stage time is set by the B loads
+  // and transposed reads, which do not shrink)
+  constexpr bool kHalfTiles = (EPI == EPI_STORE || EPI == EPI_GLU) && !NN;
   static_assert(!(MX && NN), "MXFP8 operands are always K-contiguous");
   static_assert(!F4 || (MX && EPI == EPI_STORE), "MXFP4 runs the plain-store GEMM");
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[kStageBytes / 2], sA1[kStageBytes / 2];
@@ -960,6 +970,7 @@ void grouped_gemm_kernel(GemmArgs g) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int wm_s = wave_s >> 1;   // wave row, in a scalar register
   const int wm = wave >> 1, wn = wave & 1;
   const int E = g.E;
   const int tiles_n = (g.N + BN - 1) / BN;
@@ -1066,6 +1077,7 @@ void grouped_gemm_kernel(GemmArgs g) {
     int part, slot;   // split-K part and partial-tile slot (parts > 1)
     int64_t row0;     // first row of A
     int64_t orow0;    // first row of C (row0, or e * P + row0 for EPI_WGRAD)
+    bool half;        // half-height tile: an expert's last BM / 2 rows or fewer
   };
   auto tile_info = [&](int tile) {
     // expert owning this tile: last e with s_start[e] <= tile
@@ -1100,6 +1112,7 @@ void grouped_gemm_kernel(GemmArgs g) {
       const int nk_all = (g.K * kElem + kRowBytes - 1) / kRowBytes;
       ti.kbeg = min(max(s_pad[ti.e], 0) * kElem / kRowBytes, nk_all);
       ti.kend = min(ti.kbeg + (s_split[ti.e] * kElem + kRowBytes - 1) / kRowBytes, nk_all);
+      ti.half = false;
       return ti;
     }
     ti.row0 = static_cast<int64_t>(s_pad[ti.e]) + static_cast<int64_t>(m_t) * BM;
@@ -1112,6 +1125,7 @@ void grouped_gemm_kernel(GemmArgs g) {
         (s_split[ti.e] + MOE_GROUP_ALIGN - 1) / MOE_GROUP_ALIGN * MOE_GROUP_ALIGN;
     ti.rows_pad = static_cast<int>(
         min(static_cast<int64_t>(min(BM, padded_rows - m_t * BM)), g.M_cap - ti.row0));
+    ti.half = kHalfTiles && g.half_tiles && s_split[ti.e] - m_t * BM <= BM / 2;
     return ti;
   };
 
@@ -1160,7 +1174,10 @@ void grouped_gemm_kernel(GemmArgs g) {
     k_beg = ti.kbeg;
     k_len = nk_item;
     const int64_t a_rows = EPI == EPI_WGRAD ? g.wg_rows : g.M_cap;
-    const int64_t rows_avail = ti.rows_valid > 0 ? a_rows - ti.row0 : 0;
+    // a half-height tile loads only its BM / 2 rows (the DMA of the other
+    // rows falls outside the buffer and fills zeros without a fetch)
+    const int64_t rows_all = ti.rows_valid > 0 ? a_rows - ti.row0 : 0;
+    const int64_t rows_avail = ti.half ? min(rows_all, static_cast<int64_t>(BM / 2)) : rows_all;
     const int64_t arow0 = ti.rows_valid > 0 ? ti.row0 : 0;
     // the dGLU kernel recomputes the lane offsets per tile (hoisted, they
     // are spilled and reloaded in its epilogue)
@@ -1223,30 +1240,42 @@ void grouped_gemm_kernel(GemmArgs g) {
   i32x4 pa[2][4], pb[2][4];    // MXFP4 operands
   int sca[2][4], scb[2][4];    // MXFP8 scales
   // operands of sub-step j of a stage into register set buf
+  // half: a half-height tile, whose wave row wm owns rows 64 wm .. 64 wm + 63
+  // (row blocks 0 and 1); the swizzle depends on the row modulo 16 only, so
+  // its operand addresses are the full tile's moved back by 64 wm rows
   auto read_frags = [&](const uint16_t* a_st, const uint16_t* b_st, const uint8_t* s_st, auto j,
-                        auto buf) {
-    const char* ca = reinterpret_cast<const char*>(a_st);
+                        auto buf, auto half) {
+    constexpr bool HALF = decltype(half)::value;
+    static_assert(!HALF || (kHalfTiles && !kTN), "half-height tiles: K-contiguous A only");
+    const char* ca = reinterpret_cast<const char*>(a_st) - (HALF ? wm_s * (kWaveM / 2) * kRowBytes : 0);
     const char* cb = reinterpret_cast<const char*>(b_st);
+    // A scales: row group 4 wm + mi of the full tile, 2 wm + mi of a half one
+    const uint8_t* s_a = s_st - (HALF ? wm_s * 2 * (F4 ? 256 : 128) : 0);
+    constexpr int kMiA = HALF ? 2 : 4;   // A row blocks this wave reads
     constexpr int jj = decltype(j)::value;
     if constexpr (F4) {
       // a lane's 16-byte operand of a 64-deep step: 32 values, the whole
       // E8M0 block 2 j + h of the stage row (chunk 2 j + h, as a bf16
       // sub-step reads), scaled by that block's scale
       sfor<4>([&](auto i) {
-        pa[buf][i] = *reinterpret_cast<const i32x4*>(ca + a_off[jj] + i * 32 * kRowBytes);
+        if constexpr (i < kMiA)
+          pa[buf][i] = *reinterpret_cast<const i32x4*>(ca + a_off[jj] + i * 32 * kRowBytes);
         pb[buf][i] = *reinterpret_cast<const i32x4*>(cb + b_off[jj] + i * 32 * kRowBytes);
       });
       sfor<4>([&](auto i) {
-        sca[buf][i] = s_st[sa_off4 + i * 256 + jj * 64];
+        if constexpr (i < kMiA) sca[buf][i] = s_a[sa_off4 + i * 256 + jj * 64];
         scb[buf][i] = s_st[sb_off4 + i * 256 + jj * 64];
       });
     } else if constexpr (MX) {
       // a lane's 32-byte operand of a 64-deep step: chunks 4 j + h and
       // 4 j + 2 + h, the layout v_mfma_scale_f32_32x32x64_f8f6f4 takes
       sfor<4>([&](auto i) {
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(ca + a_off[2 * jj] + i * 32 * kRowBytes);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(ca + a_off[2 * jj + 1] + i * 32 * kRowBytes);
-        qa[buf][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        if constexpr (i < kMiA) {
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(ca + a_off[2 * jj] + i * 32 * kRowBytes);
+          const i32x4 hi =
+              *reinterpret_cast<const i32x4*>(ca + a_off[2 * jj + 1] + i * 32 * kRowBytes);
+          qa[buf][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
       });
       sfor<4>([&](auto i) {
         const i32x4 lo = *reinterpret_cast<const i32x4*>(cb + b_off[2 * jj] + i * 32 * kRowBytes);
@@ -1254,7 +1283,7 @@ void grouped_gemm_kernel(GemmArgs g) {
         qb[buf][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       });
       sfor<4>([&](auto i) {
-        sca[buf][i] = s_st[sa_off + i * 128 + jj * 64];
+        if constexpr (i < kMiA) sca[buf][i] = s_a[sa_off + i * 128 + jj * 64];
         scb[buf][i] = s_st[sb_off + i * 128 + jj * 64];
       });
     } else {
@@ -1269,7 +1298,8 @@ void grouped_gemm_kernel(GemmArgs g) {
         });
       } else {
         sfor<4>([&](auto i) {
-          fa[buf][i] = *reinterpret_cast<const bf16x8*>(ca + a_off[jj] + i * 32 * kRowBytes);
+          if constexpr (i < kMiA)
+            fa[buf][i] = *reinterpret_cast<const bf16x8*>(ca + a_off[jj] + i * 32 * kRowBytes);
         });
       }
       if constexpr (NN) {
@@ -1289,8 +1319,9 @@ void grouped_gemm_kernel(GemmArgs g) {
     }
   };
   // C^T blocks: B operand first, so a lane owns one output row
-  auto mfma_all = [&](auto buf) {
-    sfor<4>([&](auto mi) { sfor<4>([&](auto ni) {
+  auto mfma_all = [&](auto buf, auto half) {
+    constexpr int kMiA = decltype(half)::value ? 2 : 4;
+    sfor<kMiA>([&](auto mi) { sfor<4>([&](auto ni) {
       if constexpr (F4)
         acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             __builtin_shufflevector(pb[buf][ni], pb[buf][ni], 0, 1, 2, 3, -1, -1, -1, -1),
@@ -1304,39 +1335,46 @@ void grouped_gemm_kernel(GemmArgs g) {
                                                               acc[mi][ni], 0, 0, 0);
     }); });
   };
-  // LDS reads per sub-step and DMA loads per stage (per wave)
+  // LDS reads per sub-step and DMA loads per stage (per wave); a half-height
+  // tile reads two A row blocks instead of four (and their scales)
   constexpr int kReads = F4 ? 16 : (MX ? 24 : (kTN ? 16 : (NN ? 12 : 8)));
+  constexpr int kReadsHalf = F4 ? 12 : (MX ? 18 : (NN ? 10 : 6));
   constexpr int kLoads = 16 + (MX ? ScaleLoader<F4>::kInstr : 0);
-  // issue order: reads spread between the 16 MFMAs of a sub-step; in the
-  // last sub-step of a stage the next stage's DMA loads go in between too
-  // (a DMA load blocks the wave until the address unit takes it)
-  auto pin = [&]() {
+  // issue order: reads spread between the 16 MFMAs of a sub-step (8 in a
+  // half-height tile); in the last sub-step of a stage the next stage's DMA
+  // loads go in between too (a DMA load blocks the wave until the address
+  // unit takes it)
+  auto pin = [&](auto half) {
+    constexpr bool HALF = decltype(half)::value;
+    constexpr int kR = HALF ? kReadsHalf : kReads;
     sfor<8>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x100, (kReads + 7) / 8, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);           // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, (kR + 7) / 8, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, HALF ? 1 : 2, 0);  // MFMA
     });
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto pin_load = [&]() {
+  auto pin_load = [&](auto half) {
+    constexpr bool HALF = decltype(half)::value;
+    constexpr int kR = HALF ? kReadsHalf : kReads;
     if constexpr (kLoads > 16) __builtin_amdgcn_sched_group_barrier(0x020, kLoads - 16, 0);
     sfor<8>([&](auto) {
       __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);           // VMEM (DMA)
-      __builtin_amdgcn_sched_group_barrier(0x100, (kReads + 7) / 8, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, (kR + 7) / 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, HALF ? 1 : 2, 0);
     });
     __builtin_amdgcn_sched_barrier(0);
   };
   // One stage (kt): cur = its buffers, nxt = the next stage's; the freed
   // cur buffers take stage kt + 2.
   auto stage = [&](const uint16_t* a_cur, const uint16_t* b_cur, const uint8_t* s_cur,
-                   uint16_t* a_nxt, uint16_t* b_nxt, uint8_t* s_nxt, int kt) {
+                   uint16_t* a_nxt, uint16_t* b_nxt, uint8_t* s_nxt, int kt, auto half) {
     sfor<NS - 1>([&](auto j) {
       __builtin_amdgcn_sched_barrier(0);
       constexpr int jj = decltype(j)::value;
       read_frags(a_cur, b_cur, s_cur, std::integral_constant<int, jj + 1>{},
-                 std::integral_constant<int, (jj + 1) % 2>{});
-      mfma_all(std::integral_constant<int, jj % 2>{});
-      pin();
+                 std::integral_constant<int, (jj + 1) % 2>{}, half);
+      mfma_all(std::integral_constant<int, jj % 2>{}, half);
+      pin(half);
     });
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
@@ -1345,9 +1383,18 @@ void grouped_gemm_kernel(GemmArgs g) {
     issue_stage(const_cast<uint16_t*>(a_cur), const_cast<uint16_t*>(b_cur),
                 const_cast<uint8_t*>(s_cur), kt + 2);
     read_frags(a_nxt, b_nxt, s_nxt, std::integral_constant<int, 0>{},
-               std::integral_constant<int, NS % 2>{});
-    mfma_all(std::integral_constant<int, (NS - 1) % 2>{});
-    pin_load();
+               std::integral_constant<int, NS % 2>{}, half);
+    mfma_all(std::integral_constant<int, (NS - 1) % 2>{}, half);
+    pin_load(half);
+  };
+  // the K loop of one tile (its stages 0 and 1 issued already)
+  auto k_loop = [&](auto half) {
+    read_frags(sA0, sB0, sS0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+               half);
+    for (int kt = 0; kt < k_len; kt += 2) {
+      stage(sA0, sB0, sS0, sA1, sB1, sS1, kt, half);
+      stage(sA1, sB1, sS1, sA0, sB0, sS0, kt + 1, half);
+    }
   };
   static_assert(NS % 2 == 0, "sub-step register sets alternate 0, 1 across stages");
 
@@ -1400,7 +1447,7 @@ void grouped_gemm_kernel(GemmArgs g) {
   float bias_next = 0.0f;
   auto load_probs = [&](const TileInfo& ti) {
     if constexpr (EPI == EPI_GLU) {
-      const int ml = wm * kWaveM + (lane & 31);
+      const int ml = wm * (ti.half ? kWaveM / 2 : kWaveM) + (lane & 31);
       sfor<4>([&](auto mi) {
         const int m = ml + mi * 32;
         pr_next[mi] = m < ti.rows_valid ? g.probs[ti.row0 + m] : 0.0f;
@@ -1458,10 +1505,11 @@ void grouped_gemm_kernel(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLoads));   // stage 0 landed
     bare_barrier();
     if (dyn && tid == 0) fetched = atomicAdd(g.tile_ctr + 16 * my_x, 1);
-    read_frags(sA0, sB0, sS0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    for (int kt = 0; kt < k_len; kt += 2) {
-      stage(sA0, sB0, sS0, sA1, sB1, sS1, kt);
-      stage(sA1, sB1, sS1, sA0, sB0, sS0, kt + 1);
+    if constexpr (kHalfTiles) {
+      if (cur.half) k_loop(std::true_type{});
+      else k_loop(std::false_type{});
+    } else {
+      k_loop(std::false_type{});
     }
     // the loads still in flight are zero fills; then every wave is done
     // with the stages and the next item may start loading
@@ -1490,7 +1538,9 @@ void grouped_gemm_kernel(GemmArgs g) {
     t.col0 = t0.col0;
     t.cols_valid = t0.cols_valid;
     t.n_t = t0.n_t;
-    t.m_lane = wm * kWaveM + (lane & 31);
+    t.mi_n = t0.half ? 2 : 4;
+    t.wrow = t0.half ? kWaveM / 2 : kWaveM;
+    t.m_lane = wm * t.wrow + (lane & 31);
     t.n_lane = wn * kWaveN + 4 * (lane >> 5);
     MxOut mo{g.mx_q, g.mx_s, g.mx_qT, g.mx_sT, g.mx_n, g.M_cap};
     if constexpr (EPI == EPI_STORE || EPI == EPI_WGRAD) {
@@ -1548,7 +1598,7 @@ void grouped_gemm_kernel(GemmArgs g) {
         // the K loop: a spill reload would wait on the next tile's loads
         const int lane_e = opaque(lane), wave_e = opaque(wave);
         TileCtx te = t;
-        te.m_lane = (wave_e >> 1) * kWaveM + (lane_e & 31);
+        te.m_lane = (wave_e >> 1) * t.wrow + (lane_e & 31);
         te.n_lane = (wave_e & 1) * kWaveN + 4 * (lane_e >> 5);
         amax = epi_glu_mx<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, pr_tile, g.act, te,
                                wave_e & 1, wave_e >> 1, lane_e, mo, s_tr + wave_e * kTrTile,

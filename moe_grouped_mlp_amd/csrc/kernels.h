@@ -96,6 +96,9 @@ struct GemmArgs {
   uint8_t* mx_sT;
   int mx_n;
   int32_t* err;          // nullable: MOE_DEVERR_BAD_OFFSETS when the offsets are inconsistent
+  // half-height tiles for an expert's last 128 rows or fewer (plain-store
+  // and GLU kernels; 0: every tile is 256 rows)
+  int half_tiles;
   // dynamic tile scheduling (nullable: static): one work counter per XCD,
   // tile_ctr[16 x] (64 bytes apart), zero before the launch
   int* tile_ctr;
