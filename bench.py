@@ -443,7 +443,11 @@ def measure(args, config, prec, log_prefix=""):
                          prec={"bf16": mg.PREC_BF16, "mxfp8": mg.PREC_MXFP8,
                                "mxfp4": mg.PREC_MXFP4}[prec], wgrad=args.wgrad,
                          recompute=args.recompute,
-                         bf16_copies=True if (args.unfused and mx) else None)
+                         # the unfused MX layers need bf16 a and dz; the fused
+                         # MXFP4 layer writes only its MXFP4 copies
+                         bf16_copies=(True if (args.unfused and prec != "bf16")
+                                      else (False if prec == "mxfp4" else None)),
+                         unfused=args.unfused)
     blk.load_weights(w1, w2)
     del w1, w2
     torch.cuda.synchronize()
@@ -508,10 +512,7 @@ def measure(args, config, prec, log_prefix=""):
         blk.combine(blk.yp, blk.out)
         if evs is not None:
             evs.record(base + 4, cur_stream())
-        if mx:
-            blk.gather(dout, blk.dyp, blk.dyp_q, blk.dyp_s)
-        else:
-            blk.gather(dout, blk.dyp)
+        blk.gather(dout, blk.dyp, *blk._mx_dst("dyp"))
         if args.recompute:
             if evs is not None:
                 evs.record(base + ev_rc, cur_stream())
@@ -616,7 +617,8 @@ def measure(args, config, prec, log_prefix=""):
     value = flops_step / (ms_step * 1e-3) / 1e12
 
     # HBM-bound steps: algorithmic bytes
-    row_bytes = H * (1 + 1 / 32) if mx else 2 * H
+    fused4 = prec == "mxfp4" and not args.unfused
+    row_bytes = H * (1 + 1 / 32) if mx else (H * (0.5 + 1 / 32) if fused4 else 2 * H)
     idx_bytes = T * k * 4 * 2 + T * k * 4 + M * 8
     kernels = {}
     if args.recompute:
@@ -647,8 +649,8 @@ def measure(args, config, prec, log_prefix=""):
     for name, b in mem.items():
         kernels[name] = {"ms": round(seg_ms[name], 4), "unit": "GB/s",
                          "rate": round(b / (seg_ms[name] * 1e-3) / 1e9, 1)}
-    if mx:
-        # MXFP8 weight copies (once per weight update; not part of the step)
+    if mx or prec == "mxfp4":
+        # MX weight copies (once per weight update; not part of the step)
         qe = HipEvents(2)
         reps = 5
         qe.record(0, stream)
@@ -659,7 +661,7 @@ def measure(args, config, prec, log_prefix=""):
         q_ms = qe.elapsed_ms(0, 1) / reps
         qe.close()
         n_w = 2 * (E * n1 * H + E * H * I)        # elements quantized (4 copies)
-        q_bytes = n_w * (2 + 1 + 1 / 32)
+        q_bytes = n_w * (2 + (1 if mx else 0.5) + 1 / 32)
         kernels["quantize_weights"] = {"ms": round(q_ms, 4), "unit": "GB/s",
                                        "rate": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
                                        "outside_step": True}
@@ -841,9 +843,6 @@ def main():
 
     _, prec_default = BENCH_CONFIGS[args.config]
     prec = args.prec or prec_default
-    if prec == "mxfp4" and not args.unfused:
-        print("the MXFP4 layer runs as separate passes: add --unfused", file=sys.stderr)
-        sys.exit(2)
     if args.unfused and (args.wgrad or args.recompute):
         print("--unfused is the baseline of the fused step (no --wgrad, --recompute)",
               file=sys.stderr)

@@ -163,6 +163,12 @@ moe_status moe_weight_repack_interleave(const void* w1, void* w1i, int E,
  *     copy of the gathered rows blocked along H (codes xp_q u8 [M_cap][H],
  *     tiled scales xp_s of M_cap*H/32 bytes, see MOE_MX_BLOCK); pad rows
  *     get zero codes and scale code 0.  Needs H % 64 == 0, M_cap % 128 == 0.
+ *   MOE_PERMUTE_WRITE_MX4: the same with an MXFP4 copy instead ([FK] §
+ *     "Fused MXFP8 and NVFP4 quantization": the 4-bit recipe's operands,
+ *     read here as E2M1 with E8M0 scales per 32 along H): codes xp_q u8
+ *     [M_cap][H / 2] (two a byte, element 2 i in the low nibble of byte i),
+ *     scales as for WRITE_MX with the MXFP4 block rule (see
+ *     moe_quantize_mxfp4).  Not together with WRITE_MX.
  *   Requires H % 32 == 0 for GATHER, M_cap >= T*k + E*(MOE_GROUP_ALIGN-1)
  *   unless the caller knows the padded total fits (else MOE_DEVERR_MCAP_
  *   OVERFLOW is raised and rows past M_cap are dropped).
@@ -170,6 +176,7 @@ moe_status moe_weight_repack_interleave(const void* w1, void* w1i, int E,
 #define MOE_PERMUTE_BUILD_MAP 0x1
 #define MOE_PERMUTE_GATHER 0x2
 #define MOE_PERMUTE_WRITE_MX 0x4
+#define MOE_PERMUTE_WRITE_MX4 0x8
 
 typedef struct moe_permute_args {
   int32_t flags;
@@ -320,6 +327,17 @@ moe_status moe_quantize_mxfp4(const moe_quant_args* args, void* stream);
  *   group (up to the next multiple of MOE_GROUP_ALIGN) get zero codes and
  *   scale code 0 in both copies.  Weights are contiguous per expert
  *   (w1_stride / w2_stride are ignored).  Needs M_cap % 128 == 0.
+ *
+ *   prec == MOE_PREC_MXFP4 ([FK] § "Fused MXFP8 and NVFP4 quantization":
+ *   the 4-bit recipe; E2M1 codes with E8M0 scales per 32 along K on MI355X,
+ *   the format of moe_quantize_mxfp4): the same fields as MXFP8, every
+ *   operand MXFP4 -- codes two a byte (element 2 i in the low nibble of
+ *   byte i), [rows][K / 2] -- and scales in the tiled layout with the
+ *   MXFP4 block rule: xp_q/xp_s (moe_permute WRITE_MX4), w1_q/w1_s and
+ *   w2_q/w2_s (moe_quantize_mxfp4 ROW of w1i and w2).  The FC1 epilogue
+ *   writes a_q/a_s, the MXFP4 copy of the stored bf16 a blocked along I
+ *   (codes [M_cap][I / 2]).  No transposed copy (aT_q and aT_s must be
+ *   NULL) and no bias (bias1 NULL), else MOE_ERR_INVALID_ARG.
  * ---------------------------------------------------------------------- */
 typedef struct moe_fwd_args {
   int32_t E, H, I;
@@ -390,6 +408,12 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* args, void* stream);
  *   only gate or only up columns) and, if dzT_q and dzT_s are both set, the
  *   transposed dzT_q [N1][M_cap] blocked along M inside each group.  Pad
  *   rows as in the forward.  Needs M_cap % 128 == 0.
+ *
+ *   prec == MOE_PREC_MXFP4: as MXFP8 with MXFP4 operands (see the forward):
+ *   dyp_q/dyp_s (moe_permute WRITE_MX4 of dOut), w2t_q/w2t_s and
+ *   w1t_q/w1t_s (moe_quantize_mxfp4 COL of w2 and w1i), and the epilogue's
+ *   dz_q/dz_s, the MXFP4 copy of the stored bf16 dz blocked along N1.  No
+ *   transposed copy (dzT_q, dzT_s NULL), no bias.
  * ---------------------------------------------------------------------- */
 typedef struct moe_bwd_args {
   int32_t E, H, I;

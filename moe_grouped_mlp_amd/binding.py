@@ -18,6 +18,7 @@ lib_path = os.path.join(HERE, "libmoe_gmlp.so")
 ACT_SWIGLU, ACT_GEGLU, ACT_SRELU = 0, 1, 2
 PREC_BF16, PREC_MXFP8, PREC_MXFP4 = 0, 1, 2
 PERMUTE_BUILD_MAP, PERMUTE_GATHER, PERMUTE_WRITE_MX = 0x1, 0x2, 0x4
+PERMUTE_WRITE_MX4 = 0x8
 QUANT_ROW, QUANT_COL = 0, 1
 GROUP_ALIGN = 128
 INTERLEAVE = 64

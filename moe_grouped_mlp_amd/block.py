@@ -22,11 +22,14 @@ and dW2 [E][H][I].  bf16 reads dz, Xp, dYp and a as stored; MXFP8 reads the
 transposed copies of a and dz the epilogues wrote and makes those of Xp and
 dYp with moe_quantize_mxfp8 (the permutes then also keep bf16 Xp and dYp).
 
-With prec=PREC_MXFP4 the layer runs as the unfused passes below: bf16
-routing and activation passes, moe_quantize_mxfp4 before each of the four
-GEMMs and the MXFP4 grouped GEMM (weight copies made by quantize_weights,
-rowwise and, for the dgrads, transposed); no weight-gradient or recompute
-path.
+With prec=PREC_MXFP4 the layer is fused the same way with MXFP4 operands:
+the permutes write MXFP4 rows, the GLU and dGLU epilogues write the MXFP4
+copies of a and dz, and quantize_weights() makes the four MXFP4 weight
+copies (rowwise and, for the dgrads, along N1 / H).  No transposed copies,
+weight-gradient, recompute or bias path.  unfused=True runs the same layer
+as separate passes instead (bf16 permutes and activation passes,
+moe_quantize_mxfp4 before each of the four grouped GEMMs): the baseline the
+fused path is measured against, which needs the bf16 copies.
 
 With recompute=True (activation recompute) the forward stores no z and the
 backward first rebuilds it with moe_grouped_gemm from the saved Xp and W1
@@ -58,7 +61,7 @@ class ExpertBlock:
                  prec: int = B.PREC_BF16, transposed_copies: bool = True,
                  bf16_copies: Optional[bool] = None, wgrad: bool = False,
                  recompute: bool = False, z_scratch: Optional[torch.Tensor] = None,
-                 device="cuda"):
+                 unfused: bool = False, device="cuda"):
         self.E, self.H, self.I, self.T, self.k = E, H, I, T, k
         self.act = act or B.act_params()
         self.gated = self.act.act != B.ACT_SRELU
@@ -72,10 +75,14 @@ class ExpertBlock:
         # tests may keep the rebuilt z after the backward, to compare it
         self.keep_recomputed_z = False
         self.mx = prec == B.PREC_MXFP8
-        # MXFP4: the layer as separate passes (no fused epilogue writes
-        # MXFP4): bf16 routing and activations, each GEMM operand quantized
-        # by moe_quantize_mxfp4 before an MXFP4 grouped GEMM
+        # MXFP4: fused like MXFP8 -- the permutes and the GLU / dGLU
+        # epilogues write the MXFP4 rowwise operands of the next GEMM -- or,
+        # through the *_unfused methods (bf16 copies needed), as separate
+        # passes with every operand quantized by moe_quantize_mxfp4
         self.mx4 = prec == B.PREC_MXFP4
+        # forward() / backward() run the unfused passes (the baseline the
+        # fused kernels are measured against; bf16 copies are then needed)
+        self.unfused = unfused
         M_cap = M_cap if M_cap is not None else T * k + E * (B.GROUP_ALIGN - 1)
         if self.mx or self.mx4:
             M_cap = -(-M_cap // B.GROUP_ALIGN) * B.GROUP_ALIGN
@@ -97,8 +104,12 @@ class ExpertBlock:
         self.bias1 = None            # optional FC1 bias, fp32 [E][N1] (load_weights)
         self.ws_route = torch.empty(max(1, B.moe_permute_workspace_size(T, E)),
                                     dtype=torch.uint8, device=dev)
-        # bf16 a and dz: operands of the bf16 GEMMs; optional with MXFP8
-        keep = (not self.mx) if bf16_copies is None else (bf16_copies or not self.mx)
+        # bf16 a and dz (and, in MXFP4, Xp and dYp): operands of the bf16
+        # GEMMs; optional with MX operands, kept by default only for the
+        # unfused layer, whose separate passes read them
+        mx_any = self.mx or self.mx4
+        keep = ((not mx_any or unfused) if bf16_copies is None
+                else (bf16_copies or not mx_any))
         if self.mx4 and (wgrad or recompute):
             raise ValueError("the MXFP4 layer has no weight-gradient or recompute path")
         if recompute:
@@ -134,6 +145,8 @@ class ExpertBlock:
                 n *= d
             return torch.empty(*shape, **u8), torch.empty(n // B.MX_BLOCK, **u8)
 
+        if self.mx4 and not keep:
+            self.xp = self.dyp = None
         if self.mx:
             self.xp = self.dyp = None
             self.xp_q, self.xp_s = mx_pair(M, H)
@@ -149,7 +162,7 @@ class ExpertBlock:
                 self.dzT_q, self.dzT_s = mx_pair(N1, M)
             else:
                 self.aT_q = self.aT_s = self.dzT_q = self.dzT_s = None
-        else:
+        elif not self.mx4 or keep:
             self.xp = torch.empty(M, H, **bf)
             self.dyp = torch.empty(M, H, **bf)
         if self.mx4:
@@ -230,18 +243,29 @@ class ExpertBlock:
     def route(self, expert_idx: torch.Tensor, probs: torch.Tensor,
               x: Optional[torch.Tensor] = None) -> None:
         flags = B.PERMUTE_BUILD_MAP
+        xq, xs = self._mx_dst("xp")
         if x is not None:
-            flags |= B.PERMUTE_GATHER | (B.PERMUTE_WRITE_MX if self.mx else 0)
+            flags |= B.PERMUTE_GATHER
+            if xq is not None:
+                flags |= B.PERMUTE_WRITE_MX4 if self.mx4 else B.PERMUTE_WRITE_MX
         B.moe_permute(flags=flags, T=self.T, k=self.k, E=self.E, H=self.H,
                       M_cap=self.M_cap, first_expert=self.first_expert,
                       expert_idx=expert_idx, probs=probs,
                       split_sizes=self.split_sizes, offsets=self.offsets,
                       padded_offsets=self.padded_offsets,
                       row_id_map=self.row_id_map, row_src=self.row_src,
-                      probs_p=self.probs_p, x=x, xp=self.xp,
-                      xp_q=self.xp_q if self.mx else None,
-                      xp_s=self.xp_s if self.mx else None,
+                      probs_p=self.probs_p, x=x, xp=self.xp, xp_q=xq, xp_s=xs,
                       err_flag=self.err_flag, workspace=self.ws_route)
+
+    def _mx_dst(self, name):
+        """The MX copy (codes, scales) the permutes write for xp or dyp:
+        MXFP8 or MXFP4, or (None, None) in bf16 and in the unfused MXFP4
+        layer (which quantizes the bf16 rows itself)."""
+        if self.mx:
+            return getattr(self, name + "_q"), getattr(self, name + "_s")
+        if self.mx4 and not self.unfused:
+            return getattr(self, name + "_q4"), getattr(self, name + "_s4")
+        return None, None
 
     def route_logits(self, logits: torch.Tensor,
                      x: Optional[torch.Tensor] = None, fused: bool = True) -> None:
@@ -274,13 +298,14 @@ class ExpertBlock:
                            row_src=self.row_src, probs_p=self.probs_p,
                            err_flag=self.err_flag, workspace=self.ws_router)
         if x is not None:
-            self.gather(x, self.xp, self.xp_q if self.mx else None,
-                        self.xp_s if self.mx else None)
+            self.gather(x, self.xp, *self._mx_dst("xp"))
 
     def gather(self, src: torch.Tensor, dst: Optional[torch.Tensor],
                dst_q: Optional[torch.Tensor] = None,
                dst_s: Optional[torch.Tensor] = None) -> None:
-        flags = B.PERMUTE_GATHER | (B.PERMUTE_WRITE_MX if dst_q is not None else 0)
+        flags = B.PERMUTE_GATHER
+        if dst_q is not None:
+            flags |= B.PERMUTE_WRITE_MX4 if self.mx4 else B.PERMUTE_WRITE_MX
         B.moe_permute(flags=flags, T=self.T, k=self.k, E=self.E,
                       H=self.H, M_cap=self.M_cap,
                       first_expert=self.first_expert,
@@ -296,6 +321,10 @@ class ExpertBlock:
                       w1_s=self.w1_s, w2_q=self.w2_q, w2_s=self.w2_s,
                       a_q=self.a_q, a_s=self.a_s, aT_q=self.aT_q,
                       aT_s=self.aT_s)
+        elif self.mx4:
+            kw = dict(xp_q=self.xp_q4, xp_s=self.xp_s4, w1_q=self.w1_q4,
+                      w1_s=self.w1_s4, w2_q=self.w2_q4, w2_s=self.w2_s4,
+                      a_q=self.a_q4, a_s=self.a_s4)
         else:
             kw = dict(xp=self.xp, w1i=self.w1i, w2=self.w2)
         B.moe_grouped_mlp_fwd(E=self.E, H=self.H, I=self.I, M_cap=self.M_cap,
@@ -344,7 +373,7 @@ class ExpertBlock:
 
     def forward(self, x, expert_idx, probs, timing_events=None):
         self.route(expert_idx, probs, x)
-        if self.mx4:
+        if self.unfused:
             self.experts_forward_unfused()
         else:
             self.experts_forward(timing_events)
@@ -360,6 +389,10 @@ class ExpertBlock:
                       w2t_s=self.w2t_s, w1t_q=self.w1t_q, w1t_s=self.w1t_s,
                       dz_q=self.dz_q, dz_s=self.dz_s, dzT_q=self.dzT_q,
                       dzT_s=self.dzT_s)
+        elif self.mx4:
+            kw = dict(dyp_q=self.dyp_q4, dyp_s=self.dyp_s4, w2t_q=self.w2t_q4,
+                      w2t_s=self.w2t_s4, w1t_q=self.w1t_q4, w1t_s=self.w1t_s4,
+                      dz_q=self.dz_q4, dz_s=self.dz_s4)
         else:
             kw = dict(dyp=self.dyp, w2=self.w2, w1i=self.w1i)
         B.moe_grouped_mlp_bwd(E=self.E, H=self.H, I=self.I, M_cap=self.M_cap,
@@ -375,11 +408,8 @@ class ExpertBlock:
             self.release_z()
 
     def backward(self, dout, timing_events=None):
-        if self.mx:
-            self.gather(dout, self.dyp, self.dyp_q, self.dyp_s)
-        else:
-            self.gather(dout, self.dyp)
-        if self.mx4:
+        self.gather(dout, self.dyp, *self._mx_dst("dyp"))
+        if self.unfused:
             self.experts_backward_unfused()
         else:
             self.experts_backward(timing_events)
@@ -414,8 +444,9 @@ class ExpertBlock:
     def experts_forward_unfused(self, events=None) -> None:
         if self.bias1 is not None:
             raise RuntimeError("the FC1 bias is applied by the fused path only")
-        if self.mx and self.a is None:
-            raise RuntimeError("the MXFP8 unfused baseline needs bf16_copies=True")
+        # MXFP8 reads the permute's MXFP8 Xp; MXFP4 quantizes the bf16 Xp
+        if (self.mx and self.a is None) or (self.mx4 and (self.a is None or self.xp is None)):
+            raise RuntimeError("the MX unfused baseline needs bf16_copies=True")
         rec = (lambda i: events.record(i)) if events else (lambda i: None)
         rec(0)
         if self.mx4:
@@ -445,8 +476,8 @@ class ExpertBlock:
         rec(3)
 
     def experts_backward_unfused(self, events=None) -> None:
-        if self.mx and self.dz is None:
-            raise RuntimeError("the MXFP8 unfused baseline needs bf16_copies=True")
+        if (self.mx and self.dz is None) or (self.mx4 and (self.dz is None or self.dyp is None)):
+            raise RuntimeError("the MX unfused baseline needs bf16_copies=True")
         if getattr(self, "da", None) is None:
             self.da = torch.empty(self.M_cap, self.I, dtype=torch.bfloat16,
                                   device=self.z.device)

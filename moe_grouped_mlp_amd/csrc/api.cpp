@@ -147,15 +147,18 @@ size_t moe_permute_workspace_size(int T, int E) {
 
 moe_status moe_permute(const moe_permute_args* a, void* stream) {
   if (!a) return MOE_ERR_INVALID_ARG;
-  const int known = MOE_PERMUTE_BUILD_MAP | MOE_PERMUTE_GATHER | MOE_PERMUTE_WRITE_MX;
+  const int known = MOE_PERMUTE_BUILD_MAP | MOE_PERMUTE_GATHER | MOE_PERMUTE_WRITE_MX |
+                    MOE_PERMUTE_WRITE_MX4;
   if (a->flags == 0 || (a->flags & ~known)) return MOE_ERR_INVALID_ARG;
+  if ((a->flags & MOE_PERMUTE_WRITE_MX) && (a->flags & MOE_PERMUTE_WRITE_MX4))
+    return MOE_ERR_INVALID_ARG;
   if (a->T < 0 || a->k < 1 || a->k > kMaxTopK || a->E < 1 || a->E > kMaxExperts ||
       a->M_cap < 0 || a->M_cap > INT32_MAX)
     return MOE_ERR_INVALID_ARG;
   if (!a->split_sizes || !a->padded_offsets || !a->row_id_map) return MOE_ERR_INVALID_ARG;
   const bool build = a->flags & MOE_PERMUTE_BUILD_MAP;
   const bool gather = a->flags & MOE_PERMUTE_GATHER;
-  const bool write_mx = a->flags & MOE_PERMUTE_WRITE_MX;
+  const bool write_mx = a->flags & (MOE_PERMUTE_WRITE_MX | MOE_PERMUTE_WRITE_MX4);
   if (write_mx && (!gather || !a->xp_q || !a->xp_s || a->H % 64 != 0 || a->M_cap % 128 != 0))
     return MOE_ERR_INVALID_ARG;
   if (build) {
@@ -297,8 +300,9 @@ static moe_status check_common(int E, int H, int I, int64_t M_cap, int prec,
       M_cap < 1 || M_cap > INT32_MAX || !act_ok(act) || cu_margin < 0)
     return MOE_ERR_INVALID_ARG;
   if (!split || !padded || !probs_p) return MOE_ERR_INVALID_ARG;
-  if (prec != MOE_PREC_BF16 && prec != MOE_PREC_MXFP8) return MOE_ERR_INVALID_ARG;
-  if (prec == MOE_PREC_MXFP8 && M_cap % 128 != 0) return MOE_ERR_INVALID_ARG;
+  if (prec != MOE_PREC_BF16 && prec != MOE_PREC_MXFP8 && prec != MOE_PREC_MXFP4)
+    return MOE_ERR_INVALID_ARG;
+  if (prec != MOE_PREC_BF16 && M_cap % 128 != 0) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -307,13 +311,16 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   if (moe_status st = check_common(a->E, a->H, a->I, a->M_cap, a->prec, a->act, a->cu_margin,
                                    a->split_sizes, a->padded_offsets, a->probs_p))
     return st;
-  const bool mx = a->prec == MOE_PREC_MXFP8;
+  const bool f4 = a->prec == MOE_PREC_MXFP4;
+  const bool mx = a->prec == MOE_PREC_MXFP8 || f4;
   const bool gated = a->act.act != MOE_ACT_SRELU;
   const int N1 = gated ? 2 * a->I : a->I;
   if (mx) {
     if (!a->xp_q || !a->xp_s || !a->w1_q || !a->w1_s || !a->w2_q || !a->w2_s || !a->a_q ||
         !a->a_s || !a->yp || ((a->aT_q != nullptr) != (a->aT_s != nullptr)))
       return MOE_ERR_INVALID_ARG;
+    // MXFP4: no transposed copy (there is no MXFP4 weight gradient), no bias
+    if (f4 && (a->aT_q || a->bias1)) return MOE_ERR_INVALID_ARG;
   } else {
     if (!a->xp || !a->w1i || !a->w2 || !a->a || !a->yp) return MOE_ERR_INVALID_ARG;
     if (a->w1_stride != 0 && a->w1_stride < static_cast<int64_t>(N1) * a->H)
@@ -373,8 +380,10 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   g.ld_act = a->I;
   g.amax = a->amax;
   record(a->timing_events[0], s);
-  if (moe_status st = launched(moe::launch_grouped_gemm(
-          g, moe::EPI_GLU, false, mx, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, g.N), s)))
+  const int grid1 = gemm_grid(cu, a->cu_margin, a->M_cap, a->E, g.N);
+  if (moe_status st = launched(f4 ? moe::launch_gemm_glu_f4(g, grid1, s)
+                                  : moe::launch_grouped_gemm(g, moe::EPI_GLU, false, mx, grid1,
+                                                             s)))
     return st;
   record(a->timing_events[1], s);
 
@@ -402,9 +411,13 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
   f.bias = nullptr;
   f.tile_ctr = ctr ? ctr + moe::kTileCtrBytes / sizeof(int) : nullptr;
   const int grid2 = gemm_grid(cu, a->cu_margin, a->M_cap, a->E, f.N);
-  if (moe_status st = attach_split(f, a->workspace, a->workspace_bytes, 0, grid2, s)) return st;
-  if (moe_status st = launched(moe::launch_grouped_gemm(f, moe::EPI_STORE, false, mx, grid2, s)))
-    return st;
+  if (f4) {   // the MXFP4 plain-store GEMM runs its last round unsplit
+    if (moe_status st = launched(moe::launch_gemm_store_f4(f, grid2, s))) return st;
+  } else {
+    if (moe_status st = attach_split(f, a->workspace, a->workspace_bytes, 0, grid2, s)) return st;
+    if (moe_status st = launched(moe::launch_grouped_gemm(f, moe::EPI_STORE, false, mx, grid2, s)))
+      return st;
+  }
   record(a->timing_events[2], s);
   return MOE_OK;
 }
@@ -418,13 +431,15 @@ static moe_status bwd_check(const moe_bwd_args* a) {
   if (moe_status st = check_common(a->E, a->H, a->I, a->M_cap, a->prec, a->act, a->cu_margin,
                                    a->split_sizes, a->padded_offsets, a->probs_p))
     return st;
-  const bool mx = a->prec == MOE_PREC_MXFP8;
+  const bool f4 = a->prec == MOE_PREC_MXFP4;
+  const bool mx = a->prec == MOE_PREC_MXFP8 || f4;
   const int N1 = a->act.act != MOE_ACT_SRELU ? 2 * a->I : a->I;
   if (!a->z || !a->dprobs_p || !a->dxp) return MOE_ERR_INVALID_ARG;
   if (mx) {
     if (!a->dyp_q || !a->dyp_s || !a->w2t_q || !a->w2t_s || !a->w1t_q || !a->w1t_s ||
         !a->dz_q || !a->dz_s || ((a->dzT_q != nullptr) != (a->dzT_s != nullptr)))
       return MOE_ERR_INVALID_ARG;
+    if (f4 && (a->dzT_q || a->bias1)) return MOE_ERR_INVALID_ARG;
   } else {
     if (!a->dyp || !a->w2 || !a->w1i || !a->dz) return MOE_ERR_INVALID_ARG;
     if (a->w1_stride != 0 && a->w1_stride < static_cast<int64_t>(N1) * a->H)
@@ -437,7 +452,8 @@ static moe_status bwd_check(const moe_bwd_args* a) {
 
 static moe_status bwd_impl(const moe_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
   if (moe_status st = bwd_check(a)) return st;
-  const bool mx = a->prec == MOE_PREC_MXFP8;
+  const bool f4 = a->prec == MOE_PREC_MXFP4;
+  const bool mx = a->prec == MOE_PREC_MXFP8 || f4;
   const bool gated = a->act.act != MOE_ACT_SRELU;
   const int N1 = gated ? 2 * a->I : a->I;
   // the dprobs partials are required; the split-K area is used when present
@@ -494,8 +510,9 @@ static moe_status bwd_impl(const moe_bwd_args* a, void* ws, size_t ws_bytes, voi
   g.dp_part = static_cast<float*>(ws);
   g.n_part = n_part;
   record(a->timing_events[0], s);
-  if (moe_status st = launched(moe::launch_grouped_gemm(
-          g, moe::EPI_DGLU, !mx, mx, gemm_grid(cu, a->cu_margin, a->M_cap, a->E, g.N), s)))
+  const int grid1 = gemm_grid(cu, a->cu_margin, a->M_cap, a->E, g.N);
+  if (moe_status st = launched(f4 ? moe::launch_gemm_dglu_f4(g, grid1, s)
+                                  : moe::launch_grouped_gemm(g, moe::EPI_DGLU, !mx, mx, grid1, s)))
     return st;
   if (moe_status st = launched(moe::launch_dprobs_reduce(g.dp_part, n_part, a->split_sizes,
                                                          a->padded_offsets, a->E, a->M_cap,
@@ -535,10 +552,13 @@ static moe_status bwd_impl(const moe_bwd_args* a, void* ws, size_t ws_bytes, voi
   const int grid2 = gemm_grid(cu, a->cu_margin, a->M_cap, a->E, f.N);
   const size_t dp_bytes =
       align256(static_cast<size_t>(a->M_cap * dgrad_parts(a->I) * sizeof(float)));
-  if (moe_status st = attach_split(f, ws, ws_bytes, dp_bytes, grid2, s))
-    return st;
-  if (moe_status st = launched(moe::launch_grouped_gemm(f, moe::EPI_STORE, !mx, mx, grid2, s)))
-    return st;
+  if (f4) {   // the MXFP4 plain-store GEMM runs its last round unsplit
+    if (moe_status st = launched(moe::launch_gemm_store_f4(f, grid2, s))) return st;
+  } else {
+    if (moe_status st = attach_split(f, ws, ws_bytes, dp_bytes, grid2, s)) return st;
+    if (moe_status st = launched(moe::launch_grouped_gemm(f, moe::EPI_STORE, !mx, mx, grid2, s)))
+      return st;
+  }
   record(a->timing_events[2], s);
   return MOE_OK;
 }

@@ -417,6 +417,34 @@ MOE_DEV void mx_row_block(const float (&v)[16], uint8_t* q_lane, uint8_t* s_byte
   if (hf == 0) *s_byte = mx_scale_code(e);
 }
 
+// MXFP4 rowwise (no transposed copy): the row's 32 values, this lane's and
+// its partner's, give one E8M0 scale and 32 E2M1 codes (16 bytes, element
+// 2 i in the low nibble of byte i).  A lane's four values of columns
+// 8 rg + 4 hf .. make a 16-bit half of the word of columns 8 rg ..; the
+// halves are exchanged with the partner (v_permlane32_swap) so that the low
+// lane stores the words of columns 0 .. 15 and the high lane 16 .. 31
+// (8 bytes each, q_lane = the block's row start + 8 hf).
+MOE_DEV void mx4_row_block(const float (&v)[16], uint8_t* q_lane, uint8_t* s_byte, int hf) {
+  float am = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(v[r]));
+  am = fmaxf(am, partner32(am, hf));
+  const int e = mx4_exponent(am);
+  const float inv = mx_inv_scale(e);
+  uint32_t h[4];
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg)
+    h[rg] = mx4_codes4(v[4 * rg], v[4 * rg + 1], v[4 * rg + 2], v[4 * rg + 3], inv);
+  // a = (h0, h1), b = (h2, h3); after the swap the low lane holds its own a
+  // and the partner's a in b, the high lane the partner's b in a and its own b
+  const auto sw = __builtin_amdgcn_permlane32_swap(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                                   false, false);
+  const uint32_t lo = sw[0], hi = sw[1];
+  *reinterpret_cast<uint2*>(q_lane) =
+      make_uint2((lo & 0xffffu) | (hi << 16), (lo >> 16) | (hi & 0xffff0000u));
+  if (hf == 0) *s_byte = mx_scale_code(e);
+}
+
 // Transposed: column c of the block is one MX block of the transposed copy
 // (rows 32 rb .. 32 rb + 31).  The wave stages its 32 x 32 bf16 block in a
 // private LDS tile (row pitch kTrPitch), then lane l gathers rows
@@ -481,10 +509,11 @@ struct MxBase {
   uint8_t* sT;   // transposed scale of (column lane % 32, row block rb)
 };
 
+template <bool F4OUT = false>
 MOE_DEV MxBase mx_base(const MxOut& o, int64_t row, int64_t rb, int lane) {
   const int hf = lane >> 5, c = lane & 31;
   MxBase b;
-  b.q = o.q + row * o.n + 16 * hf;
+  b.q = F4OUT ? o.q + row * (o.n / 2) + 8 * hf : o.q + row * o.n + 16 * hf;
   b.s = o.s + mx_scale_off(row, 0, o.n);
   b.qT = o.qT + static_cast<int64_t>(c) * o.M_cap + rb * 32 + 16 * hf;
   b.sT = o.sT + mx_scale_off(c, rb, o.M_cap);
@@ -495,9 +524,16 @@ MOE_DEV MxBase mx_base(const MxOut& o, int64_t row, int64_t rb, int lane) {
 // of a row block whose rows all lie before the group's padded end.  With
 // col0 a multiple of 32, the tiled scale offsets of (row, col0 / 32) and
 // (col0 + lane % 32, rb) are those of block 0 plus terms in col0 alone.
+// F4OUT: MXFP4 rowwise codes ([M_cap][n / 2]) and no transposed copy.
+template <bool F4OUT = false>
 MOE_DEV void mx_block_out(const float (&v)[16], const MxOut& o, const MxBase& b, uint16_t* tr,
                           int col0, int lane) {
-  mx_row_block(v, b.q + col0, b.s + (col0 >> 6) * 64 + ((col0 >> 5) & 1) * 32, lane >> 5);
+  uint8_t* const sb = b.s + (col0 >> 6) * 64 + ((col0 >> 5) & 1) * 32;
+  if constexpr (F4OUT) {
+    mx4_row_block(v, b.q + col0 / 2, sb, lane >> 5);
+    return;
+  }
+  mx_row_block(v, b.q + col0, sb, lane >> 5);
   if (o.qT)
     mx_col_block(v, tr, b.qT + static_cast<int64_t>(col0) * o.M_cap,
                  b.sT + static_cast<int64_t>(col0 >> 5) * (o.M_cap >> 6) * 64, lane);
@@ -731,7 +767,7 @@ MOE_DEV float dglu_rows(f32x16 (&acc)[4][4], const char* zrow, uint16_t* __restr
 // EPI_GLU with MXFP8 copies of a (see epi_glu).  Rows of a 32-row block
 // past the group's data but before its padded end get zero codes; a block
 // past the padded end is not touched (it belongs to the next group).
-template <int ACT>
+template <int ACT, bool F4OUT = false>
 MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz,
                          uint16_t* __restrict__ a, int64_t lda, const float (&pr)[4],
                          const ActP& act, const TileCtx& t, int wn, int wm, int lane,
@@ -749,7 +785,7 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
     const int64_t row = t.row0 + m;
     const int64_t rb = (t.row0 + blk) / 32;
     const float p = pr[mi];
-    const MxBase mb = mx_base(mo, row, rb, lane);
+    const MxBase mb = mx_base<F4OUT>(mo, row, rb, lane);
     if constexpr (gated) {
       if (wn * kWaveN < t.cols_valid) {
         const int q = (t.col0 + wn * kWaveN) / (2 * MOE_INTERLEAVE);
@@ -777,7 +813,7 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
           });
 #pragma unroll
           for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ab[r]));
-          if (blk_ok) mx_block_out(ab, mo, mb, tr, q * MOE_INTERLEAVE + h * 32, lane);
+          if (blk_ok) mx_block_out<F4OUT>(ab, mo, mb, tr, q * MOE_INTERLEAVE + h * 32, lane);
         });
       }
     } else {
@@ -803,7 +839,7 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
           });
 #pragma unroll
           for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ab[r]));
-          if (blk_ok) mx_block_out(ab, mo, mb, tr, cb, lane);
+          if (blk_ok) mx_block_out<F4OUT>(ab, mo, mb, tr, cb, lane);
         }
       });
     }
@@ -815,7 +851,7 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
 // EPI_DGLU with MXFP8 copies of dz, row block MI (see dglu_rows; pad rows
 // as in epi_glu_mx).  With the 64-column interleave a 32-column block of dz
 // holds only gate or only up columns.
-template <int ACT, int MI>
+template <int ACT, int MI, bool F4OUT = false>
 MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
                            uint16_t* __restrict__ dz, int64_t lddz, float p, const ActP& act,
                            const TileCtx& t, int wn, int wm, int lane, const MxOut& mo,
@@ -831,7 +867,7 @@ MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
   const bool blk_ok = blk < t.rows_pad;
   const int64_t row = t.row0 + m;
   const int64_t rb = (t.row0 + blk) / 32;
-  const MxBase mb = mx_base(mo, row, rb, lane);
+  const MxBase mb = mx_base<F4OUT>(mo, row, rb, lane);
   float dp = 0.0f;
   sfor<4>([&](auto ni) {
     if (wn * kWaveN + ni * 32 < t.cols_valid) {
@@ -888,10 +924,10 @@ MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
       if (blk_ok) {
         if constexpr (gated) {
           const int cbg = 2 * t.col0 + 256 * wn + 128 * (ni / 2) + 32 * (ni % 2);
-          mx_block_out(gv, mo, mb, tr, cbg, lane);
-          mx_block_out(uv, mo, mb, tr, cbg + MOE_INTERLEAVE, lane);
+          mx_block_out<F4OUT>(gv, mo, mb, tr, cbg, lane);
+          mx_block_out<F4OUT>(uv, mo, mb, tr, cbg + MOE_INTERLEAVE, lane);
         } else {
-          mx_block_out(gv, mo, mb, tr, t.col0 + 128 * wn + 32 * ni, lane);
+          mx_block_out<F4OUT>(gv, mo, mb, tr, t.col0 + 128 * wn + 32 * ni, lane);
         }
       }
     }
@@ -946,7 +982,7 @@ void grouped_gemm_kernel(GemmArgs g) {
   // and transposed reads, which do not shrink)
   constexpr bool kHalfTiles = (EPI == EPI_STORE || EPI == EPI_GLU) && !NN;
   static_assert(!(MX && NN), "MXFP8 operands are always K-contiguous");
-  static_assert(!F4 || (MX && EPI == EPI_STORE), "MXFP4 runs the plain-store GEMM");
+  static_assert(!F4 || (MX && EPI != EPI_WGRAD), "MXFP4: plain-store, GLU and dGLU GEMMs");
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[kStageBytes / 2], sA1[kStageBytes / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t sB0[kStageBytes / 2], sB1[kStageBytes / 2];
   constexpr int kScaleBytes = MX ? (F4 ? 2 * kStageS : kStageS) : 4;
@@ -957,7 +993,7 @@ void grouped_gemm_kernel(GemmArgs g) {
   __shared__ int s_tmp[kThreads / 64];
   __shared__ __attribute__((aligned(16))) float s_red[2 * BM];  // dprobs sums; the tile's bias
   // per-wave staging tiles of the transposed MXFP8 copies (MX epilogues)
-  constexpr int kTrWords = (MX && (EPI == EPI_GLU || EPI == EPI_DGLU)) ? 4 * kTrTile : 4;
+  constexpr int kTrWords = (MX && !F4 && (EPI == EPI_GLU || EPI == EPI_DGLU)) ? 4 * kTrTile : 4;
   __shared__ __attribute__((aligned(16))) uint16_t s_tr[kTrWords];
 
   const int tid = threadIdx.x;
@@ -1600,7 +1636,7 @@ void grouped_gemm_kernel(GemmArgs g) {
         TileCtx te = t;
         te.m_lane = (wave_e >> 1) * t.wrow + (lane_e & 31);
         te.n_lane = (wave_e & 1) * kWaveN + 4 * (lane_e >> 5);
-        amax = epi_glu_mx<ACT>(acc, g.C, g.ldc, g.act_out, g.ld_act, pr_tile, g.act, te,
+        amax = epi_glu_mx<ACT, F4>(acc, g.C, g.ldc, g.act_out, g.ld_act, pr_tile, g.act, te,
                                wave_e & 1, wave_e >> 1, lane_e, mo, s_tr + wave_e * kTrTile,
                                sb);
       } else
@@ -1675,7 +1711,7 @@ void grouped_gemm_kernel(GemmArgs g) {
         const char* zrow =
             reinterpret_cast<const char*>(wm_e ? zb : za) + (lane_e & 31) * kZRow;
         if constexpr (MX)
-          dp[MI] = dglu_rows_mx<ACT, MI>(acc, zrow, g.C, g.ldc, pr[MI], g.act, te, wn_e, wm_e,
+          dp[MI] = dglu_rows_mx<ACT, MI, F4>(acc, zrow, g.C, g.ldc, pr[MI], g.act, te, wn_e, wm_e,
                                          lane_e, mo, s_tr + wave_e * kTrTile, sb);
         else
           dp[MI] = dglu_rows<ACT, MI>(acc, zrow, g.C, g.ldc, pr[MI], g.act, te, wn_e, lane_e,
@@ -1734,21 +1770,21 @@ void grouped_gemm_kernel(GemmArgs g) {
 // Launch of one kernel family for the activation in g.act (SwiGLU with no
 // clamp and no linear offset takes its own instantiation when there is no
 // bias; a bias takes the instantiations flagged kActBias).
-template <int EPI, bool NN, bool MX, int BIAS>
+template <int EPI, bool NN, bool MX, int BIAS, bool F4 = false>
 hipError_t launch_act_b(const GemmArgs& g, int grid, hipStream_t s) {
   dim3 blk(kThreads), grd(grid);
   switch (g.act.act) {
     case MOE_ACT_SWIGLU:
       if (!BIAS && act_unclamped(g.act))
-        grouped_gemm_kernel<EPI, NN, kActSwigluFree, MX><<<grd, blk, 0, s>>>(g);
+        grouped_gemm_kernel<EPI, NN, kActSwigluFree, MX, F4><<<grd, blk, 0, s>>>(g);
       else
-        grouped_gemm_kernel<EPI, NN, MOE_ACT_SWIGLU | BIAS, MX><<<grd, blk, 0, s>>>(g);
+        grouped_gemm_kernel<EPI, NN, MOE_ACT_SWIGLU | BIAS, MX, F4><<<grd, blk, 0, s>>>(g);
       break;
     case MOE_ACT_GEGLU:
-      grouped_gemm_kernel<EPI, NN, MOE_ACT_GEGLU | BIAS, MX><<<grd, blk, 0, s>>>(g);
+      grouped_gemm_kernel<EPI, NN, MOE_ACT_GEGLU | BIAS, MX, F4><<<grd, blk, 0, s>>>(g);
       break;
     case MOE_ACT_SRELU:
-      grouped_gemm_kernel<EPI, NN, MOE_ACT_SRELU | BIAS, MX><<<grd, blk, 0, s>>>(g);
+      grouped_gemm_kernel<EPI, NN, MOE_ACT_SRELU | BIAS, MX, F4><<<grd, blk, 0, s>>>(g);
       break;
     default: return hipErrorInvalidValue;
   }
@@ -1759,6 +1795,15 @@ template <int EPI, bool NN, bool MX>
 hipError_t launch_act(const GemmArgs& g, int grid, hipStream_t s) {
   return g.bias ? launch_act_b<EPI, NN, MX, kActBias>(g, grid, s)
                 : launch_act_b<EPI, NN, MX, 0>(g, grid, s);
+}
+
+// MXFP4 operands with an activation epilogue (no bias)
+template <int EPI>
+hipError_t launch_act_f4(const GemmArgs& g_in, int grid, hipStream_t s) {
+  if (g_in.bias || g_in.mx_qT) return hipErrorInvalidValue;
+  GemmArgs g = g_in;
+  g.clk = gemm_clock_slot(grid);
+  return launch_act_b<EPI, false, true, 0, true>(g, grid, s);
 }
 
 }  // namespace

@@ -43,6 +43,33 @@ MOE_DEV uint32_t mx_codes4(float a, float b, float c, float d, float inv) {
 // their bit patterns).
 MOE_DEV uint32_t bf16_abs_bits(uint32_t b) { return b & 0x7fffu; }
 
+// ------------------------------------------------------------- MXFP4 ---
+// E2M1 values, one E8M0 scale per 32: e = clamp(floor(log2 max|v|) - 2,
+// -127, ...) (2 is the exponent of E2M1's largest value, 6), codes the
+// round-to-nearest-even E2M1 value of v / 2^e, saturated to +-6.  The
+// inputs are bf16 values, so v / 2^e is exact in fp32.
+
+MOE_DEV int mx4_exponent(float amax) {
+  const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 127 - 2;
+  return e < -127 ? -127 : e;
+}
+
+// E2M1 code of a scaled value, round to nearest even, 6 for |v| > 5: one
+// step up at each midpoint, ties (0.25, 1.25, 2.5, 5) staying on the even
+// code and (0.75, 1.75, 3.5) moving up to it.
+MOE_DEV uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+               (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// Four values times 2^-e -> four E2M1 codes, value i in nibble i.
+MOE_DEV uint32_t mx4_codes4(float a, float b, float c, float d, float inv) {
+  return e2m1_code(a * inv) | (e2m1_code(b * inv) << 4) | (e2m1_code(c * inv) << 8) |
+         (e2m1_code(d * inv) << 12);
+}
+
 // Byte offset of the scale of row r, K-block b in the tiled scale layout of
 // an [R][K] operand (see MOE_MX_BLOCK in moe_gmlp.h).
 MOE_DEV int64_t mx_scale_off(int64_t r, int64_t b, int64_t K) {

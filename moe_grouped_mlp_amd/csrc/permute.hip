@@ -24,12 +24,15 @@ constexpr int kRowsPerBlock = kBlock / kWave;
 // Each wave pushes one token row to its k rows.  With MXFP8 output the row
 // is encoded once (a quad of lanes holds one 32-value block: four 16-byte
 // chunks) and the same codes and scale go to every slot.
+// F4: the MX copy is MXFP4 (E2M1 codes two a byte, [M_cap][H / 2]) instead.
+template <bool F4>
 __global__ __launch_bounds__(kBlock) void gather_kernel(
     const i32x4* __restrict__ x, int T, int k, int H8, const int32_t* __restrict__ row_id_map,
     int64_t M_cap, i32x4* __restrict__ xp, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
     int tok_blocks, const int32_t* __restrict__ split, const int32_t* __restrict__ padded, int E) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int H = 8 * H8;
+  constexpr int kCodeBytes = F4 ? 4 : 8;   // code bytes of a lane's 8 values
   if (static_cast<int>(blockIdx.x) < tok_blocks) {
     for (int t = blockIdx.x * kRowsPerBlock + wave; t < T; t += tok_blocks * kRowsPerBlock) {
       int rows[kMaxTopK];
@@ -54,18 +57,29 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
           }
           m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 1, kWave)));
           m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 2, kWave)));
-          const int e = mx_exponent(__uint_as_float(m << 16));
+          const float am = __uint_as_float(m << 16);
+          const int e = F4 ? mx4_exponent(am) : mx_exponent(am);
           const float inv = mx_inv_scale(e);
-          uint2 q;
           const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
-          q.x = mx_codes4(__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xffff0000u),
-                          __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xffff0000u), inv);
-          q.y = mx_codes4(__uint_as_float(w2 << 16), __uint_as_float(w2 & 0xffff0000u),
-                          __uint_as_float(w3 << 16), __uint_as_float(w3 & 0xffff0000u), inv);
+          const float f[8] = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xffff0000u),
+                              __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xffff0000u),
+                              __uint_as_float(w2 << 16), __uint_as_float(w2 & 0xffff0000u),
+                              __uint_as_float(w3 << 16), __uint_as_float(w3 & 0xffff0000u)};
+          uint2 q;
+          if constexpr (F4) {
+            q.x = mx4_codes4(f[0], f[1], f[2], f[3], inv) |
+                  (mx4_codes4(f[4], f[5], f[6], f[7], inv) << 16);
+            q.y = 0;
+          } else {
+            q.x = mx_codes4(f[0], f[1], f[2], f[3], inv);
+            q.y = mx_codes4(f[4], f[5], f[6], f[7], inv);
+          }
 #pragma unroll
           for (int s = 0; s < kMaxTopK; ++s) {
             if (rows[s] < 0) continue;
-            *reinterpret_cast<uint2*>(xq + static_cast<int64_t>(rows[s]) * H + 8 * c) = q;
+            uint8_t* dst = xq + static_cast<int64_t>(rows[s]) * (H / (F4 ? 2 : 1)) + kCodeBytes * c;
+            if constexpr (F4) *reinterpret_cast<uint32_t*>(dst) = q.x;
+            else *reinterpret_cast<uint2*>(dst) = q;
             if ((c & 3) == 0) xs[mx_scale_off(rows[s], c >> 2, H)] = mx_scale_code(e);
           }
         }
@@ -84,7 +98,9 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
       for (int c = lane; c < H8; c += kWave) {
         if (xp) xp[r * H8 + c] = zero;
         if (xq) {
-          *reinterpret_cast<uint2*>(xq + r * H + 8 * c) = make_uint2(0, 0);
+          uint8_t* dst = xq + r * (H / (F4 ? 2 : 1)) + kCodeBytes * c;
+          if constexpr (F4) *reinterpret_cast<uint32_t*>(dst) = 0u;
+          else *reinterpret_cast<uint2*>(dst) = make_uint2(0, 0);
           if ((c & 3) == 0) xs[mx_scale_off(r, c >> 2, H)] = 0;
         }
       }
@@ -172,11 +188,17 @@ hipError_t launch_gather(const moe_permute_args& a, hipStream_t s) {
   const int H8 = a.H / 8;
   const int tok_blocks = blocks_for(a.T, 2048);
   const int pad_blocks = a.E < 256 ? a.E : 256;
-  gather_kernel<<<tok_blocks + pad_blocks, kBlock, 0, s>>>(
-      static_cast<const i32x4*>(a.x), a.T, a.k, H8, a.row_id_map, a.M_cap,
-      static_cast<i32x4*>(a.xp), (a.flags & MOE_PERMUTE_WRITE_MX) ? a.xp_q : nullptr,
-      (a.flags & MOE_PERMUTE_WRITE_MX) ? a.xp_s : nullptr, tok_blocks, a.split_sizes,
-      a.padded_offsets, a.E);
+  const bool mx8 = a.flags & MOE_PERMUTE_WRITE_MX, mx4 = a.flags & MOE_PERMUTE_WRITE_MX4;
+  if (mx4)
+    gather_kernel<true><<<tok_blocks + pad_blocks, kBlock, 0, s>>>(
+        static_cast<const i32x4*>(a.x), a.T, a.k, H8, a.row_id_map, a.M_cap,
+        static_cast<i32x4*>(a.xp), a.xp_q, a.xp_s, tok_blocks, a.split_sizes, a.padded_offsets,
+        a.E);
+  else
+    gather_kernel<false><<<tok_blocks + pad_blocks, kBlock, 0, s>>>(
+        static_cast<const i32x4*>(a.x), a.T, a.k, H8, a.row_id_map, a.M_cap,
+        static_cast<i32x4*>(a.xp), mx8 ? a.xp_q : nullptr, mx8 ? a.xp_s : nullptr, tok_blocks,
+        a.split_sizes, a.padded_offsets, a.E);
   return hipGetLastError();
 }
 

@@ -87,16 +87,6 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restri
   }
 }
 
-// E2M1 code of a scaled value |v| < 8, round to nearest even, 6 for (5, 8):
-// one step up at each midpoint, ties (0.25, 1.25, 2.5, 5) staying on the
-// even code and (0.75, 1.75, 3.5) moving up to it.
-MOE_DEV uint32_t e2m1_code(float v) {
-  const float a = fabsf(v);
-  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
-               (a >= 3.5f) + (a > 5.0f);
-  return c | ((__float_as_uint(v) >> 28) & 8u);
-}
-
 // Encodes 32 bf16 values (16 packed words) into 32 E2M1 codes (4 words,
 // element 2 i in the low nibble of byte i); returns the scale exponent
 // floor(log2 amax) - 2 (2 being the exponent of E2M1's largest value 6),

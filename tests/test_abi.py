@@ -487,3 +487,54 @@ def test_fwd_bwd_mx_validation():
         setattr(a, f, 64)
     a.dzT_s = 64
     assert _call("moe_grouped_mlp_bwd", a) == INVALID
+
+
+@no_device
+def test_permute_write_mx4_validation():
+    mx4 = B.PERMUTE_BUILD_MAP | B.PERMUTE_GATHER | B.PERMUTE_WRITE_MX4
+    ok = dict(flags=mx4, xp_q=64, xp_s=64, M_cap=640)
+    assert _call("moe_permute", _permute_args(**ok)) == DEVICE
+    assert _call("moe_permute", _permute_args(**{**ok, "xp": None})) == DEVICE
+    assert _call("moe_permute", _permute_args(**{**ok, "xp_q": None})) == INVALID
+    assert _call("moe_permute", _permute_args(**{**ok, "M_cap": 600})) == INVALID
+    assert _call("moe_permute", _permute_args(**{**ok, "H": 96})) == INVALID
+    # one MX format per call, and only with a gather
+    assert _call("moe_permute", _permute_args(
+        **{**ok, "flags": mx4 | B.PERMUTE_WRITE_MX})) == INVALID
+    assert _call("moe_permute", _permute_args(
+        **{**ok, "flags": B.PERMUTE_BUILD_MAP | B.PERMUTE_WRITE_MX4})) == INVALID
+
+
+@no_device
+def test_fwd_bwd_mxfp4_validation():
+    mx_fwd = ("xp_q", "xp_s", "w1_q", "w1_s", "w2_q", "w2_s", "a_q", "a_s")
+    base = {f: 64 for f in mx_fwd}
+    base.update(prec=B.PREC_MXFP4, xp=None, w1i=None, w2=None, a=None)
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(**base)) == DEVICE
+    for f in mx_fwd:
+        assert _call("moe_grouped_mlp_fwd", _fwd_args(**{**base, f: None})) == INVALID, f
+    # no transposed copy and no bias in MXFP4
+    assert _call("moe_grouped_mlp_fwd",
+                 _fwd_args(**{**base, "aT_q": 64, "aT_s": 64})) == INVALID
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(**{**base, "bias1": 64})) == INVALID
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(**{**base, "M_cap": 1000})) == INVALID
+
+    a = B.BwdArgs()
+    a.E, a.H, a.I, a.M_cap, a.prec = 4, 128, 256, 1024, B.PREC_MXFP4
+    a.act = B.act_params()
+    mx_bwd = ("dyp_q", "dyp_s", "w2t_q", "w2t_s", "w1t_q", "w1t_s", "dz_q", "dz_s")
+    for f in ("split_sizes", "padded_offsets", "probs_p", "z", "dprobs_p",
+              "dxp", "workspace") + mx_bwd:
+        setattr(a, f, 64)
+    a.workspace_bytes = B.moe_grouped_mlp_workspace_size(4, 128, 256, 1024,
+                                                         B.PREC_MXFP4)
+    assert _call("moe_grouped_mlp_bwd", a) == DEVICE
+    for f in mx_bwd:
+        setattr(a, f, None)
+        assert _call("moe_grouped_mlp_bwd", a) == INVALID, f
+        setattr(a, f, 64)
+    a.dzT_q, a.dzT_s = 64, 64
+    assert _call("moe_grouped_mlp_bwd", a) == INVALID
+    a.dzT_q = a.dzT_s = None
+    a.bias1 = 64
+    assert _call("moe_grouped_mlp_bwd", a) == INVALID

@@ -1,6 +1,7 @@
-"""The MXFP4 layer (ExpertBlock(prec=PREC_MXFP4): the unfused passes with
-every GEMM operand quantized by moe_quantize_mxfp4 and multiplied by the
-MXFP4 grouped GEMM) against the oracle's MXFP4 unfused reading.  Where a
+"""The unfused MXFP4 layer (ExpertBlock(prec=PREC_MXFP4, unfused=True): the
+separate passes with every GEMM operand quantized by moe_quantize_mxfp4 and
+multiplied by the MXFP4 grouped GEMM) against the oracle's MXFP4 unfused
+reading.  Where a
 GEMM reads the MXFP4 encoding of a tensor the GPU computed (a for FC2, dz
 for FC1 dgrad), a one-ulp difference in that bf16 tensor can move an E2M1
 code by a whole step; those outputs are checked element by element against
@@ -42,7 +43,7 @@ def test_mxfp4_layer_parity(case):
     M_cap = -(-wl.m_cap() // 128) * 128
     gp, _ = act_of(wl)
     blk = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, act=gp, first_expert=wl.first_expert,
-                         M_cap=M_cap, prec=mg.PREC_MXFP4)
+                         M_cap=M_cap, prec=mg.PREC_MXFP4, unfused=True)
     run_gpu_layer(wl, M_cap, block=blk)
     fw, bw = oracle_layer(wl, M_cap, mx="mxfp4", unfused=True)
     compare_routing(blk, fw.rt)
@@ -142,9 +143,10 @@ def _graph_replays_match_eager(blk, wl, rows_tensors):
             assert torch.equal(t, e), f"output {i} differs on a replay"
 
 
-def test_mxfp4_layer_graph_capture_replays_match_eager():
+@pytest.mark.parametrize("unfused", [True, False])
+def test_mxfp4_layer_graph_capture_replays_match_eager(unfused):
     wl = make_workload("tiny", seed=13, E=8, T=1024, H=256, I=256)
-    blk = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, prec=mg.PREC_MXFP4)
+    blk = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, prec=mg.PREC_MXFP4, unfused=unfused)
     _graph_replays_match_eager(blk, wl, ("yp", "dxp"))
 
 
