@@ -424,17 +424,35 @@ MOE_DEV void mx_row_block(const float (&v)[16], uint8_t* q_lane, uint8_t* s_byte
 // halves are exchanged with the partner (v_permlane32_swap) so that the low
 // lane stores the words of columns 0 .. 15 and the high lane 16 .. 31
 // (8 bytes each, q_lane = the block's row start + 8 hf).
-MOE_DEV void mx4_row_block(const float (&v)[16], uint8_t* q_lane, uint8_t* s_byte, int hf) {
-  float am = 0.0f;
+//
+// The values come as the packed bf16 words the epilogue computed (w[rg]:
+// columns 8 rg + 4 hf .. + 3), so the block maximum is taken on the bit
+// patterns (bf16 magnitudes order like unsigned integers) and the codes come
+// from the hardware's scaled conversion of the packed words.  Returns the
+// block maximum as a bf16 magnitude pattern.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+MOE_DEV uint32_t bf16_amax_bits(const uint2 (&w)[4]) {
+  u16x2_t m = {0, 0};
 #pragma unroll
-  for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(v[r]));
-  am = fmaxf(am, partner32(am, hf));
-  const int e = mx4_exponent(am);
-  const float inv = mx_inv_scale(e);
+  for (int rg = 0; rg < 4; ++rg) {
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w[rg].x & 0x7fff7fffu));
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w[rg].y & 0x7fff7fffu));
+  }
+  return m.x > m.y ? m.x : m.y;
+}
+
+MOE_DEV uint32_t mx4_row_block(const uint2 (&w)[4], uint8_t* q_lane, uint8_t* s_byte, int hf) {
+  uint32_t am = bf16_amax_bits(w);
+  const auto pa = __builtin_amdgcn_permlane32_swap(am, am, false, false);
+  const uint32_t block_am = max(am, hf ? pa[0] : pa[1]);
+  // floor(log2) of the block maximum from its exponent field, minus 2
+  int e = static_cast<int>(block_am >> 7) - 127 - 2;
+  e = e < -127 ? -127 : e;
+  const float scale = mx_scale_f32(e);
   uint32_t h[4];
 #pragma unroll
-  for (int rg = 0; rg < 4; ++rg)
-    h[rg] = mx4_codes4(v[4 * rg], v[4 * rg + 1], v[4 * rg + 2], v[4 * rg + 3], inv);
+  for (int rg = 0; rg < 4; ++rg) h[rg] = mx4_codes4_bf16(w[rg], scale);
   // a = (h0, h1), b = (h2, h3); after the swap the low lane holds its own a
   // and the partner's a in b, the high lane the partner's b in a and its own b
   const auto sw = __builtin_amdgcn_permlane32_swap(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
@@ -443,6 +461,7 @@ MOE_DEV void mx4_row_block(const float (&v)[16], uint8_t* q_lane, uint8_t* s_byt
   *reinterpret_cast<uint2*>(q_lane) =
       make_uint2((lo & 0xffffu) | (hi << 16), (lo >> 16) | (hi & 0xffff0000u));
   if (hf == 0) *s_byte = mx_scale_code(e);
+  return am;
 }
 
 // Transposed: column c of the block is one MX block of the transposed copy
@@ -524,19 +543,21 @@ MOE_DEV MxBase mx_base(const MxOut& o, int64_t row, int64_t rb, int lane) {
 // of a row block whose rows all lie before the group's padded end.  With
 // col0 a multiple of 32, the tiled scale offsets of (row, col0 / 32) and
 // (col0 + lane % 32, rb) are those of block 0 plus terms in col0 alone.
-// F4OUT: MXFP4 rowwise codes ([M_cap][n / 2]) and no transposed copy.
-template <bool F4OUT = false>
 MOE_DEV void mx_block_out(const float (&v)[16], const MxOut& o, const MxBase& b, uint16_t* tr,
                           int col0, int lane) {
   uint8_t* const sb = b.s + (col0 >> 6) * 64 + ((col0 >> 5) & 1) * 32;
-  if constexpr (F4OUT) {
-    mx4_row_block(v, b.q + col0 / 2, sb, lane >> 5);
-    return;
-  }
   mx_row_block(v, b.q + col0, sb, lane >> 5);
   if (o.qT)
     mx_col_block(v, tr, b.qT + static_cast<int64_t>(col0) * o.M_cap,
                  b.sT + static_cast<int64_t>(col0 >> 5) * (o.M_cap >> 6) * 64, lane);
+}
+
+// MXFP4 (rowwise codes [M_cap][n / 2], no transposed copy) of the same
+// block from the lane's packed bf16 words; returns the lane's maximum as a
+// bf16 magnitude pattern.
+MOE_DEV uint32_t mx4_block_out(const uint2 (&w)[4], const MxBase& b, int col0, int lane) {
+  uint8_t* const sb = b.s + (col0 >> 6) * 64 + ((col0 >> 5) & 1) * 32;
+  return mx4_row_block(w, b.q + col0 / 2, sb, lane >> 5);
 }
 
 MOE_DEV void bf16x4_to_f32(uint2 w, float* v) {
@@ -775,6 +796,7 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
   constexpr bool gated = ACT != MOE_ACT_SRELU;
   const int hf = lane >> 5;
   float amax = 0.0f;
+  uint32_t am4 = 0;   // MXFP4: the lane's max |a| as a bf16 magnitude pattern
   sfor<4>([&](auto mi) {
     sfor<4>([&](auto ni) { acc_hold(acc[mi][ni]); });
     if (mi >= t.mi_n) return;   // a half-height tile's waves own two row blocks
@@ -791,6 +813,7 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
         const int q = (t.col0 + wn * kWaveN) / (2 * MOE_INTERLEAVE);
         sfor<2>([&](auto h) {
           float ab[16];
+          uint2 wb[4];
           sfor<4>([&](auto rg) {
             const int c = h * 32 + 8 * rg + 4 * hf;
             if (row_ok && z) {
@@ -809,11 +832,18 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
             if (!row_ok) w = make_uint2(0, 0);
             if (row_ok && a)
               *reinterpret_cast<uint2*>(a + row * lda + q * MOE_INTERLEAVE + c) = w;
-            bf16x4_to_f32(w, &ab[4 * rg]);
+            if constexpr (F4OUT) wb[rg] = w;
+            else bf16x4_to_f32(w, &ab[4 * rg]);
           });
+          if constexpr (F4OUT) {
+            // rows past the padded end hold no data (zeros), so skipping
+            // them leaves the maximum unchanged
+            if (blk_ok) am4 = max(am4, mx4_block_out(wb, mb, q * MOE_INTERLEAVE + h * 32, lane));
+          } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ab[r]));
-          if (blk_ok) mx_block_out<F4OUT>(ab, mo, mb, tr, q * MOE_INTERLEAVE + h * 32, lane);
+            for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ab[r]));
+            if (blk_ok) mx_block_out(ab, mo, mb, tr, q * MOE_INTERLEAVE + h * 32, lane);
+          }
         });
       }
     } else {
@@ -821,6 +851,7 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
         if (wn * kWaveN + ni * 32 < t.cols_valid) {
           const int cb = t.col0 + wn * kWaveN + ni * 32;
           float ab[16];
+          uint2 wb[4];
           sfor<4>([&](auto rg) {
             const int n = cb + 8 * rg + 4 * hf;
             if (row_ok && z) store_bf16x4(z + row * ldz + n, acc[mi][ni], 4 * rg);
@@ -835,16 +866,22 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
             uint2 w = make_uint2(pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]));
             if (!row_ok) w = make_uint2(0, 0);
             if (row_ok && a) *reinterpret_cast<uint2*>(a + row * lda + n) = w;
-            bf16x4_to_f32(w, &ab[4 * rg]);
+            if constexpr (F4OUT) wb[rg] = w;
+            else bf16x4_to_f32(w, &ab[4 * rg]);
           });
+          if constexpr (F4OUT) {
+            if (blk_ok) am4 = max(am4, mx4_block_out(wb, mb, cb, lane));
+          } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ab[r]));
-          if (blk_ok) mx_block_out<F4OUT>(ab, mo, mb, tr, cb, lane);
+            for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ab[r]));
+            if (blk_ok) mx_block_out(ab, mo, mb, tr, cb, lane);
+          }
         }
       });
     }
     __builtin_amdgcn_sched_barrier(0);
   });
+  if constexpr (F4OUT) amax = __uint_as_float(am4 << 16);
   return amax;
 }
 
@@ -872,6 +909,7 @@ MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
   sfor<4>([&](auto ni) {
     if (wn * kWaveN + ni * 32 < t.cols_valid) {
       float gv[16], uv[16];
+      uint2 gw[4], uw[4];   // MXFP4: the packed words themselves
       sfor<4>([&](auto rg) {
         float gz[4];
         if constexpr (gated) {
@@ -900,8 +938,13 @@ MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
             *reinterpret_cast<uint2*>(db + off) = wg;
             *reinterpret_cast<uint2*>(db + off + MOE_INTERLEAVE) = wu;
           }
-          bf16x4_to_f32(wg, &gv[4 * rg]);
-          bf16x4_to_f32(wu, &uv[4 * rg]);
+          if constexpr (F4OUT) {
+            gw[rg] = wg;
+            uw[rg] = wu;
+          } else {
+            bf16x4_to_f32(wg, &gv[4 * rg]);
+            bf16x4_to_f32(wu, &uv[4 * rg]);
+          }
         } else {
           constexpr int off = 32 * ni + 8 * rg;
           bf16x4_to_f32(zread(zb, r16, 4 * ni + rg), gz);
@@ -918,16 +961,23 @@ MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
           uint2 w = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
           if (!row_ok) w = make_uint2(0, 0);
           if (row_ok && dz) *reinterpret_cast<uint2*>(dz + row * lddz + lane_col + off) = w;
-          bf16x4_to_f32(w, &gv[4 * rg]);
+          if constexpr (F4OUT) gw[rg] = w;
+          else bf16x4_to_f32(w, &gv[4 * rg]);
         }
       });
       if (blk_ok) {
         if constexpr (gated) {
           const int cbg = 2 * t.col0 + 256 * wn + 128 * (ni / 2) + 32 * (ni % 2);
-          mx_block_out<F4OUT>(gv, mo, mb, tr, cbg, lane);
-          mx_block_out<F4OUT>(uv, mo, mb, tr, cbg + MOE_INTERLEAVE, lane);
+          if constexpr (F4OUT) {
+            mx4_block_out(gw, mb, cbg, lane);
+            mx4_block_out(uw, mb, cbg + MOE_INTERLEAVE, lane);
+          } else {
+            mx_block_out(gv, mo, mb, tr, cbg, lane);
+            mx_block_out(uv, mo, mb, tr, cbg + MOE_INTERLEAVE, lane);
+          }
         } else {
-          mx_block_out<F4OUT>(gv, mo, mb, tr, t.col0 + 128 * wn + 32 * ni, lane);
+          if constexpr (F4OUT) mx4_block_out(gw, mb, t.col0 + 128 * wn + 32 * ni, lane);
+          else mx_block_out(gv, mo, mb, tr, t.col0 + 128 * wn + 32 * ni, lane);
         }
       }
     }

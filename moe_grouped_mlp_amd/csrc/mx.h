@@ -64,6 +64,26 @@ MOE_DEV uint32_t e2m1_code(float v) {
   return c | ((__float_as_uint(v) >> 28) & 8u);
 }
 
+// 2^e as an fp32, exactly (2^-127 as the subnormal it is): the scale
+// operand of gfx950's scaled conversions, which divide by it.
+MOE_DEV float mx_scale_f32(int e) {
+  return e > -127 ? __uint_as_float(static_cast<uint32_t>(e + 127) << 23)
+                  : __uint_as_float(0x00400000u);
+}
+
+// Four bf16 values (two packed words, value 0 in the low half of w.x)
+// divided by 2^e -> four E2M1 codes in the low 16 bits, value i in nibble
+// i: v_cvt_scalef32_pk_fp4_bf16, which divides by the scale, rounds to
+// nearest even and saturates at +-6 with the sign kept, the block rule
+// above (a bf16 value over a power of two is exact, so its one rounding is
+// the conversion's).
+MOE_DEV uint32_t mx4_codes4_bf16(uint2 w, float scale) {
+  const uint32_t c =
+      __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2_t, w.x), scale, 0);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(bf16x2_t, w.y), scale,
+                                                   1);
+}
+
 // Four values times 2^-e -> four E2M1 codes, value i in nibble i.
 MOE_DEV uint32_t mx4_codes4(float a, float b, float c, float d, float inv) {
   return e2m1_code(a * inv) | (e2m1_code(b * inv) << 4) | (e2m1_code(c * inv) << 8) |
