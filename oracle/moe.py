@@ -481,10 +481,11 @@ def weight_grads(fw: Forward, bw: Backward, *, mx=False, exact=False):
         dW2[e] = sum_r dYp[r]^T a[r]     [H][I]
 
     from the stored dZ, Xp, dYp and a, each result rounded to bf16 once.
-    With mx every operand is its MXFP8 copy blocked along the routed rows,
-    the contraction axis, with blocks starting at the group's padded start
-    (the transposed copies of [FK § Fused MXFP8 and NVFP4 quantization]);
-    pad rows hold zeros.  exact skips the rounding (finite-difference pins).
+    With mx every operand is its MXFP8 copy (mx="mxfp4": its MXFP4 copy)
+    blocked along the routed rows, the contraction axis, with blocks
+    starting at the group's padded start (the transposed copies of [FK §
+    Fused MXFP8 and NVFP4 quantization]); pad rows hold zeros.  exact skips
+    the rounding (finite-difference pins).
     """
     rnd = not exact
     rt = fw.rt
@@ -499,9 +500,9 @@ def weight_grads(fw: Forward, bw: Backward, *, mx=False, exact=False):
         span = slice(s0, s0 + -(-n // ALIGN) * ALIGN)   # zero past row n
         dz, xp = bw.dz[span], fw.xp[span]
         dy, a = bw.dyp[span], fw.a[span]
-        on = mx and rnd
-        dw1[e] = _maybe_bf16(_mx_operand(dz, 0, on).T @ _mx_operand(xp, 0, on), rnd)
-        dw2[e] = _maybe_bf16(_mx_operand(dy, 0, on).T @ _mx_operand(a, 0, on), rnd)
+        fmt = _operand_format(mx, rnd)
+        dw1[e] = _maybe_bf16(_mx_operand(dz, 0, fmt).T @ _mx_operand(xp, 0, fmt), rnd)
+        dw2[e] = _maybe_bf16(_mx_operand(dy, 0, fmt).T @ _mx_operand(a, 0, fmt), rnd)
     return dw1, dw2
 
 

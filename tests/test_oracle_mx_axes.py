@@ -245,7 +245,8 @@ def _expected_wgrads(fw, bw):
     return nu.round_bf16(dw1), nu.round_bf16(dw2)
 
 
-def test_weight_grad_operands_blocked_along_routed_rows():
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_weight_grad_operands_blocked_along_routed_rows(fmt):
     """Every weight-gradient operand is blocked along the routed rows (the
     contraction axis): magnitudes alternating along the columns leave that
     blocking exact and would not survive blocks along the columns."""
@@ -255,12 +256,13 @@ def test_weight_grad_operands_blocked_along_routed_rows():
                          lambda c: SMALL if c % 2 else 1.0)
     assert _lossy(bw.dz, 1) and _lossy(fw.xp, 1)
     exp1, exp2 = _expected_wgrads(fw, bw)
-    got1, got2 = moe.weight_grads(fw, bw, mx=True)
+    got1, got2 = moe.weight_grads(fw, bw, mx=fmt)
     np.testing.assert_array_equal(got1, exp1)
     np.testing.assert_array_equal(got2, exp2)
 
 
-def test_weight_grad_blocks_start_at_the_padded_group_start():
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_weight_grad_blocks_start_at_the_padded_group_start(fmt):
     """Blocks of 32 rows start at each group's padded start: magnitudes
     constant over rows [s0 + 32 j, s0 + 32 j + 32) and alternating with j
     are exact in those blocks.  The unpadded offsets (45, 115, 115) are not
@@ -282,19 +284,50 @@ def test_weight_grad_blocks_start_at_the_padded_group_start():
     seg = bw.dz[s1 - shift:s1 - shift + 64]
     assert _lossy(seg, 0)
     exp1, exp2 = _expected_wgrads(fw, bw)
-    got1, got2 = moe.weight_grads(fw, bw, mx=True)
+    got1, got2 = moe.weight_grads(fw, bw, mx=fmt)
     np.testing.assert_array_equal(got1, exp1)
     np.testing.assert_array_equal(got2, exp2)
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("n", [1, 31, 33, 95])
-def test_weight_grad_partial_last_block(n):
+def test_weight_grad_partial_last_block(n, fmt):
     """A group whose size is not a multiple of 32 ends in a partial block
     filled with the zero pad rows; it is still exact."""
     rng = np.random.default_rng(7 + n)
     _, _, rt = _routing([n, 50], 17 + n)
     fw, bw = _wgrad_case(rt, rng, lambda r: 1.0, lambda c: 1.0)
     exp1, exp2 = _expected_wgrads(fw, bw)
-    got1, got2 = moe.weight_grads(fw, bw, mx=True)
+    got1, got2 = moe.weight_grads(fw, bw, mx=fmt)
     np.testing.assert_array_equal(got1, exp1)
     np.testing.assert_array_equal(got2, exp2)
+
+
+def test_weight_grads_mxfp4_rounds_its_operands_on_the_e2m1_grid():
+    """mx="mxfp4" encodes the weight-gradient operands in E2M1, not E4M3:
+    with dz and dyp entries of magnitude 1.25 in blocks whose largest value
+    is 1.25, the block scale is 2^(0 - 2) and the E2M1 grid around 1.25 is
+    {1, 1.5} (4 and 6 times the scale): 1.25 is the midpoint and rounds to
+    the even code, 1.  MXFP8 carries 1.25 exactly (E4M3 has 3 mantissa
+    bits).  The expected gradients are the sums over each group's rows with
+    1.25 replaced by 1 (MXFP4) or kept (MXFP8)."""
+    rng = np.random.default_rng(8)
+    _, _, rt = _routing([40, 70], 18)
+    fw, bw = _wgrad_case(rt, rng, lambda r: 1.0, lambda c: 1.0)
+    valid = moe.expert_of_rows(rt) >= 0
+    for t in (bw.dz, bw.dyp):
+        sign = np.sign(t)
+        t[valid] = sign[valid] * 1.25       # every routed value is +-1.25
+    exp8 = _expected_wgrads(fw, bw)
+    got8 = moe.weight_grads(fw, bw, mx=True)
+    np.testing.assert_array_equal(got8[0], exp8[0])
+    np.testing.assert_array_equal(got8[1], exp8[1])
+    # xp and a are +-1 or +-2 (exact in E2M1 with any block maximum of 1 or 2)
+    dz4, dy4 = bw.dz.copy(), bw.dyp.copy()
+    bw.dz, bw.dyp = np.sign(dz4) * np.minimum(np.abs(dz4), 1.0), np.sign(dy4) * np.minimum(np.abs(dy4), 1.0)
+    exp4 = _expected_wgrads(fw, bw)
+    bw.dz, bw.dyp = dz4, dy4
+    got4 = moe.weight_grads(fw, bw, mx="mxfp4")
+    np.testing.assert_array_equal(got4[0], exp4[0])
+    np.testing.assert_array_equal(got4[1], exp4[1])
+    assert not np.array_equal(got4[0], got8[0])
