@@ -643,9 +643,9 @@ def measure(args, config, prec, log_prefix=""):
         q = (2 * 2 + 2 * (1 + 1 / 32)) if mx else 0.0
         mem["act_fwd"] = M * n1 * 2 + M * I * 2 + M * I * q
         mem["act_bwd"] = M * I * 2 + 2 * M * n1 * 2 + M * 4 + M * n1 * q
-    if args.wgrad and mx:
-        # MXFP8 transposed copies of Xp and dYp (bf16 in, codes + scales out)
-        mem["wgrad_quantize"] = 2 * M * H * (2 + 1 + 1 / 32)
+    if args.wgrad and (mx or prec == "mxfp4"):
+        # MX transposed copies of Xp and dYp (bf16 in, codes + scales out)
+        mem["wgrad_quantize"] = 2 * M * H * (2 + (1 if mx else 0.5) + 1 / 32)
     for name, b in mem.items():
         kernels[name] = {"ms": round(seg_ms[name], 4), "unit": "GB/s",
                          "rate": round(b / (seg_ms[name] * 1e-3) / 1e9, 1)}

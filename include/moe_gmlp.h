@@ -336,8 +336,10 @@ moe_status moe_quantize_mxfp4(const moe_quant_args* args, void* stream);
  *   MXFP4 block rule: xp_q/xp_s (moe_permute WRITE_MX4), w1_q/w1_s and
  *   w2_q/w2_s (moe_quantize_mxfp4 ROW of w1i and w2).  The FC1 epilogue
  *   writes a_q/a_s, the MXFP4 copy of the stored bf16 a blocked along I
- *   (codes [M_cap][I / 2]).  No transposed copy (aT_q and aT_s must be
- *   NULL) and no bias (bias1 NULL), else MOE_ERR_INVALID_ARG.
+ *   (codes [M_cap][I / 2]) and, when aT_q is set, aT_q/aT_s, its MXFP4
+ *   transposed copy blocked along M (codes [I][M_cap / 2], pad rows as
+ *   zeros), the operand of the MXFP4 weight gradient.  No bias (bias1
+ *   NULL), else MOE_ERR_INVALID_ARG.
  * ---------------------------------------------------------------------- */
 typedef struct moe_fwd_args {
   int32_t E, H, I;
@@ -412,8 +414,9 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* args, void* stream);
  *   prec == MOE_PREC_MXFP4: as MXFP8 with MXFP4 operands (see the forward):
  *   dyp_q/dyp_s (moe_permute WRITE_MX4 of dOut), w2t_q/w2t_s and
  *   w1t_q/w1t_s (moe_quantize_mxfp4 COL of w2 and w1i), and the epilogue's
- *   dz_q/dz_s, the MXFP4 copy of the stored bf16 dz blocked along N1.  No
- *   transposed copy (dzT_q, dzT_s NULL), no bias.
+ *   dz_q/dz_s, the MXFP4 copy of the stored bf16 dz blocked along N1, and
+ *   optionally dzT_q/dzT_s, its transposed MXFP4 copy [N1][M_cap / 2]
+ *   blocked along M.  No bias.
  * ---------------------------------------------------------------------- */
 typedef struct moe_bwd_args {
   int32_t E, H, I;
@@ -494,8 +497,14 @@ moe_status moe_grouped_mlp_bwd_noalloc(const moe_bwd_args* args, void* stream);
  *       M_cap).  Columns [padded_offsets[e], padded_offsets[e + 1]) belong to
  *       expert e and are read whole, so the pad rows there must encode zero
  *       (as the producers above write them).
+ *     prec == MOE_PREC_MXFP4: the same transposed copies in MXFP4, E2M1
+ *       codes two a byte ([n][M_cap / 2], element 2 i in the low nibble of
+ *       byte i) blocked along M with the MXFP4 block rule: aT_q / dzT_q
+ *       from the MXFP4 forward / backward, xpT_q and dypT_q from
+ *       moe_quantize_mxfp4 (MOE_QUANT_COL).  Expert e's codes are read from
+ *       its first row on, up to its split_sizes[e] rows rounded up to 32.
  *   dw1 or dw2 may be NULL to skip that GEMM; the caller owns every buffer.
- *   Needs M_cap <= 4194304 (MXFP8: M_cap % 128 == 0); H, I multiples of 64.
+ *   Needs M_cap <= 4194304 (MX: M_cap % 128 == 0); H, I multiples of 64.
  *   Invalid arguments return MOE_ERR_INVALID_ARG before any launch.
  *   timing_events: optional hipEvent_t handles recorded before dw1, between,
  *   and after dw2.
@@ -509,10 +518,10 @@ typedef struct moe_wgrad_args {
   const int32_t* split_sizes;     /* [E]   device */
   const int32_t* padded_offsets;  /* [E+1] device */
   const void* dz;  const void* xp;  const void* dyp;  const void* a;   /* bf16 */
-  const uint8_t* dzT_q;  const uint8_t* dzT_s;    /* MXFP8 [N1][M_cap] */
-  const uint8_t* xpT_q;  const uint8_t* xpT_s;    /* MXFP8 [H][M_cap]  */
-  const uint8_t* dypT_q; const uint8_t* dypT_s;   /* MXFP8 [H][M_cap]  */
-  const uint8_t* aT_q;   const uint8_t* aT_s;     /* MXFP8 [I][M_cap]  */
+  const uint8_t* dzT_q;  const uint8_t* dzT_s;    /* MX [N1][M_cap] (MXFP4: M_cap / 2 bytes a row) */
+  const uint8_t* xpT_q;  const uint8_t* xpT_s;    /* MX [H][M_cap]  */
+  const uint8_t* dypT_q; const uint8_t* dypT_s;   /* MX [H][M_cap]  */
+  const uint8_t* aT_q;   const uint8_t* aT_s;     /* MX [I][M_cap]  */
   void* dw1;                      /* bf16 [E][N1][H] or NULL */
   void* dw2;                      /* bf16 [E][H][I] or NULL  */
   void* timing_events[3];

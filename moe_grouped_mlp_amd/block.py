@@ -24,9 +24,11 @@ dYp with moe_quantize_mxfp8 (the permutes then also keep bf16 Xp and dYp).
 
 With prec=PREC_MXFP4 the layer is fused the same way with MXFP4 operands:
 the permutes write MXFP4 rows, the GLU and dGLU epilogues write the MXFP4
-copies of a and dz, and quantize_weights() makes the four MXFP4 weight
-copies (rowwise and, for the dgrads, along N1 / H).  No transposed copies,
-weight-gradient, recompute or bias path.  unfused=True runs the same layer
+copies of a and dz (rowwise and transposed), quantize_weights() makes the
+four MXFP4 weight copies (rowwise and, for the dgrads, along N1 / H), and
+weight_grads() runs the MXFP4 weight-gradient GEMMs on the transposed
+copies (those of Xp and dYp made by moe_quantize_mxfp4).  No bias path.
+unfused=True runs the same layer
 as separate passes instead (bf16 permutes and activation passes,
 moe_quantize_mxfp4 before each of the four grouped GEMMs): the baseline the
 fused path is measured against, which needs the bf16 copies.
@@ -110,8 +112,8 @@ class ExpertBlock:
         mx_any = self.mx or self.mx4
         keep = ((not mx_any or unfused) if bf16_copies is None
                 else (bf16_copies or not mx_any))
-        if self.mx4 and (wgrad or recompute):
-            raise ValueError("the MXFP4 layer has no weight-gradient or recompute path")
+        if self.mx4 and unfused and (wgrad or recompute):
+            raise ValueError("the unfused MXFP4 layer has no weight-gradient or recompute path")
         if recompute:
             # z exists only while the backward runs (see recompute_z)
             if z_scratch is not None:
@@ -175,20 +177,30 @@ class ExpertBlock:
             self.a_q4, self.a_s4 = fp4_pair(M, I)
             self.dyp_q4, self.dyp_s4 = fp4_pair(M, H)
             self.dz_q4, self.dz_s4 = fp4_pair(M, N1)
+            if transposed_copies and not unfused:
+                self.aT_q4, self.aT_s4 = fp4_pair(I, M)      # along M
+                self.dzT_q4, self.dzT_s4 = fp4_pair(N1, M)
+            else:
+                self.aT_q4 = self.aT_s4 = self.dzT_q4 = self.dzT_s4 = None
             self.w1_q4, self.w1_s4 = fp4_pair(E, N1, H)     # along H
             self.w2_q4, self.w2_s4 = fp4_pair(E, H, I)      # along I
             self.w2t_q4, self.w2t_s4 = fp4_pair(E, I, H)    # along H
             self.w1t_q4, self.w1t_s4 = fp4_pair(E, H, N1)   # along N1
         self.wgrad = wgrad
         if wgrad:
-            if self.mx:
+            if self.mx or self.mx4:
                 if not transposed_copies:
-                    raise ValueError("MXFP8 weight gradients read the transposed "
+                    raise ValueError("MX weight gradients read the transposed "
                                      "copies of a and dz (transposed_copies=True)")
-                self.xp = torch.empty(M, H, **bf)
-                self.dyp = torch.empty(M, H, **bf)
+                if self.xp is None:
+                    self.xp = torch.empty(M, H, **bf)
+                    self.dyp = torch.empty(M, H, **bf)
+            if self.mx:
                 self.xpT_q, self.xpT_s = mx_pair(H, M)
                 self.dypT_q, self.dypT_s = mx_pair(H, M)
+            elif self.mx4:
+                self.xpT_q4, self.xpT_s4 = fp4_pair(H, M)
+                self.dypT_q4, self.dypT_s4 = fp4_pair(H, M)
             self.dw1 = torch.empty(E, N1, H, **bf)
             self.dw2 = torch.empty(E, H, I, **bf)
 
@@ -324,7 +336,7 @@ class ExpertBlock:
         elif self.mx4:
             kw = dict(xp_q=self.xp_q4, xp_s=self.xp_s4, w1_q=self.w1_q4,
                       w1_s=self.w1_s4, w2_q=self.w2_q4, w2_s=self.w2_s4,
-                      a_q=self.a_q4, a_s=self.a_s4)
+                      a_q=self.a_q4, a_s=self.a_s4, aT_q=self.aT_q4, aT_s=self.aT_s4)
         else:
             kw = dict(xp=self.xp, w1i=self.w1i, w2=self.w2)
         B.moe_grouped_mlp_fwd(E=self.E, H=self.H, I=self.I, M_cap=self.M_cap,
@@ -349,10 +361,13 @@ class ExpertBlock:
                                                                                self.N1)
             else:
                 self.z = torch.empty(self.M_cap, self.N1, dtype=torch.bfloat16,
-                                     device=self.xp_q.device if self.mx else self.xp.device)
+                                     device=self.yp.device)
         if self.mx:
             self._gemm(self.N1, self.H, self.xp_q, self.w1_q, self.z, self.xp_s,
                        self.w1_s, split=False)
+        elif self.mx4:
+            self._gemm(self.N1, self.H, self.xp_q4, self.w1_q4, self.z, self.xp_s4,
+                       self.w1_s4, split=False)
         else:
             self._gemm(self.N1, self.H, self.xp, self.w1i, self.z, split=False)
         self._z_valid = True
@@ -392,7 +407,8 @@ class ExpertBlock:
         elif self.mx4:
             kw = dict(dyp_q=self.dyp_q4, dyp_s=self.dyp_s4, w2t_q=self.w2t_q4,
                       w2t_s=self.w2t_s4, w1t_q=self.w1t_q4, w1t_s=self.w1t_s4,
-                      dz_q=self.dz_q4, dz_s=self.dz_s4)
+                      dz_q=self.dz_q4, dz_s=self.dz_s4, dzT_q=self.dzT_q4,
+                      dzT_s=self.dzT_s4)
         else:
             kw = dict(dyp=self.dyp, w2=self.w2, w1i=self.w1i)
         B.moe_grouped_mlp_bwd(E=self.E, H=self.H, I=self.I, M_cap=self.M_cap,
@@ -527,6 +543,14 @@ class ExpertBlock:
             kw = dict(dzT_q=self.dzT_q, dzT_s=self.dzT_s, xpT_q=self.xpT_q,
                       xpT_s=self.xpT_s, dypT_q=self.dypT_q, dypT_s=self.dypT_s,
                       aT_q=self.aT_q, aT_s=self.aT_s)
+        elif self.mx4:
+            for src, q, s in ((self.xp, self.xpT_q4, self.xpT_s4),
+                              (self.dyp, self.dypT_q4, self.dypT_s4)):
+                B.moe_quantize_mxfp4(mode=B.QUANT_COL, batch=1, rows=self.M_cap,
+                                     cols=self.H, x=src, q=q, s=s)
+            kw = dict(dzT_q=self.dzT_q4, dzT_s=self.dzT_s4, xpT_q=self.xpT_q4,
+                      xpT_s=self.xpT_s4, dypT_q=self.dypT_q4, dypT_s=self.dypT_s4,
+                      aT_q=self.aT_q4, aT_s=self.aT_s4)
         else:
             kw = dict(dz=self.dz, xp=self.xp, dyp=self.dyp, a=self.a)
         B.moe_grouped_mlp_wgrad(E=self.E, H=self.H, I=self.I, M_cap=self.M_cap,

@@ -22,7 +22,8 @@ LIB = os.path.join(HERE, "libmoe_gmlp.so")
 
 SOURCES = ["api.cpp", "route.hip", "router.hip", "unfused.hip", "permute.hip", "quant.hip", "gemm.hip", "gemm_store.hip",
            "gemm_glu_bf16.hip", "gemm_glu_mx.hip", "gemm_dglu_bf16.hip", "gemm_dglu_mx.hip", "gemm_wgrad.hip",
-           "gemm_store_mx4.hip", "gemm_glu_mx4.hip", "gemm_dglu_mx4.hip", "noalloc.hip",
+           "gemm_store_mx4.hip", "gemm_glu_mx4.hip", "gemm_dglu_mx4.hip", "gemm_wgrad_mx4.hip",
+           "noalloc.hip",
            "router_route.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -21,6 +21,10 @@ MOE_DEV float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x
 constexpr int kActSwigluFree = 0x100;
 // flag on a GEMM kernel's activation parameter: the layer has an FC1 bias
 constexpr int kActBias = 0x200;
+// flag on an MXFP4 GLU / dGLU kernel's activation parameter: the epilogue
+// also writes the transposed MXFP4 copy (the instantiation without it keeps
+// that code, and its registers and LDS, out of the kernel)
+constexpr int kActTr = 0x400;
 inline bool act_unclamped(const ActP& p) {
   return p.glo == -__builtin_inff() && p.llo == -__builtin_inff() &&
          p.ghi == __builtin_inff() && p.lhi == __builtin_inff() && p.loff == 0.0f;

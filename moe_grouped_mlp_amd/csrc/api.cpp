@@ -319,8 +319,8 @@ moe_status moe_grouped_mlp_fwd(const moe_fwd_args* a, void* stream) {
     if (!a->xp_q || !a->xp_s || !a->w1_q || !a->w1_s || !a->w2_q || !a->w2_s || !a->a_q ||
         !a->a_s || !a->yp || ((a->aT_q != nullptr) != (a->aT_s != nullptr)))
       return MOE_ERR_INVALID_ARG;
-    // MXFP4: no transposed copy (there is no MXFP4 weight gradient), no bias
-    if (f4 && (a->aT_q || a->bias1)) return MOE_ERR_INVALID_ARG;
+    // MXFP4: no bias
+    if (f4 && a->bias1) return MOE_ERR_INVALID_ARG;
   } else {
     if (!a->xp || !a->w1i || !a->w2 || !a->a || !a->yp) return MOE_ERR_INVALID_ARG;
     if (a->w1_stride != 0 && a->w1_stride < static_cast<int64_t>(N1) * a->H)
@@ -439,7 +439,7 @@ static moe_status bwd_check(const moe_bwd_args* a) {
     if (!a->dyp_q || !a->dyp_s || !a->w2t_q || !a->w2t_s || !a->w1t_q || !a->w1t_s ||
         !a->dz_q || !a->dz_s || ((a->dzT_q != nullptr) != (a->dzT_s != nullptr)))
       return MOE_ERR_INVALID_ARG;
-    if (f4 && (a->dzT_q || a->bias1)) return MOE_ERR_INVALID_ARG;
+    if (f4 && a->bias1) return MOE_ERR_INVALID_ARG;
   } else {
     if (!a->dyp || !a->w2 || !a->w1i || !a->dz) return MOE_ERR_INVALID_ARG;
     if (a->w1_stride != 0 && a->w1_stride < static_cast<int64_t>(N1) * a->H)
@@ -681,10 +681,12 @@ moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* a, void* stream) {
       a->I % 64 != 0 || (a->gated != 0 && a->gated != 1) || a->M_cap < 1 ||
       a->M_cap > (int64_t{1} << 22) || a->cu_margin < 0)
     return MOE_ERR_INVALID_ARG;
-  if (a->prec == MOE_PREC_MXFP8 && a->M_cap % 128 != 0) return MOE_ERR_INVALID_ARG;
+  if (a->prec != MOE_PREC_BF16 && a->M_cap % 128 != 0) return MOE_ERR_INVALID_ARG;
   if (!a->split_sizes || !a->padded_offsets) return MOE_ERR_INVALID_ARG;
-  if (a->prec != MOE_PREC_BF16 && a->prec != MOE_PREC_MXFP8) return MOE_ERR_INVALID_ARG;
-  const bool mx = a->prec == MOE_PREC_MXFP8;
+  if (a->prec != MOE_PREC_BF16 && a->prec != MOE_PREC_MXFP8 && a->prec != MOE_PREC_MXFP4)
+    return MOE_ERR_INVALID_ARG;
+  const bool f4 = a->prec == MOE_PREC_MXFP4;
+  const bool mx = a->prec == MOE_PREC_MXFP8 || f4;
   const int N1 = a->gated ? 2 * a->I : a->I;
   if (mx) {
     if (a->dw1 && (!a->dzT_q || !a->dzT_s || !a->xpT_q || !a->xpT_s)) return MOE_ERR_INVALID_ARG;
@@ -703,7 +705,7 @@ moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   // C_e [P][Q] = sum over e's rows m of A[m][p] B[m][q]: bf16 A [M_cap][P],
-  // B [M_cap][Q]; MXFP8 their transposed copies
+  // B [M_cap][Q]; MX their transposed copies
   auto run = [&](const void* A, const uint8_t* As, int P, const void* Bm, const uint8_t* Bs,
                  int Q, void* C) -> moe_status {
     moe::GemmArgs g{};
@@ -731,6 +733,7 @@ moe_status moe_grouped_mlp_wgrad(const moe_wgrad_args* a, void* stream) {
     int grid = cu - a->cu_margin;
     if (grid >= 8) grid -= grid % 8;
     if (tiles < grid) grid = static_cast<int>(tiles);
+    if (f4) return launched(moe::launch_gemm_wgrad_f4(g, grid, s));
     return launched(moe::launch_grouped_gemm(g, moe::EPI_WGRAD, false, mx, grid, s));
   };
   record(a->timing_events[0], s);

@@ -1,5 +1,6 @@
 // Grouped GEMM, GLU epilogue (FC1 forward), MXFP4 operands and the MXFP4
-// copy of a (rowwise, the FC2 operand) written by the epilogue.
+// copies of a written by the epilogue (rowwise, the FC2 operand, and
+// optionally transposed, the weight gradient's).
 #include "gemm_kernel.h"
 
 namespace moe {

@@ -159,9 +159,12 @@ struct KLoader {
   int voff[8];    // bytes
   int kbyte[2];   // byte position of the lane's chunk in a stage row (even / odd j)
 
-  MOE_DEV void init(const void* base, int64_t rows_avail, int ld_bytes, int wave, int lane) {
+  // trim: bytes cut from the end of the range (a base moved into a row by
+  // that many bytes then still ends where the last row does)
+  MOE_DEV void init(const void* base, int64_t rows_avail, int ld_bytes, int wave, int lane,
+                    int trim = 0) {
     const int64_t rows = rows_avail < 256 ? rows_avail : 256;
-    rsrc = make_rsrc(base, static_cast<uint32_t>(rows * ld_bytes));
+    rsrc = make_rsrc(base, static_cast<uint32_t>(rows > 0 ? rows * ld_bytes - trim : 0));
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = 64 * wave + 8 * j + (lane >> 3);
@@ -243,10 +246,11 @@ struct ScaleLoader {
 
   // s_tile: scales of the tile's first row group; groups_avail: row groups
   // of 32 that exist from there on
-  MOE_DEV void init(const uint8_t* s_tile, int64_t groups_avail, int K, int wave, int lane) {
+  MOE_DEV void init(const uint8_t* s_tile, int64_t groups_avail, int K, int wave, int lane,
+                    int trim = 0) {
     const int64_t groups = groups_avail < 8 ? (groups_avail > 0 ? groups_avail : 0) : 8;
     const int per_group = (K / 64) * 64;
-    rsrc = make_rsrc(s_tile, static_cast<uint32_t>(groups * per_group));
+    rsrc = make_rsrc(s_tile, static_cast<uint32_t>(groups > 0 ? groups * per_group - trim : 0));
     if constexpr (F4) {
       step = lane >> 4;
 #pragma unroll
@@ -387,51 +391,15 @@ struct MxOut {
   int64_t M_cap;
 };
 
-// A lane's 16 values of one 32 x 32 output block: v[4 rg + i] is column
-// 8 rg + 4 hf + i (hf = lane / 32) of the lane's row (lane % 32), the
-// values being bf16 numbers (zero for rows that hold no data).
-//
-// Rowwise: the row's 32 values are this lane's and its partner's (lane ^ 32);
-// codes go to the block's 32 bytes of the row (q_lane: its half 16 hf ..),
-// the scale to *s_byte.  The lane's four code
-// words (columns 8 rg + 4 hf ..) are exchanged with the partner's
-// (v_permlane32_swap) so that each lane stores 16 contiguous codes: the
-// low lane columns 0 .. 15, the high lane 16 .. 31.
-MOE_DEV void mx_row_block(const float (&v)[16], uint8_t* q_lane, uint8_t* s_byte, int hf) {
-  float am = 0.0f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(v[r]));
-  am = fmaxf(am, partner32(am, hf));
-  const int e = mx_exponent(am);
-  const float inv = mx_inv_scale(e);
-  uint32_t w[4];
-#pragma unroll
-  for (int rg = 0; rg < 4; ++rg)
-    w[rg] = mx_codes4(v[4 * rg], v[4 * rg + 1], v[4 * rg + 2], v[4 * rg + 3], inv);
-  // swap(a, b): the high half of a takes the low half of b and the low half
-  // of b the high half of a.  Low lanes end with (own w0, partner w0, own
-  // w1, partner w1), high lanes with (partner w2, own w2, partner w3, own w3)
-  const auto s0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
-  const auto s1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
-  *reinterpret_cast<uint4*>(q_lane) = make_uint4(s0[0], s0[1], s1[0], s1[1]);
-  if (hf == 0) *s_byte = mx_scale_code(e);
-}
-
-// MXFP4 rowwise (no transposed copy): the row's 32 values, this lane's and
-// its partner's, give one E8M0 scale and 32 E2M1 codes (16 bytes, element
-// 2 i in the low nibble of byte i).  A lane's four values of columns
-// 8 rg + 4 hf .. make a 16-bit half of the word of columns 8 rg ..; the
-// halves are exchanged with the partner (v_permlane32_swap) so that the low
-// lane stores the words of columns 0 .. 15 and the high lane 16 .. 31
-// (8 bytes each, q_lane = the block's row start + 8 hf).
-//
-// The values come as the packed bf16 words the epilogue computed (w[rg]:
-// columns 8 rg + 4 hf .. + 3), so the block maximum is taken on the bit
-// patterns (bf16 magnitudes order like unsigned integers) and the codes come
-// from the hardware's scaled conversion of the packed words.  Returns the
-// block maximum as a bf16 magnitude pattern.
+// A lane's 16 values of one 32 x 32 output block, as the packed bf16
+// words the epilogue computed: w[rg] holds columns 8 rg + 4 hf .. + 3
+// (hf = lane / 32) of the lane's row (lane % 32), value 0 in the low half
+// of w[rg].x; zero for rows that hold no data.  Block maxima are taken on
+// the bit patterns (bf16 magnitudes order like unsigned integers) and the
+// codes come from gfx950's scaled conversions of the packed words.
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
+// max |v| over 16 packed bf16 values, as a magnitude bit pattern.
 MOE_DEV uint32_t bf16_amax_bits(const uint2 (&w)[4]) {
   u16x2_t m = {0, 0};
 #pragma unroll
@@ -442,13 +410,54 @@ MOE_DEV uint32_t bf16_amax_bits(const uint2 (&w)[4]) {
   return m.x > m.y ? m.x : m.y;
 }
 
-MOE_DEV uint32_t mx4_row_block(const uint2 (&w)[4], uint8_t* q_lane, uint8_t* s_byte, int hf) {
-  uint32_t am = bf16_amax_bits(w);
+// The maximum over a lane and its partner (lane ^ 32).
+MOE_DEV uint32_t pair_max_bits(uint32_t am, int hf) {
   const auto pa = __builtin_amdgcn_permlane32_swap(am, am, false, false);
-  const uint32_t block_am = max(am, hf ? pa[0] : pa[1]);
-  // floor(log2) of the block maximum from its exponent field, minus 2
-  int e = static_cast<int>(block_am >> 7) - 127 - 2;
-  e = e < -127 ? -127 : e;
+  return max(am, hf ? pa[0] : pa[1]);
+}
+
+// Block exponent from the block maximum's bit pattern: floor(log2 amax)
+// (its exponent field) minus the exponent of the format's largest value
+// (8 for E4M3, 2 for E2M1), at least -127.
+template <int EMAX>
+MOE_DEV int block_exponent(uint32_t amax_bits) {
+  const int e = static_cast<int>(amax_bits >> 7) - 127 - EMAX;
+  return e < -127 ? -127 : e;
+}
+
+// Rowwise MXFP8: the row's 32 values, this lane's and its partner's, give
+// one scale; codes go to the block's 32 bytes of the row (q_lane: its half
+// 16 hf ..), the scale to *s_byte.  The lane's four code words (columns
+// 8 rg + 4 hf ..) are exchanged with the partner's (v_permlane32_swap) so
+// that each lane stores 16 contiguous codes: the low lane columns 0 .. 15,
+// the high lane 16 .. 31.  Returns the lane's own maximum (bit pattern).
+MOE_DEV uint32_t mx_row_block(const uint2 (&w)[4], uint8_t* q_lane, uint8_t* s_byte, int hf) {
+  const uint32_t am = bf16_amax_bits(w);
+  const int e = block_exponent<8>(pair_max_bits(am, hf));
+  const float scale = mx_scale_f32(e);
+  uint32_t c[4];
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) c[rg] = mx_codes4_bf16(w[rg], scale);
+  // swap(a, b): the high half of a takes the low half of b and the low half
+  // of b the high half of a.  Low lanes end with (own c0, partner c0, own
+  // c1, partner c1), high lanes with (partner c2, own c2, partner c3, own c3)
+  const auto s0 = __builtin_amdgcn_permlane32_swap(c[0], c[2], false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(c[1], c[3], false, false);
+  *reinterpret_cast<uint4*>(q_lane) = make_uint4(s0[0], s0[1], s1[0], s1[1]);
+  if (hf == 0) *s_byte = mx_scale_code(e);
+  return am;
+}
+
+// MXFP4 rowwise (no transposed copy): the row's 32 values give one E8M0
+// scale and 32 E2M1 codes (16 bytes, element 2 i in the low nibble of byte
+// i).  A lane's four values of columns 8 rg + 4 hf .. make a 16-bit half of
+// the word of columns 8 rg ..; the halves are exchanged with the partner
+// (v_permlane32_swap) so that the low lane stores the words of columns
+// 0 .. 15 and the high lane 16 .. 31 (8 bytes each, q_lane = the block's
+// row start + 8 hf).  Returns the lane's own maximum (bit pattern).
+MOE_DEV uint32_t mx4_row_block(const uint2 (&w)[4], uint8_t* q_lane, uint8_t* s_byte, int hf) {
+  const uint32_t am = bf16_amax_bits(w);
+  const int e = block_exponent<2>(pair_max_bits(am, hf));
   const float scale = mx_scale_f32(e);
   uint32_t h[4];
 #pragma unroll
@@ -477,43 +486,73 @@ MOE_DEV uint32_t mx4_row_block(const uint2 (&w)[4], uint8_t* q_lane, uint8_t* s_
 constexpr int kTrPitch = 36;   // bf16 per staged row (8-byte aligned rows)
 constexpr int kTrTile = 32 * kTrPitch;
 
-// q_lane: the lane's 16 codes of its column (rows 32 rb + 16 hf ..), s_byte:
-// the column's scale.
-MOE_DEV void mx_col_block(const float (&v)[16], uint16_t* tr, uint8_t* q_lane, uint8_t* s_byte,
-                          int lane) {
+// The lane's 16 values of its column: c[t4] holds rows 16 hf + 4 t4 .. + 3
+// of column lane % 32 (packed bf16, the first row in the low half).
+//
+// The four transpose reads are one asm block that waits for them itself.
+// The compiler cannot tell the staging tile from the stage buffers that LDS
+// DMA loads may be filling at the time (the next z chunk, the next tile's
+// first stage), so a read it issued would first wait for those loads, and
+// for every store before them.  A wave's LDS operations complete in order,
+// so the reads see the staging writes just before them (the memory clobber
+// keeps those writes ahead of the block).
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+MOE_DEV void col_gather(const uint2 (&w)[4], uint16_t* tr, int lane, uint2 (&c)[4]) {
   const int row = lane & 31, hf = lane >> 5;
 #pragma unroll
-  for (int rg = 0; rg < 4; ++rg) {   // the values are bf16 numbers: keep their high halves
-    uint2 w;
-    w.x = (__float_as_uint(v[4 * rg]) >> 16) | (__float_as_uint(v[4 * rg + 1]) & 0xffff0000u);
-    w.y = (__float_as_uint(v[4 * rg + 2]) >> 16) | (__float_as_uint(v[4 * rg + 3]) & 0xffff0000u);
-    *reinterpret_cast<uint2*>(tr + row * kTrPitch + 8 * rg + 4 * hf) = w;
-  }
-  float c[16];
-  float am = 0.0f;
-  {
-    const int g = lane >> 4, s = lane & 15;
-    const uint16_t* src = tr + (16 * (g >> 1) + (s >> 2)) * kTrPitch + 16 * (g & 1) + 4 * (s & 3);
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_v4i16_t*)(src + 4 * t4 * kTrPitch));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[4 * t4 + j] = __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(x[j])) << 16);
-        am = fmaxf(am, fabsf(c[4 * t4 + j]));
-      }
-    }
-  }
-  am = fmaxf(am, partner32(am, hf));
-  const int e = mx_exponent(am);
-  const float inv = mx_inv_scale(e);
+  for (int rg = 0; rg < 4; ++rg)
+    *reinterpret_cast<uint2*>(tr + row * kTrPitch + 8 * rg + 4 * hf) = w[rg];
+  const int g = lane >> 4, s = lane & 15;
+  const uint16_t* src = tr + (16 * (g >> 1) + (s >> 2)) * kTrPitch + 16 * (g & 1) + 4 * (s & 3);
+  const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)src));
+  static_assert(kTrPitch * 2 * 4 == 288, "row offsets of the reads below");
+  u32x2_t r0, r1, r2, r3;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:288\n\t"
+      "ds_read_b64_tr_b16 %2, %4 offset:576\n\t"
+      "ds_read_b64_tr_b16 %3, %4 offset:864\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(addr)
+      : "memory");
+  c[0] = make_uint2(r0.x, r0.y);
+  c[1] = make_uint2(r1.x, r1.y);
+  c[2] = make_uint2(r2.x, r2.y);
+  c[3] = make_uint2(r3.x, r3.y);
+}
+
+// q_lane: the lane's 16 codes of its column (rows 32 rb + 16 hf ..), s_byte:
+// the column's scale.
+MOE_DEV void mx_col_block(const uint2 (&w)[4], uint16_t* tr, uint8_t* q_lane, uint8_t* s_byte,
+                          int lane) {
+  const int hf = lane >> 5;
+  uint2 c[4];
+  col_gather(w, tr, lane, c);
+  const int e = block_exponent<8>(pair_max_bits(bf16_amax_bits(c), hf));
+  const float scale = mx_scale_f32(e);
   uint4 q;
-  q.x = mx_codes4(c[0], c[1], c[2], c[3], inv);
-  q.y = mx_codes4(c[4], c[5], c[6], c[7], inv);
-  q.z = mx_codes4(c[8], c[9], c[10], c[11], inv);
-  q.w = mx_codes4(c[12], c[13], c[14], c[15], inv);
+  q.x = mx_codes4_bf16(c[0], scale);
+  q.y = mx_codes4_bf16(c[1], scale);
+  q.z = mx_codes4_bf16(c[2], scale);
+  q.w = mx_codes4_bf16(c[3], scale);
   *reinterpret_cast<uint4*>(q_lane) = q;
+  if (hf == 0) *s_byte = mx_scale_code(e);
+}
+
+// MXFP4 transposed: the lane's 16 E2M1 codes of its column (8 bytes,
+// rows 32 rb + 16 hf .., element 2 i in the low nibble of byte i).
+MOE_DEV void mx4_col_block(const uint2 (&w)[4], uint16_t* tr, uint8_t* q_lane, uint8_t* s_byte,
+                           int lane) {
+  const int hf = lane >> 5;
+  uint2 c[4];
+  col_gather(w, tr, lane, c);
+  const int e = block_exponent<2>(pair_max_bits(bf16_amax_bits(c), hf));
+  const float scale = mx_scale_f32(e);
+  uint2 q;
+  q.x = mx4_codes4_bf16(c[0], scale) | (mx4_codes4_bf16(c[1], scale) << 16);
+  q.y = mx4_codes4_bf16(c[2], scale) | (mx4_codes4_bf16(c[3], scale) << 16);
+  *reinterpret_cast<uint2*>(q_lane) = q;
   if (hf == 0) *s_byte = mx_scale_code(e);
 }
 
@@ -525,6 +564,7 @@ struct MxBase {
   uint8_t* q;    // rowwise codes: o.q + row * n + 16 hf
   uint8_t* s;    // rowwise scale of (row, K block 0)
   uint8_t* qT;   // transposed codes of column lane % 32, rows 32 rb + 16 hf ..
+                 // (MXFP4: two a byte, [n][M_cap / 2])
   uint8_t* sT;   // transposed scale of (column lane % 32, row block rb)
 };
 
@@ -534,7 +574,8 @@ MOE_DEV MxBase mx_base(const MxOut& o, int64_t row, int64_t rb, int lane) {
   MxBase b;
   b.q = F4OUT ? o.q + row * (o.n / 2) + 8 * hf : o.q + row * o.n + 16 * hf;
   b.s = o.s + mx_scale_off(row, 0, o.n);
-  b.qT = o.qT + static_cast<int64_t>(c) * o.M_cap + rb * 32 + 16 * hf;
+  b.qT = F4OUT ? o.qT + static_cast<int64_t>(c) * (o.M_cap / 2) + rb * 16 + 8 * hf
+                : o.qT + static_cast<int64_t>(c) * o.M_cap + rb * 32 + 16 * hf;
   b.sT = o.sT + mx_scale_off(c, rb, o.M_cap);
   return b;
 }
@@ -543,21 +584,29 @@ MOE_DEV MxBase mx_base(const MxOut& o, int64_t row, int64_t rb, int lane) {
 // of a row block whose rows all lie before the group's padded end.  With
 // col0 a multiple of 32, the tiled scale offsets of (row, col0 / 32) and
 // (col0 + lane % 32, rb) are those of block 0 plus terms in col0 alone.
-MOE_DEV void mx_block_out(const float (&v)[16], const MxOut& o, const MxBase& b, uint16_t* tr,
-                          int col0, int lane) {
+// Returns the lane's maximum of the block (bit pattern).
+MOE_DEV uint32_t mx_block_out(const uint2 (&w)[4], const MxOut& o, const MxBase& b,
+                              uint16_t* tr, int col0, int lane) {
   uint8_t* const sb = b.s + (col0 >> 6) * 64 + ((col0 >> 5) & 1) * 32;
-  mx_row_block(v, b.q + col0, sb, lane >> 5);
+  const uint32_t am = mx_row_block(w, b.q + col0, sb, lane >> 5);
   if (o.qT)
-    mx_col_block(v, tr, b.qT + static_cast<int64_t>(col0) * o.M_cap,
+    mx_col_block(w, tr, b.qT + static_cast<int64_t>(col0) * o.M_cap,
                  b.sT + static_cast<int64_t>(col0 >> 5) * (o.M_cap >> 6) * 64, lane);
+  return am;
 }
 
-// MXFP4 (rowwise codes [M_cap][n / 2], no transposed copy) of the same
-// block from the lane's packed bf16 words; returns the lane's maximum as a
-// bf16 magnitude pattern.
-MOE_DEV uint32_t mx4_block_out(const uint2 (&w)[4], const MxBase& b, int col0, int lane) {
+// Both MXFP4 copies (rowwise codes [M_cap][n / 2], transposed [n][M_cap / 2])
+// of the same block; returns the lane's maximum as a bf16 magnitude pattern.
+// TR: the kernel writes the transposed copy (o.qT set).
+template <bool TR>
+MOE_DEV uint32_t mx4_block_out(const uint2 (&w)[4], const MxOut& o, const MxBase& b,
+                               uint16_t* tr, int col0, int lane) {
   uint8_t* const sb = b.s + (col0 >> 6) * 64 + ((col0 >> 5) & 1) * 32;
-  return mx4_row_block(w, b.q + col0 / 2, sb, lane >> 5);
+  const uint32_t am = mx4_row_block(w, b.q + col0 / 2, sb, lane >> 5);
+  if constexpr (TR)
+    mx4_col_block(w, tr, b.qT + static_cast<int64_t>(col0) * (o.M_cap / 2),
+                  b.sT + static_cast<int64_t>(col0 >> 5) * (o.M_cap >> 6) * 64, lane);
+  return am;
 }
 
 MOE_DEV void bf16x4_to_f32(uint2 w, float* v) {
@@ -788,15 +837,15 @@ MOE_DEV float dglu_rows(f32x16 (&acc)[4][4], const char* zrow, uint16_t* __restr
 // EPI_GLU with MXFP8 copies of a (see epi_glu).  Rows of a 32-row block
 // past the group's data but before its padded end get zero codes; a block
 // past the padded end is not touched (it belongs to the next group).
-template <int ACT, bool F4OUT = false>
+// F4OUT: MXFP4 copies; TR (MXFP4): with the transposed copy.
+template <int ACT, bool F4OUT = false, bool TR = true>
 MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t ldz,
                          uint16_t* __restrict__ a, int64_t lda, const float (&pr)[4],
                          const ActP& act, const TileCtx& t, int wn, int wm, int lane,
                          const MxOut& mo, uint16_t* tr, const float* sb) {
   constexpr bool gated = ACT != MOE_ACT_SRELU;
   const int hf = lane >> 5;
-  float amax = 0.0f;
-  uint32_t am4 = 0;   // MXFP4: the lane's max |a| as a bf16 magnitude pattern
+  uint32_t am = 0;   // the lane's max |a| as a bf16 magnitude pattern
   sfor<4>([&](auto mi) {
     sfor<4>([&](auto ni) { acc_hold(acc[mi][ni]); });
     if (mi >= t.mi_n) return;   // a half-height tile's waves own two row blocks
@@ -812,7 +861,6 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
       if (wn * kWaveN < t.cols_valid) {
         const int q = (t.col0 + wn * kWaveN) / (2 * MOE_INTERLEAVE);
         sfor<2>([&](auto h) {
-          float ab[16];
           uint2 wb[4];
           sfor<4>([&](auto rg) {
             const int c = h * 32 + 8 * rg + 4 * hf;
@@ -832,17 +880,14 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
             if (!row_ok) w = make_uint2(0, 0);
             if (row_ok && a)
               *reinterpret_cast<uint2*>(a + row * lda + q * MOE_INTERLEAVE + c) = w;
-            if constexpr (F4OUT) wb[rg] = w;
-            else bf16x4_to_f32(w, &ab[4 * rg]);
+            wb[rg] = w;
           });
-          if constexpr (F4OUT) {
-            // rows past the padded end hold no data (zeros), so skipping
-            // them leaves the maximum unchanged
-            if (blk_ok) am4 = max(am4, mx4_block_out(wb, mb, q * MOE_INTERLEAVE + h * 32, lane));
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ab[r]));
-            if (blk_ok) mx_block_out(ab, mo, mb, tr, q * MOE_INTERLEAVE + h * 32, lane);
+          // rows past the padded end hold no data (zeros), so skipping
+          // them leaves the maximum unchanged
+          if (blk_ok) {
+            const int cb = q * MOE_INTERLEAVE + h * 32;
+            am = max(am, F4OUT ? mx4_block_out<TR>(wb, mo, mb, tr, cb, lane)
+                               : mx_block_out(wb, mo, mb, tr, cb, lane));
           }
         });
       }
@@ -850,7 +895,6 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
       sfor<4>([&](auto ni) {
         if (wn * kWaveN + ni * 32 < t.cols_valid) {
           const int cb = t.col0 + wn * kWaveN + ni * 32;
-          float ab[16];
           uint2 wb[4];
           sfor<4>([&](auto rg) {
             const int n = cb + 8 * rg + 4 * hf;
@@ -866,29 +910,23 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
             uint2 w = make_uint2(pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]));
             if (!row_ok) w = make_uint2(0, 0);
             if (row_ok && a) *reinterpret_cast<uint2*>(a + row * lda + n) = w;
-            if constexpr (F4OUT) wb[rg] = w;
-            else bf16x4_to_f32(w, &ab[4 * rg]);
+            wb[rg] = w;
           });
-          if constexpr (F4OUT) {
-            if (blk_ok) am4 = max(am4, mx4_block_out(wb, mb, cb, lane));
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ab[r]));
-            if (blk_ok) mx_block_out(ab, mo, mb, tr, cb, lane);
-          }
+          if (blk_ok)
+            am = max(am, F4OUT ? mx4_block_out<TR>(wb, mo, mb, tr, cb, lane)
+                               : mx_block_out(wb, mo, mb, tr, cb, lane));
         }
       });
     }
     __builtin_amdgcn_sched_barrier(0);
   });
-  if constexpr (F4OUT) amax = __uint_as_float(am4 << 16);
-  return amax;
+  return __uint_as_float(am << 16);
 }
 
 // EPI_DGLU with MXFP8 copies of dz, row block MI (see dglu_rows; pad rows
 // as in epi_glu_mx).  With the 64-column interleave a 32-column block of dz
 // holds only gate or only up columns.
-template <int ACT, int MI, bool F4OUT = false>
+template <int ACT, int MI, bool F4OUT = false, bool TR = true>
 MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
                            uint16_t* __restrict__ dz, int64_t lddz, float p, const ActP& act,
                            const TileCtx& t, int wn, int wm, int lane, const MxOut& mo,
@@ -908,8 +946,7 @@ MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
   float dp = 0.0f;
   sfor<4>([&](auto ni) {
     if (wn * kWaveN + ni * 32 < t.cols_valid) {
-      float gv[16], uv[16];
-      uint2 gw[4], uw[4];   // MXFP4: the packed words themselves
+      uint2 gw[4], uw[4];
       sfor<4>([&](auto rg) {
         float gz[4];
         if constexpr (gated) {
@@ -938,13 +975,8 @@ MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
             *reinterpret_cast<uint2*>(db + off) = wg;
             *reinterpret_cast<uint2*>(db + off + MOE_INTERLEAVE) = wu;
           }
-          if constexpr (F4OUT) {
-            gw[rg] = wg;
-            uw[rg] = wu;
-          } else {
-            bf16x4_to_f32(wg, &gv[4 * rg]);
-            bf16x4_to_f32(wu, &uv[4 * rg]);
-          }
+          gw[rg] = wg;
+          uw[rg] = wu;
         } else {
           constexpr int off = 32 * ni + 8 * rg;
           bf16x4_to_f32(zread(zb, r16, 4 * ni + rg), gz);
@@ -961,23 +993,22 @@ MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
           uint2 w = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
           if (!row_ok) w = make_uint2(0, 0);
           if (row_ok && dz) *reinterpret_cast<uint2*>(dz + row * lddz + lane_col + off) = w;
-          if constexpr (F4OUT) gw[rg] = w;
-          else bf16x4_to_f32(w, &gv[4 * rg]);
+          gw[rg] = w;
         }
       });
       if (blk_ok) {
         if constexpr (gated) {
           const int cbg = 2 * t.col0 + 256 * wn + 128 * (ni / 2) + 32 * (ni % 2);
           if constexpr (F4OUT) {
-            mx4_block_out(gw, mb, cbg, lane);
-            mx4_block_out(uw, mb, cbg + MOE_INTERLEAVE, lane);
+            mx4_block_out<TR>(gw, mo, mb, tr, cbg, lane);
+            mx4_block_out<TR>(uw, mo, mb, tr, cbg + MOE_INTERLEAVE, lane);
           } else {
-            mx_block_out(gv, mo, mb, tr, cbg, lane);
-            mx_block_out(uv, mo, mb, tr, cbg + MOE_INTERLEAVE, lane);
+            mx_block_out(gw, mo, mb, tr, cbg, lane);
+            mx_block_out(uw, mo, mb, tr, cbg + MOE_INTERLEAVE, lane);
           }
         } else {
-          if constexpr (F4OUT) mx4_block_out(gw, mb, t.col0 + 128 * wn + 32 * ni, lane);
-          else mx_block_out(gv, mo, mb, tr, t.col0 + 128 * wn + 32 * ni, lane);
+          if constexpr (F4OUT) mx4_block_out<TR>(gw, mo, mb, tr, t.col0 + 128 * wn + 32 * ni, lane);
+          else mx_block_out(gw, mo, mb, tr, t.col0 + 128 * wn + 32 * ni, lane);
         }
       }
     }
@@ -1018,12 +1049,16 @@ MOE_DEV int block_exclusive_scan(int v, int* s_tmp, int& total) {
 // scales; K counts values, so a row holds K / 2 bytes and a 128-byte stage
 // four 64-deep steps.
 // ACTF: the activation (ACT), plus kActBias when the layer has an FC1 bias
-// (g.bias non-null; GLU and DGLU epilogues only).
+// (g.bias non-null; GLU and DGLU epilogues only) and, in the MXFP4 GLU and
+// dGLU kernels, kActTr when the epilogue writes the transposed copy.
 template <int EPI, bool NN, int ACTF, bool MX, bool F4 = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_kernel(GemmArgs g) {
-  constexpr int ACT = ACTF & ~kActBias;
+  constexpr int ACT = ACTF & ~(kActBias | kActTr);
   constexpr bool kBias = (ACTF & kActBias) != 0 && (EPI == EPI_GLU || EPI == EPI_DGLU);
+  // transposed MX copies from the GLU / dGLU epilogue: MXFP8 decides at run
+  // time (mx_qT), MXFP4 by instantiation (kActTr)
+  constexpr bool kTrOut = !F4 || (ACTF & kActTr) != 0;
   // half-height tiles (an expert's last 128 rows or fewer) in the plain-store
   // and GLU kernels with K-contiguous weights: the dGLU epilogue streams z in
   // 64-row chunks laid out for full tiles, the weight gradient's rows are not
@@ -1032,7 +1067,7 @@ void grouped_gemm_kernel(GemmArgs g) {
   // and transposed reads, which do not shrink)
   constexpr bool kHalfTiles = (EPI == EPI_STORE || EPI == EPI_GLU) && !NN;
   static_assert(!(MX && NN), "MXFP8 operands are always K-contiguous");
-  static_assert(!F4 || (MX && EPI != EPI_WGRAD), "MXFP4: plain-store, GLU and dGLU GEMMs");
+  static_assert(!F4 || MX, "MXFP4 operands are microscaled");
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[kStageBytes / 2], sA1[kStageBytes / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t sB0[kStageBytes / 2], sB1[kStageBytes / 2];
   constexpr int kScaleBytes = MX ? (F4 ? 2 * kStageS : kStageS) : 4;
@@ -1043,7 +1078,7 @@ void grouped_gemm_kernel(GemmArgs g) {
   __shared__ int s_tmp[kThreads / 64];
   __shared__ __attribute__((aligned(16))) float s_red[2 * BM];  // dprobs sums; the tile's bias
   // per-wave staging tiles of the transposed MXFP8 copies (MX epilogues)
-  constexpr int kTrWords = (MX && !F4 && (EPI == EPI_GLU || EPI == EPI_DGLU)) ? 4 * kTrTile : 4;
+  constexpr int kTrWords = (MX && kTrOut && (EPI == EPI_GLU || EPI == EPI_DGLU)) ? 4 * kTrTile : 4;
   __shared__ __attribute__((aligned(16))) uint16_t s_tr[kTrWords];
 
   const int tid = threadIdx.x;
@@ -1160,6 +1195,8 @@ void grouped_gemm_kernel(GemmArgs g) {
   struct TileInfo {
     int e, m_t, n_t, col0, cols_valid, rows_valid, rows_pad;
     int kbeg, kend;   // K stages of this work item
+    int kshift;       // MXFP4 weight gradient: the group's first row (K starts there)
+    int kvalid;       // MXFP4 weight gradient: the group's rows, rounded up to 32
     int part, slot;   // split-K part and partial-tile slot (parts > 1)
     int64_t row0;     // first row of A
     int64_t orow0;    // first row of C (row0, or e * P + row0 for EPI_WGRAD)
@@ -1195,12 +1232,26 @@ void grouped_gemm_kernel(GemmArgs g) {
       // clamped to the stages of M_cap rows, so inconsistent offsets stay
       // inside the operands (bf16 stages are 64 rows; a last partial one is
       // cut by the row limit, and MXFP8 needs M_cap % 128 == 0)
+      ti.half = false;
+      if constexpr (F4) {
+        // a stage is 256 rows but groups start at multiples of 128: K
+        // counts from the group's first row (the loaders' bases move there)
+        // and stops at its rows rounded up to a 32-row block, past which
+        // the loads fill zeros; offsets are clamped into [0, M_cap]
+        const int64_t p0 = min(max(static_cast<int64_t>(s_pad[ti.e]), int64_t{0}), g.M_cap);
+        const int64_t n = min(max(static_cast<int64_t>(s_split[ti.e]), int64_t{0}), g.M_cap - p0);
+        ti.kshift = static_cast<int>(p0);
+        ti.kvalid = static_cast<int>((n + 31) / 32 * 32);
+        ti.kbeg = 0;
+        ti.kend = static_cast<int>((n + 255) / 256);
+        return ti;
+      }
       const int nk_all = (g.K * kElem + kRowBytes - 1) / kRowBytes;
       ti.kbeg = min(max(s_pad[ti.e], 0) * kElem / kRowBytes, nk_all);
       ti.kend = min(ti.kbeg + (s_split[ti.e] * kElem + kRowBytes - 1) / kRowBytes, nk_all);
-      ti.half = false;
       return ti;
     }
+    ti.kshift = ti.kvalid = 0;
     ti.row0 = static_cast<int64_t>(s_pad[ti.e]) + static_cast<int64_t>(m_t) * BM;
     ti.orow0 = ti.row0;
     // rows_valid <= 0 only with inconsistent offsets: the tile then loads
@@ -1237,6 +1288,10 @@ void grouped_gemm_kernel(GemmArgs g) {
   // rather than in lockstep: the first one's L2 miss brings the slice in and
   // the others hit, instead of all of them waiting on the same MALL/HBM fetch.
   int k_rot = 0, k_beg = 0, k_len = nk;
+  // bytes per operand row and 64-deep steps the loads stop at (MXFP4 weight
+  // gradient: the tile's group, from its first row)
+  constexpr bool kF4W = F4 && EPI == EPI_WGRAD;
+  int k_lim = k_bytes, steps_lim = k_steps64;
   auto issue_stage = [&](uint16_t* a_st, uint16_t* b_st, uint8_t* s_st, int kt) {
     const bool valid = kt < k_len;
     int kk = kt + k_rot;
@@ -1246,11 +1301,11 @@ void grouped_gemm_kernel(GemmArgs g) {
       la_n.issue_lim(a_st, kk * BK * (g.wg_rows * 2), wave_s, valid, kk, row_end, lane);
       lb_n.issue_lim(b_st, kk * BK * (g.N * 2), wave_s, valid, kk, row_end, lane);
     } else {
-      la.template issue<MX>(a_st, kk, wave_s, valid, k_bytes);
+      la.template issue<MX>(a_st, kk, wave_s, valid, kF4W ? k_lim : k_bytes);
       if constexpr (NN) lb_n.issue(b_st, kk * BK * (g.N * 2), wave_s, valid);
-      else lb_k.template issue<MX>(b_st, kk, wave_s, valid, k_bytes);
+      else lb_k.template issue<MX>(b_st, kk, wave_s, valid, kF4W ? k_lim : k_bytes);
     }
-    if constexpr (MX) ls.issue(s_st, kk, wave_s, valid, k_steps64);
+    if constexpr (MX) ls.issue(s_st, kk, wave_s, valid, kF4W ? steps_lim : k_steps64);
   };
   // point the loaders at a tile (its first two stages are issued next)
   const int lane_k = lane, wave_k = wave;
@@ -1276,6 +1331,12 @@ void grouped_gemm_kernel(GemmArgs g) {
       la_n.init(reinterpret_cast<const uint16_t*>(A),
                 static_cast<uint32_t>(static_cast<int64_t>(g.K) * g.wg_rows * 2), g.wg_rows,
                 static_cast<int>(ti.row0), wave, lane);
+    } else if constexpr (kF4W) {
+      // the rows of A^T and B^T are read from the group's first row on
+      k_lim = ti.kvalid / 2;
+      steps_lim = ti.kvalid / 64 + (ti.kvalid % 64 != 0);
+      la.init(A + arow0 * k_bytes + ti.kshift / 2, rows_avail, k_bytes, wave, lane,
+              ti.kshift / 2);
     } else {
       la.init(A + arow0 * k_bytes, rows_avail, k_bytes, wave, lane);
     }
@@ -1283,6 +1344,9 @@ void grouped_gemm_kernel(GemmArgs g) {
     if constexpr (NN) {
       lb_n.init(reinterpret_cast<const uint16_t*>(Bexp),
                 static_cast<uint32_t>(static_cast<int64_t>(g.K) * g.N * 2), g.N, ti.col0, wave, lane);
+    } else if constexpr (kF4W) {
+      lb_k.init(Bexp + static_cast<int64_t>(ti.col0) * k_bytes + ti.kshift / 2, g.N - ti.col0,
+                k_bytes, wave, lane, ti.kshift / 2);
     } else {
       lb_k.init(Bexp + static_cast<int64_t>(ti.col0) * k_bytes, g.N - ti.col0, k_bytes, wave, lane);
     }
@@ -1294,7 +1358,12 @@ void grouped_gemm_kernel(GemmArgs g) {
       const uint8_t* sbase =
           a_side ? g.a_s + (arow0 / 32) * per_group
                  : g.b_s + static_cast<int64_t>(ti.e) * g.b_s_stride + (ti.col0 / 32) * per_group;
-      ls.init(sbase, a_side ? rows_avail / 32 : (g.N - ti.col0) / 32, g.K, wave, lane);
+      // MXFP4 weight gradient: the group's first 32-row block is an even
+      // one (groups start at multiples of 128), so its pair of the tiled
+      // layout starts kshift / 64 pairs (kshift bytes) into the row group
+      const int sshift = kF4W ? ti.kshift : 0;
+      ls.init(sbase + sshift, a_side ? rows_avail / 32 : (g.N - ti.col0) / 32, g.K, wave, lane,
+              sshift);
     }
   };
   auto start_tile = [&](const TileInfo& ti) {
@@ -1686,7 +1755,7 @@ void grouped_gemm_kernel(GemmArgs g) {
         TileCtx te = t;
         te.m_lane = (wave_e >> 1) * t.wrow + (lane_e & 31);
         te.n_lane = (wave_e & 1) * kWaveN + 4 * (lane_e >> 5);
-        amax = epi_glu_mx<ACT, F4>(acc, g.C, g.ldc, g.act_out, g.ld_act, pr_tile, g.act, te,
+        amax = epi_glu_mx<ACT, F4, kTrOut>(acc, g.C, g.ldc, g.act_out, g.ld_act, pr_tile, g.act, te,
                                wave_e & 1, wave_e >> 1, lane_e, mo, s_tr + wave_e * kTrTile,
                                sb);
       } else
@@ -1741,11 +1810,11 @@ void grouped_gemm_kernel(GemmArgs g) {
         uint16_t* zb = MI % 2 ? sB1 : sB0;
         // chunk MI has landed once at most the loads issued after it are
         // outstanding: chunk MI + 1 (MI < 3), or stage 0 of the next tile
-        // (bf16; with MXFP8 nothing is issued after chunk 3 but stores)
+        // (issued after block 2), which may be in flight
         if constexpr (MI < 3) {
           __builtin_amdgcn_s_waitcnt(wait_vmcnt(ZL::kInstr));
         } else {
-          if (!MX && more) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLoads));
+          if (more) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLoads));
           else __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
         }
         if constexpr (kBias && MI == 0) {
@@ -1761,7 +1830,7 @@ void grouped_gemm_kernel(GemmArgs g) {
         const char* zrow =
             reinterpret_cast<const char*>(wm_e ? zb : za) + (lane_e & 31) * kZRow;
         if constexpr (MX)
-          dp[MI] = dglu_rows_mx<ACT, MI, F4>(acc, zrow, g.C, g.ldc, pr[MI], g.act, te, wn_e, wm_e,
+          dp[MI] = dglu_rows_mx<ACT, MI, F4, kTrOut>(acc, zrow, g.C, g.ldc, pr[MI], g.act, te, wn_e, wm_e,
                                          lane_e, mo, s_tr + wave_e * kTrTile, sb);
         else
           dp[MI] = dglu_rows<ACT, MI>(acc, zrow, g.C, g.ldc, pr[MI], g.act, te, wn_e, lane_e,
@@ -1773,22 +1842,13 @@ void grouped_gemm_kernel(GemmArgs g) {
         if constexpr (MI < 2) {
           zl.issue(za, zb, MI + 2, wave_s, lane_e);
         } else if constexpr (MI == 2) {
-          // MXFP8: stage 0 waits for the last block, whose LDS transpose
-          // reads the compiler would otherwise order behind these loads
-          if constexpr (!MX) {
-            if (more) {
-              point_tile(cur);
-              issue_stage(sA0, sB0, sS0, 0);
-            }
+          // stage 0 of the next tile goes out before the last row block
+          if (more) {
+            point_tile(cur);
+            issue_stage(sA0, sB0, sS0, 0);
           }
         } else {
-          if (more) {
-            if constexpr (MX) {
-              point_tile(cur);
-              issue_stage(sA0, sB0, sS0, 0);
-            }
-            issue_stage(sA1, sB1, sS1, 1);
-          }
+          if (more) issue_stage(sA1, sB1, sS1, 1);
         }
       });
       sfor<4>([&](auto mi) {
@@ -1825,8 +1885,8 @@ hipError_t launch_act_b(const GemmArgs& g, int grid, hipStream_t s) {
   dim3 blk(kThreads), grd(grid);
   switch (g.act.act) {
     case MOE_ACT_SWIGLU:
-      if (!BIAS && act_unclamped(g.act))
-        grouped_gemm_kernel<EPI, NN, kActSwigluFree, MX, F4><<<grd, blk, 0, s>>>(g);
+      if (!(BIAS & kActBias) && act_unclamped(g.act))
+        grouped_gemm_kernel<EPI, NN, kActSwigluFree | BIAS, MX, F4><<<grd, blk, 0, s>>>(g);
       else
         grouped_gemm_kernel<EPI, NN, MOE_ACT_SWIGLU | BIAS, MX, F4><<<grd, blk, 0, s>>>(g);
       break;
@@ -1850,10 +1910,11 @@ hipError_t launch_act(const GemmArgs& g, int grid, hipStream_t s) {
 // MXFP4 operands with an activation epilogue (no bias)
 template <int EPI>
 hipError_t launch_act_f4(const GemmArgs& g_in, int grid, hipStream_t s) {
-  if (g_in.bias || g_in.mx_qT) return hipErrorInvalidValue;
+  if (g_in.bias) return hipErrorInvalidValue;
   GemmArgs g = g_in;
   g.clk = gemm_clock_slot(grid);
-  return launch_act_b<EPI, false, true, 0, true>(g, grid, s);
+  return g.mx_qT ? launch_act_b<EPI, false, true, kActTr, true>(g, grid, s)
+                 : launch_act_b<EPI, false, true, 0, true>(g, grid, s);
 }
 
 }  // namespace

@@ -115,10 +115,13 @@ int64_t* gemm_clock_slot(int grid);
 // MXFP4 operands (A, B: packed E2M1 codes, K / 2 bytes per row; b_stride
 // in values), plain store, no split-K
 hipError_t launch_gemm_store_f4(const GemmArgs& g, int grid, hipStream_t s);
-// MXFP4 operands with the GLU / dGLU epilogue, whose MX copy (mx_q, mx_s)
-// is then MXFP4 rowwise ([M_cap][mx_n / 2] codes; mx_qT must be null); no bias
+// MXFP4 operands with the GLU / dGLU epilogue, whose MX copies are then
+// MXFP4: rowwise (mx_q, mx_s: [M_cap][mx_n / 2] codes) and, when mx_qT is
+// set, transposed (mx_qT, mx_sT: [mx_n][M_cap / 2]); no bias
 hipError_t launch_gemm_glu_f4(const GemmArgs& g, int grid, hipStream_t s);
 hipError_t launch_gemm_dglu_f4(const GemmArgs& g, int grid, hipStream_t s);
+// MXFP4 weight-gradient GEMM (transposed copies, K along the routed rows)
+hipError_t launch_gemm_wgrad_f4(const GemmArgs& g, int grid, hipStream_t s);
 int grouped_gemm_tile_n();  // BN of the launched configuration
 // bytes of split_ws + split_cnt for a grid of `grid` workgroups
 size_t grouped_gemm_split_bytes(int grid);

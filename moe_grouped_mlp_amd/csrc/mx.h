@@ -39,6 +39,25 @@ MOE_DEV uint32_t mx_codes4(float a, float b, float c, float d, float inv) {
   return static_cast<uint32_t>(w);
 }
 
+// Four bf16 values (two packed words, value 0 in the low half of w.x)
+// divided by 2^e (scale = 2^e) -> four E4M3 codes, little-endian:
+// v_cvt_scalef32_pk_fp8_bf16 divides by the scale and rounds to nearest
+// even, but turns magnitudes past 464 (whose rounding would pass the
+// largest code) into NaN, 0x7f / 0xff, where the block rule saturates at
+// 448, 0x7e / 0xfe: those bytes are moved one code down.  The block
+// exponent keeps |v| / 2^e below 512, so nothing else can come out as NaN.
+typedef short short2_t __attribute__((ext_vector_type(2)));
+MOE_DEV uint32_t mx_codes4_bf16(uint2 w, float scale) {
+  short2_t r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2_t, w.x), scale,
+                                                false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2_t, w.y), scale,
+                                                true);
+  const uint32_t c = __builtin_bit_cast(uint32_t, r);
+  const uint32_t nan = ((c & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u;
+  return c - (nan >> 7);
+}
+
 // |v| of a bf16 pattern as an ordered integer (bf16 magnitudes compare like
 // their bit patterns).
 MOE_DEV uint32_t bf16_abs_bits(uint32_t b) { return b & 0x7fffu; }

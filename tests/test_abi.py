@@ -268,6 +268,11 @@ def test_wgrad_validation():
     assert _call("moe_grouped_mlp_wgrad", args(**{**mx, "aT_s": None})) == INVALID
     assert _call("moe_grouped_mlp_wgrad", args(**{**mx, "xpT_q": None})) == INVALID
     assert _call("moe_grouped_mlp_wgrad", args(**{**mx, "M_cap": 1000})) == INVALID
+    # MXFP4 the same way
+    f4 = {**mx, "prec": B.PREC_MXFP4}
+    assert _call("moe_grouped_mlp_wgrad", args(**f4)) == DEVICE
+    assert _call("moe_grouped_mlp_wgrad", args(**{**f4, "dzT_s": None})) == INVALID
+    assert _call("moe_grouped_mlp_wgrad", args(**{**f4, "M_cap": 1000})) == INVALID
 
 
 @no_device
@@ -513,9 +518,10 @@ def test_fwd_bwd_mxfp4_validation():
     assert _call("moe_grouped_mlp_fwd", _fwd_args(**base)) == DEVICE
     for f in mx_fwd:
         assert _call("moe_grouped_mlp_fwd", _fwd_args(**{**base, f: None})) == INVALID, f
-    # no transposed copy and no bias in MXFP4
+    # the transposed copy is optional (both pointers or neither); no bias
     assert _call("moe_grouped_mlp_fwd",
-                 _fwd_args(**{**base, "aT_q": 64, "aT_s": 64})) == INVALID
+                 _fwd_args(**{**base, "aT_q": 64, "aT_s": 64})) == DEVICE
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(**{**base, "aT_q": 64})) == INVALID
     assert _call("moe_grouped_mlp_fwd", _fwd_args(**{**base, "bias1": 64})) == INVALID
     assert _call("moe_grouped_mlp_fwd", _fwd_args(**{**base, "M_cap": 1000})) == INVALID
 
@@ -534,7 +540,9 @@ def test_fwd_bwd_mxfp4_validation():
         assert _call("moe_grouped_mlp_bwd", a) == INVALID, f
         setattr(a, f, 64)
     a.dzT_q, a.dzT_s = 64, 64
+    assert _call("moe_grouped_mlp_bwd", a) == DEVICE
+    a.dzT_s = None
     assert _call("moe_grouped_mlp_bwd", a) == INVALID
-    a.dzT_q = a.dzT_s = None
+    a.dzT_q = None
     a.bias1 = 64
     assert _call("moe_grouped_mlp_bwd", a) == INVALID

@@ -214,3 +214,127 @@ def test_fused_and_unfused_mxfp4_share_operands():
     for e in range(wl.E):
         valid[pad[e]:pad[e] + split[e]] = True
     assert_close(host_f64(fused.z)[valid], host_f64(unf.z)[valid], "z")
+
+
+# ------------------------------------------------ transposed copies, dW ---
+def _unpack(b):
+    """Packed E2M1 codes (element 2 i in the low nibble of byte i) -> one
+    code per element."""
+    b = np.asarray(b, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def _decode_T(q, s, n, M_cap):
+    """A transposed MXFP4 copy ([n][M_cap / 2] codes, tiled scales with
+    R = n, K = M_cap) decoded to float64 [n][M_cap]."""
+    codes = _unpack(q.detach().cpu().numpy().reshape(n, M_cap // 2))
+    scales = mx_scales_plain(s, n, M_cap)
+    return nu.mxfp4_dequantize(codes, scales, axis=1)
+
+
+def _routed_rows(blk):
+    split = blk.split_sizes.cpu().numpy()
+    pad = blk.padded_offsets.cpu().numpy()
+    valid = np.zeros(blk.M_cap, dtype=bool)
+    for e in range(blk.E):
+        valid[pad[e]:pad[e] + split[e]] = True
+    return valid, split, pad
+
+
+@pytest.mark.parametrize("case", ["tiny", "gptoss_act", "dsv3_zipf_empty", "srelu"])
+def test_fused_mxfp4_transposed_copies_bit_exact(case):
+    """The GLU and dGLU epilogues' transposed MXFP4 copies of a and dz
+    ([n][M_cap / 2], blocks of 32 rows along M) are the oracle's MXFP4
+    encoding of the GPU's own bf16 a and dz (pad rows as zeros), bit for
+    bit; the rowwise copies stay so too."""
+    kw = dict(CASES[case])
+    wl = make_workload(kw.pop("name"), seed=12, **kw)
+    M_cap = -(-wl.m_cap() // 128) * 128
+    blk = run_gpu_layer(wl, M_cap, prec=mg.PREC_MXFP4, bf16_copies=True)
+    assert blk.aT_q4 is not None and blk.dzT_q4 is not None
+    valid, _, _ = _routed_rows(blk)
+    mp = int(blk.padded_offsets[-1].item())
+    for name, src, n in (("a", blk.a, wl.I), ("dz", blk.dz, blk.N1)):
+        v = rows_with_pad_zeroed(host_f64(src)[:mp], valid[:mp])
+        assert_mx4_equal(getattr(blk, name + "_q4"), getattr(blk, name + "_s4"), M_cap, n, mp,
+                         v, f"{name} MXFP4 rowwise")
+        codes, scales = nu.mxfp4_quantize(v.T, axis=1)        # [n][mp]
+        qT = getattr(blk, name + "T_q4").cpu().numpy().reshape(n, M_cap // 2)[:, :mp // 2]
+        sT = mx_scales_plain(getattr(blk, name + "T_s4"), n, M_cap)[:, :mp // 32]
+        np.testing.assert_array_equal(sT, scales, err_msg=f"{name} MXFP4 transposed scales")
+        np.testing.assert_array_equal(qT, nu.pack_nibbles(codes),
+                                      err_msg=f"{name} MXFP4 transposed codes")
+    assert int(blk.err_flag.cpu()[0]) == 0
+
+
+@pytest.mark.parametrize("case", ["tiny", "multi_tile_ragged", "gptoss_act", "dsv3_zipf_empty"])
+def test_mxfp4_weight_grads(case):
+    """MXFP4 weight gradients (moe_grouped_mlp_wgrad, prec MXFP4) from the
+    transposed copies: element by element against the float64 contraction
+    of the GPU's own operands decoded (each group's rows, one bf16
+    rounding), the Xp and dYp copies bit-exact against the oracle's
+    encoding of the permuted rows, and against the independent oracle
+    (weight_grads(mx="mxfp4")) by relative L2 error."""
+    kw = dict(CASES[case])
+    wl = make_workload(kw.pop("name"), seed=14, **kw)
+    M_cap = -(-wl.m_cap() // 128) * 128
+    gp, _ = act_of(wl)
+    blk = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, act=gp, first_expert=wl.first_expert,
+                         M_cap=M_cap, prec=mg.PREC_MXFP4, wgrad=True)
+    run_gpu_layer(wl, M_cap, block=blk)
+    blk.dw1.fill_(float("nan"))
+    blk.dw2.fill_(float("nan"))
+    blk.weight_grads()
+    torch.cuda.synchronize()
+    assert int(blk.err_flag.cpu()[0]) == 0
+    fw, bw = oracle_layer(wl, M_cap, mx="mxfp4")
+    mp = int(fw.rt.padded_offsets[-1])
+    H, I, N1 = wl.H, wl.I, blk.N1
+    # the quantize passes' copies of Xp and dYp: exact inputs, so bit-exact
+    for name, ref, n in (("xp", fw.xp, H), ("dyp", bw.dyp, H)):
+        codes, scales = nu.mxfp4_quantize(ref[:mp].T, axis=1)
+        qT = getattr(blk, name + "T_q4").cpu().numpy().reshape(n, M_cap // 2)[:, :mp // 2]
+        np.testing.assert_array_equal(qT, nu.pack_nibbles(codes), err_msg=name)
+        np.testing.assert_array_equal(
+            mx_scales_plain(getattr(blk, name + "T_s4"), n, M_cap)[:, :mp // 32], scales,
+            err_msg=name)
+    D = _decode_T(blk.dzT_q4, blk.dzT_s4, N1, M_cap)
+    X = _decode_T(blk.xpT_q4, blk.xpT_s4, H, M_cap)
+    Y = _decode_T(blk.dypT_q4, blk.dypT_s4, H, M_cap)
+    A = _decode_T(blk.aT_q4, blk.aT_s4, I, M_cap)
+    _, split, pad = _routed_rows(blk)
+    dw1 = host_f64(blk.dw1)
+    dw2 = host_f64(blk.dw2)
+    for e in range(wl.E):
+        r = slice(int(pad[e]), int(pad[e]) + int(split[e]))
+        assert_close(dw1[e], nu.round_bf16(D[:, r] @ X[:, r].T), f"dW1 expert {e}")
+        assert_close(dw2[e], nu.round_bf16(Y[:, r] @ A[:, r].T), f"dW2 expert {e}")
+    o1, o2 = om.weight_grads(fw, bw, mx="mxfp4")
+    gated = wl.act != "srelu"
+    # dW1 rows follow dz's interleaved column order; the oracle's are logical
+    g1 = np.stack([uninterleave_cols(dw1[e].T, wl.I).T for e in range(wl.E)]) if gated else dw1
+    for got, ref, what in ((g1, o1, "dW1"), (dw2, o2, "dW2")):
+        l2 = _rel_l2(got, ref)
+        assert l2 < 5e-2, f"{what}: relative L2 error {l2:.3e} against the oracle"
+
+
+def test_mxfp4_recompute_rebuilds_z_bit_for_bit():
+    """Activation recompute in MXFP4: z rebuilt by the MXFP4 plain-store GEMM
+    from the saved Xp and W1 copies equals the z the fused forward stores,
+    and the backward's outputs are those of the block that keeps z."""
+    wl = make_workload("tiny", seed=15, E=8, T=1024, H=256, I=256)
+    M_cap = -(-wl.m_cap() // 128) * 128
+    keep = run_gpu_layer(wl, M_cap, prec=mg.PREC_MXFP4, bf16_copies=False)
+    gp, _ = act_of(wl)
+    rc = mg.ExpertBlock(wl.E, wl.H, wl.I, wl.T, wl.k, act=gp, M_cap=M_cap,
+                        prec=mg.PREC_MXFP4, recompute=True, bf16_copies=False)
+    rc.keep_recomputed_z = True
+    run_gpu_layer(wl, M_cap, block=rc)
+    valid, _, _ = _routed_rows(keep)
+    v = torch.from_numpy(valid).cuda()
+    assert torch.equal(rc.z[v], keep.z[v])
+    for n in ("out", "dx", "dprobs"):
+        assert torch.equal(getattr(rc, n), getattr(keep, n)), n

@@ -98,8 +98,10 @@ def test_mxfp4_layer_parity(case):
 
 
 def test_mxfp4_layer_rejects_fused_only_options():
-    with pytest.raises(ValueError):
-        mg.ExpertBlock(4, 256, 128, 64, 2, prec=mg.PREC_MXFP4, recompute=True)
+    """Weight gradients and recompute belong to the fused MXFP4 layer."""
+    for kw in (dict(recompute=True), dict(wgrad=True)):
+        with pytest.raises(ValueError):
+            mg.ExpertBlock(4, 256, 128, 64, 2, prec=mg.PREC_MXFP4, unfused=True, **kw)
 
 
 def _graph_replays_match_eager(blk, wl, rows_tensors):
