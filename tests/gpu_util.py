@@ -311,6 +311,9 @@ def assert_mx_rule(q_gpu, s_plain_gpu, ref, what):
     assert bad.size == 0, (f"{what}: {bad.size} of {scales.size} scales differ; first at "
                            f"{bad[:5]}: gpu {s_plain_gpu.reshape(-1)[bad[:5]]} oracle "
                            f"{scales.reshape(-1)[bad[:5]]}")
+    # no NaN code (0x7f / 0xff): the block rule saturates at 448
+    nan = np.flatnonzero((q.reshape(-1) & 0x7f) == 0x7f)
+    assert nan.size == 0, f"{what}: {nan.size} NaN codes, first at {nan[:5]}"
     dist = np.abs(e4m3_ordinal(q) - e4m3_ordinal(codes))
     assert dist.max(initial=0) <= 1, f"{what}: a code differs by {dist.max()} steps"
     assert (dist > 0).mean() <= MX_CODE_FRAC, \
