@@ -19,6 +19,10 @@ whole-layer oracle is too slow at these sizes, so:
     involved: the MXFP8 copy of the permuted input rows (bit-exact), FC1
     outputs z, the activation a, the FC2-dgrad + dActivation output dz, and
     secondarily the MXFP8 copies of the oracle's own a and dz;
+  * MXFP4 (Mixtral, GPT-OSS): the fused MXFP4 copies of a and dz, rowwise
+    and transposed, on whole sampled 32-row blocks bit-exact against the
+    oracle's encoding of the GPU's own bf16 rows; the permuted input rows'
+    copy bit-exact; sampled z, a and dz against the oracle on MXFP4 operands;
   * amax equals max |a| over the valid rows (a property at any size);
   * the whole DSv3-share step captured in one HIP graph replays to the eager
     results bit for bit (bf16 and MXFP8).
@@ -57,7 +61,8 @@ def _run(name, prec):
     # bench.py's block; with MXFP8 the bf16 a and dz are kept for the checks
     # (they do not change what is computed)
     blk = mg.ExpertBlock(E, H, I, T, k, act=act,
-                         prec=mg.PREC_MXFP8 if prec == "mxfp8" else mg.PREC_BF16,
+                         prec={"bf16": mg.PREC_BF16, "mxfp8": mg.PREC_MXFP8,
+                               "mxfp4": mg.PREC_MXFP4}[prec],
                          bf16_copies=True)
     blk.load_weights(w1, w2)
     blk.forward(x, idx, probs)
@@ -278,6 +283,102 @@ def test_full_size_mx_sampled(name):
         assert_mx_near(q, sc, ref, what, code_frac=0.05, far_frac=0.01, scale_frac=1.0)
     n_scale = sum(int(np.any(sc != ref[1])) for q, sc, ref, what in mx_checks)
     assert n_scale <= len(mx_checks) // 4, f"{n_scale} of {len(mx_checks)} block scales differ"
+
+
+def _unpack4(b):
+    b = np.asarray(b, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def _mx4_copies_exact(blk, rt, prefix, bf16_t, n, blocks, what):
+    """The fused MXFP4 copies (rowwise along n, transposed along M) of whole
+    sampled 32-row blocks against the oracle's MXFP4 encoding of the GPU's
+    own bf16 rows (pad rows as zeros), bit for bit."""
+    M_cap = blk.M_cap
+    valid = rt.row_src >= 0
+    sidx = mx_scale_index(M_cap, n)
+    sidx_t = mx_scale_index(n, M_cap)
+    q = getattr(blk, prefix + "_q4").view(M_cap, n // 2)
+    sc = getattr(blk, prefix + "_s4").cpu().numpy()
+    qT = getattr(blk, prefix + "T_q4").view(n, M_cap // 2)
+    sT = getattr(blk, prefix + "T_s4").cpu().numpy()
+    for b in blocks:
+        r = np.arange(32 * b, 32 * b + 32)
+        rows = torch.as_tensor(r, device="cuda")
+        v = rows_with_pad_zeroed(nu.bf16_to_f64(_bits(bf16_t[rows])), valid[r])
+        codes, scales = nu.mxfp4_quantize(v, axis=1)
+        np.testing.assert_array_equal(sc[sidx[r]], scales, err_msg=f"{what} rowwise scales {b}")
+        np.testing.assert_array_equal(q[rows].cpu().numpy(), nu.pack_nibbles(codes),
+                                      err_msg=f"{what} rowwise codes {b}")
+        codes, scales = nu.mxfp4_quantize(v.T, axis=1)
+        np.testing.assert_array_equal(sT[sidx_t[:, b:b + 1]], scales,
+                                      err_msg=f"{what} transposed scales {b}")
+        np.testing.assert_array_equal(qT[:, 16 * b:16 * b + 16].cpu().numpy(),
+                                      nu.pack_nibbles(codes), err_msg=f"{what} transposed codes {b}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["mixtral", "gptoss"])
+def test_full_size_mxfp4_sampled(name):
+    """The fused MXFP4 layer at the full Mixtral and GPT-OSS sizes: routing
+    in full; the MXFP4 copies of a and dz (rowwise and transposed) on whole
+    sampled 32-row blocks, bit-exact against the oracle's encoding of the
+    GPU's own bf16 rows; the permuted input rows' MXFP4 copy bit-exact; and
+    sampled (row, column) outputs z, a and dz against the oracle on MXFP4
+    operands (the weight rows or columns involved, encoded along their K)."""
+    cfg, blk, (x, dout, w1, w2, idx, probs), rt, op = _run(name, "mxfp4")
+    H, I = cfg["H"], cfg["I"]
+    M_cap = blk.M_cap
+    _amax_property(blk)
+    blocks = _sample_row_blocks(rt, 6, seed=3 + len(name))
+    print(f"checking the MXFP4 copies of a and dz on row blocks {blocks}", flush=True)
+    _mx4_copies_exact(blk, rt, "a", blk.a, I, blocks, "a")
+    _mx4_copies_exact(blk, rt, "dz", blk.dz, 2 * I, blocks, "dz")
+    rng = np.random.default_rng(12)
+    valid_rows = np.flatnonzero(rt.row_src >= 0)
+    rows = np.sort(rng.choice(valid_rows, size=12, replace=False))
+    cblocks = np.sort(rng.choice(I // 32, size=2, replace=False))
+    cols = np.concatenate([32 * b + np.arange(32) for b in cblocks])
+    expert = om.expert_of_rows(rt)
+    packed = np.argsort(om.interleave_rows(I))
+    sidx_x = mx_scale_index(M_cap, H)
+    xq_g = blk.xp_q4.view(M_cap, H // 2)[torch.as_tensor(rows, device="cuda")].cpu().numpy()
+    xs_g = blk.xp_s4.cpu().numpy()
+    sel = torch.as_tensor(rows, device="cuda")
+    z_g = nu.bf16_to_f64(_bits(blk.z[sel]))
+    a_g = nu.bf16_to_f64(_bits(blk.a[sel]))
+    dz_g = nu.bf16_to_f64(_bits(blk.dz[sel]))
+    z_ref, z_got, a_ref, a_got, dz_ref, dz_got = [], [], [], [], [], []
+    for n_, r in enumerate(rows):
+        t, e = int(rt.row_src[r]), int(expert[r])
+        p = float(rt.probs_p[r])
+        xr = nu.bf16_to_f64(_bits(x[t]))
+        codes, scales = nu.mxfp4_quantize(xr[None, :], axis=1)
+        np.testing.assert_array_equal(xq_g[n_], nu.pack_nibbles(codes)[0], err_msg=f"xp row {r}")
+        np.testing.assert_array_equal(xs_g[sidx_x[r]], scales[0], err_msg=f"xp scales row {r}")
+        xq = nu.mxfp4_round(xr[None, :], axis=1)[0]
+        w1e = w1[e]
+        g_rows = nu.mxfp4_round(nu.bf16_to_f64(_bits(w1e[torch.as_tensor(cols, device="cuda")])), 1)
+        u_rows = nu.mxfp4_round(nu.bf16_to_f64(_bits(w1e[torch.as_tensor(I + cols, device="cuda")])), 1)
+        zg, zu = g_rows @ xq, u_rows @ xq
+        z_ref += [om.round_bf16(zg), om.round_bf16(zu)]
+        z_got += [z_g[n_][packed[cols]], z_g[n_][packed[I + cols]]]
+        s_half = om.act_forward(np.concatenate([zg, zu])[None, :], op)[0]
+        a_ref.append(om.round_bf16(p * s_half))
+        a_got.append(a_g[n_][cols])
+        dr = nu.bf16_to_f64(_bits(dout[t]))
+        dq = nu.mxfp4_round(dr[None, :], axis=1)[0]
+        w2c = nu.bf16_to_f64(_bits(w2[e][:, torch.as_tensor(cols, device="cuda")].contiguous()))
+        da = dq @ nu.mxfp4_round(w2c, axis=0)
+        zs = np.concatenate([om.round_bf16(zg), om.round_bf16(zu)])[None, :]
+        dz_ref.append(om.round_bf16(om.act_backward(zs, p * da[None, :], op)[0]))
+        dz_got.append(np.concatenate([dz_g[n_][packed[cols]], dz_g[n_][packed[I + cols]]]))
+    assert_close_mx(np.concatenate(z_got), np.concatenate(z_ref), "z samples")
+    assert_close_mx(np.concatenate(a_got), np.concatenate(a_ref), "a samples")
+    assert_close_mx(np.concatenate(dz_got), np.concatenate(dz_ref), "dz samples")
 
 
 @pytest.mark.timeout(900)
