@@ -1,7 +1,7 @@
 """Benchmark of the fused grouped-MLP MoE expert block on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mixtral]
-                    [--prec bf16|mxfp8]
+                    [--prec bf16|mxfp8|mxfp4] [--cached-weights]
 
 One step = the whole hot path of a training step of one expert layer:
 route + permute (X), FC1 grouped GEMM with the fused SwiGLU + prob-scale
@@ -9,8 +9,11 @@ epilogue, FC2 grouped GEMM, unpermute; permute (dOut), FC2 dgrad grouped GEMM
 with the fused dSwiGLU epilogue, FC1 dgrad grouped GEMM, unpermute (dX) +
 dprobs.  With --prec mxfp8 the permutes write MXFP8 rows, the four GEMMs take
 MXFP8 operands and the epilogues also write MXFP8 copies (rowwise and
-transposed) of a and dz; the MXFP8 weight copies are made once, outside the
-step (once per weight update), and timed on their own.  Inputs are
+transposed) of a and dz.  An MX step starts by making the weight copies
+from the bf16 master weights, which change every training step (one pass
+per weight writes both of its copies); --cached-weights reuses copies made
+before the step instead (as over the microbatches of one optimizer step)
+and times the quantization on its own.  Inputs are
 synthetic (seeded), already resident in HBM when the timed region starts.
 The value is algorithmic GEMM TFLOP/s of the step: 12 * M * H * I flops (18 with
 --wgrad, which adds the weight-gradient GEMMs)
@@ -471,6 +474,13 @@ def measure(args, config, prec, log_prefix=""):
     if args.recompute:
         ev_rc = n_ev
         n_ev += 1
+    # MX layers start the step by quantizing the bf16 master weights (they
+    # change every training step); the event after it opens the routing
+    qw_in_step = prec != "bf16" and not args.cached_weights
+    ev_qw = None
+    if qw_in_step:
+        ev_qw = n_ev
+        n_ev += 1
 
     def cur_stream():
         return torch.cuda.current_stream().cuda_stream
@@ -482,11 +492,18 @@ def measure(args, config, prec, log_prefix=""):
         def record(self, i):
             self.evs.record(self.base + i, cur_stream())
 
+    def quantize_weights(evs, base):
+        if qw_in_step:
+            blk.quantize_weights()
+            if evs is not None:
+                evs.record(base + ev_qw, cur_stream())
+
     def step_unfused(evs=None, base=0):
         # 0 start; 1-4 forward GEMM / act / GEMM boundaries; 5 after the
         # unpermute; 6-9 backward boundaries; 10 after the dX unpermute
         if evs is not None:
             evs.record(base + 0, cur_stream())
+        quantize_weights(evs, base)
         blk.route(idx, probs, x)
         blk.experts_forward_unfused(None if evs is None else _Rec(evs, base + 1))
         blk.combine(blk.yp, blk.out)
@@ -506,6 +523,7 @@ def measure(args, config, prec, log_prefix=""):
             return step_unfused(evs, base)
         if evs is not None:
             evs.record(base + 0, cur_stream())
+        quantize_weights(evs, base)
         blk.route(idx, probs, x)
         blk.experts_forward(None if evs is None else
                             [evs.ev[base + 1], evs.ev[base + 2], evs.ev[base + 3]])
@@ -599,19 +617,22 @@ def measure(args, config, prec, log_prefix=""):
     def seg(a, b):
         return sum(evs.elapsed_ms(n_ev * i + a, n_ev * i + b) for i in range(n_eager)) / n_eager
 
+    r0 = ev_qw if qw_in_step else 0    # the routing starts after the weight quantization
     if args.unfused:
-        seg_ms = {"route_permute_x": seg(0, 1), "fc1": seg(1, 2), "act_fwd": seg(2, 3),
+        seg_ms = {"route_permute_x": seg(r0, 1), "fc1": seg(1, 2), "act_fwd": seg(2, 3),
                   "fc2": seg(3, 4), "unpermute_out": seg(4, 5), "permute_dout": seg(5, 6),
                   "fc2_dgrad": seg(6, 7), "act_bwd": seg(7, 8), "fc1_dgrad": seg(8, 9),
                   "unpermute_dx": seg(9, 10)}
     else:
-        seg_ms = {"route_permute_x": seg(0, 1), "fc1": seg(1, 2), "fc2": seg(2, 3),
+        seg_ms = {"route_permute_x": seg(r0, 1), "fc1": seg(1, 2), "fc2": seg(2, 3),
                   "unpermute_out": seg(3, 4), "permute_dout": seg(4, 5),
                   "fc2_dgrad": seg(5, 6), "fc1_dgrad": seg(6, 7), "unpermute_dx": seg(7, 8)}
     if args.wgrad:
         seg_ms.update(wgrad_quantize=seg(8, 9), wgrad_dw1=seg(9, 10), wgrad_dw2=seg(10, 11))
     if args.recompute:
         seg_ms.update(permute_dout=seg(4, ev_rc), fc1_recompute=seg(ev_rc, 5))
+    if qw_in_step:
+        seg_ms["quantize_weights"] = seg(0, ev_qw)
     evs.close()
     assert int(blk.err_flag.cpu()[0]) == 0
     value = flops_step / (ms_step * 1e-3) / 1e12
@@ -646,11 +667,16 @@ def measure(args, config, prec, log_prefix=""):
     if args.wgrad and (mx or prec == "mxfp4"):
         # MX transposed copies of Xp and dYp (bf16 in, codes + scales out)
         mem["wgrad_quantize"] = 2 * M * H * (2 + (1 if mx else 0.5) + 1 / 32)
+    if qw_in_step:
+        # the two weights read once each, both MX copies of each written
+        n_w = E * n1 * H + E * H * I
+        mem["quantize_weights"] = n_w * (2 + 2 * ((1 if mx else 0.5) + 1 / 32))
     for name, b in mem.items():
         kernels[name] = {"ms": round(seg_ms[name], 4), "unit": "GB/s",
                          "rate": round(b / (seg_ms[name] * 1e-3) / 1e9, 1)}
-    if mx or prec == "mxfp4":
-        # MX weight copies (once per weight update; not part of the step)
+    if (mx or prec == "mxfp4") and not qw_in_step:
+        # MX weight copies, timed on their own (--cached-weights: the step
+        # reuses copies made before it)
         qe = HipEvents(2)
         reps = 5
         qe.record(0, stream)
@@ -660,8 +686,8 @@ def measure(args, config, prec, log_prefix=""):
         torch.cuda.synchronize()
         q_ms = qe.elapsed_ms(0, 1) / reps
         qe.close()
-        n_w = 2 * (E * n1 * H + E * H * I)        # elements quantized (4 copies)
-        q_bytes = n_w * (2 + (1 if mx else 0.5) + 1 / 32)
+        n_w = E * n1 * H + E * H * I             # both copies of each weight in one pass
+        q_bytes = n_w * (2 + 2 * ((1 if mx else 0.5) + 1 / 32))
         kernels["quantize_weights"] = {"ms": round(q_ms, 4), "unit": "GB/s",
                                        "rate": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
                                        "outside_step": True}
@@ -822,6 +848,10 @@ def main():
                          "activation and its gradient as separate passes")
     ap.add_argument("--gemm", action="store_true",
                     help="time the FC2-shaped plain grouped GEMM in bf16, MXFP8 and MXFP4")
+    ap.add_argument("--cached-weights", action="store_true",
+                    help="MX layers: reuse weight copies made before the step (as over "
+                         "the microbatches of one optimizer step) instead of quantizing "
+                         "the bf16 master weights inside it")
     ap.add_argument("--recompute", action="store_true",
                     help="activation recompute: the forward stores no z, the backward "
                          "rebuilds it with FC1's GEMM (timed as fc1_recompute)")
@@ -872,8 +902,8 @@ def main():
         pk8 = PEAK_TFLOPS["mxfp8"]
         secondary = {
             "config": "mixtral_mx expert layer, MXFP8 operands (E4M3 with E8M0 scales per 32 "
-                      "along K), fused quantize + transposed copies in the FC1 and dSwiGLU "
-                      "epilogues",
+                      "along K), bf16 master weights quantized inside the step, fused quantize "
+                      "+ transposed copies in the FC1 and dSwiGLU epilogues",
             "value": round(s["value"], 3), "unit": "TFLOP/s", "ms_per_step": round(s["ms_step"], 4),
             "pct_mfma_peak": round(100.0 * s["value"] / pk8, 2), "timing": s["timing"],
             "pct_mfma_peak_at_measured_clock": (
@@ -916,7 +946,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.config} expert layer: E={E} top-{k} T={T} H={H} "
                                f"I={I} {cfg['act']} beta={cfg['beta']} clamp={cfg['clamp']}, "
-                               f"{prec}, route+permute+FC1+FC2+unpermute and backward "
+                               f"{prec}, "
+                               f"{'weight quantization (bf16 masters -> MX copies)+' if prec != 'bf16' and not args.cached_weights else ''}"
+                               f"route+permute+FC1+FC2+unpermute and backward "
                                f"(FC2 dgrad+dAct, FC1 dgrad, dX, dprobs"
                                f"{', dW1, dW2' if args.wgrad else ''})"
                                f"{'; unfused baseline (plain GEMMs + separate activation passes)' if args.unfused else ''}"

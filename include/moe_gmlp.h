@@ -235,15 +235,20 @@ moe_status moe_unpermute(const moe_unpermute_args* args, void* stream);
  *   MOE_QUANT_COL: blocks along rows, written transposed so that the
  *     consumer's K = rows is contiguous: q [batch][cols][rows], scales
  *     tiled with R = cols, K = rows.
+ *   MOE_QUANT_BOTH: ROW into q / s and COL into qT / sT in one pass that
+ *     reads x once ([TE] § "Challenge 3": the master weights are cast for
+ *     every step, so the two copies of a weight are made together).
  *   The weight copies the MXFP8 forward and backward read are
  *     ROW of w1i (K = H), ROW of w2 (K = I), COL of w2 (K = H) and COL of
- *     w1i (K = N1).
+ *     w1i (K = N1): BOTH of w1i and BOTH of w2.
  *   rows and cols must be multiples of 64.  If amax != NULL, *amax is raised
  *   to max|x| (the caller zeroes it first).  Memory-bound: reads 2 bytes and
- *   writes 33/32 bytes per element.
+ *   writes 33/32 bytes per element and copy.  qT and sT are read only in
+ *   the BOTH mode.
  * ---------------------------------------------------------------------- */
 #define MOE_QUANT_ROW 0
 #define MOE_QUANT_COL 1
+#define MOE_QUANT_BOTH 2
 
 typedef struct moe_quant_args {
   int32_t mode;
@@ -253,6 +258,8 @@ typedef struct moe_quant_args {
   uint8_t* q;                  /* device */
   uint8_t* s;                  /* device */
   float* amax;                 /* optional device float */
+  uint8_t* qT;                 /* device, MOE_QUANT_BOTH: the COL codes */
+  uint8_t* sT;                 /* device, MOE_QUANT_BOTH: the COL scales */
 } moe_quant_args;
 
 moe_status moe_quantize_mxfp8(const moe_quant_args* args, void* stream);
@@ -274,6 +281,8 @@ moe_status moe_quantize_mxfp8(const moe_quant_args* args, void* stream);
  *     tiled with R = rows, K = cols.
  *   MOE_QUANT_COL: blocks along rows, written transposed: q
  *     [batch][cols][rows / 2], scales tiled with R = cols, K = rows
+ *     (rows % 64 == 0).
+ *   MOE_QUANT_BOTH: ROW into q / s and COL into qT / sT, one pass
  *     (rows % 64 == 0).
  *   rows % 32 == 0, cols % 64 == 0; amax must be NULL.  Memory-bound: reads
  *   2 bytes, writes 17/32 bytes per element.

@@ -11,7 +11,7 @@ from .binding import (  # noqa: F401
     ERR_DEVICE, ERR_INVALID_ARG, ERR_LAUNCH, ERR_UNSUPPORTED, ERR_WORKSPACE,
     GROUP_ALIGN, INTERLEAVE, MX_BLOCK,
     PERMUTE_BUILD_MAP, PERMUTE_GATHER, PERMUTE_WRITE_MX, PERMUTE_WRITE_MX4, PREC_BF16,
-    PREC_MXFP4, PREC_MXFP8, QUANT_COL, QUANT_ROW, MoeError, act_params, lib, lib_path,
+    PREC_MXFP4, PREC_MXFP8, QUANT_BOTH, QUANT_COL, QUANT_ROW, MoeError, act_params, lib, lib_path,
     DEVERR_SYNC_TIMEOUT, DEVERR_BAD_OFFSETS, NOALLOC_SCRATCH_BYTES,
     moe_grouped_mlp_bwd, moe_grouped_mlp_bwd_noalloc, moe_grouped_mlp_fwd,
     moe_grouped_mlp_wgrad, moe_router_topk, moe_router_route,

@@ -19,7 +19,7 @@ ACT_SWIGLU, ACT_GEGLU, ACT_SRELU = 0, 1, 2
 PREC_BF16, PREC_MXFP8, PREC_MXFP4 = 0, 1, 2
 PERMUTE_BUILD_MAP, PERMUTE_GATHER, PERMUTE_WRITE_MX = 0x1, 0x2, 0x4
 PERMUTE_WRITE_MX4 = 0x8
-QUANT_ROW, QUANT_COL = 0, 1
+QUANT_ROW, QUANT_COL, QUANT_BOTH = 0, 1, 2
 GROUP_ALIGN = 128
 INTERLEAVE = 64
 MX_BLOCK = 32
@@ -76,7 +76,8 @@ class UnpermuteArgs(ctypes.Structure):
 class QuantArgs(ctypes.Structure):
     _fields_ = [("mode", c_int32), ("batch", c_int32), ("rows", c_int32),
                 ("cols", c_int32), ("x_stride", c_int64), ("x", c_void_p),
-                ("q", c_void_p), ("s", c_void_p), ("amax", c_void_p)]
+                ("q", c_void_p), ("s", c_void_p), ("amax", c_void_p),
+                ("qT", c_void_p), ("sT", c_void_p)]
 
 
 class FwdArgs(ctypes.Structure):
@@ -296,16 +297,17 @@ def moe_unpermute(*, T, k, H, M_cap, row_id_map, yp, out, dprobs_p=None,
 
 
 def moe_quantize_mxfp8(*, mode, batch, rows, cols, x, q, s, x_stride=0,
-                       amax=None, stream=None):
+                       amax=None, qT=None, sT=None, stream=None):
     a = QuantArgs(mode, batch, rows, cols, x_stride, _ptr(x), _ptr(q), _ptr(s),
-                  _ptr(amax))
+                  _ptr(amax), _ptr(qT), _ptr(sT))
     _check("moe_quantize_mxfp8",
            lib().moe_quantize_mxfp8(ctypes.byref(a), _stream(stream)))
 
 
 def moe_quantize_mxfp4(*, batch, rows, cols, x, q, s, mode=QUANT_ROW, x_stride=0,
-                       stream=None):
-    a = QuantArgs(mode, batch, rows, cols, x_stride, _ptr(x), _ptr(q), _ptr(s), None)
+                       qT=None, sT=None, stream=None):
+    a = QuantArgs(mode, batch, rows, cols, x_stride, _ptr(x), _ptr(q), _ptr(s), None,
+                  _ptr(qT), _ptr(sT))
     _check("moe_quantize_mxfp4",
            lib().moe_quantize_mxfp4(ctypes.byref(a), _stream(stream)))
 

@@ -229,27 +229,23 @@ class ExpertBlock:
             self.quantize_weights()
 
     def quantize_weights(self) -> None:
-        """MXFP8 copies of the bf16 weights, each blocked along the K of the
+        """MX copies of the bf16 weights, each blocked along the K of the
         GEMM that reads it: W1i along H (FC1), W2 along I (FC2), W2 along H
         (FC2 dgrad, stored [E][I][H]) and W1i along N1 (FC1 dgrad, stored
-        [E][H][N1])."""
+        [E][H][N1]).  In training the bf16 master weights change every step,
+        so a step starts with this (bench.py times it inside the step)."""
         E, H, I, N1 = self.E, self.H, self.I, self.N1
+        # one pass per weight writes both of its copies (ROW into q / s, COL
+        # into qT / sT), reading the bf16 weight once
         if self.mx4:
-            for mode, x, rows, cols, q, sc in (
-                    (B.QUANT_ROW, self.w1i, N1, H, self.w1_q4, self.w1_s4),
-                    (B.QUANT_ROW, self.w2, H, I, self.w2_q4, self.w2_s4),
-                    (B.QUANT_COL, self.w2, H, I, self.w2t_q4, self.w2t_s4),
-                    (B.QUANT_COL, self.w1i, N1, H, self.w1t_q4, self.w1t_s4)):
-                B.moe_quantize_mxfp4(mode=mode, batch=E, rows=rows, cols=cols, x=x, q=q,
-                                     s=sc)
-            return
-        for mode, x, rows, cols, q, sc in (
-                (B.QUANT_ROW, self.w1i, N1, H, self.w1_q, self.w1_s),
-                (B.QUANT_ROW, self.w2, H, I, self.w2_q, self.w2_s),
-                (B.QUANT_COL, self.w2, H, I, self.w2t_q, self.w2t_s),
-                (B.QUANT_COL, self.w1i, N1, H, self.w1t_q, self.w1t_s)):
-            B.moe_quantize_mxfp8(mode=mode, batch=E, rows=rows, cols=cols, x=x,
-                                 q=q, s=sc)
+            sfx, quant = "4", B.moe_quantize_mxfp4
+        else:
+            sfx, quant = "", B.moe_quantize_mxfp8
+        for x, rows, cols, row_copy, col_copy in ((self.w1i, N1, H, "w1", "w1t"),
+                                                  (self.w2, H, I, "w2", "w2t")):
+            quant(mode=B.QUANT_BOTH, batch=E, rows=rows, cols=cols, x=x,
+                  q=getattr(self, row_copy + "_q" + sfx), s=getattr(self, row_copy + "_s" + sfx),
+                  qT=getattr(self, col_copy + "_q" + sfx), sT=getattr(self, col_copy + "_s" + sfx))
 
     # ------------------------------------------------------------ forward --
     def route(self, expert_idx: torch.Tensor, probs: torch.Tensor,

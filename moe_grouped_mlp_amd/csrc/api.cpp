@@ -198,9 +198,9 @@ int64_t moe_mx_scale_offset(int64_t r, int64_t b, int64_t K) {
 }
 
 moe_status moe_quantize_mxfp8(const moe_quant_args* a, void* stream) {
-  if (!a || (a->mode != MOE_QUANT_ROW && a->mode != MOE_QUANT_COL) || a->batch < 0 ||
+  if (!a || a->mode < MOE_QUANT_ROW || a->mode > MOE_QUANT_BOTH || a->batch < 0 ||
       a->rows < 64 || a->cols < 64 || a->rows % 64 != 0 || a->cols % 64 != 0 || !a->x || !a->q ||
-      !a->s)
+      !a->s || (a->mode == MOE_QUANT_BOTH && (!a->qT || !a->sT)))
     return MOE_ERR_INVALID_ARG;
   const int64_t n = static_cast<int64_t>(a->rows) * a->cols;
   if (a->x_stride != 0 && (a->x_stride < n || a->x_stride % 8 != 0)) return MOE_ERR_INVALID_ARG;
@@ -213,11 +213,11 @@ moe_status moe_quantize_mxfp8(const moe_quant_args* a, void* stream) {
 }
 
 moe_status moe_quantize_mxfp4(const moe_quant_args* a, void* stream) {
-  if (!a || (a->mode != MOE_QUANT_ROW && a->mode != MOE_QUANT_COL) || a->batch < 0 ||
+  if (!a || a->mode < MOE_QUANT_ROW || a->mode > MOE_QUANT_BOTH || a->batch < 0 ||
       a->rows < 32 || a->cols < 64 || a->rows % 32 != 0 || a->cols % 64 != 0 || !a->x || !a->q ||
-      !a->s || a->amax)
+      !a->s || a->amax || (a->mode == MOE_QUANT_BOTH && (!a->qT || !a->sT)))
     return MOE_ERR_INVALID_ARG;
-  if (a->mode == MOE_QUANT_COL && a->rows % 64 != 0) return MOE_ERR_INVALID_ARG;
+  if (a->mode != MOE_QUANT_ROW && a->rows % 64 != 0) return MOE_ERR_INVALID_ARG;
   const int64_t n = static_cast<int64_t>(a->rows) * a->cols;
   if (a->x_stride != 0 && (a->x_stride < n || a->x_stride % 8 != 0)) return MOE_ERR_INVALID_ARG;
   int cu = 0;

@@ -1,13 +1,19 @@
-// MXFP8 encoding helpers (E4M3 values, one E8M0 scale per 32 values).
+// Microscaling encoding helpers: MXFP8 (E4M3 values) and MXFP4 (E2M1
+// values), one E8M0 scale per 32 values.
 //
-// The block rule: e = clamp(floor(log2 max|v|) - 8, -127, 127) (-127 for an
-// all-zero block), scale code e + 127, code = E4M3 round-to-nearest-even of
-// v / 2^e saturated to +-448 (TE + BioNeMo Mixtral tutorial, § "Challenge 2:
-// model size and activation memory", Fig. 3).  The inputs are always bf16
-// values, so v / 2^e is exact in fp32 and the only rounding is the final
-// one, done by v_cvt_pk_fp8_f32 (E4M3 round-to-nearest-even; it turns values
-// past 464 into NaN, so they are clamped to +-448 first, which equals
-// saturating after rounding).
+// The MXFP8 block rule: e = clamp(floor(log2 max|v|) - 8, -127, 127) (-127
+// for an all-zero block), scale code e + 127, code = E4M3 round-to-nearest-
+// even of v / 2^e saturated to +-448 (TE + BioNeMo Mixtral tutorial,
+// § "Challenge 2: model size and activation memory", Fig. 3).  MXFP4 takes
+// e = floor(log2 max|v|) - 2 (2 being the exponent of E2M1's largest value,
+// 6) and the E2M1 round-to-nearest-even value of v / 2^e, saturated to +-6.
+// The inputs are always bf16 values, so v / 2^e is exact and the only
+// rounding is the conversion's: gfx950's scaled conversions of packed bf16
+// words (v_cvt_scalef32_pk_{fp8,fp4}_bf16), which divide by a power-of-two
+// scale and round to nearest even.  They were checked against the block
+// rule on every finite bf16 value at every scale exponent: the FP4 one
+// matches it, the FP8 one except that it gives NaN where the rule saturates
+// (mx_codes4_bf16 corrects that).
 #pragma once
 
 #include "common.h"
@@ -23,20 +29,19 @@ MOE_DEV int mx_exponent(float amax) {
   return e < -127 ? -127 : e;
 }
 
-// 2^-e as an fp32 (normal for every e mx_exponent returns).
-MOE_DEV float mx_inv_scale(int e) { return __uint_as_float(static_cast<uint32_t>(127 - e) << 23); }
+// The MXFP4 block exponent (see above), at least -127.
+MOE_DEV int mx4_exponent(float amax) {
+  const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 127 - 2;
+  return e < -127 ? -127 : e;
+}
 
 MOE_DEV uint8_t mx_scale_code(int e) { return static_cast<uint8_t>(e + 127); }
 
-// Four values times 2^-e -> four E4M3 codes, little-endian in one word.
-MOE_DEV uint32_t mx_codes4(float a, float b, float c, float d, float inv) {
-  a = __builtin_amdgcn_fmed3f(a * inv, -448.0f, 448.0f);
-  b = __builtin_amdgcn_fmed3f(b * inv, -448.0f, 448.0f);
-  c = __builtin_amdgcn_fmed3f(c * inv, -448.0f, 448.0f);
-  d = __builtin_amdgcn_fmed3f(d * inv, -448.0f, 448.0f);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return static_cast<uint32_t>(w);
+// 2^e as an fp32, exactly (2^-127 as the subnormal it is): the scale
+// operand of the scaled conversions, which divide by it.
+MOE_DEV float mx_scale_f32(int e) {
+  return e > -127 ? __uint_as_float(static_cast<uint32_t>(e + 127) << 23)
+                  : __uint_as_float(0x00400000u);
 }
 
 // Four bf16 values (two packed words, value 0 in the low half of w.x)
@@ -58,44 +63,10 @@ MOE_DEV uint32_t mx_codes4_bf16(uint2 w, float scale) {
   return c - (nan >> 7);
 }
 
-// |v| of a bf16 pattern as an ordered integer (bf16 magnitudes compare like
-// their bit patterns).
-MOE_DEV uint32_t bf16_abs_bits(uint32_t b) { return b & 0x7fffu; }
-
-// ------------------------------------------------------------- MXFP4 ---
-// E2M1 values, one E8M0 scale per 32: e = clamp(floor(log2 max|v|) - 2,
-// -127, ...) (2 is the exponent of E2M1's largest value, 6), codes the
-// round-to-nearest-even E2M1 value of v / 2^e, saturated to +-6.  The
-// inputs are bf16 values, so v / 2^e is exact in fp32.
-
-MOE_DEV int mx4_exponent(float amax) {
-  const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 127 - 2;
-  return e < -127 ? -127 : e;
-}
-
-// E2M1 code of a scaled value, round to nearest even, 6 for |v| > 5: one
-// step up at each midpoint, ties (0.25, 1.25, 2.5, 5) staying on the even
-// code and (0.75, 1.75, 3.5) moving up to it.
-MOE_DEV uint32_t e2m1_code(float v) {
-  const float a = fabsf(v);
-  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
-               (a >= 3.5f) + (a > 5.0f);
-  return c | ((__float_as_uint(v) >> 28) & 8u);
-}
-
-// 2^e as an fp32, exactly (2^-127 as the subnormal it is): the scale
-// operand of gfx950's scaled conversions, which divide by it.
-MOE_DEV float mx_scale_f32(int e) {
-  return e > -127 ? __uint_as_float(static_cast<uint32_t>(e + 127) << 23)
-                  : __uint_as_float(0x00400000u);
-}
-
 // Four bf16 values (two packed words, value 0 in the low half of w.x)
 // divided by 2^e -> four E2M1 codes in the low 16 bits, value i in nibble
 // i: v_cvt_scalef32_pk_fp4_bf16, which divides by the scale, rounds to
-// nearest even and saturates at +-6 with the sign kept, the block rule
-// above (a bf16 value over a power of two is exact, so its one rounding is
-// the conversion's).
+// nearest even and saturates at +-6 with the sign kept, the block rule.
 MOE_DEV uint32_t mx4_codes4_bf16(uint2 w, float scale) {
   const uint32_t c =
       __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2_t, w.x), scale, 0);
@@ -103,11 +74,9 @@ MOE_DEV uint32_t mx4_codes4_bf16(uint2 w, float scale) {
                                                    1);
 }
 
-// Four values times 2^-e -> four E2M1 codes, value i in nibble i.
-MOE_DEV uint32_t mx4_codes4(float a, float b, float c, float d, float inv) {
-  return e2m1_code(a * inv) | (e2m1_code(b * inv) << 4) | (e2m1_code(c * inv) << 8) |
-         (e2m1_code(d * inv) << 12);
-}
+// |v| of a bf16 pattern as an ordered integer (bf16 magnitudes compare like
+// their bit patterns).
+MOE_DEV uint32_t bf16_abs_bits(uint32_t b) { return b & 0x7fffu; }
 
 // Byte offset of the scale of row r, K-block b in the tiled scale layout of
 // an [R][K] operand (see MOE_MX_BLOCK in moe_gmlp.h).

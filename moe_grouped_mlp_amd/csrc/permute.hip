@@ -59,20 +59,15 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
           m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 2, kWave)));
           const float am = __uint_as_float(m << 16);
           const int e = F4 ? mx4_exponent(am) : mx_exponent(am);
-          const float inv = mx_inv_scale(e);
-          const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
-          const float f[8] = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xffff0000u),
-                              __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xffff0000u),
-                              __uint_as_float(w2 << 16), __uint_as_float(w2 & 0xffff0000u),
-                              __uint_as_float(w3 << 16), __uint_as_float(w3 & 0xffff0000u)};
+          const float scale = mx_scale_f32(e);
+          const uint2 lo = make_uint2(v[0], v[1]), hi = make_uint2(v[2], v[3]);
           uint2 q;
           if constexpr (F4) {
-            q.x = mx4_codes4(f[0], f[1], f[2], f[3], inv) |
-                  (mx4_codes4(f[4], f[5], f[6], f[7], inv) << 16);
+            q.x = mx4_codes4_bf16(lo, scale) | (mx4_codes4_bf16(hi, scale) << 16);
             q.y = 0;
           } else {
-            q.x = mx_codes4(f[0], f[1], f[2], f[3], inv);
-            q.y = mx_codes4(f[4], f[5], f[6], f[7], inv);
+            q.x = mx_codes4_bf16(lo, scale);
+            q.y = mx_codes4_bf16(hi, scale);
           }
 #pragma unroll
           for (int s = 0; s < kMaxTopK; ++s) {

@@ -10,9 +10,11 @@
 // reduction and the unit's 64 scale bytes are one contiguous store.
 //   ROW  blocks along the contiguous axis: lane l reads 64 contiguous bytes
 //        of row l % 32 (its block l / 32) with four 16-byte loads.
-//   COL  blocks along rows, output transposed: a workgroup stages a 64-row
-//        x 128-column slice of x in LDS; thread t encodes column t % 128 over
-//        rows 32 (t / 128) .. +31 and writes those 32 codes contiguously.
+//   COL  blocks along rows, output transposed: a workgroup stages a 128-row
+//        x 128-column slice of x in LDS; a thread encodes one column over 32
+//        rows and writes those 32 codes contiguously.
+//   BOTH the COL kernel also encodes the staged slice along its rows (a
+//        thread per row block), so x is read once for both copies.
 #include "common.h"
 #include "kernels.h"
 #include "mx.h"
@@ -21,7 +23,8 @@ namespace moe {
 namespace {
 
 // Encodes 32 bf16 values (as 16 packed words) into 32 codes (8 words);
-// returns the scale exponent.
+// returns the scale exponent.  The codes come from gfx950's scaled
+// conversion of the packed words (mx_codes4_bf16).
 MOE_DEV int mx_encode32(const uint32_t (&w)[16], uint32_t (&codes)[8]) {
   uint32_t m = 0;
 #pragma unroll
@@ -30,13 +33,9 @@ MOE_DEV int mx_encode32(const uint32_t (&w)[16], uint32_t (&codes)[8]) {
     m = max(m, bf16_abs_bits(w[i] >> 16));
   }
   const int e = mx_exponent(__uint_as_float(m << 16));
-  const float inv = mx_inv_scale(e);
+  const float scale = mx_scale_f32(e);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t u = w[2 * i], v = w[2 * i + 1];
-    codes[i] = mx_codes4(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u),
-                         __uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u), inv);
-  }
+  for (int i = 0; i < 8; ++i) codes[i] = mx_codes4_bf16(make_uint2(w[2 * i], w[2 * i + 1]), scale);
   return e;
 }
 
@@ -90,54 +89,73 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restri
 // Encodes 32 bf16 values (16 packed words) into 32 E2M1 codes (4 words,
 // element 2 i in the low nibble of byte i); returns the scale exponent
 // floor(log2 amax) - 2 (2 being the exponent of E2M1's largest value 6),
-// clamped to -127.  The bf16 input times 2^-e is exact in fp32.
+// clamped to -127.  The codes come from gfx950's scaled conversion of the
+// packed words (mx4_codes4_bf16).
 MOE_DEV int mx4_encode32(const uint32_t (&w)[16], uint32_t (&packed)[4]) {
   uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) m = max(m, max(bf16_abs_bits(w[i]), bf16_abs_bits(w[i] >> 16)));
-  int e = static_cast<int>((m >> 7) & 0xffu) - 127 - 2;
-  e = e < -127 ? -127 : e;
-  const float inv = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+  const int e = mx4_exponent(__uint_as_float(m << 16));
+  const float scale = mx_scale_f32(e);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t p = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t b = w[4 * i + j];
-      p |= e2m1_code(__uint_as_float(b << 16) * inv) << (8 * j);
-      p |= e2m1_code(__uint_as_float(b & 0xffff0000u) * inv) << (8 * j + 4);
-    }
-    packed[i] = p;
-  }
+  for (int i = 0; i < 4; ++i)
+    packed[i] = mx4_codes4_bf16(make_uint2(w[4 * i], w[4 * i + 1]), scale) |
+                (mx4_codes4_bf16(make_uint2(w[4 * i + 2], w[4 * i + 3]), scale) << 16);
   return e;
 }
 
 // x [batch][rows][cols] -> q [batch][cols][rows], s tiled (R = cols, K = rows);
-// F4: MXFP4 codes, q [batch][cols][rows / 2], no amax
-constexpr int kColTileR = 64, kColTileC = 128;
+// F4: MXFP4 codes, q [batch][cols][rows / 2], no amax.
+// ROW (the BOTH mode): also qr [batch][rows][cols] (F4: cols / 2 bytes a row),
+// sr tiled (R = rows, K = cols), from the same staged slice.
+constexpr int kColTileR = 128, kColTileC = 128;
 constexpr int kColPitch = kColTileC + 2;  // bf16 per LDS row (odd word stride)
 
+// Encodes one 32-value block (16 packed bf16 words) and stores its codes
+// (MXFP8: 32 bytes, MXFP4: 16) at dst; returns the scale exponent.
 template <bool F4>
+MOE_DEV int encode_store32(const uint32_t (&w)[16], uint8_t* dst) {
+  if constexpr (F4) {
+    uint32_t packed[4];
+    const int e = mx4_encode32(w, packed);
+    *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    return e;
+  } else {
+    uint32_t codes[8];
+    const int e = mx_encode32(w, codes);
+    reinterpret_cast<uint4*>(dst)[0] = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+    reinterpret_cast<uint4*>(dst)[1] = make_uint4(codes[4], codes[5], codes[6], codes[7]);
+    return e;
+  }
+}
+
+// A workgroup stages a slice of up to 128 rows x 128 columns: a column's
+// codes of the slice (128 rows) are then one whole 128-byte line (MXFP8).
+template <bool F4, bool ROW>
 __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restrict__ x,
                                                         int64_t x_stride, int batch, int rows,
                                                         int cols, uint8_t* __restrict__ q,
                                                         uint8_t* __restrict__ s,
-                                                        float* __restrict__ amax) {
+                                                        float* __restrict__ amax,
+                                                        uint8_t* __restrict__ qr,
+                                                        uint8_t* __restrict__ sr) {
   __shared__ uint16_t tile[kColTileR * kColPitch];
   const int t = threadIdx.x;
-  const int tiles_r = rows / kColTileR;
+  const int tiles_r = (rows + kColTileR - 1) / kColTileR;
   const int tiles_c = (cols + kColTileC - 1) / kColTileC;
   const int64_t tiles = static_cast<int64_t>(batch) * tiles_r * tiles_c;
   const int64_t per_batch_q = static_cast<int64_t>(rows) * cols;
+  constexpr int kDiv = F4 ? 2 : 1;   // values per code byte
   uint32_t wmax = 0;
   for (int64_t id = blockIdx.x; id < tiles; id += gridDim.x) {
     const int bi = static_cast<int>(id / (static_cast<int64_t>(tiles_r) * tiles_c));
     const int rem = static_cast<int>(id % (static_cast<int64_t>(tiles_r) * tiles_c));
     const int r0 = (rem / tiles_c) * kColTileR, c0 = (rem % tiles_c) * kColTileC;
-    const int cw = min(kColTileC, cols - c0);  // multiple of 64
+    const int rr = min(kColTileR, rows - r0);  // 64 or 128
+    const int cw = min(kColTileC, cols - c0);  // 64 or 128
     const uint16_t* xb = x + bi * x_stride;
-    // stage: 64 rows x cw columns, 8 bf16 per thread-iteration
-    for (int i = t; i < kColTileR * (cw / 8); i += 256) {
+    // stage: rr rows x cw columns, 8 bf16 per thread-iteration
+    for (int i = t; i < rr * (cw / 8); i += 256) {
       const int r = i / (cw / 8), c8 = i % (cw / 8);
       const uint4 v = *reinterpret_cast<const uint4*>(xb + static_cast<int64_t>(r0 + r) * cols +
                                                       c0 + 8 * c8);
@@ -145,36 +163,42 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
       d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
     }
     __syncthreads();
-    const int c = t % kColTileC, half = t / kColTileC;
-    if (c < cw) {
+    // COL: column c, rows 32 h .. 32 h + 31 of the slice
+    for (int u = t; u < cw * (rr / 32); u += 256) {
+      const int c = u % cw, h = u / cw;
       uint32_t w[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = 32 * half + 2 * i;
+        const int r = 32 * h + 2 * i;
         w[i] = static_cast<uint32_t>(tile[r * kColPitch + c]) |
                (static_cast<uint32_t>(tile[(r + 1) * kColPitch + c]) << 16);
       }
       const int cc = c0 + c;
-      const int64_t qoff = bi * per_batch_q + static_cast<int64_t>(cc) * rows + r0 + 32 * half;
-      int e;
-      if constexpr (F4) {
-        uint32_t packed[4];
-        e = mx4_encode32(w, packed);
-        *reinterpret_cast<uint4*>(q + qoff / 2) =
-            make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      } else {
-        uint32_t codes[8];
-        e = mx_encode32(w, codes);
-        uint4* dst = reinterpret_cast<uint4*>(q + qoff);
-        dst[0] = make_uint4(codes[0], codes[1], codes[2], codes[3]);
-        dst[1] = make_uint4(codes[4], codes[5], codes[6], codes[7]);
-      }
-      s[bi * (per_batch_q / 32) + mx_scale_off(cc, r0 / 32 + half, rows)] =
+      const int64_t qoff = bi * per_batch_q + static_cast<int64_t>(cc) * rows + r0 + 32 * h;
+      const int e = encode_store32<F4>(w, q + qoff / kDiv);
+      s[bi * (per_batch_q / 32) + mx_scale_off(cc, r0 / 32 + h, rows)] =
           static_cast<uint8_t>(e + 127);
       if (!F4 && amax) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           wmax = max(wmax, max(bf16_abs_bits(w[i]), bf16_abs_bits(w[i] >> 16)));
+      }
+    }
+    if constexpr (ROW) {
+      // row r of the slice, its 32-column block b: consecutive threads take
+      // the blocks of a row, so a wave's reads (rows at a 65-word pitch,
+      // blocks 16 words apart) fall on distinct banks
+      for (int u = t; u < rr * (cw / 32); u += 256) {
+        const int r = u / (cw / 32), b = u % (cw / 32);
+        uint32_t w[16];
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(tile + r * kColPitch + 32 * b);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w[i] = src[i];
+        const int64_t row = r0 + r;
+        const int col = c0 + 32 * b;
+        const int e = encode_store32<F4>(w, qr + (bi * per_batch_q + row * cols + col) / kDiv);
+        sr[bi * (per_batch_q / 32) + mx_scale_off(row, col / 32, cols)] =
+            static_cast<uint8_t>(e + 127);
       }
     }
     __syncthreads();
@@ -239,10 +263,15 @@ hipError_t launch_quantize_mxfp4(const moe_quant_args& a, hipStream_t st) {
     quant_row_fp4_kernel<<<quant_grid(units, 4), 256, 0, st>>>(x, a.x_stride, a.batch, a.rows,
                                                                a.cols, a.q, a.s);
   } else {
-    const int64_t tiles = static_cast<int64_t>(a.batch) * (a.rows / kColTileR) *
+    const int64_t tiles = static_cast<int64_t>(a.batch) * ((a.rows + kColTileR - 1) / kColTileR) *
                           ((a.cols + kColTileC - 1) / kColTileC);
-    quant_col_kernel<true><<<quant_grid(tiles, 1), 256, 0, st>>>(x, a.x_stride, a.batch, a.rows,
-                                                                 a.cols, a.q, a.s, nullptr);
+    // BOTH: the COL copy goes to qT / sT, the ROW copy to q / s
+    if (a.mode == MOE_QUANT_BOTH)
+      quant_col_kernel<true, true><<<quant_grid(tiles, 1), 256, 0, st>>>(
+          x, a.x_stride, a.batch, a.rows, a.cols, a.qT, a.sT, nullptr, a.q, a.s);
+    else
+      quant_col_kernel<true, false><<<quant_grid(tiles, 1), 256, 0, st>>>(
+          x, a.x_stride, a.batch, a.rows, a.cols, a.q, a.s, nullptr, nullptr, nullptr);
   }
   return hipGetLastError();
 }
@@ -254,10 +283,14 @@ hipError_t launch_quantize_mxfp8(const moe_quant_args& a, hipStream_t st) {
     quant_row_kernel<<<quant_grid(units, 4), 256, 0, st>>>(x, a.x_stride, a.batch, a.rows, a.cols,
                                                            a.q, a.s, a.amax);
   } else {
-    const int64_t tiles = static_cast<int64_t>(a.batch) * (a.rows / kColTileR) *
+    const int64_t tiles = static_cast<int64_t>(a.batch) * ((a.rows + kColTileR - 1) / kColTileR) *
                           ((a.cols + kColTileC - 1) / kColTileC);
-    quant_col_kernel<false><<<quant_grid(tiles, 1), 256, 0, st>>>(x, a.x_stride, a.batch, a.rows, a.cols,
-                                                           a.q, a.s, a.amax);
+    if (a.mode == MOE_QUANT_BOTH)
+      quant_col_kernel<false, true><<<quant_grid(tiles, 1), 256, 0, st>>>(
+          x, a.x_stride, a.batch, a.rows, a.cols, a.qT, a.sT, a.amax, a.q, a.s);
+    else
+      quant_col_kernel<false, false><<<quant_grid(tiles, 1), 256, 0, st>>>(
+          x, a.x_stride, a.batch, a.rows, a.cols, a.q, a.s, a.amax, nullptr, nullptr);
   }
   return hipGetLastError();
 }

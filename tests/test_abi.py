@@ -424,7 +424,11 @@ def _quant_args(**kw):
 def test_quantize_validation():
     assert _call("moe_quantize_mxfp8", _quant_args()) == DEVICE
     assert _call("moe_quantize_mxfp8", _quant_args(mode=B.QUANT_COL)) == DEVICE
-    assert _call("moe_quantize_mxfp8", _quant_args(mode=2)) == INVALID
+    # BOTH needs the COL destination as well
+    assert _call("moe_quantize_mxfp8", _quant_args(mode=B.QUANT_BOTH)) == INVALID
+    assert _call("moe_quantize_mxfp8", _quant_args(mode=B.QUANT_BOTH, qT=64)) == INVALID
+    assert _call("moe_quantize_mxfp8", _quant_args(mode=B.QUANT_BOTH, qT=64, sT=64)) == DEVICE
+    assert _call("moe_quantize_mxfp8", _quant_args(mode=3)) == INVALID
     assert _call("moe_quantize_mxfp8", _quant_args(rows=96)) == INVALID    # % 64
     assert _call("moe_quantize_mxfp8", _quant_args(cols=160)) == INVALID   # % 64
     assert _call("moe_quantize_mxfp8", _quant_args(batch=-1)) == INVALID
@@ -441,7 +445,11 @@ def test_quantize_mxfp4_validation():
     assert _call("moe_quantize_mxfp4", _quant_args(rows=96)) == DEVICE      # % 32 is enough
     assert _call("moe_quantize_mxfp4", _quant_args(mode=B.QUANT_COL)) == DEVICE
     assert _call("moe_quantize_mxfp4", _quant_args(mode=B.QUANT_COL, rows=96)) == INVALID
-    assert _call("moe_quantize_mxfp4", _quant_args(mode=2)) == INVALID
+    assert _call("moe_quantize_mxfp4", _quant_args(mode=B.QUANT_BOTH)) == INVALID
+    assert _call("moe_quantize_mxfp4", _quant_args(mode=B.QUANT_BOTH, qT=64, sT=64)) == DEVICE
+    assert _call("moe_quantize_mxfp4",
+                 _quant_args(mode=B.QUANT_BOTH, qT=64, sT=64, rows=96)) == INVALID   # % 64
+    assert _call("moe_quantize_mxfp4", _quant_args(mode=3)) == INVALID
     assert _call("moe_quantize_mxfp4", _quant_args(rows=80)) == INVALID     # % 32
     assert _call("moe_quantize_mxfp4", _quant_args(cols=160)) == INVALID    # % 64
     assert _call("moe_quantize_mxfp4", _quant_args(amax=64)) == INVALID

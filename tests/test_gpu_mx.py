@@ -83,6 +83,52 @@ def test_quantize_bit_exact(mode, batch, rows, cols, pad):
     assert float(amax.cpu()[0]) == np.abs(v).max()
 
 
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("batch,rows,cols,pad", [(1, 64, 64, 0), (3, 128, 192, 0),
+                                                 (2, 192, 2880, 40)])
+def test_quantize_both_copies_in_one_pass(fmt, batch, rows, cols, pad):
+    """MOE_QUANT_BOTH writes the ROW copy to q / s and the COL copy to qT /
+    sT in one pass: each bit-exact against the oracle's encoding along its
+    axis (and so equal to the one-copy modes)."""
+    rng = np.random.default_rng(rows + cols + 17)
+    bits = _hard_bf16(rng, (batch, rows, cols))
+    stride = rows * cols + pad
+    flat = np.zeros(batch * stride, np.uint16)
+    for b in range(batch):
+        flat[b * stride:b * stride + rows * cols] = bits[b].reshape(-1)
+    x = dev_bf16(flat)
+    nq = batch * rows * cols // (2 if fmt == "mxfp4" else 1)
+    q, qT = (torch.full((nq,), 0xAB, dtype=torch.uint8, device="cuda") for _ in range(2))
+    s, sT = (torch.full((batch * rows * cols // 32,), 0xAB, dtype=torch.uint8, device="cuda")
+             for _ in range(2))
+    kw = dict(mode=mg.QUANT_BOTH, batch=batch, rows=rows, cols=cols, x=x, q=q, s=s, qT=qT, sT=sT,
+              x_stride=stride if pad else 0)
+    if fmt == "mxfp8":
+        amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+        mg.moe_quantize_mxfp8(amax=amax, **kw)
+    else:
+        mg.moe_quantize_mxfp4(**kw)
+    torch.cuda.synchronize()
+    v = nu.bf16_to_f64(bits)
+    for qq, ss, transposed in ((q, s, False), (qT, sT, True)):
+        R, K = (cols, rows) if transposed else (rows, cols)
+        qh = qq.cpu().numpy().reshape(batch, -1)
+        sh = ss.cpu().numpy().reshape(batch, -1)
+        for b in range(batch):
+            src = v[b].T if transposed else v[b]
+            s_plain = mx_scales_plain(torch.from_numpy(sh[b]), R, K)
+            what = f"{fmt} BOTH {'COL' if transposed else 'ROW'} batch {b}"
+            if fmt == "mxfp8":
+                assert_mx_equal(qh[b].reshape(R, K), s_plain, nu.mx_quantize(src, axis=1), what)
+            else:
+                codes, scales = nu.mxfp4_quantize(src, axis=1)
+                np.testing.assert_array_equal(qh[b].reshape(R, K // 2), nu.pack_nibbles(codes),
+                                              err_msg=what)
+                np.testing.assert_array_equal(s_plain, scales, err_msg=what)
+    if fmt == "mxfp8":
+        assert float(amax.cpu()[0]) == np.abs(v).max()
+
+
 def test_permute_write_mx_bit_exact():
     wl = make_workload("dsv3", T=1500, H=448, with_weights=False)
     x = wl.x
