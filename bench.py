@@ -474,8 +474,9 @@ def measure(args, config, prec, log_prefix=""):
     if args.recompute:
         ev_rc = n_ev
         n_ev += 1
-    # MX layers start the step by quantizing the bf16 master weights (they
-    # change every training step); the event after it opens the routing
+    # MX layers quantize the bf16 master weights in every step (they change
+    # every training step), right after the routing, skipping the experts
+    # that received no rows; the event before it closes the routing
     qw_in_step = prec != "bf16" and not args.cached_weights
     ev_qw = None
     if qw_in_step:
@@ -494,17 +495,17 @@ def measure(args, config, prec, log_prefix=""):
 
     def quantize_weights(evs, base):
         if qw_in_step:
-            blk.quantize_weights()
             if evs is not None:
                 evs.record(base + ev_qw, cur_stream())
+            blk.quantize_weights(live_only=True)
 
     def step_unfused(evs=None, base=0):
         # 0 start; 1-4 forward GEMM / act / GEMM boundaries; 5 after the
         # unpermute; 6-9 backward boundaries; 10 after the dX unpermute
         if evs is not None:
             evs.record(base + 0, cur_stream())
-        quantize_weights(evs, base)
         blk.route(idx, probs, x)
+        quantize_weights(evs, base)
         blk.experts_forward_unfused(None if evs is None else _Rec(evs, base + 1))
         blk.combine(blk.yp, blk.out)
         if evs is not None:
@@ -523,8 +524,8 @@ def measure(args, config, prec, log_prefix=""):
             return step_unfused(evs, base)
         if evs is not None:
             evs.record(base + 0, cur_stream())
-        quantize_weights(evs, base)
         blk.route(idx, probs, x)
+        quantize_weights(evs, base)
         blk.experts_forward(None if evs is None else
                             [evs.ev[base + 1], evs.ev[base + 2], evs.ev[base + 3]])
         blk.combine(blk.yp, blk.out)
@@ -617,14 +618,14 @@ def measure(args, config, prec, log_prefix=""):
     def seg(a, b):
         return sum(evs.elapsed_ms(n_ev * i + a, n_ev * i + b) for i in range(n_eager)) / n_eager
 
-    r0 = ev_qw if qw_in_step else 0    # the routing starts after the weight quantization
+    r1 = ev_qw if qw_in_step else 1    # the weight quantization follows the routing
     if args.unfused:
-        seg_ms = {"route_permute_x": seg(r0, 1), "fc1": seg(1, 2), "act_fwd": seg(2, 3),
+        seg_ms = {"route_permute_x": seg(0, r1), "fc1": seg(1, 2), "act_fwd": seg(2, 3),
                   "fc2": seg(3, 4), "unpermute_out": seg(4, 5), "permute_dout": seg(5, 6),
                   "fc2_dgrad": seg(6, 7), "act_bwd": seg(7, 8), "fc1_dgrad": seg(8, 9),
                   "unpermute_dx": seg(9, 10)}
     else:
-        seg_ms = {"route_permute_x": seg(r0, 1), "fc1": seg(1, 2), "fc2": seg(2, 3),
+        seg_ms = {"route_permute_x": seg(0, r1), "fc1": seg(1, 2), "fc2": seg(2, 3),
                   "unpermute_out": seg(3, 4), "permute_dout": seg(4, 5),
                   "fc2_dgrad": seg(5, 6), "fc1_dgrad": seg(6, 7), "unpermute_dx": seg(7, 8)}
     if args.wgrad:
@@ -632,7 +633,7 @@ def measure(args, config, prec, log_prefix=""):
     if args.recompute:
         seg_ms.update(permute_dout=seg(4, ev_rc), fc1_recompute=seg(ev_rc, 5))
     if qw_in_step:
-        seg_ms["quantize_weights"] = seg(0, ev_qw)
+        seg_ms["quantize_weights"] = seg(ev_qw, 1)
     evs.close()
     assert int(blk.err_flag.cpu()[0]) == 0
     value = flops_step / (ms_step * 1e-3) / 1e12
@@ -668,8 +669,10 @@ def measure(args, config, prec, log_prefix=""):
         # MX transposed copies of Xp and dYp (bf16 in, codes + scales out)
         mem["wgrad_quantize"] = 2 * M * H * (2 + (1 if mx else 0.5) + 1 / 32)
     if qw_in_step:
-        # the two weights read once each, both MX copies of each written
-        n_w = E * n1 * H + E * H * I
+        # the two weights of every expert that has rows, read once each,
+        # both MX copies of each written
+        live = int((blk.split_sizes > 0).sum().item())
+        n_w = live * (n1 * H + H * I)
         mem["quantize_weights"] = n_w * (2 + 2 * ((1 if mx else 0.5) + 1 / 32))
     for name, b in mem.items():
         kernels[name] = {"ms": round(seg_ms[name], 4), "unit": "GB/s",

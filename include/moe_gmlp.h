@@ -244,7 +244,9 @@ moe_status moe_unpermute(const moe_unpermute_args* args, void* stream);
  *   rows and cols must be multiples of 64.  If amax != NULL, *amax is raised
  *   to max|x| (the caller zeroes it first).  Memory-bound: reads 2 bytes and
  *   writes 33/32 bytes per element and copy.  qT and sT are read only in
- *   the BOTH mode.
+ *   the BOTH mode.  With live (say the split sizes, batch = E), the batch
+ *   entries of experts with no routed rows are skipped: a step's GEMMs read
+ *   no weight of such an expert.
  * ---------------------------------------------------------------------- */
 #define MOE_QUANT_ROW 0
 #define MOE_QUANT_COL 1
@@ -260,6 +262,9 @@ typedef struct moe_quant_args {
   float* amax;                 /* optional device float */
   uint8_t* qT;                 /* device, MOE_QUANT_BOTH: the COL codes */
   uint8_t* sT;                 /* device, MOE_QUANT_BOTH: the COL scales */
+  const int32_t* live;         /* optional device int32 [batch]: entries with
+                                  live[b] == 0 are skipped (their codes and
+                                  scales keep what they held) */
 } moe_quant_args;
 
 moe_status moe_quantize_mxfp8(const moe_quant_args* args, void* stream);

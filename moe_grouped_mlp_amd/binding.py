@@ -77,7 +77,7 @@ class QuantArgs(ctypes.Structure):
     _fields_ = [("mode", c_int32), ("batch", c_int32), ("rows", c_int32),
                 ("cols", c_int32), ("x_stride", c_int64), ("x", c_void_p),
                 ("q", c_void_p), ("s", c_void_p), ("amax", c_void_p),
-                ("qT", c_void_p), ("sT", c_void_p)]
+                ("qT", c_void_p), ("sT", c_void_p), ("live", c_void_p)]
 
 
 class FwdArgs(ctypes.Structure):
@@ -297,17 +297,17 @@ def moe_unpermute(*, T, k, H, M_cap, row_id_map, yp, out, dprobs_p=None,
 
 
 def moe_quantize_mxfp8(*, mode, batch, rows, cols, x, q, s, x_stride=0,
-                       amax=None, qT=None, sT=None, stream=None):
+                       amax=None, qT=None, sT=None, live=None, stream=None):
     a = QuantArgs(mode, batch, rows, cols, x_stride, _ptr(x), _ptr(q), _ptr(s),
-                  _ptr(amax), _ptr(qT), _ptr(sT))
+                  _ptr(amax), _ptr(qT), _ptr(sT), _ptr(live))
     _check("moe_quantize_mxfp8",
            lib().moe_quantize_mxfp8(ctypes.byref(a), _stream(stream)))
 
 
 def moe_quantize_mxfp4(*, batch, rows, cols, x, q, s, mode=QUANT_ROW, x_stride=0,
-                       qT=None, sT=None, stream=None):
+                       qT=None, sT=None, live=None, stream=None):
     a = QuantArgs(mode, batch, rows, cols, x_stride, _ptr(x), _ptr(q), _ptr(s), None,
-                  _ptr(qT), _ptr(sT))
+                  _ptr(qT), _ptr(sT), _ptr(live))
     _check("moe_quantize_mxfp4",
            lib().moe_quantize_mxfp4(ctypes.byref(a), _stream(stream)))
 

@@ -228,12 +228,15 @@ class ExpertBlock:
         if self.mx or self.mx4:
             self.quantize_weights()
 
-    def quantize_weights(self) -> None:
+    def quantize_weights(self, live_only: bool = False) -> None:
         """MX copies of the bf16 weights, each blocked along the K of the
         GEMM that reads it: W1i along H (FC1), W2 along I (FC2), W2 along H
         (FC2 dgrad, stored [E][I][H]) and W1i along N1 (FC1 dgrad, stored
         [E][H][N1]).  In training the bf16 master weights change every step,
-        so a step starts with this (bench.py times it inside the step)."""
+        so a step makes them anew (bench.py times it inside the step).
+        live_only: after route(), skip the experts with no routed rows (this
+        step's GEMMs read none of their weights; their copies are left as
+        they were)."""
         E, H, I, N1 = self.E, self.H, self.I, self.N1
         # one pass per weight writes both of its copies (ROW into q / s, COL
         # into qT / sT), reading the bf16 weight once
@@ -245,7 +248,8 @@ class ExpertBlock:
                                                   (self.w2, H, I, "w2", "w2t")):
             quant(mode=B.QUANT_BOTH, batch=E, rows=rows, cols=cols, x=x,
                   q=getattr(self, row_copy + "_q" + sfx), s=getattr(self, row_copy + "_s" + sfx),
-                  qT=getattr(self, col_copy + "_q" + sfx), sT=getattr(self, col_copy + "_s" + sfx))
+                  qT=getattr(self, col_copy + "_q" + sfx), sT=getattr(self, col_copy + "_s" + sfx),
+                  live=self.split_sizes if live_only else None)
 
     # ------------------------------------------------------------ forward --
     def route(self, expert_idx: torch.Tensor, probs: torch.Tensor,

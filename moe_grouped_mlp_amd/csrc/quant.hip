@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restri
                                                         int64_t x_stride, int batch, int rows,
                                                         int cols, uint8_t* __restrict__ q,
                                                         uint8_t* __restrict__ s,
-                                                        float* __restrict__ amax) {
+                                                        float* __restrict__ amax,
+                                                        const int32_t* __restrict__ live) {
   const int lane = threadIdx.x & 63;
   const int units_r = rows / 32, units_c = cols / 64;
   const int64_t units = static_cast<int64_t>(batch) * units_r * units_c;
@@ -55,6 +56,7 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restri
   for (int64_t u = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64; u < units;
        u += static_cast<int64_t>(gridDim.x) * blockDim.x / 64) {
     const int bi = static_cast<int>(u / (static_cast<int64_t>(units_r) * units_c));
+    if (live && live[bi] == 0) continue;   // wave-uniform
     const int rem = static_cast<int>(u % (static_cast<int64_t>(units_r) * units_c));
     const int ur = rem / units_c, uc = rem % units_c;
     const int row = ur * 32 + (lane & 31);
@@ -138,7 +140,8 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
                                                         uint8_t* __restrict__ s,
                                                         float* __restrict__ amax,
                                                         uint8_t* __restrict__ qr,
-                                                        uint8_t* __restrict__ sr) {
+                                                        uint8_t* __restrict__ sr,
+                                                        const int32_t* __restrict__ live) {
   __shared__ uint16_t tile[kColTileR * kColPitch];
   const int t = threadIdx.x;
   const int tiles_r = (rows + kColTileR - 1) / kColTileR;
@@ -149,6 +152,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
   uint32_t wmax = 0;
   for (int64_t id = blockIdx.x; id < tiles; id += gridDim.x) {
     const int bi = static_cast<int>(id / (static_cast<int64_t>(tiles_r) * tiles_c));
+    if (live && live[bi] == 0) continue;   // uniform over the workgroup
     const int rem = static_cast<int>(id % (static_cast<int64_t>(tiles_r) * tiles_c));
     const int r0 = (rem / tiles_c) * kColTileR, c0 = (rem % tiles_c) * kColTileC;
     const int rr = min(kColTileR, rows - r0);  // 64 or 128
@@ -224,7 +228,8 @@ __global__ __launch_bounds__(256) void quant_row_fp4_kernel(const uint16_t* __re
                                                             int64_t x_stride, int batch,
                                                             int rows, int cols,
                                                             uint8_t* __restrict__ q,
-                                                            uint8_t* __restrict__ s) {
+                                                            uint8_t* __restrict__ s,
+                                                            const int32_t* __restrict__ live) {
   const int lane = threadIdx.x & 63;
   const int units_r = rows / 32, units_c = cols / 64;
   const int64_t units = static_cast<int64_t>(batch) * units_r * units_c;
@@ -232,6 +237,7 @@ __global__ __launch_bounds__(256) void quant_row_fp4_kernel(const uint16_t* __re
   for (int64_t u = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64; u < units;
        u += static_cast<int64_t>(gridDim.x) * blockDim.x / 64) {
     const int bi = static_cast<int>(u / (static_cast<int64_t>(units_r) * units_c));
+    if (live && live[bi] == 0) continue;   // wave-uniform
     const int rem = static_cast<int>(u % (static_cast<int64_t>(units_r) * units_c));
     const int ur = rem / units_c, uc = rem % units_c;
     const int row = ur * 32 + (lane & 31);
@@ -261,17 +267,17 @@ hipError_t launch_quantize_mxfp4(const moe_quant_args& a, hipStream_t st) {
   if (a.mode == MOE_QUANT_ROW) {
     const int64_t units = static_cast<int64_t>(a.batch) * (a.rows / 32) * (a.cols / 64);
     quant_row_fp4_kernel<<<quant_grid(units, 4), 256, 0, st>>>(x, a.x_stride, a.batch, a.rows,
-                                                               a.cols, a.q, a.s);
+                                                               a.cols, a.q, a.s, a.live);
   } else {
     const int64_t tiles = static_cast<int64_t>(a.batch) * ((a.rows + kColTileR - 1) / kColTileR) *
                           ((a.cols + kColTileC - 1) / kColTileC);
     // BOTH: the COL copy goes to qT / sT, the ROW copy to q / s
     if (a.mode == MOE_QUANT_BOTH)
       quant_col_kernel<true, true><<<quant_grid(tiles, 1), 256, 0, st>>>(
-          x, a.x_stride, a.batch, a.rows, a.cols, a.qT, a.sT, nullptr, a.q, a.s);
+          x, a.x_stride, a.batch, a.rows, a.cols, a.qT, a.sT, nullptr, a.q, a.s, a.live);
     else
       quant_col_kernel<true, false><<<quant_grid(tiles, 1), 256, 0, st>>>(
-          x, a.x_stride, a.batch, a.rows, a.cols, a.q, a.s, nullptr, nullptr, nullptr);
+          x, a.x_stride, a.batch, a.rows, a.cols, a.q, a.s, nullptr, nullptr, nullptr, a.live);
   }
   return hipGetLastError();
 }
@@ -281,16 +287,16 @@ hipError_t launch_quantize_mxfp8(const moe_quant_args& a, hipStream_t st) {
   if (a.mode == MOE_QUANT_ROW) {
     const int64_t units = static_cast<int64_t>(a.batch) * (a.rows / 32) * (a.cols / 64);
     quant_row_kernel<<<quant_grid(units, 4), 256, 0, st>>>(x, a.x_stride, a.batch, a.rows, a.cols,
-                                                           a.q, a.s, a.amax);
+                                                           a.q, a.s, a.amax, a.live);
   } else {
     const int64_t tiles = static_cast<int64_t>(a.batch) * ((a.rows + kColTileR - 1) / kColTileR) *
                           ((a.cols + kColTileC - 1) / kColTileC);
     if (a.mode == MOE_QUANT_BOTH)
       quant_col_kernel<false, true><<<quant_grid(tiles, 1), 256, 0, st>>>(
-          x, a.x_stride, a.batch, a.rows, a.cols, a.qT, a.sT, a.amax, a.q, a.s);
+          x, a.x_stride, a.batch, a.rows, a.cols, a.qT, a.sT, a.amax, a.q, a.s, a.live);
     else
       quant_col_kernel<false, false><<<quant_grid(tiles, 1), 256, 0, st>>>(
-          x, a.x_stride, a.batch, a.rows, a.cols, a.q, a.s, a.amax, nullptr, nullptr);
+          x, a.x_stride, a.batch, a.rows, a.cols, a.q, a.s, a.amax, nullptr, nullptr, a.live);
   }
   return hipGetLastError();
 }

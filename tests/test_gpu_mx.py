@@ -129,6 +129,37 @@ def test_quantize_both_copies_in_one_pass(fmt, batch, rows, cols, pad):
         assert float(amax.cpu()[0]) == np.abs(v).max()
 
 
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_quantize_skips_entries_that_are_not_live(fmt):
+    """With live (a device int32 per batch entry), entries whose count is 0
+    keep what their codes and scales held; the others are encoded as
+    without the mask."""
+    rng = np.random.default_rng(23)
+    batch, rows, cols = 4, 128, 192
+    bits = _hard_bf16(rng, (batch, rows, cols))
+    x = dev_bf16(bits.reshape(-1))
+    live = torch.tensor([3, 0, 1, 0], dtype=torch.int32, device="cuda")
+    nq = batch * rows * cols // (2 if fmt == "mxfp4" else 1)
+    outs = [torch.full((n,), 0xAB, dtype=torch.uint8, device="cuda")
+            for n in (nq, batch * rows * cols // 32, nq, batch * rows * cols // 32)]
+    q, s, qT, sT = outs
+    quant = mg.moe_quantize_mxfp8 if fmt == "mxfp8" else mg.moe_quantize_mxfp4
+    quant(mode=mg.QUANT_BOTH, batch=batch, rows=rows, cols=cols, x=x, q=q, s=s, qT=qT, sT=sT,
+          live=live)
+    ref = [torch.full_like(t, 0xAB) for t in outs]
+    quant(mode=mg.QUANT_BOTH, batch=batch, rows=rows, cols=cols, x=x, q=ref[0], s=ref[1],
+          qT=ref[2], sT=ref[3])
+    torch.cuda.synchronize()
+    for got, full in zip(outs, ref):
+        g = got.view(batch, -1)
+        f = full.view(batch, -1)
+        for b in range(batch):
+            if b in (1, 3):
+                assert bool((g[b] == 0xAB).all()), f"entry {b} was written"
+            else:
+                assert torch.equal(g[b], f[b]), f"entry {b}"
+
+
 def test_permute_write_mx_bit_exact():
     wl = make_workload("dsv3", T=1500, H=448, with_weights=False)
     x = wl.x
