@@ -919,6 +919,16 @@ def main():
                          "frac": round(s["fc1_rate"] / pk8, 4), "traffic": None,
                          "avg_launch_ms": round(s["fc1_ms"], 4)},
         }
+        qw = s["kernels"].get("quantize_weights", {}).get("ms")
+        if qw is not None and not s["kernels"]["quantize_weights"].get("outside_step"):
+            # the same step less the weight quantization (once per optimizer
+            # step, so shared by the microbatches of gradient accumulation):
+            # derived from the eager pass's segment time, not timed apart
+            ms_wo = s["ms_step"] - qw
+            secondary["weight_quantize_ms"] = qw
+            secondary["ms_per_step_without_weight_quantize"] = round(ms_wo, 4)
+            secondary["value_without_weight_quantize"] = round(
+                s["flops_step"] / (ms_wo * 1e-3) / 1e12, 3)
         log(f"secondary MXFP8: step {s['ms_step']:.3f} ms, {s['value']:.1f} TFLOP/s "
             f"({100 * s['value'] / pk8:.1f}% of fp8 peak)")
 
