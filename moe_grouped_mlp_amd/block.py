@@ -10,8 +10,11 @@ of a training step on the current stream:
             dprobs)
 
 With prec=PREC_MXFP8 the permutes write MXFP8 rows (no bf16 copy), the four
-GEMMs take MXFP8 operands, and quantize_weights() (once per weight update)
-makes the four weight copies the GEMMs read, each blocked along its K.  The
+GEMMs take MXFP8 operands, and quantize_weights() (after every weight update;
+load_weights() calls it) makes the four weight copies the GEMMs read, each
+blocked along its K.  A training step whose optimizer has just changed the
+bf16 weights calls quantize_weights(live_only=True) between route() and the
+GEMMs: it then skips the experts that received no rows this step.  The
 epilogues then write only the MXFP8 copies of a and dz that the next GEMMs
 (and weight-gradient GEMMs) read, unless bf16_copies=True also asks for the
 bf16 tensors.
