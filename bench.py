@@ -29,8 +29,9 @@ on both sides) the mean, which is `value`.  Per-kernel times come from a
 separate eager pass with hipEvents between the library's launches.  The
 default run (Mixtral, bf16) also measures the Mixtral layer with MXFP8
 operands in the same process (`secondary`, with its own fp8 roofline
-fraction), the top-k router, and a plain device copy as the practical HBM
-ceiling of the gather and combine kernels.  The GPT-OSS layer runs in MXFP8
+fraction), the GPT-OSS layer (MXFP8) and the DeepSeek-V3 share (bf16 and
+MXFP8) as compact lines (`other_layers`), the top-k router, and a plain
+device copy as the practical HBM ceiling of the gather and combine kernels.  The GPT-OSS layer runs in MXFP8
 (slope 1.702, clamp at +-7) unless --prec says otherwise.
 
 Prints one JSON line (stdout).  Progress goes to stderr.
@@ -845,7 +846,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the secondary Mixtral MXFP8 measurement of the default run")
+                    help="skip the secondary Mixtral MXFP8 and the other-layer measurements "
+                         "of the default run")
     ap.add_argument("--unfused", action="store_true",
                     help="the unfused baseline (bf16): plain grouped GEMMs with the "
                          "activation and its gradient as separate passes")
@@ -932,6 +934,34 @@ def main():
         log(f"secondary MXFP8: step {s['ms_step']:.3f} ms, {s['value']:.1f} TFLOP/s "
             f"({100 * s['value'] / pk8:.1f}% of fp8 peak)")
 
+    # the other layers the pages measure, each at its own configuration, in
+    # the same run (GPT-OSS: MXFP8 with beta 1.702 and clamp 7; DSv3 share:
+    # bf16 and MXFP8); compact lines, the full ones come from --config
+    others = None
+    if (args.config == "mixtral" and prec == "bf16" and not args.no_secondary
+            and not (args.unfused or args.wgrad or args.recompute)):
+        others = {}
+        for oc, op in (("gptoss", "mxfp8"), ("dsv3", "bf16"), ("dsv3", "mxfp8")):
+            o = measure(args, oc, op, log_prefix=f"{oc} {op}: ")
+            pko = PEAK_TFLOPS[op]
+            ck = o["timing"]["gemm_shader_clock_ghz"]
+            others[f"{oc}_{op}"] = {
+                "workload": f"{oc} expert layer: E={o['E']} top-{o['k']} T={o['T']} "
+                            f"H={o['H']} I={o['I']} {o['cfg']['act']} beta={o['cfg']['beta']} "
+                            f"clamp={o['cfg']['clamp']}, {op}",
+                "value": round(o["value"], 3), "unit": "TFLOP/s",
+                "ms_per_step": round(o["ms_step"], 4),
+                "median_ms": o["timing"]["median_ms"], "p10_ms": o["timing"]["p10_ms"],
+                "p90_ms": o["timing"]["p90_ms"],
+                "pct_mfma_peak": round(100.0 * o["value"] / pko, 2),
+                "pct_mfma_peak_at_measured_clock": (
+                    round(100.0 * o["value"] / (pko * ck / 2.4), 2) if ck else None),
+                "gemm_shader_clock_ghz": ck, "group_skew": o["skew"],
+                "kernel_ms": {n: v["ms"] for n, v in o["kernels"].items()},
+            }
+            log(f"{oc} {op}: step {o['ms_step']:.3f} ms, {o['value']:.1f} TFLOP/s "
+                f"({100 * o['value'] / pko:.1f}% of {op} peak)")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -992,6 +1022,8 @@ def main():
             r["fc1_rate"] / (peak * clock / 2.4), 4)
     if secondary is not None:
         out["secondary"] = secondary
+    if others is not None:
+        out["other_layers"] = others
     print(json.dumps(out), flush=True)
 
 
