@@ -160,6 +160,69 @@ def test_quantize_skips_entries_that_are_not_live(fmt):
                 assert torch.equal(g[b], f[b]), f"entry {b}"
 
 
+@pytest.mark.parametrize("fmt,mode", [("mxfp8", mg.QUANT_BOTH), ("mxfp8", mg.QUANT_ROW),
+                                      ("mxfp8", mg.QUANT_COL), ("mxfp4", mg.QUANT_BOTH),
+                                      ("mxfp4", mg.QUANT_ROW)])
+def test_quantize_many_slices_per_workgroup(fmt, mode):
+    """Inputs larger than one pass of the launch (more 128 x 128 slices than
+    workgroups, more 32 x 64 units than waves), with 64-row and 64-column
+    tails: sampled slices bit-exact against the oracle's encoding along the
+    copy's axis, so each workgroup's later slices (loaded while the one
+    before was being encoded) are checked too."""
+    batch, rows, cols = 3, 4160, 4160
+    rng = np.random.default_rng(77 + mode)
+    bits = _hard_bf16(rng, (batch, rows, cols))
+    x = dev_bf16(bits.reshape(-1))
+    n = batch * rows * cols
+    f4 = fmt == "mxfp4"
+    nq = n // 2 if f4 else n
+    q, qT = (torch.full((nq,), 0xAB, dtype=torch.uint8, device="cuda") for _ in range(2))
+    s, sT = (torch.full((n // 32,), 0xAB, dtype=torch.uint8, device="cuda") for _ in range(2))
+    kw = dict(mode=mode, batch=batch, rows=rows, cols=cols, x=x, q=q, s=s)
+    if mode == mg.QUANT_BOTH:
+        kw.update(qT=qT, sT=sT)
+    (mg.moe_quantize_mxfp4 if f4 else mg.moe_quantize_mxfp8)(**kw)
+    torch.cuda.synchronize()
+    # (codes, scales) of the ROW copy (q / s unless COL-only) and the COL copy
+    row_out = (q, s) if mode in (mg.QUANT_ROW, mg.QUANT_BOTH) else None
+    col_out = (qT, sT) if mode == mg.QUANT_BOTH else ((q, s) if mode == mg.QUANT_COL else None)
+    per_b = nq // batch
+    ts = 128
+    n_r, n_c = -(-rows // ts), -(-cols // ts)
+    picks = [(b, i, j) for b in range(batch) for i, j in
+             [(n_r - 1, n_c - 1), (0, 0), (n_r - 1, 0), (0, n_c - 1)]] + \
+            [(int(rng.integers(batch)), int(rng.integers(n_r)), int(rng.integers(n_c)))
+             for _ in range(24)]
+
+    def check(out, transposed, b, r0, c0, rr, cw):
+        qq, ss = out
+        R, K = (cols, rows) if transposed else (rows, cols)
+        qb = qq[b * per_b:(b + 1) * per_b].cpu().numpy().reshape(R, K // 2 if f4 else K)
+        sb = mx_scales_plain(ss[b * (n // batch // 32):(b + 1) * (n // batch // 32)], R, K)
+        v = nu.bf16_to_f64(bits[b, r0:r0 + rr, c0:c0 + cw])
+        if transposed:
+            v, (a0, a1, k0, kn) = v.T, (c0, cw, r0, rr)
+        else:
+            a0, a1, k0, kn = r0, rr, c0, cw
+        what = f"{fmt} mode {mode} {'COL' if transposed else 'ROW'} batch {b} slice ({r0}, {c0})"
+        s_got = sb[a0:a0 + a1, k0 // 32:(k0 + kn) // 32]
+        if f4:
+            codes, scales = nu.mxfp4_quantize(v, axis=1)
+            np.testing.assert_array_equal(qb[a0:a0 + a1, k0 // 2:(k0 + kn) // 2],
+                                          nu.pack_nibbles(codes), err_msg=what)
+            np.testing.assert_array_equal(s_got, scales, err_msg=what)
+        else:
+            assert_mx_equal(qb[a0:a0 + a1, k0:k0 + kn], s_got, nu.mx_quantize(v, axis=1), what)
+
+    for b, i, j in picks:
+        r0, c0 = i * ts, j * ts
+        rr, cw = min(ts, rows - r0), min(ts, cols - c0)
+        if row_out is not None:
+            check(row_out, False, b, r0, c0, rr, cw)
+        if col_out is not None:
+            check(col_out, True, b, r0, c0, rr, cw)
+
+
 def test_permute_write_mx_bit_exact():
     wl = make_workload("dsv3", T=1500, H=448, with_weights=False)
     x = wl.x
