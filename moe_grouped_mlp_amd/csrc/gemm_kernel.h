@@ -497,7 +497,12 @@ constexpr int kTrTile = 32 * kTrPitch;
 // so the reads see the staging writes just before them (the memory clobber
 // keeps those writes ahead of the block).
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+// REDERIVE: the addresses are re-derived from the lane at every block
+// rather than kept live across the epilogue (the MXFP4 dGLU kernel spilled
+// them and reloaded them in front of its stores).
+template <bool REDERIVE>
 MOE_DEV void col_gather(const uint2 (&w)[4], uint16_t* tr, int lane, uint2 (&c)[4]) {
+  if constexpr (REDERIVE) lane = opaque(lane);
   const int row = lane & 31, hf = lane >> 5;
 #pragma unroll
   for (int rg = 0; rg < 4; ++rg)
@@ -528,7 +533,7 @@ MOE_DEV void mx_col_block(const uint2 (&w)[4], uint16_t* tr, uint8_t* q_lane, ui
                           int lane) {
   const int hf = lane >> 5;
   uint2 c[4];
-  col_gather(w, tr, lane, c);
+  col_gather<false>(w, tr, lane, c);
   const int e = block_exponent<8>(pair_max_bits(bf16_amax_bits(c), hf));
   const float scale = mx_scale_f32(e);
   uint4 q;
@@ -546,7 +551,7 @@ MOE_DEV void mx4_col_block(const uint2 (&w)[4], uint16_t* tr, uint8_t* q_lane, u
                            int lane) {
   const int hf = lane >> 5;
   uint2 c[4];
-  col_gather(w, tr, lane, c);
+  col_gather<true>(w, tr, lane, c);
   const int e = block_exponent<2>(pair_max_bits(bf16_amax_bits(c), hf));
   const float scale = mx_scale_f32(e);
   uint2 q;
@@ -556,26 +561,24 @@ MOE_DEV void mx4_col_block(const uint2 (&w)[4], uint16_t* tr, uint8_t* q_lane, u
   if (hf == 0) *s_byte = mx_scale_code(e);
 }
 
-// The lane's store addresses of its row block (32 rows starting at row
-// block rb, the lane's row `row`) for the block at column 0; the block at a
-// column col0 (a multiple of 32) adds wave-uniform offsets only (mx_block_out),
-// so no per-lane 64-bit address arithmetic is repeated block by block.
+// MXFP8: the lane's store addresses of its row block (32 rows starting at
+// row block rb, the lane's row `row`) for the block at column 0; the block
+// at a column col0 (a multiple of 32) adds wave-uniform offsets only
+// (mx_block_out), so no per-lane 64-bit address arithmetic is repeated
+// block by block.
 struct MxBase {
   uint8_t* q;    // rowwise codes: o.q + row * n + 16 hf
   uint8_t* s;    // rowwise scale of (row, K block 0)
   uint8_t* qT;   // transposed codes of column lane % 32, rows 32 rb + 16 hf ..
-                 // (MXFP4: two a byte, [n][M_cap / 2])
   uint8_t* sT;   // transposed scale of (column lane % 32, row block rb)
 };
 
-template <bool F4OUT = false>
 MOE_DEV MxBase mx_base(const MxOut& o, int64_t row, int64_t rb, int lane) {
   const int hf = lane >> 5, c = lane & 31;
   MxBase b;
-  b.q = F4OUT ? o.q + row * (o.n / 2) + 8 * hf : o.q + row * o.n + 16 * hf;
+  b.q = o.q + row * o.n + 16 * hf;
   b.s = o.s + mx_scale_off(row, 0, o.n);
-  b.qT = F4OUT ? o.qT + static_cast<int64_t>(c) * (o.M_cap / 2) + rb * 16 + 8 * hf
-                : o.qT + static_cast<int64_t>(c) * o.M_cap + rb * 32 + 16 * hf;
+  b.qT = o.qT + static_cast<int64_t>(c) * o.M_cap + rb * 32 + 16 * hf;
   b.sT = o.sT + mx_scale_off(c, rb, o.M_cap);
   return b;
 }
@@ -595,18 +598,59 @@ MOE_DEV uint32_t mx_block_out(const uint2 (&w)[4], const MxOut& o, const MxBase&
   return am;
 }
 
+// MXFP4: store addresses of one 32-row block, rows r0b .. r0b + 31 (r0b a
+// multiple of 32, wave-uniform; lane l owns row r0b + l % 32 and, in the
+// transposed copy, column l % 32 of every 32-column block): the block's
+// bases, wave-uniform so they stay in scalar registers, and the lane's
+// offsets from them, 32-bit.  Holding no per-lane 64-bit addresses frees
+// the vector registers whose spills the MXFP4 dGLU kernel reloaded in front
+// of its stores (a reload waits for every store issued before it).  (The
+// MXFP8 kernels measured slightly slower this way and keep MxBase.)
+struct MxBase4 {
+  uint8_t* q;         // rowwise codes of row r0b
+  uint8_t* s;         // rowwise scales of row group r0b / 32, K block 0
+  uint8_t* qT;        // transposed codes of column 0 at row r0b
+  uint8_t* sT;        // transposed scale of (column 0, row block r0b / 32)
+  uint32_t q_lane;    // (l % 32) rows + 8 hf bytes
+  uint32_t qT_lane;   // (l % 32) columns + 8 hf bytes
+};
+
+// The copies stay below 4 GiB (checked by the host), so the lane offsets
+// fit 32 bits.
+MOE_DEV MxBase4 mx_base4(const MxOut& o, int64_t r0b, int lane) {
+  const uint32_t hf = static_cast<uint32_t>(lane) >> 5, c = static_cast<uint32_t>(lane) & 31;
+  const int64_t rb = r0b >> 5;
+  MxBase4 b;
+  b.q = o.q + r0b * (o.n / 2);
+  b.s = o.s + rb * (o.n >> 6) * 64;                 // mx_scale_off(r0b + c, 0, n) - c
+  b.qT = o.qT + rb * 16;
+  b.sT = o.sT + (rb >> 1) * 64 + (rb & 1) * 32;     // mx_scale_off(c, rb, M_cap) - c
+  b.q_lane = c * static_cast<uint32_t>(o.n / 2) + 8u * hf;
+  b.qT_lane = c * static_cast<uint32_t>(o.M_cap / 2) + 8u * hf;
+  return b;
+}
+
 // Both MXFP4 copies (rowwise codes [M_cap][n / 2], transposed [n][M_cap / 2])
-// of the same block; returns the lane's maximum as a bf16 magnitude pattern.
-// TR: the kernel writes the transposed copy (o.qT set).
+// of the block at columns col0 .. col0 + 31 (col0 % 32 == 0, wave-uniform);
+// returns the lane's maximum as a bf16 magnitude pattern.  TR: the kernel
+// writes the transposed copy (o.qT set).
 template <bool TR>
-MOE_DEV uint32_t mx4_block_out(const uint2 (&w)[4], const MxOut& o, const MxBase& b,
+MOE_DEV uint32_t mx4_block_out(const uint2 (&w)[4], const MxOut& o, const MxBase4& b,
                                uint16_t* tr, int col0, int lane) {
-  uint8_t* const sb = b.s + (col0 >> 6) * 64 + ((col0 >> 5) & 1) * 32;
-  const uint32_t am = mx4_row_block(w, b.q + col0 / 2, sb, lane >> 5);
+  const uint32_t c = static_cast<uint32_t>(lane) & 31;
+  uint8_t* const sb = b.s + ((col0 >> 6) * 64 + ((col0 >> 5) & 1) * 32) + c;
+  const uint32_t am = mx4_row_block(w, b.q + col0 / 2 + b.q_lane, sb, lane >> 5);
   if constexpr (TR)
-    mx4_col_block(w, tr, b.qT + static_cast<int64_t>(col0) * (o.M_cap / 2),
-                  b.sT + static_cast<int64_t>(col0 >> 5) * (o.M_cap >> 6) * 64, lane);
+    mx4_col_block(w, tr, b.qT + static_cast<int64_t>(col0) * (o.M_cap / 2) + b.qT_lane,
+                  b.sT + static_cast<int64_t>(col0 >> 5) * (o.M_cap >> 6) * 64 + c, lane);
   return am;
+}
+
+// The block bases of either format (MXFP4: r0b is the block's first row).
+template <bool F4OUT>
+MOE_DEV auto mx_block_base(const MxOut& o, int64_t row, int64_t r0b, int lane) {
+  if constexpr (F4OUT) return mx_base4(o, r0b, lane);
+  else return mx_base(o, row, r0b >> 5, lane);
 }
 
 MOE_DEV void bf16x4_to_f32(uint2 w, float* v) {
@@ -845,6 +889,11 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
                          const MxOut& mo, uint16_t* tr, const float* sb) {
   constexpr bool gated = ACT != MOE_ACT_SRELU;
   const int hf = lane >> 5;
+  if constexpr (F4OUT) {
+    // the wave's row and column: uniform, so the block bases stay scalar
+    wm = __builtin_amdgcn_readfirstlane(wm);
+    wn = __builtin_amdgcn_readfirstlane(wn);
+  }
   uint32_t am = 0;   // the lane's max |a| as a bf16 magnitude pattern
   sfor<4>([&](auto mi) {
     sfor<4>([&](auto ni) { acc_hold(acc[mi][ni]); });
@@ -854,9 +903,8 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
     const int blk = wm * t.wrow + mi * 32;
     const bool blk_ok = blk < t.rows_pad;
     const int64_t row = t.row0 + m;
-    const int64_t rb = (t.row0 + blk) / 32;
     const float p = pr[mi];
-    const MxBase mb = mx_base<F4OUT>(mo, row, rb, lane);
+    const auto mb = mx_block_base<F4OUT>(mo, row, t.row0 + blk, lane);
     if constexpr (gated) {
       if (wn * kWaveN < t.cols_valid) {
         const int q = (t.col0 + wn * kWaveN) / (2 * MOE_INTERLEAVE);
@@ -886,8 +934,8 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
           // them leaves the maximum unchanged
           if (blk_ok) {
             const int cb = q * MOE_INTERLEAVE + h * 32;
-            am = max(am, F4OUT ? mx4_block_out<TR>(wb, mo, mb, tr, cb, lane)
-                               : mx_block_out(wb, mo, mb, tr, cb, lane));
+            if constexpr (F4OUT) am = max(am, mx4_block_out<TR>(wb, mo, mb, tr, cb, lane));
+            else am = max(am, mx_block_out(wb, mo, mb, tr, cb, lane));
           }
         });
       }
@@ -913,8 +961,8 @@ MOE_DEV float epi_glu_mx(f32x16 (&acc)[4][4], uint16_t* __restrict__ z, int64_t 
             wb[rg] = w;
           });
           if (blk_ok)
-            am = max(am, F4OUT ? mx4_block_out<TR>(wb, mo, mb, tr, cb, lane)
-                               : mx_block_out(wb, mo, mb, tr, cb, lane));
+            if constexpr (F4OUT) am = max(am, mx4_block_out<TR>(wb, mo, mb, tr, cb, lane));
+            else am = max(am, mx_block_out(wb, mo, mb, tr, cb, lane));
         }
       });
     }
@@ -933,6 +981,11 @@ MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
                            uint16_t* tr, const float* sb) {
   constexpr bool gated = ACT != MOE_ACT_SRELU;
   sfor<4>([&](auto ni) { acc_hold(acc[MI][ni]); });
+  if constexpr (F4OUT) {
+    // the wave's row and column: uniform, so the block bases stay scalar
+    wm = __builtin_amdgcn_readfirstlane(wm);
+    wn = __builtin_amdgcn_readfirstlane(wn);
+  }
   const int h = lane >> 5, r16 = opaque(lane & 15);
   const int lane_col = gated ? 2 * t.col0 + 256 * wn + 4 * h : t.col0 + 128 * wn + 4 * h;
   const char* zb = zrow + (gated ? 512 : 256) * wn + 8 * h;
@@ -941,8 +994,7 @@ MOE_DEV float dglu_rows_mx(f32x16 (&acc)[4][4], const char* zrow,
   const int blk = wm * kWaveM + MI * 32;
   const bool blk_ok = blk < t.rows_pad;
   const int64_t row = t.row0 + m;
-  const int64_t rb = (t.row0 + blk) / 32;
-  const MxBase mb = mx_base<F4OUT>(mo, row, rb, lane);
+  const auto mb = mx_block_base<F4OUT>(mo, row, t.row0 + blk, lane);
   float dp = 0.0f;
   sfor<4>([&](auto ni) {
     if (wn * kWaveN + ni * 32 < t.cols_valid) {
@@ -1831,7 +1883,7 @@ void grouped_gemm_kernel(GemmArgs g) {
             reinterpret_cast<const char*>(wm_e ? zb : za) + (lane_e & 31) * kZRow;
         if constexpr (MX)
           dp[MI] = dglu_rows_mx<ACT, MI, F4, kTrOut>(acc, zrow, g.C, g.ldc, pr[MI], g.act, te, wn_e, wm_e,
-                                         lane_e, mo, s_tr + wave_e * kTrTile, sb);
+                                         lane_e, mo, s_tr + (F4 ? __builtin_amdgcn_readfirstlane(wave_e) : wave_e) * kTrTile, sb);
         else
           dp[MI] = dglu_rows<ACT, MI>(acc, zrow, g.C, g.ldc, pr[MI], g.act, te, wn_e, lane_e,
                                       sb);
