@@ -353,7 +353,8 @@ moe_status moe_quantize_mxfp4(const moe_quant_args* args, void* stream);
  *   (codes [M_cap][I / 2]) and, when aT_q is set, aT_q/aT_s, its MXFP4
  *   transposed copy blocked along M (codes [I][M_cap / 2], pad rows as
  *   zeros), the operand of the MXFP4 weight gradient.  No bias (bias1
- *   NULL), else MOE_ERR_INVALID_ARG.
+ *   NULL), else MOE_ERR_INVALID_ARG.  MXFP4 serves M_cap up to 2^27 and I
+ *   up to 2^26 (forward and backward), else MOE_ERR_UNSUPPORTED.
  * ---------------------------------------------------------------------- */
 typedef struct moe_fwd_args {
   int32_t E, H, I;

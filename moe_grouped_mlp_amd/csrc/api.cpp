@@ -305,6 +305,10 @@ static moe_status check_common(int E, int H, int I, int64_t M_cap, int prec,
   if (prec != MOE_PREC_BF16 && prec != MOE_PREC_MXFP8 && prec != MOE_PREC_MXFP4)
     return MOE_ERR_INVALID_ARG;
   if (prec != MOE_PREC_BF16 && M_cap % 128 != 0) return MOE_ERR_INVALID_ARG;
+  // MXFP4 epilogues address 31 rows or columns of a copy with 32-bit lane
+  // offsets
+  if (prec == MOE_PREC_MXFP4 && (M_cap > (int64_t(1) << 27) || I > (1 << 26)))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

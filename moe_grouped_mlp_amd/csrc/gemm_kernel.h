@@ -615,8 +615,8 @@ struct MxBase4 {
   uint32_t qT_lane;   // (l % 32) columns + 8 hf bytes
 };
 
-// The copies stay below 4 GiB (checked by the host), so the lane offsets
-// fit 32 bits.
+// The lane offsets span at most 31 rows or columns of a copy: 32 bits for
+// M_cap up to 2^27 and I up to 2^26 (checked by the host).
 MOE_DEV MxBase4 mx_base4(const MxOut& o, int64_t r0b, int lane) {
   const uint32_t hf = static_cast<uint32_t>(lane) >> 5, c = static_cast<uint32_t>(lane) & 31;
   const int64_t rb = r0b >> 5;

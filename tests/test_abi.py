@@ -532,6 +532,10 @@ def test_fwd_bwd_mxfp4_validation():
     assert _call("moe_grouped_mlp_fwd", _fwd_args(**{**base, "aT_q": 64})) == INVALID
     assert _call("moe_grouped_mlp_fwd", _fwd_args(**{**base, "bias1": 64})) == INVALID
     assert _call("moe_grouped_mlp_fwd", _fwd_args(**{**base, "M_cap": 1000})) == INVALID
+    # the MXFP4 epilogues' 32-bit lane offsets: M_cap up to 2^27, I up to 2^26
+    assert _call("moe_grouped_mlp_fwd",
+                 _fwd_args(**{**base, "M_cap": (1 << 27) + 128})) == UNSUPPORTED
+    assert _call("moe_grouped_mlp_fwd", _fwd_args(**{**base, "I": (1 << 26) + 64})) == UNSUPPORTED
 
     a = B.BwdArgs()
     a.E, a.H, a.I, a.M_cap, a.prec = 4, 128, 256, 1024, B.PREC_MXFP4
