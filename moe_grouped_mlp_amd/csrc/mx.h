@@ -74,6 +74,16 @@ MOE_DEV uint32_t mx4_codes4_bf16(uint2 w, float scale) {
                                                    1);
 }
 
+// The largest of a quad's four values (lanes 4 i .. 4 i + 3, every lane
+// active): DPP quad permutations [1 0 3 2] and [2 3 0 1], no LDS traffic.
+MOE_DEV uint32_t mx_quad_max(uint32_t m) {
+  m = max(m, static_cast<uint32_t>(
+                 __builtin_amdgcn_mov_dpp(static_cast<int>(m), 0xB1, 0xF, 0xF, false)));
+  m = max(m, static_cast<uint32_t>(
+                 __builtin_amdgcn_mov_dpp(static_cast<int>(m), 0x4E, 0xF, 0xF, false)));
+  return m;
+}
+
 // |v| of a bf16 pattern as an ordered integer (bf16 magnitudes compare like
 // their bit patterns).
 MOE_DEV uint32_t bf16_abs_bits(uint32_t b) { return b & 0x7fffu; }

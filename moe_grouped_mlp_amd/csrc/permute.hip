@@ -41,8 +41,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
         rows[s] = (r >= 0 && r < M_cap) ? r : -1;
       }
       const i32x4* src = x + static_cast<int64_t>(t) * H8;
-      for (int c = lane; c < H8; c += kWave) {
-        const i32x4 v = src[c];
+      auto put = [&](int c, const i32x4 v) {
         if (xp) {
 #pragma unroll
           for (int s = 0; s < kMaxTopK; ++s)
@@ -55,8 +54,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
             const uint32_t w = static_cast<uint32_t>(v[i]);
             m = max(m, max(bf16_abs_bits(w), bf16_abs_bits(w >> 16)));
           }
-          m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 1, kWave)));
-          m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 2, kWave)));
+          m = mx_quad_max(m);
           const float am = __uint_as_float(m << 16);
           const int e = F4 ? mx4_exponent(am) : mx_exponent(am);
           const float scale = mx_scale_f32(e);
@@ -78,6 +76,25 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
             if ((c & 3) == 0) xs[mx_scale_off(rows[s], c >> 2, H)] = mx_scale_code(e);
           }
         }
+      };
+      if (!xq) {
+        // plain copy: four of the row's 16-byte chunks per lane are loaded
+        // before any is stored, so several loads are in flight at once (a
+        // chunk past the row re-reads the first one, which is in range, and
+        // is not stored); measured faster for bf16 rows, not for MX rows
+        for (int c0 = lane; c0 < H8; c0 += 4 * kWave) {
+          i32x4 vs[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int c = c0 + u * kWave;
+            vs[u] = src[c < H8 ? c : c0];
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (c0 + u * kWave < H8) put(c0 + u * kWave, vs[u]);
+        }
+      } else {
+        for (int c = lane; c < H8; c += kWave) put(c, src[c]);
       }
     }
     return;

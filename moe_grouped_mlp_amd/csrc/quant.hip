@@ -24,16 +24,6 @@ namespace {
 
 MOE_DEV float amax_of_bits(uint32_t m) { return __uint_as_float(m << 16); }
 
-// The largest of a quad's four maxima (lanes 4 i .. 4 i + 3): DPP quad
-// permutations [1 0 3 2] and [2 3 0 1].
-MOE_DEV uint32_t quad_max(uint32_t m) {
-  m = max(m, static_cast<uint32_t>(
-                 __builtin_amdgcn_mov_dpp(static_cast<int>(m), 0xB1, 0xF, 0xF, false)));
-  m = max(m, static_cast<uint32_t>(
-                 __builtin_amdgcn_mov_dpp(static_cast<int>(m), 0x4E, 0xF, 0xF, false)));
-  return m;
-}
-
 // Largest magnitude of 8 bf16 values (4 packed words), as a bit pattern.
 MOE_DEV uint32_t amax8_bits(const uint4& v) {
   const uint32_t a = max(max(bf16_abs_bits(v.x), bf16_abs_bits(v.x >> 16)),
@@ -99,7 +89,7 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restri
                   (ch >> 2) * 32 + rl;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t m = quad_max(amax8_bits(v[j]));
+      const uint32_t m = mx_quad_max(amax8_bits(v[j]));
       const int e = block_exp<F4>(m);
       store_codes8<F4>(v[j], mx_scale_f32(e), q, off0 + static_cast<int64_t>(8 * j) * cols);
       if ((lane & 3) == 0) sb[8 * j] = mx_scale_code(e);
@@ -313,7 +303,7 @@ __global__ __launch_bounds__(256) void quant_slice8_kernel(const uint16_t* __res
           const int k = t + 256 * j;
           const int r = k / g.cpr, c = k % g.cpr;
           const uint4 w = *reinterpret_cast<const uint4*>(tile + r * kSlPitch + 8 * c);
-          const uint32_t m = quad_max(amax8_bits(w));
+          const uint32_t m = mx_quad_max(amax8_bits(w));
           const int e = block_exp<false>(m);
           const int64_t row = g.r0 + r;
           const int col = g.c0 + 8 * c;
