@@ -137,25 +137,45 @@ __global__ __launch_bounds__(kBlock) void unpermute_kernel(
       for (int s = 0; s < kMaxTopK; ++s) if (s == lane) r = rows[s];
       dprobs[static_cast<int64_t>(t) * k + lane] = r >= 0 ? dprobs_p[r] : 0.0f;
     }
-    for (int c = lane; c < H8; c += kWave) {
-      float acc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    // two 16-byte chunks per lane per pass, so that 2k loads are in flight;
+    // each chunk still sums its slots in slot order (a second chunk past
+    // the row re-reads the first, which is in range, and is not stored)
+    for (int c0 = lane; c0 < H8; c0 += 2 * kWave) {
+      const bool two = c0 + kWave < H8;
+      const int c1 = two ? c0 + kWave : c0;
+      i32x4 v0[kMaxTopK], v1[kMaxTopK];
 #pragma unroll
       for (int s = 0; s < kMaxTopK; ++s) {
         if (rows[s] < 0) continue;
-        const i32x4 v = yp[static_cast<int64_t>(rows[s]) * H8 + c];
+        const i32x4* row = yp + static_cast<int64_t>(rows[s]) * H8;
+        v0[s] = row[c0];
+        v1[s] = row[c1];
+      }
+      float acc0[8], acc1[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc0[i] = acc1[i] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < kMaxTopK; ++s) {
+        if (rows[s] < 0) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t w = static_cast<uint32_t>(v[i]);
-          acc[2 * i] += __uint_as_float(w << 16);
-          acc[2 * i + 1] += __uint_as_float(w & 0xffff0000u);
+          const uint32_t w0 = static_cast<uint32_t>(v0[s][i]);
+          const uint32_t w1 = static_cast<uint32_t>(v1[s][i]);
+          acc0[2 * i] += __uint_as_float(w0 << 16);
+          acc0[2 * i + 1] += __uint_as_float(w0 & 0xffff0000u);
+          acc1[2 * i] += __uint_as_float(w1 << 16);
+          acc1[2 * i + 1] += __uint_as_float(w1 & 0xffff0000u);
         }
       }
-      i32x4 o;
+      i32x4 o0, o1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = static_cast<int>(pack_bf16x2(acc[2 * i], acc[2 * i + 1]));
-      out[static_cast<int64_t>(t) * H8 + c] = o;
+      for (int i = 0; i < 4; ++i) {
+        o0[i] = static_cast<int>(pack_bf16x2(acc0[2 * i], acc0[2 * i + 1]));
+        o1[i] = static_cast<int>(pack_bf16x2(acc1[2 * i], acc1[2 * i + 1]));
+      }
+      i32x4* dst = out + static_cast<int64_t>(t) * H8;
+      dst[c0] = o0;
+      if (two) dst[c1] = o1;
     }
   }
 }
