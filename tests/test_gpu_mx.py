@@ -162,7 +162,7 @@ def test_quantize_skips_entries_that_are_not_live(fmt):
 
 @pytest.mark.parametrize("fmt,mode", [("mxfp8", mg.QUANT_BOTH), ("mxfp8", mg.QUANT_ROW),
                                       ("mxfp8", mg.QUANT_COL), ("mxfp4", mg.QUANT_BOTH),
-                                      ("mxfp4", mg.QUANT_ROW)])
+                                      ("mxfp4", mg.QUANT_ROW), ("mxfp4", mg.QUANT_COL)])
 def test_quantize_many_slices_per_workgroup(fmt, mode):
     """Inputs larger than one pass of the launch (more 128 x 128 slices than
     workgroups, more 32 x 64 units than waves), with 64-row and 64-column
