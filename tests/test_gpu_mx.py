@@ -130,15 +130,23 @@ def test_quantize_both_copies_in_one_pass(fmt, batch, rows, cols, pad):
 
 
 @pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
-def test_quantize_skips_entries_that_are_not_live(fmt):
+@pytest.mark.parametrize("batch,rows,cols", [(4, 128, 192), (300, 64, 320), (1100, 64, 128)])
+def test_quantize_skips_entries_that_are_not_live(fmt, batch, rows, cols):
     """With live (a device int32 per batch entry), entries whose count is 0
     keep what their codes and scales held; the others are encoded as
-    without the mask."""
-    rng = np.random.default_rng(23)
-    batch, rows, cols = 4, 128, 192
+    without the mask: a hand-picked mask on 4 entries, and random masks
+    (about 30% of the entries off, the first always off) on 300 and 1100
+    small entries."""
+    rng = np.random.default_rng(23 + batch)
     bits = _hard_bf16(rng, (batch, rows, cols))
     x = dev_bf16(bits.reshape(-1))
-    live = torch.tensor([3, 0, 1, 0], dtype=torch.int32, device="cuda")
+    if batch == 4:
+        counts = np.array([3, 0, 1, 0], dtype=np.int32)
+    else:
+        counts = rng.integers(0, 4, batch).astype(np.int32) * (rng.random(batch) < 0.7)
+        counts[:2] = (0, 5)
+    dead = set(np.flatnonzero(counts == 0).tolist())
+    live = torch.from_numpy(counts).to("cuda")
     nq = batch * rows * cols // (2 if fmt == "mxfp4" else 1)
     outs = [torch.full((n,), 0xAB, dtype=torch.uint8, device="cuda")
             for n in (nq, batch * rows * cols // 32, nq, batch * rows * cols // 32)]
@@ -153,11 +161,13 @@ def test_quantize_skips_entries_that_are_not_live(fmt):
     for got, full in zip(outs, ref):
         g = got.view(batch, -1)
         f = full.view(batch, -1)
+        written = (g != 0xAB).any(dim=1).cpu().numpy()
+        same = (g == f).all(dim=1).cpu().numpy()
         for b in range(batch):
-            if b in (1, 3):
-                assert bool((g[b] == 0xAB).all()), f"entry {b} was written"
+            if b in dead:
+                assert not written[b], f"entry {b} was written"
             else:
-                assert torch.equal(g[b], f[b]), f"entry {b}"
+                assert same[b], f"entry {b}"
 
 
 @pytest.mark.parametrize("fmt,mode", [("mxfp8", mg.QUANT_BOTH), ("mxfp8", mg.QUANT_ROW),
